@@ -1,0 +1,285 @@
+"""Benchmark of one tree-verification step on one MI355X.
+
+A step = spec_tree_attn -> spec_tree_reject -> spec_kv_compact over one batch
+of the synthetic workload (default: the chain configuration, a Llama-2-13B-
+shaped layer: 40 MHA heads, head dim 128, bf16 paged KV, prefix 2048, chain
+of 4 drafts + root, vocabulary 32000, temperature 1).  Metric: verified tree
+tokens per second = B * T / step time.
+
+Inputs are resident in HBM before timing starts.  Several copies of every
+input are cycled so that consecutive steps never find their data in the
+256 MB MALL / L2 (each copy is re-read only after the others have streamed
+through).  Steps are replayed from HIP graphs (one capture per copy), so the
+timed region holds only GPU work; the K timed steps are bracketed by
+torch.cuda.synchronize().  Per-kernel average durations come from HIP events
+around graphs that repeat one call many times on the same stream.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+METRIC = "verified tree tokens/sec at 1 MI355X"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def depths(parent_row):
+    d = [0] * len(parent_row)
+    for i in range(1, len(parent_row)):
+        d[i] = d[parent_row[i]] + 1
+    return d
+
+
+def attn_work(w):
+    elt = 2 if w.dtype == "bf16" else 4
+    kv = sum((int(L) + w.T) for L in w.prefix_lens) * w.Hkv * w.D * elt * 2
+    qo = 2 * w.B * w.T * w.Hq * w.D * elt
+    pairs = sum(w.T * int(L) + sum(dd + 1 for dd in depths(w.parent[b])) for b, L in enumerate(w.prefix_lens))
+    return kv + qo, 4.0 * w.Hq * w.D * pairs
+
+
+def reject_bytes(w, nacc, stop_rejections):
+    """Bytes the walk needs: target-logit rows of the visited nodes, plus the
+    draft row of a stop node whose residual had to be formed."""
+    return sum((int(L) + 1) * w.V * 4 + (w.V * 4 if stop_rejections[b] else 0) for b, L in enumerate(nacc))
+
+
+def compact_bytes(w, acc, nacc):
+    elt = 2 if w.dtype == "bf16" else 4
+    moved = 0
+    for b, L in enumerate(nacc):
+        path = acc[b][:int(L) + 1]
+        moved += sum(1 for d, n in enumerate(path) if n != d)
+    return moved * w.Hkv * w.D * elt * 2 * 2  # K and V, read + write
+
+
+def cpu_baseline(cfg, budget_s):
+    """The oracle (as it stands) on the same workload, timed on the host cores."""
+    import oracle
+    from workloads import make_config
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w = make_config(cfg)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.tree_attention(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_lens, w.parent, w.scale,
+                              dtype=w.dtype)
+        r = oracle.tree_reject(w.target_logits, w.draft_probs, w.draft_tokens, w.parent, w.temperature,
+                               w.without_replacement, w.seed, steps)
+        oracle.kv_compact(w.k_cache, w.v_cache, w.block_table, w.prefix_lens, r["accepted_nodes"],
+                          r["num_accepted"])
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 200:
+            break
+    return {"value": w.B * w.T * steps / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} full steps of the same workload (fp64 NumPy attention + walk + compaction), "
+                      f"{el:.1f} s, {len(os.sched_getaffinity(0))} host cores visible"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="workload id 0..4 (default 1: chain)")
+    ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: auto, >= 768 MB)")
+    ap.add_argument("--kernel-reps", type=int, default=0, help="launches per per-kernel timing graph")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--offset", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tree_verify_attention_masked_amd as stv
+    from workloads import make_config
+
+    stv.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] building workload {args.config}")
+    w = make_config(args.config)
+
+    def up(a, kv=False):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if kv and w.dtype == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to(dev)
+
+    per_copy = (w.k_cache.nbytes * 2 + w.q.nbytes + w.target_logits.nbytes + w.draft_probs.nbytes)
+    R = args.copies or max(1, min(16, math.ceil(768e6 / per_copy)))
+    log(f"[bench] {R} input copies of {per_copy / 1e6:.1f} MB")
+    shared = dict(bt=up(w.block_table), lens=up(w.prefix_lens), parent=up(w.parent), tok=up(w.draft_tokens))
+    copies = []
+    for _ in range(R):
+        c = dict(q=up(w.q, True), k=up(w.k_cache, True), v=up(w.v_cache, True), logits=up(w.target_logits),
+                 probs=up(w.draft_probs))
+        c["out"] = torch.empty_like(c["q"])
+        c["acc"] = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
+        c["toks"] = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
+        c["nacc"] = torch.empty((w.B,), dtype=torch.int32, device=dev)
+        c["new_lens"] = torch.empty((w.B,), dtype=torch.int32, device=dev)
+        c["status"] = torch.zeros((w.B,), dtype=torch.int32, device=dev)
+        copies.append(c)
+    code = stv.SPEC_BF16 if w.dtype == "bf16" else stv.SPEC_F32
+    ws_attn = stv.spec_tree_attn_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, w.max_blocks, code)
+    attn_ws = torch.empty(max(ws_attn, 1), dtype=torch.uint8, device=dev)
+    rej_ws = torch.empty(int(stv.load_library().spec_tree_reject_workspace_size(w.B, w.T, w.V)),
+                         dtype=torch.uint8, device=dev)
+
+    def attn(c):
+        stv.spec_tree_attn(c["q"], c["k"], c["v"], shared["bt"], shared["lens"], shared["parent"], scale=w.scale,
+                           out=c["out"], status=c["status"], workspace=attn_ws if ws_attn else None)
+
+    def reject(c):
+        stv.spec_tree_reject(c["logits"], c["probs"], shared["tok"], shared["parent"], w.temperature,
+                             w.without_replacement, w.seed, args.offset, accepted_nodes=c["acc"],
+                             out_tokens=c["toks"], num_accepted=c["nacc"], status=c["status"], workspace=rej_ws)
+
+    def compact(c):
+        stv.spec_kv_compact(c["k"], c["v"], shared["bt"], shared["lens"], c["acc"], c["nacc"],
+                            new_lens=c["new_lens"], status=c["status"])
+
+    def step(c):
+        attn(c)
+        reject(c)
+        compact(c)
+
+    for c in copies:  # eager pass: validates and warms every copy
+        step(c)
+    torch.cuda.synchronize()
+    st = sum(int(c["status"].abs().sum()) for c in copies)
+    if st:
+        raise SystemExit(f"device reported input errors: {[c['status'].tolist() for c in copies]}")
+
+    def capture(fn_list):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for fn in fn_list:
+                    fn()
+        torch.cuda.current_stream().wait_stream(s)
+        return g
+
+    step_graphs = [capture([lambda c=c: step(c)]) for c in copies]
+    log(f"[bench] captured {len(step_graphs)} step graphs; warmup {args.warmup}")
+    for i in range(args.warmup):
+        step_graphs[i % R].replay()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(K):
+        step_graphs[i % R].replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    log(f"[bench] {K} steps: wall {wall * 1e3:.3f} ms, events {gpu_ms:.3f} ms")
+    ms_per_step = wall * 1e3 / K
+    value = w.B * w.T * K / wall
+
+    # per-kernel average durations: one graph = reps launches of one call over the copies
+    reps = args.kernel_reps or max(R, 8 * R if per_copy < 100e6 else R)
+    kdur = {}
+    for name, fn in (("tree_attn", attn), ("tree_reject", reject), ("kv_compact", compact)):
+        g = capture([lambda c=copies[i % R]: fn(c) for i in range(reps)])
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        rounds = max(1, 200 // reps)
+        e0.record()
+        for _ in range(rounds):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        kdur[name] = e0.elapsed_time(e1) * 1e-3 / (rounds * reps)  # seconds per call
+        log(f"[bench] {name}: {kdur[name] * 1e6:.2f} us per call")
+
+    acc = copies[0]["acc"].cpu().numpy()
+    nacc = copies[0]["nacc"].cpu().numpy()
+    # did the stop node form a residual (some child of it rejected)?
+    stop_rej = []
+    for b in range(w.B):
+        u = int(acc[b][int(nacc[b])])
+        stop_rej.append(any(int(w.parent[b][i]) == u for i in range(1, w.T)))
+    a_bytes, a_flops = attn_work(w)
+    work = {
+        "tree_attn": ("hbm", a_bytes, a_flops),
+        "tree_reject": ("hbm", reject_bytes(w, nacc, stop_rej), 0.0),
+        "kv_compact": ("hbm", compact_bytes(w, acc, nacc), 0.0),
+    }
+    dominant = max(kdur, key=kdur.get)
+    bound, bytes_, flops = work[dominant]
+    if dominant == "tree_attn" and flops / max(bytes_, 1) > BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+        bound = "mfma"
+    if bound == "hbm":
+        achieved = bytes_ / kdur[dominant] / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = flops / kdur[dominant] / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = dominant
+
+    kernels = {}
+    for name, (b_, by, fl) in work.items():
+        kernels[name] = {"us": round(kdur[name] * 1e6, 2), "bytes": int(by),
+                         "GB/s": round(by / kdur[name] / 1e9, 1)}
+        if fl:
+            kernels[name]["TFLOP/s"] = round(fl / kdur[name] / 1e12, 2)
+    kernels["tree_attn"]["hbm_frac"] = round(a_bytes / kdur["tree_attn"] / 1e9 / HBM_PEAK_GBS, 4)
+    kernels["tree_attn"]["mfma_frac"] = round(a_flops / kdur["tree_attn"] / 1e12 / BF16_PEAK_TFLOPS, 4)
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log(f"[bench] oracle baseline (~{args.cpu_budget:.0f} s)")
+        cpu = cpu_baseline(args.config, args.cpu_budget)
+
+    cfg = w.summary()
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu,
+        "kernels": kernels, "accepted_per_step": round(float(np.mean(nacc + 1)), 3),
+        "input_copies": R,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * spectree.h — C ABI of the tree-verification hot path of tree-based
+ * speculative decoding, for AMD Instinct MI355X (gfx950).
+ *
+ * Three calls, one per step of verifying a flattened draft tree in one target
+ * pass:
+ *   spec_tree_attn    tree-masked verify attention over a paged KV prefix
+ *   spec_tree_reject  tree rejection sampling (greedy, with replacement,
+ *                     or Sequoia-style without replacement)
+ *   spec_kv_compact   keep only the accepted root-to-leaf path in the KV cache
+ *
+ * Conventions shared by every call
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing, keeps no global state and is reentrant.
+ *   - Each call only enqueues work on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream).  No call synchronises or copies to the host,
+ *     so a caller can chain draft and verify steps without a CPU round trip.
+ *   - Shapes and pointers are checked on the host before anything is launched;
+ *     a failed check returns a negative spec_status and launches nothing.
+ *   - Device contents that the host cannot see without a copy (the parent
+ *     array, block-table entries, prefix lengths, draft tokens, NaN logits,
+ *     accepted paths) are checked by the kernels.  A kernel that finds a bad
+ *     value never reads or writes out of bounds; it ORs a SPEC_DEV_* bit into
+ *     `status[b]` (when `status` is not NULL) and writes a defined result for
+ *     that sequence (documented per call).  `status` must be zero-filled by
+ *     the caller before the first call that should report into it.
+ *   - Draft tree: T nodes flattened in topological order.  Node 0 is the root
+ *     (the last committed token); parent[b][0] = -1 and 0 <= parent[b][i] < i.
+ *     Node i may attend to tree node j iff j is i or an ancestor of i (the
+ *     tree_mask of "Report: Support nextn speculative decoding", EAGLE
+ *     implementation summary, step 3).
+ *   - Paged KV cache: [num_blocks, Hkv, block_size, D] for K and for V, with
+ *     block_size = 16.  Logical position t of sequence b lives at
+ *     cache[block_table[b][t / 16]][kv_head][t % 16][:].  Tree node i's K/V row
+ *     is at logical position prefix_lens[b] + i, written by the caller before
+ *     spec_tree_attn (with its rotary position prefix_lens[b] + depth(i)).
+ */
+#ifndef SPECTREE_H
+#define SPECTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_ERR_INVALID_ARG = -1, /* null pointer, non-positive or inconsistent size */
+  SPEC_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype, D, block size, T > 256) */
+  SPEC_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than the *_workspace_size */
+  SPEC_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} spec_status;
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+/* Device-detected input errors, OR-ed into status[b]. */
+enum {
+  SPEC_DEV_PARENT = 1,     /* parent[b] is not a topological parent array */
+  SPEC_DEV_BLOCK = 2,      /* a needed block_table entry is outside [0, num_blocks) */
+  SPEC_DEV_LENGTH = 4,     /* prefix_lens[b] < 0 or prefix_lens[b] + T > max_blocks_per_seq * 16 */
+  SPEC_DEV_TOKEN = 8,      /* a draft token outside [0, V) */
+  SPEC_DEV_NONFINITE = 16, /* NaN/Inf in a target-logit row or a draft probability that was read */
+  SPEC_DEV_EMPTY = 32,     /* a distribution with zero total mass had to be sampled */
+  SPEC_DEV_PATH = 64       /* accepted path not of the form 0 = n_0 < n_1 < ... < n_L < T */
+};
+
+/* Human-readable name of a spec_status value. */
+const char* spec_status_string(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int spec_version(void);
+
+/* ------------------------------------------------------------------------
+ * spec_tree_attn — tree-masked verify attention.
+ *
+ * For every sequence b, tree node i and query head h (kv head g = h / (Hq/Hkv)):
+ *   keys K(i) = prefix positions 0 .. prefix_lens[b]-1, plus positions
+ *               prefix_lens[b] + j for every ancestor-or-self j of i;
+ *   out[b,i,h,:] = softmax_t(scale * <q[b,i,h,:], k_t>) . v_t  over t in K(i).
+ * This is the multi-query paged attention used to score all drafted tokens in
+ * one pass (vLLM PR "[WIP] Speculative decoding using a draft model", future
+ * work list; EAGLE report, step 3: attention is skipped for unrelated draft
+ * tokens).  Accumulation is fp32; bf16 inputs use bf16 matrix-core products.
+ *
+ *   q            [B, T, Hq, D] dtype, contiguous
+ *   k_cache      [num_blocks, Hkv, 16, D] dtype
+ *   v_cache      [num_blocks, Hkv, 16, D] dtype
+ *   block_table  [B, max_blocks_per_seq] int32; must cover prefix_lens[b] + T
+ *   prefix_lens  [B] int32, >= 0
+ *   parent       [B, T] int32
+ *   out          [B, T, Hq, D] dtype (written)
+ *   scale        softmax scale (callers normally pass 1/sqrt(D))
+ *   status       [B] int32 or NULL; on a device-detected error the rows of the
+ *                affected sequence are still written, from the subset of keys
+ *                that could be read safely
+ *   workspace    device scratch of at least spec_tree_attn_workspace_size(...)
+ *                bytes (may be NULL when that size is 0); its contents need no
+ *                initialisation and are not meaningful after the call
+ * Supported: dtype SPEC_BF16 with D = 128, dtype SPEC_F32 with D in {64, 128};
+ * block_size = 16; 1 <= T <= 256; Hq % Hkv == 0.  B == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+size_t spec_tree_attn_workspace_size(int B, int T, int Hq, int Hkv, int D,
+                                     int max_blocks_per_seq, int dtype);
+
+int spec_tree_attn(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_table, const int32_t* prefix_lens,
+                   const int32_t* parent, void* out,
+                   int B, int T, int Hq, int Hkv, int D, int block_size,
+                   int max_blocks_per_seq, int num_blocks, float scale, int dtype,
+                   int32_t* status, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * spec_tree_reject — tree rejection sampling.
+ *
+ * Per sequence, walk the tree from the root.  At the current node u, with
+ * p = softmax(target_logits[b,u,:] / temperature) and q = draft_probs[b,u,:]:
+ * try the children c of u in increasing index order with x = draft_tokens[b,c]
+ * and a uniform r: accept iff r * q(x) < p(x) ("Speculative Decoding" notes,
+ * "Draft Token Validation": accept when p >= q, else with probability p/q).
+ * After each rejected child p becomes max(p - q, 0) renormalised (left as is if
+ * that mass is 0); with without_replacement != 0, q also loses x and is
+ * renormalised (Sequoia summary, "Robust Sampling").  An accepted child becomes
+ * the current node.  When the current node has no untried child left, one
+ * token is drawn from the current p by inverse CDF in vocabulary order (the
+ * residual token, or the bonus token after a fully accepted branch).
+ * temperature == 0 is greedy: accept the first child whose token equals the
+ * argmax of the target logits (lowest index on ties), else emit that argmax.
+ *
+ * Randomness: Philox4x32-10 (Salmon et al., SC'11) with key = (seed lo, seed
+ * hi) and counter = (node, b, purpose + 2*(offset >> 32), offset lo), purpose
+ * 0 for the accept test of child `node`, 1 for the final draw at `node`;
+ * uniform = (word0 >> 8) * 2^-24.  A draw depends only on (seed, offset, b,
+ * node, purpose).  Decisions are taken in fp64 from the fp32 inputs.
+ *
+ *   target_logits [B, T, V] float32; row u = logits of the token after node u
+ *   draft_probs   [B, T, V] float32; row u = draft distribution the children
+ *                 of u were drafted from, used as given (not renormalised)
+ *   draft_tokens  [B, T] int32; token of node i (entry 0 ignored)
+ *   parent        [B, T] int32
+ *   accepted_nodes[B, T] int32 out: n_0 = 0, n_1 .. n_L, then -1
+ *   out_tokens    [B, T] int32 out: tokens of n_1 .. n_L, the drawn token, then -1
+ *   num_accepted  [B] int32 out: L
+ *   status        [B] int32 or NULL; on a device-detected error the sequence
+ *                 gets L = 0, accepted_nodes = [0, -1, ...], out_tokens all -1
+ *   workspace     >= spec_tree_reject_workspace_size(B, T, V) bytes; contents
+ *                 need no initialisation
+ * Supported: 1 <= T <= 256, 1 <= V <= 262144, temperature >= 0 and finite.
+ * ---------------------------------------------------------------------- */
+size_t spec_tree_reject_workspace_size(int B, int T, int V);
+
+int spec_tree_reject(const float* target_logits, const float* draft_probs,
+                     const int32_t* draft_tokens, const int32_t* parent,
+                     int B, int T, int V, float temperature, int without_replacement,
+                     uint64_t seed, uint64_t offset,
+                     int32_t* accepted_nodes, int32_t* out_tokens, int32_t* num_accepted,
+                     int32_t* status, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* ------------------------------------------------------------------------
+ * spec_kv_compact — selective KV-cache compaction (in place).
+ *
+ * For d = 1 .. L (L = num_accepted[b], path n_d = accepted_nodes[b][d]) and
+ * every kv head, the K and V rows at logical position prefix_lens[b] + n_d are
+ * moved to prefix_lens[b] + d, with the result of doing so in increasing d
+ * (a destination that is also a later source is read before it is written).
+ * Nothing else is written; slots past the new length keep stale data (the
+ * rejected tokens' KV is evicted: EAGLE report, "Important Implementation
+ * Detail"; SGLang doc, "Prefix Match").  new_lens[b] = prefix_lens[b] + L + 1.
+ *
+ *   k_cache, v_cache [num_blocks, Hkv, 16, D] dtype, modified in place
+ *   block_table, prefix_lens as for spec_tree_attn
+ *   accepted_nodes [B, T] int32, num_accepted [B] int32 (spec_tree_reject's output)
+ *   new_lens       [B] int32 out, or NULL
+ *   status         [B] int32 or NULL; a sequence with a bad path or table is
+ *                  left untouched and new_lens[b] = prefix_lens[b]
+ * Supported: as spec_tree_attn.  Sequences must not share blocks.
+ * ---------------------------------------------------------------------- */
+int spec_kv_compact(void* k_cache, void* v_cache, const int32_t* block_table,
+                    const int32_t* prefix_lens, const int32_t* accepted_nodes,
+                    const int32_t* num_accepted, int32_t* new_lens,
+                    int B, int T, int Hkv, int D, int block_size,
+                    int max_blocks_per_seq, int num_blocks, int dtype,
+                    int32_t* status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECTREE_H */

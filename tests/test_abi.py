@@ -1,0 +1,111 @@
+"""The C ABI library loads, exports every function include/spectree.h declares,
+and rejects bad arguments on the host before anything reaches the GPU.  No
+compute call is made here (these tests run without a GPU)."""
+import ctypes
+
+import pytest
+
+import tree_verify_attention_masked_amd as stv
+from tree_verify_attention_masked_amd import binding
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return stv.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = stv.header_functions()
+    assert {"spec_tree_attn", "spec_tree_reject", "spec_kv_compact"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(binding._SIGNATURES) == set(names)
+
+
+def test_status_strings_and_version(lib):
+    assert stv.spec_version() >= 100
+    for code in (0, -1, -2, -3, -4):
+        assert stv.spec_status_string(code).startswith("SPEC_")
+    assert stv.spec_status_string(7) == "unknown spec_status"
+
+
+def test_workspace_sizes(lib):
+    # fp32 and single-split bf16 need none; split-KV needs room for every partial
+    assert lib.spec_tree_attn_workspace_size(1, 8, 2, 2, 64, 9, 0) == 0
+    ws = lib.spec_tree_attn_workspace_size(1, 5, 40, 40, 128, 129, 1)
+    assert ws > 0 and ws % 4 == 0
+    assert lib.spec_tree_attn_workspace_size(1, 5, 40, 40, 100, 129, 1) == 0  # unsupported head dim
+    assert lib.spec_tree_reject_workspace_size(2, 5, 32000) == 2 * 5 * 8 * 16
+    assert lib.spec_tree_reject_workspace_size(0, 5, 32000) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def _attn(lib, **kw):
+    a = dict(B=1, T=5, Hq=4, Hkv=4, D=128, bs=16, mb=8, nb=8, scale=0.1, dtype=1, ws=None, wsz=0)
+    a.update(kw)
+    ptrs = [FAKE] * 7
+    if kw.get("null_q"):
+        ptrs[0] = None
+    return lib.spec_tree_attn(*ptrs, a["B"], a["T"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["mb"], a["nb"],
+                              a["scale"], a["dtype"], None, a["ws"], a["wsz"], None)
+
+
+def test_attn_host_validation(lib):
+    assert _attn(lib, null_q=True) == -1
+    assert _attn(lib, T=0) == -1
+    assert _attn(lib, Hq=6, Hkv=4) == -1
+    assert _attn(lib, D=64) == -2  # bf16 needs D = 128
+    assert _attn(lib, dtype=0, D=96) == -2
+    assert _attn(lib, bs=8) == -2
+    assert _attn(lib, T=300, mb=40) == -2
+    assert _attn(lib, mb=0) == -1
+    assert _attn(lib, T=200, mb=8) == -1  # the table cannot even hold the tree
+    assert _attn(lib, scale=float("nan")) == -1
+    assert _attn(lib, dtype=5) == -1
+    assert _attn(lib, B=0) == 0  # empty batch: nothing to do
+    # a split-KV plan without workspace
+    assert _attn(lib, T=5, Hq=40, Hkv=40, mb=129, nb=129) == -3
+
+
+def _reject(lib, **kw):
+    a = dict(B=1, T=4, V=100, tau=1.0, ws=FAKE, wsz=1 << 20, null_logits=False)
+    a.update(kw)
+    logits = None if a["null_logits"] else FAKE
+    return lib.spec_tree_reject(logits, FAKE, FAKE, FAKE, a["B"], a["T"], a["V"], a["tau"], 0, 0, 0,
+                                FAKE, FAKE, FAKE, None, a["ws"], a["wsz"], None)
+
+
+def test_reject_host_validation(lib):
+    assert _reject(lib, null_logits=True) == -1
+    assert _reject(lib, tau=-1.0) == -1
+    assert _reject(lib, tau=float("inf")) == -1
+    assert _reject(lib, T=0) == -1
+    assert _reject(lib, T=257) == -2
+    assert _reject(lib, V=300000) == -2
+    assert _reject(lib, ws=None) == -3
+    assert _reject(lib, wsz=10) == -3
+    assert _reject(lib, B=0) == 0
+
+
+def test_compact_host_validation(lib):
+    def call(**kw):
+        a = dict(B=1, T=5, Hkv=2, D=128, bs=16, mb=4, nb=4, dtype=1)
+        a.update(kw)
+        return lib.spec_kv_compact(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, a["B"], a["T"], a["Hkv"], a["D"],
+                                   a["bs"], a["mb"], a["nb"], a["dtype"], None, None)
+    assert call(D=32) == -2
+    assert call(bs=32) == -2
+    assert call(Hkv=0) == -1
+    assert call(B=0) == 0
+    assert lib.spec_kv_compact(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 5, 2, 128, 16, 4, 4, 1, None,
+                               None) == -1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 2, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        stv.spec_tree_attn(q, q, q, torch.zeros(1, 1, dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
+                           torch.zeros(1, 2, dtype=torch.int32))

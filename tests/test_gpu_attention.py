@@ -1,0 +1,113 @@
+"""GPU parity of spec_tree_attn against the fp64 oracle (called through the C ABI).
+
+Tolerance: bf16 outputs |gpu - oracle| <= 2e-2 + 1e-2 |oracle|; fp32 outputs
+1e-5 + 1e-5 |oracle|.  Small cases compare every output and span several KV
+tiles, several splits, a ragged last page and each kernel variant (key-split
+for <= 16 rows per kv head, 64-row and 256-row tiles); the five configurations
+run at full size, all outputs where the oracle is quick, sampled rows
+otherwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import DevWorkload, assert_attn_close, attn_to_f64
+from workloads import make_config, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_full(w):
+    d = DevWorkload(w)
+    out = d.attn()
+    torch.cuda.synchronize()
+    ref = oracle.tree_attention(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_lens, w.parent,
+                                w.scale, dtype=w.dtype)
+    err = assert_attn_close(attn_to_f64(w, out), ref, w.dtype, w.name)
+    assert int(d.status.abs().sum()) == 0
+    return err
+
+
+SMALL = [
+    # (name, kwargs)
+    ("f32_d64_tree", dict(B=2, Hq=4, Hkv=2, D=64, dtype="f32", prefix=[0, 77], tree="random", T=9, max_depth=4)),
+    ("f32_d128_chain", dict(B=1, Hq=3, Hkv=1, D=128, dtype="f32", prefix=[50], tree="chain", gamma=6)),
+    ("keysplit_chain", dict(B=2, Hq=4, Hkv=4, D=128, dtype="bf16", prefix=[17, 1000], tree="chain", gamma=4)),
+    ("keysplit_tree_gqa", dict(B=3, Hq=8, Hkv=4, D=128, dtype="bf16", prefix=[0, 15, 333], tree="random", T=8,
+                               max_depth=3, shuffle_blocks=True)),
+    ("rows64_tree", dict(B=3, Hq=8, Hkv=2, D=128, dtype="bf16", prefix=[1, 130, 700], tree="random", T=7,
+                         max_depth=4, shuffle_blocks=True)),
+    ("rows64_many_splits", dict(B=1, Hq=4, Hkv=1, D=128, dtype="bf16", prefix=[6000], tree="random", T=16,
+                                max_depth=5)),
+    ("rows256_tree", dict(B=1, Hq=16, Hkv=1, D=128, dtype="bf16", prefix=[900], tree="random", T=70,
+                          max_depth=8, shuffle_blocks=True)),
+    ("rows256_ragged", dict(B=2, Hq=32, Hkv=2, D=128, dtype="bf16", prefix=[5, 2222], tree="random", T=40,
+                            max_depth=6)),
+    ("single_node", dict(B=3, Hq=4, Hkv=2, D=128, dtype="bf16", prefix=[0, 1, 31], tree="fixed", parent=[-1])),
+    ("deep_chain_t256", dict(B=1, Hq=2, Hkv=1, D=128, dtype="bf16", prefix=[100], tree="chain", gamma=255)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_small_cases(name, kw):
+    w = make_workload(name=name, tag=400 + SMALL.index((name, kw)), V=8, **kw)
+    print(f"[attn] {name} B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} lens={w.prefix_lens.tolist()}", flush=True)
+    _run_full(w)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 3])
+def test_config_full(cfg):
+    w = make_config(cfg)
+    print(f"[attn] config {cfg} {w.name}", flush=True)
+    _run_full(w)
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_config_sampled_rows(cfg):
+    w = make_config(cfg)
+    print(f"[attn] config {cfg} {w.name} (sampled rows)", flush=True)
+    d = DevWorkload(w)
+    out = attn_to_f64(w, d.attn())
+    assert int(d.status.abs().sum()) == 0
+    rng = np.random.default_rng(cfg)
+    rows = [(int(rng.integers(w.B)), int(rng.integers(w.T)), int(rng.integers(w.Hq))) for _ in range(200)]
+    rows += [(w.B - 1, i, h) for i in range(w.T) for h in (0, w.Hq - 1)]  # every node of one sequence
+    ref = oracle.tree_attention_rows(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_lens, w.parent,
+                                     w.scale, rows, dtype=w.dtype)
+    got = np.stack([out[b, i, h] for b, i, h in rows])
+    assert_attn_close(got, ref, w.dtype, w.name)
+
+
+def test_bad_inputs_are_reported_not_faulted():
+    w = make_workload(tag=480, B=3, Hq=4, Hkv=4, D=128, dtype="bf16", V=8, prefix=[20, 40, 60], tree="random",
+                      T=6, max_depth=3)
+    d = DevWorkload(w)
+    d.parent[1, 3] = 5  # not topological
+    d.block_table[2, 0] = w.num_blocks + 7  # outside the pool
+    d.prefix_lens[0] = -4
+    d.attn()
+    st = d.status.cpu().numpy()
+    assert st[0] & 4 and st[1] & 1 and st[2] & 2
+
+
+def test_empty_batch_is_a_no_op():
+    w = make_workload(tag=481, B=1, Hq=2, Hkv=2, D=128, dtype="bf16", V=8, prefix=[4], tree="chain", gamma=2)
+    d = DevWorkload(w)
+    import tree_verify_attention_masked_amd as stv
+    out = stv.spec_tree_attn(d.q[:0], d.k, d.v, d.block_table[:0], d.prefix_lens[:0], d.parent[:0])
+    assert out.shape[0] == 0
+
+
+def test_block_permutation_invariance_on_gpu():
+    w = make_workload(tag=482, B=2, Hq=8, Hkv=2, D=128, dtype="bf16", V=8, prefix=[300, 45], tree="random",
+                      T=12, max_depth=4, extra_blocks=5)
+    d = DevWorkload(w)
+    a = d.attn().clone()
+    perm = torch.from_numpy(np.random.default_rng(1).permutation(w.num_blocks)).cuda()
+    inv = torch.argsort(perm).to(torch.int32)
+    d.k = d.k[perm].contiguous()
+    d.v = d.v[perm].contiguous()
+    d.block_table = inv[d.block_table.long()].contiguous()
+    b = d.attn()
+    assert torch.equal(a, b)  # same data in the same order: bit-identical

@@ -1,0 +1,113 @@
+"""GPU parity of spec_tree_reject against the oracle (C ABI).
+
+Accepted nodes, emitted tokens and L must be bit-identical to the oracle
+(same Philox stream) for every sequence, except from a draw the oracle flags
+as lying within 1e-6 of its decision threshold; such sequences only have to
+agree on the path decided before that draw, and are counted.
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import DevWorkload, compare_reject, oracle_reject
+from workloads import make_config, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _many_offsets(w, offsets, temperature=None, wr=None):
+    d = DevWorkload(w)
+    flagged = 0
+    for off in offsets:
+        got = d.reject(temperature=temperature, without_replacement=wr, offset=off)
+        torch.cuda.synchronize()
+        ref = oracle_reject(w, temperature=temperature, without_replacement=wr, offset=off)
+        flagged += compare_reject(got, ref)
+    assert int(d.status.abs().sum()) == 0
+    return flagged
+
+
+@pytest.mark.parametrize("V", [3, 5, 8])
+@pytest.mark.parametrize("wr", [False, True])
+def test_tiny_vocab_many_draws(V, wr):
+    # tiny vocabularies make rejections, sibling residuals and duplicate tokens frequent
+    w = make_workload(tag=500 + V, B=3, Hq=2, Hkv=2, D=64, dtype="f32", V=V, prefix=[4, 4, 4], tree="random",
+                      T=12, max_depth=3, draft_mode="without_replacement" if wr else "iid",
+                      temperature=0.8, without_replacement=wr, with_kv=True)
+    print(f"[reject] tiny V={V} wr={wr}", flush=True)
+    assert _many_offsets(w, range(60)) <= 3
+
+
+def test_greedy_tiny():
+    w = make_workload(tag=520, B=4, Hq=2, Hkv=2, D=64, dtype="f32", V=4, prefix=[4] * 4, tree="random", T=10,
+                      max_depth=4, temperature=0.0)
+    _many_offsets(w, [0])
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 3])
+def test_config_parity(cfg):
+    w = make_config(cfg)
+    print(f"[reject] config {cfg} {w.name}", flush=True)
+    flagged = _many_offsets(w, range(12))
+    assert flagged <= 1
+
+
+def test_config2_greedy_and_sampled():
+    w = make_config(2)
+    print("[reject] config 2 greedy + 0.7", flush=True)
+    _many_offsets(w, [0], temperature=0.0)
+    assert _many_offsets(w, range(3)) <= 1
+
+
+def test_config4_parity():
+    w = make_config(4, with_kv=False)
+    print("[reject] config 4", flush=True)
+    assert _many_offsets(w, range(2)) <= 1
+
+
+def test_worked_example_on_gpu():
+    # the SGLang doc's prefix match: drafts "and it's so hot", target "and it's very warm"
+    V = 8
+    w = make_workload(tag=530, B=1, Hq=2, Hkv=2, D=64, dtype="f32", V=V, prefix=[3], tree="chain", gamma=4,
+                      temperature=0.0)
+    w.draft_tokens[0] = [0, 1, 2, 3, 4]
+    logits = np.random.default_rng(0).standard_normal((1, 5, V)).astype(np.float32)
+    for u, t in enumerate([1, 2, 5, 6, 7]):
+        logits[0, u, t] = logits[0, u].max() + 1
+    w.target_logits = logits
+    d = DevWorkload(w)
+    acc, toks, nacc = (t.cpu().numpy() for t in d.reject())
+    assert nacc[0] == 2 and acc[0].tolist() == [0, 1, 2, -1, -1] and toks[0].tolist() == [1, 2, 5, -1, -1]
+
+
+def test_device_errors_reported():
+    w = make_workload(tag=540, B=3, Hq=2, Hkv=2, D=64, dtype="f32", V=16, prefix=[4] * 3, tree="random", T=6,
+                      max_depth=3, temperature=1.0)
+    d = DevWorkload(w)
+    d.parent[0, 2] = 4
+    d.tokens[1, 3] = 99
+    d.logits[2, 0, 5] = float("nan")
+    acc, toks, nacc = d.reject()
+    st = d.status.cpu().numpy()
+    assert st[0] & 1 and st[1] & 8 and st[2] & 16
+    assert (nacc.cpu().numpy() == 0).all() and (toks.cpu().numpy() == -1).all()
+
+
+def test_statistics_single_child_acceptance_rate():
+    # P(accept) of one child equals sum_x min(p(x), q(x)); draws indexed by offset
+    V, n = 6, 4000
+    w = make_workload(tag=550, B=1, Hq=2, Hkv=2, D=64, dtype="f32", V=V, prefix=[2], tree="chain", gamma=1,
+                      temperature=1.0)
+    d = DevWorkload(w)
+    rng = np.random.default_rng(3)
+    q = w.draft_probs[0, 0].astype(np.float64)
+    p = np.exp(w.target_logits[0, 0].astype(np.float64) - w.target_logits[0, 0].max())
+    p /= p.sum()
+    beta = np.minimum(p, q / q.sum()).sum()
+    acc = 0
+    toks = rng.choice(V, size=n, p=q / q.sum())
+    for off in range(n):
+        d.tokens[0, 1] = int(toks[off])
+        _, _, nacc = d.reject(offset=off)
+        acc += int(nacc.item())
+    assert abs(acc / n - beta) < 4 * np.sqrt(beta * (1 - beta) / n)

@@ -1,0 +1,28 @@
+"""MI355X-native tree verification for speculative decoding.
+
+The hot path of verifying a flattened draft tree in one target pass, as three
+calls into libspectree (hand-written HIP for gfx950, C ABI in
+include/spectree.h):
+
+  spec_tree_attn    tree-masked verify attention over a paged KV prefix
+  spec_tree_reject  tree rejection sampling (greedy / with / without replacement)
+  spec_kv_compact   keep only the accepted path in the KV cache
+
+This package is the thin PyTorch binding: tensors in, device pointers and the
+current HIP stream out to the library.
+"""
+from .binding import (  # noqa: F401
+    DEV_ERRORS,
+    LIB_PATH,
+    SPEC_BF16,
+    SPEC_F32,
+    SpecError,
+    header_functions,
+    load_library,
+    spec_kv_compact,
+    spec_status_string,
+    spec_tree_attn,
+    spec_tree_attn_workspace_size,
+    spec_tree_reject,
+    spec_version,
+)

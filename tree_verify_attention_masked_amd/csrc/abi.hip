@@ -1,0 +1,163 @@
+// extern "C" entry points of libspectree: host-side validation, planning and
+// launches on the caller's stream.  No call allocates, synchronises or copies
+// to the host.
+#include <cmath>
+
+#include "common.h"
+
+using namespace spectree;
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool dtype_ok(int dtype, int D) {
+  if (dtype == SPEC_BF16) return D == 128;
+  if (dtype == SPEC_F32) return D == 64 || D == 128;
+  return false;
+}
+
+// Shape checks shared by attention and compaction.  Returns SPEC_OK or an error.
+int check_kv_shapes(int B, int T, int Hkv, int D, int block_size, int max_blocks, int num_blocks, int dtype) {
+  if (B < 0 || T < 1 || Hkv < 1 || D < 1 || max_blocks < 1 || num_blocks < 1) return SPEC_ERR_INVALID_ARG;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_INVALID_ARG;
+  if (block_size != kBlockSize || T > kMaxT || !dtype_ok(dtype, D)) return SPEC_ERR_UNSUPPORTED;
+  if (static_cast<long>(max_blocks) * kBlockSize < T) return SPEC_ERR_INVALID_ARG;
+  if (static_cast<long>(max_blocks) * kBlockSize > (1L << 30)) return SPEC_ERR_UNSUPPORTED;
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_status_string(int status) {
+  switch (status) {
+    case SPEC_OK:
+      return "SPEC_OK";
+    case SPEC_ERR_INVALID_ARG:
+      return "SPEC_ERR_INVALID_ARG: null pointer or inconsistent size";
+    case SPEC_ERR_UNSUPPORTED:
+      return "SPEC_ERR_UNSUPPORTED: dtype, head dim, block size or tree size not supported";
+    case SPEC_ERR_WORKSPACE:
+      return "SPEC_ERR_WORKSPACE: workspace missing or too small";
+    case SPEC_ERR_HIP:
+      return "SPEC_ERR_HIP: HIP launch failed";
+    default:
+      return "unknown spec_status";
+  }
+}
+
+int spec_version(void) { return kVersion; }
+
+size_t spec_tree_attn_workspace_size(int B, int T, int Hq, int Hkv, int D, int max_blocks_per_seq, int dtype) {
+  if (B <= 0 || T < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || max_blocks_per_seq < 1 || !dtype_ok(dtype, D))
+    return 0;
+  return plan_attn(B, T, Hq, Hkv, D, max_blocks_per_seq, dtype).ws_bytes;
+}
+
+int spec_tree_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                   const int32_t* prefix_lens, const int32_t* parent, void* out, int B, int T, int Hq, int Hkv,
+                   int D, int block_size, int max_blocks_per_seq, int num_blocks, float scale, int dtype,
+                   int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_kv_shapes(B, T, Hkv, D, block_size, max_blocks_per_seq, num_blocks, dtype);
+  if (rc != SPEC_OK) return rc;
+  if (Hq < Hkv || Hq % Hkv != 0) return SPEC_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return SPEC_ERR_INVALID_ARG;
+  if (B == 0) return SPEC_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !prefix_lens || !parent || !out) return SPEC_ERR_INVALID_ARG;
+  const AttnPlan plan = plan_attn(B, T, Hq, Hkv, D, max_blocks_per_seq, dtype);
+  if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes)) return SPEC_ERR_WORKSPACE;
+  AttnLaunch L{};
+  L.q = q;
+  L.k = k_cache;
+  L.v = v_cache;
+  L.block_table = block_table;
+  L.prefix_lens = prefix_lens;
+  L.parent = parent;
+  L.out = out;
+  L.status = status;
+  L.workspace = workspace;
+  L.B = B;
+  L.T = T;
+  L.Hq = Hq;
+  L.Hkv = Hkv;
+  L.D = D;
+  L.max_blocks = max_blocks_per_seq;
+  L.num_blocks = num_blocks;
+  L.scale = scale;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = (dtype == SPEC_BF16) ? launch_attn_bf16(plan, L, s) : launch_attn_f32(plan, L, s);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+size_t spec_tree_reject_workspace_size(int B, int T, int V) {
+  if (B <= 0 || T < 1 || V < 1) return 0;
+  return reject_workspace_bytes(B, T, V);
+}
+
+int spec_tree_reject(const float* target_logits, const float* draft_probs, const int32_t* draft_tokens,
+                     const int32_t* parent, int B, int T, int V, float temperature, int without_replacement,
+                     uint64_t seed, uint64_t offset, int32_t* accepted_nodes, int32_t* out_tokens,
+                     int32_t* num_accepted, int32_t* status, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (B < 0 || T < 1 || V < 1) return SPEC_ERR_INVALID_ARG;
+  if (T > kMaxT || V > kMaxV) return SPEC_ERR_UNSUPPORTED;
+  if (!(temperature >= 0.0f) || !std::isfinite(temperature)) return SPEC_ERR_INVALID_ARG;
+  if (B == 0) return SPEC_OK;
+  if (!target_logits || !draft_tokens || !parent || !accepted_nodes || !out_tokens || !num_accepted)
+    return SPEC_ERR_INVALID_ARG;
+  if (temperature > 0.0f && !draft_probs) return SPEC_ERR_INVALID_ARG;
+  const size_t need = reject_workspace_bytes(B, T, V);
+  if (workspace == nullptr || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
+  RejectLaunch L{};
+  L.logits = target_logits;
+  L.q = draft_probs;
+  L.tokens = draft_tokens;
+  L.parent = parent;
+  L.B = B;
+  L.T = T;
+  L.V = V;
+  L.temperature = temperature;
+  L.without_replacement = without_replacement;
+  L.seed = seed;
+  L.offset = offset;
+  L.accepted = accepted_nodes;
+  L.out_tokens = out_tokens;
+  L.num_accepted = num_accepted;
+  L.status = status;
+  L.workspace = workspace;
+  const hipError_t e = launch_reject(L, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+int spec_kv_compact(void* k_cache, void* v_cache, const int32_t* block_table, const int32_t* prefix_lens,
+                    const int32_t* accepted_nodes, const int32_t* num_accepted, int32_t* new_lens, int B, int T,
+                    int Hkv, int D, int block_size, int max_blocks_per_seq, int num_blocks, int dtype,
+                    int32_t* status, void* stream) {
+  int rc = check_kv_shapes(B, T, Hkv, D, block_size, max_blocks_per_seq, num_blocks, dtype);
+  if (rc != SPEC_OK) return rc;
+  if (B == 0) return SPEC_OK;
+  if (!k_cache || !v_cache || !block_table || !prefix_lens || !accepted_nodes || !num_accepted)
+    return SPEC_ERR_INVALID_ARG;
+  CompactLaunch L{};
+  L.k = k_cache;
+  L.v = v_cache;
+  L.block_table = block_table;
+  L.prefix_lens = prefix_lens;
+  L.accepted = accepted_nodes;
+  L.num_accepted = num_accepted;
+  L.new_lens = new_lens;
+  L.status = status;
+  L.B = B;
+  L.T = T;
+  L.Hkv = Hkv;
+  L.D = D;
+  L.max_blocks = max_blocks_per_seq;
+  L.num_blocks = num_blocks;
+  L.elem_bytes = dtype == SPEC_BF16 ? 2 : 4;
+  const hipError_t e = launch_compact(L, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+}  // extern "C"

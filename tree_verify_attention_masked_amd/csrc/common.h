@@ -1,0 +1,105 @@
+// Internal helpers shared by the HIP kernels of libspectree (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "spectree.h"
+
+namespace spectree {
+
+constexpr int kBlockSize = 16;
+constexpr int kMaxT = 256;          // ancestor bitsets hold 4 x 64 bits
+constexpr int kMaxV = 262144;       // rejected-token bitmap of the sampler lives in LDS
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// float -> bfloat16 bits, round to nearest even, NaN kept quiet.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ void report(int32_t* status, int b, int32_t bits) {
+  if (status != nullptr && bits != 0) atomicOr(status + b, bits);
+}
+
+// ---------------------------------------------------------------------------
+// launch wrappers implemented in the kernel translation units
+// ---------------------------------------------------------------------------
+
+struct AttnPlan {
+  int mode;       // 0: fp32 VALU kernel, 1: bf16 key-split (<=16 rows), 2: bf16 row-split
+  int rows;       // R = T * G query rows per (sequence, kv head)
+  int rt;         // rows per workgroup
+  int nrb;        // 16-row blocks per wave
+  int n_rt;       // row tiles per (sequence, kv head)
+  int splits;     // KV splits per (sequence, kv head)
+  int pps;        // pages per split
+  long items;     // workgroups of the main kernel (before XCD padding)
+  size_t ws_bytes;
+};
+
+AttnPlan plan_attn(int B, int T, int Hq, int Hkv, int D, int max_blocks, int dtype);
+
+struct AttnLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  const int32_t* prefix_lens;
+  const int32_t* parent;
+  void* out;
+  int32_t* status;
+  void* workspace;
+  int B, T, Hq, Hkv, D, max_blocks, num_blocks;
+  float scale;
+};
+
+hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& a, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnPlan& plan, const AttnLaunch& a, hipStream_t stream);
+
+struct RejectLaunch {
+  const float* logits;
+  const float* q;
+  const int32_t* tokens;
+  const int32_t* parent;
+  int B, T, V;
+  float temperature;
+  int without_replacement;
+  uint64_t seed, offset;
+  int32_t* accepted;
+  int32_t* out_tokens;
+  int32_t* num_accepted;
+  int32_t* status;
+  void* workspace;
+};
+
+size_t reject_workspace_bytes(int B, int T, int V);
+hipError_t launch_reject(const RejectLaunch& a, hipStream_t stream);
+
+struct CompactLaunch {
+  void* k;
+  void* v;
+  const int32_t* block_table;
+  const int32_t* prefix_lens;
+  const int32_t* accepted;
+  const int32_t* num_accepted;
+  int32_t* new_lens;
+  int32_t* status;
+  int B, T, Hkv, D, max_blocks, num_blocks, elem_bytes;
+};
+
+hipError_t launch_compact(const CompactLaunch& a, hipStream_t stream);
+
+}  // namespace spectree
