@@ -83,6 +83,17 @@ def _final_margin(weights, u, x):
     return min(u - lo, c[x] / c[-1] - u)
 
 
+def final_draw_candidates(weights, u, margin=None):
+    """Tokens whose normalised CDF interval [C[x-1], C[x]) / C[V-1] lies within
+    `margin` of u (nonzero weight only): the tokens a draw flagged at that
+    margin may legitimately return."""
+    margin = FLAG_MARGIN if margin is None else margin
+    w = np.asarray(weights, dtype=np.float64)
+    c = np.cumsum(w) / w.sum()
+    lo = np.concatenate([[0.0], c[:-1]])
+    return np.nonzero((w > 0) & (lo < u + margin) & (c > u - margin))[0]
+
+
 class PhiloxDraws:
     """The real source of randomness: Philox4x32-10 uniforms, with margins recorded."""
 
@@ -91,6 +102,7 @@ class PhiloxDraws:
         self.offset = int(offset)
         self.records = []  # (kind, b, node, margin, path_len)
         self.path_len = 0
+        self.final_candidates = None  # set when the final draw is flagged
 
     def accept(self, b, node, p_x, q_x) -> bool:
         r = uniform_draw(self.seed, self.offset, b, node, PURPOSE_ACCEPT)
@@ -101,7 +113,10 @@ class PhiloxDraws:
     def sample(self, b, node, weights) -> int:
         u = uniform_draw(self.seed, self.offset, b, node, PURPOSE_FINAL)
         x = inverse_cdf(weights, u)
-        self.records.append(("final", b, node, _final_margin(weights, u, x), self.path_len))
+        m = _final_margin(weights, u, x)
+        self.records.append(("final", b, node, m, self.path_len))
+        if m < FLAG_MARGIN:
+            self.final_candidates = final_draw_candidates(weights, u)
         return x
 
 
@@ -154,13 +169,17 @@ def tree_reject(target_logits, draft_probs, draft_tokens, parent, temperature,
     entries -1), num_accepted [B] (= L, the number of accepted draft nodes),
     and `flag_path_len` [B]: -1 if no draw of the sequence came within
     FLAG_MARGIN of its threshold, else the path length when the first such
-    draw was taken (outputs beyond that point are not decided robustly)."""
+    draw was taken (outputs beyond that point are not decided robustly);
+    `flag_kind` [B]: "" / "accept" / "final" for that first flagged draw, and
+    `final_candidates`: {b: tokens a flagged final draw may return}."""
     B, T, V = target_logits.shape
     tau = float(np.float32(temperature))
     acc = np.full((B, T), -1, dtype=np.int32)
     out = np.full((B, T), -1, dtype=np.int32)
     nacc = np.zeros(B, dtype=np.int32)
     flag = np.full(B, -1, dtype=np.int32)
+    kind_of = [""] * B
+    cands = {}
     margins = []
     for b in range(B):
         draws = PhiloxDraws(seed, offset)
@@ -175,5 +194,9 @@ def tree_reject(target_logits, draft_probs, draft_tokens, parent, temperature,
             margins.append(m)
             if m < FLAG_MARGIN and flag[b] < 0:
                 flag[b] = plen
+                kind_of[b] = kind
+        if kind_of[b] == "final":
+            cands[b] = draws.final_candidates
     return {"accepted_nodes": acc, "out_tokens": out, "num_accepted": nacc,
-            "flag_path_len": flag, "margins": np.array(margins)}
+            "flag_path_len": flag, "flag_kind": kind_of, "final_candidates": cands,
+            "margins": np.array(margins)}

@@ -80,16 +80,31 @@ def attn_to_f64(w, out):
     return t.astype(np.float64)
 
 
-def compare_reject(got, ref):
-    """Bit-exact comparison of the walk outputs, except after a flagged draw.
-    Returns the number of sequences with a flagged draw."""
+def compare_reject(got, ref, stats=None):
+    """Bit-exact comparison of the walk outputs with the oracle's.
+
+    A sequence none of whose draws the oracle flags (within 1e-6 of its
+    threshold) must match exactly.  If the first flagged draw is the final
+    one, the path, L and accepted tokens must still match exactly and the
+    emitted token must be one of the tokens whose CDF interval lies within
+    1e-6 of the uniform.  If an accept test is flagged, the path decided
+    before it must match.  Returns the number of flagged sequences."""
     acc, toks, nacc = (t.cpu().numpy() for t in got)
     flagged = 0
     for b in range(acc.shape[0]):
         fl = int(ref["flag_path_len"][b])
+        kind = ref["flag_kind"][b] if "flag_kind" in ref else ""
         if fl >= 0:
             flagged += 1
             assert (acc[b, :fl] == ref["accepted_nodes"][b, :fl]).all(), f"seq {b}: path differs before a flagged draw"
+            if kind == "final":
+                L = int(ref["num_accepted"][b])
+                assert nacc[b] == L and (acc[b] == ref["accepted_nodes"][b]).all(), f"seq {b}: path"
+                assert (toks[b, :L] == ref["out_tokens"][b, :L]).all(), f"seq {b}: accepted tokens"
+                assert toks[b, L] in set(int(x) for x in ref["final_candidates"][b]), \
+                    f"seq {b}: emitted {toks[b, L]} not among {ref['final_candidates'][b]}"
+                if stats is not None:
+                    stats["final_flag_same"] = stats.get("final_flag_same", 0) + int(toks[b, L] == ref["out_tokens"][b, L])
             continue
         assert nacc[b] == ref["num_accepted"][b], f"seq {b}: L {nacc[b]} vs {ref['num_accepted'][b]}"
         assert (acc[b] == ref["accepted_nodes"][b]).all(), f"seq {b}: accepted {acc[b]} vs {ref['accepted_nodes'][b]}"

@@ -416,3 +416,11 @@ def test_tree_reject_output_format_and_flags():
     assert res["out_tokens"][0, :L].tolist() == [int(w.draft_tokens[0][n]) for n in acc[1:L + 1]]
     assert 0 <= res["out_tokens"][0, L] < w.V
     assert res["flag_path_len"][0] == -1  # no draw of this seed sits within 1e-6 of a threshold
+
+
+def test_final_draw_candidates_bracket_the_draw():
+    from oracle.reject import final_draw_candidates
+    w = np.array([0.25, 0.0, 0.25, 0.5])
+    assert final_draw_candidates(w, 0.5 + 1e-7).tolist() == [2, 3]  # at the boundary between 2 and 3
+    assert final_draw_candidates(w, 0.7).tolist() == [3]
+    assert final_draw_candidates(w, 0.25 - 5e-7).tolist() == [0, 2]  # token 1 has no weight
