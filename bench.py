@@ -150,9 +150,9 @@ def main():
         copies.append(c)
     code = stv.SPEC_BF16 if w.dtype == "bf16" else stv.SPEC_F32
     ws_attn = stv.spec_tree_attn_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, w.max_blocks, code)
-    attn_ws = torch.empty(max(ws_attn, 1), dtype=torch.uint8, device=dev)
-    rej_ws = torch.empty(int(stv.load_library().spec_tree_reject_workspace_size(w.B, w.T, w.V)),
-                         dtype=torch.uint8, device=dev)
+    attn_ws = torch.zeros(max(ws_attn, 1), dtype=torch.uint8, device=dev)  # zero once: split arrival counters
+    rej_ws = torch.zeros(int(stv.load_library().spec_tree_reject_workspace_size(w.B, w.T, w.V)),
+                         dtype=torch.uint8, device=dev)  # zero once: the sampler's barrier counters
 
     def attn(c):
         stv.spec_tree_attn(c["q"], c["k"], c["v"], shared["bt"], shared["lens"], shared["parent"], scale=w.scale,

@@ -63,7 +63,9 @@ enum {
   SPEC_DEV_TOKEN = 8,      /* a draft token outside [0, V) */
   SPEC_DEV_NONFINITE = 16, /* NaN/Inf in a target-logit row or a draft probability that was read */
   SPEC_DEV_EMPTY = 32,     /* a distribution with zero total mass had to be sampled */
-  SPEC_DEV_PATH = 64       /* accepted path not of the form 0 = n_0 < n_1 < ... < n_L < T */
+  SPEC_DEV_PATH = 64,      /* accepted path not of the form 0 = n_0 < n_1 < ... < n_L < T */
+  SPEC_DEV_TIMEOUT = 128   /* the workgroups sampling one sequence did not all run at once
+                              (bounded wait expired); outputs of that sequence are undefined */
 };
 
 /* Human-readable name of a spec_status value. */
@@ -96,8 +98,12 @@ int spec_version(void);
  *                affected sequence are still written, from the subset of keys
  *                that could be read safely
  *   workspace    device scratch of at least spec_tree_attn_workspace_size(...)
- *                bytes (may be NULL when that size is 0); its contents need no
- *                initialisation and are not meaningful after the call
+ *                bytes (may be NULL when that size is 0).  When the KV range
+ *                is split over several workgroups, the first bytes hold one
+ *                arrival counter per (sequence, kv head): they must be zero
+ *                before the first call, and every call that completes leaves
+ *                them zero (zero-fill a workspace once, then reuse it).  Calls
+ *                that overlap in time must not share a workspace.
  * Supported: dtype SPEC_BF16 with D = 128, dtype SPEC_F32 with D in {64, 128};
  * block_size = 16; 1 <= T <= 256; Hq % Hkv == 0.  B == 0 is a no-op.
  * ---------------------------------------------------------------------- */
@@ -145,8 +151,16 @@ int spec_tree_attn(const void* q, const void* k_cache, const void* v_cache,
  *   num_accepted  [B] int32 out: L
  *   status        [B] int32 or NULL; on a device-detected error the sequence
  *                 gets L = 0, accepted_nodes = [0, -1, ...], out_tokens all -1
- *   workspace     >= spec_tree_reject_workspace_size(B, T, V) bytes; contents
- *                 need no initialisation
+ *   workspace     >= spec_tree_reject_workspace_size(B, T, V) bytes.  Its first
+ *                 64 * B bytes hold barrier counters and must be zero before
+ *                 the first call; every call that completes leaves them zero,
+ *                 so a workspace is zero-filled once and then reused.  Calls
+ *                 that overlap in time must not share a workspace.
+ * Execution: each sequence is sampled by up to 32 cooperating workgroups that
+ * exchange partial sums through the workspace; the grid (B x team size, at
+ * most 256 workgroups unless B > 256) must be able to run at once, which holds
+ * on an otherwise idle MI355X.  If it cannot, the waits are bounded and the
+ * sequence reports SPEC_DEV_TIMEOUT.
  * Supported: 1 <= T <= 256, 1 <= V <= 262144, temperature >= 0 and finite.
  * ---------------------------------------------------------------------- */
 size_t spec_tree_reject_workspace_size(int B, int T, int V);

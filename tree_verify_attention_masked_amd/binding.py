@@ -25,7 +25,8 @@ SPEC_ERR_HIP = -4
 SPEC_F32 = 0
 SPEC_BF16 = 1
 
-DEV_ERRORS = {1: "parent", 2: "block", 4: "length", 8: "token", 16: "nonfinite", 32: "empty", 64: "path"}
+DEV_ERRORS = {1: "parent", 2: "block", 4: "length", 8: "token", 16: "nonfinite", 32: "empty", 64: "path",
+              128: "timeout"}
 
 _c_i32p = ctypes.c_void_p
 _vp = ctypes.c_void_p
@@ -142,8 +143,8 @@ def spec_tree_attn(q, k_cache, v_cache, block_table, prefix_lens, parent, scale=
     if status is not None:
         _need(status, "status", torch.int32, 1)
     ws = int(lib.spec_tree_attn_workspace_size(B, T, Hq, Hkv, D, mb, code))
-    if workspace is None and ws > 0:
-        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    if workspace is None and ws > 0:  # zero-filled: its header holds split arrival counters
+        workspace = torch.zeros(ws, dtype=torch.uint8, device=q.device)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib.spec_tree_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(prefix_lens),
                             _ptr(parent), _ptr(out), B, T, Hq, Hkv, D, bs, mb, nb, float(scale), code,
@@ -177,8 +178,8 @@ def spec_tree_reject(target_logits, draft_probs, draft_tokens, parent, temperatu
     if status is not None:
         _need(status, "status", torch.int32, 1)
     ws = int(lib.spec_tree_reject_workspace_size(B, T, V))
-    if workspace is None and ws > 0:
-        workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    if workspace is None and ws > 0:  # zero-filled: its header holds the team barrier counters
+        workspace = torch.zeros(ws, dtype=torch.uint8, device=dev)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib.spec_tree_reject(_ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(parent),
                               B, T, V, float(temperature), int(bool(without_replacement)),

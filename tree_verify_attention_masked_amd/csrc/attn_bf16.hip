@@ -1,4 +1,7 @@
-// Tree-masked verify attention, bf16 inputs, head dim 128, gfx950 matrix cores.
+// Tree-masked verify attention, bf16 inputs, head dim 128, gfx950 matrix cores:
+// planning for every bf16 shape, and the kernel for many query rows per kv head
+// (> 64: wide trees times GQA groups).  Shapes with <= 64 rows use the
+// streaming kernel (attn_stream.hip).
 //
 // Work item = (sequence b, kv head g, KV split s, row tile rt).  The query rows
 // of one (b, g) are the T tree nodes times the G query heads of the group
@@ -9,14 +12,15 @@
 // bitset of the row's node (the tree_mask of the EAGLE implementation summary
 // in "Report: Support nextn speculative decoding").
 //
-// Matrix-core mapping (v_mfma_f32_16x16x32_bf16, one 64-lane wave):
-//   S^T[key, row] = K[key, :] . Q[row, :]     A = K from LDS, B = Q in registers
-//   O^T[d, row]  += V^T[d, key] . P^T[key, row]
-// With S^T as the accumulator every lane holds 8 scores of ONE row, which is
-// exactly the B operand the PV product needs, so P never leaves registers; the
-// key order inside the 32-wide contraction is permuted identically in V^T.
-// V is staged transposed in LDS.  Online softmax runs in the log2 domain.
-// Splits write unnormalised partials (O, m, l) that a second kernel merges.
+// A workgroup holds 4 waves x NRB blocks of 16 rows.  Per iteration the
+// workgroup stages a 64-key tile (4 pages) in LDS -- K in its natural layout,
+// V transposed with the keys of each 32-key half paired as (k, k+16) -- while
+// the next tile's loads are in flight in registers.  Each wave computes, per
+// 32-key half and row block, S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (8
+// scores of one row per lane), the online softmax in the log2 domain, and
+// O^T += V^T P^T with P packed in the (k, k+16) order.  Splits write
+// unnormalised partials (O, m, l); the last workgroup of a (b, g, rt) to finish
+// merges them (arrival counter in the workspace, reset by that workgroup).
 #include <algorithm>
 
 #include "common.h"
@@ -26,8 +30,12 @@ namespace {
 
 constexpr int kD = 128;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kTile = 64;             // keys per iteration (4 pages)
+constexpr int kKS = kD + 8;           // LDS row stride of K (bf16), 272 B
+constexpr int kVS = kTile + 8;        // LDS row stride of V^T (bf16 slots), 144 B
+constexpr int kMaxSplitPages = 1024;  // pages per split (planning keeps below)
 
-struct BArgs {
+struct TArgs2 {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
@@ -36,20 +44,17 @@ struct BArgs {
   const int32_t* parent;
   uint16_t* out;
   int32_t* status;
-  float* part_o;   // [items, RT, D]
-  float* part_ml;  // [items, RT, 2]
+  float* part_o;       // [items][RT][D]
+  float* part_ml;      // [items][RT][2]
+  unsigned* counters;  // [B * Hkv * n_rt]
   int B, T, Hq, Hkv, G, R, n_rt, splits, pps, max_blocks, num_blocks;
   long items;
-  float sl2;  // scale * log2(e)
+  float sl2;
 };
 
-__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
-// Ancestor-or-self bitsets of all T nodes of sequence b into LDS (4 x 64 bits
-// per node).  A node whose parent chain is not topological keeps only itself.
-__device__ int build_ancestors(const int32_t* parent_b, int T, uint64_t* anc) {
+// Ancestor-or-self bitsets (4 x 64 bits per node) from the LDS copy of a parent
+// row.  A node whose parent chain is not topological keeps only itself.
+__device__ int build_ancestors_lds(const int* par, int T, uint64_t* anc) {
   int err = 0;
   for (int i = threadIdx.x; i < T; i += blockDim.x) {
     uint64_t w[4] = {0, 0, 0, 0};
@@ -57,7 +62,7 @@ __device__ int build_ancestors(const int32_t* parent_b, int T, uint64_t* anc) {
     bool ok = true;
     for (int steps = 0; steps <= T; ++steps) {
       w[j >> 6] |= 1ull << (j & 63);
-      const int p = parent_b[j];
+      const int p = par[j];
       if (j == 0) {
         ok = (p == -1);
         break;
@@ -78,23 +83,19 @@ __device__ int build_ancestors(const int32_t* parent_b, int T, uint64_t* anc) {
   return err;
 }
 
-template <int WR, int WK, int NRB>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(const BArgs a) {
-  constexpr int TILE = 32 * WK;      // keys staged per iteration
-  constexpr int PAGES = TILE / 16;   // pages per iteration
-  constexpr int RT = 16 * NRB * WR;  // query rows per workgroup
-  constexpr int KSTR = kD + 8;       // LDS row stride of K (elements)
-  constexpr int VSTR = TILE + 8;     // LDS row stride of V^T (elements)
-  static_assert(WR * WK == 4, "four waves per workgroup");
-  static_assert(WK == 1 || NRB == 1, "key-split workgroups hold one row block");
-
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[TILE * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * VSTR];
+template <int NRB>
+__global__ __launch_bounds__(256) void attn_tile_kernel(const TArgs2 a) {
+  constexpr int RT = 64 * NRB;  // rows per workgroup
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * kKS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * kVS];
   __shared__ uint64_t anc[kMaxT * 4];
+  __shared__ int s_par[kMaxT];
+  __shared__ int s_blk[kMaxSplitPages];
+  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int quad = lane >> 4;
 
@@ -109,6 +110,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const BArgs a) {
   rest /= a.splits;
   const int g = static_cast<int>(rest % a.Hkv);
   const int b = static_cast<int>(rest / a.Hkv);
+  const long bgr = (static_cast<long>(b) * a.Hkv + g) * a.n_rt + rt;
 
   int err = 0;
   int Lb = a.plen[b];
@@ -121,13 +123,25 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const BArgs a) {
   const int npages = (n_keys + kBlockSize - 1) / kBlockSize;
   const int p0 = s * a.pps;
   const int p1 = min(npages, p0 + a.pps);
-  const int n_it = p1 > p0 ? (p1 - p0 + PAGES - 1) / PAGES : 0;
-  const int kend = min(n_keys, p1 * kBlockSize);  // keys past the split belong to the next one
+  const int kend = min(n_keys, p1 * kBlockSize);
+  const int n_it = p1 > p0 ? (p1 - p0 + 3) / 4 : 0;
+  const bool tail = n_it > 0 && kend > Lb;
 
-  if (n_it > 0 && p1 * kBlockSize > Lb) err |= build_ancestors(a.parent + static_cast<long>(b) * a.T, a.T, anc);
+  // the split's block indices and the parent row, staged once in LDS
+  const int32_t* bt_b = a.bt + static_cast<long>(b) * a.max_blocks;
+  for (int i = tid; i < p1 - p0; i += 256) {
+    const int blk = bt_b[p0 + i];
+    const bool ok = blk >= 0 && blk < a.num_blocks;
+    if (!ok) err |= SPEC_DEV_BLOCK;
+    s_blk[i] = ok ? blk : -1;
+  }
+  if (tail)
+    for (int i = tid; i < a.T; i += 256) s_par[i] = a.parent[static_cast<long>(b) * a.T + i];
+  __syncthreads();
+  if (tail) err |= build_ancestors_lds(s_par, a.T, anc);
 
   // query fragments (B operand of S^T): Q[row][c*32 + quad*8 .. +7]
-  const int row_base = rt * RT + (WR == 1 ? 0 : wave * NRB * 16);
+  const int row_base = rt * RT + wave * NRB * 16;
   bf16x8 qf[NRB][4];
   int node_of[NRB];
 #pragma unroll
@@ -138,7 +152,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const BArgs a) {
       const int node = r / a.G, hh = r % a.G;
       const uint16_t* qp = a.q + ((static_cast<long>(b) * a.T + node) * a.Hq + g * a.G + hh) * kD + quad * 8;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qf[rb][c] = ld_bf16x8(qp + c * 32);
+      for (int c = 0; c < 4; ++c) qf[rb][c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + c * 32));
     } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c) qf[rb][c] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
@@ -155,117 +169,120 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const BArgs a) {
     for (int dt = 0; dt < 8; ++dt) o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Each thread moves one 16-byte chunk per page and tensor: key kin, dims d0..d0+7.
+  // Staging: thread (key kin = tid/16, dims d0 = (tid%16)*8) moves, for each
+  // 32-key half st and 16-key quarter h, one 16-byte chunk of K and of V.
+  // Loads are unconditional (pages past the split re-read its last page);
+  // validity is a flag applied when the chunk is written to LDS.
   const int kin = tid >> 4;
   const int d0 = (tid & 15) * 8;
-  u32x4 kr[PAGES], vr[PAGES];
-  const int32_t* bt_b = a.bt + static_cast<long>(b) * a.max_blocks;
+  u32x4 kr[2][2], vr[2][2];
+  bool okr[2][2];
   auto load_tile = [&](int it) {
 #pragma unroll
-    for (int n = 0; n < PAGES; ++n) {
-      const int page = p0 + it * PAGES + n;
-      const int pos = page * kBlockSize + kin;
-      kr[n] = u32x4{0, 0, 0, 0};
-      vr[n] = u32x4{0, 0, 0, 0};
-      if (page < p1 && pos < n_keys) {
-        const int blk = bt_b[page];
-        if (blk < 0 || blk >= a.num_blocks) {
-          err |= SPEC_DEV_BLOCK;
-        } else {
-          const long off = ((static_cast<long>(blk) * a.Hkv + g) * kBlockSize + kin) * kD + d0;
-          kr[n] = *reinterpret_cast<const u32x4*>(a.k + off);
-          vr[n] = *reinterpret_cast<const u32x4*>(a.v + off);
-        }
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int pg = p0 + 4 * it + 2 * st + h;
+        const int page = min(pg, max(p1 - 1, p0));
+        const int blk = p1 > p0 ? s_blk[page - p0] : -1;
+        okr[st][h] = (pg * kBlockSize + kin < kend) && blk >= 0;
+        const long off = ((static_cast<long>(max(blk, 0)) * a.Hkv + g) * kBlockSize + kin) * kD + d0;
+        kr[st][h] = *reinterpret_cast<const u32x4*>(a.k + off);
+        vr[st][h] = *reinterpret_cast<const u32x4*>(a.v + off);
       }
-    }
   };
-
+  __syncthreads();  // s_blk and anc are ready
   if (n_it > 0) load_tile(0);
-  const int koff = (WK == 1) ? 0 : wave * 32;
+
   for (int it = 0; it < n_it; ++it) {
-    __syncthreads();
+    __syncthreads();  // the previous tile is no longer read
 #pragma unroll
-    for (int n = 0; n < PAGES; ++n) {
-      *reinterpret_cast<u32x4*>(&Ks[(n * 16 + kin) * KSTR + d0]) = kr[n];
-      const int col = n * 16 + kin;
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Vt[(d0 + 2 * j) * VSTR + col] = static_cast<uint16_t>(vr[n][j] & 0xffffu);
-        Vt[(d0 + 2 * j + 1) * VSTR + col] = static_cast<uint16_t>(vr[n][j] >> 16);
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<u32x4*>(&Ks[(st * 32 + h * 16 + kin) * kKS + d0]) =
+            okr[st][h] ? kr[st][h] : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const uint32_t a0 = okr[st][0] ? vr[st][0][e2] : 0u, a1 = okr[st][1] ? vr[st][1][e2] : 0u;
+        const uint32_t lo = (a0 & 0xffffu) | (a1 << 16);
+        const uint32_t hi = (a0 >> 16) | (a1 & 0xffff0000u);
+        const int d = d0 + 2 * e2;
+        *reinterpret_cast<uint32_t*>(&Vt[d * kVS + st * 32 + 2 * kin]) = lo;
+        *reinterpret_cast<uint32_t*>(&Vt[(d + 1) * kVS + st * 32 + 2 * kin]) = hi;
       }
     }
     __syncthreads();
     if (it + 1 < n_it) load_tile(it + 1);
 
-    const int sub0 = (p0 + it * PAGES) * kBlockSize + koff;  // logical position of this wave's key 0
-    const bool need_mask = sub0 + 32 > Lb || sub0 + 32 > kend;
-
-    bf16x8 kf[2][4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int st = 0; st < 2; ++st) {
+      const int key0 = (p0 + 4 * it + 2 * st) * kBlockSize;
+      const bool need_mask = key0 + 32 > Lb || key0 + 32 > kend;
+      bf16x8 kf[2][4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kf[kt][c] = ld_bf16x8(&Ks[(koff + kt * 16 + l16) * KSTR + c * 32 + quad * 8]);
-    bf16x8 vf[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint16_t* vp = &Vt[(dt * 16 + l16) * VSTR + koff + quad * 4];
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
-      vf[dt] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-    }
-
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][c], qf[rb][c], sacc[kt], 0, 0, 0);
-      float sv[8];
+          kf[h][c] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(&Ks[(st * 32 + h * 16 + l16) * kKS + c * 32 + quad * 8]));
+      bf16x8 pf[NRB];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int rb = 0; rb < NRB; ++rb) {
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = sacc[kt][i] * a.sl2;
-          if (need_mask) {
-            const int pos = sub0 + kt * 16 + quad * 4 + i;
-            bool ok = pos < kend;
-            if (ok && pos >= Lb) {
-              const int j = pos - Lb;
-              ok = (anc[node_of[rb] * 4 + (j >> 6)] >> (j & 63)) & 1ull;
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h][c], qf[rb][c], sacc[h], 0, 0, 0);
+        // lane holds S[row l16][key h*16 + quad*4 + i]; PV slot j <-> (h = j % 2, i = j / 2)
+        float sv[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = sacc[h][i] * a.sl2;
+            if (need_mask) {
+              const int pos = key0 + h * 16 + quad * 4 + i;
+              bool ok = pos < kend;
+              if (ok && pos >= Lb) {
+                const int jj = pos - Lb;
+                ok = (anc[node_of[rb] * 4 + (jj >> 6)] >> (jj & 63)) & 1ull;
+              }
+              x = ok ? x : -INFINITY;
             }
-            x = ok ? x : -INFINITY;
+            sv[2 * i + h] = x;
           }
-          sv[kt * 4 + i] = x;
+        float mx = sv[0];
+#pragma unroll
+        for (int j2 = 1; j2 < 8; ++j2) mx = fmaxf(mx, sv[j2]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[rb], mx);
+        const bool none = (m_new == -INFINITY);
+        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        float psum = 0.f;
+#pragma unroll
+        for (int j2 = 0; j2 < 8; ++j2) {
+          const float p = none ? 0.f : __builtin_amdgcn_exp2f(sv[j2] - m_new);
+          psum += p;
+          pf[rb][j2] = static_cast<__bf16>(p);
         }
-      float mx = sv[0];
+        l_run[rb] = l_run[rb] * alpha + psum;
+        m_run[rb] = m_new;
 #pragma unroll
-      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[rb], mx);
-      const bool none = (m_new == -INFINITY);
-      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-      float psum = 0.f;
-      bf16x8 pf;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = none ? 0.f : __builtin_amdgcn_exp2f(sv[j] - m_new);
-        psum += p;
-        pf[j] = static_cast<__bf16>(p);
+        for (int dt = 0; dt < 8; ++dt) o[rb][dt] *= alpha;
       }
-      l_run[rb] = l_run[rb] * alpha + psum;
-      m_run[rb] = m_new;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        o[rb][dt] *= alpha;
-        o[rb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, o[rb][dt], 0, 0, 0);
+        const bf16x8 vf = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(&Vt[(dt * 16 + l16) * kVS + st * 32 + quad * 8]));
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          o[rb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb], o[rb][dt], 0, 0, 0);
       }
     }
   }
-
-  // row sums: the four lanes of a row hold disjoint key subsets
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     l_run[rb] += __shfl_xor(l_run[rb], 16);
@@ -274,132 +291,99 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const BArgs a) {
   report(a.status, b, err);
 
   const bool direct = (a.splits == 1);
-  if constexpr (WK == 1) {
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const int r = row_base + rb * 16 + l16;
-      if (r >= a.R) continue;
-      const int rl = r - rt * RT;
-      if (direct) {
-        const int node = r / a.G, hh = r % a.G;
-        uint16_t* op = a.out + ((static_cast<long>(b) * a.T + node) * a.Hq + g * a.G + hh) * kD;
-        const float inv = l_run[rb] > 0.f ? 1.f / l_run[rb] : 0.f;
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int r = row_base + rb * 16 + l16;
+    if (r >= a.R) continue;
+    const int rl = r - rt * RT;
+    if (direct) {
+      const int node = r / a.G, hh = r % a.G;
+      uint16_t* op = a.out + ((static_cast<long>(b) * a.T + node) * a.Hq + g * a.G + hh) * kD;
+      const float inv = l_run[rb] > 0.f ? 1.f / l_run[rb] : 0.f;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const uint32_t w0 = f32_to_bf16(o[rb][dt][0] * inv) | (static_cast<uint32_t>(f32_to_bf16(o[rb][dt][1] * inv)) << 16);
-          const uint32_t w1 = f32_to_bf16(o[rb][dt][2] * inv) | (static_cast<uint32_t>(f32_to_bf16(o[rb][dt][3] * inv)) << 16);
-          *reinterpret_cast<u32x2*>(op + dt * 16 + quad * 4) = u32x2{w0, w1};
-        }
-      } else {
-        float* po = a.part_o + (item * RT + rl) * kD;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + quad * 4) = o[rb][dt];
-        if (quad == 0) {
-          a.part_ml[(item * RT + rl) * 2 + 0] = m_run[rb];
-          a.part_ml[(item * RT + rl) * 2 + 1] = l_run[rb];
-        }
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint32_t w0 =
+            f32_to_bf16(o[rb][dt][0] * inv) | (static_cast<uint32_t>(f32_to_bf16(o[rb][dt][1] * inv)) << 16);
+        const uint32_t w1 =
+            f32_to_bf16(o[rb][dt][2] * inv) | (static_cast<uint32_t>(f32_to_bf16(o[rb][dt][3] * inv)) << 16);
+        *reinterpret_cast<u32x2*>(op + dt * 16 + quad * 4) = u32x2{w0, w1};
       }
-    }
-  } else {
-    // four waves hold the same 16 rows over disjoint keys: merge through LDS
-    __syncthreads();
-    float* mo = reinterpret_cast<float*>(Ks);  // [4][16][128]
-    float* ml = reinterpret_cast<float*>(Vt);  // [4][16][2]
+    } else {
+      float* po = a.part_o + (item * RT + rl) * kD;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<f32x4*>(&mo[(wave * 16 + l16) * kD + dt * 16 + quad * 4]) = o[0][dt];
-    if (quad == 0) {
-      ml[(wave * 16 + l16) * 2 + 0] = m_run[0];
-      ml[(wave * 16 + l16) * 2 + 1] = l_run[0];
-    }
-    __syncthreads();
-    const int row = tid >> 4;
-    const int dseg = (tid & 15) * 8;
-    const int r = rt * RT + row;
-    if (r < a.R) {
-      float mw[4], mstar = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        mw[w] = ml[(w * 16 + row) * 2];
-        mstar = fmaxf(mstar, mw[w]);
-      }
-      float lstar = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float wt = (mw[w] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw[w] - mstar);
-        lstar += wt * ml[(w * 16 + row) * 2 + 1];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] += wt * mo[(w * 16 + row) * kD + dseg + j];
-      }
-      const int rl = r - rt * RT;
-      if (direct) {
-        const int node = r / a.G, hh = r % a.G;
-        uint16_t* op = a.out + ((static_cast<long>(b) * a.T + node) * a.Hq + g * a.G + hh) * kD + dseg;
-        const float inv = lstar > 0.f ? 1.f / lstar : 0.f;
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          w[j] = f32_to_bf16(acc[2 * j] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * j + 1] * inv)) << 16);
-        *reinterpret_cast<u32x4*>(op) = u32x4{w[0], w[1], w[2], w[3]};
-      } else {
-        float* po = a.part_o + (item * RT + rl) * kD + dseg;
-        *reinterpret_cast<f32x4*>(po) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-        *reinterpret_cast<f32x4*>(po + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-        if ((tid & 15) == 0) {
-          a.part_ml[(item * RT + rl) * 2 + 0] = mstar;
-          a.part_ml[(item * RT + rl) * 2 + 1] = lstar;
-        }
+      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + quad * 4) = o[rb][dt];
+      if (quad == 0) {
+        a.part_ml[(item * RT + rl) * 2 + 0] = m_run[rb];
+        a.part_ml[(item * RT + rl) * 2 + 1] = l_run[rb];
       }
     }
   }
-}
+  if (direct) return;
 
-// Merge the split partials of one (b, g, row tile): O = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s.
-template <int RT>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const BArgs a) {
-  const long bgr = blockIdx.x;  // (b * Hkv + g) * n_rt + rt
-  const int rt = static_cast<int>(bgr % a.n_rt);
-  const long bg = bgr / a.n_rt;
-  const int g = static_cast<int>(bg % a.Hkv);
-  const int b = static_cast<int>(bg / a.Hkv);
-  const int tid = threadIdx.x;
-  const int dq = (tid & 31) * 4;
-  for (int rl = tid >> 5; rl < RT; rl += 8) {
+  // the last workgroup of (b, g, rt) to arrive merges every split
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    const unsigned prev = atomicAdd(&a.counters[bgr], 1u);
+    s_last = (prev == static_cast<unsigned>(a.splits - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const long first = (bgr / a.n_rt) * a.splits * a.n_rt + rt;  // item of split 0
+  const int dseg = (tid & 15) * 8;
+  for (int rl = tid >> 4; rl < RT; rl += 16) {
     const int r = rt * RT + rl;
     if (r >= a.R) break;
-    float mstar = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) {
-      const long item = (bg * a.splits + s) * a.n_rt + rt;
-      mstar = fmaxf(mstar, a.part_ml[(item * RT + rl) * 2]);
-    }
-    float lstar = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.splits; ++s) {
-      const long item = (bg * a.splits + s) * a.n_rt + rt;
-      const float ms = a.part_ml[(item * RT + rl) * 2];
-      if (ms == -INFINITY) continue;
-      const float wt = __builtin_amdgcn_exp2f(ms - mstar);
-      lstar += wt * a.part_ml[(item * RT + rl) * 2 + 1];
-      acc += wt * *reinterpret_cast<const f32x4*>(a.part_o + (item * RT + rl) * kD + dq);
+    float mstar = -INFINITY, lstar = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int sp0 = 0; sp0 < a.splits; sp0 += 8) {
+      float ms[8], ls[8];
+      f32x4 x0[8], x1[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        ms[k] = -INFINITY;
+        ls[k] = 0.f;
+        x0[k] = x1[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (sp0 + k < a.splits) {
+          const long it2 = first + static_cast<long>(sp0 + k) * a.n_rt;
+          ms[k] = a.part_ml[(it2 * RT + rl) * 2];
+          ls[k] = a.part_ml[(it2 * RT + rl) * 2 + 1];
+          const float* po = a.part_o + (it2 * RT + rl) * kD + dseg;
+          x0[k] = *reinterpret_cast<const f32x4*>(po);
+          x1[k] = *reinterpret_cast<const f32x4*>(po + 4);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (ms[k] == -INFINITY) continue;
+        const float m_new = fmaxf(mstar, ms[k]);
+        const float fa = __builtin_amdgcn_exp2f(mstar - m_new);
+        const float fb = __builtin_amdgcn_exp2f(ms[k] - m_new);
+        lstar = lstar * fa + ls[k] * fb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] = acc[e] * fa + x0[k][e] * fb;
+          acc[4 + e] = acc[4 + e] * fa + x1[k][e] * fb;
+        }
+        mstar = m_new;
+      }
     }
     const float inv = lstar > 0.f ? 1.f / lstar : 0.f;
     const int node = r / a.G, hh = r % a.G;
-    uint16_t* op = a.out + ((static_cast<long>(b) * a.T + node) * a.Hq + g * a.G + hh) * kD + dq;
-    const uint32_t w0 = f32_to_bf16(acc[0] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[1] * inv)) << 16);
-    const uint32_t w1 = f32_to_bf16(acc[2] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[3] * inv)) << 16);
-    *reinterpret_cast<u32x2*>(op) = u32x2{w0, w1};
+    uint16_t* op = a.out + ((static_cast<long>(b) * a.T + node) * a.Hq + g * a.G + hh) * kD + dseg;
+    uint32_t wds[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      wds[e] = f32_to_bf16(acc[2 * e] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * e + 1] * inv)) << 16);
+    *reinterpret_cast<u32x4*>(op) = u32x4{wds[0], wds[1], wds[2], wds[3]};
   }
+  if (tid == 0) atomicExch(&a.counters[bgr], 0u);
 }
 
-template <int WR, int WK, int NRB>
-hipError_t run(const AttnPlan& plan, const BArgs& args, hipStream_t stream) {
-  constexpr int RT = 16 * NRB * WR;
+template <int NRB>
+hipError_t run_tile(const TArgs2& args, hipStream_t stream) {
   const long grid = ((args.items + 7) / 8) * 8;
-  hipLaunchKernelGGL((attn_bf16_kernel<WR, WK, NRB>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, args);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.splits == 1) return e;
-  hipLaunchKernelGGL((attn_combine_kernel<RT>), dim3(static_cast<unsigned>(static_cast<long>(args.B) * args.Hkv * args.n_rt)),
-                     dim3(256), 0, stream, args);
+  hipLaunchKernelGGL((attn_tile_kernel<NRB>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 
@@ -421,44 +405,34 @@ AttnPlan plan_attn(int B, int T, int Hq, int Hkv, int D, int max_blocks, int dty
     return p;
   }
   (void)D;
-  int pages_per_it;
-  if (p.rows <= 16) {
-    p.mode = 1;
-    p.rt = 16;
-    p.nrb = 1;
-    pages_per_it = 8;
-  } else if (p.rows < 1024) {
-    p.mode = 2;
-    p.rt = 64;
-    p.nrb = 1;
-    pages_per_it = 2;
-  } else {
-    p.mode = 2;
-    p.rt = 256;
-    p.nrb = 4;
-    pages_per_it = 2;
+  if (p.rows <= 64) {
+    plan_stream(p, B, Hkv, max_blocks);
+    return p;
   }
+  // many rows: 128-row tiles, or 256-row tiles from 1024 rows up
+  p.mode = 2;
+  p.nrb = p.rows >= 1024 ? 4 : 2;
+  p.rt = 64 * p.nrb;
   p.n_rt = (p.rows + p.rt - 1) / p.rt;
   const long base = static_cast<long>(B) * Hkv * p.n_rt;
-  // Aim for ~1024 workgroups; keep the partial traffic (2 * splits * rows fp32
-  // rows per head) under ~1/4 of the KV bytes; splits hold whole iterations.
-  const long want = std::max<long>(1, (1024 + base - 1) / base);
-  const long kv_keys = static_cast<long>(max_blocks) * kBlockSize;
-  long cap = std::max<long>(1, kv_keys / (8L * p.rows));
-  if (p.rows >= 1024) cap = std::max<long>(cap, 4);  // matrix-core bound: parallelism first
-  long splits = std::min(want, cap);
-  int pps = static_cast<int>((max_blocks + splits - 1) / splits);
-  pps = ((pps + pages_per_it - 1) / pages_per_it) * pages_per_it;
+  // ~one workgroup per CU; at least 16 pages (256 keys) per split
+  long splits = std::max<long>(1, (256 + base - 1) / base);
+  splits = std::min<long>(splits, std::max<long>(1, max_blocks / 16));
+  long pps = (max_blocks + splits - 1) / splits;
+  pps = (pps + 3) / 4 * 4;
+  pps = std::min<long>(pps, kMaxSplitPages);
   splits = (max_blocks + pps - 1) / pps;
-  p.pps = pps;
+  p.pps = static_cast<int>(pps);
   p.splits = static_cast<int>(splits);
   p.items = base * p.splits;
-  p.ws_bytes = p.splits > 1 ? static_cast<size_t>(p.items) * p.rt * (kD + 2) * sizeof(float) : 0;
+  const size_t head = (static_cast<size_t>(base) * sizeof(unsigned) + 255) / 256 * 256;
+  p.ws_bytes = p.splits > 1 ? head + static_cast<size_t>(p.items) * p.rt * (kD + 2) * sizeof(float) : 0;
   return p;
 }
 
 hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& L, hipStream_t stream) {
-  BArgs a{};
+  if (plan.mode == 3) return launch_attn_stream(plan, L, stream);
+  TArgs2 a{};
   a.q = static_cast<const uint16_t*>(L.q);
   a.k = static_cast<const uint16_t*>(L.k);
   a.v = static_cast<const uint16_t*>(L.v);
@@ -481,12 +455,14 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& L, hipStream
   a.items = plan.items;
   a.sl2 = L.scale * kLog2e;
   if (plan.splits > 1) {
-    a.part_o = static_cast<float*>(L.workspace);
+    const size_t base = static_cast<size_t>(L.B) * L.Hkv * plan.n_rt;
+    const size_t head = (base * sizeof(unsigned) + 255) / 256 * 256;
+    a.counters = static_cast<unsigned*>(L.workspace);
+    a.part_o = reinterpret_cast<float*>(static_cast<char*>(L.workspace) + head);
     a.part_ml = a.part_o + static_cast<size_t>(plan.items) * plan.rt * kD;
   }
-  if (plan.mode == 1) return run<1, 4, 1>(plan, a, stream);
-  if (plan.nrb == 1) return run<4, 1, 1>(plan, a, stream);
-  return run<4, 1, 4>(plan, a, stream);
+  if (plan.nrb == 4) return run_tile<4>(a, stream);
+  return run_tile<2>(a, stream);
 }
 
 }  // namespace spectree

@@ -39,7 +39,8 @@ __device__ __forceinline__ void report(int32_t* status, int b, int32_t bits) {
 // ---------------------------------------------------------------------------
 
 struct AttnPlan {
-  int mode;       // 0: fp32 VALU kernel, 1: bf16 key-split (<=16 rows), 2: bf16 row-split
+  int mode;       // 0: fp32 VALU kernel, 1: bf16 key-split (<=16 rows), 2: bf16 row-split,
+                  // 3: bf16 streaming kernel (<=64 rows)
   int rows;       // R = T * G query rows per (sequence, kv head)
   int rt;         // rows per workgroup
   int nrb;        // 16-row blocks per wave
@@ -67,6 +68,8 @@ struct AttnLaunch {
 };
 
 hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& a, hipStream_t stream);
+void plan_stream(AttnPlan& p, int B, int Hkv, int max_blocks);
+hipError_t launch_attn_stream(const AttnPlan& plan, const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnPlan& plan, const AttnLaunch& a, hipStream_t stream);
 
 struct RejectLaunch {
@@ -86,6 +89,7 @@ struct RejectLaunch {
 };
 
 size_t reject_workspace_bytes(int B, int T, int V);
+size_t reject_workspace_zero_bytes(int B);
 hipError_t launch_reject(const RejectLaunch& a, hipStream_t stream);
 
 struct CompactLaunch {

@@ -8,35 +8,70 @@
 // Scalable and Robust Speculative Decoding" summary, "Robust Sampling") also
 // removes each rejected token from q and renormalises q.
 //
-// Two kernels:
-//   row_stats: per (row, 4096-token chunk) the max logit and the first index
-//     holding it, and sum exp((l - max) / temperature) in fp64.
-//   walk: one 1024-thread workgroup per sequence walks the tree.  The target
-//     row of the current node is p(x) = exp((l_x - m) / t) / Z.  The residual
-//     after j rejections is kept in closed form,
+// One kernel.  Each sequence is walked by a TEAM of NW workgroups; member w
+// owns the contiguous vocabulary slice [w*S, (w+1)*S) and keeps the slices of
+// the rows it works on in LDS.  Every member replays the same walk (same
+// inputs, same Philox draws, merges done by one wave in a fixed order, so the
+// same decisions); vocabulary-wide quantities are merged from the members'
+// slice partials, exchanged through the workspace at a team barrier:
+//   * row statistics of node u: max logit, first argmax, sum exp((l-max)/t)
+//     in fp64 -- rows 0..E-1 before the walk, deeper rows when reached;
+//   * the residual after j rejections, kept in closed form
 //         p~_j(x) = max(p(x) - C_j(x) q(x), 0) / N_j,
-//     with one coefficient C_j for every token not yet removed from q and a
-//     frozen coefficient for each removed token (at most one per rejected
-//     sibling), and q~_j(x) = s_j q(x) for tokens still in q.  Each rejection
-//     costs one vocabulary-wide fp64 reduction for N_{j+1}; no V-sized state
-//     is stored.  Decisions are taken in fp64.
-// Uniforms come from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with
-// key (seed lo, seed hi) and counter (node, b, purpose + 2*(offset >> 32),
-// offset lo); u = (word0 >> 8) * 2^-24.
+//     one coefficient C_j for every token still in q and a frozen coefficient
+//     per token removed from q (without replacement), q~_j = s_j q on the
+//     tokens still in q.  Each rejection is one pass over the slice that
+//     publishes the slice mass of the new residual, scanned over per-thread
+//     contiguous segments in index order;
+//   * the final draw: after a rejection the last pass already holds the
+//     scanned weights; for a bonus draw the slice masses of p follow from the
+//     row statistics.  The member whose range holds u * total finds the token
+//     inside its slice.
+// Team barriers spin on a per-sequence counter with a bounded wait; the last
+// member to leave resets the counters, so the workspace header stays zero.
+// Decisions are taken in fp64 from the fp32 inputs.  Uniforms: Philox4x32-10
+// (Salmon, Moraes, Dror, Shaw, SC'11), key (seed lo, seed hi), counter (node,
+// b, purpose + 2*(offset >> 32), offset lo); u = (word0 >> 8) * 2^-24.
+#include <algorithm>
+
 #include "common.h"
 
 namespace spectree {
 namespace {
 
-constexpr int kChunk = 4096;
-constexpr int kWalkThreads = 1024;
-constexpr int kWalkWaves = kWalkThreads / 64;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxEager = 8;     // rows whose statistics are taken before the walk
+constexpr int kMaxTeam = 32;     // workgroups per sequence (one wave merges their partials)
+constexpr int kEagerCap = 8192;  // floats of eager-row logit slices kept in LDS
+constexpr int kSliceCap = 8192;  // floats of the current row's logits / draft probs kept in LDS
+constexpr int kSyncStride = 16;  // uint32 words of barrier state per sequence (64 B)
+constexpr unsigned kSpinLimit = 1u << 24;
 
-struct RowStat {
-  float m;   // max logit of the chunk (-inf if all -inf)
-  int idx;   // first index holding m; -1 if the chunk holds NaN or +inf
-  double z;  // sum over the chunk of exp((l - m) / temperature)
+struct Rec {
+  float m;   // slice max logit (-inf if none)
+  int idx;   // first index of the max; -1 if the slice holds NaN or +inf
+  double z;  // sum over the slice of exp((l - m) / t), or a slice mass
 };
+
+struct Team {
+  int NW, S, E;
+};
+
+Team team_shape(int B, int T, int V) {
+  Team t;
+  int nw = std::max(1, std::min(kMaxTeam, 256 / std::max(B, 1)));
+  nw = std::min(nw, std::max(1, (V + 511) / 512));
+  t.NW = nw;
+  t.S = (V + nw - 1) / nw;
+  t.E = std::min(T, kMaxEager);
+  if (t.S > kEagerCap) {
+    t.E = 0;
+  } else {
+    t.E = std::min(t.E, kEagerCap / t.S);
+  }
+  return t;
+}
 
 // ---------------------------------------------------------------------------
 // Philox4x32-10: ten rounds of the multiply/xor bijection, key bumped by the
@@ -72,141 +107,202 @@ __device__ __forceinline__ double draw_uniform(uint64_t seed, uint64_t offset, i
 
 __device__ __forceinline__ bool bad_logit(float v) { return isnan(v) || v == INFINITY; }
 
-// ---------------------------------------------------------------------------
-// row statistics
-// ---------------------------------------------------------------------------
-struct SArgs {
-  const float* logits;
-  RowStat* stats;
-  int V, nchunks, greedy;
-  double inv_tau;
-};
-
-__global__ __launch_bounds__(256) void row_stats_kernel(const SArgs a) {
-  __shared__ float s_m[4];
-  __shared__ int s_i[4];
-  __shared__ double s_z[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = blockIdx.x % a.nchunks;
-  const long row = blockIdx.x / a.nchunks;
-  const float* lr = a.logits + row * a.V;
-  const int x0 = c * kChunk, x1 = min(a.V, x0 + kChunk);
-
-  float mx = -INFINITY;
-  int ix = 0x7fffffff;
-  bool bad = false;
-  for (int x = x0 + tid; x < x1; x += 256) {
-    const float v = lr[x];
-    bad |= bad_logit(v);
-    if (v > mx) {  // strictly greater: a thread keeps its first index of the max
-      mx = v;
-      ix = x;
-    }
-  }
-  // max with lowest index on ties
-#pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) {
-    const float om = __shfl_xor(mx, w);
-    const int oi = __shfl_xor(ix, w);
-    if (om > mx || (om == mx && oi < ix)) {
-      mx = om;
-      ix = oi;
-    }
-  }
-  bad = __any(bad);
-  if (lane == 0) {
-    s_m[wave] = mx;
-    s_i[wave] = bad ? -1 : ix;
-  }
-  __syncthreads();
-  float m = s_m[0];
-  int idx = s_i[0];
-  bool anybad = s_i[0] < 0;
-  for (int w = 1; w < 4; ++w) {
-    anybad |= s_i[w] < 0;
-    if (s_m[w] > m || (s_m[w] == m && s_i[w] < idx)) {
-      m = s_m[w];
-      idx = s_i[w];
-    }
-  }
-  double z = 0.0;
-  if (!a.greedy && m != -INFINITY && !anybad) {
-    const double md = static_cast<double>(m);
-    for (int x = x0 + tid; x < x1; x += 256) z += exp((static_cast<double>(lr[x]) - md) * a.inv_tau);
-#pragma unroll
-    for (int w = 32; w >= 1; w >>= 1) z += __shfl_xor(z, w);
-    if (lane == 0) s_z[wave] = z;
-    __syncthreads();
-    z = s_z[0] + s_z[1] + s_z[2] + s_z[3];
-  }
-  if (tid == 0) {
-    RowStat st;
-    st.m = m;
-    st.idx = anybad ? -1 : (idx == 0x7fffffff ? x0 : idx);
-    st.z = z;
-    a.stats[row * a.nchunks + c] = st;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// tree walk
-// ---------------------------------------------------------------------------
-struct WArgs {
+struct TArgs {
   const float* logits;
   const float* q;
   const int32_t* tokens;
   const int32_t* parent;
-  const RowStat* stats;
   int32_t* accepted;
   int32_t* out_tokens;
   int32_t* num_accepted;
   int32_t* status;
-  int T, V, nchunks, greedy, wr;
+  unsigned* sync;  // [B][kSyncStride]: arrive counter, exit counter
+  Rec* eager;      // [B][NW][max(E,1)]
+  Rec* part;       // [B][2][NW]
+  int T, V, NW, S, E, greedy, wr;
   double inv_tau;
   uint64_t seed, offset;
 };
 
-__device__ double block_sum(double v, double* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) v += __shfl_xor(v, w);
+// Team barrier number `target`: every member has published its partials.
+__device__ __forceinline__ void team_barrier(unsigned* ctr, unsigned target, int* fail) {
   __syncthreads();
-  if (lane == 0) red[wave] = v;
+  if (threadIdx.x == 0 && *fail == 0) {
+    __threadfence();
+    atomicAdd(ctr, 1u);
+    unsigned spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        *fail = 1;
+        break;
+      }
+    }
+    __threadfence();
+  }
   __syncthreads();
-  double t = 0.0;
-#pragma unroll
-  for (int w = 0; w < kWalkWaves; ++w) t += red[w];  // fixed order: every thread gets the same value
-  return t;
 }
 
-__global__ __launch_bounds__(kWalkThreads) void walk_kernel(const WArgs a) {
+// Copy rows [r * src_stride + i], r < nrows, i < n (nrows * n <= 32 * kThreads) of global
+// memory into LDS dst[r * n + i].  Every load of a thread is issued before its first
+// store, so the copy costs one memory latency.
+__device__ __forceinline__ void stage_rows(float* dst, const float* src, long src_stride, int nrows, int n) {
+  constexpr int kB = 32;
+  const int cnt = nrows * n;
+  if (cnt <= 0) return;
+  const int tid = threadIdx.x;
+  float v[kB];
+  int r = tid / n, i = tid - (tid / n) * n;
+#pragma unroll
+  for (int k = 0; k < kB; ++k) {
+    v[k] = (k * kThreads + tid < cnt) ? src[r * src_stride + i] : 0.f;
+    i += kThreads;
+    while (i >= n) {
+      i -= n;
+      ++r;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kB; ++k)
+    if (k * kThreads + tid < cnt) dst[k * kThreads + tid] = v[k];
+}
+
+// Max with the lowest index on ties, over the 64 lanes of a wave.
+__device__ __forceinline__ void wave_argmax(float& m, int& i) {
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const float om = __shfl_xor(m, w);
+    const int oi = __shfl_xor(i, w);
+    if (om > m || (om == m && oi < i)) {
+      m = om;
+      i = oi;
+    }
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (lane order).
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int w = 1; w < 64; w <<= 1) {
+    const double o = __shfl_up(v, w);
+    if (lane >= w) v += o;
+  }
+  return v;
+}
+
+// Statistics of up to kMaxEager rows whose slices are rows[r * stride + i], i < n.
+__device__ __forceinline__ void slice_stats_rows(const float* rows, int stride, int nrows, int n, int v0, bool greedy,
+                                 double inv_tau, Rec* out, float* redm, int* redi, double* redz) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int r = 0; r < nrows; ++r) {
+    float mx = -INFINITY;
+    int ix = 0x7fffffff;
+    bool bad = false;
+    for (int i = tid; i < n; i += kThreads) {
+      const float v = rows[r * stride + i];
+      bad |= bad_logit(v);
+      if (v > mx) {
+        mx = v;
+        ix = v0 + i;
+      }
+    }
+    wave_argmax(mx, ix);
+    bad = __any(bad);
+    if (lane == 0) {
+      redm[r * kWaves + wave] = mx;
+      redi[r * kWaves + wave] = bad ? -1 : ix;
+    }
+  }
+  __syncthreads();
+  for (int r = 0; r < nrows; ++r) {
+    float m = redm[r * kWaves];
+    int idx = redi[r * kWaves];
+    bool anybad = idx < 0;
+    for (int w = 1; w < kWaves; ++w) {
+      const float om = redm[r * kWaves + w];
+      const int oi = redi[r * kWaves + w];
+      anybad |= oi < 0;
+      if (om > m || (om == m && oi < idx)) {
+        m = om;
+        idx = oi;
+      }
+    }
+    double z = 0.0;
+    if (!greedy && m != -INFINITY && !anybad) {
+      const double md = static_cast<double>(m);
+      for (int i = tid; i < n; i += kThreads) z += exp((static_cast<double>(rows[r * stride + i]) - md) * inv_tau);
+    }
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) z += __shfl_xor(z, w);
+    if (lane == 0) redz[r * kWaves + wave] = z;
+    if (tid == 0) {
+      out[r].m = m;
+      out[r].idx = anybad ? -1 : (idx == 0x7fffffff ? v0 : idx);
+    }
+  }
+  __syncthreads();
+  if (tid == 0)
+    for (int r = 0; r < nrows; ++r) {
+      double t = 0.0;
+      for (int w = 0; w < kWaves; ++w) t += redz[r * kWaves + w];
+      out[r].z = t;
+    }
+  __syncthreads();
+}
+
+// kFits: the slice (S <= kSliceCap floats) lives in LDS, so every slice access is an
+// LDS access; otherwise the slices are read from global memory where they lie.
+template <bool kFits>
+__global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
+  __shared__ float eager_l[kEagerCap];
+  __shared__ float cur_lbuf[kSliceCap];
+  __shared__ float cur_qbuf[kSliceCap];
   __shared__ int16_t first_child[kMaxT], next_sib[kMaxT];
-  __shared__ int s_tok[kMaxT], s_path[kMaxT];
-  __shared__ uint32_t rej_bits[kMaxV / 32];
+  __shared__ int s_par[kMaxT], s_tok[kMaxT], s_path[kMaxT];
+  __shared__ float s_lx[kMaxT], s_qx[kMaxT];  // logit / draft prob of node c's token in its parent's row
   __shared__ int rej_tok[kMaxT];
   __shared__ double rej_c[kMaxT];
-  __shared__ double red[kWalkWaves];
-  __shared__ double sh_incl[kWalkWaves];
-  __shared__ int sh_err, sh_len, sh_u, sh_c, sh_x, sh_state, sh_nrej, sh_emit;
-  __shared__ double sh_m, sh_iz, sh_C, sh_N, sh_s;
+  __shared__ float redm[kMaxEager * kWaves];
+  __shared__ int redi[kMaxEager * kWaves];
+  __shared__ double redz[kMaxEager * kWaves];
+  __shared__ Rec s_rec[kMaxEager];
+  __shared__ double sh_incl[kWaves];
+  __shared__ int sh_err, sh_fail, sh_len, sh_u, sh_c, sh_x, sh_state, sh_nrej, sh_emit_local, sh_owner, sh_arg;
+  __shared__ double sh_m, sh_iz, sh_C, sh_Cold, sh_N, sh_s, sh_lo, sh_target, sh_total;
 
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int T = a.T, V = a.V;
-  const int32_t* par = a.parent + static_cast<long>(b) * T;
-  const int32_t* tk = a.tokens + static_cast<long>(b) * T;
+  const int NW = a.NW;
+  const int b = blockIdx.x / NW;
+  const int wg = blockIdx.x % NW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = a.T, V = a.V, S = a.S, E = a.E;
+  const int v0 = min(V, wg * S), v1 = min(V, v0 + S);
+  const int n = v1 - v0;
+  const int seg = (n + kThreads - 1) / kThreads;  // per-thread contiguous segment of the slice
+  const int i0 = min(n, tid * seg), i1 = min(n, i0 + seg);
+  const float* lg_b = a.logits + static_cast<long>(b) * T * V;
+  const float* q_b = a.q + static_cast<long>(b) * T * V;
+  unsigned* ctr = a.sync + static_cast<long>(b) * kSyncStride;
+  unsigned phase = 0;
+  int buf = 0;
+  Rec* eager = a.eager + static_cast<long>(b) * NW * max(E, 1);
+  Rec* part = a.part + static_cast<long>(b) * 2 * NW;
 
-  for (int i = tid; i < (V + 31) / 32; i += kWalkThreads) rej_bits[i] = 0u;
+  // tree, tokens and the accept-test operands of every drafted node
+  for (int i = tid; i < T; i += kThreads) {
+    s_par[i] = a.parent[static_cast<long>(b) * T + i];
+    s_tok[i] = a.tokens[static_cast<long>(b) * T + i];
+  }
+  __syncthreads();
   if (tid == 0) {
     int err = 0;
     for (int i = 0; i < T; ++i) {
       first_child[i] = -1;
       next_sib[i] = -1;
-      s_tok[i] = tk[i];
     }
-    if (par[0] != -1) err |= SPEC_DEV_PARENT;
+    if (s_par[0] != -1) err |= SPEC_DEV_PARENT;
     for (int i = T - 1; i >= 1; --i) {  // prepend in decreasing order: child lists come out increasing
-      const int p = par[i];
+      const int p = s_par[i];
       if (p < 0 || p >= i) {
         err |= SPEC_DEV_PARENT;
         continue;
@@ -216,72 +312,144 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(const WArgs a) {
       first_child[p] = static_cast<int16_t>(i);
     }
     sh_err = err;
+    sh_fail = 0;
     sh_len = 1;
     s_path[0] = 0;
     sh_u = 0;
-    sh_emit = -1;
     sh_nrej = 0;
+    sh_emit_local = -1;
+    sh_owner = 0;
   }
   __syncthreads();
 
-  if (sh_err == 0 && a.greedy) {
-    if (tid == 0) {
-      int u = 0;
-      for (;;) {
-        const RowStat* st = a.stats + (static_cast<long>(b) * T + u) * a.nchunks;
-        float best = -INFINITY;
-        int bi = 0x7fffffff;
-        bool bad = false;
-        for (int c = 0; c < a.nchunks; ++c) {
-          bad |= st[c].idx < 0;
-          if (st[c].m > best || (st[c].m == best && st[c].idx < bi)) {
-            best = st[c].m;
-            bi = st[c].idx;
-          }
-        }
-        if (bad) {
-          sh_err |= SPEC_DEV_NONFINITE;
-          break;
-        }
-        int c = first_child[u];
-        while (c >= 0 && s_tok[c] != bi) c = next_sib[c];
-        if (c < 0) {
-          sh_emit = bi;
-          break;
-        }
-        s_path[sh_len++] = c;
-        u = c;
-      }
+  int emitted = -1;  // greedy argmax, known to every member
+  if (sh_err == 0) {
+    for (int c = 1 + tid; c < T; c += kThreads) {
+      const long off = static_cast<long>(s_par[c]) * V + s_tok[c];
+      s_lx[c] = lg_b[off];
+      s_qx[c] = a.greedy ? 0.f : q_b[off];
     }
-  } else if (sh_err == 0) {
+    // statistics of the first E rows, from their LDS slices
+    if (kFits && E > 0) {
+      stage_rows(eager_l, lg_b + v0, V, E, n);
+      __syncthreads();
+      slice_stats_rows(eager_l, n, E, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+      if (tid < E) eager[wg * E + tid] = s_rec[tid];
+      team_barrier(ctr, NW * ++phase, &sh_fail);
+    }
+
     for (;;) {  // one iteration per visited node
-      if (tid == 0) {
-        const int u = sh_u;
-        const RowStat* st = a.stats + (static_cast<long>(b) * T + u) * a.nchunks;
-        float m = -INFINITY;
-        bool bad = false;
-        for (int c = 0; c < a.nchunks; ++c) {
-          bad |= st[c].idx < 0;
-          m = fmaxf(m, st[c].m);
+      if (sh_fail) break;
+      const int u = sh_u;
+      const bool has_kids = first_child[u] >= 0;
+      // this node's logit slice (LDS when it fits) and, if it has children, its draft slice
+      const float* cl;
+      const float* cq;
+      if constexpr (kFits) {
+        if (u < E) {
+          cl = eager_l + u * n;
+        } else {
+          stage_rows(cur_lbuf, lg_b + static_cast<long>(u) * V + v0, 0, 1, n);
+          cl = cur_lbuf;
         }
-        double z = 0.0;
-        for (int c = 0; c < a.nchunks; ++c)
-          if (st[c].m != -INFINITY) z += st[c].z * exp((static_cast<double>(st[c].m) - m) * a.inv_tau);
-        if (bad) sh_err |= SPEC_DEV_NONFINITE;
-        if (!(z > 0.0)) sh_err |= SPEC_DEV_EMPTY;
-        sh_m = m;
-        sh_iz = 1.0 / z;
-        sh_C = 0.0;
-        sh_N = 1.0;
-        sh_s = 1.0;
-        for (int k = 0; k < sh_nrej; ++k) rej_bits[rej_tok[k] >> 5] &= ~(1u << (rej_tok[k] & 31));
-        sh_nrej = 0;
-        sh_c = first_child[u];
+        if (!a.greedy && has_kids) stage_rows(cur_qbuf, q_b + static_cast<long>(u) * V + v0, 0, 1, n);
+        cq = cur_qbuf;
+      } else {
+        cl = lg_b + static_cast<long>(u) * V + v0;
+        cq = q_b + static_cast<long>(u) * V + v0;
+      }
+      __syncthreads();
+      const Rec* rows = eager + u;
+      int rstride = E;
+      if (u >= E) {  // a deeper row: its statistics now
+        slice_stats_rows(cl, 0, 1, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+        if (tid == 0) part[buf * NW + wg] = s_rec[0];
+        team_barrier(ctr, NW * ++phase, &sh_fail);
+        if (sh_fail) break;
+        rows = part + buf * NW;
+        rstride = 1;
+        buf ^= 1;
+      }
+      // merge the members' statistics: one wave, member order
+      if (wave == 0) {
+        Rec r;
+        r.m = -INFINITY;
+        r.idx = 0x7fffffff;
+        r.z = 0.0;
+        if (lane < NW) r = rows[lane * rstride];
+        const bool badr = lane < NW && r.idx < 0;
+        float m = r.m;
+        int arg = badr ? 0x7fffffff : r.idx;
+        wave_argmax(m, arg);
+        double zt = 0.0;
+        if (!a.greedy && lane < NW && r.m != -INFINITY) zt = r.z * exp((static_cast<double>(r.m) - m) * a.inv_tau);
+        zt = wave_incl_scan(zt);  // lane 63 holds the member-order sum
+        const bool anybad = __any(badr);
+        if (lane == 63) {
+          int err = 0;
+          if (anybad) err |= SPEC_DEV_NONFINITE;
+          if (!a.greedy && !(zt > 0.0)) err |= SPEC_DEV_EMPTY;
+          sh_err |= err;
+          sh_m = m;
+          sh_iz = 1.0 / zt;
+          sh_arg = arg;
+          sh_C = 0.0;
+          sh_N = 1.0;
+          sh_s = 1.0;
+          sh_nrej = 0;
+          sh_c = first_child[u];
+        }
       }
       __syncthreads();
       if (sh_err) break;
-      const float* lrow = a.logits + (static_cast<long>(b) * T + sh_u) * V;
-      const float* qrow = a.q + (static_cast<long>(b) * T + sh_u) * V;
+      if (a.greedy) {
+        if (tid == 0) {
+          int c = first_child[u];
+          while (c >= 0 && s_tok[c] != sh_arg) c = next_sib[c];
+          if (c >= 0) {
+            s_path[sh_len++] = c;
+            sh_u = c;
+          }
+          sh_state = c >= 0 ? 1 : 0;
+        }
+        __syncthreads();
+        if (sh_state == 1) continue;
+        emitted = sh_arg;
+        break;
+      }
+      const double m = sh_m, iz = sh_iz;
+      auto weight = [&](int i) -> double {  // current residual weight of slice element i
+        const double p = exp((static_cast<double>(cl[i]) - m) * a.inv_tau) * iz;
+        const double C = sh_C;
+        const int nrej = sh_nrej;
+        if (nrej == 0 && C == 0.0) return p;
+        const int x = v0 + i;
+        double cx = C;
+        for (int k = 0; k < nrej; ++k)
+          if (rej_tok[k] == x) cx = rej_c[k];
+        return fmax(p - cx * static_cast<double>(cq[i]), 0.0);
+      };
+      // publish the slice mass of the current weights, scanned in index order
+      double excl = 0.0, incl = 0.0;  // this thread's range within the slice
+      auto scan_slice = [&](bool check_q) -> bool {
+        double mine = 0.0;
+        bool badq = false;
+        for (int i = i0; i < i1; ++i) {
+          if (check_q) badq |= isnan(cq[i]);
+          mine += weight(i);
+        }
+        badq = __syncthreads_or(badq);
+        incl = wave_incl_scan(mine);
+        if (lane == 63) sh_incl[wave] = incl;
+        __syncthreads();
+        double before = 0.0;
+        for (int w = 0; w < wave; ++w) before += sh_incl[w];
+        incl += before;
+        excl = __shfl_up(incl, 1);
+        if (lane == 0) excl = before;
+        return badq;
+      };
+      bool scanned = false;  // part[buf] holds the slice masses of the current weights
       // try the children of u in turn
       for (;;) {
         if (tid == 0) {
@@ -290,67 +458,71 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(const WArgs a) {
             sh_state = 0;  // no untried child: final draw at u
           } else {
             const int x = s_tok[c];
-            const double px = exp((static_cast<double>(lrow[x]) - sh_m) * a.inv_tau) * sh_iz;
-            const float qf = qrow[x];
+            const double px = exp((static_cast<double>(s_lx[c]) - m) * a.inv_tau) * iz;
+            const float qf = s_qx[c];
             if (isnan(qf)) sh_err |= SPEC_DEV_NONFINITE;
             const double qx = static_cast<double>(qf);
-            const bool removed = (rej_bits[x >> 5] >> (x & 31)) & 1u;
-            double cx = sh_C;
-            if (removed)
-              for (int k = 0; k < sh_nrej; ++k)
-                if (rej_tok[k] == x) cx = rej_c[k];
-            const double ax = fmax(px - cx * qx, 0.0);
-            const double pt = ax / sh_N;
+            int k = 0;
+            while (k < sh_nrej && rej_tok[k] != x) ++k;
+            const bool removed = k < sh_nrej;
+            const double cx = removed ? rej_c[k] : sh_C;
+            const double pt = fmax(px - cx * qx, 0.0) / sh_N;
             const double qt = removed ? 0.0 : sh_s * qx;
             const double r = draw_uniform(a.seed, a.offset, b, c, 0);
             sh_x = x;
-            sh_state = (r * qt < pt) ? 1 : 2;  // 1 accept, 2 reject
+            if (r * qt < pt) {
+              sh_state = 1;  // accept
+            } else {
+              sh_state = 2;  // reject: the residual uses C' = C + N s for the tokens still in q
+              sh_Cold = sh_C;
+              sh_C = sh_C + sh_N * sh_s;
+            }
           }
         }
         __syncthreads();
         if (sh_state != 2 || sh_err) break;
-        // residual after rejecting sh_x: C' = C + N s for tokens still in q
-        const double Cp = sh_C + sh_N * sh_s;
-        const double iz = sh_iz, m = sh_m;
-        double part = 0.0;
-        bool badq = false;
-        for (int x = tid; x < V; x += kWalkThreads) {
-          const float qf = qrow[x];
-          badq |= isnan(qf);
-          const double p = exp((static_cast<double>(lrow[x]) - m) * a.inv_tau) * iz;
-          part += fmax(p - Cp * static_cast<double>(qf), 0.0);
+        const bool badq = scan_slice(true);
+        if (tid == kThreads - 1) {
+          Rec r;
+          r.m = 0.f;
+          r.idx = badq ? -1 : 0;
+          r.z = incl;  // slice mass: the last thread's inclusive sum
+          part[buf * NW + wg] = r;
         }
-        if (badq) sh_err |= SPEC_DEV_NONFINITE;  // benign race: every writer sets the same bit
-        const double mass = block_sum(part, red);
-        if (tid == 0) {
-          double tot = mass;
-          for (int k = 0; k < sh_nrej; ++k) {  // removed tokens keep their frozen coefficient
-            const int y = rej_tok[k];
-            const double py = exp((static_cast<double>(lrow[y]) - m) * a.inv_tau) * iz;
-            const double qy = static_cast<double>(qrow[y]);
-            tot += fmax(py - rej_c[k] * qy, 0.0) - fmax(py - Cp * qy, 0.0);
-          }
-          if (tot > 0.0) {
-            sh_C = Cp;
-            sh_N = tot;
-          }
-          if (a.wr) {
-            const int x = sh_x;
-            const bool removed = (rej_bits[x >> 5] >> (x & 31)) & 1u;
-            if (!removed) {
-              const double q_old = sh_s * static_cast<double>(qrow[x]);
-              rej_bits[x >> 5] |= 1u << (x & 31);
-              rej_tok[sh_nrej] = x;
-              rej_c[sh_nrej] = sh_C;
-              ++sh_nrej;
-              if (q_old < 1.0) sh_s = sh_s / (1.0 - q_old);
+        team_barrier(ctr, NW * ++phase, &sh_fail);
+        if (sh_fail) break;
+        if (wave == 0) {
+          const Rec r = lane < NW ? part[buf * NW + lane] : Rec{0.f, 0, 0.0};
+          const double tot = wave_incl_scan(r.z);
+          const bool anybad = __any(lane < NW && r.idx < 0);
+          if (lane == 63) {
+            if (anybad) sh_err |= SPEC_DEV_NONFINITE;
+            if (tot > 0.0) {
+              sh_N = tot;
+            } else {
+              sh_C = sh_Cold;  // zero residual mass: p~ stays as it was
             }
+            if (a.wr) {
+              const int x = sh_x;
+              int k = 0;
+              while (k < sh_nrej && rej_tok[k] != x) ++k;
+              if (k == sh_nrej) {
+                const double q_old = sh_s * static_cast<double>(s_qx[sh_c]);
+                rej_tok[sh_nrej] = x;
+                rej_c[sh_nrej] = sh_C;
+                ++sh_nrej;
+                if (q_old < 1.0) sh_s = sh_s / (1.0 - q_old);
+              }
+            }
+            sh_total = tot;
+            sh_c = next_sib[sh_c];
           }
-          sh_c = next_sib[sh_c];
         }
         __syncthreads();
+        scanned = sh_total > 0.0;
+        if (sh_c >= 0) buf ^= 1;  // else part[buf] serves the final draw
       }
-      if (sh_err) break;
+      if (sh_err || sh_fail) break;
       if (sh_state == 1) {
         if (tid == 0) {
           s_path[sh_len++] = sh_c;
@@ -359,120 +531,139 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(const WArgs a) {
         __syncthreads();
         continue;
       }
-      // final draw at u: inverse CDF of w(x) = max(p(x) - C(x) q(x), 0) in index order
-      const double uu = draw_uniform(a.seed, a.offset, b, sh_u, 1);
-      const int seg = (V + kWalkThreads - 1) / kWalkThreads;
-      const int x0 = min(V, tid * seg), x1 = min(V, x0 + seg);
-      const double C = sh_C, iz = sh_iz, m = sh_m;
-      auto weight = [&](int x) -> double {
-        const double p = exp((static_cast<double>(lrow[x]) - m) * a.inv_tau) * iz;
-        double cx = C;
-        if ((rej_bits[x >> 5] >> (x & 31)) & 1u)
-          for (int k = 0; k < sh_nrej; ++k)
-            if (rej_tok[k] == x) cx = rej_c[k];
-        return fmax(p - cx * static_cast<double>(qrow[x]), 0.0);
-      };
-      double mine = 0.0;
-      for (int x = x0; x < x1; ++x) mine += weight(x);
-      // inclusive scan of the per-thread sums in thread order
-      const int lane = tid & 63, wave = tid >> 6;
-      double incl = mine;
-#pragma unroll
-      for (int w = 1; w < 64; w <<= 1) {
-        const double o = __shfl_up(incl, w);
-        if (lane >= w) incl += o;
-      }
-      if (lane == 63) sh_incl[wave] = incl;
-      __syncthreads();
-      double before = 0.0;
-      for (int w = 0; w < wave; ++w) before += sh_incl[w];
-      double total = 0.0;
-      for (int w = 0; w < kWalkWaves; ++w) total += sh_incl[w];
-      incl += before;
-      double excl = __shfl_up(incl, 1);
-      if (lane == 0) excl = before;
-      const double target = uu * total;
-      if (tid == 0 && !(total > 0.0)) sh_err |= SPEC_DEV_EMPTY;
-      if (total > 0.0 && excl <= target && target < incl) {
-        double acc = excl;
-        int pick = -1, last = -1;
-        for (int x = x0; x < x1; ++x) {
-          const double w = weight(x);
-          if (w > 0.0) last = x;
-          acc += w;
-          if (acc > target) {
-            pick = x;
-            break;
-          }
+      // final draw at u: inverse CDF of the current weights in index order
+      const bool bonus = (sh_C == 0.0 && sh_nrej == 0);  // no rejection here: the weights are p
+      if (!scanned) {
+        scan_slice(false);
+        if (!bonus) {  // a zero-mass residual left earlier weights in place: publish them
+          buf ^= 1;    // the other buffer: members may still read the last pass's
+          if (tid == kThreads - 1) part[buf * NW + wg] = Rec{0.f, 0, incl};
+          team_barrier(ctr, NW * ++phase, &sh_fail);
+          if (sh_fail) break;
         }
-        sh_emit = pick >= 0 ? pick : last;
+      }
+      if (wave == 0) {
+        double mass = 0.0;
+        if (!bonus || scanned) {
+          if (lane < NW) mass = part[buf * NW + lane].z;
+        } else if (lane < NW) {
+          const Rec r = rows[lane * rstride];
+          if (r.m != -INFINITY) mass = r.z * exp((static_cast<double>(r.m) - m) * a.inv_tau) * iz;
+        }
+        const double inc = wave_incl_scan(mass);
+        double exc = __shfl_up(inc, 1);
+        if (lane == 0) exc = 0.0;
+        const double total = __shfl(inc, 63);
+        const double uu = draw_uniform(a.seed, a.offset, b, u, 1);
+        const double target = uu * total;
+        const bool here = lane < NW && exc <= target && target < inc;
+        const unsigned long long hit = __ballot(here);
+        const unsigned long long nz = __ballot(lane < NW && mass > 0.0);
+        const int owner = hit ? (__ffsll(static_cast<long long>(hit)) - 1)
+                              : (nz ? (63 - __clzll(static_cast<long long>(nz))) : 0);
+        const double lo = __shfl(exc, owner);
+        if (lane == 0) {
+          if (!(total > 0.0)) sh_err |= SPEC_DEV_EMPTY;
+          sh_owner = owner;
+          sh_lo = lo;
+          sh_target = target;
+        }
+      }
+      __syncthreads();
+      if (wg == sh_owner && sh_err == 0) {
+        const double t_lo = sh_lo + excl, t_hi = sh_lo + incl;
+        const double target = sh_target;
+        const bool last_nonempty = i1 > i0 && i1 == n;
+        if ((t_lo <= target && target < t_hi) || (last_nonempty && target >= t_hi)) {
+          double run = t_lo;
+          int pick = -1, lastnz = -1;
+          for (int i = i0; i < i1; ++i) {
+            const double w = weight(i);
+            if (w > 0.0) lastnz = i;
+            run += w;
+            if (run > target) {
+              pick = i;
+              break;
+            }
+          }
+          const int k = pick >= 0 ? pick : lastnz;
+          if (k >= 0) sh_emit_local = v0 + k;
+        }
       }
       __syncthreads();
       break;
     }
   }
   __syncthreads();
+  if (sh_fail && tid == 0) atomicOr(&sh_err, SPEC_DEV_TIMEOUT);
+  __syncthreads();
 
+  // outputs: member 0 writes the path; the member holding the drawn token writes it
+  const int err = sh_err;
+  const int L = err ? 0 : sh_len - 1;
   if (tid == 0) {
     int32_t* acc_b = a.accepted + static_cast<long>(b) * T;
     int32_t* out_b = a.out_tokens + static_cast<long>(b) * T;
-    const int err = sh_err;
-    const int L = err ? 0 : sh_len - 1;
-    for (int i = 0; i < T; ++i) {
-      acc_b[i] = (i <= L) ? (err ? (i == 0 ? 0 : -1) : s_path[i]) : -1;
-      out_b[i] = -1;
+    if (wg == 0) {
+      for (int i = 0; i < T; ++i) {
+        acc_b[i] = (i == 0) ? 0 : ((!err && i <= L) ? s_path[i] : -1);
+        if (err || i != L || a.greedy) out_b[i] = (!err && i < L) ? s_tok[s_path[i + 1]] : -1;
+      }
+      if (!err && a.greedy) out_b[L] = emitted;
+      a.num_accepted[b] = L;
+      report(a.status, b, err);
     }
-    if (!err) {
-      for (int d = 1; d <= L; ++d) out_b[d - 1] = s_tok[s_path[d]];
-      out_b[L] = sh_emit;
+    if (!err && !a.greedy && wg == sh_owner) out_b[L] = sh_emit_local;
+    // leave: the last member out resets the barrier counters for the next call
+    const unsigned prev = atomicAdd(ctr + 1, 1u);
+    if (prev == static_cast<unsigned>(NW - 1)) {
+      atomicExch(ctr, 0u);
+      atomicExch(ctr + 1, 0u);
     }
-    a.num_accepted[b] = L;
-    report(a.status, b, err);
   }
 }
 
 }  // namespace
 
 size_t reject_workspace_bytes(int B, int T, int V) {
-  const int nchunks = (V + kChunk - 1) / kChunk;
-  return static_cast<size_t>(B) * T * nchunks * sizeof(RowStat);
+  const Team t = team_shape(B, T, V);
+  const size_t sync = static_cast<size_t>(B) * kSyncStride * sizeof(unsigned);
+  return sync + static_cast<size_t>(B) * t.NW * (std::max(t.E, 1) + 2) * sizeof(Rec);
 }
 
+size_t reject_workspace_zero_bytes(int B) { return static_cast<size_t>(B) * kSyncStride * sizeof(unsigned); }
+
 hipError_t launch_reject(const RejectLaunch& L, hipStream_t stream) {
-  const int nchunks = (L.V + kChunk - 1) / kChunk;
+  const Team t = team_shape(L.B, L.T, L.V);
   const bool greedy = (L.temperature == 0.0f);
-  const double inv_tau = greedy ? 0.0 : 1.0 / static_cast<double>(L.temperature);
-  RowStat* stats = static_cast<RowStat*>(L.workspace);
-  SArgs s{};
-  s.logits = L.logits;
-  s.stats = stats;
-  s.V = L.V;
-  s.nchunks = nchunks;
-  s.greedy = greedy;
-  s.inv_tau = inv_tau;
-  const long rows = static_cast<long>(L.B) * L.T;
-  hipLaunchKernelGGL(row_stats_kernel, dim3(static_cast<unsigned>(rows * nchunks)), dim3(256), 0, stream, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  WArgs w{};
-  w.logits = L.logits;
-  w.q = L.q;
-  w.tokens = L.tokens;
-  w.parent = L.parent;
-  w.stats = stats;
-  w.accepted = L.accepted;
-  w.out_tokens = L.out_tokens;
-  w.num_accepted = L.num_accepted;
-  w.status = L.status;
-  w.T = L.T;
-  w.V = L.V;
-  w.nchunks = nchunks;
-  w.greedy = greedy;
-  w.wr = L.without_replacement ? 1 : 0;
-  w.inv_tau = inv_tau;
-  w.seed = L.seed;
-  w.offset = L.offset;
-  hipLaunchKernelGGL(walk_kernel, dim3(static_cast<unsigned>(L.B)), dim3(kWalkThreads), 0, stream, w);
+  TArgs a{};
+  a.logits = L.logits;
+  a.q = L.q;
+  a.tokens = L.tokens;
+  a.parent = L.parent;
+  a.accepted = L.accepted;
+  a.out_tokens = L.out_tokens;
+  a.num_accepted = L.num_accepted;
+  a.status = L.status;
+  a.sync = static_cast<unsigned*>(L.workspace);
+  a.eager = reinterpret_cast<Rec*>(static_cast<char*>(L.workspace) + reject_workspace_zero_bytes(L.B));
+  a.part = a.eager + static_cast<size_t>(L.B) * t.NW * std::max(t.E, 1);
+  a.T = L.T;
+  a.V = L.V;
+  a.NW = t.NW;
+  a.S = t.S;
+  a.E = t.E;
+  a.greedy = greedy;
+  a.wr = L.without_replacement ? 1 : 0;
+  a.inv_tau = greedy ? 0.0 : 1.0 / static_cast<double>(L.temperature);
+  a.seed = L.seed;
+  a.offset = L.offset;
+  const dim3 grid(static_cast<unsigned>(L.B * t.NW));
+  if (t.S <= kSliceCap) {
+    hipLaunchKernelGGL(reject_team_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(reject_team_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
