@@ -1,25 +1,28 @@
 // Tree-masked verify attention for few query rows per kv head (<= 64: chains,
 // single-token decode, small trees), bf16, head dim 128.  HBM-bound: the design
-// keeps as many KV bytes in flight as possible.
+// keeps as many KV bytes in flight per CU as LDS allows.
 //
 // Work item = (sequence b, kv head g, split s of the KV pages).  The rows are
 // the T*G (node, query head) pairs of the group (<= 4 blocks of 16).  Each of
-// the 4 waves of a workgroup streams its own 32-key tiles (tiles w, w+4, ...):
-//   * K goes straight from HBM into the A operand of v_mfma_f32_16x16x32_bf16
-//     (lane l holds key l%16, dims c*32 + (l/16)*8 .. +7: 16 contiguous bytes),
-//     giving S^T = K Q^T with 8 scores of one row per lane;
-//   * V is loaded in its natural layout and transposed through a wave-private
-//     LDS region: lane (key k, quad q) writes the pair (V[k][d], V[k+16][d]) as
-//     one 32-bit word, so a row of V^T holds the 32 keys in the order
-//     k, k+16, k+1, k+17, ...; the scores are packed into the PV operand in the
-//     same order, so O^T += V^T P^T needs no other data movement;
-//   * loads for the next DEPTH-1 tiles are issued before a tile is computed.
+// the 4 waves of a workgroup streams its own pages (s*pps + wave + 4k) through
+// a private ring of DEPTH page slots in LDS, filled by direct global->LDS loads
+// (global_load_lds_dwordx4), so prefetch depth costs no registers:
+//   * K lands key-major with its 16-byte chunks XOR-swizzled by the key, so the
+//     A operand of v_mfma_f32_16x16x32_bf16 (lane l: key l%16, dims
+//     c*32 + (l/16)*8 .. +7) is one conflict-free ds_read_b128; S^T = K Q^T
+//     leaves 4 scores of one row per lane (keys 4*(l/16) + i);
+//   * V lands key-major with an even swizzle, and ds_read_b64_tr_b16 (within
+//     16 lanes: out[i][m] = mem[addr[i/4 + 4m] + i%4]) turns it into the A
+//     operand of v_mfma_f32_16x16x16_bf16 for O^T += V^T P^T, whose B operand
+//     is exactly the S^T accumulator layout, so P needs no data movement.
 // Keys at prefix + j are tree nodes, masked by the row's ancestor bits (the
 // tree_mask of "Report: Support nextn speculative decoding", EAGLE
-// implementation summary, step 3).  The four waves merge through LDS; splits
-// write partials (O, m, l) and the last workgroup of a (b, g) to finish merges
-// them (a per-(b, g) arrival counter in the workspace, reset by that
-// workgroup), so the whole call is one launch.
+// implementation summary, step 3); with T <= 64 each node's ancestor set is
+// one 64-bit word, built by pointer doubling across the lanes of a wave.  The
+// four waves merge through LDS; when a (b, g) spans several splits, each
+// writes a partial (O, m, l) and the last one to finish merges them (a
+// per-(b, g) arrival counter in the workspace, reset by that workgroup), so
+// the whole call is one launch.
 #include <algorithm>
 
 #include "common.h"
@@ -28,9 +31,13 @@ namespace spectree {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kVS = 40;  // V^T row stride in LDS, in bf16 slots (32 keys + 8 pad, 80 B)
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kMaxSplitPages = 128;  // pages per split (plan_stream never exceeds it)
+constexpr int kPageBytes = kBlockSize * kD * 2;  // one page of one head: 4 KB
+constexpr int kSlotBytes = 2 * kPageBytes;       // K page, then V page
+constexpr int kMaxWavePages = 64;                // pages per wave and split (one lane holds each block index)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 struct StArgs {
   const uint16_t* q;
@@ -49,54 +56,67 @@ struct StArgs {
   float sl2;
 };
 
-// Orders this wave's LDS writes and reads of the V^T region in program order.
-// The hardware executes one wave's LDS operations in order, so only the
-// compiler has to be kept from moving them across each other; a memory fence
-// here would also wait for the prefetched global loads.
-__device__ __forceinline__ void wave_lds_fence() { __asm__ volatile("" ::: "memory"); }
+// Waits until at most n of this wave's vector-memory operations are in flight.
+// The compiler does not track the LDS side of direct global->LDS loads, so the
+// kernel places these waits itself; the memory clobber keeps LDS accesses on
+// their side of the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds() { __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// parent_b is the LDS copy of the sequence's parent row.
-__device__ int build_ancestors_st(const int* parent_b, int T, uint64_t* anc) {
-  int err = 0;
-  for (int i = threadIdx.x; i < T; i += blockDim.x) {
-    uint64_t w[4] = {0, 0, 0, 0};
-    int j = i;
-    bool ok = true;
-    for (int steps = 0; steps <= T; ++steps) {
-      w[j >> 6] |= 1ull << (j & 63);
-      const int p = parent_b[j];
-      if (j == 0) {
-        ok = (p == -1);
-        break;
-      }
-      if (p < 0 || p >= j) {
-        ok = false;
-        break;
-      }
-      j = p;
+// vmcnt(8 * n): the loads of the n pages issued after the one to be read may stay in flight.
+template <int DEPTH>
+__device__ __forceinline__ void wait_pages_after(int n) {
+  if constexpr (DEPTH >= 4) {
+    if (n >= 3) {
+      wait_vm<24>();
+      return;
     }
-    if (!ok) {
-      err = SPEC_DEV_PARENT;
-      w[0] = w[1] = w[2] = w[3] = 0;
-      w[i >> 6] = 1ull << (i & 63);
-    }
-    for (int k = 0; k < 4; ++k) anc[i * 4 + k] = w[k];
   }
-  return err;
+  if constexpr (DEPTH >= 3) {
+    if (n >= 2) {
+      wait_vm<16>();
+      return;
+    }
+  }
+  if constexpr (DEPTH >= 2) {
+    if (n >= 1) {
+      wait_vm<8>();
+      return;
+    }
+  }
+  wait_vm<0>();
 }
 
-struct TileRegs {
-  u32x4 k[2][4];  // [16-key half][32-dim chunk]
-  u32x4 v[2][4];
-  bool ok[2];     // this lane's key of each half is a real key of the split
-};
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(p)));
+}
+
+// Eight transposed V^T fragments (ds_read_b64_tr_b16 at the given LDS byte
+// addresses), complete on return.  Issued from assembly because the compiler
+// would otherwise drain every in-flight direct global->LDS load before them.
+__device__ __forceinline__ void read_vt(s16x4 (&v)[8], uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t a4,
+                                        uint32_t a5, uint32_t a6, uint32_t a7) {
+  __asm__ volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(a4), "v"(a5), "v"(a6), "v"(a7)
+      : "memory");
+}
 
 template <int NRB, int DEPTH>
 __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t vt_all[4 * kD * kVS];  // 40 KB: 4 waves' V^T, later merge space
-  __shared__ uint64_t anc[kMaxT * 4];
-  __shared__ int s_par[kMaxT];
-  __shared__ int s_blk[kMaxSplitPages];  // block index of each page of this split (-1: invalid)
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4 * DEPTH * kSlotBytes];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
@@ -104,8 +124,9 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int quad = lane >> 4;
-  uint16_t* vt = vt_all + wave * kD * kVS;
 
+  // Consecutive workgroup ids are dealt round-robin to the 8 XCDs; give each
+  // XCD a contiguous run of items.
   const long per = (a.items + 7) / 8;
   const long item = static_cast<long>(blockIdx.x % 8) * per + blockIdx.x / 8;
   if (item >= a.items) return;
@@ -114,35 +135,14 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
   const int g = static_cast<int>(bg % a.Hkv);
   const int b = static_cast<int>(bg / a.Hkv);
 
-  int err = 0;
-  int Lb = a.plen[b];
-  const int cap = a.max_blocks * kBlockSize - a.T;
-  if (Lb < 0 || Lb > cap) {
-    err |= SPEC_DEV_LENGTH;
-    Lb = Lb < 0 ? 0 : cap;
-  }
-  const int n_keys = Lb + a.T;
-  const int npages = (n_keys + kBlockSize - 1) / kBlockSize;
-  const int p0 = s * a.pps;
-  const int p1 = min(npages, p0 + a.pps);
-  const int kend = min(n_keys, p1 * kBlockSize);
-  const int n_tiles = p1 > p0 ? (p1 - p0 + 1) / 2 : 0;
-  const int my_tiles = n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0;
-
-  // the split's block indices and the parent row, staged once: no dependent global loads later
-  const int32_t* bt_b = a.bt + static_cast<long>(b) * a.max_blocks;
-  const bool tail = n_tiles > 0 && kend > Lb;
-  for (int i = tid; i < p1 - p0; i += 256) {
-    const int blk = bt_b[p0 + i];
-    const bool ok = blk >= 0 && blk < a.num_blocks;
-    if (!ok) err |= SPEC_DEV_BLOCK;
-    s_blk[i] = ok ? blk : -1;
-  }
-  if (tail)
-    for (int i = tid; i < a.T; i += 256) s_par[i] = a.parent[static_cast<long>(b) * a.T + i];
-  __syncthreads();
-  if (tail) err |= build_ancestors_st(s_par, a.T, anc);
-  __syncthreads();
+  // Independent prologue loads: prefix length, this wave's block indices (lane
+  // k holds page s*pps + wave + 4k), the parent row (lane = node), the queries.
+  const int plen_raw = a.plen[b];
+  const int wave_pages_max = a.pps / 4;
+  const int pg_lane = s * a.pps + wave + 4 * lane;
+  int blk = -1;
+  if (lane < wave_pages_max && pg_lane < a.max_blocks) blk = a.bt[static_cast<long>(b) * a.max_blocks + pg_lane];
+  const int par = lane < a.T ? a.parent[static_cast<long>(b) * a.T + lane] : -1;
 
   // query fragments: B operand of S^T, Q[row][c*32 + quad*8 .. +7]
   bf16x8 qf[NRB][4];
@@ -162,6 +162,54 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
     }
   }
 
+  int err = 0;
+  int Lb = plen_raw;
+  const int cap = a.max_blocks * kBlockSize - a.T;
+  if (Lb < 0 || Lb > cap) {
+    err |= SPEC_DEV_LENGTH;
+    Lb = Lb < 0 ? 0 : cap;
+  }
+  const int n_keys = Lb + a.T;
+  const int npages = (n_keys + kBlockSize - 1) / kBlockSize;
+  const int n_used = (npages + a.pps - 1) / a.pps;  // splits of this (b, g) that hold keys
+  if (s >= n_used) return;
+  const int p0 = s * a.pps;
+  const int p1 = min(npages, p0 + a.pps);
+  const int kend = min(n_keys, p1 * kBlockSize);
+  const int n_mine = p1 - p0 > wave ? (p1 - p0 - wave + 3) / 4 : 0;
+  {
+    const bool real = lane < n_mine;
+    const bool bad = real && !(blk >= 0 && blk < a.num_blocks);
+    if (__any(bad)) err |= SPEC_DEV_BLOCK;
+    blk = (real && !bad) ? blk : -1;
+  }
+
+  // Ancestor-or-self words by pointer doubling: lane i follows its parent
+  // chain 1, 2, 4, ... steps at a time.  A chain that is not topological (or
+  // whose root has a parent) leaves its nodes with only themselves.
+  uint64_t anc_row[NRB];
+  const bool tail = kend > Lb;
+  if (tail) {
+    const bool in = lane < a.T;
+    const bool valid = in && (lane == 0 ? par == -1 : (par >= 0 && par < lane));
+    int j = (lane == 0 || !valid) ? lane : par;
+    uint64_t A = 1ull << lane;
+    int okc = valid || !in;
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {
+      A |= __shfl(A, j);
+      okc &= __shfl(okc, j);
+      j = __shfl(j, j);
+    }
+    if (__any(in && !okc)) err |= SPEC_DEV_PARENT;
+    if (!okc) A = 1ull << lane;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) anc_row[rb] = __shfl(A, node_of[rb]);
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) anc_row[rb] = 0;
+  }
+
   float m_run[NRB], l_run[NRB];
   f32x4 o[NRB][8];
 #pragma unroll
@@ -172,113 +220,110 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
     for (int dt = 0; dt < 8; ++dt) o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Loads are unconditional so the compiler can count them: a tile past this
-  // wave's range re-reads its last tile, a page past the split its last page
-  // (cache hits); such keys are flagged and masked when the tile is computed.
-  auto load_tile = [&](int j, TileRegs& t) {  // j-th tile of this wave
-    const int tile = wave + 4 * min(j, max(my_tiles - 1, 0));
+  uint8_t* my_ring = ring + wave * DEPTH * kSlotBytes;
+  // Per-lane byte offsets inside a slot.  DMA: instruction t, lane i fills LDS
+  // bytes t*1024 + 16 i = key (4t + i/16), position i%16, which holds chunk
+  // position ^ key of K, position ^ 2*(key % 8) of V.
+  const int dma_key = lane >> 4;
+  const int dma_pos = lane & 15;
+  // K fragment c: key l16, chunk 4c + quad.
+  // V^T fragment dt: key 4*quad + l16/4, dims dt*16 + 4*(l16%4) .. +3.
+  const int vkey = 4 * quad + (l16 >> 2);
+  uint32_t vt_off[8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int page = min(p0 + 2 * tile + h, max(p1 - 1, p0));
-      const int pos = (p0 + 2 * tile + h) * kBlockSize + l16;
-      const int blk = p1 > p0 ? s_blk[page - p0] : -1;
-      t.ok[h] = (j < my_tiles) && (pos < kend) && blk >= 0;
-      const long off = ((static_cast<long>(max(blk, 0)) * a.Hkv + g) * kBlockSize + l16) * kD + quad * 8;
+  for (int dt = 0; dt < 8; ++dt)
+    vt_off[dt] = vkey * 256 + (((2 * dt + ((l16 & 3) >> 1)) ^ (2 * (vkey & 7))) * 16) + (l16 & 1) * 8;
+  auto issue = [&](int k) {  // page k of this wave into slot k % DEPTH; k is wave-uniform
+    const int bk = __builtin_amdgcn_readlane(blk, k);
+    const long base = (static_cast<long>(bk < 0 ? 0 : bk) * a.Hkv + g) * (kBlockSize * kD);
+    uint8_t* slot = my_ring + (k % DEPTH) * kSlotBytes;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        t.k[h][c] = *reinterpret_cast<const u32x4*>(a.k + off + c * 32);
-        t.v[h][c] = *reinterpret_cast<const u32x4*>(a.v + off + c * 32);
-      }
+    for (int t = 0; t < 4; ++t) {
+      const int key = 4 * t + dma_key;
+      const uint16_t* ks = a.k + base + key * kD + ((dma_pos ^ key) * 8);
+      const uint16_t* vs = a.v + base + key * kD + ((dma_pos ^ (2 * (key & 7))) * 8);
+      __builtin_amdgcn_global_load_lds(ks, slot + t * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vs, slot + kPageBytes + t * 1024, 16, 0, 0);
     }
   };
 
-  auto compute_tile = [&](int j, const TileRegs& t) {
-    const int tile = wave + 4 * j;
-    const int key0 = (p0 + 2 * tile) * kBlockSize;  // logical position of this tile's key 0
-    // V^T into this wave's LDS region: word (d, pair k) = (V[k][d], V[k+16][d])
-    wave_lds_fence();
+#pragma unroll
+  for (int k = 0; k < DEPTH; ++k)
+    if (k < n_mine) issue(k);
+
+  for (int k = 0; k < n_mine; ++k) {
+    wait_pages_after<DEPTH>(min(n_mine - 1 - k, DEPTH - 1));
+    uint8_t* slot = my_ring + (k % DEPTH) * kSlotBytes;
+    const int page = p0 + wave + 4 * k;
+    const int key0 = page * kBlockSize;
+    const int bk = __builtin_amdgcn_readlane(blk, k);
+    const int nvalid = bk < 0 ? 0 : min(kBlockSize, kend - key0);
+    if (nvalid < kBlockSize) {
+      // keys past the split (or a whole invalid page): zero their V rows so that
+      // p = 0 never meets a NaN; their scores are masked below
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (4 * t + dma_key >= nvalid)
+          *reinterpret_cast<u32x4*>(slot + kPageBytes + (4 * t + dma_key) * 256 + dma_pos * 16) = u32x4{0, 0, 0, 0};
+    }
+    bf16x8 kf[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t a0 = t.ok[0] ? t.v[0][c][e2] : 0u, a1 = t.ok[1] ? t.v[1][c][e2] : 0u;
-        const uint32_t lo = (a0 & 0xffffu) | (a1 << 16);
-        const uint32_t hi = (a0 >> 16) | (a1 & 0xffff0000u);
-        const int d = c * 32 + quad * 8 + 2 * e2;
-        *reinterpret_cast<uint32_t*>(&vt[d * kVS + 2 * l16]) = lo;
-        *reinterpret_cast<uint32_t*>(&vt[(d + 1) * kVS + 2 * l16]) = hi;
-      }
-    wave_lds_fence();
-    const bool need_mask = key0 + 32 > Lb || key0 + 32 > kend;
-    bf16x8 pf[NRB];
+      kf[c] = __builtin_bit_cast(bf16x8,
+                                 *reinterpret_cast<const u32x4*>(slot + l16 * 256 + (((4 * c + quad) ^ l16) * 16)));
+    s16x4 vf[8];
+    {
+      const uint32_t vb = lds_addr(slot + kPageBytes);
+      read_vt(vf, vb + vt_off[0], vb + vt_off[1], vb + vt_off[2], vb + vt_off[3], vb + vt_off[4], vb + vt_off[5],
+              vb + vt_off[6], vb + vt_off[7]);
+    }
+    wait_lds();  // the slot is in registers: refill it
+    if (k + DEPTH < n_mine) issue(k + DEPTH);
+
+    const bool need_mask = nvalid < kBlockSize || key0 + kBlockSize > Lb;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int c = 0; c < 4; ++c) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], qf[rb][c], sacc, 0, 0, 0);
+      // lane holds S[row l16][key 4*quad + i]
+      float sv[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[h][c]), qf[rb][c], sacc[h],
-                                                            0, 0, 0);
-      // lane holds S[row l16][key h*16 + quad*4 + i]; PV slot j <-> (h = j % 2, i = j / 2)
-      float sv[8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = sacc[h][i] * a.sl2;
-          if (need_mask) {
-            const int pos = key0 + h * 16 + quad * 4 + i;
-            bool ok = pos < kend;
-            if (ok && pos >= Lb) {
-              const int jj = pos - Lb;
-              ok = (anc[node_of[rb] * 4 + (jj >> 6)] >> (jj & 63)) & 1ull;
-            }
-            x = ok ? x : -INFINITY;
-          }
-          sv[2 * i + h] = x;
+      for (int i = 0; i < 4; ++i) {
+        float x = sacc[i] * a.sl2;
+        if (need_mask) {
+          const int kin = 4 * quad + i;
+          const int pos = key0 + kin;
+          bool ok = kin < nvalid;
+          if (ok && pos >= Lb) ok = (anc_row[rb] >> (pos - Lb)) & 1ull;
+          x = ok ? x : -INFINITY;
         }
-      float mx = sv[0];
-#pragma unroll
-      for (int j2 = 1; j2 < 8; ++j2) mx = fmaxf(mx, sv[j2]);
+        sv[i] = x;
+      }
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run[rb], mx);
       const bool none = (m_new == -INFINITY);
-      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+      bf16x4 pb;
       float psum = 0.f;
 #pragma unroll
-      for (int j2 = 0; j2 < 8; ++j2) {
-        const float p = none ? 0.f : __builtin_amdgcn_exp2f(sv[j2] - m_new);
+      for (int i = 0; i < 4; ++i) {
+        const float p = none ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_new);
         psum += p;
-        pf[rb][j2] = static_cast<__bf16>(p);
+        pb[i] = static_cast<__bf16>(p);
       }
-      l_run[rb] = l_run[rb] * alpha + psum;
+      if (!__all(m_new == m_run[rb])) {  // the running max moved somewhere in the wave: rescale
+        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[rb][dt] *= alpha;
+      }
+      l_run[rb] += psum;
       m_run[rb] = m_new;
+      const s16x4 pf = __builtin_bit_cast(s16x4, pb);
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[rb][dt] *= alpha;
-    }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const bf16x8 vf =
-          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&vt[(dt * 16 + l16) * kVS + quad * 8]));
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) o[rb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb], o[rb][dt], 0, 0, 0);
-    }
-  };
-
-  // software pipeline: DEPTH tiles in flight per wave
-  TileRegs buf[DEPTH];
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load_tile(d, buf[d]);
-  for (int j0 = 0; j0 < my_tiles; j0 += DEPTH) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int j = j0 + d;
-      if (j < my_tiles) {
-        compute_tile(j, buf[d]);
-        load_tile(j + DEPTH, buf[d]);
-      }
+      for (int dt = 0; dt < 8; ++dt) o[rb][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[dt], pf, o[rb][dt], 0, 0, 0);
     }
   }
 #pragma unroll
@@ -288,12 +333,12 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
   }
   report(a.status, b, err);
 
-  // merge the four waves, 16 rows at a time, through LDS
-  float* mo = reinterpret_cast<float*>(vt_all);  // [4][16][128]
-  float* ml = mo + 4 * 16 * kD;                  // [4][16][2]
+  // merge the four waves, 16 rows at a time, through LDS (the rings are drained)
+  float* mo = reinterpret_cast<float*>(ring);  // [4][16][128]
+  float* ml = mo + 4 * 16 * kD;                // [4][16][2]
   const int row = tid >> 4;
   const int dseg = (tid & 15) * 8;
-  const bool direct = a.splits == 1;
+  const bool direct = n_used == 1;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     __syncthreads();
@@ -343,12 +388,12 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
   }
   if (direct) return;
 
-  // the last workgroup of (b, g) to arrive merges every split
+  // the last of the n_used workgroups of (b, g) to arrive merges their partials
   __syncthreads();
   if (tid == 0) {
     __threadfence();
     const unsigned prev = atomicAdd(&a.counters[bg], 1u);
-    s_last = (prev == static_cast<unsigned>(a.splits - 1));
+    s_last = (prev == static_cast<unsigned>(n_used - 1));
     if (s_last) __threadfence();
   }
   __syncthreads();
@@ -358,7 +403,7 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
   for (int r = row; r < a.R; r += 16) {
     // online merge over the splits, 8 partials' loads in flight at a time
     float mstar = -INFINITY, lstar = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int sp0 = 0; sp0 < a.splits; sp0 += 8) {
+    for (int sp0 = 0; sp0 < n_used; sp0 += 8) {
       float ms[8], ls[8];
       f32x4 x0[8], x1[8];
 #pragma unroll
@@ -366,7 +411,7 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
         ms[k] = -INFINITY;
         ls[k] = 0.f;
         x0[k] = x1[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (sp0 + k < a.splits) {
+        if (sp0 + k < n_used) {
           const long it = first + sp0 + k;
           ms[k] = a.part_ml[(it * a.R + r) * 2];
           ls[k] = a.part_ml[(it * a.R + r) * 2 + 1];
@@ -409,23 +454,57 @@ hipError_t run_stream(const StArgs& args, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int DEPTH>
+hipError_t run_stream_rows(int nrb, const StArgs& args, hipStream_t stream) {
+  switch (nrb) {
+    case 1:
+      return run_stream<1, DEPTH>(args, stream);
+    case 2:
+      return run_stream<2, DEPTH>(args, stream);
+    case 3:
+      return run_stream<3, DEPTH>(args, stream);
+    default:
+      return run_stream<4, DEPTH>(args, stream);
+  }
+}
+
 }  // namespace
 
 // Plan for the streaming kernel: rows <= 64 per (b, g).  Pages per split are a
-// multiple of 8 (one 32-key tile per wave and round); a workgroup holds a whole
-// CU (one wave per SIMD), so small problems aim for one split per CU; at most
-// 128 pages (2048 keys) per split keeps ragged batches balanced.
+// multiple of 4 (one page per wave and round), at most 4 * 64.  A workgroup
+// with DEPTH slots per wave holds 4 * DEPTH * 8 KB of LDS, so 160 KB fits
+// 160 / (32 DEPTH) of them per CU; the split size minimises the estimated
+// makespan: rounds of resident workgroups times (pages per wave + a fixed cost
+// of a few pages' time for the prologue latency and the merge).
+#ifndef SPEC_STREAM_DEPTH
+#define SPEC_STREAM_DEPTH 4
+#endif
+#ifndef SPEC_STREAM_OVERHEAD_PAGES
+#define SPEC_STREAM_OVERHEAD_PAGES 3
+#endif
 void plan_stream(AttnPlan& p, int B, int Hkv, int max_blocks) {
   p.mode = 3;
   p.rt = p.rows;
   p.nrb = (p.rows + 15) / 16;
   p.n_rt = 1;
+  p.depth = SPEC_STREAM_DEPTH;
   const long bg = static_cast<long>(B) * Hkv;
-  long pps = (static_cast<long>(max_blocks) * bg + 255) / 256;
-  pps = std::max<long>(8, std::min<long>(128, pps));
-  pps = (pps + 7) / 8 * 8;
-  p.pps = static_cast<int>(pps);
-  p.splits = static_cast<int>((max_blocks + pps - 1) / pps);
+  const long per_cu = std::max(1, 160 / (32 * p.depth));
+  const long slots = 256 * per_cu;
+  long best_pps = 4 * kMaxWavePages;
+  double best = 1e30;
+  for (long pps = 4; pps <= 4 * kMaxWavePages; pps += 4) {
+    const long splits = (max_blocks + pps - 1) / pps;
+    const long items = bg * splits;
+    const long rounds = (items + slots - 1) / slots;
+    const double cost = static_cast<double>(rounds) * (static_cast<double>(pps) / 4 + SPEC_STREAM_OVERHEAD_PAGES);
+    if (cost < best - 1e-9) {
+      best = cost;
+      best_pps = pps;
+    }
+  }
+  p.pps = static_cast<int>(best_pps);
+  p.splits = static_cast<int>((max_blocks + best_pps - 1) / best_pps);
   p.items = bg * p.splits;
   const size_t head = (static_cast<size_t>(bg) * sizeof(unsigned) + 255) / 256 * 256;
   p.ws_bytes = p.splits > 1 ? head + static_cast<size_t>(p.items) * p.rows * (kD + 2) * sizeof(float) : 0;
@@ -460,15 +539,13 @@ hipError_t launch_attn_stream(const AttnPlan& plan, const AttnLaunch& L, hipStre
     a.part_o = reinterpret_cast<float*>(static_cast<char*>(L.workspace) + head);
     a.part_ml = a.part_o + static_cast<size_t>(plan.items) * plan.rows * kD;
   }
-  switch (plan.nrb) {
-    case 1:
-      return run_stream<1, 3>(a, stream);
+  switch (plan.depth) {
     case 2:
-      return run_stream<2, 2>(a, stream);
+      return run_stream_rows<2>(plan.nrb, a, stream);
     case 3:
-      return run_stream<3, 1>(a, stream);
+      return run_stream_rows<3>(plan.nrb, a, stream);
     default:
-      return run_stream<4, 1>(a, stream);
+      return run_stream_rows<4>(plan.nrb, a, stream);
   }
 }
 

@@ -48,6 +48,7 @@ struct AttnPlan {
   int splits;     // KV splits per (sequence, kv head)
   int pps;        // pages per split
   long items;     // workgroups of the main kernel (before XCD padding)
+  int depth;      // streaming kernel: page slots per wave
   size_t ws_bytes;
 };
 

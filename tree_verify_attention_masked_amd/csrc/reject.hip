@@ -191,64 +191,141 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
   return v;
 }
 
-// Statistics of up to kMaxEager rows whose slices are rows[r * stride + i], i < n.
+// Statistics of up to R rows whose slices are rows[r * stride + i], i < n:
+// slice max, its first index (-1 if the slice holds NaN or +inf) and the sum of
+// exp((l - max) / t).  The rows are reduced side by side, so each shuffle step
+// waits once for all of them.
+template <int R>
 __device__ __forceinline__ void slice_stats_rows(const float* rows, int stride, int nrows, int n, int v0, bool greedy,
-                                 double inv_tau, Rec* out, float* redm, int* redi, double* redz) {
+                                                 double inv_tau, Rec* out, float* redm, int* redi, double* redz) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int r = 0; r < nrows; ++r) {
-    float mx = -INFINITY;
-    int ix = 0x7fffffff;
-    bool bad = false;
-    for (int i = tid; i < n; i += kThreads) {
-      const float v = rows[r * stride + i];
-      bad |= bad_logit(v);
-      if (v > mx) {
-        mx = v;
-        ix = v0 + i;
+  float mx[R];
+  int ix[R];
+  bool bad[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    mx[r] = -INFINITY;
+    ix[r] = 0x7fffffff;
+    bad[r] = false;
+  }
+  for (int i = tid; i < n; i += kThreads) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r < nrows) {
+        const float v = rows[r * stride + i];
+        bad[r] |= bad_logit(v);
+        if (v > mx[r]) {
+          mx[r] = v;
+          ix[r] = v0 + i;
+        }
       }
-    }
-    wave_argmax(mx, ix);
-    bad = __any(bad);
-    if (lane == 0) {
-      redm[r * kWaves + wave] = mx;
-      redi[r * kWaves + wave] = bad ? -1 : ix;
     }
   }
-  __syncthreads();
-  for (int r = 0; r < nrows; ++r) {
-    float m = redm[r * kWaves];
-    int idx = redi[r * kWaves];
-    bool anybad = idx < 0;
-    for (int w = 1; w < kWaves; ++w) {
-      const float om = redm[r * kWaves + w];
-      const int oi = redi[r * kWaves + w];
-      anybad |= oi < 0;
-      if (om > m || (om == m && oi < idx)) {
-        m = om;
-        idx = oi;
-      }
-    }
-    double z = 0.0;
-    if (!greedy && m != -INFINITY && !anybad) {
-      const double md = static_cast<double>(m);
-      for (int i = tid; i < n; i += kThreads) z += exp((static_cast<double>(rows[r * stride + i]) - md) * inv_tau);
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    float om[R];
+    int oi[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      om[r] = __shfl_xor(mx[r], w);
+      oi[r] = __shfl_xor(ix[r], w);
     }
 #pragma unroll
-    for (int w = 32; w >= 1; w >>= 1) z += __shfl_xor(z, w);
-    if (lane == 0) redz[r * kWaves + wave] = z;
-    if (tid == 0) {
-      out[r].m = m;
-      out[r].idx = anybad ? -1 : (idx == 0x7fffffff ? v0 : idx);
+    for (int r = 0; r < R; ++r)
+      if (om[r] > mx[r] || (om[r] == mx[r] && oi[r] < ix[r])) {
+        mx[r] = om[r];
+        ix[r] = oi[r];
+      }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool anyb = __any(bad[r]);
+    if (lane == 0 && r < nrows) {
+      redm[r * kWaves + wave] = mx[r];
+      redi[r * kWaves + wave] = anyb ? -1 : ix[r];
     }
   }
   __syncthreads();
-  if (tid == 0)
-    for (int r = 0; r < nrows; ++r) {
-      double t = 0.0;
-      for (int w = 0; w < kWaves; ++w) t += redz[r * kWaves + w];
-      out[r].z = t;
+  float m[R];
+  double z[R];
+  bool live[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m[r] = -INFINITY;
+    int idx = 0x7fffffff;
+    bool anybad = false;
+    if (r < nrows) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float om = redm[r * kWaves + w];
+        const int oi = redi[r * kWaves + w];
+        anybad |= oi < 0;
+        if (w == 0 || om > m[r] || (om == m[r] && oi < idx)) {
+          m[r] = om;
+          idx = oi;
+        }
+      }
+      if (tid == 0) {
+        out[r].m = m[r];
+        out[r].idx = anybad ? -1 : (idx == 0x7fffffff ? v0 : idx);
+      }
     }
+    live[r] = r < nrows && !greedy && m[r] != -INFINITY && !anybad;
+    z[r] = 0.0;
+  }
+  for (int i = tid; i < n; i += kThreads) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (live[r]) z[r] += exp((static_cast<double>(rows[r * stride + i]) - static_cast<double>(m[r])) * inv_tau);
+  }
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    double oz[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) oz[r] = __shfl_xor(z[r], w);
+#pragma unroll
+    for (int r = 0; r < R; ++r) z[r] += oz[r];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < nrows) redz[r * kWaves + wave] = z[r];
+  }
   __syncthreads();
+  if (tid < nrows) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += redz[tid * kWaves + w];
+    out[tid].z = t;
+  }
+  __syncthreads();
+}
+
+// Merges the members' statistics of one row in one wave (lane w < NW holds
+// member w's record): max logit, first argmax, 1/z with z summed in member order,
+// error bits, and each member's share of p (slice mass of p, for a draw from p).
+__device__ __forceinline__ void merge_row(const Rec& r, bool member, bool greedy, double inv_tau, float* m_out,
+                                          double* iz_out, int* arg_out, int* err_out, double* mass_out) {
+  const int lane = threadIdx.x & 63;
+  const bool badr = member && r.idx < 0;
+  float m = r.m;
+  int arg = badr ? 0x7fffffff : r.idx;
+  wave_argmax(m, arg);
+  double zl = 0.0;
+  if (!greedy && member && r.m != -INFINITY) zl = r.z * exp((static_cast<double>(r.m) - m) * inv_tau);
+  const double zt = __shfl(wave_incl_scan(zl), 63);  // member-order sum
+  const bool anybad = __any(badr);
+  const double iz = 1.0 / zt;
+  if (member) mass_out[lane] = greedy ? 0.0 : zl * iz;
+  if (lane == 0) {
+    int err = 0;
+    if (anybad) err |= SPEC_DEV_NONFINITE;
+    if (!greedy && !(zt > 0.0)) err |= SPEC_DEV_EMPTY;
+    *err_out = err;
+    *m_out = m;
+    *iz_out = iz;
+    *arg_out = arg;
+  }
 }
 
 // kFits: the slice (S <= kSliceCap floats) lives in LDS, so every slice access is an
@@ -262,11 +339,17 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   __shared__ int s_par[kMaxT], s_tok[kMaxT], s_path[kMaxT];
   __shared__ float s_lx[kMaxT], s_qx[kMaxT];  // logit / draft prob of node c's token in its parent's row
   __shared__ int rej_tok[kMaxT];
+  __shared__ double s_ru[kMaxT], s_fu[kMaxT];  // accept draw of node c, final draw at node u
   __shared__ double rej_c[kMaxT];
   __shared__ float redm[kMaxEager * kWaves];
   __shared__ int redi[kMaxEager * kWaves];
   __shared__ double redz[kMaxEager * kWaves];
   __shared__ Rec s_rec[kMaxEager];
+  // merged statistics of the eager rows (index r < E) and of the current deeper row (index kMaxEager)
+  __shared__ float e_m[kMaxEager + 1];
+  __shared__ double e_iz[kMaxEager + 1];
+  __shared__ int e_arg[kMaxEager + 1], e_err[kMaxEager + 1];
+  __shared__ double e_mass[(kMaxEager + 1) * kMaxTeam];  // each member's share of p
   __shared__ double sh_incl[kWaves];
   __shared__ int sh_err, sh_fail, sh_len, sh_u, sh_c, sh_x, sh_state, sh_nrej, sh_emit_local, sh_owner, sh_arg;
   __shared__ double sh_m, sh_iz, sh_C, sh_Cold, sh_N, sh_s, sh_lo, sh_target, sh_total;
@@ -293,25 +376,8 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
     s_par[i] = a.parent[static_cast<long>(b) * T + i];
     s_tok[i] = a.tokens[static_cast<long>(b) * T + i];
   }
-  __syncthreads();
   if (tid == 0) {
-    int err = 0;
-    for (int i = 0; i < T; ++i) {
-      first_child[i] = -1;
-      next_sib[i] = -1;
-    }
-    if (s_par[0] != -1) err |= SPEC_DEV_PARENT;
-    for (int i = T - 1; i >= 1; --i) {  // prepend in decreasing order: child lists come out increasing
-      const int p = s_par[i];
-      if (p < 0 || p >= i) {
-        err |= SPEC_DEV_PARENT;
-        continue;
-      }
-      if (s_tok[i] < 0 || s_tok[i] >= V) err |= SPEC_DEV_TOKEN;
-      next_sib[i] = first_child[p];
-      first_child[p] = static_cast<int16_t>(i);
-    }
-    sh_err = err;
+    sh_err = 0;
     sh_fail = 0;
     sh_len = 1;
     s_path[0] = 0;
@@ -319,6 +385,32 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
     sh_nrej = 0;
     sh_emit_local = -1;
     sh_owner = 0;
+  }
+  __syncthreads();
+  // child lists (increasing order) and checks, one node per thread: first_child[i]
+  // is the first c > i whose parent is i, next_sib[i] the first c > i sharing
+  // i's parent
+  {
+    int err = 0;
+    for (int i = tid; i < T; i += kThreads) {
+      const int p = s_par[i];
+      const bool ok = (i == 0) ? p == -1 : (p >= 0 && p < i);
+      if (!ok) err |= SPEC_DEV_PARENT;
+      if (i > 0 && ok && (s_tok[i] < 0 || s_tok[i] >= V)) err |= SPEC_DEV_TOKEN;
+      int fc = -1, ns = -1;
+      for (int c = i + 1; c < T && (fc < 0 || (ns < 0 && ok && i > 0)); ++c) {
+        const int pc = s_par[c];
+        if (fc < 0 && pc == i) fc = c;
+        if (ns < 0 && ok && i > 0 && pc == p) ns = c;
+      }
+      first_child[i] = static_cast<int16_t>(fc);
+      next_sib[i] = static_cast<int16_t>(ok ? ns : -1);
+      if (!a.greedy) {
+        s_ru[i] = draw_uniform(a.seed, a.offset, b, i, 0);
+        s_fu[i] = draw_uniform(a.seed, a.offset, b, i, 1);
+      }
+    }
+    if (err) atomicOr(&sh_err, err);
   }
   __syncthreads();
 
@@ -333,9 +425,26 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
     if (kFits && E > 0) {
       stage_rows(eager_l, lg_b + v0, V, E, n);
       __syncthreads();
-      slice_stats_rows(eager_l, n, E, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+      slice_stats_rows<kMaxEager>(eager_l, n, E, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
       if (tid < E) eager[wg * E + tid] = s_rec[tid];
       team_barrier(ctr, NW * ++phase, &sh_fail);
+      // merge every eager row at once (wave w: rows w and w + 4), member order
+      if (!sh_fail) {
+        Rec rr[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = wave + h * kWaves;
+          rr[h] = Rec{-INFINITY, 0x7fffffff, 0.0};
+          if (r < E && lane < NW) rr[h] = eager[lane * E + r];
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = wave + h * kWaves;
+          if (r < E) merge_row(rr[h], lane < NW, a.greedy, a.inv_tau, &e_m[r], &e_iz[r], &e_arg[r], &e_err[r],
+                               &e_mass[r * kMaxTeam]);
+        }
+      }
+      __syncthreads();
     }
 
     for (;;) {  // one iteration per visited node
@@ -359,46 +468,33 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         cq = q_b + static_cast<long>(u) * V + v0;
       }
       __syncthreads();
-      const Rec* rows = eager + u;
-      int rstride = E;
+      const Rec* rows = part;  // members' statistics of a row past the eager ones
       if (u >= E) {  // a deeper row: its statistics now
-        slice_stats_rows(cl, 0, 1, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+        slice_stats_rows<1>(cl, 0, 1, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
         if (tid == 0) part[buf * NW + wg] = s_rec[0];
         team_barrier(ctr, NW * ++phase, &sh_fail);
         if (sh_fail) break;
         rows = part + buf * NW;
-        rstride = 1;
         buf ^= 1;
-      }
-      // merge the members' statistics: one wave, member order
-      if (wave == 0) {
-        Rec r;
-        r.m = -INFINITY;
-        r.idx = 0x7fffffff;
-        r.z = 0.0;
-        if (lane < NW) r = rows[lane * rstride];
-        const bool badr = lane < NW && r.idx < 0;
-        float m = r.m;
-        int arg = badr ? 0x7fffffff : r.idx;
-        wave_argmax(m, arg);
-        double zt = 0.0;
-        if (!a.greedy && lane < NW && r.m != -INFINITY) zt = r.z * exp((static_cast<double>(r.m) - m) * a.inv_tau);
-        zt = wave_incl_scan(zt);  // lane 63 holds the member-order sum
-        const bool anybad = __any(badr);
-        if (lane == 63) {
-          int err = 0;
-          if (anybad) err |= SPEC_DEV_NONFINITE;
-          if (!a.greedy && !(zt > 0.0)) err |= SPEC_DEV_EMPTY;
-          sh_err |= err;
-          sh_m = m;
-          sh_iz = 1.0 / zt;
-          sh_arg = arg;
-          sh_C = 0.0;
-          sh_N = 1.0;
-          sh_s = 1.0;
-          sh_nrej = 0;
-          sh_c = first_child[u];
+        if (wave == 0) {
+          Rec r = Rec{-INFINITY, 0x7fffffff, 0.0};
+          if (lane < NW) r = rows[lane];
+          merge_row(r, lane < NW, a.greedy, a.inv_tau, &e_m[kMaxEager], &e_iz[kMaxEager], &e_arg[kMaxEager],
+                    &e_err[kMaxEager], &e_mass[kMaxEager * kMaxTeam]);
         }
+        __syncthreads();
+      }
+      const int er = u < E ? u : kMaxEager;  // this row's merged statistics
+      if (tid == 0) {
+        sh_err |= e_err[er];
+        sh_m = e_m[er];
+        sh_iz = e_iz[er];
+        sh_arg = e_arg[er];
+        sh_C = 0.0;
+        sh_N = 1.0;
+        sh_s = 1.0;
+        sh_nrej = 0;
+        sh_c = first_child[u];
       }
       __syncthreads();
       if (sh_err) break;
@@ -468,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
             const double cx = removed ? rej_c[k] : sh_C;
             const double pt = fmax(px - cx * qx, 0.0) / sh_N;
             const double qt = removed ? 0.0 : sh_s * qx;
-            const double r = draw_uniform(a.seed, a.offset, b, c, 0);
+            const double r = s_ru[c];
             sh_x = x;
             if (r * qt < pt) {
               sh_state = 1;  // accept
@@ -547,14 +643,13 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         if (!bonus || scanned) {
           if (lane < NW) mass = part[buf * NW + lane].z;
         } else if (lane < NW) {
-          const Rec r = rows[lane * rstride];
-          if (r.m != -INFINITY) mass = r.z * exp((static_cast<double>(r.m) - m) * a.inv_tau) * iz;
+          mass = e_mass[er * kMaxTeam + lane];
         }
         const double inc = wave_incl_scan(mass);
         double exc = __shfl_up(inc, 1);
         if (lane == 0) exc = 0.0;
         const double total = __shfl(inc, 63);
-        const double uu = draw_uniform(a.seed, a.offset, b, u, 1);
+        const double uu = s_fu[u];
         const double target = uu * total;
         const bool here = lane < NW && exc <= target && target < inc;
         const unsigned long long hit = __ballot(here);
