@@ -114,6 +114,18 @@ __device__ __forceinline__ void read_vt(s16x4 (&v)[8], uint32_t a0, uint32_t a1,
       : "memory");
 }
 
+// Split partials cross workgroups (and XCDs, whose L2s are not coherent with
+// each other).  They are written and read as relaxed agent-scope atomics
+// (write-through stores, coherent loads), so publishing them needs only this
+// wave's stores to have completed before the arrival counter is bumped -- no
+// write-back or invalidation of the whole L2, which a fence would cost.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int NRB, int DEPTH>
 __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[4 * DEPTH * kSlotBytes];
@@ -377,11 +389,11 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
         *reinterpret_cast<u32x4*>(op) = u32x4{wds[0], wds[1], wds[2], wds[3]};
       } else {
         float* po = a.part_o + (item * a.R + r) * kD + dseg;
-        *reinterpret_cast<f32x4*>(po) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-        *reinterpret_cast<f32x4*>(po + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st_agent(po + e, acc[e]);
         if ((tid & 15) == 0) {
-          a.part_ml[(item * a.R + r) * 2 + 0] = mstar;
-          a.part_ml[(item * a.R + r) * 2 + 1] = lstar;
+          st_agent(&a.part_ml[(item * a.R + r) * 2 + 0], mstar);
+          st_agent(&a.part_ml[(item * a.R + r) * 2 + 1], lstar);
         }
       }
     }
@@ -389,16 +401,14 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
   if (direct) return;
 
   // the last of the n_used workgroups of (b, g) to arrive merges their partials
+  wait_vm<0>();  // this wave's partial stores have reached the coherent level
   __syncthreads();
   if (tid == 0) {
-    __threadfence();
-    const unsigned prev = atomicAdd(&a.counters[bg], 1u);
+    const unsigned prev = __hip_atomic_fetch_add(&a.counters[bg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == static_cast<unsigned>(n_used - 1));
-    if (s_last) __threadfence();
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   const long first = bg * a.splits;
   for (int r = row; r < a.R; r += 16) {
     // online merge over the splits, 8 partials' loads in flight at a time
@@ -413,11 +423,14 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
         x0[k] = x1[k] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (sp0 + k < n_used) {
           const long it = first + sp0 + k;
-          ms[k] = a.part_ml[(it * a.R + r) * 2];
-          ls[k] = a.part_ml[(it * a.R + r) * 2 + 1];
+          ms[k] = ld_agent(&a.part_ml[(it * a.R + r) * 2]);
+          ls[k] = ld_agent(&a.part_ml[(it * a.R + r) * 2 + 1]);
           const float* po = a.part_o + (it * a.R + r) * kD + dseg;
-          x0[k] = *reinterpret_cast<const f32x4*>(po);
-          x1[k] = *reinterpret_cast<const f32x4*>(po + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x0[k][e] = ld_agent(po + e);
+            x1[k][e] = ld_agent(po + 4 + e);
+          }
         }
       }
 #pragma unroll
@@ -444,7 +457,7 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
       wds[e] = f32_to_bf16(acc[2 * e] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * e + 1] * inv)) << 16);
     *reinterpret_cast<u32x4*>(op) = u32x4{wds[0], wds[1], wds[2], wds[3]};
   }
-  if (tid == 0) atomicExch(&a.counters[bg], 0u);
+  if (tid == 0) __hip_atomic_store(&a.counters[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int NRB, int DEPTH>

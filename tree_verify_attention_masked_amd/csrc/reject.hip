@@ -55,7 +55,7 @@ struct Rec {
 };
 
 struct Team {
-  int NW, S, E;
+  int NW, S, ld, E;  // members, slice length, LDS row stride (S rounded up to 4), eager rows (0, 1, 2, 4 or 8)
 };
 
 Team team_shape(int B, int T, int V) {
@@ -64,12 +64,10 @@ Team team_shape(int B, int T, int V) {
   nw = std::min(nw, std::max(1, (V + 511) / 512));
   t.NW = nw;
   t.S = (V + nw - 1) / nw;
-  t.E = std::min(T, kMaxEager);
-  if (t.S > kEagerCap) {
-    t.E = 0;
-  } else {
-    t.E = std::min(t.E, kEagerCap / t.S);
-  }
+  t.ld = (t.S + 3) & ~3;
+  int e = std::min(T, kMaxEager);
+  e = t.ld > kEagerCap ? 0 : std::min(e, kEagerCap / t.ld);
+  t.E = e >= 8 ? 8 : e >= 4 ? 4 : e >= 2 ? 2 : e;
   return t;
 }
 
@@ -119,7 +117,7 @@ struct TArgs {
   unsigned* sync;  // [B][kSyncStride]: arrive counter, exit counter
   Rec* eager;      // [B][NW][max(E,1)]
   Rec* part;       // [B][2][NW]
-  int T, V, NW, S, E, greedy, wr;
+  int T, V, NW, S, ld, E, greedy, wr;
   double inv_tau;
   uint64_t seed, offset;
 };
@@ -143,19 +141,23 @@ __device__ __forceinline__ void team_barrier(unsigned* ctr, unsigned target, int
   __syncthreads();
 }
 
-// Copy rows [r * src_stride + i], r < nrows, i < n (nrows * n <= 32 * kThreads) of global
-// memory into LDS dst[r * n + i].  Every load of a thread is issued before its first
+// Copy rows [r * src_stride + i], r < nrows, i < n (nrows * n <= 32 * kThreads) of
+// global memory into LDS dst[r * ld + i], from one or two sources (the second
+// only if src2 is set).  Every load of a thread is issued before its first
 // store, so the copy costs one memory latency.
-__device__ __forceinline__ void stage_rows(float* dst, const float* src, long src_stride, int nrows, int n) {
+__device__ __forceinline__ void stage_rows(float* dst, const float* src, float* dst2, const float* src2, int ld,
+                                           long src_stride, int nrows, int n) {
   constexpr int kB = 32;
   const int cnt = nrows * n;
   if (cnt <= 0) return;
   const int tid = threadIdx.x;
-  float v[kB];
+  float v[kB], v2[kB];
+  int off_s[kB], off_d[kB];
   int r = tid / n, i = tid - (tid / n) * n;
 #pragma unroll
   for (int k = 0; k < kB; ++k) {
-    v[k] = (k * kThreads + tid < cnt) ? src[r * src_stride + i] : 0.f;
+    off_s[k] = static_cast<int>(r * src_stride) + i;
+    off_d[k] = r * ld + i;
     i += kThreads;
     while (i >= n) {
       i -= n;
@@ -163,8 +165,32 @@ __device__ __forceinline__ void stage_rows(float* dst, const float* src, long sr
     }
   }
 #pragma unroll
+  for (int k = 0; k < kB; ++k) {
+    const bool in = k * kThreads + tid < cnt;
+    v[k] = in ? src[off_s[k]] : 0.f;
+    v2[k] = (in && src2) ? src2[off_s[k]] : 0.f;
+  }
+#pragma unroll
   for (int k = 0; k < kB; ++k)
-    if (k * kThreads + tid < cnt) dst[k * kThreads + tid] = v[k];
+    if (k * kThreads + tid < cnt) {
+      dst[off_d[k]] = v[k];
+      if (src2) dst2[off_d[k]] = v2[k];
+    }
+}
+
+// Four consecutive slice elements at p (16-byte aligned in LDS); from global
+// memory only the first `valid` are read.
+template <bool kLds>
+__device__ __forceinline__ f32x4 load4(const float* p, int valid) {
+  if constexpr (kLds) {
+    return *reinterpret_cast<const f32x4*>(p);
+  } else {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < valid) v[e] = p[e];
+    return v;
+  }
 }
 
 // Max with the lowest index on ties, over the 64 lanes of a wave.
@@ -191,14 +217,17 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
   return v;
 }
 
-// Statistics of up to R rows whose slices are rows[r * stride + i], i < n:
-// slice max, its first index (-1 if the slice holds NaN or +inf) and the sum of
-// exp((l - max) / t).  The rows are reduced side by side, so each shuffle step
-// waits once for all of them.
-template <int R>
-__device__ __forceinline__ void slice_stats_rows(const float* rows, int stride, int nrows, int n, int v0, bool greedy,
-                                                 double inv_tau, Rec* out, float* redm, int* redi, double* redz) {
+// Statistics of R rows whose slices are rows[r * ld + i], i < n: slice max, its
+// first index (-1 if the slice holds NaN or +inf) and the sum of
+// exp((l - max) / t).  Each thread takes a contiguous run of 4-element chunks;
+// the rows are reduced side by side, so each shuffle step waits once for all.
+template <int R, bool kLds>
+__device__ __forceinline__ void slice_stats_rows(const float* rows, int ld, int n, int v0, bool greedy, double inv_tau,
+                                                 Rec* out, float* redm, int* redi, double* redz) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nc = (n + 3) >> 2;
+  const int per = (nc + kThreads - 1) / kThreads;
+  const int c0 = min(nc, tid * per), c1 = min(nc, c0 + per);
   float mx[R];
   int ix[R];
   bool bad[R];
@@ -208,18 +237,22 @@ __device__ __forceinline__ void slice_stats_rows(const float* rows, int stride, 
     ix[r] = 0x7fffffff;
     bad[r] = false;
   }
-  for (int i = tid; i < n; i += kThreads) {
+  for (int c = c0; c < c1; ++c) {
+    f32x4 v[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r < nrows) {
-        const float v = rows[r * stride + i];
-        bad[r] |= bad_logit(v);
-        if (v > mx[r]) {
-          mx[r] = v;
-          ix[r] = v0 + i;
+    for (int r = 0; r < R; ++r) v[r] = load4<kLds>(rows + r * ld + 4 * c, n - 4 * c);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool in = 4 * c + e < n;
+        const float x = v[r][e];
+        bad[r] |= in && bad_logit(x);
+        if (in && x > mx[r]) {
+          mx[r] = x;
+          ix[r] = v0 + 4 * c + e;
         }
       }
-    }
   }
 #pragma unroll
   for (int w = 32; w >= 1; w >>= 1) {
@@ -240,43 +273,49 @@ __device__ __forceinline__ void slice_stats_rows(const float* rows, int stride, 
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const bool anyb = __any(bad[r]);
-    if (lane == 0 && r < nrows) {
+    if (lane == 0) {
       redm[r * kWaves + wave] = mx[r];
       redi[r * kWaves + wave] = anyb ? -1 : ix[r];
     }
   }
   __syncthreads();
   float m[R];
-  double z[R];
   bool live[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     m[r] = -INFINITY;
     int idx = 0x7fffffff;
     bool anybad = false;
-    if (r < nrows) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float om = redm[r * kWaves + w];
-        const int oi = redi[r * kWaves + w];
-        anybad |= oi < 0;
-        if (w == 0 || om > m[r] || (om == m[r] && oi < idx)) {
-          m[r] = om;
-          idx = oi;
-        }
-      }
-      if (tid == 0) {
-        out[r].m = m[r];
-        out[r].idx = anybad ? -1 : (idx == 0x7fffffff ? v0 : idx);
+    for (int w = 0; w < kWaves; ++w) {
+      const float om = redm[r * kWaves + w];
+      const int oi = redi[r * kWaves + w];
+      anybad |= oi < 0;
+      if (w == 0 || om > m[r] || (om == m[r] && oi < idx)) {
+        m[r] = om;
+        idx = oi;
       }
     }
-    live[r] = r < nrows && !greedy && m[r] != -INFINITY && !anybad;
-    z[r] = 0.0;
+    if (tid == 0) {
+      out[r].m = m[r];
+      out[r].idx = anybad ? -1 : (idx == 0x7fffffff ? v0 : idx);
+    }
+    live[r] = !greedy && m[r] != -INFINITY && !anybad;
   }
-  for (int i = tid; i < n; i += kThreads) {
+  double z[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) z[r] = 0.0;
+  for (int c = c0; c < c1; ++c) {
+    f32x4 v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = load4<kLds>(rows + r * ld + 4 * c, n - 4 * c);
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (live[r]) z[r] += exp((static_cast<double>(rows[r * stride + i]) - static_cast<double>(m[r])) * inv_tau);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double t = exp((static_cast<double>(v[r][e]) - static_cast<double>(m[r])) * inv_tau);
+        z[r] += (live[r] && 4 * c + e < n) ? t : 0.0;
+      }
   }
 #pragma unroll
   for (int w = 32; w >= 1; w >>= 1) {
@@ -288,11 +327,10 @@ __device__ __forceinline__ void slice_stats_rows(const float* rows, int stride, 
   }
   if (lane == 0) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (r < nrows) redz[r * kWaves + wave] = z[r];
+    for (int r = 0; r < R; ++r) redz[r * kWaves + wave] = z[r];
   }
   __syncthreads();
-  if (tid < nrows) {
+  if (tid < R) {
     double t = 0.0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) t += redz[tid * kWaves + w];
@@ -332,9 +370,10 @@ __device__ __forceinline__ void merge_row(const Rec& r, bool member, bool greedy
 // LDS access; otherwise the slices are read from global memory where they lie.
 template <bool kFits>
 __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
-  __shared__ float eager_l[kEagerCap];
-  __shared__ float cur_lbuf[kSliceCap];
-  __shared__ float cur_qbuf[kSliceCap];
+  __shared__ __attribute__((aligned(16))) float eager_l[kEagerCap];  // logit slices of rows 0 .. E-1, stride ld
+  __shared__ __attribute__((aligned(16))) float eager_q[kEagerCap];  // their draft-probability slices
+  __shared__ __attribute__((aligned(16))) float cur_lbuf[kSliceCap];
+  __shared__ __attribute__((aligned(16))) float cur_qbuf[kSliceCap];
   __shared__ int16_t first_child[kMaxT], next_sib[kMaxT];
   __shared__ int s_par[kMaxT], s_tok[kMaxT], s_path[kMaxT];
   __shared__ float s_lx[kMaxT], s_qx[kMaxT];  // logit / draft prob of node c's token in its parent's row
@@ -358,11 +397,14 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   const int b = blockIdx.x / NW;
   const int wg = blockIdx.x % NW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int T = a.T, V = a.V, S = a.S, E = a.E;
+  const int T = a.T, V = a.V, S = a.S, E = a.E, ld = a.ld;
   const int v0 = min(V, wg * S), v1 = min(V, v0 + S);
   const int n = v1 - v0;
-  const int seg = (n + kThreads - 1) / kThreads;  // per-thread contiguous segment of the slice
-  const int i0 = min(n, tid * seg), i1 = min(n, i0 + seg);
+  // this thread's contiguous run of 4-element chunks of the slice: elements [i0, i1)
+  const int nc = (n + 3) >> 2;
+  const int per = (nc + kThreads - 1) / kThreads;
+  const int c0 = min(nc, tid * per), c1 = min(nc, c0 + per);
+  const int i0 = min(n, 4 * c0), i1 = min(n, 4 * c1);
   const float* lg_b = a.logits + static_cast<long>(b) * T * V;
   const float* q_b = a.q + static_cast<long>(b) * T * V;
   unsigned* ctr = a.sync + static_cast<long>(b) * kSyncStride;
@@ -423,9 +465,22 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
     }
     // statistics of the first E rows, from their LDS slices
     if (kFits && E > 0) {
-      stage_rows(eager_l, lg_b + v0, V, E, n);
+      stage_rows(eager_l, lg_b + v0, eager_q, a.greedy ? nullptr : q_b + v0, ld, V, E, n);
       __syncthreads();
-      slice_stats_rows<kMaxEager>(eager_l, n, E, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+      switch (E) {
+        case 1:
+          slice_stats_rows<1, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+          break;
+        case 2:
+          slice_stats_rows<2, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+          break;
+        case 4:
+          slice_stats_rows<4, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+          break;
+        default:
+          slice_stats_rows<8, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+          break;
+      }
       if (tid < E) eager[wg * E + tid] = s_rec[tid];
       team_barrier(ctr, NW * ++phase, &sh_fail);
       // merge every eager row at once (wave w: rows w and w + 4), member order
@@ -456,13 +511,14 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       const float* cq;
       if constexpr (kFits) {
         if (u < E) {
-          cl = eager_l + u * n;
+          cl = eager_l + u * ld;
+          cq = eager_q + u * ld;
         } else {
-          stage_rows(cur_lbuf, lg_b + static_cast<long>(u) * V + v0, 0, 1, n);
+          stage_rows(cur_lbuf, lg_b + static_cast<long>(u) * V + v0, cur_qbuf,
+                     (!a.greedy && has_kids) ? q_b + static_cast<long>(u) * V + v0 : nullptr, ld, 0, 1, n);
           cl = cur_lbuf;
+          cq = cur_qbuf;
         }
-        if (!a.greedy && has_kids) stage_rows(cur_qbuf, q_b + static_cast<long>(u) * V + v0, 0, 1, n);
-        cq = cur_qbuf;
       } else {
         cl = lg_b + static_cast<long>(u) * V + v0;
         cq = q_b + static_cast<long>(u) * V + v0;
@@ -470,7 +526,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       __syncthreads();
       const Rec* rows = part;  // members' statistics of a row past the eager ones
       if (u >= E) {  // a deeper row: its statistics now
-        slice_stats_rows<1>(cl, 0, 1, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+        slice_stats_rows<1, kFits>(cl, ld, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
         if (tid == 0) part[buf * NW + wg] = s_rec[0];
         team_barrier(ctr, NW * ++phase, &sh_fail);
         if (sh_fail) break;
@@ -514,8 +570,9 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         break;
       }
       const double m = sh_m, iz = sh_iz;
-      auto weight = [&](int i) -> double {  // current residual weight of slice element i
-        const double p = exp((static_cast<double>(cl[i]) - m) * a.inv_tau) * iz;
+      // current residual weight of slice element i with logit l and draft probability q
+      auto weight = [&](float l, float q, int i) -> double {
+        const double p = exp((static_cast<double>(l) - m) * a.inv_tau) * iz;
         const double C = sh_C;
         const int nrej = sh_nrej;
         if (nrej == 0 && C == 0.0) return p;
@@ -523,16 +580,23 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         double cx = C;
         for (int k = 0; k < nrej; ++k)
           if (rej_tok[k] == x) cx = rej_c[k];
-        return fmax(p - cx * static_cast<double>(cq[i]), 0.0);
+        return fmax(p - cx * static_cast<double>(q), 0.0);
       };
       // publish the slice mass of the current weights, scanned in index order
       double excl = 0.0, incl = 0.0;  // this thread's range within the slice
       auto scan_slice = [&](bool check_q) -> bool {
         double mine = 0.0;
         bool badq = false;
-        for (int i = i0; i < i1; ++i) {
-          if (check_q) badq |= isnan(cq[i]);
-          mine += weight(i);
+        for (int c = c0; c < c1; ++c) {
+          const f32x4 lv = load4<kFits>(cl + 4 * c, n - 4 * c);
+          const f32x4 qv = load4<kFits>(cq + 4 * c, n - 4 * c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool in = 4 * c + e < n;
+            if (check_q) badq |= in && isnan(qv[e]);
+            const double w = weight(lv[e], qv[e], 4 * c + e);
+            mine += in ? w : 0.0;
+          }
         }
         badq = __syncthreads_or(badq);
         incl = wave_incl_scan(mine);
@@ -672,13 +736,17 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         if ((t_lo <= target && target < t_hi) || (last_nonempty && target >= t_hi)) {
           double run = t_lo;
           int pick = -1, lastnz = -1;
-          for (int i = i0; i < i1; ++i) {
-            const double w = weight(i);
-            if (w > 0.0) lastnz = i;
-            run += w;
-            if (run > target) {
-              pick = i;
-              break;
+          for (int c = c0; c < c1 && pick < 0; ++c) {
+            const f32x4 lv = load4<kFits>(cl + 4 * c, n - 4 * c);
+            const f32x4 qv = load4<kFits>(cq + 4 * c, n - 4 * c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * c + e;
+              if (pick >= 0 || i >= n) continue;
+              const double w = weight(lv[e], qv[e], i);
+              if (w > 0.0) lastnz = i;
+              run += w;
+              if (run > target) pick = i;
             }
           }
           const int k = pick >= 0 ? pick : lastnz;
@@ -747,6 +815,7 @@ hipError_t launch_reject(const RejectLaunch& L, hipStream_t stream) {
   a.V = L.V;
   a.NW = t.NW;
   a.S = t.S;
+  a.ld = t.ld;
   a.E = t.E;
   a.greedy = greedy;
   a.wr = L.without_replacement ? 1 : 0;
@@ -754,7 +823,7 @@ hipError_t launch_reject(const RejectLaunch& L, hipStream_t stream) {
   a.seed = L.seed;
   a.offset = L.offset;
   const dim3 grid(static_cast<unsigned>(L.B * t.NW));
-  if (t.S <= kSliceCap) {
+  if (t.ld <= kSliceCap) {
     hipLaunchKernelGGL(reject_team_kernel<true>, grid, dim3(kThreads), 0, stream, a);
   } else {
     hipLaunchKernelGGL(reject_team_kernel<false>, grid, dim3(kThreads), 0, stream, a);
