@@ -66,7 +66,7 @@ Team team_shape(int B, int T, int V) {
   t.S = (V + nw - 1) / nw;
   t.ld = (t.S + 3) & ~3;
   int e = std::min(T, kMaxEager);
-  e = t.ld > kEagerCap ? 0 : std::min(e, kEagerCap / t.ld);
+  e = t.ld > kEagerCap ? 0 : std::min(e, kEagerCap / t.ld);  // >= 1 when the slice fits (T >= 1)
   t.E = e >= 8 ? 8 : e >= 4 ? 4 : e >= 2 ? 2 : e;
   return t;
 }
@@ -105,6 +105,55 @@ __device__ __forceinline__ double draw_uniform(uint64_t seed, uint64_t offset, i
 
 __device__ __forceinline__ bool bad_logit(float v) { return isnan(v) || v == INFINITY; }
 
+// e^x for N arguments at once, meant for x <= 0 (softmax terms); arguments are
+// clamped to [-746, 709], so -inf and NaN give a finite value the caller masks.
+// Cody-Waite reduction x = n ln2 + r, |r| <= ln2/2, with ln2 split into a part
+// of 24 significant bits (n * hi exact) and the rest; e^r by its Taylor
+// polynomial to degree 13 (truncation below 5e-18), evaluated by Horner's rule
+// for all N arguments in lockstep so their dependency chains overlap; scaled by 2^n.
+template <int N>
+__device__ __forceinline__ void exp_lockstep(double (&x)[N]) {
+  constexpr double kLog2e = 1.4426950408889634074;
+  constexpr double kLn2Hi = 0.693145751953125;          // ln 2 rounded to 24 bits
+  constexpr double kLn2Lo = 1.4286068203094172321e-06;  // ln 2 - kLn2Hi
+  constexpr double kF[14] = {1.0,
+                             1.0,
+                             1.0 / 2,
+                             1.0 / 6,
+                             1.0 / 24,
+                             1.0 / 120,
+                             1.0 / 720,
+                             1.0 / 5040,
+                             1.0 / 40320,
+                             1.0 / 362880,
+                             1.0 / 3628800,
+                             1.0 / 39916800,
+                             1.0 / 479001600,
+                             1.0 / 6227020800.0};
+  double r[N], p[N];
+  int k[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const double xv = fmin(fmax(x[j], -746.0), 709.0);
+    const double kd = rint(xv * kLog2e);
+    r[j] = fma(-kd, kLn2Lo, fma(-kd, kLn2Hi, xv));
+    k[j] = static_cast<int>(kd);
+    p[j] = kF[13];
+  }
+#pragma unroll
+  for (int d = 12; d >= 0; --d)
+#pragma unroll
+    for (int j = 0; j < N; ++j) p[j] = fma(p[j], r[j], kF[d]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] = ldexp(p[j], k[j]);
+}
+
+__device__ __forceinline__ double exp1(double x) {
+  double v[1] = {x};
+  exp_lockstep<1>(v);
+  return v[0];
+}
+
 struct TArgs {
   const float* logits;
   const float* q;
@@ -141,42 +190,41 @@ __device__ __forceinline__ void team_barrier(unsigned* ctr, unsigned target, int
   __syncthreads();
 }
 
-// Copy rows [r * src_stride + i], r < nrows, i < n (nrows * n <= 32 * kThreads) of
-// global memory into LDS dst[r * ld + i], from one or two sources (the second
-// only if src2 is set).  Every load of a thread is issued before its first
-// store, so the copy costs one memory latency.
-__device__ __forceinline__ void stage_rows(float* dst, const float* src, float* dst2, const float* src2, int ld,
-                                           long src_stride, int nrows, int n) {
-  constexpr int kB = 32;
-  const int cnt = nrows * n;
-  if (cnt <= 0) return;
-  const int tid = threadIdx.x;
-  float v[kB], v2[kB];
-  int off_s[kB], off_d[kB];
-  int r = tid / n, i = tid - (tid / n) * n;
+// Copies rows [r * src_stride + i], r < nrows, i < n (nrows * n <= 32 * kThreads)
+// of global memory into LDS dst[r * ld + i] (nrows, n >= 1).  issue() starts the
+// thread's loads -- exactly 32, unconditional (lanes past the end re-read
+// element 0), so the compiler can count them and a wait for loads issued
+// before them still fits the 6-bit vector-memory counter; commit() writes them
+// to LDS, so other work can run while they are in flight.
+struct Staging {
+  static constexpr int kB = 32;
+  float v[kB];
+  int off_d[kB];
+  int cnt;
+
+  __device__ __forceinline__ void issue(const float* src, int ld, long src_stride, int nrows, int n) {
+    cnt = nrows * n;
+    const int tid = threadIdx.x;
+    int r = tid / n, i = tid - (tid / n) * n;
 #pragma unroll
-  for (int k = 0; k < kB; ++k) {
-    off_s[k] = static_cast<int>(r * src_stride) + i;
-    off_d[k] = r * ld + i;
-    i += kThreads;
-    while (i >= n) {
-      i -= n;
-      ++r;
+    for (int k = 0; k < kB; ++k) {
+      const int off_s = (k * kThreads + tid < cnt) ? static_cast<int>(r * src_stride) + i : 0;
+      off_d[k] = r * ld + i;
+      v[k] = src[off_s];
+      i += kThreads;
+      while (i >= n) {
+        i -= n;
+        ++r;
+      }
     }
   }
+  __device__ __forceinline__ void commit(float* dst) const {
+    const int tid = threadIdx.x;
 #pragma unroll
-  for (int k = 0; k < kB; ++k) {
-    const bool in = k * kThreads + tid < cnt;
-    v[k] = in ? src[off_s[k]] : 0.f;
-    v2[k] = (in && src2) ? src2[off_s[k]] : 0.f;
+    for (int k = 0; k < kB; ++k)
+      if (k * kThreads + tid < cnt) dst[off_d[k]] = v[k];
   }
-#pragma unroll
-  for (int k = 0; k < kB; ++k)
-    if (k * kThreads + tid < cnt) {
-      dst[off_d[k]] = v[k];
-      if (src2) dst2[off_d[k]] = v2[k];
-    }
-}
+};
 
 // Four consecutive slice elements at p (16-byte aligned in LDS); from global
 // memory only the first `valid` are read.
@@ -309,13 +357,17 @@ __device__ __forceinline__ void slice_stats_rows(const float* rows, int ld, int 
     f32x4 v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) v[r] = load4<kLds>(rows + r * ld + 4 * c, n - 4 * c);
+    double t[4 * R];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const double t = exp((static_cast<double>(v[r][e]) - static_cast<double>(m[r])) * inv_tau);
-        z[r] += (live[r] && 4 * c + e < n) ? t : 0.0;
-      }
+      for (int e = 0; e < 4; ++e)
+        t[4 * r + e] = (static_cast<double>(v[r][e]) - static_cast<double>(m[r])) * inv_tau;
+    exp_lockstep<4 * R>(t);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[r] += (live[r] && 4 * c + e < n) ? t[4 * r + e] : 0.0;
   }
 #pragma unroll
   for (int w = 32; w >= 1; w >>= 1) {
@@ -350,7 +402,7 @@ __device__ __forceinline__ void merge_row(const Rec& r, bool member, bool greedy
   int arg = badr ? 0x7fffffff : r.idx;
   wave_argmax(m, arg);
   double zl = 0.0;
-  if (!greedy && member && r.m != -INFINITY) zl = r.z * exp((static_cast<double>(r.m) - m) * inv_tau);
+  if (!greedy && member && r.m != -INFINITY) zl = r.z * exp1((static_cast<double>(r.m) - m) * inv_tau);
   const double zt = __shfl(wave_incl_scan(zl), 63);  // member-order sum
   const bool anybad = __any(badr);
   const double iz = 1.0 / zt;
@@ -413,10 +465,16 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   Rec* eager = a.eager + static_cast<long>(b) * NW * max(E, 1);
   Rec* part = a.part + static_cast<long>(b) * 2 * NW;
 
-  // tree, tokens and the accept-test operands of every drafted node
-  for (int i = tid; i < T; i += kThreads) {
-    s_par[i] = a.parent[static_cast<long>(b) * T + i];
-    s_tok[i] = a.tokens[static_cast<long>(b) * T + i];
+  // tree and tokens first (T <= kThreads: one node per thread), then the eager
+  // logit slices, which depend on nothing else and stay in flight through the
+  // tree build
+  const int pv = a.parent[static_cast<long>(b) * T + min(tid, T - 1)];
+  const int tv = a.tokens[static_cast<long>(b) * T + min(tid, T - 1)];
+  Staging stage_l, stage_q;
+  if constexpr (kFits) stage_l.issue(lg_b + v0, ld, V, E, n);  // E >= 1 whenever the slice fits
+  if (tid < T) {
+    s_par[tid] = pv;
+    s_tok[tid] = tv;
   }
   if (tid == 0) {
     sh_err = 0;
@@ -458,14 +516,17 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
 
   int emitted = -1;  // greedy argmax, known to every member
   if (sh_err == 0) {
-    for (int c = 1 + tid; c < T; c += kThreads) {
-      const long off = static_cast<long>(s_par[c]) * V + s_tok[c];
-      s_lx[c] = lg_b[off];
-      s_qx[c] = a.greedy ? 0.f : q_b[off];
-    }
+    // accept-test operands of every drafted node and the eager draft slices: in
+    // flight during the statistics
+    const int cx = 1 + tid;
+    const int nd = min(cx, T - 1);  // lanes past the tree re-read a valid node (or element 0)
+    const long off = nd >= 1 ? static_cast<long>(s_par[nd]) * V + s_tok[nd] : 0;
+    const float lx = lg_b[off];
+    const float qx = (a.greedy ? lg_b : q_b)[off];
+    if constexpr (kFits) stage_q.issue((a.greedy ? lg_b : q_b) + v0, ld, V, E, n);
     // statistics of the first E rows, from their LDS slices
-    if (kFits && E > 0) {
-      stage_rows(eager_l, lg_b + v0, eager_q, a.greedy ? nullptr : q_b + v0, ld, V, E, n);
+    if (kFits) {
+      stage_l.commit(eager_l);
       __syncthreads();
       switch (E) {
         case 1:
@@ -482,6 +543,11 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
           break;
       }
       if (tid < E) eager[wg * E + tid] = s_rec[tid];
+      if (!a.greedy) stage_q.commit(eager_q);
+      if (cx < T) {
+        s_lx[cx] = lx;
+        s_qx[cx] = qx;
+      }
       team_barrier(ctr, NW * ++phase, &sh_fail);
       // merge every eager row at once (wave w: rows w and w + 4), member order
       if (!sh_fail) {
@@ -500,6 +566,12 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         }
       }
       __syncthreads();
+    } else {
+      if (cx < T) {
+        s_lx[cx] = lx;
+        s_qx[cx] = qx;
+      }
+      __syncthreads();
     }
 
     for (;;) {  // one iteration per visited node
@@ -514,8 +586,11 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
           cl = eager_l + u * ld;
           cq = eager_q + u * ld;
         } else {
-          stage_rows(cur_lbuf, lg_b + static_cast<long>(u) * V + v0, cur_qbuf,
-                     (!a.greedy && has_kids) ? q_b + static_cast<long>(u) * V + v0 : nullptr, ld, 0, 1, n);
+          Staging sl, sq;
+          sl.issue(lg_b + static_cast<long>(u) * V + v0, ld, 0, 1, n);
+          sq.issue((a.greedy ? lg_b : q_b) + static_cast<long>(u) * V + v0, ld, 0, 1, n);
+          sl.commit(cur_lbuf);
+          if (!a.greedy && has_kids) sq.commit(cur_qbuf);
           cl = cur_lbuf;
           cq = cur_qbuf;
         }
@@ -570,17 +645,24 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         break;
       }
       const double m = sh_m, iz = sh_iz;
-      // current residual weight of slice element i with logit l and draft probability q
-      auto weight = [&](float l, float q, int i) -> double {
-        const double p = exp((static_cast<double>(l) - m) * a.inv_tau) * iz;
+      // current residual weights of the 4 slice elements 4c .. 4c+3 (logits lv, draft probabilities qv)
+      auto weight4 = [&](const f32x4& lv, const f32x4& qv, int c, double (&w)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (static_cast<double>(lv[e]) - m) * a.inv_tau;
+        exp_lockstep<4>(w);
         const double C = sh_C;
         const int nrej = sh_nrej;
-        if (nrej == 0 && C == 0.0) return p;
-        const int x = v0 + i;
-        double cx = C;
-        for (int k = 0; k < nrej; ++k)
-          if (rej_tok[k] == x) cx = rej_c[k];
-        return fmax(p - cx * static_cast<double>(q), 0.0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[e] *= iz;
+          if (nrej > 0 || C != 0.0) {
+            const int x = v0 + 4 * c + e;
+            double cx = C;
+            for (int k = 0; k < nrej; ++k)
+              if (rej_tok[k] == x) cx = rej_c[k];
+            w[e] = fmax(w[e] - cx * static_cast<double>(qv[e]), 0.0);
+          }
+        }
       };
       // publish the slice mass of the current weights, scanned in index order
       double excl = 0.0, incl = 0.0;  // this thread's range within the slice
@@ -590,12 +672,13 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         for (int c = c0; c < c1; ++c) {
           const f32x4 lv = load4<kFits>(cl + 4 * c, n - 4 * c);
           const f32x4 qv = load4<kFits>(cq + 4 * c, n - 4 * c);
+          double w[4];
+          weight4(lv, qv, c, w);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const bool in = 4 * c + e < n;
             if (check_q) badq |= in && isnan(qv[e]);
-            const double w = weight(lv[e], qv[e], 4 * c + e);
-            mine += in ? w : 0.0;
+            mine += in ? w[e] : 0.0;
           }
         }
         badq = __syncthreads_or(badq);
@@ -618,7 +701,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
             sh_state = 0;  // no untried child: final draw at u
           } else {
             const int x = s_tok[c];
-            const double px = exp((static_cast<double>(s_lx[c]) - m) * a.inv_tau) * iz;
+            const double px = exp1((static_cast<double>(s_lx[c]) - m) * a.inv_tau) * iz;
             const float qf = s_qx[c];
             if (isnan(qf)) sh_err |= SPEC_DEV_NONFINITE;
             const double qx = static_cast<double>(qf);
@@ -739,13 +822,14 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
           for (int c = c0; c < c1 && pick < 0; ++c) {
             const f32x4 lv = load4<kFits>(cl + 4 * c, n - 4 * c);
             const f32x4 qv = load4<kFits>(cq + 4 * c, n - 4 * c);
+            double w[4];
+            weight4(lv, qv, c, w);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int i = 4 * c + e;
               if (pick >= 0 || i >= n) continue;
-              const double w = weight(lv[e], qv[e], i);
-              if (w > 0.0) lastnz = i;
-              run += w;
+              if (w[e] > 0.0) lastnz = i;
+              run += w[e];
               if (run > target) pick = i;
             }
           }
