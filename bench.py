@@ -15,13 +15,24 @@ torch.cuda.synchronize().  Per-kernel average durations come from HIP events
 around graphs that repeat one call many times on the same stream.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
+
+`roofline.traffic` comes from the committed rocprofv3 counter summary
+(profiles/pmc_<workload>.md, FETCH_SIZE and WRITE_SIZE per dispatch, scaled by
+what the same counters read for a plain 256 MiB copy); it is null when that
+summary was taken from other kernel sources than the ones built now.
+`--summarize trace|pmc DIR...` turns rocprofv3 CSV output into those summaries
+(host only, no GPU).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -36,8 +47,104 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 METRIC = "verified tree tokens/sec at 1 MI355X"
 
 
+KERNEL_KEYS = (("tree_attn", ("attn_",)), ("tree_reject", ("reject",)), ("kv_compact", ("compact",)))
+CALIB_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources and headers the library is built from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tree_verify_attention_masked_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*"))) + [os.path.join(ROOT, "include", "spectree.h")]:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_key(name):
+    low = name.lower()
+    for key, pats in KERNEL_KEYS:
+        if any(p in low for p in pats):
+            return key
+    return None
+
+
+def read_csvs(d, suffix):
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize(kind, dirs, workload):
+    """Markdown summary of rocprofv3 output (kernel trace stats, or FETCH_SIZE / WRITE_SIZE runs)."""
+    out = []
+    if kind == "trace":
+        rows = read_csvs(dirs[0], "kernel_stats.csv")
+        out.append("| kernel | calls | average duration (us) | total (us) | share |")
+        out.append("|---|---|---|---|---|")
+        for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0))):
+            name = r.get("Name", "")
+            avg = float(r.get("AverageNs", 0)) / 1e3
+            out.append(f"| `{name[:90]}` | {r.get('Calls')} | {avg:.2f} | {float(r.get('TotalDurationNs', 0)) / 1e3:.1f} | "
+                       f"{float(r.get('Percentage', 0)):.1f}% |")
+        return "\n".join(out)
+    # pmc: dirs = [fetch_dir, write_dir]
+    per = {}
+    calib = {}
+    for d, counter in zip(dirs, ("FETCH_SIZE", "WRITE_SIZE")):
+        disp = {}
+        for r in read_csvs(d, "counter_collection.csv"):
+            if r.get("Counter_Name") != counter:
+                continue
+            key = (r.get("Dispatch_Id"), r.get("Kernel_Name", ""))
+            disp[key] = disp.get(key, 0.0) + float(r.get("Counter_Value", 0))
+        for (_, name), kib in disp.items():
+            k = kernel_key(name)
+            if k:
+                per.setdefault(k, {}).setdefault(counter, []).append(kib)
+            elif "copy" in name.lower() and kib > 0.5 * CALIB_BYTES / 1024:
+                calib.setdefault(counter, []).append(kib)
+    factors = {c: (float(np.median(v)) * 1024 / CALIB_BYTES if v else None) for c, v in calib.items()}
+    res = {"workload": workload, "source_sha256": kernel_source_hash(), "calibration": factors, "kernels": {}}
+    out.append("| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/launch (scaled) |")
+    out.append("|---|---|---|---|---|")
+    for k, cs in sorted(per.items()):
+        f = float(np.mean(cs.get("FETCH_SIZE", [0.0])))
+        wv = float(np.mean(cs.get("WRITE_SIZE", [0.0])))
+        ff, fw = factors.get("FETCH_SIZE") or 1.0, factors.get("WRITE_SIZE") or 1.0
+        traffic = f * 1024 / ff + wv * 1024 / fw
+        res["kernels"][k] = {"fetch_kib": round(f, 1), "write_kib": round(wv, 1), "traffic_bytes": int(traffic)}
+        out.append(f"| {k} | {len(cs.get('FETCH_SIZE', []))} | {f:.1f} | {wv:.1f} | {traffic / 1e6:.3f} MB |")
+    out.append("")
+    out.append(f"Calibration (256 MiB device copy): FETCH_SIZE reads {factors.get('FETCH_SIZE')} x, "
+               f"WRITE_SIZE {factors.get('WRITE_SIZE')} x the bytes copied.")
+    out.append("")
+    out.append("```json")
+    out.append(json.dumps(res))
+    out.append("```")
+    return "\n".join(out)
+
+
+def committed_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from profiles/pmc_<workload>.md, if taken from the current sources."""
+    f = os.path.join(ROOT, "profiles", f"pmc_{workload}.md")
+    if not os.path.exists(f):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(f).read(), re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("source_sha256") != kernel_source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return int(k["traffic_bytes"]) if k else None
 
 
 def depths(parent_row):
@@ -109,7 +216,15 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=0, help="launches per per-kernel timing graph")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--offset", type=int, default=0)
+    ap.add_argument("--calib-copy", action="store_true", help="run one 256 MiB device copy (counter calibration)")
+    ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
+                    help="trace DIR | pmc FETCH_DIR WRITE_DIR: print a markdown summary of rocprofv3 output")
+    ap.add_argument("--workload-name", default="chain", help="workload name recorded by --summarize pmc")
     args = ap.parse_args()
+
+    if args.summarize:
+        print(summarize(args.summarize[0], args.summarize[1:], args.workload_name))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -171,6 +286,13 @@ def main():
         attn(c)
         reject(c)
         compact(c)
+
+    if args.calib_copy:  # a plain copy of known size, for scaling the HBM counters
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for c in copies:  # eager pass: validates and warms every copy
         step(c)
@@ -254,6 +376,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
     roof["kernel"] = dominant
+    t_bytes = committed_traffic(w.name, dominant)
+    if t_bytes is not None:
+        roof["traffic"] = t_bytes
 
     kernels = {}
     for name, (b_, by, fl) in work.items():
