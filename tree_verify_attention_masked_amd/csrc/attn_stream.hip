@@ -48,10 +48,11 @@ struct StArgs {
   const int32_t* parent;
   uint16_t* out;
   int32_t* status;
-  float* part_o;       // [items][R][D]
+  float* part_o;       // [items][R][D]; within each row, element e of dims 8j..8j+7 at 16e + j
   float* part_ml;      // [items][R][2]
   unsigned* counters;  // [B * Hkv], zero between calls
   int B, T, Hq, Hkv, G, R, splits, pps, max_blocks, num_blocks;
+  int reorder;  // order items full splits first (B <= 64, more items than resident workgroups)
   long items;
   float sl2;
 };
@@ -137,15 +138,47 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
   const int l16 = lane & 15;
   const int quad = lane >> 4;
 
-  // Consecutive workgroup ids are dealt round-robin to the 8 XCDs; give each
-  // XCD a contiguous run of items.
-  const long per = (a.items + 7) / 8;
-  const long item = static_cast<long>(blockIdx.x % 8) * per + blockIdx.x / 8;
+  // Items in launch order: splits read disjoint pages, so there is no cache
+  // reuse to keep within an XCD, and dealing consecutive items to different
+  // XCDs balances ragged batches.  With `reorder`, workgroup ids go first to
+  // the full splits of every (b, g), then to each (b, g)'s last split, then to
+  // nothing: the long items start first and the short ones fill the tail.
+  long item = blockIdx.x;
   if (item >= a.items) return;
-  const int s = static_cast<int>(item % a.splits);
+  int s = static_cast<int>(item % a.splits);
+  int g = static_cast<int>((item / a.splits) % a.Hkv);
+  int b = static_cast<int>(item / a.splits / a.Hkv);
+  if (a.reorder) {
+    int lb = lane < a.B ? a.plen[lane] : 0;
+    const int cap = a.max_blocks * kBlockSize - a.T;
+    lb = lb < 0 ? 0 : (lb > cap ? cap : lb);
+    const int nu = lane < a.B ? (((lb + a.T + kBlockSize - 1) / kBlockSize) + a.pps - 1) / a.pps : 0;
+    const int full = lane < a.B ? (nu - 1) * a.Hkv : 0;
+    int incl = full;  // inclusive prefix sum over sequences
+#pragma unroll
+    for (int w = 1; w < 64; w <<= 1) {
+      const int o = __shfl_up(incl, w);
+      if (lane >= w) incl += o;
+    }
+    const int F = __shfl(incl, 63);
+    const int id = static_cast<int>(blockIdx.x);
+    if (id < F) {
+      const unsigned long long hit = __ballot(incl > id);
+      b = __ffsll(static_cast<long long>(hit)) - 1;
+      const int k = id - (__shfl(incl, b) - __shfl(full, b));
+      const int nb = __shfl(nu, b) - 1;
+      g = k / nb;
+      s = k % nb;
+    } else if (id - F < a.B * a.Hkv) {
+      b = (id - F) / a.Hkv;
+      g = (id - F) % a.Hkv;
+      s = __shfl(nu, b) - 1;
+    } else {
+      return;
+    }
+    item = (static_cast<long>(b) * a.Hkv + g) * a.splits + s;
+  }
   const long bg = item / a.splits;
-  const int g = static_cast<int>(bg % a.Hkv);
-  const int b = static_cast<int>(bg / a.Hkv);
 
   // Independent prologue loads: prefix length, this wave's block indices (lane
   // k holds page s*pps + wave + 4k), the parent row (lane = node), the queries.
@@ -388,9 +421,10 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
           wds[e] = f32_to_bf16(acc[2 * e] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * e + 1] * inv)) << 16);
         *reinterpret_cast<u32x4*>(op) = u32x4{wds[0], wds[1], wds[2], wds[3]};
       } else {
-        float* po = a.part_o + (item * a.R + r) * kD + dseg;
+        // element e of dims dseg .. dseg+7 at e*16 + dseg/8: each store instruction writes whole lines
+        float* po = a.part_o + (item * a.R + r) * kD + (tid & 15);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st_agent(po + e, acc[e]);
+        for (int e = 0; e < 8; ++e) st_agent(po + e * 16, acc[e]);
         if ((tid & 15) == 0) {
           st_agent(&a.part_ml[(item * a.R + r) * 2 + 0], mstar);
           st_agent(&a.part_ml[(item * a.R + r) * 2 + 1], lstar);
@@ -425,11 +459,11 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
           const long it = first + sp0 + k;
           ms[k] = ld_agent(&a.part_ml[(it * a.R + r) * 2]);
           ls[k] = ld_agent(&a.part_ml[(it * a.R + r) * 2 + 1]);
-          const float* po = a.part_o + (it * a.R + r) * kD + dseg;
+          const float* po = a.part_o + (it * a.R + r) * kD + (tid & 15);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            x0[k][e] = ld_agent(po + e);
-            x1[k][e] = ld_agent(po + 4 + e);
+            x0[k][e] = ld_agent(po + e * 16);
+            x1[k][e] = ld_agent(po + (4 + e) * 16);
           }
         }
       }
@@ -462,7 +496,7 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
 
 template <int NRB, int DEPTH>
 hipError_t run_stream(const StArgs& args, hipStream_t stream) {
-  const long grid = ((args.items + 7) / 8) * 8;
+  const long grid = args.items;
   hipLaunchKernelGGL((attn_stream_kernel<NRB, DEPTH>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, args);
   return hipGetLastError();
 }
@@ -492,6 +526,9 @@ hipError_t run_stream_rows(int nrb, const StArgs& args, hipStream_t stream) {
 #ifndef SPEC_STREAM_DEPTH
 #define SPEC_STREAM_DEPTH 4
 #endif
+#ifndef SPEC_STREAM_RAGGED_PPS
+#define SPEC_STREAM_RAGGED_PPS 256
+#endif
 #ifndef SPEC_STREAM_OVERHEAD_PAGES
 #define SPEC_STREAM_OVERHEAD_PAGES 3
 #endif
@@ -506,7 +543,11 @@ void plan_stream(AttnPlan& p, int B, int Hkv, int max_blocks) {
   const long slots = 256 * per_cu;
   long best_pps = 4 * kMaxWavePages;
   double best = 1e30;
-  for (long pps = 4; pps <= 4 * kMaxWavePages; pps += 4) {
+  // Much more work than wave slots (batched serving): bounded items, so that
+  // ragged sequence lengths leave a short tail.
+  const long max_pps =
+      static_cast<long>(max_blocks) * bg >= 8 * slots * 64 ? SPEC_STREAM_RAGGED_PPS : 4 * kMaxWavePages;
+  for (long pps = 4; pps <= max_pps; pps += 4) {
     const long splits = (max_blocks + pps - 1) / pps;
     const long items = bg * splits;
     const long rounds = (items + slots - 1) / slots;
@@ -545,6 +586,7 @@ hipError_t launch_attn_stream(const AttnPlan& plan, const AttnLaunch& L, hipStre
   a.num_blocks = L.num_blocks;
   a.items = plan.items;
   a.sl2 = L.scale * kLog2e;
+  a.reorder = (plan.splits > 1 && L.B <= 64 && plan.items > 256L * std::max(1, 160 / (32 * plan.depth))) ? 1 : 0;
   if (plan.splits > 1) {
     const size_t bg = static_cast<size_t>(L.B) * L.Hkv;
     a.counters = static_cast<unsigned*>(L.workspace);
