@@ -171,12 +171,31 @@ struct TArgs {
   uint64_t seed, offset;
 };
 
-// Team barrier number `target`: every member has published its partials.
+// Records exchanged between members (the team spans XCDs, whose L2s are not
+// coherent with each other) are written and read as relaxed agent-scope
+// atomics: write-through stores, coherent loads.  A barrier then needs only
+// each wave's stores to have completed before its arrival is counted -- no
+// write-back or invalidation of the whole L2, which a fence would cost.
+__device__ __forceinline__ void st_rec(Rec* p, const Rec& r) {
+  __hip_atomic_store(&p->m, r.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&p->idx, r.idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&p->z, r.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ Rec ld_rec(const Rec* p) {
+  Rec* q = const_cast<Rec*>(p);
+  Rec r;
+  r.m = __hip_atomic_load(&q->m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  r.idx = __hip_atomic_load(&q->idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  r.z = __hip_atomic_load(&q->z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return r;
+}
+
+// Team barrier number `target`: every member has published its records.
 __device__ __forceinline__ void team_barrier(unsigned* ctr, unsigned target, int* fail) {
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's record stores are complete
   __syncthreads();
   if (threadIdx.x == 0 && *fail == 0) {
-    __threadfence();
-    atomicAdd(ctr, 1u);
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     unsigned spins = 0;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       __builtin_amdgcn_s_sleep(1);
@@ -185,46 +204,28 @@ __device__ __forceinline__ void team_barrier(unsigned* ctr, unsigned target, int
         break;
       }
     }
-    __threadfence();
   }
   __syncthreads();
 }
 
-// Copies rows [r * src_stride + i], r < nrows, i < n (nrows * n <= 32 * kThreads)
-// of global memory into LDS dst[r * ld + i] (nrows, n >= 1).  issue() starts the
-// thread's loads -- exactly 32, unconditional (lanes past the end re-read
-// element 0), so the compiler can count them and a wait for loads issued
-// before them still fits the 6-bit vector-memory counter; commit() writes them
-// to LDS, so other work can run while they are in flight.
-struct Staging {
-  static constexpr int kB = 32;
-  float v[kB];
-  int off_d[kB];
-  int cnt;
+// Starts copying rows [r * src_stride + i], r < nrows, i < n, of global memory
+// into LDS dst[r * ld + i] with direct global->LDS loads: one instruction moves
+// 64 consecutive floats (lane i to LDS dword i of the instruction's base), so
+// the copy needs no registers and almost no index arithmetic.  The data may be
+// read after this wave's vector-memory counter has drained and a workgroup
+// barrier.
+__device__ __forceinline__ void stage_dma(float* dst, const float* src, int ld, long src_stride, int nrows, int n) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int per_row = (n + 63) >> 6;
+  for (int j = wave; j < nrows * per_row; j += kWaves) {
+    const int r = j / per_row, c = j - r * per_row;
+    const int i = c * 64 + lane;
+    if (i < n) __builtin_amdgcn_global_load_lds(src + r * src_stride + i, dst + r * ld + c * 64, 4, 0, 0);
+  }
+}
 
-  __device__ __forceinline__ void issue(const float* src, int ld, long src_stride, int nrows, int n) {
-    cnt = nrows * n;
-    const int tid = threadIdx.x;
-    int r = tid / n, i = tid - (tid / n) * n;
-#pragma unroll
-    for (int k = 0; k < kB; ++k) {
-      const int off_s = (k * kThreads + tid < cnt) ? static_cast<int>(r * src_stride) + i : 0;
-      off_d[k] = r * ld + i;
-      v[k] = src[off_s];
-      i += kThreads;
-      while (i >= n) {
-        i -= n;
-        ++r;
-      }
-    }
-  }
-  __device__ __forceinline__ void commit(float* dst) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int k = 0; k < kB; ++k)
-      if (k * kThreads + tid < cnt) dst[off_d[k]] = v[k];
-  }
-};
+__device__ __forceinline__ void wait_dma() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Four consecutive slice elements at p (16-byte aligned in LDS); from global
 // memory only the first `valid` are read.
@@ -241,29 +242,75 @@ __device__ __forceinline__ f32x4 load4(const float* p, int valid) {
   }
 }
 
-// Max with the lowest index on ties, over the 64 lanes of a wave.
-__device__ __forceinline__ void wave_argmax(float& m, int& i) {
-#pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) {
-    const float om = __shfl_xor(m, w);
-    const int oi = __shfl_xor(i, w);
-    if (om > m || (om == m && oi < i)) {
-      m = om;
-      i = oi;
-    }
+// Cross-lane steps through DPP (a few cycles each, instead of an LDS round trip
+// per shuffle).  A wave-wide inclusive scan is row_shr 1, 2, 4, 8 within each
+// row of 16 lanes, then row_bcast:15 into rows 1 and 3 and row_bcast:31 into
+// rows 2 and 3; lanes without a source keep `old` (the operation's identity).
+// Every lane of the wave must be active.
+constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118;
+constexpr int kBcast15 = 0x142, kBcast31 = 0x143, kWaveShr1 = 0x138;
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_i(int old, int x) {
+  return __builtin_amdgcn_update_dpp(old, x, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f(float old, float x) {
+  return __builtin_bit_cast(float, dpp_i<CTRL, ROWS>(__builtin_bit_cast(int, old), __builtin_bit_cast(int, x)));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_d(double old, double x) {
+  const long long o = __builtin_bit_cast(long long, old), v = __builtin_bit_cast(long long, x);
+  const int lo = dpp_i<CTRL, ROWS>(static_cast<int>(o), static_cast<int>(v));
+  const int hi = dpp_i<CTRL, ROWS>(static_cast<int>(o >> 32), static_cast<int>(v >> 32));
+  return __builtin_bit_cast(double, (static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+__device__ __forceinline__ float lane63_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  const long long v = __builtin_bit_cast(long long, x);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(v), l);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), l);
+  return __builtin_bit_cast(double, (static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+
+// (max, lowest index of the max) combined with the value DPP brings in.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void argmax_step(float& m, int& i) {
+  const float om = dpp_f<CTRL, ROWS>(-INFINITY, m);
+  const int oi = dpp_i<CTRL, ROWS>(0x7fffffff, i);
+  if (om > m || (om == m && oi < i)) {
+    m = om;
+    i = oi;
   }
+}
+
+// Max with the lowest index on ties over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ void wave_argmax(float& m, int& i) {
+  argmax_step<kShr1, 0xF>(m, i);
+  argmax_step<kShr2, 0xF>(m, i);
+  argmax_step<kShr4, 0xF>(m, i);
+  argmax_step<kShr8, 0xF>(m, i);
+  argmax_step<kBcast15, 0xA>(m, i);
+  argmax_step<kBcast31, 0xC>(m, i);
+  m = lane63_f(m);
+  i = __builtin_amdgcn_readlane(i, 63);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave (lane order).
 __device__ __forceinline__ double wave_incl_scan(double v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int w = 1; w < 64; w <<= 1) {
-    const double o = __shfl_up(v, w);
-    if (lane >= w) v += o;
-  }
+  v += dpp_d<kShr1, 0xF>(0.0, v);
+  v += dpp_d<kShr2, 0xF>(0.0, v);
+  v += dpp_d<kShr4, 0xF>(0.0, v);
+  v += dpp_d<kShr8, 0xF>(0.0, v);
+  v += dpp_d<kBcast15, 0xA>(0.0, v);
+  v += dpp_d<kBcast31, 0xC>(0.0, v);
   return v;
 }
+
+// The previous lane's value (lane 0: `first`).
+__device__ __forceinline__ double wave_shift_up(double v, double first) { return dpp_d<kWaveShr1, 0xF>(first, v); }
 
 // Statistics of R rows whose slices are rows[r * ld + i], i < n: slice max, its
 // first index (-1 if the slice holds NaN or +inf) and the sum of
@@ -303,21 +350,7 @@ __device__ __forceinline__ void slice_stats_rows(const float* rows, int ld, int 
       }
   }
 #pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) {
-    float om[R];
-    int oi[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      om[r] = __shfl_xor(mx[r], w);
-      oi[r] = __shfl_xor(ix[r], w);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (om[r] > mx[r] || (om[r] == mx[r] && oi[r] < ix[r])) {
-        mx[r] = om[r];
-        ix[r] = oi[r];
-      }
-  }
+  for (int r = 0; r < R; ++r) wave_argmax(mx[r], ix[r]);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const bool anyb = __any(bad[r]);
@@ -370,13 +403,7 @@ __device__ __forceinline__ void slice_stats_rows(const float* rows, int ld, int 
       for (int e = 0; e < 4; ++e) z[r] += (live[r] && 4 * c + e < n) ? t[4 * r + e] : 0.0;
   }
 #pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) {
-    double oz[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) oz[r] = __shfl_xor(z[r], w);
-#pragma unroll
-    for (int r = 0; r < R; ++r) z[r] += oz[r];
-  }
+  for (int r = 0; r < R; ++r) z[r] = readlane_d(wave_incl_scan(z[r]), 63);
   if (lane == 0) {
 #pragma unroll
     for (int r = 0; r < R; ++r) redz[r * kWaves + wave] = z[r];
@@ -403,7 +430,7 @@ __device__ __forceinline__ void merge_row(const Rec& r, bool member, bool greedy
   wave_argmax(m, arg);
   double zl = 0.0;
   if (!greedy && member && r.m != -INFINITY) zl = r.z * exp1((static_cast<double>(r.m) - m) * inv_tau);
-  const double zt = __shfl(wave_incl_scan(zl), 63);  // member-order sum
+  const double zt = readlane_d(wave_incl_scan(zl), 63);  // member-order sum
   const bool anybad = __any(badr);
   const double iz = 1.0 / zt;
   if (member) mass_out[lane] = greedy ? 0.0 : zl * iz;
@@ -465,13 +492,15 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   Rec* eager = a.eager + static_cast<long>(b) * NW * max(E, 1);
   Rec* part = a.part + static_cast<long>(b) * 2 * NW;
 
-  // tree and tokens first (T <= kThreads: one node per thread), then the eager
-  // logit slices, which depend on nothing else and stay in flight through the
-  // tree build
+  // tree and tokens (T <= kThreads: one node per thread) and the eager logit and
+  // draft slices, which depend on nothing else: all in flight together
   const int pv = a.parent[static_cast<long>(b) * T + min(tid, T - 1)];
   const int tv = a.tokens[static_cast<long>(b) * T + min(tid, T - 1)];
-  Staging stage_l, stage_q;
-  if constexpr (kFits) stage_l.issue(lg_b + v0, ld, V, E, n);  // E >= 1 whenever the slice fits
+  if constexpr (kFits) {  // E >= 1 whenever the slice fits
+    stage_dma(eager_l, lg_b + v0, ld, V, E, n);
+    if (!a.greedy) stage_dma(eager_q, q_b + v0, ld, V, E, n);
+    wait_dma();
+  }
   if (tid < T) {
     s_par[tid] = pv;
     s_tok[tid] = tv;
@@ -523,11 +552,8 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
     const long off = nd >= 1 ? static_cast<long>(s_par[nd]) * V + s_tok[nd] : 0;
     const float lx = lg_b[off];
     const float qx = (a.greedy ? lg_b : q_b)[off];
-    if constexpr (kFits) stage_q.issue((a.greedy ? lg_b : q_b) + v0, ld, V, E, n);
-    // statistics of the first E rows, from their LDS slices
+    // statistics of the first E rows, from their LDS slices (landed before the tree build's barrier)
     if (kFits) {
-      stage_l.commit(eager_l);
-      __syncthreads();
       switch (E) {
         case 1:
           slice_stats_rows<1, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
@@ -542,8 +568,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
           slice_stats_rows<8, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
           break;
       }
-      if (tid < E) eager[wg * E + tid] = s_rec[tid];
-      if (!a.greedy) stage_q.commit(eager_q);
+      if (tid < E) st_rec(&eager[wg * E + tid], s_rec[tid]);
       if (cx < T) {
         s_lx[cx] = lx;
         s_qx[cx] = qx;
@@ -556,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         for (int h = 0; h < 2; ++h) {
           const int r = wave + h * kWaves;
           rr[h] = Rec{-INFINITY, 0x7fffffff, 0.0};
-          if (r < E && lane < NW) rr[h] = eager[lane * E + r];
+          if (r < E && lane < NW) rr[h] = ld_rec(&eager[lane * E + r]);
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -586,11 +611,9 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
           cl = eager_l + u * ld;
           cq = eager_q + u * ld;
         } else {
-          Staging sl, sq;
-          sl.issue(lg_b + static_cast<long>(u) * V + v0, ld, 0, 1, n);
-          sq.issue((a.greedy ? lg_b : q_b) + static_cast<long>(u) * V + v0, ld, 0, 1, n);
-          sl.commit(cur_lbuf);
-          if (!a.greedy && has_kids) sq.commit(cur_qbuf);
+          stage_dma(cur_lbuf, lg_b + static_cast<long>(u) * V + v0, ld, 0, 1, n);
+          if (!a.greedy && has_kids) stage_dma(cur_qbuf, q_b + static_cast<long>(u) * V + v0, ld, 0, 1, n);
+          wait_dma();
           cl = cur_lbuf;
           cq = cur_qbuf;
         }
@@ -602,14 +625,14 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       const Rec* rows = part;  // members' statistics of a row past the eager ones
       if (u >= E) {  // a deeper row: its statistics now
         slice_stats_rows<1, kFits>(cl, ld, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
-        if (tid == 0) part[buf * NW + wg] = s_rec[0];
+        if (tid == 0) st_rec(&part[buf * NW + wg], s_rec[0]);
         team_barrier(ctr, NW * ++phase, &sh_fail);
         if (sh_fail) break;
         rows = part + buf * NW;
         buf ^= 1;
         if (wave == 0) {
           Rec r = Rec{-INFINITY, 0x7fffffff, 0.0};
-          if (lane < NW) r = rows[lane];
+          if (lane < NW) r = ld_rec(&rows[lane]);
           merge_row(r, lane < NW, a.greedy, a.inv_tau, &e_m[kMaxEager], &e_iz[kMaxEager], &e_arg[kMaxEager],
                     &e_err[kMaxEager], &e_mass[kMaxEager * kMaxTeam]);
         }
@@ -688,8 +711,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         double before = 0.0;
         for (int w = 0; w < wave; ++w) before += sh_incl[w];
         incl += before;
-        excl = __shfl_up(incl, 1);
-        if (lane == 0) excl = before;
+        excl = wave_shift_up(incl, before);  // lane 0: the waves before it
         return badq;
       };
       bool scanned = false;  // part[buf] holds the slice masses of the current weights
@@ -730,12 +752,12 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
           r.m = 0.f;
           r.idx = badq ? -1 : 0;
           r.z = incl;  // slice mass: the last thread's inclusive sum
-          part[buf * NW + wg] = r;
+          st_rec(&part[buf * NW + wg], r);
         }
         team_barrier(ctr, NW * ++phase, &sh_fail);
         if (sh_fail) break;
         if (wave == 0) {
-          const Rec r = lane < NW ? part[buf * NW + lane] : Rec{0.f, 0, 0.0};
+          const Rec r = lane < NW ? ld_rec(&part[buf * NW + lane]) : Rec{0.f, 0, 0.0};
           const double tot = wave_incl_scan(r.z);
           const bool anybad = __any(lane < NW && r.idx < 0);
           if (lane == 63) {
@@ -780,7 +802,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         scan_slice(false);
         if (!bonus) {  // a zero-mass residual left earlier weights in place: publish them
           buf ^= 1;    // the other buffer: members may still read the last pass's
-          if (tid == kThreads - 1) part[buf * NW + wg] = Rec{0.f, 0, incl};
+          if (tid == kThreads - 1) st_rec(&part[buf * NW + wg], Rec{0.f, 0, incl});
           team_barrier(ctr, NW * ++phase, &sh_fail);
           if (sh_fail) break;
         }
@@ -788,14 +810,13 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       if (wave == 0) {
         double mass = 0.0;
         if (!bonus || scanned) {
-          if (lane < NW) mass = part[buf * NW + lane].z;
+          if (lane < NW) mass = ld_rec(&part[buf * NW + lane]).z;
         } else if (lane < NW) {
           mass = e_mass[er * kMaxTeam + lane];
         }
         const double inc = wave_incl_scan(mass);
-        double exc = __shfl_up(inc, 1);
-        if (lane == 0) exc = 0.0;
-        const double total = __shfl(inc, 63);
+        const double exc = wave_shift_up(inc, 0.0);
+        const double total = readlane_d(inc, 63);
         const double uu = s_fu[u];
         const double target = uu * total;
         const bool here = lane < NW && exc <= target && target < inc;
@@ -803,7 +824,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         const unsigned long long nz = __ballot(lane < NW && mass > 0.0);
         const int owner = hit ? (__ffsll(static_cast<long long>(hit)) - 1)
                               : (nz ? (63 - __clzll(static_cast<long long>(nz))) : 0);
-        const double lo = __shfl(exc, owner);
+        const double lo = readlane_d(exc, owner);
         if (lane == 0) {
           if (!(total > 0.0)) sh_err |= SPEC_DEV_EMPTY;
           sh_owner = owner;
