@@ -280,10 +280,9 @@ template <int CTRL, int ROWS>
 __device__ __forceinline__ void argmax_step(float& m, int& i) {
   const float om = dpp_f<CTRL, ROWS>(-INFINITY, m);
   const int oi = dpp_i<CTRL, ROWS>(0x7fffffff, i);
-  if (om > m || (om == m && oi < i)) {
-    m = om;
-    i = oi;
-  }
+  const bool take = om > m || (om == m && oi < i);  // selects, not branches
+  m = take ? om : m;
+  i = take ? oi : i;
 }
 
 // Max with the lowest index on ties over the 64 lanes of a wave, in every lane.
@@ -314,106 +313,105 @@ __device__ __forceinline__ double wave_shift_up(double v, double first) { return
 
 // Statistics of R rows whose slices are rows[r * ld + i], i < n: slice max, its
 // first index (-1 if the slice holds NaN or +inf) and the sum of
-// exp((l - max) / t).  Each thread takes a contiguous run of 4-element chunks;
-// the rows are reduced side by side, so each shuffle step waits once for all.
+// exp((l - max) / t), into out[0 .. R-1].  One pass per thread over its
+// contiguous 4-element chunks keeps a running (max, first argmax, sum of exp
+// relative to the running max) per row; the partials go to LDS (`scratch`, at
+// least R * kThreads * 16 bytes) and wave w then reduces row w over all threads,
+// so each wave's dependency chain covers one row, not R.
 template <int R, bool kLds>
 __device__ __forceinline__ void slice_stats_rows(const float* rows, int ld, int n, int v0, bool greedy, double inv_tau,
-                                                 Rec* out, float* redm, int* redi, double* redz) {
+                                                 Rec* out, void* scratch) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* pm = static_cast<float*>(scratch);
+  int* pi = reinterpret_cast<int*>(pm + R * kThreads);
+  double* pz = reinterpret_cast<double*>(pi + R * kThreads);
   const int nc = (n + 3) >> 2;
   const int per = (nc + kThreads - 1) / kThreads;
   const int c0 = min(nc, tid * per), c1 = min(nc, c0 + per);
   float mx[R];
   int ix[R];
-  bool bad[R];
+  double z[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     mx[r] = -INFINITY;
     ix[r] = 0x7fffffff;
-    bad[r] = false;
+    z[r] = 0.0;
   }
   for (int c = c0; c < c1; ++c) {
     f32x4 v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) v[r] = load4<kLds>(rows + r * ld + 4 * c, n - 4 * c);
+    float cm[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r) {
+      cm[r] = mx[r];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 4; ++e) {  // a NaN or +inf pins the row's max at +inf with index -1
         const bool in = 4 * c + e < n;
         const float x = v[r][e];
-        bad[r] |= in && bad_logit(x);
-        if (in && x > mx[r]) {
-          mx[r] = x;
-          ix[r] = v0 + 4 * c + e;
-        }
+        const bool bad = in && bad_logit(x);
+        const bool take = (in && x > cm[r]) || bad;
+        cm[r] = take ? (bad ? INFINITY : x) : cm[r];
+        ix[r] = take ? (bad ? -1 : v0 + 4 * c + e) : ix[r];
       }
+    }
+    double t[5 * R];  // the chunk's terms, then the factor rescaling the running sum
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[4 * r + e] = (static_cast<double>(v[r][e]) - static_cast<double>(cm[r])) * inv_tau;
+      t[4 * R + r] = (static_cast<double>(mx[r]) - static_cast<double>(cm[r])) * inv_tau;
+    }
+    exp_lockstep<5 * R>(t);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      double zz = (mx[r] == -INFINITY) ? 0.0 : z[r] * t[4 * R + r];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zz += (4 * c + e < n) ? t[4 * r + e] : 0.0;
+      z[r] = zz;
+      mx[r] = cm[r];
+    }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) wave_argmax(mx[r], ix[r]);
-#pragma unroll
   for (int r = 0; r < R; ++r) {
-    const bool anyb = __any(bad[r]);
+    pm[r * kThreads + tid] = mx[r];
+    pi[r * kThreads + tid] = ix[r];
+    pz[r * kThreads + tid] = z[r];
+  }
+  __syncthreads();
+  for (int r = wave; r < R; r += kWaves) {
+    constexpr int K = kThreads / 64;
+    float m = -INFINITY, ms[K];
+    int i = 0x7fffffff;
+    double zs[K];
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {  // thread order k*64 + lane: ties keep the lower index
+      ms[k] = pm[r * kThreads + k * 64 + lane];
+      const int ik = pi[r * kThreads + k * 64 + lane];
+      zs[k] = pz[r * kThreads + k * 64 + lane];
+      bad |= ik < 0;
+      const bool take = ms[k] > m || (ms[k] == m && ik < i);
+      m = take ? ms[k] : m;
+      i = take ? ik : i;
+    }
+    bad = __any(bad);
+    wave_argmax(m, i);
+    double zl = 0.0;
+    if (!greedy && !bad && m != -INFINITY) {
+      double f[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) f[k] = (static_cast<double>(ms[k]) - static_cast<double>(m)) * inv_tau;
+      exp_lockstep<K>(f);
+#pragma unroll
+      for (int k = 0; k < K; ++k) zl += (ms[k] == -INFINITY) ? 0.0 : zs[k] * f[k];
+    }
+    const double zt = readlane_d(wave_incl_scan(zl), 63);
     if (lane == 0) {
-      redm[r * kWaves + wave] = mx[r];
-      redi[r * kWaves + wave] = anyb ? -1 : ix[r];
+      out[r].m = m;
+      out[r].idx = bad ? -1 : (i == 0x7fffffff ? v0 : i);
+      out[r].z = zt;
     }
-  }
-  __syncthreads();
-  float m[R];
-  bool live[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    m[r] = -INFINITY;
-    int idx = 0x7fffffff;
-    bool anybad = false;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float om = redm[r * kWaves + w];
-      const int oi = redi[r * kWaves + w];
-      anybad |= oi < 0;
-      if (w == 0 || om > m[r] || (om == m[r] && oi < idx)) {
-        m[r] = om;
-        idx = oi;
-      }
-    }
-    if (tid == 0) {
-      out[r].m = m[r];
-      out[r].idx = anybad ? -1 : (idx == 0x7fffffff ? v0 : idx);
-    }
-    live[r] = !greedy && m[r] != -INFINITY && !anybad;
-  }
-  double z[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) z[r] = 0.0;
-  for (int c = c0; c < c1; ++c) {
-    f32x4 v[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) v[r] = load4<kLds>(rows + r * ld + 4 * c, n - 4 * c);
-    double t[4 * R];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        t[4 * r + e] = (static_cast<double>(v[r][e]) - static_cast<double>(m[r])) * inv_tau;
-    exp_lockstep<4 * R>(t);
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) z[r] += (live[r] && 4 * c + e < n) ? t[4 * r + e] : 0.0;
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) z[r] = readlane_d(wave_incl_scan(z[r]), 63);
-  if (lane == 0) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) redz[r * kWaves + wave] = z[r];
-  }
-  __syncthreads();
-  if (tid < R) {
-    double t = 0.0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) t += redz[tid * kWaves + w];
-    out[tid].z = t;
   }
   __syncthreads();
 }
@@ -459,9 +457,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   __shared__ int rej_tok[kMaxT];
   __shared__ double s_ru[kMaxT], s_fu[kMaxT];  // accept draw of node c, final draw at node u
   __shared__ double rej_c[kMaxT];
-  __shared__ float redm[kMaxEager * kWaves];
-  __shared__ int redi[kMaxEager * kWaves];
-  __shared__ double redz[kMaxEager * kWaves];
+  __shared__ __attribute__((aligned(16))) double row_partials[2 * kThreads];  // one row's statistics partials
   __shared__ Rec s_rec[kMaxEager];
   // merged statistics of the eager rows (index r < E) and of the current deeper row (index kMaxEager)
   __shared__ float e_m[kMaxEager + 1];
@@ -556,16 +552,16 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
     if (kFits) {
       switch (E) {
         case 1:
-          slice_stats_rows<1, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+          slice_stats_rows<1, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, cur_lbuf);
           break;
         case 2:
-          slice_stats_rows<2, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+          slice_stats_rows<2, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, cur_lbuf);
           break;
         case 4:
-          slice_stats_rows<4, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+          slice_stats_rows<4, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, cur_lbuf);
           break;
         default:
-          slice_stats_rows<8, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+          slice_stats_rows<8, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, cur_lbuf);
           break;
       }
       if (tid < E) st_rec(&eager[wg * E + tid], s_rec[tid]);
@@ -624,7 +620,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       __syncthreads();
       const Rec* rows = part;  // members' statistics of a row past the eager ones
       if (u >= E) {  // a deeper row: its statistics now
-        slice_stats_rows<1, kFits>(cl, ld, n, v0, a.greedy, a.inv_tau, s_rec, redm, redi, redz);
+        slice_stats_rows<1, kFits>(cl, ld, n, v0, a.greedy, a.inv_tau, s_rec, row_partials);
         if (tid == 0) st_rec(&part[buf * NW + wg], s_rec[0]);
         team_barrier(ctr, NW * ++phase, &sh_fail);
         if (sh_fail) break;
