@@ -46,6 +46,12 @@ SMALL = [
                             max_depth=6)),
     ("single_node", dict(B=3, Hq=4, Hkv=2, D=128, dtype="bf16", prefix=[0, 1, 31], tree="fixed", parent=[-1])),
     ("deep_chain_t256", dict(B=1, Hq=2, Hkv=1, D=128, dtype="bf16", prefix=[100], tree="chain", gamma=255)),
+    # few keys per row: a row sum that is not the sum over all four lanes of the
+    # row shows up here (with thousands of keys it averages out)
+    ("rows128_chain_short_prefix", dict(B=1, Hq=2, Hkv=1, D=128, dtype="bf16", prefix=[96], tree="chain",
+                                        gamma=95)),
+    ("rows256_tree_short_prefix", dict(B=1, Hq=16, Hkv=1, D=128, dtype="bf16", prefix=[5], tree="random", T=64,
+                                       max_depth=6)),
 ]
 
 

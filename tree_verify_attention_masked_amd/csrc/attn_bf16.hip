@@ -30,10 +30,106 @@ namespace {
 
 constexpr int kD = 128;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kTile = 64;             // keys per iteration (4 pages)
-constexpr int kKS = kD + 8;           // LDS row stride of K (bf16), 272 B
-constexpr int kVS = kTile + 8;        // LDS row stride of V^T (bf16 slots), 144 B
-constexpr int kMaxSplitPages = 1024;  // pages per split (planning keeps below)
+constexpr int kPageBytes = kBlockSize * kD * 2;  // one page of one head: 4 KB
+constexpr int kTileBytes = 8 * kPageBytes;       // 4 K pages, then 4 V pages: 64 keys
+constexpr int kMaxSplitPages = 1024;             // pages per split (planning keeps below)
+
+__device__ __forceinline__ void wait_vm0() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(p)));
+}
+
+// Fragments of the two pages of a 32-key half (page A at LDS byte address base,
+// page B at base + 4096), complete on return.  Issued from assembly: the compiler
+// would otherwise drain every in-flight direct global->LDS load (the next tile)
+// before them.
+// K: kA[c], kB[c] = ds_read_b128 at base (+4096) + koff[c].
+__device__ __forceinline__ void read_k_pair(u32x4 (&kA)[4], u32x4 (&kB)[4], uint32_t base, const uint32_t (&koff)[4]) {
+  __asm__ volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\t"
+      "ds_read_b128 %5, %9 offset:4096\n\t"
+      "ds_read_b128 %6, %10 offset:4096\n\t"
+      "ds_read_b128 %7, %11 offset:4096\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kA[0]), "=&v"(kA[1]), "=&v"(kA[2]), "=&v"(kA[3]), "=&v"(kB[0]), "=&v"(kB[1]), "=&v"(kB[2]), "=&v"(kB[3])
+      : "v"(base + koff[0]), "v"(base + koff[1]), "v"(base + koff[2]), "v"(base + koff[3])
+      : "memory");
+}
+// V^T: vA[dt], vB[dt] = ds_read_b64_tr_b16 at base (+4096) + voff[dt].
+__device__ __forceinline__ void read_vt_pair(u32x2 (&vA)[8], u32x2 (&vB)[8], uint32_t base,
+                                             const uint32_t (&voff)[8]) {
+  __asm__ volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %17\n\t"
+      "ds_read_b64_tr_b16 %2, %18\n\t"
+      "ds_read_b64_tr_b16 %3, %19\n\t"
+      "ds_read_b64_tr_b16 %4, %20\n\t"
+      "ds_read_b64_tr_b16 %5, %21\n\t"
+      "ds_read_b64_tr_b16 %6, %22\n\t"
+      "ds_read_b64_tr_b16 %7, %23\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %9, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %10, %18 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %11, %19 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %12, %20 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %13, %21 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %14, %22 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:4096\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(vA[0]), "=&v"(vA[1]), "=&v"(vA[2]), "=&v"(vA[3]), "=&v"(vA[4]), "=&v"(vA[5]), "=&v"(vA[6]), "=&v"(vA[7]),
+        "=&v"(vB[0]), "=&v"(vB[1]), "=&v"(vB[2]), "=&v"(vB[3]), "=&v"(vB[4]), "=&v"(vB[5]), "=&v"(vB[6]), "=&v"(vB[7])
+      : "v"(base + voff[0]), "v"(base + voff[1]), "v"(base + voff[2]), "v"(base + voff[3]), "v"(base + voff[4]),
+        "v"(base + voff[5]), "v"(base + voff[6]), "v"(base + voff[7])
+      : "memory");
+}
+
+// Max / sum over the four lanes l%16 + 16q of a row (VALU lane swaps, no LDS):
+// v_permlane16_swap of a value with a copy of itself leaves rows (0,1) and (2,3)
+// of the two registers exchanged, so combining them joins lanes l and l^16;
+// v_permlane32_swap likewise joins l and l^32.  Written in assembly because,
+// given one value for both operands, the compiler keeps only one of the two
+// results of the swap builtins.
+__device__ __forceinline__ float quad_max(float x) {
+  float y;
+  __asm__(
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane16_swap_b32 %0, %1\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32 %0, %0, %1\n\t"
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %1\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "+v"(x), "=&v"(y));
+  return x;
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  float y;
+  __asm__(
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane16_swap_b32 %0, %1\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32 %0, %0, %1\n\t"
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %1\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32 %0, %0, %1"
+      : "+v"(x), "=&v"(y));
+  return x;
+}
 
 struct TArgs2 {
   const uint16_t* q;
@@ -86,8 +182,7 @@ __device__ int build_ancestors_lds(const int* par, int T, uint64_t* anc) {
 template <int NRB>
 __global__ __launch_bounds__(256) void attn_tile_kernel(const TArgs2 a) {
   constexpr int RT = 64 * NRB;  // rows per workgroup
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * kKS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * kVS];
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[2 * kTileBytes];  // 2 x (4 K pages, 4 V pages)
   __shared__ uint64_t anc[kMaxT * 4];
   __shared__ int s_par[kMaxT];
   __shared__ int s_blk[kMaxSplitPages];
@@ -169,125 +264,133 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TArgs2 a) {
     for (int dt = 0; dt < 8; ++dt) o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Staging: thread (key kin = tid/16, dims d0 = (tid%16)*8) moves, for each
-  // 32-key half st and 16-key quarter h, one 16-byte chunk of K and of V.
-  // Loads are unconditional (pages past the split re-read its last page);
-  // validity is a flag applied when the chunk is written to LDS.
-  const int kin = tid >> 4;
-  const int d0 = (tid & 15) * 8;
-  u32x4 kr[2][2], vr[2][2];
-  bool okr[2][2];
-  auto load_tile = [&](int it) {
+  // Tiles of 64 keys (4 pages), double-buffered in LDS.  For tile `it`, wave w
+  // brings page 4*it + w straight from HBM into LDS (direct global->LDS loads):
+  // K key-major with 16-byte chunk c of key k at position c ^ k, V key-major with
+  // chunk c at c ^ 2*(k % 8), so the K fragments are conflict-free ds_read_b128
+  // and the V^T fragments conflict-free ds_read_b64_tr_b16.  Pages past the split
+  // (or with an invalid block) re-read a valid page and are masked; their V rows
+  // are zeroed so that p = 0 never meets a NaN.
+  const int dma_key = lane >> 4, dma_pos = lane & 15;
+  auto tile_page = [&](int it) { return p0 + 4 * it + wave; };
+  auto page_block = [&](int pg) { return pg < p1 ? s_blk[pg - p0] : -1; };
+  auto issue_tile = [&](int it) {
+    const int pg = tile_page(it);
+    const int blk = page_block(min(pg, p1 - 1));
+    const long base = (static_cast<long>(blk < 0 ? 0 : blk) * a.Hkv + g) * (kBlockSize * kD);
+    uint8_t* kdst = tiles + (it & 1) * kTileBytes + wave * kPageBytes;
+    uint8_t* vdst = kdst + 4 * kPageBytes;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int pg = p0 + 4 * it + 2 * st + h;
-        const int page = min(pg, max(p1 - 1, p0));
-        const int blk = p1 > p0 ? s_blk[page - p0] : -1;
-        okr[st][h] = (pg * kBlockSize + kin < kend) && blk >= 0;
-        const long off = ((static_cast<long>(max(blk, 0)) * a.Hkv + g) * kBlockSize + kin) * kD + d0;
-        kr[st][h] = *reinterpret_cast<const u32x4*>(a.k + off);
-        vr[st][h] = *reinterpret_cast<const u32x4*>(a.v + off);
-      }
+    for (int t = 0; t < 4; ++t) {
+      const int key = 4 * t + dma_key;
+      __builtin_amdgcn_global_load_lds(a.k + base + key * kD + ((dma_pos ^ key) * 8), kdst + t * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.v + base + key * kD + ((dma_pos ^ (2 * (key & 7))) * 8), vdst + t * 1024, 16, 0,
+                                       0);
+    }
   };
+  // per-lane LDS offsets of the fragments within one page
+  uint32_t k_off[4], vt_off[8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) k_off[c] = l16 * 256 + (((4 * c + quad) ^ l16) * 16);
+  {
+    const int vkey = 4 * quad + (l16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      vt_off[dt] = vkey * 256 + (((2 * dt + ((l16 & 3) >> 1)) ^ (2 * (vkey & 7))) * 16) + (l16 & 1) * 8;
+  }
+
   __syncthreads();  // s_blk and anc are ready
-  if (n_it > 0) load_tile(0);
+  if (n_it > 0) issue_tile(0);
 
   for (int it = 0; it < n_it; ++it) {
-    __syncthreads();  // the previous tile is no longer read
+    wait_vm0();  // this wave's page of tile `it` has landed
+    {
+      const int pg = tile_page(it);
+      const int nvalid = page_block(pg) < 0 ? 0 : min(kBlockSize, kend - pg * kBlockSize);
+      uint8_t* vpage = tiles + (it & 1) * kTileBytes + 4 * kPageBytes + wave * kPageBytes;
+      if (nvalid < kBlockSize) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<u32x4*>(&Ks[(st * 32 + h * 16 + kin) * kKS + d0]) =
-            okr[st][h] ? kr[st][h] : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t a0 = okr[st][0] ? vr[st][0][e2] : 0u, a1 = okr[st][1] ? vr[st][1][e2] : 0u;
-        const uint32_t lo = (a0 & 0xffffu) | (a1 << 16);
-        const uint32_t hi = (a0 >> 16) | (a1 & 0xffff0000u);
-        const int d = d0 + 2 * e2;
-        *reinterpret_cast<uint32_t*>(&Vt[d * kVS + st * 32 + 2 * kin]) = lo;
-        *reinterpret_cast<uint32_t*>(&Vt[(d + 1) * kVS + st * 32 + 2 * kin]) = hi;
+        for (int t = 0; t < 4; ++t)
+          if (4 * t + dma_key >= nvalid)
+            *reinterpret_cast<u32x4*>(vpage + (4 * t + dma_key) * 256 + dma_pos * 16) = u32x4{0, 0, 0, 0};
       }
     }
-    __syncthreads();
-    if (it + 1 < n_it) load_tile(it + 1);
+    __syncthreads();  // tile `it` is complete and every wave is done with tile it-1
+    if (it + 1 < n_it) issue_tile(it + 1);
 
+    const uint8_t* kt = tiles + (it & 1) * kTileBytes;
+    const uint8_t* vt = kt + 4 * kPageBytes;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int key0 = (p0 + 4 * it + 2 * st) * kBlockSize;
+    for (int h = 0; h < 2; ++h) {  // 32-key halves: pages 2h (A) and 2h+1 (B)
+      const int key0 = (p0 + 4 * it + 2 * h) * kBlockSize;
       const bool need_mask = key0 + 32 > Lb || key0 + 32 > kend;
+      u32x4 kr[2][4];
+      u32x2 vA[8], vB[8];
+      read_k_pair(kr[0], kr[1], lds_addr(kt + (2 * h) * kPageBytes), k_off);
+      read_vt_pair(vA, vB, lds_addr(vt + (2 * h) * kPageBytes), vt_off);
       bf16x8 kf[2][4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          kf[h][c] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(&Ks[(st * 32 + h * 16 + l16) * kKS + c * 32 + quad * 8]));
-      bf16x8 pf[NRB];
+        for (int c = 0; c < 4; ++c) kf[pb][c] = __builtin_bit_cast(bf16x8, kr[pb][c]);
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h][c], qf[rb][c], sacc[h], 0, 0, 0);
-        // lane holds S[row l16][key h*16 + quad*4 + i]; PV slot j <-> (h = j % 2, i = j / 2)
+        for (int c = 0; c < 4; ++c) {
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][c], qf[rb][c], sa, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][c], qf[rb][c], sb, 0, 0, 0);
+        }
+        // lane holds S[row l16][key0 + 4*quad + i] (page A) and [key0 + 16 + 4*quad + i] (page B);
+        // PV slot i <-> page A key 4*quad + i, slot 4 + i <-> page B key 4*quad + i
         float sv[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int i = 0; i < 4; ++i) {
+          sv[i] = sa[i] * a.sl2;
+          sv[4 + i] = sb[i] * a.sl2;
+        }
+        if (need_mask) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = sacc[h][i] * a.sl2;
-            if (need_mask) {
-              const int pos = key0 + h * 16 + quad * 4 + i;
-              bool ok = pos < kend;
-              if (ok && pos >= Lb) {
-                const int jj = pos - Lb;
-                ok = (anc[node_of[rb] * 4 + (jj >> 6)] >> (jj & 63)) & 1ull;
-              }
-              x = ok ? x : -INFINITY;
+          for (int j = 0; j < 8; ++j) {
+            const int pos = key0 + (j >> 2) * 16 + 4 * quad + (j & 3);
+            bool ok = pos < kend;
+            if (ok && pos >= Lb) {
+              const int jj = pos - Lb;
+              ok = (anc[node_of[rb] * 4 + (jj >> 6)] >> (jj & 63)) & 1ull;
             }
-            sv[2 * i + h] = x;
+            sv[j] = ok ? sv[j] : -INFINITY;
           }
-        float mx = sv[0];
-#pragma unroll
-        for (int j2 = 1; j2 < 8; ++j2) mx = fmaxf(mx, sv[j2]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        }
+        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        mx = quad_max(mx);
         const float m_new = fmaxf(m_run[rb], mx);
         const bool none = (m_new == -INFINITY);
-        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        bf16x8 pf;
         float psum = 0.f;
 #pragma unroll
-        for (int j2 = 0; j2 < 8; ++j2) {
-          const float p = none ? 0.f : __builtin_amdgcn_exp2f(sv[j2] - m_new);
-          psum += p;
-          pf[rb][j2] = static_cast<__bf16>(p);
+        for (int j = 0; j < 8; ++j) {
+          const float pj = none ? 0.f : __builtin_amdgcn_exp2f(sv[j] - m_new);
+          psum += pj;
+          pf[j] = static_cast<__bf16>(pj);
         }
-        l_run[rb] = l_run[rb] * alpha + psum;
+        if (!__all(m_new == m_run[rb])) {  // the running max moved somewhere in the wave: rescale
+          const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+          l_run[rb] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) o[rb][dt] *= alpha;
+        }
+        l_run[rb] += psum;
         m_run[rb] = m_new;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[rb][dt] *= alpha;
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const bf16x8 vf = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&Vt[(dt * 16 + l16) * kVS + st * 32 + quad * 8]));
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-          o[rb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb], o[rb][dt], 0, 0, 0);
+        for (int dt = 0; dt < 8; ++dt) {
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{vA[dt][0], vA[dt][1], vB[dt][0], vB[dt][1]});
+          o[rb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[rb][dt], 0, 0, 0);
+        }
       }
     }
   }
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    l_run[rb] += __shfl_xor(l_run[rb], 16);
-    l_run[rb] += __shfl_xor(l_run[rb], 32);
-  }
+  for (int rb = 0; rb < NRB; ++rb) l_run[rb] = quad_sum(l_run[rb]);
   report(a.status, b, err);
 
   const bool direct = (a.splits == 1);
