@@ -1,7 +1,8 @@
 """GPU parity of spec_tree_attn against the fp64 oracle (called through the C ABI).
 
-Tolerance: bf16 outputs |gpu - oracle| <= 2e-2 + 1e-2 |oracle|; fp32 outputs
-1e-5 + 1e-5 |oracle|.  Small cases compare every output and span several KV
+Tolerance: bf16 outputs |gpu - oracle| <= 2^-8 (attn(|V|) + |oracle|) + 1e-5,
+the bf16 rounding of the probabilities and of the output (helpers.py derives
+it); fp32 outputs 1e-5 + 1e-5 |oracle|.  Small cases compare every output and span several KV
 tiles, several splits, a ragged last page and each kernel variant (key-split
 for <= 16 rows per kv head, 64-row and 256-row tiles); the five configurations
 run at full size, all outputs where the oracle is quick, sampled rows
@@ -12,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import DevWorkload, assert_attn_close, attn_to_f64
+from helpers import DevWorkload, assert_attn_close, attn_to_f64, oracle_attn
 from workloads import make_config, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -22,9 +23,8 @@ def _run_full(w):
     d = DevWorkload(w)
     out = d.attn()
     torch.cuda.synchronize()
-    ref = oracle.tree_attention(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_lens, w.parent,
-                                w.scale, dtype=w.dtype)
-    err = assert_attn_close(attn_to_f64(w, out), ref, w.dtype, w.name)
+    ref, ref_abs = oracle_attn(w)
+    err = assert_attn_close(attn_to_f64(w, out), ref, w.dtype, w.name, ref_abs)
     assert int(d.status.abs().sum()) == 0
     return err
 
@@ -79,10 +79,9 @@ def test_config_sampled_rows(cfg):
     rng = np.random.default_rng(cfg)
     rows = [(int(rng.integers(w.B)), int(rng.integers(w.T)), int(rng.integers(w.Hq))) for _ in range(200)]
     rows += [(w.B - 1, i, h) for i in range(w.T) for h in (0, w.Hq - 1)]  # every node of one sequence
-    ref = oracle.tree_attention_rows(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_lens, w.parent,
-                                     w.scale, rows, dtype=w.dtype)
+    ref, ref_abs = oracle_attn(w, rows)
     got = np.stack([out[b, i, h] for b, i, h in rows])
-    assert_attn_close(got, ref, w.dtype, w.name)
+    assert_attn_close(got, ref, w.dtype, w.name, ref_abs)
 
 
 def test_bad_inputs_are_reported_not_faulted():

@@ -94,10 +94,9 @@ def test_verify_step_end_to_end(cfg):
     acc, toks, nacc = d.reject()
     new_lens = d.compact(acc, nacc)
     torch.cuda.synchronize()
-    ref_out = oracle.tree_attention(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_lens, w.parent,
-                                    w.scale, dtype=w.dtype)
-    from helpers import assert_attn_close, attn_to_f64
-    assert_attn_close(attn_to_f64(w, out), ref_out, w.dtype, "step attention")
+    from helpers import assert_attn_close, attn_to_f64, oracle_attn
+    ref_out, ref_abs = oracle_attn(w)
+    assert_attn_close(attn_to_f64(w, out), ref_out, w.dtype, "step attention", ref_abs)
     ref = oracle_reject(w)
     assert compare_reject((acc, toks, nacc), ref) == 0
     k_ref, v_ref, lens_ref = oracle.kv_compact(w.k_cache, w.v_cache, w.block_table, w.prefix_lens,
