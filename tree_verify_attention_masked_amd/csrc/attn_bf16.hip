@@ -13,14 +13,17 @@
 // in "Report: Support nextn speculative decoding").
 //
 // A workgroup holds 4 waves x NRB blocks of 16 rows.  Per iteration the
-// workgroup stages a 64-key tile (4 pages) in LDS -- K in its natural layout,
-// V transposed with the keys of each 32-key half paired as (k, k+16) -- while
-// the next tile's loads are in flight in registers.  Each wave computes, per
-// 32-key half and row block, S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (8
-// scores of one row per lane), the online softmax in the log2 domain, and
-// O^T += V^T P^T with P packed in the (k, k+16) order.  Splits write
-// unnormalised partials (O, m, l); the last workgroup of a (b, g, rt) to finish
-// merges them (arrival counter in the workspace, reset by that workgroup).
+// workgroup takes a 64-key tile (4 pages of K, 4 of V), each wave bringing one
+// page of each straight from HBM into LDS (direct global->LDS loads, double
+// buffered, so the next tile streams in while this one is used).  Each wave then
+// computes, per 32-key half (a pair of pages) and row block, S^T = K Q^T with
+// v_mfma_f32_16x16x32_bf16 (8 scores of one row per lane), the online softmax in
+// the log2 domain, and O^T += V^T P^T with v_mfma_f32_16x16x32_bf16 whose 32-key
+// operand holds 4 keys of each page per lane (V^T fragments from
+// ds_read_b64_tr_b16).  One split writes the normalised output; several write
+// unnormalised partials (O, m, l) and the last workgroup of a (b, g, rt) to
+// finish merges them (arrival counter in the workspace, reset by that
+// workgroup).
 #include <algorithm>
 
 #include "common.h"
@@ -90,6 +93,13 @@ __device__ __forceinline__ void read_vt_pair(u32x2 (&vA)[8], u32x2 (&vB)[8], uin
       : "v"(base + voff[0]), "v"(base + voff[1]), "v"(base + voff[2]), "v"(base + voff[3]), "v"(base + voff[4]),
         "v"(base + voff[5]), "v"(base + voff[6]), "v"(base + voff[7])
       : "memory");
+}
+
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Max / sum over the four lanes l%16 + 16q of a row (VALU lane swaps, no LDS):
@@ -394,12 +404,11 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TArgs2 a) {
   report(a.status, b, err);
 
   const bool direct = (a.splits == 1);
+  if (direct) {
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const int r = row_base + rb * 16 + l16;
-    if (r >= a.R) continue;
-    const int rl = r - rt * RT;
-    if (direct) {
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r = row_base + rb * 16 + l16;
+      if (r >= a.R) continue;
       const int node = r / a.G, hh = r % a.G;
       uint16_t* op = a.out + ((static_cast<long>(b) * a.T + node) * a.Hq + g * a.G + hh) * kD;
       const float inv = l_run[rb] > 0.f ? 1.f / l_run[rb] : 0.f;
@@ -411,76 +420,93 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TArgs2 a) {
             f32_to_bf16(o[rb][dt][2] * inv) | (static_cast<uint32_t>(f32_to_bf16(o[rb][dt][3] * inv)) << 16);
         *reinterpret_cast<u32x2*>(op + dt * 16 + quad * 4) = u32x2{w0, w1};
       }
-    } else {
-      float* po = a.part_o + (item * RT + rl) * kD;
+    }
+    return;
+  }
+
+  // Split partials, one 16-row block of 2048 floats per (wave, rb), in the
+  // accumulator layout: element i of o[rb][dt] of lane l at (dt*4 + i)*64 + l, so
+  // that each store (and each load of the merge) covers 64 consecutive floats.
+  // Partials are read by another workgroup, possibly on another XCD (whose L2 is
+  // not coherent with this one): they are written and read as relaxed agent-scope
+  // atomics, and the arrival counter is bumped once this workgroup's stores have
+  // completed -- no fence, which would write back and invalidate the whole L2.
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + quad * 4) = o[rb][dt];
-      if (quad == 0) {
-        a.part_ml[(item * RT + rl) * 2 + 0] = m_run[rb];
-        a.part_ml[(item * RT + rl) * 2 + 1] = l_run[rb];
-      }
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int blk16 = wave * NRB + rb;
+    float* pb = a.part_o + (item * RT + blk16 * 16) * kD + lane;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st_agent(pb + (dt * 4 + i) * 64, o[rb][dt][i]);
+    if (quad == 0) {
+      st_agent(&a.part_ml[(item * RT + blk16 * 16 + l16) * 2 + 0], m_run[rb]);
+      st_agent(&a.part_ml[(item * RT + blk16 * 16 + l16) * 2 + 1], l_run[rb]);
     }
   }
-  if (direct) return;
-
-  // the last workgroup of (b, g, rt) to arrive merges every split
+  wait_vm0();  // this wave's partial stores have completed
   __syncthreads();
   if (tid == 0) {
-    __threadfence();
-    const unsigned prev = atomicAdd(&a.counters[bgr], 1u);
+    const unsigned prev = __hip_atomic_fetch_add(&a.counters[bgr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == static_cast<unsigned>(a.splits - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+
+  // The last workgroup of (b, g, rt) merges every split: wave w takes the 16-row
+  // blocks w, w+4, ..., each lane the elements it would hold in the accumulator
+  // layout, with the loads of four splits in flight at a time.
   const long first = (bgr / a.n_rt) * a.splits * a.n_rt + rt;  // item of split 0
-  const int dseg = (tid & 15) * 8;
-  for (int rl = tid >> 4; rl < RT; rl += 16) {
-    const int r = rt * RT + rl;
-    if (r >= a.R) break;
-    float mstar = -INFINITY, lstar = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int sp0 = 0; sp0 < a.splits; sp0 += 8) {
-      float ms[8], ls[8];
-      f32x4 x0[8], x1[8];
+  for (int blk16 = wave; blk16 < RT / 16; blk16 += 4) {
+    const int r = rt * RT + blk16 * 16 + l16;
+    if (rt * RT + blk16 * 16 >= a.R) break;
+    float mstar = -INFINITY, lstar = 0.f, acc[32];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+    for (int e = 0; e < 32; ++e) acc[e] = 0.f;
+    for (int sp0 = 0; sp0 < a.splits; sp0 += 4) {
+      float ms[4], ls[4], x[4][32];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
         ms[k] = -INFINITY;
         ls[k] = 0.f;
-        x0[k] = x1[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 32; ++e) x[k][e] = 0.f;
         if (sp0 + k < a.splits) {
           const long it2 = first + static_cast<long>(sp0 + k) * a.n_rt;
-          ms[k] = a.part_ml[(it2 * RT + rl) * 2];
-          ls[k] = a.part_ml[(it2 * RT + rl) * 2 + 1];
-          const float* po = a.part_o + (it2 * RT + rl) * kD + dseg;
-          x0[k] = *reinterpret_cast<const f32x4*>(po);
-          x1[k] = *reinterpret_cast<const f32x4*>(po + 4);
+          ms[k] = ld_agent(&a.part_ml[(it2 * RT + blk16 * 16 + l16) * 2 + 0]);
+          ls[k] = ld_agent(&a.part_ml[(it2 * RT + blk16 * 16 + l16) * 2 + 1]);
+          const float* pb = a.part_o + (it2 * RT + blk16 * 16) * kD + lane;
+#pragma unroll
+          for (int e = 0; e < 32; ++e) x[k][e] = ld_agent(pb + e * 64);
         }
       }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 4; ++k) {
         if (ms[k] == -INFINITY) continue;
         const float m_new = fmaxf(mstar, ms[k]);
-        const float fa = __builtin_amdgcn_exp2f(mstar - m_new);
+        const float fa = __builtin_amdgcn_exp2f(mstar - m_new);  // 0 while mstar is -inf
         const float fb = __builtin_amdgcn_exp2f(ms[k] - m_new);
         lstar = lstar * fa + ls[k] * fb;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[e] = acc[e] * fa + x0[k][e] * fb;
-          acc[4 + e] = acc[4 + e] * fa + x1[k][e] * fb;
-        }
+        for (int e = 0; e < 32; ++e) acc[e] = acc[e] * fa + x[k][e] * fb;
         mstar = m_new;
       }
     }
-    const float inv = lstar > 0.f ? 1.f / lstar : 0.f;
-    const int node = r / a.G, hh = r % a.G;
-    uint16_t* op = a.out + ((static_cast<long>(b) * a.T + node) * a.Hq + g * a.G + hh) * kD + dseg;
-    uint32_t wds[4];
+    if (r < a.R) {
+      const int node = r / a.G, hh = r % a.G;
+      uint16_t* op = a.out + ((static_cast<long>(b) * a.T + node) * a.Hq + g * a.G + hh) * kD;
+      const float inv = lstar > 0.f ? 1.f / lstar : 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      wds[e] = f32_to_bf16(acc[2 * e] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * e + 1] * inv)) << 16);
-    *reinterpret_cast<u32x4*>(op) = u32x4{wds[0], wds[1], wds[2], wds[3]};
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint32_t w0 = f32_to_bf16(acc[dt * 4 + 0] * inv) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[dt * 4 + 1] * inv)) << 16);
+        const uint32_t w1 = f32_to_bf16(acc[dt * 4 + 2] * inv) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[dt * 4 + 3] * inv)) << 16);
+        *reinterpret_cast<u32x2*>(op + dt * 16 + quad * 4) = u32x2{w0, w1};
+      }
+    }
   }
-  if (tid == 0) atomicExch(&a.counters[bgr], 0u);
+  if (tid == 0) __hip_atomic_store(&a.counters[bgr], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int NRB>
