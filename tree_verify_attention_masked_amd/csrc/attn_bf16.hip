@@ -12,7 +12,10 @@
 // bitset of the row's node (the tree_mask of the EAGLE implementation summary
 // in "Report: Support nextn speculative decoding").
 //
-// A workgroup holds 4 waves x NRB blocks of 16 rows.  Per iteration the
+// A workgroup holds 4 waves x NRB blocks of 16 rows (NRB = 2: 128 rows, at
+// most 256 registers per lane, two workgroups per CU, so that while one wave
+// of a SIMD waits on its softmax chain the other keeps the matrix core busy).
+// Per iteration the
 // workgroup takes a 64-key tile (4 pages of K, 4 of V), each wave bringing one
 // page of each straight from HBM into LDS (direct global->LDS loads, double
 // buffered, so the next tile streams in while this one is used).  Each wave then
@@ -190,7 +193,7 @@ __device__ int build_ancestors_lds(const int* par, int T, uint64_t* anc) {
 }
 
 template <int NRB>
-__global__ __launch_bounds__(256) void attn_tile_kernel(const TArgs2 a) {
+__global__ __launch_bounds__(256, NRB == 2 ? 2 : 1) void attn_tile_kernel(const TArgs2 a) {
   constexpr int RT = 64 * NRB;  // rows per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t tiles[2 * kTileBytes];  // 2 x (4 K pages, 4 V pages)
   __shared__ uint64_t anc[kMaxT * 4];
@@ -334,6 +337,31 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TArgs2 a) {
     for (int h = 0; h < 2; ++h) {  // 32-key halves: pages 2h (A) and 2h+1 (B)
       const int key0 = (p0 + 4 * it + 2 * h) * kBlockSize;
       const bool need_mask = key0 + 32 > Lb || key0 + 32 > kend;
+      // Bit t of vis[rb] (before the shift by 4*quad) says whether key key0 + t is
+      // visible to the lane's row: prefix keys are, tree keys by the ancestor
+      // bitset, keys at or past the split end are not.  Shifts are uniform.
+      uint32_t vis[NRB];
+      if (need_mask) {
+        const int d = key0 - Lb;  // tree index of key0 (negative inside the prefix)
+        const int nv = kend - key0;
+        const uint32_t endm = nv >= 32 ? 0xFFFFFFFFu : (nv <= 0 ? 0u : ((1u << nv) - 1u));
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const uint64_t* an = anc + node_of[rb] * 4;
+          uint32_t w;
+          if (d >= 0) {
+            const int wi = d >> 6, sh = d & 63;
+            const uint64_t lo = an[wi];
+            const uint64_t hi = wi + 1 < 4 ? an[wi + 1] : 0ull;
+            w = static_cast<uint32_t>(sh == 0 ? lo : ((lo >> sh) | (hi << (64 - sh))));
+          } else if (d > -32) {
+            w = (static_cast<uint32_t>(an[0]) << (-d)) | ((1u << (-d)) - 1u);
+          } else {
+            w = 0xFFFFFFFFu;
+          }
+          vis[rb] = (w & endm) >> (4 * quad);
+        }
+      }
       u32x4 kr[2][4];
       u32x2 vA[8], vB[8];
       read_k_pair(kr[0], kr[1], lds_addr(kt + (2 * h) * kPageBytes), k_off);
@@ -352,39 +380,33 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TArgs2 a) {
           sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][c], qf[rb][c], sb, 0, 0, 0);
         }
         // lane holds S[row l16][key0 + 4*quad + i] (page A) and [key0 + 16 + 4*quad + i] (page B);
-        // PV slot i <-> page A key 4*quad + i, slot 4 + i <-> page B key 4*quad + i
+        // PV slot i <-> page A key 4*quad + i, slot 4 + i <-> page B key 4*quad + i.
+        // Scores stay unscaled here; the scale enters the exponent.
         float sv[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sv[i] = sa[i] * a.sl2;
-          sv[4 + i] = sb[i] * a.sl2;
+          sv[i] = sa[i];
+          sv[4 + i] = sb[i];
         }
         if (need_mask) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int pos = key0 + (j >> 2) * 16 + 4 * quad + (j & 3);
-            bool ok = pos < kend;
-            if (ok && pos >= Lb) {
-              const int jj = pos - Lb;
-              ok = (anc[node_of[rb] * 4 + (jj >> 6)] >> (jj & 63)) & 1ull;
-            }
-            sv[j] = ok ? sv[j] : -INFINITY;
-          }
+          for (int j = 0; j < 8; ++j) sv[j] = ((vis[rb] >> ((j >> 2) * 16 + (j & 3))) & 1u) ? sv[j] : -INFINITY;
         }
         float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
         mx = quad_max(mx);
         const float m_new = fmaxf(m_run[rb], mx);
         const bool none = (m_new == -INFINITY);
+        const float msl = -m_new * a.sl2;
         bf16x8 pf;
         float psum = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float pj = none ? 0.f : __builtin_amdgcn_exp2f(sv[j] - m_new);
+          const float pj = none ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sv[j], a.sl2, msl));
           psum += pj;
           pf[j] = static_cast<__bf16>(pj);
         }
         if (!__all(m_new == m_run[rb])) {  // the running max moved somewhere in the wave: rescale
-          const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+          const float alpha = none ? 1.f : __builtin_amdgcn_exp2f((m_run[rb] - m_new) * a.sl2);
           l_run[rb] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) o[rb][dt] *= alpha;
@@ -440,7 +462,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TArgs2 a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) st_agent(pb + (dt * 4 + i) * 64, o[rb][dt][i]);
     if (quad == 0) {
-      st_agent(&a.part_ml[(item * RT + blk16 * 16 + l16) * 2 + 0], m_run[rb]);
+      st_agent(&a.part_ml[(item * RT + blk16 * 16 + l16) * 2 + 0], m_run[rb] * a.sl2);  // log2 units
       st_agent(&a.part_ml[(item * RT + blk16 * 16 + l16) * 2 + 1], l_run[rb]);
     }
   }
@@ -457,16 +479,17 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TArgs2 a) {
   // blocks w, w+4, ..., each lane the elements it would hold in the accumulator
   // layout, with the loads of four splits in flight at a time.
   const long first = (bgr / a.n_rt) * a.splits * a.n_rt + rt;  // item of split 0
+  constexpr int KS = NRB == 2 ? 2 : 4;  // splits whose loads are in flight together
   for (int blk16 = wave; blk16 < RT / 16; blk16 += 4) {
     const int r = rt * RT + blk16 * 16 + l16;
     if (rt * RT + blk16 * 16 >= a.R) break;
     float mstar = -INFINITY, lstar = 0.f, acc[32];
 #pragma unroll
     for (int e = 0; e < 32; ++e) acc[e] = 0.f;
-    for (int sp0 = 0; sp0 < a.splits; sp0 += 4) {
-      float ms[4], ls[4], x[4][32];
+    for (int sp0 = 0; sp0 < a.splits; sp0 += KS) {
+      float ms[KS], ls[KS], x[KS][32];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < KS; ++k) {
         ms[k] = -INFINITY;
         ls[k] = 0.f;
 #pragma unroll
@@ -481,7 +504,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TArgs2 a) {
         }
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < KS; ++k) {
         if (ms[k] == -INFINITY) continue;
         const float m_new = fmaxf(mstar, ms[k]);
         const float fa = __builtin_amdgcn_exp2f(mstar - m_new);  // 0 while mstar is -inf
@@ -538,14 +561,14 @@ AttnPlan plan_attn(int B, int T, int Hq, int Hkv, int D, int max_blocks, int dty
     plan_stream(p, B, Hkv, max_blocks);
     return p;
   }
-  // many rows: 128-row tiles, or 256-row tiles from 1024 rows up
+  // many rows: 128-row tiles, two workgroups per CU
   p.mode = 2;
-  p.nrb = p.rows >= 1024 ? 4 : 2;
+  p.nrb = 2;
   p.rt = 64 * p.nrb;
   p.n_rt = (p.rows + p.rt - 1) / p.rt;
   const long base = static_cast<long>(B) * Hkv * p.n_rt;
-  // ~one workgroup per CU; at least 16 pages (256 keys) per split
-  long splits = std::max<long>(1, (256 + base - 1) / base);
+  // ~two workgroups per CU; at least 16 pages (256 keys) per split
+  long splits = std::max<long>(1, (512 + base - 1) / base);
   splits = std::min<long>(splits, std::max<long>(1, max_blocks / 16));
   long pps = (max_blocks + splits - 1) / splits;
   pps = (pps + 3) / 4 * 4;
@@ -590,7 +613,6 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& L, hipStream
     a.part_o = reinterpret_cast<float*>(static_cast<char*>(L.workspace) + head);
     a.part_ml = a.part_o + static_cast<size_t>(plan.items) * plan.rt * kD;
   }
-  if (plan.nrb == 4) return run_tile<4>(a, stream);
   return run_tile<2>(a, stream);
 }
 
