@@ -8,9 +8,13 @@ import torch
 import oracle
 import tree_verify_attention_masked_amd as stv
 
-# fp32 attention outputs vs the fp64 oracle
+# Attention outputs vs the fp64 oracle, per element.  The stated bar:
+#   bf16 |gpu - oracle| <= 2e-2 + 1e-2 |oracle|,  fp32 <= 1e-5 + 1e-5 |oracle|.
+BF16_ATOL, BF16_RTOL = 2e-2, 1e-2
 F32_ATOL, F32_RTOL = 1e-5, 1e-5
-# bf16 attention outputs vs the fp64 oracle, per element:
+# bf16 outputs must also meet a bound derived from the arithmetic, because the
+# stated bar is of the order of the outputs themselves once a row averages over
+# thousands of keys:
 #   |gpu - oracle| <= BF16_U2 * (attn(|V|) + |oracle|) + BF16_FLOOR
 # The inputs are exact bf16 values; scores are products of bf16 values summed in
 # fp32 (relative error ~1e-5, negligible).  Two roundings to bf16 (unit roundoff
@@ -100,11 +104,16 @@ def oracle_attn(w, rows=None):
 def assert_attn_close(got, ref, dtype, what="", ref_abs=None):
     got = np.asarray(got, dtype=np.float64)
     err = np.abs(got - ref)
+    atol, rtol = (BF16_ATOL, BF16_RTOL) if dtype == "bf16" else (F32_ATOL, F32_RTOL)
+    bad = ~(err <= atol + rtol * np.abs(ref))
+    if bad.any():
+        idx = np.argwhere(bad)[:5].tolist()
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside the stated tolerance; "
+                             f"max abs err {err.max():.3e}; first {idx}")
     if dtype == "bf16":
-        assert ref_abs is not None, "the bf16 bound needs attn(|V|) from the oracle"
+        assert ref_abs is not None, "the bf16 rounding bound needs attn(|V|) from the oracle"
         bad = ~(err <= BF16_U2 * (np.asarray(ref_abs) + np.abs(ref)) + BF16_FLOOR)
-    else:
-        bad = ~(err <= F32_ATOL + F32_RTOL * np.abs(ref))
+        what = f"{what} (bf16 rounding bound)"
     if bad.any():
         idx = np.argwhere(bad)[:5].tolist()
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; "

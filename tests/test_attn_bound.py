@@ -1,6 +1,7 @@
-"""The bf16 attention bound of the GPU parity tests, checked on the CPU.
+"""The bf16 rounding bound of the GPU parity tests, checked on the CPU.
 
-The bound (helpers.BF16_U2, derived there) must accept everything bf16
+Besides the stated tolerance, bf16 attention outputs must meet a bound derived
+from the arithmetic (helpers.BF16_U2, derived there).  It must accept everything bf16
 rounding can do to a correct kernel -- the oracle output rounded to bf16, and a
 model that rounds the probabilities to bf16 before the P.V product -- and must
 reject the mistakes it is there to catch, even with thousands of keys per row
