@@ -512,9 +512,15 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
     sh_owner = 0;
   }
   __syncthreads();
-  // child lists (increasing order) and checks, one node per thread: first_child[i]
-  // is the first c > i whose parent is i, next_sib[i] the first c > i sharing
-  // i's parent
+  // Checks, the Philox uniforms, and the child lists: bit c of kids[p] is set for
+  // every child c of p (an LDS atomic per node), so first_child[i] (the first c
+  // whose parent is i) and next_sib[i] (the first c > i sharing i's parent) are
+  // lowest-set-bit lookups, with no scan over the tree.  kids lives in cur_qbuf,
+  // which is first written when a deeper row is staged.
+  constexpr int kKW = kMaxT / 32;  // bitset words per parent
+  uint32_t* kids = reinterpret_cast<uint32_t*>(cur_qbuf);
+  for (int i = tid; i < T * kKW; i += kThreads) kids[i] = 0u;
+  __syncthreads();
   {
     int err = 0;
     for (int i = tid; i < T; i += kThreads) {
@@ -522,20 +528,32 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       const bool ok = (i == 0) ? p == -1 : (p >= 0 && p < i);
       if (!ok) err |= SPEC_DEV_PARENT;
       if (i > 0 && ok && (s_tok[i] < 0 || s_tok[i] >= V)) err |= SPEC_DEV_TOKEN;
-      int fc = -1, ns = -1;
-      for (int c = i + 1; c < T && (fc < 0 || (ns < 0 && ok && i > 0)); ++c) {
-        const int pc = s_par[c];
-        if (fc < 0 && pc == i) fc = c;
-        if (ns < 0 && ok && i > 0 && pc == p) ns = c;
-      }
-      first_child[i] = static_cast<int16_t>(fc);
-      next_sib[i] = static_cast<int16_t>(ok ? ns : -1);
+      if (i > 0 && ok) atomicOr(&kids[p * kKW + (i >> 5)], 1u << (i & 31));
       if (!a.greedy) {
         s_ru[i] = draw_uniform(a.seed, a.offset, b, i, 0);
         s_fu[i] = draw_uniform(a.seed, a.offset, b, i, 1);
       }
     }
     if (err) atomicOr(&sh_err, err);
+  }
+  __syncthreads();
+  for (int i = tid; i < T; i += kThreads) {
+    int fc = -1;
+    for (int w = 0; w < kKW && fc < 0; ++w) {
+      const uint32_t m = kids[i * kKW + w];
+      if (m) fc = w * 32 + __builtin_ctz(m);
+    }
+    const int p = s_par[i];
+    int ns = -1;
+    if (i > 0 && p >= 0 && p < i) {
+      for (int w = (i + 1) >> 5; w < kKW && ns < 0; ++w) {
+        uint32_t m = kids[p * kKW + w];
+        if (w == ((i + 1) >> 5)) m &= 0xFFFFFFFFu << ((i + 1) & 31);
+        if (m) ns = w * 32 + __builtin_ctz(m);
+      }
+    }
+    first_child[i] = static_cast<int16_t>(fc);
+    next_sib[i] = static_cast<int16_t>(ns);
   }
   __syncthreads();
 
