@@ -209,19 +209,40 @@ __device__ __forceinline__ void team_barrier(unsigned* ctr, unsigned target, int
 }
 
 // Starts copying rows [r * src_stride + i], r < nrows, i < n, of global memory
-// into LDS dst[r * ld + i] with direct global->LDS loads: one instruction moves
-// 64 consecutive floats (lane i to LDS dword i of the instruction's base), so
-// the copy needs no registers and almost no index arithmetic.  The data may be
-// read after this wave's vector-memory counter has drained and a workgroup
-// barrier.
+// into LDS dst[r * ld + i] (ld a multiple of 4) with direct global->LDS loads:
+// lane i of an instruction writes LDS word(s) i of the instruction's base, so
+// the copy needs no registers.  When the rows are 16-byte aligned one
+// instruction moves 256 consecutive floats (16 bytes a lane) and the last n % 4
+// elements of a row go 4 bytes a lane; otherwise every instruction moves 64
+// floats.  Instructions are dealt to the waves round-robin by a running count
+// (no division in the issue loop).  The data may be read after this wave's
+// vector-memory counter has drained and a workgroup barrier.
 __device__ __forceinline__ void stage_dma(float* dst, const float* src, int ld, long src_stride, int nrows, int n) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int per_row = (n + 63) >> 6;
-  for (int j = wave; j < nrows * per_row; j += kWaves) {
-    const int r = j / per_row, c = j - r * per_row;
-    const int i = c * 64 + lane;
-    if (i < n) __builtin_amdgcn_global_load_lds(src + r * src_stride + i, dst + r * ld + c * 64, 4, 0, 0);
+  const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15) == 0) && ((src_stride & 3) == 0);
+  int j = 0;
+  if (vec) {
+    const int n4 = n & ~3;
+    const int per_row = (n4 + 255) >> 8;
+    for (int r = 0; r < nrows; ++r)
+      for (int c = 0; c < per_row; ++c, ++j)
+        if ((j & (kWaves - 1)) == wave) {
+          const int i = c * 256 + lane * 4;
+          if (i < n4) __builtin_amdgcn_global_load_lds(src + r * src_stride + i, dst + r * ld + c * 256, 16, 0, 0);
+        }
+    if (n4 < n)
+      for (int r = 0; r < nrows; ++r, ++j)
+        if ((j & (kWaves - 1)) == wave && lane < n - n4)
+          __builtin_amdgcn_global_load_lds(src + r * src_stride + n4 + lane, dst + r * ld + n4, 4, 0, 0);
+  } else {
+    const int per_row = (n + 63) >> 6;
+    for (int r = 0; r < nrows; ++r)
+      for (int c = 0; c < per_row; ++c, ++j)
+        if ((j & (kWaves - 1)) == wave) {
+          const int i = c * 64 + lane;
+          if (i < n) __builtin_amdgcn_global_load_lds(src + r * src_stride + i, dst + r * ld + c * 64, 4, 0, 0);
+        }
   }
 }
 
