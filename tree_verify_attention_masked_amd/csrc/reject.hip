@@ -580,13 +580,12 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
 
   int emitted = -1;  // greedy argmax, known to every member
   if (sh_err == 0) {
-    // accept-test operands of every drafted node and the eager draft slices: in
-    // flight during the statistics
+    // accept-test operands of every drafted node (logit and draft probability of
+    // its token in its parent's row): loaded just before the first team barrier,
+    // whose latency they share, and stored to LDS after it
     const int cx = 1 + tid;
     const int nd = min(cx, T - 1);  // lanes past the tree re-read a valid node (or element 0)
     const long off = nd >= 1 ? static_cast<long>(s_par[nd]) * V + s_tok[nd] : 0;
-    const float lx = lg_b[off];
-    const float qx = (a.greedy ? lg_b : q_b)[off];
     // statistics of the first E rows, from their LDS slices (landed before the tree build's barrier)
     if (kFits) {
       switch (E) {
@@ -604,11 +603,13 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
           break;
       }
       if (tid < E) st_rec(&eager[wg * E + tid], s_rec[tid]);
+      const float lx = lg_b[off];
+      const float qx = (a.greedy ? lg_b : q_b)[off];
+      team_barrier(ctr, NW * ++phase, &sh_fail);
       if (cx < T) {
         s_lx[cx] = lx;
         s_qx[cx] = qx;
       }
-      team_barrier(ctr, NW * ++phase, &sh_fail);
       // merge every eager row at once (wave w: rows w and w + 4), member order
       if (!sh_fail) {
         Rec rr[2];
@@ -628,8 +629,8 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       __syncthreads();
     } else {
       if (cx < T) {
-        s_lx[cx] = lx;
-        s_qx[cx] = qx;
+        s_lx[cx] = lg_b[off];
+        s_qx[cx] = (a.greedy ? lg_b : q_b)[off];
       }
       __syncthreads();
     }
