@@ -4,8 +4,8 @@ Tolerance: bf16 outputs |gpu - oracle| <= 2e-2 + 1e-2 |oracle| (the stated
 bar) and also <= 2^-8 (attn(|V|) + |oracle|) + 1e-5, twice the effect of the
 bf16 rounding of the probabilities and of the output (helpers.py derives it);
 fp32 outputs 1e-5 + 1e-5 |oracle|.  Small cases compare every output and span several KV
-tiles, several splits, a ragged last page and each kernel variant (key-split
-for <= 16 rows per kv head, 64-row and 256-row tiles); the five configurations
+tiles, several splits, a ragged last page and each kernel variant (streaming
+for <= 16 rows per kv head, 64-row and 128-row tiles); the five configurations
 run at full size, all outputs where the oracle is quick, sampled rows
 otherwise.
 """

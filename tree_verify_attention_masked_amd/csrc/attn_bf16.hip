@@ -1,7 +1,7 @@
 // Tree-masked verify attention, bf16 inputs, head dim 128, gfx950 matrix cores:
-// planning for every bf16 shape, and the kernel for many query rows per kv head
-// (> 64: wide trees times GQA groups).  Shapes with <= 64 rows use the
-// streaming kernel (attn_stream.hip).
+// planning for every bf16 shape, and the kernel for more than 16 query rows per
+// kv head (trees times GQA groups).  Shapes with <= 16 rows (chains, decode,
+// small trees) use the streaming kernel (attn_stream.hip).
 //
 // Work item = (sequence b, kv head g, KV split s, row tile rt).  The query rows
 // of one (b, g) are the T tree nodes times the G query heads of the group
@@ -10,12 +10,13 @@
 // 0 .. prefix+T-1 of the sequence, read page by page through the block table;
 // keys at prefix + j are tree nodes and are masked by the ancestor-or-self
 // bitset of the row's node (the tree_mask of the EAGLE implementation summary
-// in "Report: Support nextn speculative decoding").
+// in "Report: Support nextn speculative decoding").  Splits that start past a
+// sequence's end exit at once and take no part in its merge.
 //
-// A workgroup holds 4 waves x NRB blocks of 16 rows (NRB = 2: 128 rows, at
-// most 256 registers per lane, two workgroups per CU, so that while one wave
-// of a SIMD waits on its softmax chain the other keeps the matrix core busy).
-// Per iteration the
+// A workgroup holds 4 waves x NRB blocks of 16 rows (NRB = 1: 64 rows, up to
+// 64 rows per kv head; NRB = 2: 128 rows), at most 256 registers per lane, two
+// workgroups per CU, so that while one wave of a SIMD waits on its softmax
+// chain the other keeps the matrix core busy.  Per iteration the
 // workgroup takes a 64-key tile (4 pages of K, 4 of V), each wave bringing one
 // page of each straight from HBM into LDS (direct global->LDS loads, double
 // buffered, so the next tile streams in while this one is used).  Each wave then
@@ -193,7 +194,7 @@ __device__ int build_ancestors_lds(const int* par, int T, uint64_t* anc) {
 }
 
 template <int NRB>
-__global__ __launch_bounds__(256, NRB == 2 ? 2 : 1) void attn_tile_kernel(const TArgs2 a) {
+__global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const TArgs2 a) {
   constexpr int RT = 64 * NRB;  // rows per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t tiles[2 * kTileBytes];  // 2 x (4 K pages, 4 V pages)
   __shared__ uint64_t anc[kMaxT * 4];
@@ -229,6 +230,8 @@ __global__ __launch_bounds__(256, NRB == 2 ? 2 : 1) void attn_tile_kernel(const 
   }
   const int n_keys = Lb + a.T;
   const int npages = (n_keys + kBlockSize - 1) / kBlockSize;
+  const int n_used = (npages + a.pps - 1) / a.pps;  // splits of this (b, g) that hold keys
+  if (s >= n_used) return;
   const int p0 = s * a.pps;
   const int p1 = min(npages, p0 + a.pps);
   const int kend = min(n_keys, p1 * kBlockSize);
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(256, NRB == 2 ? 2 : 1) void attn_tile_kernel(const 
   for (int rb = 0; rb < NRB; ++rb) l_run[rb] = quad_sum(l_run[rb]);
   report(a.status, b, err);
 
-  const bool direct = (a.splits == 1);
+  const bool direct = (n_used == 1);
   if (direct) {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -470,7 +473,7 @@ __global__ __launch_bounds__(256, NRB == 2 ? 2 : 1) void attn_tile_kernel(const 
   __syncthreads();
   if (tid == 0) {
     const unsigned prev = __hip_atomic_fetch_add(&a.counters[bgr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == static_cast<unsigned>(a.splits - 1));
+    s_last = (prev == static_cast<unsigned>(n_used - 1));
   }
   __syncthreads();
   if (!s_last) return;
@@ -479,14 +482,14 @@ __global__ __launch_bounds__(256, NRB == 2 ? 2 : 1) void attn_tile_kernel(const 
   // blocks w, w+4, ..., each lane the elements it would hold in the accumulator
   // layout, with the loads of four splits in flight at a time.
   const long first = (bgr / a.n_rt) * a.splits * a.n_rt + rt;  // item of split 0
-  constexpr int KS = NRB == 2 ? 2 : 4;  // splits whose loads are in flight together
+  constexpr int KS = NRB <= 2 ? 2 : 4;  // splits whose loads are in flight together
   for (int blk16 = wave; blk16 < RT / 16; blk16 += 4) {
     const int r = rt * RT + blk16 * 16 + l16;
     if (rt * RT + blk16 * 16 >= a.R) break;
     float mstar = -INFINITY, lstar = 0.f, acc[32];
 #pragma unroll
     for (int e = 0; e < 32; ++e) acc[e] = 0.f;
-    for (int sp0 = 0; sp0 < a.splits; sp0 += KS) {
+    for (int sp0 = 0; sp0 < n_used; sp0 += KS) {
       float ms[KS], ls[KS], x[KS][32];
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
@@ -494,7 +497,7 @@ __global__ __launch_bounds__(256, NRB == 2 ? 2 : 1) void attn_tile_kernel(const 
         ls[k] = 0.f;
 #pragma unroll
         for (int e = 0; e < 32; ++e) x[k][e] = 0.f;
-        if (sp0 + k < a.splits) {
+        if (sp0 + k < n_used) {
           const long it2 = first + static_cast<long>(sp0 + k) * a.n_rt;
           ms[k] = ld_agent(&a.part_ml[(it2 * RT + blk16 * 16 + l16) * 2 + 0]);
           ls[k] = ld_agent(&a.part_ml[(it2 * RT + blk16 * 16 + l16) * 2 + 1]);
@@ -557,18 +560,22 @@ AttnPlan plan_attn(int B, int T, int Hq, int Hkv, int D, int max_blocks, int dty
     return p;
   }
   (void)D;
-  if (p.rows <= 64) {
+  if (p.rows <= 16) {  // chains, decode, small trees: the streaming kernel
     plan_stream(p, B, Hkv, max_blocks);
     return p;
   }
-  // many rows: 128-row tiles, two workgroups per CU
+  // more rows: 64-row tiles up to 64 rows per kv head, else 128-row tiles; two
+  // workgroups per CU
   p.mode = 2;
-  p.nrb = 2;
+  p.nrb = p.rows <= 64 ? 1 : 2;
   p.rt = 64 * p.nrb;
   p.n_rt = (p.rows + p.rt - 1) / p.rt;
   const long base = static_cast<long>(B) * Hkv * p.n_rt;
   // ~two workgroups per CU; at least 16 pages (256 keys) per split
   long splits = std::max<long>(1, (512 + base - 1) / base);
+  // long sequences of a ragged batch: at most 512 pages per split, so the
+  // longest ones do not set the makespan alone
+  splits = std::max<long>(splits, (max_blocks + 511) / 512);
   splits = std::min<long>(splits, std::max<long>(1, max_blocks / 16));
   long pps = (max_blocks + splits - 1) / splits;
   pps = (pps + 3) / 4 * 4;
@@ -613,6 +620,7 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& L, hipStream
     a.part_o = reinterpret_cast<float*>(static_cast<char*>(L.workspace) + head);
     a.part_ml = a.part_o + static_cast<size_t>(plan.items) * plan.rt * kD;
   }
+  if (plan.nrb == 1) return run_tile<1>(a, stream);
   return run_tile<2>(a, stream);
 }
 

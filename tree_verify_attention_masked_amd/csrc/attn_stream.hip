@@ -517,7 +517,8 @@ hipError_t run_stream_rows(int nrb, const StArgs& args, hipStream_t stream) {
 
 }  // namespace
 
-// Plan for the streaming kernel: rows <= 64 per (b, g).  Pages per split are a
+// Plan for the streaming kernel (up to 64 rows per (b, g); the planner sends it
+// at most 16).  Pages per split are a
 // multiple of 4 (one page per wave and round), at most 4 * 64.  A workgroup
 // with DEPTH slots per wave holds 4 * DEPTH * 8 KB of LDS, so 160 KB fits
 // 160 / (32 DEPTH) of them per CU; the split size minimises the estimated
