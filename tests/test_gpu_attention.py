@@ -53,6 +53,13 @@ SMALL = [
                                         gamma=95)),
     ("rows256_tree_short_prefix", dict(B=1, Hq=16, Hkv=1, D=128, dtype="bf16", prefix=[5], tree="random", T=64,
                                        max_depth=6)),
+    # routing boundaries: 17 rows (the first tile-kernel shape), 64 rows over a
+    # ragged batch whose sequences need 1..3 splits (later splits exit at once),
+    # 65 rows (a second 128-row tile that is almost empty)
+    ("rows17_chain", dict(B=2, Hq=1, Hkv=1, D=128, dtype="bf16", prefix=[40, 300], tree="chain", gamma=16)),
+    ("rows64_ragged_splits", dict(B=3, Hq=8, Hkv=2, D=128, dtype="bf16", prefix=[3, 9000, 700], tree="random", T=16,
+                                  max_depth=5, shuffle_blocks=True)),
+    ("rows65_tree", dict(B=1, Hq=5, Hkv=1, D=128, dtype="bf16", prefix=[1234], tree="random", T=13, max_depth=4)),
 ]
 
 
