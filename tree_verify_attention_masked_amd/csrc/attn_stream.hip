@@ -501,24 +501,11 @@ hipError_t run_stream(const StArgs& args, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int DEPTH>
-hipError_t run_stream_rows(int nrb, const StArgs& args, hipStream_t stream) {
-  switch (nrb) {
-    case 1:
-      return run_stream<1, DEPTH>(args, stream);
-    case 2:
-      return run_stream<2, DEPTH>(args, stream);
-    case 3:
-      return run_stream<3, DEPTH>(args, stream);
-    default:
-      return run_stream<4, DEPTH>(args, stream);
-  }
-}
-
 }  // namespace
 
-// Plan for the streaming kernel (up to 64 rows per (b, g); the planner sends it
-// at most 16).  Pages per split are a
+// Plan for the streaming kernel (the kernel takes up to 64 rows per (b, g); the
+// attention planner sends it at most 16, one 16-row block, and only that shape
+// is instantiated).  Pages per split are a
 // multiple of 4 (one page per wave and round), at most 4 * 64.  A workgroup
 // with DEPTH slots per wave holds 4 * DEPTH * 8 KB of LDS, so 160 KB fits
 // 160 / (32 DEPTH) of them per CU; the split size minimises the estimated
@@ -595,14 +582,8 @@ hipError_t launch_attn_stream(const AttnPlan& plan, const AttnLaunch& L, hipStre
     a.part_o = reinterpret_cast<float*>(static_cast<char*>(L.workspace) + head);
     a.part_ml = a.part_o + static_cast<size_t>(plan.items) * plan.rows * kD;
   }
-  switch (plan.depth) {
-    case 2:
-      return run_stream_rows<2>(plan.nrb, a, stream);
-    case 3:
-      return run_stream_rows<3>(plan.nrb, a, stream);
-    default:
-      return run_stream_rows<4>(plan.nrb, a, stream);
-  }
+  if (plan.nrb != 1 || plan.depth != SPEC_STREAM_DEPTH) return hipErrorInvalidValue;  // not a planned shape
+  return run_stream<1, SPEC_STREAM_DEPTH>(a, stream);
 }
 
 }  // namespace spectree
