@@ -100,9 +100,10 @@ int spec_version(void);
  *   workspace    device scratch of at least spec_tree_attn_workspace_size(...)
  *                bytes (may be NULL when that size is 0).  When the KV range
  *                is split over several workgroups, the first bytes hold one
- *                arrival counter per (sequence, kv head): they must be zero
- *                before the first call, and every call that completes leaves
- *                them zero (zero-fill a workspace once, then reuse it).  Calls
+ *                arrival counter per (sequence, kv head, block of query rows),
+ *                which must be zero before the first call; every call that
+ *                completes leaves them zero (zero-fill a workspace once, then
+ *                reuse it).  The rest holds the splits' partial results.  Calls
  *                that overlap in time must not share a workspace.
  * Supported: dtype SPEC_BF16 with D = 128, dtype SPEC_F32 with D in {64, 128};
  * block_size = 16; 1 <= T <= 256; Hq % Hkv == 0.  B == 0 is a no-op.

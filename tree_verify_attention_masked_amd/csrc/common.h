@@ -39,8 +39,8 @@ __device__ __forceinline__ void report(int32_t* status, int b, int32_t bits) {
 // ---------------------------------------------------------------------------
 
 struct AttnPlan {
-  int mode;       // 0: fp32 VALU kernel, 1: bf16 key-split (<=16 rows), 2: bf16 row-split,
-                  // 3: bf16 streaming kernel (<=64 rows)
+  int mode;       // 0: fp32 VALU kernel, 2: bf16 tile kernel (> 16 rows), 3: bf16 streaming
+                  // kernel (<= 16 rows)
   int rows;       // R = T * G query rows per (sequence, kv head)
   int rt;         // rows per workgroup
   int nrb;        // 16-row blocks per wave
