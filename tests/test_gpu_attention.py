@@ -60,6 +60,10 @@ SMALL = [
     ("rows64_ragged_splits", dict(B=3, Hq=8, Hkv=2, D=128, dtype="bf16", prefix=[3, 9000, 700], tree="random", T=16,
                                   max_depth=5, shuffle_blocks=True)),
     ("rows65_tree", dict(B=1, Hq=5, Hkv=1, D=128, dtype="bf16", prefix=[1234], tree="random", T=13, max_depth=4)),
+    # fp32 kernel: ancestors past the first 64 lanes' words, GQA over a long and an almost empty prefix
+    ("f32_d64_deep_chain", dict(B=1, Hq=2, Hkv=1, D=64, dtype="f32", prefix=[70], tree="chain", gamma=200)),
+    ("f32_d128_gqa_tree", dict(B=2, Hq=6, Hkv=2, D=128, dtype="f32", prefix=[1300, 1], tree="random", T=40,
+                               max_depth=7, shuffle_blocks=True)),
 ]
 
 
@@ -94,6 +98,18 @@ def test_config_sampled_rows(cfg):
 
 def test_bad_inputs_are_reported_not_faulted():
     w = make_workload(tag=480, B=3, Hq=4, Hkv=4, D=128, dtype="bf16", V=8, prefix=[20, 40, 60], tree="random",
+                      T=6, max_depth=3)
+    d = DevWorkload(w)
+    d.parent[1, 3] = 5  # not topological
+    d.block_table[2, 0] = w.num_blocks + 7  # outside the pool
+    d.prefix_lens[0] = -4
+    d.attn()
+    st = d.status.cpu().numpy()
+    assert st[0] & 4 and st[1] & 1 and st[2] & 2
+
+
+def test_bad_inputs_are_reported_not_faulted_f32():
+    w = make_workload(tag=483, B=3, Hq=2, Hkv=2, D=64, dtype="f32", V=8, prefix=[20, 40, 60], tree="random",
                       T=6, max_depth=3)
     d = DevWorkload(w)
     d.parent[1, 3] = 5  # not topological
