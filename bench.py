@@ -1,6 +1,8 @@
 """Benchmark of one tree-verification step on one MI355X.
 
-A step = spec_tree_attn -> spec_tree_reject -> spec_kv_compact over one batch
+A step = spec_tree_attn -> spec_tree_reject_compact (tree rejection sampling,
+then compaction of the KV cache along the accepted path, in one launch; the
+same outputs as spec_tree_reject followed by spec_kv_compact) over one batch
 of the synthetic workload (default: the chain configuration, a Llama-2-13B-
 shaped layer: 40 MHA heads, head dim 128, bf16 paged KV, prefix 2048, chain
 of 4 drafts + root, vocabulary 32000, temperature 1).  Metric: verified tree
@@ -47,7 +49,7 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 METRIC = "verified tree tokens/sec at 1 MI355X"
 
 
-KERNEL_KEYS = (("tree_attn", ("attn_",)), ("tree_reject", ("reject",)), ("kv_compact", ("compact",)))
+KERNEL_KEYS = (("tree_attn", ("attn_",)), ("tree_reject_compact", ("reject",)), ("kv_compact", ("kv_compact",)))
 CALIB_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
 
 
@@ -273,19 +275,16 @@ def main():
         stv.spec_tree_attn(c["q"], c["k"], c["v"], shared["bt"], shared["lens"], shared["parent"], scale=w.scale,
                            out=c["out"], status=c["status"], workspace=attn_ws if ws_attn else None)
 
-    def reject(c):
-        stv.spec_tree_reject(c["logits"], c["probs"], shared["tok"], shared["parent"], w.temperature,
-                             w.without_replacement, w.seed, args.offset, accepted_nodes=c["acc"],
-                             out_tokens=c["toks"], num_accepted=c["nacc"], status=c["status"], workspace=rej_ws)
-
-    def compact(c):
-        stv.spec_kv_compact(c["k"], c["v"], shared["bt"], shared["lens"], c["acc"], c["nacc"],
-                            new_lens=c["new_lens"], status=c["status"])
+    def reject_compact(c):
+        stv.spec_tree_reject_compact(c["logits"], c["probs"], shared["tok"], shared["parent"], w.temperature,
+                                     c["k"], c["v"], shared["bt"], shared["lens"], w.without_replacement, w.seed,
+                                     args.offset, accepted_nodes=c["acc"], out_tokens=c["toks"],
+                                     num_accepted=c["nacc"], new_lens=c["new_lens"], status=c["status"],
+                                     workspace=rej_ws)
 
     def step(c):
         attn(c)
-        reject(c)
-        compact(c)
+        reject_compact(c)
 
     if args.calib_copy:  # a plain copy of known size, for scaling the HBM counters
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
@@ -336,7 +335,7 @@ def main():
     # per-kernel average durations: one graph = reps launches of one call over the copies
     reps = args.kernel_reps or max(R, 8 * R if per_copy < 100e6 else R)
     kdur = {}
-    for name, fn in (("tree_attn", attn), ("tree_reject", reject), ("kv_compact", compact)):
+    for name, fn in (("tree_attn", attn), ("tree_reject_compact", reject_compact)):
         g = capture([lambda c=copies[i % R]: fn(c) for i in range(reps)])
         g.replay()
         torch.cuda.synchronize()
@@ -360,8 +359,7 @@ def main():
     a_bytes, a_flops = attn_work(w)
     work = {
         "tree_attn": ("hbm", a_bytes, a_flops),
-        "tree_reject": ("hbm", reject_bytes(w, nacc, stop_rej), 0.0),
-        "kv_compact": ("hbm", compact_bytes(w, acc, nacc), 0.0),
+        "tree_reject_compact": ("hbm", reject_bytes(w, nacc, stop_rej) + compact_bytes(w, acc, nacc), 0.0),
     }
     dominant = max(kdur, key=kdur.get)
     bound, bytes_, flops = work[dominant]

@@ -8,6 +8,7 @@
  *   spec_tree_reject  tree rejection sampling (greedy, with replacement,
  *                     or Sequoia-style without replacement)
  *   spec_kv_compact   keep only the accepted root-to-leaf path in the KV cache
+ * and spec_tree_reject_compact, the last two in one launch.
  *
  * Conventions shared by every call
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
@@ -199,6 +200,35 @@ int spec_kv_compact(void* k_cache, void* v_cache, const int32_t* block_table,
                     int B, int T, int Hkv, int D, int block_size,
                     int max_blocks_per_seq, int num_blocks, int dtype,
                     int32_t* status, void* stream);
+
+/* ----------------------------------------------------------------------
+ * spec_tree_reject_compact — spec_tree_reject followed by spec_kv_compact
+ * along the path it accepted, in one launch.
+ *
+ * The vLLM PR ("[WIP] Speculative decoding using a draft model", guide for
+ * reviewers) asks that the verifier and the cache update run without a host
+ * round trip between them; here they also share one kernel: once a team has
+ * walked a sequence's tree, its workgroups move the accepted rows of the kv
+ * heads they own, from the path they already hold.  Every output equals that of
+ * calling spec_tree_reject and then spec_kv_compact on its accepted_nodes and
+ * num_accepted (after a sampler error, L = 0: the cache is left as it is and
+ * new_lens[b] = prefix_lens[b] + 1).
+ *
+ *   the first 17 arguments  as for spec_tree_reject
+ *   k_cache .. num_blocks, dtype  as for spec_kv_compact (T is the sampler's)
+ *   status  receives both kernels' device error bits
+ * Supported: as spec_tree_reject and spec_kv_compact together.
+ * ---------------------------------------------------------------------- */
+int spec_tree_reject_compact(const float* target_logits, const float* draft_probs,
+                             const int32_t* draft_tokens, const int32_t* parent,
+                             int B, int T, int V, float temperature, int without_replacement,
+                             uint64_t seed, uint64_t offset,
+                             int32_t* accepted_nodes, int32_t* out_tokens, int32_t* num_accepted,
+                             int32_t* status, void* workspace, size_t workspace_bytes,
+                             void* k_cache, void* v_cache, const int32_t* block_table,
+                             const int32_t* prefix_lens, int32_t* new_lens,
+                             int Hkv, int D, int block_size, int max_blocks_per_seq,
+                             int num_blocks, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

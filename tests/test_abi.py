@@ -105,6 +105,23 @@ def test_compact_host_validation(lib):
                                None) == -1
 
 
+def test_reject_compact_host_validation(lib):
+    def call(**kw):
+        a = dict(B=1, T=5, V=100, tau=1.0, ws=FAKE, wsz=1 << 20, k=FAKE, Hkv=2, D=128, bs=16, mb=4, nb=4, dtype=1)
+        a.update(kw)
+        return lib.spec_tree_reject_compact(FAKE, FAKE, FAKE, FAKE, a["B"], a["T"], a["V"], a["tau"], 0, 0, 0,
+                                            FAKE, FAKE, FAKE, None, a["ws"], a["wsz"], a["k"], FAKE, FAKE, FAKE,
+                                            None, a["Hkv"], a["D"], a["bs"], a["mb"], a["nb"], a["dtype"], None)
+    assert call(tau=-1.0) == -1     # the sampler's checks
+    assert call(T=257) == -2
+    assert call(wsz=10) == -3
+    assert call(k=None) == -1       # the compaction's checks
+    assert call(D=32) == -2
+    assert call(bs=32) == -2
+    assert call(Hkv=0) == -1
+    assert call(B=0) == 0
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 2, 2, 128, dtype=torch.bfloat16)

@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import oracle
+import tree_verify_attention_masked_amd as stv
 from helpers import DevWorkload, compare_reject, host_kv, oracle_reject
 from workloads import make_config, make_workload
 
@@ -104,3 +105,28 @@ def test_verify_step_end_to_end(cfg):
     assert np.array_equal(host_kv(w, d.k).view(np.uint8), k_ref.view(np.uint8))
     assert np.array_equal(new_lens.cpu().numpy(), lens_ref)
     assert int(d.status.abs().sum()) == 0
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_fused_reject_compact_equals_separate_calls(cfg):
+    """spec_tree_reject_compact == spec_tree_reject, then spec_kv_compact on its path:
+    same path, tokens and lengths, and the whole K and V caches bit-equal."""
+    w = make_config(cfg)
+    print(f"[fused] config {cfg} {w.name}", flush=True)
+    sep, fus = DevWorkload(w), DevWorkload(w)  # two independent copies of the caches
+    acc1, toks1, n1 = sep.reject()
+    lens1 = sep.compact(acc1, n1)
+    acc2, toks2, n2, lens2 = stv.spec_tree_reject_compact(
+        fus.logits, fus.probs, fus.tokens, fus.parent, w.temperature, fus.k, fus.v, fus.block_table,
+        fus.prefix_lens, w.without_replacement, w.seed, w.offset, status=fus.status)
+    torch.cuda.synchronize()
+    for x, y, what in ((acc1, acc2, "accepted_nodes"), (toks1, toks2, "out_tokens"), (n1, n2, "num_accepted"),
+                       (lens1, lens2, "new_lens"), (sep.status, fus.status, "status")):
+        assert torch.equal(x, y), what
+    assert torch.equal(_bits(sep.k), _bits(fus.k)) and torch.equal(_bits(sep.v), _bits(fus.v))
+    moved = int((acc1[:, 1:] != torch.arange(1, w.T, device=acc1.device)).logical_and(acc1[:, 1:] >= 0).sum())
+    print(f"[fused] config {cfg}: accepted {n1.tolist()[:8]}, rows off their place {moved}", flush=True)

@@ -8,6 +8,8 @@ include/spectree.h):
   spec_tree_reject  tree rejection sampling (greedy / with / without replacement)
   spec_kv_compact   keep only the accepted path in the KV cache
 
+and spec_tree_reject_compact, the last two in one launch.
+
 This package is the thin PyTorch binding: tensors in, device pointers and the
 current HIP stream out to the library.
 """
@@ -24,5 +26,6 @@ from .binding import (  # noqa: F401
     spec_tree_attn,
     spec_tree_attn_workspace_size,
     spec_tree_reject,
+    spec_tree_reject_compact,
     spec_version,
 )

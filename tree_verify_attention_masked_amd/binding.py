@@ -43,6 +43,9 @@ _SIGNATURES = {
     "spec_tree_reject": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_uint64,
                               ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_kv_compact": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
+    "spec_tree_reject_compact": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_uint64,
+                                      ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp, _sz,
+                                      _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
 }
 
 _lib = None
@@ -212,6 +215,54 @@ def spec_kv_compact(k_cache, v_cache, block_table, prefix_lens, accepted_nodes, 
                              _stream(k_cache.device))
     _check(rc, "spec_kv_compact")
     return new_lens
+
+
+def spec_tree_reject_compact(target_logits, draft_probs, draft_tokens, parent, temperature, k_cache, v_cache,
+                             block_table, prefix_lens, without_replacement=False, seed=0, offset=0,
+                             accepted_nodes=None, out_tokens=None, num_accepted=None, new_lens=None, status=None,
+                             workspace=None):
+    """spec_tree_reject, then compaction of the KV cache along the accepted path, in one launch.
+    Returns (accepted_nodes [B,T], out_tokens [B,T], num_accepted [B], new_lens [B])."""
+    lib = load_library()
+    _need(target_logits, "target_logits", torch.float32, 3)
+    _need(draft_tokens, "draft_tokens", torch.int32, 2)
+    _need(parent, "parent", torch.int32, 2)
+    _need(k_cache, "k_cache", ndim=4)
+    _need(v_cache, "v_cache", k_cache.dtype, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(prefix_lens, "prefix_lens", torch.int32, 1)
+    B, T, V = target_logits.shape
+    if draft_probs is not None:
+        _need(draft_probs, "draft_probs", torch.float32, 3)
+        if tuple(draft_probs.shape) != (B, T, V):
+            raise ValueError("draft_probs shape disagrees with target_logits")
+    if tuple(draft_tokens.shape) != (B, T) or tuple(parent.shape) != (B, T):
+        raise ValueError("draft_tokens / parent shapes disagree with target_logits")
+    nb, Hkv, bs, D = k_cache.shape
+    dev = target_logits.device
+    if accepted_nodes is None:
+        accepted_nodes = torch.empty((B, T), dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, T), dtype=torch.int32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if new_lens is None:
+        new_lens = torch.empty((B,), dtype=torch.int32, device=dev)
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    ws = int(lib.spec_tree_reject_workspace_size(B, T, V))
+    if workspace is None and ws > 0:  # zero-filled: its header holds the team barrier counters
+        workspace = torch.zeros(ws, dtype=torch.uint8, device=dev)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.spec_tree_reject_compact(_ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(parent),
+                                      B, T, V, float(temperature), int(bool(without_replacement)),
+                                      int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1),
+                                      _ptr(accepted_nodes), _ptr(out_tokens), _ptr(num_accepted), _ptr(status),
+                                      _ptr(workspace), wsz, _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                      _ptr(prefix_lens), _ptr(new_lens), Hkv, D, bs, block_table.shape[1], nb,
+                                      _dtype_code(k_cache), _stream(dev))
+    _check(rc, "spec_tree_reject_compact")
+    return accepted_nodes, out_tokens, num_accepted, new_lens
 
 
 def spec_status_string(code: int) -> str:

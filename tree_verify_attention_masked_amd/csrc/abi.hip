@@ -96,11 +96,15 @@ size_t spec_tree_reject_workspace_size(int B, int T, int V) {
   return reject_workspace_bytes(B, T, V);
 }
 
-int spec_tree_reject(const float* target_logits, const float* draft_probs, const int32_t* draft_tokens,
-                     const int32_t* parent, int B, int T, int V, float temperature, int without_replacement,
-                     uint64_t seed, uint64_t offset, int32_t* accepted_nodes, int32_t* out_tokens,
-                     int32_t* num_accepted, int32_t* status, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host validation of the sampler's arguments and its launch description.
+int make_reject(const float* target_logits, const float* draft_probs, const int32_t* draft_tokens,
+                const int32_t* parent, int B, int T, int V, float temperature, int without_replacement, uint64_t seed,
+                uint64_t offset, int32_t* accepted_nodes, int32_t* out_tokens, int32_t* num_accepted,
+                int32_t* status, void* workspace, size_t workspace_bytes, RejectLaunch* L) {
   if (B < 0 || T < 1 || V < 1) return SPEC_ERR_INVALID_ARG;
   if (T > kMaxT || V > kMaxV) return SPEC_ERR_UNSUPPORTED;
   if (!(temperature >= 0.0f) || !std::isfinite(temperature)) return SPEC_ERR_INVALID_ARG;
@@ -110,23 +114,66 @@ int spec_tree_reject(const float* target_logits, const float* draft_probs, const
   if (temperature > 0.0f && !draft_probs) return SPEC_ERR_INVALID_ARG;
   const size_t need = reject_workspace_bytes(B, T, V);
   if (workspace == nullptr || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
-  RejectLaunch L{};
-  L.logits = target_logits;
-  L.q = draft_probs;
-  L.tokens = draft_tokens;
-  L.parent = parent;
-  L.B = B;
-  L.T = T;
-  L.V = V;
-  L.temperature = temperature;
-  L.without_replacement = without_replacement;
-  L.seed = seed;
-  L.offset = offset;
-  L.accepted = accepted_nodes;
-  L.out_tokens = out_tokens;
-  L.num_accepted = num_accepted;
-  L.status = status;
-  L.workspace = workspace;
+  *L = RejectLaunch{};
+  L->logits = target_logits;
+  L->q = draft_probs;
+  L->tokens = draft_tokens;
+  L->parent = parent;
+  L->B = B;
+  L->T = T;
+  L->V = V;
+  L->temperature = temperature;
+  L->without_replacement = without_replacement;
+  L->seed = seed;
+  L->offset = offset;
+  L->accepted = accepted_nodes;
+  L->out_tokens = out_tokens;
+  L->num_accepted = num_accepted;
+  L->status = status;
+  L->workspace = workspace;
+  return SPEC_OK;
+}
+
+// Host validation of the compaction's arguments (the path pointers are checked
+// by the caller when they are inputs) and its launch description.
+int make_compact(void* k_cache, void* v_cache, const int32_t* block_table, const int32_t* prefix_lens,
+                 int32_t* new_lens, int B, int T, int Hkv, int D, int block_size, int max_blocks_per_seq,
+                 int num_blocks, int dtype, int32_t* status, CompactLaunch* L) {
+  const int rc = check_kv_shapes(B, T, Hkv, D, block_size, max_blocks_per_seq, num_blocks, dtype);
+  if (rc != SPEC_OK) return rc;
+  if (B == 0) return SPEC_OK;
+  if (!k_cache || !v_cache || !block_table || !prefix_lens) return SPEC_ERR_INVALID_ARG;
+  *L = CompactLaunch{};
+  L->k = k_cache;
+  L->v = v_cache;
+  L->block_table = block_table;
+  L->prefix_lens = prefix_lens;
+  L->new_lens = new_lens;
+  L->status = status;
+  L->B = B;
+  L->T = T;
+  L->Hkv = Hkv;
+  L->D = D;
+  L->max_blocks = max_blocks_per_seq;
+  L->num_blocks = num_blocks;
+  L->elem_bytes = dtype == SPEC_BF16 ? 2 : 4;
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_tree_reject(const float* target_logits, const float* draft_probs, const int32_t* draft_tokens,
+                     const int32_t* parent, int B, int T, int V, float temperature, int without_replacement,
+                     uint64_t seed, uint64_t offset, int32_t* accepted_nodes, int32_t* out_tokens,
+                     int32_t* num_accepted, int32_t* status, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  RejectLaunch L;
+  const int rc = make_reject(target_logits, draft_probs, draft_tokens, parent, B, T, V, temperature,
+                             without_replacement, seed, offset, accepted_nodes, out_tokens, num_accepted, status,
+                             workspace, workspace_bytes, &L);
+  if (rc != SPEC_OK || B == 0) return rc;
   const hipError_t e = launch_reject(L, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
@@ -135,28 +182,35 @@ int spec_kv_compact(void* k_cache, void* v_cache, const int32_t* block_table, co
                     const int32_t* accepted_nodes, const int32_t* num_accepted, int32_t* new_lens, int B, int T,
                     int Hkv, int D, int block_size, int max_blocks_per_seq, int num_blocks, int dtype,
                     int32_t* status, void* stream) {
-  int rc = check_kv_shapes(B, T, Hkv, D, block_size, max_blocks_per_seq, num_blocks, dtype);
-  if (rc != SPEC_OK) return rc;
-  if (B == 0) return SPEC_OK;
-  if (!k_cache || !v_cache || !block_table || !prefix_lens || !accepted_nodes || !num_accepted)
-    return SPEC_ERR_INVALID_ARG;
-  CompactLaunch L{};
-  L.k = k_cache;
-  L.v = v_cache;
-  L.block_table = block_table;
-  L.prefix_lens = prefix_lens;
+  CompactLaunch L;
+  const int rc = make_compact(k_cache, v_cache, block_table, prefix_lens, new_lens, B, T, Hkv, D, block_size,
+                              max_blocks_per_seq, num_blocks, dtype, status, &L);
+  if (rc != SPEC_OK || B == 0) return rc;
+  if (!accepted_nodes || !num_accepted) return SPEC_ERR_INVALID_ARG;
   L.accepted = accepted_nodes;
   L.num_accepted = num_accepted;
-  L.new_lens = new_lens;
-  L.status = status;
-  L.B = B;
-  L.T = T;
-  L.Hkv = Hkv;
-  L.D = D;
-  L.max_blocks = max_blocks_per_seq;
-  L.num_blocks = num_blocks;
-  L.elem_bytes = dtype == SPEC_BF16 ? 2 : 4;
   const hipError_t e = launch_compact(L, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+int spec_tree_reject_compact(const float* target_logits, const float* draft_probs, const int32_t* draft_tokens,
+                             const int32_t* parent, int B, int T, int V, float temperature, int without_replacement,
+                             uint64_t seed, uint64_t offset, int32_t* accepted_nodes, int32_t* out_tokens,
+                             int32_t* num_accepted, int32_t* status, void* workspace, size_t workspace_bytes,
+                             void* k_cache, void* v_cache, const int32_t* block_table, const int32_t* prefix_lens,
+                             int32_t* new_lens, int Hkv, int D, int block_size, int max_blocks_per_seq,
+                             int num_blocks, int dtype, void* stream) {
+  RejectLaunch R;
+  int rc = make_reject(target_logits, draft_probs, draft_tokens, parent, B, T, V, temperature, without_replacement,
+                       seed, offset, accepted_nodes, out_tokens, num_accepted, status, workspace, workspace_bytes,
+                       &R);
+  if (rc != SPEC_OK) return rc;
+  CompactLaunch C;
+  rc = make_compact(k_cache, v_cache, block_table, prefix_lens, new_lens, B, T, Hkv, D, block_size,
+                    max_blocks_per_seq, num_blocks, dtype, status, &C);
+  if (rc != SPEC_OK || B == 0) return rc;
+  R.compact = &C;  // copied into the kernel arguments at launch
+  const hipError_t e = launch_reject(R, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

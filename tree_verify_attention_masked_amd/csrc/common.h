@@ -73,6 +73,18 @@ void plan_stream(AttnPlan& p, int B, int Hkv, int max_blocks);
 hipError_t launch_attn_stream(const AttnPlan& plan, const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnPlan& plan, const AttnLaunch& a, hipStream_t stream);
 
+struct CompactLaunch {
+  void* k;
+  void* v;
+  const int32_t* block_table;
+  const int32_t* prefix_lens;
+  const int32_t* accepted;
+  const int32_t* num_accepted;
+  int32_t* new_lens;
+  int32_t* status;
+  int B, T, Hkv, D, max_blocks, num_blocks, elem_bytes;
+};
+
 struct RejectLaunch {
   const float* logits;
   const float* q;
@@ -87,23 +99,12 @@ struct RejectLaunch {
   int32_t* num_accepted;
   int32_t* status;
   void* workspace;
+  const CompactLaunch* compact;  // non-null: compact the KV cache along the accepted path in the same launch
 };
 
 size_t reject_workspace_bytes(int B, int T, int V);
 size_t reject_workspace_zero_bytes(int B);
 hipError_t launch_reject(const RejectLaunch& a, hipStream_t stream);
-
-struct CompactLaunch {
-  void* k;
-  void* v;
-  const int32_t* block_table;
-  const int32_t* prefix_lens;
-  const int32_t* accepted;
-  const int32_t* num_accepted;
-  int32_t* new_lens;
-  int32_t* status;
-  int B, T, Hkv, D, max_blocks, num_blocks, elem_bytes;
-};
 
 hipError_t launch_compact(const CompactLaunch& a, hipStream_t stream);
 

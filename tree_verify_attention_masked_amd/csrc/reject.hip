@@ -35,6 +35,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "compact_dev.h"
 
 namespace spectree {
 namespace {
@@ -169,6 +170,8 @@ struct TArgs {
   int T, V, NW, S, ld, E, greedy, wr;
   double inv_tau;
   uint64_t seed, offset;
+  int fuse;         // compact the KV cache along the accepted path after the walk
+  CompactLaunch c;  // its arguments (accepted / num_accepted unused: the path is in LDS)
 };
 
 // Records exchanged between members (the team spans XCDs, whose L2s are not
@@ -513,6 +516,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   // draft slices, which depend on nothing else: all in flight together
   const int pv = a.parent[static_cast<long>(b) * T + min(tid, T - 1)];
   const int tv = a.tokens[static_cast<long>(b) * T + min(tid, T - 1)];
+  const int c_lb = a.fuse ? a.c.prefix_lens[b] : 0;  // the compaction's prefix length, loaded early
   if constexpr (kFits) {  // E >= 1 whenever the slice fits
     stage_dma(eager_l, lg_b + v0, ld, V, E, n);
     if (!a.greedy) stage_dma(eager_q, q_b + v0, ld, V, E, n);
@@ -918,6 +922,28 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       report(a.status, b, err);
     }
     if (!err && !a.greedy && wg == sh_owner) out_b[L] = sh_emit_local;
+  }
+  if (a.fuse) {
+    // KV compaction along the path every member holds (s_path[0..L]; L = 0
+    // after a sampler error, which leaves the cache as it is): member 0 plans
+    // it and reports, every member moves the kv heads g = wg, wg + NW, ...
+    // through its (now free) current-row LDS buffer
+    if (tid == 0) {
+      int first = 1 << 30;
+      const int cerr = compact_plan(a.c, b, c_lb, s_path, L, &first);
+      sh_c = cerr ? -1 : L;  // the walk is over: its scratch words are free
+      sh_x = first;
+      if (wg == 0) {
+        if (a.c.new_lens != nullptr) a.c.new_lens[b] = cerr ? c_lb : c_lb + L + 1;
+        report(a.status, b, cerr);
+      }
+    }
+    __syncthreads();
+    const int cL = sh_c, cfirst = sh_x;
+    for (int g = wg; g < a.c.Hkv; g += NW)
+      compact_move(a.c, b, g, c_lb, cL, cfirst, s_path, reinterpret_cast<uint8_t*>(cur_lbuf));
+  }
+  if (tid == 0) {
     // leave: the last member out resets the barrier counters for the next call
     const unsigned prev = atomicAdd(ctr + 1, 1u);
     if (prev == static_cast<unsigned>(NW - 1)) {
@@ -963,6 +989,8 @@ hipError_t launch_reject(const RejectLaunch& L, hipStream_t stream) {
   a.inv_tau = greedy ? 0.0 : 1.0 / static_cast<double>(L.temperature);
   a.seed = L.seed;
   a.offset = L.offset;
+  a.fuse = L.compact != nullptr;
+  if (a.fuse) a.c = *L.compact;
   const dim3 grid(static_cast<unsigned>(L.B * t.NW));
   if (t.ld <= kSliceCap) {
     hipLaunchKernelGGL(reject_team_kernel<true>, grid, dim3(kThreads), 0, stream, a);
