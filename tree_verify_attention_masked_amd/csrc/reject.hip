@@ -520,8 +520,15 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   if constexpr (kFits) {  // E >= 1 whenever the slice fits
     stage_dma(eager_l, lg_b + v0, ld, V, E, n);
     if (!a.greedy) stage_dma(eager_q, q_b + v0, ld, V, E, n);
-    wait_dma();
   }
+  // the Philox uniforms of every node depend on none of the loads in flight:
+  // drawn while they land
+  if (!a.greedy)
+    for (int i = tid; i < T; i += kThreads) {
+      s_ru[i] = draw_uniform(a.seed, a.offset, b, i, 0);
+      s_fu[i] = draw_uniform(a.seed, a.offset, b, i, 1);
+    }
+  if constexpr (kFits) wait_dma();
   if (tid < T) {
     s_par[tid] = pv;
     s_tok[tid] = tv;
@@ -537,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
     sh_owner = 0;
   }
   __syncthreads();
-  // Checks, the Philox uniforms, and the child lists: bit c of kids[p] is set for
+  // Checks and the child lists: bit c of kids[p] is set for
   // every child c of p (an LDS atomic per node), so first_child[i] (the first c
   // whose parent is i) and next_sib[i] (the first c > i sharing i's parent) are
   // lowest-set-bit lookups, with no scan over the tree.  kids lives in cur_qbuf,
@@ -554,10 +561,6 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       if (!ok) err |= SPEC_DEV_PARENT;
       if (i > 0 && ok && (s_tok[i] < 0 || s_tok[i] >= V)) err |= SPEC_DEV_TOKEN;
       if (i > 0 && ok) atomicOr(&kids[p * kKW + (i >> 5)], 1u << (i & 31));
-      if (!a.greedy) {
-        s_ru[i] = draw_uniform(a.seed, a.offset, b, i, 0);
-        s_fu[i] = draw_uniform(a.seed, a.offset, b, i, 1);
-      }
     }
     if (err) atomicOr(&sh_err, err);
   }
