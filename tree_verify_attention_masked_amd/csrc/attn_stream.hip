@@ -512,7 +512,7 @@ hipError_t run_stream(const StArgs& args, hipStream_t stream) {
 // makespan: rounds of resident workgroups times (pages per wave + a fixed cost
 // of a few pages' time for the prologue latency and the merge).
 #ifndef SPEC_STREAM_DEPTH
-#define SPEC_STREAM_DEPTH 4
+#define SPEC_STREAM_DEPTH 3
 #endif
 #ifndef SPEC_STREAM_RAGGED_PPS
 #define SPEC_STREAM_RAGGED_PPS 256

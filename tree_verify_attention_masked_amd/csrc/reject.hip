@@ -43,7 +43,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxEager = 8;     // rows whose statistics are taken before the walk
-constexpr int kMaxTeam = 32;     // workgroups per sequence (one wave merges their partials)
+constexpr int kMaxTeam = 64;     // workgroups per sequence (one wave merges their partials)
+constexpr int kDeepTeam = 32;    // at most this many for trees with deeper rows (more than 16 nodes)
 constexpr int kEagerCap = 8192;  // floats of eager-row logit slices kept in LDS
 constexpr int kSliceCap = 8192;  // floats of the current row's logits / draft probs kept in LDS
 constexpr int kSyncStride = 16;  // uint32 words of barrier state per sequence (64 B)
@@ -61,7 +62,7 @@ struct Team {
 
 Team team_shape(int B, int T, int V) {
   Team t;
-  int nw = std::max(1, std::min(kMaxTeam, 256 / std::max(B, 1)));
+  int nw = std::max(1, std::min(T > 16 ? kDeepTeam : kMaxTeam, 256 / std::max(B, 1)));
   nw = std::min(nw, std::max(1, (V + 511) / 512));
   t.NW = nw;
   t.S = (V + nw - 1) / nw;
@@ -550,8 +551,10 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   // lowest-set-bit lookups, with no scan over the tree.  kids lives in cur_qbuf,
   // which is first written when a deeper row is staged.
   constexpr int kKW = kMaxT / 32;  // bitset words per parent
+  const int nkw = (T + 31) >> 5;   // words in use
   uint32_t* kids = reinterpret_cast<uint32_t*>(cur_qbuf);
-  for (int i = tid; i < T * kKW; i += kThreads) kids[i] = 0u;
+  for (int i = tid; i < T * kKW; i += kThreads)
+    if ((i & (kKW - 1)) < nkw) kids[i] = 0u;
   __syncthreads();
   {
     int err = 0;
@@ -567,14 +570,14 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   __syncthreads();
   for (int i = tid; i < T; i += kThreads) {
     int fc = -1;
-    for (int w = 0; w < kKW && fc < 0; ++w) {
+    for (int w = 0; w < nkw && fc < 0; ++w) {
       const uint32_t m = kids[i * kKW + w];
       if (m) fc = w * 32 + __builtin_ctz(m);
     }
     const int p = s_par[i];
     int ns = -1;
     if (i > 0 && p >= 0 && p < i) {
-      for (int w = (i + 1) >> 5; w < kKW && ns < 0; ++w) {
+      for (int w = (i + 1) >> 5; w < nkw && ns < 0; ++w) {
         uint32_t m = kids[p * kKW + w];
         if (w == ((i + 1) >> 5)) m &= 0xFFFFFFFFu << ((i + 1) & 31);
         if (m) ns = w * 32 + __builtin_ctz(m);
