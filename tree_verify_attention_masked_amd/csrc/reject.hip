@@ -336,39 +336,29 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
 // The previous lane's value (lane 0: `first`).
 __device__ __forceinline__ double wave_shift_up(double v, double first) { return dpp_d<kWaveShr1, 0xF>(first, v); }
 
-// Statistics of R rows whose slices are rows[r * ld + i], i < n: slice max, its
-// first index (-1 if the slice holds NaN or +inf) and the sum of
-// exp((l - max) / t), into out[0 .. R-1].  One pass per thread over its
-// contiguous 4-element chunks keeps a running (max, first argmax, sum of exp
-// relative to the running max) per row; the partials go to LDS (`scratch`, at
-// least R * kThreads * 16 bytes) and wave w then reduces row w over all threads,
-// so each wave's dependency chain covers one row, not R.
-template <int R, bool kLds>
-__device__ __forceinline__ void slice_stats_rows(const float* rows, int ld, int n, int v0, bool greedy, double inv_tau,
-                                                 Rec* out, void* scratch) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float* pm = static_cast<float*>(scratch);
-  int* pi = reinterpret_cast<int*>(pm + R * kThreads);
-  double* pz = reinterpret_cast<double*>(pi + R * kThreads);
-  const int nc = (n + 3) >> 2;
-  const int per = (nc + kThreads - 1) / kThreads;
-  const int c0 = min(nc, tid * per), c1 = min(nc, c0 + per);
-  float mx[R];
-  int ix[R];
-  double z[R];
+// Running (max, first argmax, sum of exp((l - max) / t) relative to the running
+// max) of NR rows, row r at base[r * stride + i], over the 4-element chunks
+// c0, c0 + step, ... (< nc) of a slice of n elements (global index v0 + i).
+// Consecutive lanes take consecutive chunks, so each LDS read instruction
+// covers one contiguous run (no bank conflicts); chunks are visited in
+// increasing order, so the index kept is the first of the lane's max.  A NaN or
+// +inf pins the row's max at +inf with index -1.
+template <int NR, bool kLds>
+__device__ __forceinline__ void scan_chunks(const float* base, int stride, int n, int v0, double inv_tau, int c0, int nc,
+                                            int step, float (&mx)[NR], int (&ix)[NR], double (&z)[NR]) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int r = 0; r < NR; ++r) {
     mx[r] = -INFINITY;
     ix[r] = 0x7fffffff;
     z[r] = 0.0;
   }
-  for (int c = c0; c < c1; ++c) {
-    f32x4 v[R];
+  for (int c = c0; c < nc; c += step) {
+    f32x4 v[NR];
 #pragma unroll
-    for (int r = 0; r < R; ++r) v[r] = load4<kLds>(rows + r * ld + 4 * c, n - 4 * c);
-    float cm[R];
+    for (int r = 0; r < NR; ++r) v[r] = load4<kLds>(base + r * stride + 4 * c, n - 4 * c);
+    float cm[NR];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < NR; ++r) {
       cm[r] = mx[r];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {  // a NaN or +inf pins the row's max at +inf with index -1
@@ -380,23 +370,44 @@ __device__ __forceinline__ void slice_stats_rows(const float* rows, int ld, int 
         ix[r] = take ? (bad ? -1 : v0 + 4 * c + e) : ix[r];
       }
     }
-    double t[5 * R];  // the chunk's terms, then the factor rescaling the running sum
+    double t[5 * NR];  // the chunk's terms, then the factor rescaling the running sum
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < NR; ++r) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) t[4 * r + e] = (static_cast<double>(v[r][e]) - static_cast<double>(cm[r])) * inv_tau;
-      t[4 * R + r] = (static_cast<double>(mx[r]) - static_cast<double>(cm[r])) * inv_tau;
+      t[4 * NR + r] = (static_cast<double>(mx[r]) - static_cast<double>(cm[r])) * inv_tau;
     }
-    exp_lockstep<5 * R>(t);
+    exp_lockstep<5 * NR>(t);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      double zz = (mx[r] == -INFINITY) ? 0.0 : z[r] * t[4 * R + r];
+    for (int r = 0; r < NR; ++r) {
+      double zz = (mx[r] == -INFINITY) ? 0.0 : z[r] * t[4 * NR + r];
 #pragma unroll
       for (int e = 0; e < 4; ++e) zz += (4 * c + e < n) ? t[4 * r + e] : 0.0;
       z[r] = zz;
       mx[r] = cm[r];
     }
   }
+}
+
+// Statistics of R rows whose slices are rows[r * ld + i], i < n: slice max, its
+// first index (-1 if the slice holds NaN or +inf) and the sum of
+// exp((l - max) / t), into out[0 .. R-1].  One pass per thread over every
+// kThreads-th 4-element chunk keeps a running (max, first argmax, sum of exp
+// relative to the running max) per row; the partials go to LDS (`scratch`, at
+// least R * kThreads * 16 bytes) and wave w then reduces row w over all threads,
+// so each wave's dependency chain covers one row, not R.
+template <int R, bool kLds>
+__device__ __forceinline__ void slice_stats_rows(const float* rows, int ld, int n, int v0, bool greedy, double inv_tau,
+                                                 Rec* out, void* scratch) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* pm = static_cast<float*>(scratch);
+  int* pi = reinterpret_cast<int*>(pm + R * kThreads);
+  double* pz = reinterpret_cast<double*>(pi + R * kThreads);
+  const int nc = (n + 3) >> 2;
+  float mx[R];
+  int ix[R];
+  double z[R];
+  scan_chunks<R, kLds>(rows, ld, n, v0, inv_tau, tid, nc, kThreads, mx, ix, z);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     pm[r * kThreads + tid] = mx[r];
@@ -411,7 +422,7 @@ __device__ __forceinline__ void slice_stats_rows(const float* rows, int ld, int 
     double zs[K];
     bool bad = false;
 #pragma unroll
-    for (int k = 0; k < K; ++k) {  // thread order k*64 + lane: ties keep the lower index
+    for (int k = 0; k < K; ++k) {  // ties keep the lower index
       ms[k] = pm[r * kThreads + k * 64 + lane];
       const int ik = pi[r * kThreads + k * 64 + lane];
       zs[k] = pz[r * kThreads + k * 64 + lane];
@@ -435,6 +446,48 @@ __device__ __forceinline__ void slice_stats_rows(const float* rows, int ld, int 
     if (lane == 0) {
       out[r].m = m;
       out[r].idx = bad ? -1 : (i == 0x7fffffff ? v0 : i);
+      out[r].z = zt;
+    }
+  }
+  __syncthreads();
+}
+
+// Statistics of R = 4 or 8 rows (as slice_stats_rows) with every row owned by
+// one wave: wave w takes row w and, for R = 8, row w + 4; lane l scans chunks
+// l, l + 64, ... of the row and the wave reduces its rows at once, with no
+// partials in LDS and no workgroup barrier before the reduction.
+template <int R>
+__device__ __forceinline__ void slice_stats_rows_by_wave(const float* rows, int ld, int n, int v0, bool greedy,
+                                                         double inv_tau, Rec* out) {
+  static_assert(R % kWaves == 0, "whole rows per wave");
+  constexpr int RPW = R / kWaves;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nc = (n + 3) >> 2;
+  float mx[RPW];
+  int ix[RPW];
+  double z[RPW];
+  scan_chunks<RPW, true>(rows + wave * ld, kWaves * ld, n, v0, inv_tau, lane, nc, 64, mx, ix, z);
+  float m[RPW];
+  int arg[RPW];
+  bool bad[RPW];
+  double f[RPW];
+#pragma unroll
+  for (int h = 0; h < RPW; ++h) {
+    bad[h] = __any(ix[h] < 0);
+    m[h] = mx[h];
+    arg[h] = ix[h];
+    wave_argmax(m[h], arg[h]);  // ties keep the lower index
+    f[h] = (static_cast<double>(mx[h]) - static_cast<double>(m[h])) * inv_tau;
+  }
+  exp_lockstep<RPW>(f);
+#pragma unroll
+  for (int h = 0; h < RPW; ++h) {
+    const double zl = (!greedy && !bad[h] && m[h] != -INFINITY && mx[h] != -INFINITY) ? z[h] * f[h] : 0.0;
+    const double zt = readlane_d(wave_incl_scan(zl), 63);
+    if (lane == 0) {
+      const int r = wave + h * kWaves;
+      out[r].m = m[h];
+      out[r].idx = bad[h] ? -1 : (arg[h] == 0x7fffffff ? v0 : arg[h]);
       out[r].z = zt;
     }
   }
@@ -606,10 +659,10 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
           slice_stats_rows<2, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, cur_lbuf);
           break;
         case 4:
-          slice_stats_rows<4, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, cur_lbuf);
+          slice_stats_rows_by_wave<4>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec);
           break;
         default:
-          slice_stats_rows<8, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, cur_lbuf);
+          slice_stats_rows_by_wave<8>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec);
           break;
       }
       if (tid < E) st_rec(&eager[wg * E + tid], s_rec[tid]);
