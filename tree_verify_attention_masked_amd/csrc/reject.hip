@@ -543,6 +543,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   __shared__ int e_arg[kMaxEager + 1], e_err[kMaxEager + 1];
   __shared__ double e_mass[(kMaxEager + 1) * kMaxTeam];  // each member's share of p
   __shared__ double sh_incl[kWaves];
+  __shared__ double s_lastmass[kMaxTeam];  // the members' slice masses of the last residual pass
   __shared__ int sh_err, sh_fail, sh_len, sh_u, sh_c, sh_x, sh_state, sh_nrej, sh_emit_local, sh_owner, sh_arg;
   __shared__ double sh_m, sh_iz, sh_C, sh_Cold, sh_N, sh_s, sh_lo, sh_target, sh_total;
 
@@ -857,6 +858,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         if (sh_fail) break;
         if (wave == 0) {
           const Rec r = lane < NW ? ld_rec(&part[buf * NW + lane]) : Rec{0.f, 0, 0.0};
+          s_lastmass[lane] = r.z;  // kept for the final draw: no second load of the same records
           const double tot = wave_incl_scan(r.z);
           const bool anybad = __any(lane < NW && r.idx < 0);
           if (lane == 63) {
@@ -908,7 +910,9 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       }
       if (wave == 0) {
         double mass = 0.0;
-        if (!bonus || scanned) {
+        if (scanned) {  // part[buf] holds the last residual pass, merged above
+          mass = s_lastmass[lane];
+        } else if (!bonus) {
           if (lane < NW) mass = ld_rec(&part[buf * NW + lane]).z;
         } else if (lane < NW) {
           mass = e_mass[er * kMaxTeam + lane];
