@@ -270,7 +270,7 @@ def main():
     ws_attn = stv.spec_tree_attn_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, w.max_blocks, code)
     attn_ws = torch.zeros(max(ws_attn, 1), dtype=torch.uint8, device=dev)  # zero once: split arrival counters
     rej_ws = torch.zeros(int(stv.load_library().spec_tree_reject_workspace_size(w.B, w.T, w.V)),
-                         dtype=torch.uint8, device=dev)  # zero once: the sampler's barrier counters
+                         dtype=torch.uint8, device=dev)  # zero once: the sampler's epochs and tagged exchange slots
 
     def attn(c):
         stv.spec_tree_attn(c["q"], c["k"], c["v"], shared["bt"], shared["lens"], shared["parent"], scale=w.scale,

@@ -153,12 +153,14 @@ int spec_tree_attn(const void* q, const void* k_cache, const void* v_cache,
  *   num_accepted  [B] int32 out: L
  *   status        [B] int32 or NULL; on a device-detected error the sequence
  *                 gets L = 0, accepted_nodes = [0, -1, ...], out_tokens all -1
- *   workspace     >= spec_tree_reject_workspace_size(B, T, V) bytes.  Its first
- *                 64 * B bytes hold barrier counters and must be zero before
- *                 the first call; every call that completes leaves them zero,
- *                 so a workspace is zero-filled once and then reused.  Calls
- *                 that overlap in time must not share a workspace.
- * Execution: each sequence is sampled by up to 32 cooperating workgroups that
+ *   workspace     >= spec_tree_reject_workspace_size(B, T, V) bytes, all of it
+ *                 zero before the first call.  It holds, per sequence, an exit
+ *                 counter and a call epoch (the first 64 * B bytes) and the
+ *                 exchange slots, each tagged with the call it was written in;
+ *                 every call that completes leaves it ready for the next, so a
+ *                 workspace is zero-filled once and then reused.  Calls that
+ *                 overlap in time must not share a workspace.
+ * Execution: each sequence is sampled by up to 64 cooperating workgroups that
  * exchange partial sums through the workspace; the grid (B x team size, at
  * most 256 workgroups unless B > 256) must be able to run at once, which holds
  * on an otherwise idle MI355X.  If it cannot, the waits are bounded and the

@@ -36,7 +36,7 @@ def test_workspace_sizes(lib):
     assert ws > 0 and ws % 4 == 0
     assert lib.spec_tree_attn_workspace_size(1, 5, 40, 40, 100, 129, 1) == 0  # unsupported head dim
     ws = lib.spec_tree_reject_workspace_size(2, 5, 32000)
-    assert ws >= 2 * 64 and ws % 16 == 0  # barrier header + partial records
+    assert ws >= 2 * 64 and ws % 16 == 0  # per-sequence header + exchange slots
     assert lib.spec_tree_reject_workspace_size(4, 5, 32000) > ws
     assert lib.spec_tree_reject_workspace_size(0, 5, 32000) == 0
 

@@ -1,9 +1,11 @@
 """Repeated calls sharing one workspace (the way a serving loop or a captured
-graph calls the library): the workspace is zero-filled once, and every call
-must leave the split-arrival and team-barrier counters in its header back at
-zero.  A counter left behind would stop the next call's merge (its output would
-never be written) or its team barriers; the output is poisoned with NaN before
-each call so that a skipped write cannot pass on stale data."""
+graph calls the library): the workspace is zero-filled once.  Attention must
+leave its split-arrival counters back at zero (a counter left behind would stop
+the next call's merge, so its output would never be written; the output is
+poisoned with NaN before each call so that a skipped write cannot pass on stale
+data).  The sampler's exchange slots carry a per-call tag taken from a
+per-sequence epoch in the workspace header: slots written by earlier calls must
+never be taken for this call's, including across the epoch's wrap-around."""
 import numpy as np
 import pytest
 import torch
@@ -67,3 +69,43 @@ def test_sampler_reuses_one_workspace(cfg):
         assert int(d.status.abs().sum()) == 0
         ref = oracle_reject(w, offset=offset)
         compare_reject((acc, toks, nacc), ref)
+
+
+SYNC_WORDS = 16  # int32 words of sampler header per sequence: [1] exit counter, [2] epoch
+
+
+@pytest.mark.parametrize("cfg", [1, 0])
+def test_sampler_epoch_wraps(cfg):
+    """Start the epoch three calls before it wraps (white-box: the header words of
+    each sequence) and check every call against the oracle: the call whose next
+    tag would be 0 restarts the epoch at 0 after clearing every slot, so the
+    stale slots of the first two calls (tags 2^32 - 2 and 2^32 - 1) and of all
+    earlier calls cannot pass for the later calls' (tags 1, 2)."""
+    w = make_config(cfg, with_kv=False)
+    print(f"[reuse] epoch wrap, sampler config {cfg} {w.name}", flush=True)
+    d = DevWorkload(w)
+    lib = stv.load_library()
+    ws = torch.zeros(int(lib.spec_tree_reject_workspace_size(w.B, w.T, w.V)), dtype=torch.uint8, device="cuda")
+    words = ws[: w.B * SYNC_WORDS * 4].view(torch.int32).view(w.B, SYNC_WORDS)
+    # slots of an earlier cycle: run once from a fresh epoch on other logits, so
+    # every slot that walk used holds tag 1 and records that differ from the later
+    # calls' (a slot taken for the wrong call changes their decisions), then move
+    # the epoch to 2^32 - 3
+    stv.spec_tree_reject(d.logits * 0.5, d.probs, d.tokens, d.parent, w.temperature, w.without_replacement, w.seed,
+                         0, status=d.status, workspace=ws)
+    torch.cuda.synchronize()
+    assert words[:, 2].tolist() == [1] * w.B
+    words[:, 2] = -3  # 0xFFFFFFFD
+    for call, offset in enumerate((5, 6, 7, 8)):
+        acc = torch.full((w.B, w.T), -7, dtype=torch.int32, device="cuda")
+        toks = torch.full((w.B, w.T), -7, dtype=torch.int32, device="cuda")
+        nacc = torch.full((w.B,), -7, dtype=torch.int32, device="cuda")
+        stv.spec_tree_reject(d.logits, d.probs, d.tokens, d.parent, w.temperature, w.without_replacement, w.seed,
+                             offset, accepted_nodes=acc, out_tokens=toks, num_accepted=nacc, status=d.status,
+                             workspace=ws)
+        torch.cuda.synchronize()
+        assert int(d.status.abs().sum()) == 0, f"call {call}: device status {d.status.tolist()}"
+        compare_reject((acc, toks, nacc), oracle_reject(w, offset=offset))
+        expect = [-2, 0, 1, 2][call]  # 0xFFFFFFFE, then the wrap to 0, then 1, 2
+        assert words[:, 2].tolist() == [expect] * w.B, f"call {call}: epochs {words[:, 2].tolist()}"
+        assert words[:, 1].tolist() == [0] * w.B, "exit counters must be back at zero"

@@ -27,8 +27,9 @@
 //     scanned weights; for a bonus draw the slice masses of p follow from the
 //     row statistics.  The member whose range holds u * total finds the token
 //     inside its slice.
-// Team barriers spin on a per-sequence counter with a bounded wait; the last
-// member to leave resets the counters, so the workspace header stays zero.
+// Members exchange records through tagged slots (one per exchange and member,
+// written once per call): a reader polls the slots themselves until every one
+// carries this call's tag, with a bounded wait.
 // Decisions are taken in fp64 from the fp32 inputs.  Uniforms: Philox4x32-10
 // (Salmon, Moraes, Dror, Shaw, SC'11), key (seed lo, seed hi), counter (node,
 // b, purpose + 2*(offset >> 32), offset lo); u = (word0 >> 8) * 2^-24.
@@ -47,13 +48,17 @@ constexpr int kMaxTeam = 64;     // workgroups per sequence (one wave merges the
 constexpr int kDeepTeam = 32;    // at most this many for trees with deeper rows (more than 16 nodes)
 constexpr int kEagerCap = 8192;  // floats of eager-row logit slices kept in LDS
 constexpr int kSliceCap = 8192;  // floats of the current row's logits / draft probs kept in LDS
-constexpr int kSyncStride = 16;  // uint32 words of barrier state per sequence (64 B)
+constexpr int kSyncStride = 16;  // uint32 words per sequence (64 B): [1] exit counter, [2] call epoch
 constexpr unsigned kSpinLimit = 1u << 24;
 
 struct Rec {
   float m;   // slice max logit (-inf if none)
   int idx;   // first index of the max; -1 if the slice holds NaN or +inf
   double z;  // sum over the slice of exp((l - m) / t), or a slice mass
+};
+
+struct Slot {
+  unsigned long long w[4];  // (tag << 32) | 32 bits of a Rec: m, idx, z high, z low
 };
 
 struct Team {
@@ -165,9 +170,10 @@ struct TArgs {
   int32_t* out_tokens;
   int32_t* num_accepted;
   int32_t* status;
-  unsigned* sync;  // [B][kSyncStride]: arrive counter, exit counter
-  Rec* eager;      // [B][NW][max(E,1)]
-  Rec* part;       // [B][2][NW]
+  unsigned* sync;  // [B][kSyncStride]: word 1 exit counter, word 2 call epoch
+  Slot* eager;     // [B][NW][max(E,1)]: statistics of the eager rows
+  Slot* part;      // [B][part_rows][NW]: one row of slots per later exchange
+  int part_rows;
   int T, V, NW, S, ld, E, greedy, wr;
   double inv_tau;
   uint64_t seed, offset;
@@ -175,41 +181,68 @@ struct TArgs {
   CompactLaunch c;  // its arguments (accepted / num_accepted unused: the path is in LDS)
 };
 
-// Records exchanged between members (the team spans XCDs, whose L2s are not
-// coherent with each other) are written and read as relaxed agent-scope
-// atomics: write-through stores, coherent loads.  A barrier then needs only
-// each wave's stores to have completed before its arrival is counted -- no
-// write-back or invalidation of the whole L2, which a fence would cost.
-__device__ __forceinline__ void st_rec(Rec* p, const Rec& r) {
-  __hip_atomic_store(&p->m, r.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(&p->idx, r.idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(&p->z, r.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ Rec ld_rec(const Rec* p) {
-  Rec* q = const_cast<Rec*>(p);
-  Rec r;
-  r.m = __hip_atomic_load(&q->m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  r.idx = __hip_atomic_load(&q->idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  r.z = __hip_atomic_load(&q->z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return r;
+// Records cross workgroups (the team spans XCDs, whose L2s are not coherent
+// with each other) through slots written once per call.  Each of a slot's four
+// 64-bit words carries the call's tag in its high half and 32 bits of the
+// record in its low half, and is written and read as one relaxed agent-scope
+// atomic (write-through store, coherent load; naturally aligned 64-bit
+// accesses are single-copy atomic).  A reader that finds the tag in all four
+// words therefore holds the whole record: no arrival counter, no wait for the
+// writer's stores to complete, no fence (which would write back and invalidate
+// the whole L2), and no second round trip to read the record after a barrier.
+// Tags are never 0, so a zero-filled workspace holds no valid slot.
+__device__ __forceinline__ void put_slot(Slot* p, const Rec& r, uint32_t tag) {
+  const unsigned long long t = static_cast<unsigned long long>(tag) << 32;
+  const unsigned long long zb = static_cast<unsigned long long>(__double_as_longlong(r.z));
+  __hip_atomic_store(&p->w[0], t | __float_as_uint(r.m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&p->w[1], t | static_cast<uint32_t>(r.idx), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&p->w[2], t | (zb >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&p->w[3], t | (zb & 0xFFFFFFFFull), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Team barrier number `target`: every member has published its records.
-__device__ __forceinline__ void team_barrier(unsigned* ctr, unsigned target, int* fail) {
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's record stores are complete
-  __syncthreads();
-  if (threadIdx.x == 0 && *fail == 0) {
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        *fail = 1;
-        break;
-      }
+// One wave, every lane active: lane w < NW waits until slot base[h][w * stride]
+// of each of the NR rows h carries `tag`, and returns member w's records
+// (lanes >= NW get `dflt`).  The wait is bounded: past kSpinLimit polls lane 0
+// sets *fail and the records are not to be used.
+template <int NR>
+__device__ __forceinline__ void get_slots(const Slot* const (&base)[NR], int stride, int NW, uint32_t tag,
+                                          const Rec& dflt, Rec (&out)[NR], int* fail) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long w[NR][4];
+  bool ok = lane >= NW;
+  unsigned spins = 0;
+  for (;;) {
+    if (!ok) {
+#pragma unroll
+      for (int h = 0; h < NR; ++h)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          w[h][k] = __hip_atomic_load(const_cast<unsigned long long*>(&base[h][lane * stride].w[k]), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      ok = true;
+#pragma unroll
+      for (int h = 0; h < NR; ++h)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ok = ok && static_cast<uint32_t>(w[h][k] >> 32) == tag;
+    }
+    if (__all(ok)) break;
+    if (++spins > kSpinLimit) {
+      if (lane == 0) *fail = 1;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+#pragma unroll
+  for (int h = 0; h < NR; ++h) {
+    if (lane < NW) {
+      out[h].m = __uint_as_float(static_cast<uint32_t>(w[h][0]));
+      out[h].idx = static_cast<int>(static_cast<uint32_t>(w[h][1]));
+      out[h].z = __longlong_as_double(static_cast<long long>(((w[h][2] & 0xFFFFFFFFull) << 32) |
+                                                             (w[h][3] & 0xFFFFFFFFull)));
+    } else {
+      out[h] = dflt;
     }
   }
-  __syncthreads();
 }
 
 // Starts copying rows [r * src_stride + i], r < nrows, i < n, of global memory
@@ -562,10 +595,12 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   const float* lg_b = a.logits + static_cast<long>(b) * T * V;
   const float* q_b = a.q + static_cast<long>(b) * T * V;
   unsigned* ctr = a.sync + static_cast<long>(b) * kSyncStride;
-  unsigned phase = 0;
-  int buf = 0;
-  Rec* eager = a.eager + static_cast<long>(b) * NW * max(E, 1);
-  Rec* part = a.part + static_cast<long>(b) * 2 * NW;
+  Slot* eager = a.eager + static_cast<long>(b) * NW * max(E, 1);
+  Slot* part = a.part + static_cast<long>(b) * a.part_rows * NW;
+  int xrow = 0;  // the next row of part slots (one per exchange after the eager one)
+  // the call's tag: the sequence's epoch (advanced by the last member to leave) + 1
+  const uint32_t epoch = __hip_atomic_load(ctr + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t tag = epoch + 1u;
 
   // tree and tokens (T <= kThreads: one node per thread) and the eager logit and
   // draft slices, which depend on nothing else: all in flight together
@@ -666,29 +701,29 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
           slice_stats_rows_by_wave<8>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec);
           break;
       }
-      if (tid < E) st_rec(&eager[wg * E + tid], s_rec[tid]);
+      if (tid < E) put_slot(&eager[wg * E + tid], s_rec[tid], tag);
       const float lx = lg_b[off];
       const float qx = (a.greedy ? lg_b : q_b)[off];
-      team_barrier(ctr, NW * ++phase, &sh_fail);
+      // gather every member's eager rows (wave w: rows w and w + 4) and merge them, member order
+      const Rec none = Rec{-INFINITY, 0x7fffffff, 0.0};
+      if (wave + kWaves < E) {
+        const Slot* const rows2[2] = {eager + wave, eager + wave + kWaves};
+        Rec rr[2];
+        get_slots<2>(rows2, E, NW, tag, none, rr, &sh_fail);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          merge_row(rr[h], lane < NW, a.greedy, a.inv_tau, &e_m[wave + h * kWaves], &e_iz[wave + h * kWaves],
+                    &e_arg[wave + h * kWaves], &e_err[wave + h * kWaves], &e_mass[(wave + h * kWaves) * kMaxTeam]);
+      } else if (wave < E) {
+        const Slot* const rows1[1] = {eager + wave};
+        Rec rr[1];
+        get_slots<1>(rows1, E, NW, tag, none, rr, &sh_fail);
+        merge_row(rr[0], lane < NW, a.greedy, a.inv_tau, &e_m[wave], &e_iz[wave], &e_arg[wave], &e_err[wave],
+                  &e_mass[wave * kMaxTeam]);
+      }
       if (cx < T) {
         s_lx[cx] = lx;
         s_qx[cx] = qx;
-      }
-      // merge every eager row at once (wave w: rows w and w + 4), member order
-      if (!sh_fail) {
-        Rec rr[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int r = wave + h * kWaves;
-          rr[h] = Rec{-INFINITY, 0x7fffffff, 0.0};
-          if (r < E && lane < NW) rr[h] = ld_rec(&eager[lane * E + r]);
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int r = wave + h * kWaves;
-          if (r < E) merge_row(rr[h], lane < NW, a.greedy, a.inv_tau, &e_m[r], &e_iz[r], &e_arg[r], &e_err[r],
-                               &e_mass[r * kMaxTeam]);
-        }
       }
       __syncthreads();
     } else {
@@ -722,21 +757,24 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         cq = q_b + static_cast<long>(u) * V + v0;
       }
       __syncthreads();
-      const Rec* rows = part;  // members' statistics of a row past the eager ones
       if (u >= E) {  // a deeper row: its statistics now
         slice_stats_rows<1, kFits>(cl, ld, n, v0, a.greedy, a.inv_tau, s_rec, row_partials);
-        if (tid == 0) st_rec(&part[buf * NW + wg], s_rec[0]);
-        team_barrier(ctr, NW * ++phase, &sh_fail);
-        if (sh_fail) break;
-        rows = part + buf * NW;
-        buf ^= 1;
+        if (xrow >= a.part_rows) {  // more exchanges than planned: cannot happen for a valid tree
+          if (tid == 0) sh_fail = 1;
+          break;
+        }
+        Slot* xs = part + xrow * NW;
+        ++xrow;
+        if (tid == 0) put_slot(&xs[wg], s_rec[0], tag);
         if (wave == 0) {
-          Rec r = Rec{-INFINITY, 0x7fffffff, 0.0};
-          if (lane < NW) r = ld_rec(&rows[lane]);
-          merge_row(r, lane < NW, a.greedy, a.inv_tau, &e_m[kMaxEager], &e_iz[kMaxEager], &e_arg[kMaxEager],
+          const Slot* const rows1[1] = {xs};
+          Rec r[1];
+          get_slots<1>(rows1, 1, NW, tag, Rec{-INFINITY, 0x7fffffff, 0.0}, r, &sh_fail);
+          merge_row(r[0], lane < NW, a.greedy, a.inv_tau, &e_m[kMaxEager], &e_iz[kMaxEager], &e_arg[kMaxEager],
                     &e_err[kMaxEager], &e_mass[kMaxEager * kMaxTeam]);
         }
         __syncthreads();
+        if (sh_fail) break;
       }
       const int er = u < E ? u : kMaxEager;  // this row's merged statistics
       if (tid == 0) {
@@ -814,7 +852,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         excl = wave_shift_up(incl, before);  // lane 0: the waves before it
         return badq;
       };
-      bool scanned = false;  // part[buf] holds the slice masses of the current weights
+      bool scanned = false;  // s_lastmass holds the members' slice masses of the current weights
       // try the children of u in turn
       for (;;) {
         if (tid == 0) {
@@ -847,18 +885,25 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         __syncthreads();
         if (sh_state != 2 || sh_err) break;
         const bool badq = scan_slice(true);
+        if (xrow >= a.part_rows) {
+          if (tid == 0) sh_fail = 1;
+          break;
+        }
+        Slot* xs = part + xrow * NW;
+        ++xrow;
         if (tid == kThreads - 1) {
           Rec r;
           r.m = 0.f;
           r.idx = badq ? -1 : 0;
           r.z = incl;  // slice mass: the last thread's inclusive sum
-          st_rec(&part[buf * NW + wg], r);
+          put_slot(&xs[wg], r, tag);
         }
-        team_barrier(ctr, NW * ++phase, &sh_fail);
-        if (sh_fail) break;
         if (wave == 0) {
-          const Rec r = lane < NW ? ld_rec(&part[buf * NW + lane]) : Rec{0.f, 0, 0.0};
-          s_lastmass[lane] = r.z;  // kept for the final draw: no second load of the same records
+          const Slot* const rows1[1] = {xs};
+          Rec rr[1];
+          get_slots<1>(rows1, 1, NW, tag, Rec{0.f, 0, 0.0}, rr, &sh_fail);
+          const Rec r = rr[0];
+          s_lastmass[lane] = r.z;  // kept for the final draw
           const double tot = wave_incl_scan(r.z);
           const bool anybad = __any(lane < NW && r.idx < 0);
           if (lane == 63) {
@@ -885,8 +930,8 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
           }
         }
         __syncthreads();
+        if (sh_fail) break;
         scanned = sh_total > 0.0;
-        if (sh_c >= 0) buf ^= 1;  // else part[buf] serves the final draw
       }
       if (sh_err || sh_fail) break;
       if (sh_state == 1) {
@@ -902,18 +947,27 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       if (!scanned) {
         scan_slice(false);
         if (!bonus) {  // a zero-mass residual left earlier weights in place: publish them
-          buf ^= 1;    // the other buffer: members may still read the last pass's
-          if (tid == kThreads - 1) st_rec(&part[buf * NW + wg], Rec{0.f, 0, incl});
-          team_barrier(ctr, NW * ++phase, &sh_fail);
+          if (xrow >= a.part_rows) {
+            if (tid == 0) sh_fail = 1;
+            break;
+          }
+          Slot* xs = part + xrow * NW;
+          ++xrow;
+          if (tid == kThreads - 1) put_slot(&xs[wg], Rec{0.f, 0, incl}, tag);
+          if (wave == 0) {
+            const Slot* const rows1[1] = {xs};
+            Rec rr[1];
+            get_slots<1>(rows1, 1, NW, tag, Rec{0.f, 0, 0.0}, rr, &sh_fail);
+            s_lastmass[lane] = rr[0].z;
+          }
+          __syncthreads();
           if (sh_fail) break;
         }
       }
       if (wave == 0) {
         double mass = 0.0;
-        if (scanned) {  // part[buf] holds the last residual pass, merged above
+        if (scanned || !bonus) {  // the masses gathered by the last exchange
           mass = s_lastmass[lane];
-        } else if (!bonus) {
-          if (lane < NW) mass = ld_rec(&part[buf * NW + lane]).z;
         } else if (lane < NW) {
           mass = e_mass[er * kMaxTeam + lane];
         }
@@ -1007,21 +1061,39 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       compact_move(a.c, b, g, c_lb, cL, cfirst, s_path, reinterpret_cast<uint8_t*>(cur_lbuf));
   }
   if (tid == 0) {
-    // leave: the last member out resets the barrier counters for the next call
+    // Leave.  The last member out resets the exit counter and advances the
+    // sequence's epoch, so the next call's tag differs from every tag written
+    // before.  When the next tag would be 0 (after 2^32 - 1 calls) the epoch
+    // starts again at 0, and this member first clears every slot of the
+    // sequence, so no slot written in an earlier cycle can carry a later tag.
     const unsigned prev = atomicAdd(ctr + 1, 1u);
     if (prev == static_cast<unsigned>(NW - 1)) {
-      atomicExch(ctr, 0u);
       atomicExch(ctr + 1, 0u);
+      unsigned next = epoch + 1u;
+      if (next == 0xFFFFFFFFu) {
+        next = 0u;
+        const long ne = static_cast<long>(NW) * max(E, 1), np = static_cast<long>(a.part_rows) * NW;
+        for (long i = 0; i < ne + np; ++i) {
+          Slot* sl = i < ne ? eager + i : part + (i - ne);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) __hip_atomic_store(&sl->w[k], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      atomicExch(ctr + 2, next);
     }
   }
 }
 
 }  // namespace
 
+// Exchanges after the eager one: at most one per visited row past the eager
+// rows (<= T), one per rejected child (<= T - 1) and one final republish.
+int part_rows(int T) { return 2 * T + 1; }
+
 size_t reject_workspace_bytes(int B, int T, int V) {
   const Team t = team_shape(B, T, V);
   const size_t sync = static_cast<size_t>(B) * kSyncStride * sizeof(unsigned);
-  return sync + static_cast<size_t>(B) * t.NW * (std::max(t.E, 1) + 2) * sizeof(Rec);
+  return sync + static_cast<size_t>(B) * t.NW * (std::max(t.E, 1) + part_rows(T)) * sizeof(Slot);
 }
 
 size_t reject_workspace_zero_bytes(int B) { return static_cast<size_t>(B) * kSyncStride * sizeof(unsigned); }
@@ -1039,8 +1111,9 @@ hipError_t launch_reject(const RejectLaunch& L, hipStream_t stream) {
   a.num_accepted = L.num_accepted;
   a.status = L.status;
   a.sync = static_cast<unsigned*>(L.workspace);
-  a.eager = reinterpret_cast<Rec*>(static_cast<char*>(L.workspace) + reject_workspace_zero_bytes(L.B));
+  a.eager = reinterpret_cast<Slot*>(static_cast<char*>(L.workspace) + reject_workspace_zero_bytes(L.B));
   a.part = a.eager + static_cast<size_t>(L.B) * t.NW * std::max(t.E, 1);
+  a.part_rows = part_rows(L.T);
   a.T = L.T;
   a.V = L.V;
   a.NW = t.NW;
