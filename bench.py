@@ -209,6 +209,102 @@ def cpu_baseline(cfg, budget_s):
                       f"{el:.1f} s, {len(os.sched_getaffinity(0))} host cores visible"}
 
 
+
+SWEEP_SHAPES = (
+    # name, layer shape of the configuration it follows, tree builder, tree sizes, prefix lengths
+    ("sequoia_shape", 3, dict(), (1, 2, 4, 8, 16, 32, 64, 128, 256), (1024, 4096, 8192)),
+    ("eagle_shape", 2, dict(tree="random"), (1, 2, 4, 8, 16, 32, 64, 128), (1024, 4096)),
+)
+
+
+def sweep():
+    """Verify cost against tree size and prefix length (one JSON line per point):
+    the layer shapes of the Sequoia-scale configuration (B1, 64 q / 8 kv heads,
+    V 32000, tau 0.6, without replacement, Sequoia-profile trees of depth <= 10)
+    and of the EAGLE-style one (B8, 32 q / 8 kv heads, V 128256, tau 0.7, random
+    trees of depth <= 6), T from 1 to 256 (128 for the wider one), timed per call
+    as in the main run (graphs of back-to-back calls over input copies that
+    together exceed the 256 MB MALL where memory allows)."""
+    import torch
+
+    import tree_verify_attention_masked_amd as stv
+    from workloads import make_config
+
+    lib = stv.load_library()
+    dev = torch.device("cuda:0")
+    for name, cfg, over, Ts, prefixes in SWEEP_SHAPES:
+        for L in prefixes:
+            for T in Ts:
+                depth_cap = 10 if cfg == 3 else 6
+                w = make_config(cfg, T=T, prefix=L, max_depth=min(depth_cap, max(T - 1, 0)), **over)
+                log(f"[sweep] {name} T={T} prefix={L}")
+
+                def up(a, kv=False):
+                    t = torch.from_numpy(np.ascontiguousarray(a))
+                    if kv:
+                        t = t.view(torch.int16).view(torch.bfloat16)
+                    return t.to(dev)
+
+                per_copy = w.k_cache.nbytes * 2 + w.q.nbytes + w.target_logits.nbytes + w.draft_probs.nbytes
+                R = max(1, min(8, math.ceil(512e6 / per_copy)))
+                bt, lens, parent, tok = up(w.block_table), up(w.prefix_lens), up(w.parent), up(w.draft_tokens)
+                cps = [dict(q=up(w.q, True), k=up(w.k_cache, True), v=up(w.v_cache, True), logits=up(w.target_logits),
+                            probs=up(w.draft_probs)) for _ in range(R)]
+                status = torch.zeros((w.B,), dtype=torch.int32, device=dev)
+                ws_a = stv.spec_tree_attn_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, w.max_blocks, stv.SPEC_BF16)
+                attn_ws = torch.zeros(max(ws_a, 1), dtype=torch.uint8, device=dev)
+                rej_ws = torch.zeros(int(lib.spec_tree_reject_workspace_size(w.B, w.T, w.V)), dtype=torch.uint8,
+                                     device=dev)
+                for c in cps:
+                    c["out"] = torch.empty_like(c["q"])
+
+                def attn(c):
+                    stv.spec_tree_attn(c["q"], c["k"], c["v"], bt, lens, parent, scale=w.scale, out=c["out"],
+                                       status=status, workspace=attn_ws if ws_a else None)
+
+                def rejc(c):
+                    stv.spec_tree_reject_compact(c["logits"], c["probs"], tok, parent, w.temperature, c["k"], c["v"],
+                                                 bt, lens, w.without_replacement, w.seed, 0, status=status,
+                                                 workspace=rej_ws)
+
+                us = {}
+                for key, fn in (("attn_us", attn), ("reject_compact_us", rejc)):
+                    for c in cps:
+                        fn(c)
+                    torch.cuda.synchronize()
+                    reps = R * max(1, 8 // R)
+                    g = torch.cuda.CUDAGraph()
+                    st = torch.cuda.Stream()
+                    st.wait_stream(torch.cuda.current_stream())
+                    with torch.cuda.stream(st):
+                        with torch.cuda.graph(g, stream=st):
+                            for i in range(reps):
+                                fn(cps[i % R])
+                    torch.cuda.current_stream().wait_stream(st)
+                    g.replay()
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    rounds = max(1, 64 // reps)
+                    e0.record()
+                    for _ in range(rounds):
+                        g.replay()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    us[key] = e0.elapsed_time(e1) * 1e3 / (rounds * reps)
+                if int(status.abs().sum()):
+                    raise SystemExit(f"device reported input errors: {status.tolist()}")
+                a_bytes, a_flops = attn_work(w)
+                step = us["attn_us"] + us["reject_compact_us"]
+                print(json.dumps({"shape": name, "T": w.T, "prefix": L, "B": w.B, "depth": int(w.info["depth"]),
+                                  "attn_us": round(us["attn_us"], 2),
+                                  "reject_compact_us": round(us["reject_compact_us"], 2),
+                                  "step_us": round(step, 2), "verified_tokens_per_s": round(w.B * w.T / step * 1e6, 1),
+                                  "attn_GBps": round(a_bytes / us["attn_us"] / 1e3, 1),
+                                  "attn_TFLOPs": round(a_flops / us["attn_us"] / 1e6, 2), "input_copies": R}),
+                      flush=True)
+                del cps, attn_ws, rej_ws
+                torch.cuda.empty_cache()
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +319,7 @@ def main():
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
                     help="trace DIR | pmc FETCH_DIR WRITE_DIR: print a markdown summary of rocprofv3 output")
     ap.add_argument("--workload-name", default="chain", help="workload name recorded by --summarize pmc")
+    ap.add_argument("--sweep", action="store_true", help="verify cost against tree size and prefix length (one GPU)")
     args = ap.parse_args()
 
     if args.summarize:
@@ -233,6 +330,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        sweep()
+        return
 
     import torch
 
