@@ -158,6 +158,7 @@ struct TArgs2 {
   float* part_ml;      // [items][RT][2]
   unsigned* counters;  // [B * Hkv * n_rt]
   int B, T, Hq, Hkv, G, R, n_rt, splits, pps, max_blocks, num_blocks;
+  int reorder;  // longest items first (one row tile, B <= 64)
   long items;
   float sl2;
 };
@@ -208,10 +209,56 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
   const int l16 = lane & 15;
   const int quad = lane >> 4;
 
-  // Consecutive workgroup ids are dealt round-robin to the 8 XCDs; give each
-  // XCD a contiguous run of items so the row tiles of one KV chunk share an L2.
-  const long per = (a.items + 7) / 8;
-  const long item = static_cast<long>(blockIdx.x % 8) * per + blockIdx.x / 8;
+  long item;
+  if (a.reorder) {
+    // Ragged batch, one row tile, more items than resident workgroups: the
+    // longest items go first, so the short ones fill the tail.  Workgroup ids
+    // are taken in dispatch order: first every full split (pps pages) of every
+    // (b, g), then each (b, g)'s last split by decreasing length (ties: lower
+    // b), then ids that exit at once.  Lane b of each wave holds sequence b.
+    const int lane = tid & 63;
+    int lb = lane < a.B ? a.plen[lane] : 0;
+    const int cap = a.max_blocks * kBlockSize - a.T;
+    lb = lb < 0 ? 0 : (lb > cap ? cap : lb);
+    const int np = (lb + a.T + kBlockSize - 1) / kBlockSize;
+    const int nu = lane < a.B ? (np + a.pps - 1) / a.pps : 0;
+    const int full = lane < a.B ? (nu - 1) * a.Hkv : 0;
+    const int last = lane < a.B ? np - (nu - 1) * a.pps : -1;
+    int incl = full;  // inclusive prefix sum over sequences
+#pragma unroll
+    for (int w = 1; w < 64; w <<= 1) {
+      const int o = __shfl_up(incl, w);
+      if (lane >= w) incl += o;
+    }
+    const int F = __shfl(incl, 63);
+    const int id = static_cast<int>(blockIdx.x);
+    int b, g, s;
+    if (id < F) {
+      b = __ffsll(static_cast<long long>(__ballot(incl > id))) - 1;
+      const int k = id - (__shfl(incl, b) - __shfl(full, b));
+      const int ns = __shfl(nu, b) - 1;
+      g = k / ns;
+      s = k % ns;
+    } else if (id - F < a.B * a.Hkv) {
+      const int j = id - F, rank = j / a.Hkv;
+      g = j % a.Hkv;
+      int my_rank = 0;  // lanes before this one in the order of last splits
+      for (int o = 0; o < a.B; ++o) {
+        const int lo = __shfl(last, o);
+        my_rank += (lo > last || (lo == last && o < lane)) ? 1 : 0;
+      }
+      b = __ffsll(static_cast<long long>(__ballot(lane < a.B && my_rank == rank))) - 1;
+      s = __shfl(nu, b) - 1;
+    } else {
+      return;
+    }
+    item = (static_cast<long>(b) * a.Hkv + g) * a.splits + s;  // one row tile
+  } else {
+    // Consecutive workgroup ids are dealt round-robin to the 8 XCDs; give each
+    // XCD a contiguous run of items so the row tiles of one KV chunk share an L2.
+    const long per = (a.items + 7) / 8;
+    item = static_cast<long>(blockIdx.x % 8) * per + blockIdx.x / 8;
+  }
   if (item >= a.items) return;
   const int rt = static_cast<int>(item % a.n_rt);
   long rest = item / a.n_rt;
@@ -544,6 +591,9 @@ hipError_t run_tile(const TArgs2& args, hipStream_t stream) {
 
 }  // namespace
 
+#ifndef SPEC_TILE_RAGGED_PPS
+#define SPEC_TILE_RAGGED_PPS 256
+#endif
 AttnPlan plan_attn(int B, int T, int Hq, int Hkv, int D, int max_blocks, int dtype) {
   AttnPlan p{};
   const int G = Hq / Hkv;
@@ -577,6 +627,10 @@ AttnPlan plan_attn(int B, int T, int Hq, int Hkv, int D, int max_blocks, int dty
   // longest ones do not set the makespan alone
   splits = std::max<long>(splits, (max_blocks + 511) / 512);
   splits = std::min<long>(splits, std::max<long>(1, max_blocks / 16));
+  // a ragged batch with more items than resident workgroups is dispatched longest
+  // items first, and cut finer so that no item sets the makespan alone
+  p.reorder = (p.n_rt == 1 && B <= 64 && base * splits > 512) ? 1 : 0;  // 512: two per CU
+  if (p.reorder) splits = std::max<long>(splits, (max_blocks + SPEC_TILE_RAGGED_PPS - 1) / SPEC_TILE_RAGGED_PPS);
   long pps = (max_blocks + splits - 1) / splits;
   pps = (pps + 3) / 4 * 4;
   pps = std::min<long>(pps, kMaxSplitPages);
@@ -612,6 +666,7 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& L, hipStream
   a.max_blocks = L.max_blocks;
   a.num_blocks = L.num_blocks;
   a.items = plan.items;
+  a.reorder = plan.reorder;
   a.sl2 = L.scale * kLog2e;
   if (plan.splits > 1) {
     const size_t base = static_cast<size_t>(L.B) * L.Hkv * plan.n_rt;

@@ -49,6 +49,7 @@ struct AttnPlan {
   int pps;        // pages per split
   long items;     // workgroups of the main kernel (before XCD padding)
   int depth;      // streaming kernel: page slots per wave
+  int reorder;    // tile kernel: longest items first (ragged batches with more items than resident workgroups)
   size_t ws_bytes;
 };
 
