@@ -210,7 +210,9 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
   const int quad = lane >> 4;
 
   long item;
-  if (a.reorder) {
+  bool reorder = false;
+  if constexpr (NRB == 1) reorder = a.reorder != 0;  // (the 128-row kernel is at its register limit)
+  if (reorder) {
     // Ragged batch, one row tile, more items than resident workgroups: the
     // longest items go first, so the short ones fill the tail.  Workgroup ids
     // are taken in dispatch order: first every full split (pps pages) of every
@@ -629,7 +631,7 @@ AttnPlan plan_attn(int B, int T, int Hq, int Hkv, int D, int max_blocks, int dty
   splits = std::min<long>(splits, std::max<long>(1, max_blocks / 16));
   // a ragged batch with more items than resident workgroups is dispatched longest
   // items first, and cut finer so that no item sets the makespan alone
-  p.reorder = (p.n_rt == 1 && B <= 64 && base * splits > 512) ? 1 : 0;  // 512: two per CU
+  p.reorder = (p.nrb == 1 && p.n_rt == 1 && B <= 64 && base * splits > 512) ? 1 : 0;  // 512: two per CU
   if (p.reorder) splits = std::max<long>(splits, (max_blocks + SPEC_TILE_RAGGED_PPS - 1) / SPEC_TILE_RAGGED_PPS);
   long pps = (max_blocks + splits - 1) / splits;
   pps = (pps + 3) / 4 * 4;
