@@ -60,6 +60,12 @@ SMALL = [
     ("rows64_ragged_splits", dict(B=3, Hq=8, Hkv=2, D=128, dtype="bf16", prefix=[3, 9000, 700], tree="random", T=16,
                                   max_depth=5, shuffle_blocks=True)),
     ("rows65_tree", dict(B=1, Hq=5, Hkv=1, D=128, dtype="bf16", prefix=[1234], tree="random", T=13, max_depth=4)),
+    # a ragged batch with more 64-row items than resident workgroups: dispatched
+    # longest items first (full splits, then last splits by decreasing length);
+    # every row is checked, so an item the id mapping skipped or repeated fails
+    ("rows64_longest_first", dict(B=64, Hq=32, Hkv=8, D=128, dtype="bf16",
+                                  prefix=[9000] + [16 + (37 * i) % 600 for i in range(63)], tree="random", T=16,
+                                  max_depth=5, shuffle_blocks=True)),
     # fp32 kernel: ancestors past the first 64 lanes' words, GQA over a long and an almost empty prefix
     ("f32_d64_deep_chain", dict(B=1, Hq=2, Hkv=1, D=64, dtype="f32", prefix=[70], tree="chain", gamma=200)),
     ("f32_d128_gqa_tree", dict(B=2, Hq=6, Hkv=2, D=128, dtype="f32", prefix=[1300, 1], tree="random", T=40,
