@@ -210,6 +210,40 @@ def cpu_baseline(cfg, budget_s):
 
 
 
+def capture_graph(fn_list):
+    """A HIP graph of the calls in fn_list, captured on a side stream."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for fn in fn_list:
+                fn()
+    torch.cuda.current_stream().wait_stream(s)
+    return g
+
+
+def seconds_per_call(fn, copies, reps, calls):
+    """Average duration of fn(copy): HIP events on the current stream around
+    replays of one graph of `reps` back-to-back calls cycling over the copies,
+    about `calls` calls in all."""
+    import torch
+
+    g = capture_graph([lambda c=copies[i % len(copies)]: fn(c) for i in range(reps)])
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rounds = max(1, calls // reps)
+    e0.record()
+    for _ in range(rounds):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (rounds * reps)
+
+
 SWEEP_SHAPES = (
     # name, layer shape of the configuration it follows, tree builder, tree sizes, prefix lengths
     ("sequoia_shape", 3, dict(), (1, 2, 4, 8, 16, 32, 64, 128, 256), (1024, 4096, 8192)),
@@ -269,28 +303,10 @@ def sweep():
 
                 us = {}
                 for key, fn in (("attn_us", attn), ("reject_compact_us", rejc)):
-                    for c in cps:
+                    for c in cps:  # eager pass: validates every copy
                         fn(c)
                     torch.cuda.synchronize()
-                    reps = R * max(1, 8 // R)
-                    g = torch.cuda.CUDAGraph()
-                    st = torch.cuda.Stream()
-                    st.wait_stream(torch.cuda.current_stream())
-                    with torch.cuda.stream(st):
-                        with torch.cuda.graph(g, stream=st):
-                            for i in range(reps):
-                                fn(cps[i % R])
-                    torch.cuda.current_stream().wait_stream(st)
-                    g.replay()
-                    torch.cuda.synchronize()
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    rounds = max(1, 64 // reps)
-                    e0.record()
-                    for _ in range(rounds):
-                        g.replay()
-                    e1.record()
-                    torch.cuda.synchronize()
-                    us[key] = e0.elapsed_time(e1) * 1e3 / (rounds * reps)
+                    us[key] = seconds_per_call(fn, cps, R * max(1, 8 // R), 64) * 1e6
                 if int(status.abs().sum()):
                     raise SystemExit(f"device reported input errors: {status.tolist()}")
                 a_bytes, a_flops = attn_work(w)
@@ -402,23 +418,12 @@ def main():
     if st:
         raise SystemExit(f"device reported input errors: {[c['status'].tolist() for c in copies]}")
 
-    def capture(fn_list):
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                for fn in fn_list:
-                    fn()
-        torch.cuda.current_stream().wait_stream(s)
-        return g
-
     # One graph holds G consecutive steps (step i on copy i % R), so a replay
     # launches G steps at once and the host's per-launch cost is paid once per
     # G steps; single-step graphs cover the remainder of K.
     G = R * max(1, math.ceil(8 / R))
-    step_graphs = [capture([lambda c=c: step(c)]) for c in copies]
-    run_graph = capture([lambda c=copies[i % R]: step(c) for i in range(G)])
+    step_graphs = [capture_graph([lambda c=c: step(c)]) for c in copies]
+    run_graph = capture_graph([lambda c=copies[i % R]: step(c) for i in range(G)])
     log(f"[bench] captured {len(step_graphs)} step graphs and one graph of {G} steps; warmup {args.warmup}")
     for i in range(args.warmup):
         step_graphs[i % R].replay()
@@ -446,17 +451,7 @@ def main():
     reps = args.kernel_reps or max(R, 8 * R if per_copy < 100e6 else R)
     kdur = {}
     for name, fn in (("tree_attn", attn), ("tree_reject_compact", reject_compact)):
-        g = capture([lambda c=copies[i % R]: fn(c) for i in range(reps)])
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        rounds = max(1, 200 // reps)
-        e0.record()
-        for _ in range(rounds):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        kdur[name] = e0.elapsed_time(e1) * 1e-3 / (rounds * reps)  # seconds per call
+        kdur[name] = seconds_per_call(fn, copies, reps, 200)
         log(f"[bench] {name}: {kdur[name] * 1e6:.2f} us per call")
 
     acc = copies[0]["acc"].cpu().numpy()
