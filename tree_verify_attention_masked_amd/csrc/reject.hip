@@ -633,49 +633,77 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
     sh_emit_local = -1;
     sh_owner = 0;
   }
-  __syncthreads();
-  // Checks and the child lists: bit c of kids[p] is set for
-  // every child c of p (an LDS atomic per node), so first_child[i] (the first c
-  // whose parent is i) and next_sib[i] (the first c > i sharing i's parent) are
-  // lowest-set-bit lookups, with no scan over the tree.  kids lives in cur_qbuf,
-  // which is first written when a deeper row is staged.
-  constexpr int kKW = kMaxT / 32;  // bitset words per parent
-  const int nkw = (T + 31) >> 5;   // words in use
-  uint32_t* kids = reinterpret_cast<uint32_t*>(cur_qbuf);
-  for (int i = tid; i < T * kKW; i += kThreads)
-    if ((i & (kKW - 1)) < nkw) kids[i] = 0u;
-  __syncthreads();
-  {
-    int err = 0;
-    for (int i = tid; i < T; i += kThreads) {
-      const int p = s_par[i];
-      const bool ok = (i == 0) ? p == -1 : (p >= 0 && p < i);
-      if (!ok) err |= SPEC_DEV_PARENT;
-      if (i > 0 && ok && (s_tok[i] < 0 || s_tok[i] >= V)) err |= SPEC_DEV_TOKEN;
-      if (i > 0 && ok) atomicOr(&kids[p * kKW + (i >> 5)], 1u << (i & 31));
-    }
-    if (err) atomicOr(&sh_err, err);
-  }
-  __syncthreads();
-  for (int i = tid; i < T; i += kThreads) {
-    int fc = -1;
-    for (int w = 0; w < nkw && fc < 0; ++w) {
-      const uint32_t m = kids[i * kKW + w];
-      if (m) fc = w * 32 + __builtin_ctz(m);
-    }
-    const int p = s_par[i];
-    int ns = -1;
-    if (i > 0 && p >= 0 && p < i) {
-      for (int w = (i + 1) >> 5; w < nkw && ns < 0; ++w) {
-        uint32_t m = kids[p * kKW + w];
-        if (w == ((i + 1) >> 5)) m &= 0xFFFFFFFFu << ((i + 1) & 31);
-        if (m) ns = w * 32 + __builtin_ctz(m);
+  if (T <= 64) {
+    // Checks and the child lists in wave 0, lane i = node i: the children of u
+    // are the lanes whose parent is u (one ballot per node), first_child[i] is
+    // the lowest of i's, next_sib[i] the lowest of its parent's above i.  (tid 0
+    // initialised sh_err above, earlier in this wave's program order.)
+    if (wave == 0) {
+      const bool in = lane < T;
+      const bool ok = in && (lane == 0 ? pv == -1 : (pv >= 0 && pv < lane));
+      int err = 0;
+      if (in && !ok) err |= SPEC_DEV_PARENT;
+      if (in && lane > 0 && ok && (tv < 0 || tv >= V)) err |= SPEC_DEV_TOKEN;
+      const bool child = in && lane > 0 && ok;
+      unsigned long long mine = 0;
+      for (int u = 0; u < T; ++u) {
+        const unsigned long long m = __ballot(child && pv == u);
+        if (lane == u) mine = m;
       }
+      const unsigned long long sibs = __shfl(mine, child ? pv : 0);
+      const unsigned long long later = sibs & ~((2ull << lane) - 1ull);  // siblings after this node
+      if (in) {
+        first_child[lane] = static_cast<int16_t>(mine ? __ffsll(static_cast<long long>(mine)) - 1 : -1);
+        next_sib[lane] = static_cast<int16_t>(child && later ? __ffsll(static_cast<long long>(later)) - 1 : -1);
+      }
+      if (err) atomicOr(&sh_err, err);
     }
-    first_child[i] = static_cast<int16_t>(fc);
-    next_sib[i] = static_cast<int16_t>(ns);
+    __syncthreads();
+  } else {
+    __syncthreads();
+    // Checks and the child lists: bit c of kids[p] is set for
+    // every child c of p (an LDS atomic per node), so first_child[i] (the first c
+    // whose parent is i) and next_sib[i] (the first c > i sharing i's parent) are
+    // lowest-set-bit lookups, with no scan over the tree.  kids lives in cur_qbuf,
+    // which is first written when a deeper row is staged.
+    constexpr int kKW = kMaxT / 32;  // bitset words per parent
+    const int nkw = (T + 31) >> 5;   // words in use
+    uint32_t* kids = reinterpret_cast<uint32_t*>(cur_qbuf);
+    for (int i = tid; i < T * kKW; i += kThreads)
+      if ((i & (kKW - 1)) < nkw) kids[i] = 0u;
+    __syncthreads();
+    {
+      int err = 0;
+      for (int i = tid; i < T; i += kThreads) {
+        const int p = s_par[i];
+        const bool ok = (i == 0) ? p == -1 : (p >= 0 && p < i);
+        if (!ok) err |= SPEC_DEV_PARENT;
+        if (i > 0 && ok && (s_tok[i] < 0 || s_tok[i] >= V)) err |= SPEC_DEV_TOKEN;
+        if (i > 0 && ok) atomicOr(&kids[p * kKW + (i >> 5)], 1u << (i & 31));
+      }
+      if (err) atomicOr(&sh_err, err);
+    }
+    __syncthreads();
+    for (int i = tid; i < T; i += kThreads) {
+      int fc = -1;
+      for (int w = 0; w < nkw && fc < 0; ++w) {
+        const uint32_t m = kids[i * kKW + w];
+        if (m) fc = w * 32 + __builtin_ctz(m);
+      }
+      const int p = s_par[i];
+      int ns = -1;
+      if (i > 0 && p >= 0 && p < i) {
+        for (int w = (i + 1) >> 5; w < nkw && ns < 0; ++w) {
+          uint32_t m = kids[p * kKW + w];
+          if (w == ((i + 1) >> 5)) m &= 0xFFFFFFFFu << ((i + 1) & 31);
+          if (m) ns = w * 32 + __builtin_ctz(m);
+        }
+      }
+      first_child[i] = static_cast<int16_t>(fc);
+      next_sib[i] = static_cast<int16_t>(ns);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   int emitted = -1;  // greedy argmax, known to every member
   if (sh_err == 0) {
