@@ -14,7 +14,9 @@ written from the pages that describe tree-based speculative decoding:
   Sampling");
 * selective KV-cache compaction to the accepted path (the EAGLE report's
   "Important Implementation Detail" and "Issue: Speculative Decoding on vLLM";
-  the SGLang "SpeculativeDecoding" doc, "Prefix Match").
+  the SGLang "SpeculativeDecoding" doc, "Prefix Match");
+* the step before attention: rotary positions that follow the tree and the
+  write of the tree's K/V rows into the paged cache (``rope.py``).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  It shares no code with the HIP library
@@ -41,3 +43,4 @@ from .reject import (  # noqa: F401
     FLAG_MARGIN,
 )
 from .compact import kv_compact  # noqa: F401
+from .rope import rope, tree_kv_write, tree_positions  # noqa: F401
