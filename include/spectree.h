@@ -8,7 +8,9 @@
  *   spec_tree_reject  tree rejection sampling (greedy, with replacement,
  *                     or Sequoia-style without replacement)
  *   spec_kv_compact   keep only the accepted root-to-leaf path in the KV cache
- * and spec_tree_reject_compact, the last two in one launch.
+ * and spec_tree_reject_compact, the last two in one launch; and, for the step
+ * before them, spec_tree_kv_write (the tree's K/V rows into the paged cache,
+ * keys and queries rotated for their tree positions).
  *
  * Conventions shared by every call
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
@@ -34,7 +36,8 @@
  *     block_size = 16.  Logical position t of sequence b lives at
  *     cache[block_table[b][t / 16]][kv_head][t % 16][:].  Tree node i's K/V row
  *     is at logical position prefix_lens[b] + i, written by the caller before
- *     spec_tree_attn (with its rotary position prefix_lens[b] + depth(i)).
+ *     spec_tree_attn (with its rotary position prefix_lens[b] + depth(i)), for
+ *     instance with spec_tree_kv_write.
  */
 #ifndef SPECTREE_H
 #define SPECTREE_H
@@ -231,6 +234,35 @@ int spec_tree_reject_compact(const float* target_logits, const float* draft_prob
                              const int32_t* prefix_lens, int32_t* new_lens,
                              int Hkv, int D, int block_size, int max_blocks_per_seq,
                              int num_blocks, int dtype, void* stream);
+
+/* ----------------------------------------------------------------------
+ * spec_tree_kv_write — the step before verify attention: write every tree
+ * node's K and V rows into the paged cache, the key (and, if given, the
+ * queries, in place) rotated for the node's position.
+ *
+ * Node i of sequence b is at position prefix_lens[b] + depth(i): the tree is
+ * scored in one flattened pass ("Report: Support nextn speculative decoding",
+ * implementation summary, step 3), each token at the position it would have
+ * along its own path (the position_ids of "Issue: Speculative Decoding on
+ * vLLM").  Its rows go to logical slot prefix_lens[b] + i, where
+ * spec_tree_attn reads them.  Rotation: RoFormer's rotary position embedding
+ * in the half-split layout -- for j < D/2 the pair (x_j, x_{j+D/2}) at position
+ * p turns by p * rope_theta^(-2j/D) (angles in fp64) -- or none when
+ * rope_theta == 0.  V rows are copied bit for bit.
+ *
+ *   k_new, v_new [B, T, Hkv, D] dtype: the nodes' keys (before rotation) and values
+ *   q            [B, T, Hq, D] dtype, rotated in place, or NULL
+ *   k_cache, v_cache, block_table, prefix_lens, parent  as for spec_tree_attn;
+ *                the caches are written at the T slots of each sequence only
+ *   status       [B] int32 or NULL; a bad parent row or prefix length leaves
+ *                the sequence unwritten, a bad block index skips that slot's rows
+ *   rope_theta   >= 0 and finite (10000 for Llama-2 layers, 500000 for Llama-3)
+ * Supported: as spec_tree_attn; Hq % Hkv == 0 when q is given.
+ * ---------------------------------------------------------------------- */
+int spec_tree_kv_write(const void* k_new, const void* v_new, void* q, void* k_cache, void* v_cache,
+                       const int32_t* block_table, const int32_t* prefix_lens, const int32_t* parent,
+                       int32_t* status, int B, int T, int Hq, int Hkv, int D, int block_size,
+                       int max_blocks_per_seq, int num_blocks, float rope_theta, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -122,6 +122,27 @@ def test_reject_compact_host_validation(lib):
     assert call(B=0) == 0
 
 
+
+def test_kv_write_host_validation(lib):
+    def call(**kw):
+        a = dict(B=1, T=5, Hq=4, Hkv=2, D=128, bs=16, mb=4, nb=4, theta=10000.0, dtype=1, q=FAKE, k=FAKE)
+        a.update(kw)
+        return lib.spec_tree_kv_write(a["k"], FAKE, a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, None, a["B"], a["T"],
+                                      a["Hq"], a["Hkv"], a["D"], a["bs"], a["mb"], a["nb"], a["theta"], a["dtype"],
+                                      None)
+    assert call(k=None) == -1
+    assert call(Hq=3) == -1            # query heads must be a multiple of kv heads
+    assert call(Hq=0) == -1
+    assert call(theta=-1.0) == -1
+    assert call(theta=float("nan")) == -1
+    assert call(theta=float("inf")) == -1
+    assert call(D=64) == -2            # bf16 needs D = 128
+    assert call(bs=8) == -2
+    assert call(T=300, mb=40) == -2
+    assert call(T=100, mb=4) == -1     # the table cannot hold the tree
+    assert call(B=0) == 0
+    assert call(B=0, q=None, Hq=0) == 0  # no queries to rotate
+
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 2, 2, 128, dtype=torch.bfloat16)

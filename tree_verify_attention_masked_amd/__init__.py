@@ -8,7 +8,9 @@ include/spectree.h):
   spec_tree_reject  tree rejection sampling (greedy / with / without replacement)
   spec_kv_compact   keep only the accepted path in the KV cache
 
-and spec_tree_reject_compact, the last two in one launch.
+and spec_tree_reject_compact, the last two in one launch; spec_tree_kv_write
+writes the tree's K/V rows into the paged cache (rotated for their tree
+positions) before the attention.
 
 This package is the thin PyTorch binding: tensors in, device pointers and the
 current HIP stream out to the library.
@@ -27,5 +29,6 @@ from .binding import (  # noqa: F401
     spec_tree_attn_workspace_size,
     spec_tree_reject,
     spec_tree_reject_compact,
+    spec_tree_kv_write,
     spec_version,
 )

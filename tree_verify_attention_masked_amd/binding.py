@@ -43,6 +43,8 @@ _SIGNATURES = {
     "spec_tree_reject": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_uint64,
                               ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_kv_compact": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
+    "spec_tree_kv_write": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                                ctypes.c_float, _i, _vp]),
     "spec_tree_reject_compact": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_uint64,
                                       ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp, _sz,
                                       _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
@@ -263,6 +265,37 @@ def spec_tree_reject_compact(target_logits, draft_probs, draft_tokens, parent, t
                                       _dtype_code(k_cache), _stream(dev))
     _check(rc, "spec_tree_reject_compact")
     return accepted_nodes, out_tokens, num_accepted, new_lens
+
+
+def spec_tree_kv_write(k_new, v_new, q, k_cache, v_cache, block_table, prefix_lens, parent, rope_theta,
+                       status=None):
+    """Write every tree node's K/V rows into the paged cache at slot prefix + node, the keys and (if q is
+    given) the queries rotated in place for position prefix + depth.  Returns nothing."""
+    lib = load_library()
+    _need(k_new, "k_new", ndim=4)
+    _need(v_new, "v_new", k_new.dtype, 4)
+    _need(k_cache, "k_cache", k_new.dtype, 4)
+    _need(v_cache, "v_cache", k_new.dtype, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(prefix_lens, "prefix_lens", torch.int32, 1)
+    _need(parent, "parent", torch.int32, 2)
+    B, T, Hkv, D = k_new.shape
+    if tuple(v_new.shape) != (B, T, Hkv, D):
+        raise ValueError("v_new shape disagrees with k_new")
+    Hq = 0
+    if q is not None:
+        _need(q, "q", k_new.dtype, 4)
+        if q.shape[0] != B or q.shape[1] != T or q.shape[3] != D:
+            raise ValueError("q shape disagrees with k_new")
+        Hq = q.shape[2]
+    nb, _, bs, _ = k_cache.shape
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    rc = lib.spec_tree_kv_write(_ptr(k_new), _ptr(v_new), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                _ptr(prefix_lens), _ptr(parent), _ptr(status), B, T, Hq, Hkv, D, bs,
+                                block_table.shape[1], nb, float(rope_theta), _dtype_code(k_new),
+                                _stream(k_new.device))
+    _check(rc, "spec_tree_kv_write")
 
 
 def spec_status_string(code: int) -> str:

@@ -214,4 +214,39 @@ int spec_tree_reject_compact(const float* target_logits, const float* draft_prob
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
+int spec_tree_kv_write(const void* k_new, const void* v_new, void* q, void* k_cache, void* v_cache,
+                       const int32_t* block_table, const int32_t* prefix_lens, const int32_t* parent,
+                       int32_t* status, int B, int T, int Hq, int Hkv, int D, int block_size,
+                       int max_blocks_per_seq, int num_blocks, float rope_theta, int dtype, void* stream) {
+  const int rc = check_kv_shapes(B, T, Hkv, D, block_size, max_blocks_per_seq, num_blocks, dtype);
+  if (rc != SPEC_OK) return rc;
+  if (q != nullptr && (Hq < 1 || Hq % Hkv != 0)) return SPEC_ERR_INVALID_ARG;
+  if (!(rope_theta >= 0.0f) || std::isinf(rope_theta)) return SPEC_ERR_INVALID_ARG;
+  if (B == 0) return SPEC_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !prefix_lens || !parent) {
+    return SPEC_ERR_INVALID_ARG;
+  }
+  KvWriteLaunch L{};
+  L.k_new = k_new;
+  L.v_new = v_new;
+  L.q = q;
+  L.k_cache = k_cache;
+  L.v_cache = v_cache;
+  L.block_table = block_table;
+  L.prefix_lens = prefix_lens;
+  L.parent = parent;
+  L.status = status;
+  L.B = B;
+  L.T = T;
+  L.Hq = Hq;
+  L.Hkv = Hkv;
+  L.D = D;
+  L.max_blocks = max_blocks_per_seq;
+  L.num_blocks = num_blocks;
+  L.bf16 = dtype == SPEC_BF16 ? 1 : 0;
+  L.theta = rope_theta;
+  const hipError_t e = launch_kv_write(L, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
 }  // extern "C"

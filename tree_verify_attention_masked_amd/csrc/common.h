@@ -109,4 +109,20 @@ hipError_t launch_reject(const RejectLaunch& a, hipStream_t stream);
 
 hipError_t launch_compact(const CompactLaunch& a, hipStream_t stream);
 
+struct KvWriteLaunch {
+  const void* k_new;
+  const void* v_new;
+  void* q;  // nullable
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  const int32_t* prefix_lens;
+  const int32_t* parent;
+  int32_t* status;
+  int B, T, Hq, Hkv, D, max_blocks, num_blocks, bf16;
+  float theta;
+};
+
+hipError_t launch_kv_write(const KvWriteLaunch& a, hipStream_t stream);
+
 }  // namespace spectree
