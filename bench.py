@@ -17,6 +17,10 @@ work and one host launch per several steps; the K timed steps are bracketed by
 torch.cuda.synchronize().  Per-kernel average durations come from HIP events
 around graphs that repeat one call many times on the same stream.
 
+The line's `kernels` also times spec_tree_kv_write (the step before attention:
+the tree's K/V rows into the cache, rotated for their tree positions); it is not
+part of the timed step, whose inputs already hold those rows.
+
 Prints ONE JSON line on stdout; progress goes to stderr.
 
 `roofline.traffic` comes from the committed rocprofv3 counter summary
@@ -454,6 +458,19 @@ def main():
         kdur[name] = seconds_per_call(fn, copies, reps, 200)
         log(f"[bench] {name}: {kdur[name] * 1e6:.2f} us per call")
 
+    # The step before attention (not part of the timed step, whose inputs already
+    # hold the tree's rows): the tree's K/V rows into the cache, keys and queries
+    # rotated for their tree positions.
+    kv_new = dict(k=torch.zeros((w.B, w.T, w.Hkv, w.D), dtype=copies[0]["k"].dtype, device=dev))
+    kv_new["v"] = torch.zeros_like(kv_new["k"])
+
+    def kv_write(c):
+        stv.spec_tree_kv_write(kv_new["k"], kv_new["v"], c["q"], c["k"], c["v"], shared["bt"], shared["lens"],
+                               shared["parent"], 10000.0, status=c["status"])
+
+    t_kvw = seconds_per_call(kv_write, copies, reps, 200)
+    log(f"[bench] tree_kv_write: {t_kvw * 1e6:.2f} us per call")
+
     acc = copies[0]["acc"].cpu().numpy()
     nacc = copies[0]["nacc"].cpu().numpy()
     # did the stop node form a residual (some child of it rejected)?
@@ -489,6 +506,10 @@ def main():
                          "GB/s": round(by / kdur[name] / 1e9, 1)}
         if fl:
             kernels[name]["TFLOP/s"] = round(fl / kdur[name] / 1e12, 2)
+    elt = 2 if w.dtype == "bf16" else 4
+    kvw_bytes = w.B * w.T * w.D * elt * (4 * w.Hkv + 2 * w.Hq)  # K, V in and out; Q in and out
+    kernels["tree_kv_write"] = {"us": round(t_kvw * 1e6, 2), "bytes": int(kvw_bytes),
+                                "GB/s": round(kvw_bytes / t_kvw / 1e9, 1), "in_step": False}
     kernels["tree_attn"]["hbm_frac"] = round(a_bytes / kdur["tree_attn"] / 1e9 / HBM_PEAK_GBS, 4)
     kernels["tree_attn"]["mfma_frac"] = round(a_flops / kdur["tree_attn"] / 1e12 / BF16_PEAK_TFLOPS, 4)
 

@@ -12,10 +12,11 @@
 // turns by p * theta^(-2j/D); theta = 0 writes the rows unrotated.
 //
 // One workgroup per (sequence, chunk of rows): the parent row is staged in LDS
-// and every node's depth found by pointer jumping (8 rounds cover T <= 256);
-// then each wave takes one row at a time -- a query head, a key head or a value
-// head of one node -- with lane j on the pair (j, j + D/2).  Angles, sines and
-// cosines are taken in fp64, so positions of any length keep full precision.
+// and every node's depth found by pointer jumping (ceil(log2 T) rounds); then
+// each wave takes four rows at a time (query, key or value heads of the nodes,
+// their loads in flight together), lane j on the pair (j, j + D/2).  Angles,
+// sines and cosines are taken in fp64, so positions of any length keep full
+// precision.
 #include <math.h>
 
 #include "common.h"
@@ -56,6 +57,7 @@ __device__ __forceinline__ void st_elt(void* p, long i, float v) {
 }
 
 constexpr int kRowsPerBlock = 4;  // one per wave
+constexpr int kUnroll = 4;        // rows per wave in flight together
 
 template <bool kBf16>
 __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
     if (!ok) atomicOr(&s_err, SPEC_DEV_PARENT);
   }
   __syncthreads();
-  for (int r = 0; r < 8; ++r) {  // after round r, up = the ancestor 2^(r+1) steps above (or -1)
+  for (int r = 0; (1 << r) < T; ++r) {  // after round r, up = the ancestor 2^(r+1) steps above (or -1)
     int up = -1, dep = 0;
     if (tid < T) {
       up = s_up[tid];
@@ -102,45 +104,81 @@ __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
   const int nrows = T * per_node;
   const int half = a.D >> 1;
   const int32_t* bt_b = a.bt + static_cast<long>(b) * a.max_blocks;
-  for (int row = blockIdx.x * kRowsPerBlock + wave; row < nrows; row += gridDim.x * kRowsPerBlock) {
-    const int i = row / per_node, r = row % per_node;
-    const void* src;
-    void* dst;
-    long si, di;
-    bool rot;
-    if (r < a.Hq) {  // a query head, rotated in place
-      if (a.q == nullptr) continue;
-      si = di = ((static_cast<long>(b) * T + i) * a.Hq + r) * a.D;
-      src = a.q;
-      dst = a.q;
-      rot = a.rotate != 0;
-    } else {
-      const bool is_k = r < a.Hq + a.Hkv;
-      const int g = r - a.Hq - (is_k ? 0 : a.Hkv);
-      const int t = Lb + i;
-      const int blk = bt_b[t / kBlockSize];
-      if (blk < 0 || blk >= a.num_blocks) {
-        if (lane == 0) report(a.status, b, SPEC_DEV_BLOCK);
-        continue;
+  // Each wave takes a contiguous run of rows, kUnroll at a time so that their
+  // loads are in flight together; consecutive rows mostly belong to one node,
+  // whose angles (the same for all its heads) are computed once.
+  const int nwaves = gridDim.x * kRowsPerBlock;
+  const int rpw = (nrows + nwaves - 1) / nwaves;
+  const int r_begin = min(nrows, (blockIdx.x * kRowsPerBlock + wave) * rpw);
+  const int r_end = min(nrows, r_begin + rpw);
+  int trig_node = -1;  // node whose cosine and sine this lane holds
+  double c = 1.0, sn = 0.0;
+  for (int row0 = r_begin; row0 < r_end; row0 += kUnroll) {
+    long si[kUnroll], di[kUnroll];
+    const void* src[kUnroll];
+    void* dst[kUnroll];
+    bool live[kUnroll], rot[kUnroll];
+    int node[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int row = row0 + u;
+      live[u] = false;
+      rot[u] = false;
+      node[u] = 0;
+      si[u] = di[u] = 0;
+      src[u] = nullptr;
+      dst[u] = nullptr;
+      if (row >= r_end) continue;
+      const int i = row / per_node, r = row % per_node;
+      node[u] = i;
+      if (r < a.Hq) {  // a query head, rotated in place
+        si[u] = di[u] = ((static_cast<long>(b) * T + i) * a.Hq + r) * a.D;
+        src[u] = a.q;
+        dst[u] = a.q;
+        rot[u] = a.rotate != 0;
+        live[u] = true;
+      } else {
+        const bool is_k = r < a.Hq + a.Hkv;
+        const int g = r - a.Hq - (is_k ? 0 : a.Hkv);
+        const int t = Lb + i;
+        const int blk = bt_b[t / kBlockSize];
+        if (blk < 0 || blk >= a.num_blocks) {
+          if (lane == 0) report(a.status, b, SPEC_DEV_BLOCK);
+          continue;
+        }
+        si[u] = ((static_cast<long>(b) * T + i) * a.Hkv + g) * a.D;
+        di[u] = ((static_cast<long>(blk) * a.Hkv + g) * kBlockSize + t % kBlockSize) * a.D;
+        src[u] = is_k ? a.k_new : a.v_new;
+        dst[u] = is_k ? a.k_cache : a.v_cache;
+        rot[u] = is_k && a.rotate != 0;
+        live[u] = true;
       }
-      si = ((static_cast<long>(b) * T + i) * a.Hkv + g) * a.D;
-      di = ((static_cast<long>(blk) * a.Hkv + g) * kBlockSize + t % kBlockSize) * a.D;
-      src = is_k ? a.k_new : a.v_new;
-      dst = is_k ? a.k_cache : a.v_cache;
-      rot = is_k && a.rotate != 0;
     }
     if (lane < half) {
-      const float x0 = ld_elt<kBf16>(src, si + lane), x1 = ld_elt<kBf16>(src, si + lane + half);
-      float y0 = x0, y1 = x1;
-      if (rot) {
-        const double ang =
-            static_cast<double>(Lb + s_dep[i]) * exp2(-(2.0 * lane / a.D) * a.log2_theta);
-        const double c = cos(ang), s = sin(ang);
-        y0 = static_cast<float>(static_cast<double>(x0) * c - static_cast<double>(x1) * s);
-        y1 = static_cast<float>(static_cast<double>(x1) * c + static_cast<double>(x0) * s);
+      float x0[kUnroll], x1[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        x0[u] = live[u] ? ld_elt<kBf16>(src[u], si[u] + lane) : 0.f;
+        x1[u] = live[u] ? ld_elt<kBf16>(src[u], si[u] + lane + half) : 0.f;
       }
-      st_elt<kBf16>(dst, di + lane, y0);
-      st_elt<kBf16>(dst, di + lane + half, y1);
+      const double inv_freq = exp2(-(2.0 * lane / a.D) * a.log2_theta);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (!live[u]) continue;
+        float y0 = x0[u], y1 = x1[u];
+        if (rot[u]) {
+          if (node[u] != trig_node) {
+            const double ang = static_cast<double>(Lb + s_dep[node[u]]) * inv_freq;
+            c = cos(ang);
+            sn = sin(ang);
+            trig_node = node[u];
+          }
+          y0 = static_cast<float>(static_cast<double>(x0[u]) * c - static_cast<double>(x1[u]) * sn);
+          y1 = static_cast<float>(static_cast<double>(x1[u]) * c + static_cast<double>(x0[u]) * sn);
+        }
+        st_elt<kBf16>(dst[u], di[u] + lane, y0);
+        st_elt<kBf16>(dst[u], di[u] + lane + half, y1);
+      }
     }
   }
 }
@@ -168,7 +206,10 @@ hipError_t launch_kv_write(const KvWriteLaunch& L, hipStream_t stream) {
   a.rotate = L.theta > 0.0f ? 1 : 0;
   a.log2_theta = L.theta > 0.0f ? log2(static_cast<double>(L.theta)) : 0.0;
   const long rows = static_cast<long>(L.T) * (a.Hq + 2 * a.Hkv);
-  const long chunks = std::min<long>((rows + kRowsPerBlock - 1) / kRowsPerBlock, 64);
+  // about 1024 workgroups in all (each finds the tree's depths once)
+  const long per_seq = std::max<long>(1, std::min<long>((rows + kRowsPerBlock - 1) / kRowsPerBlock,
+                                                        1024 / std::max(1, L.B)));
+  const long chunks = per_seq;
   const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(L.B));
   if (L.bf16) {
     hipLaunchKernelGGL(tree_kv_write_kernel<true>, grid, dim3(256), 0, stream, a);
