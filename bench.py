@@ -18,8 +18,10 @@ torch.cuda.synchronize().  Per-kernel average durations come from HIP events
 around graphs that repeat one call many times on the same stream.
 
 The line's `kernels` also times spec_tree_kv_write (the step before attention:
-the tree's K/V rows into the cache, rotated for their tree positions); it is not
-part of the timed step, whose inputs already hold those rows.
+the tree's K/V rows into the cache, rotated for their tree positions) and
+spec_tree_truncate (top-k 50 then top-p 0.9 on the target logits, out of place);
+neither is part of the timed step, whose inputs already hold the tree's rows and
+whose target is not truncated.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
@@ -471,6 +473,16 @@ def main():
     t_kvw = seconds_per_call(kv_write, copies, reps, 200)
     log(f"[bench] tree_kv_write: {t_kvw * 1e6:.2f} us per call")
 
+    # Top-k / top-p truncation of the target logits (top-k 50, then top-p 0.9), out of place so that
+    # every call sees the untruncated rows; not part of the timed step, whose target is not truncated.
+    trunc_out = torch.empty_like(copies[0]["logits"])
+
+    def truncate(c):
+        stv.spec_tree_truncate(c["logits"], w.temperature, 50, 0.9, out=trunc_out, status=c["status"])
+
+    t_trunc = seconds_per_call(truncate, copies, reps, 200)
+    log(f"[bench] tree_truncate: {t_trunc * 1e6:.2f} us per call")
+
     acc = copies[0]["acc"].cpu().numpy()
     nacc = copies[0]["nacc"].cpu().numpy()
     # did the stop node form a residual (some child of it rejected)?
@@ -510,6 +522,10 @@ def main():
     kvw_bytes = w.B * w.T * w.D * elt * (4 * w.Hkv + 2 * w.Hq)  # K, V in and out; Q in and out
     kernels["tree_kv_write"] = {"us": round(t_kvw * 1e6, 2), "bytes": int(kvw_bytes),
                                 "GB/s": round(kvw_bytes / t_kvw / 1e9, 1), "in_step": False}
+    trunc_bytes = w.B * w.T * w.V * 4 * 2  # every logit read once and written once (out of place)
+    kernels["tree_truncate"] = {"us": round(t_trunc * 1e6, 2), "bytes": int(trunc_bytes),
+                                "GB/s": round(trunc_bytes / t_trunc / 1e9, 1), "in_step": False,
+                                "top_k": 50, "top_p": 0.9}
     kernels["tree_attn"]["hbm_frac"] = round(a_bytes / kdur["tree_attn"] / 1e9 / HBM_PEAK_GBS, 4)
     kernels["tree_attn"]["mfma_frac"] = round(a_flops / kdur["tree_attn"] / 1e12 / BF16_PEAK_TFLOPS, 4)
 

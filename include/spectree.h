@@ -10,7 +10,8 @@
  *   spec_kv_compact   keep only the accepted root-to-leaf path in the KV cache
  * and spec_tree_reject_compact, the last two in one launch; and, for the step
  * before them, spec_tree_kv_write (the tree's K/V rows into the paged cache,
- * keys and queries rotated for their tree positions).
+ * keys and queries rotated for their tree positions); spec_tree_truncate
+ * applies top-k / top-p to the target logits before the sampler.
  *
  * Conventions shared by every call
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
@@ -263,6 +264,38 @@ int spec_tree_kv_write(const void* k_new, const void* v_new, void* q, void* k_ca
                        const int32_t* block_table, const int32_t* prefix_lens, const int32_t* parent,
                        int32_t* status, int B, int T, int Hq, int Hkv, int D, int block_size,
                        int max_blocks_per_seq, int num_blocks, float rope_theta, int dtype, void* stream);
+
+/* ----------------------------------------------------------------------
+ * spec_tree_truncate — top-k / top-p truncation of the target logits, for a
+ * sampler that verifies against a truncated target (the Sequoia summary,
+ * "Sequoia: Scalable and Robust Speculative Decoding", robustness to the top-p
+ * hyperparameter).  Run it on target_logits before spec_tree_reject.
+ *
+ * Every row (b, u) keeps {x : logit >= t} and sets the other entries to -inf,
+ * so the sampler gives them probability 0 in every acceptance test, residual
+ * and final draw.  t is the k-th largest finite logit for top-k (Fan et al.
+ * 2018) and, for top-p (Holtzman et al. 2020), the largest logit value v such
+ * that {logit >= v} holds at least top_p of softmax(logits / temperature);
+ * equal logits are never split.  Both rules: top-k first, then top-p over the
+ * top-k set renormalised.  Temperature 0: top-p keeps the logits tied at the
+ * maximum.  The top-p masses are fp32 exponentials summed in fp64 (about 1e-7
+ * relative): a top_p within that distance of a cumulative mass may keep one
+ * group of equal logits more or fewer than exact arithmetic would.
+ *
+ *   logits_in    [B, T, V] float32
+ *   logits_out   [B, T, V] float32: == logits_in for in place (only dropped
+ *                entries are written), else disjoint from it (every entry
+ *                written)
+ *   temperature  >= 0 and finite, the sampler's
+ *   top_k        <= 0: off; >= the row's count of finite logits keeps them all
+ *   top_p        > 0; >= 1: off
+ *   status       [B] int32 or NULL; a row holding NaN or +inf gets
+ *                SPEC_DEV_NONFINITE and is left as it is (copied when out of place)
+ * Supported: any B, T >= 1, 1 <= V <= 2^24.  Caller-side -inf entries count as
+ * dropped already.
+ * ---------------------------------------------------------------------- */
+int spec_tree_truncate(const float* logits_in, float* logits_out, int B, int T, int V,
+                       float temperature, int top_k, float top_p, int32_t* status, void* stream);
 
 #ifdef __cplusplus
 }

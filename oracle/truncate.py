@@ -56,21 +56,21 @@ def _keep_top_p(vals: np.ndarray, kept: np.ndarray, temperature: float, top_p: f
     """Mask of the nucleus within `kept`, and the decision's margin: the
     distance of top_p from the two cumulative masses around the threshold
     (mass of the values above t, and of the values >= t)."""
-    if top_p >= 1.0:
+    if top_p >= 1.0 or not kept.any():
         return kept.copy(), math.inf
     if temperature == 0.0:
         return kept & (vals == vals[kept].max()), math.inf
-    p = np.zeros(vals.size, dtype=np.float64)
-    p[kept] = softmax64(vals[kept], temperature)  # renormalised on the kept set
-    distinct = np.unique(vals[kept])[::-1]        # distinct values, descending
-    above = 0.0                                   # mass of the values > the current one
-    for v in distinct:
-        at = above + p[kept & (vals == v)].sum()
-        if at >= top_p:
-            return kept & (vals >= v), min(top_p - above, at - top_p)
-        above = at
-    # the masses summed short of top_p by rounding: keep everything
-    return kept.copy(), 0.0
+    pk = softmax64(vals[kept], temperature)                 # renormalised on the kept set
+    distinct, group = np.unique(vals[kept], return_inverse=True)
+    distinct = distinct[::-1]                               # distinct values, descending
+    group_mass = np.bincount(group, weights=pk, minlength=distinct.size)[::-1]
+    at = np.cumsum(group_mass)                              # mass of the values >= distinct[j]
+    reached = np.flatnonzero(at >= top_p)
+    if reached.size == 0:  # the masses summed short of top_p by rounding: keep everything
+        return kept.copy(), 0.0
+    j = int(reached[0])
+    above = float(at[j - 1]) if j > 0 else 0.0              # mass of the values > distinct[j]
+    return kept & (vals >= distinct[j]), min(top_p - above, float(at[j]) - top_p)
 
 
 def truncate_row(logits_row, temperature, top_k, top_p):

@@ -149,3 +149,24 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         stv.spec_tree_attn(q, q, q, torch.zeros(1, 1, dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
                            torch.zeros(1, 2, dtype=torch.int32))
+
+
+def test_truncate_host_validation(lib):
+    def call(**kw):
+        a = dict(B=1, T=5, V=100, tau=1.0, k=10, p=0.9, i=FAKE, o=FAKE)
+        a.update(kw)
+        return lib.spec_tree_truncate(a["i"], a["o"], a["B"], a["T"], a["V"], a["tau"], a["k"], a["p"], None, None)
+    assert call(i=None) == -1
+    assert call(o=None) == -1
+    assert call(B=-1) == -1
+    assert call(T=0) == -1
+    assert call(V=0) == -1
+    assert call(V=(1 << 24) + 1) == -2
+    assert call(tau=-0.5) == -1
+    assert call(tau=float("inf")) == -1
+    assert call(tau=float("nan")) == -1
+    assert call(p=0.0) == -1
+    assert call(p=float("nan")) == -1
+    assert call(B=0) == 0
+    assert call(B=0, i=None) == 0    # nothing to do before the pointers matter
+

@@ -89,6 +89,8 @@ def test_ties_kept_whole_and_minus_inf_not_counted():
     assert kept(np.array([-np.inf, 5, 4, 3], np.float32), 1.0, 2, 1.0) == [1, 2]
     assert kept(np.array([-np.inf, 5, 4, 3], np.float32), 1.0, 3, 1.0) == [1, 2, 3]
     assert kept(np.full(6, 0.25, np.float32), 1.0, 0, 0.5) == list(range(6))
+    assert kept(np.full(4, -np.inf, np.float32), 1.0, 2, 0.5) == []
+    assert kept(np.full(4, -np.inf, np.float32), 0.0, 2, 0.5) == []
 
 
 def test_switches_off_leave_the_row_alone():

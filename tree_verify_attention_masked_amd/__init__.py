@@ -10,7 +10,8 @@ include/spectree.h):
 
 and spec_tree_reject_compact, the last two in one launch; spec_tree_kv_write
 writes the tree's K/V rows into the paged cache (rotated for their tree
-positions) before the attention.
+positions) before the attention; spec_tree_truncate applies top-k / top-p to
+the target logits before the sampler.
 
 This package is the thin PyTorch binding: tensors in, device pointers and the
 current HIP stream out to the library.
@@ -30,5 +31,6 @@ from .binding import (  # noqa: F401
     spec_tree_reject,
     spec_tree_reject_compact,
     spec_tree_kv_write,
+    spec_tree_truncate,
     spec_version,
 )

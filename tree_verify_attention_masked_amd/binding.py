@@ -45,6 +45,7 @@ _SIGNATURES = {
     "spec_kv_compact": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "spec_tree_kv_write": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                                 ctypes.c_float, _i, _vp]),
+    "spec_tree_truncate": (_i, [_vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_float, _vp, _vp]),
     "spec_tree_reject_compact": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_uint64,
                                       ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp, _sz,
                                       _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
@@ -304,3 +305,23 @@ def spec_status_string(code: int) -> str:
 
 def spec_version() -> int:
     return int(load_library().spec_version())
+
+
+def spec_tree_truncate(target_logits, temperature, top_k=0, top_p=1.0, out=None, status=None):
+    """Top-k / top-p truncation of [B, T, V] float32 target logits: dropped entries become -inf.  In place
+    when out is None (returns target_logits), else into out (a disjoint [B, T, V] float32 tensor)."""
+    lib = load_library()
+    _need(target_logits, "target_logits", torch.float32, 3)
+    B, T, V = target_logits.shape
+    if out is None:
+        out = target_logits
+    else:
+        _need(out, "out", torch.float32, 3)
+        if tuple(out.shape) != (B, T, V):
+            raise ValueError("out shape disagrees with target_logits")
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    rc = lib.spec_tree_truncate(_ptr(target_logits), _ptr(out), B, T, V, float(temperature), int(top_k),
+                                float(top_p), _ptr(status), _stream(target_logits.device))
+    _check(rc, "spec_tree_truncate")
+    return out

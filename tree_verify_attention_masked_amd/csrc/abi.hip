@@ -249,4 +249,27 @@ int spec_tree_kv_write(const void* k_new, const void* v_new, void* q, void* k_ca
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
+int spec_tree_truncate(const float* logits_in, float* logits_out, int B, int T, int V, float temperature,
+                       int top_k, float top_p, int32_t* status, void* stream) {
+  if (B < 0 || T < 1 || V < 1) return SPEC_ERR_INVALID_ARG;
+  if (V > (1 << 24)) return SPEC_ERR_UNSUPPORTED;
+  if (!(temperature >= 0.0f) || std::isinf(temperature)) return SPEC_ERR_INVALID_ARG;
+  if (!(top_p > 0.0f)) return SPEC_ERR_INVALID_ARG;  // also NaN
+  if (B == 0) return SPEC_OK;
+  if (!logits_in || !logits_out) return SPEC_ERR_INVALID_ARG;
+  if (static_cast<long long>(B) * T > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
+  TruncateLaunch L{};
+  L.in = logits_in;
+  L.out = logits_out;
+  L.status = status;
+  L.B = B;
+  L.T = T;
+  L.V = V;
+  L.temperature = temperature;
+  L.top_k = top_k;
+  L.top_p = top_p;
+  const hipError_t e = launch_truncate(L, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
 }  // extern "C"

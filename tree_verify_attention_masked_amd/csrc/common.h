@@ -125,4 +125,16 @@ struct KvWriteLaunch {
 
 hipError_t launch_kv_write(const KvWriteLaunch& a, hipStream_t stream);
 
+struct TruncateLaunch {
+  const float* in;
+  float* out;  // == in: in place
+  int32_t* status;
+  int B, T, V;
+  float temperature;
+  int top_k;
+  float top_p;
+};
+
+hipError_t launch_truncate(const TruncateLaunch& a, hipStream_t stream);
+
 }  // namespace spectree
