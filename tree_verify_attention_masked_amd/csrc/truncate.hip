@@ -125,12 +125,65 @@ struct Row {
   }
 };
 
+// For a candidate value v: the measure of the listed entries above v and equal
+// to v, and whether a listed entry lies below v.  The list is padded to a
+// multiple of 8 with (-inf, 0), which is never above, equal to or counted
+// below a finite v; eight entries are read at a time.
+constexpr int kPad = 8;
+__device__ __forceinline__ void rank_in_list(const Shared& sh, int ncp, float v, double& a, double& e,
+                                             bool& lower) {
+  a = 0.0;
+  e = 0.0;
+  lower = false;
+  for (int k = 0; k < ncp; k += kPad) {
+    float w[kPad];
+    double mm[kPad];
+#pragma unroll
+    for (int j = 0; j < kPad; ++j) {
+      w[j] = sh.cv[k + j];
+      mm[j] = sh.cm[k + j];
+    }
+#pragma unroll
+    for (int j = 0; j < kPad; ++j) {
+      a += w[j] > v ? mm[j] : 0.0;
+      e += w[j] == v ? mm[j] : 0.0;
+      lower |= w[j] < v && w[j] != -INFINITY;
+    }
+  }
+}
+
+// f(i, row[i]) for every i < V owned by this thread, kU loads in flight at a
+// time (a row's pass would otherwise wait out one memory latency per element).
+constexpr int kU = 16;
+template <typename R, typename F>
+__device__ __forceinline__ void for_row(const R& row, int V, int tid, F&& f) {
+  for (int base = 0; base < V; base += kThreads * kU) {
+    float v[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int i = base + j * kThreads + tid;
+      v[j] = i < V ? row[i] : -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int i = base + j * kThreads + tid;
+      if (i < V) f(i, v[j]);
+    }
+  }
+}
+
 // The largest value t in [lo, hi] with measure{lo <= l, l >= t} >= target,
 // given that the measure above hi (none, on entry) is below the target.
 // mass = false: the measure is the count; true: the mass weight(l, m, c).
+// keep_top: when the chosen bucket and everything above it fit the candidate
+// list (and nothing lies above the range), gather all of them, so that the
+// list then holds every element >= the returned threshold (*listed = count,
+// else 0).
 template <bool kLds>
 __device__ float select_threshold(const Row<kLds>& row, int V, bool mass, double target, float lo, float hi,
-                                  float m, double c, Shared& sh, int tid, int lane, int wave) {
+                                  float m, double c, Shared& sh, int tid, int lane, int wave, bool keep_top,
+                                  int* listed) {
+  *listed = 0;
   double above = 0.0;  // measure of the considered elements above the current range
   for (int round = 0; round < kMaxRounds; ++round) {
     if (!(lo < hi)) return lo;  // one value left: the target lies within its measure
@@ -143,14 +196,13 @@ __device__ float select_threshold(const Row<kLds>& row, int V, bool mass, double
       sh.found = 0;
     }
     __syncthreads();
-    for (int i = tid; i < V; i += kThreads) {
-      const float l = row[i];
+    for_row(row, V, tid, [&](int, float l) {
       if (l >= lo && l <= hi) {
         const int k = bucket(l, dhi, s);
         atomicAdd(&sh.cnt[k], 1u);
         if (mass) atomicAdd(&sh.meas[k], weight(l, m, c));
       }
-    }
+    });
     __syncthreads();
     // inclusive prefix sum over the buckets (value-descending order), one bucket per thread
     const unsigned cj = sh.cnt[tid];
@@ -179,54 +231,59 @@ __device__ float select_threshold(const Row<kLds>& row, int V, bool mass, double
     const unsigned n = sel >= 0 ? sh.cnt[sel] : 0u;
     __syncthreads();  // read by everyone before they change
     if (sel < 0) return lo;  // rounding left the target above the whole range: keep all of it
-    above = a_sel;
+    const bool whole = keep_top && above == 0.0 && a_sel + n <= static_cast<double>(kCand);
+    above = whole ? 0.0 : a_sel;
+    // value bounds of the chosen bucket, one bucket width wider on each side: a
+    // single compare drops nearly every element before the exact bucket test
+    float vlo = static_cast<float>(dhi - (sel + 2.0) / s);
+    if (static_cast<double>(vlo) > dhi - (sel + 2.0) / s) vlo = nextafterf(vlo, -INFINITY);
+    float vhi = static_cast<float>(dhi - (sel - 1.0) / s);
+    if (static_cast<double>(vhi) < dhi - (sel - 1.0) / s) vhi = nextafterf(vhi, INFINITY);
+    if (whole) vhi = INFINITY;
     if (n <= static_cast<unsigned>(kCand)) {
-      for (int i = tid; i < V; i += kThreads) {
-        const float l = row[i];
-        if (l >= lo && l <= hi && bucket(l, dhi, s) == sel) {
+      for_row(row, V, tid, [&](int, float l) {
+        if (l >= vlo && l <= vhi && l >= lo && l <= hi &&
+            (whole ? bucket(l, dhi, s) <= sel : bucket(l, dhi, s) == sel)) {
           const int k = atomicAdd(&sh.n, 1);
           if (k < kCand) {  // always: the same test counted at most kCand of them
             sh.cv[k] = l;
             sh.cm[k] = mass ? weight(l, m, c) : 1.0;
           }
         }
-      }
+      });
       __syncthreads();
       const int nc = min(sh.n, kCand);
+      const int ncp = (nc + kPad - 1) / kPad * kPad;
+      if (tid >= nc && tid < ncp) {
+        sh.cv[tid] = -INFINITY;
+        sh.cm[tid] = 0.0;
+      }
+      __syncthreads();
       if (tid < nc) {
         const float v = sh.cv[tid];
-        double a = 0.0, e = 0.0;
-        int below = 0;
-        for (int k = 0; k < nc; ++k) {
-          const float w = sh.cv[k];
-          if (w > v) {
-            a += sh.cm[k];
-          } else if (w == v) {
-            e += sh.cm[k];
-          } else {
-            ++below;
-          }
-        }
+        double a, e;
+        bool lower;
+        rank_in_list(sh, ncp, v, a, e, lower);
         if (above + a < target && above + a + e >= target) {
           sh.t = v;  // every candidate equal to v writes the same value
           sh.found = 1;
         }
-        if (below == 0) sh.tmin = v;
+        if (!lower) sh.tmin = v;
       }
       __syncthreads();
       const float res = sh.found ? sh.t : sh.tmin;  // not found: rounding again, keep the whole bucket
       __syncthreads();
+      if (whole) *listed = nc;
       return res;
     }
     // crowded bucket: its elements' range is the next range
     float nlo = INFINITY, nhi = -INFINITY;
-    for (int i = tid; i < V; i += kThreads) {
-      const float l = row[i];
-      if (l >= lo && l <= hi && bucket(l, dhi, s) == sel) {
+    for_row(row, V, tid, [&](int, float l) {
+      if (l >= vlo && l <= vhi && l >= lo && l <= hi && bucket(l, dhi, s) == sel) {
         nlo = fminf(nlo, l);
         nhi = fmaxf(nhi, l);
       }
-    }
+    });
     block_minmax(nlo, nhi, sh, lane, wave);
     lo = nlo;
     hi = nhi;
@@ -248,8 +305,7 @@ __global__ __launch_bounds__(kThreads) void truncate_kernel(const TrArgs a) {
   // pass 1: stage the row, its finite range, its finite count, NaN / +inf
   float mn = INFINITY, mx = -INFINITY;
   int nfin = 0, bad = 0;
-  for (int i = tid; i < V; i += kThreads) {
-    const float l = in[i];
+  for_row(in, V, tid, [&](int i, float l) {
     if constexpr (kLds) s_row[i] = l;
     bad |= (isnan(l) || l == INFINITY) ? 1 : 0;
     if (l != -INFINITY) {
@@ -257,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void truncate_kernel(const TrArgs a) {
       mx = fmaxf(mx, l);
       ++nfin;
     }
-  }
+  });
 #pragma unroll
   for (int o = 32; o; o >>= 1) {
     nfin += __shfl_xor(nfin, o);
@@ -280,39 +336,58 @@ __global__ __launch_bounds__(kThreads) void truncate_kernel(const TrArgs a) {
   if (bad) {
     if (tid == 0) report(a.status, static_cast<int>(r / a.T), SPEC_DEV_NONFINITE);
   } else if (nfin > 0) {
+    int listed = 0;  // > 0: the candidate list holds every element >= t
     if (a.top_k > 0 && a.top_k < nfin) {
       t = select_threshold<kLds>(row, V, false, static_cast<double>(a.top_k), mn, mx, mx, a.c, sh, tid, lane,
-                                 wave);
+                                 wave, a.top_p < 1.0f && a.tau > 0.0f, &listed);
     }
     if (a.top_p < 1.0f) {
       if (a.tau == 0.0f) {
         t = mx;
+      } else if (listed > 0) {
+        // top-p over the top-k set, all of it in the list: masses, their sum, and
+        // each candidate's mass above and equal to it
+        if (tid < listed) sh.cm[tid] = sh.cv[tid] >= t ? weight(sh.cv[tid], mx, a.c) : 0.0;
+        __syncthreads();
+        const double z = block_sum(tid < listed ? sh.cm[tid] : 0.0, sh, lane, wave);
+        const double target = static_cast<double>(a.top_p) * z;
+        if (tid == 0) sh.found = 0;
+        __syncthreads();
+        if (tid < listed && sh.cv[tid] >= t) {
+          const float v = sh.cv[tid];
+          double above, eq;
+          bool lower;
+          rank_in_list(sh, (listed + kPad - 1) / kPad * kPad, v, above, eq, lower);
+          if (above < target && above + eq >= target) {
+            sh.t = v;
+            sh.found = 1;
+          }
+        }
+        __syncthreads();
+        if (sh.found) t = sh.t;  // not found: rounding left top_p above the total, keep the top-k set
+        __syncthreads();
       } else {
         const float lo = t == -INFINITY ? mn : t;
         double z = 0.0;
-        for (int i = tid; i < V; i += kThreads) {
-          const float l = row[i];
+        for_row(row, V, tid, [&](int, float l) {
           if (l >= lo) z += weight(l, mx, a.c);
-        }
+        });
         z = block_sum(z, sh, lane, wave);
+        int unused;
         t = select_threshold<kLds>(row, V, true, static_cast<double>(a.top_p) * z, lo, mx, mx, a.c, sh, tid,
-                                   lane, wave);
+                                   lane, wave, false, &unused);
       }
     }
   }
   // write: dropped entries become -inf; out of place, the kept ones are copied
   if (a.in_place) {
     if (t != -INFINITY) {
-      for (int i = tid; i < V; i += kThreads) {
-        const float l = row[i];
+      for_row(row, V, tid, [&](int i, float l) {
         if (l < t && l != -INFINITY) out[i] = -INFINITY;
-      }
+      });
     }
   } else {
-    for (int i = tid; i < V; i += kThreads) {
-      const float l = row[i];
-      out[i] = l < t ? -INFINITY : l;
-    }
+    for_row(row, V, tid, [&](int i, float l) { out[i] = l < t ? -INFINITY : l; });
   }
 }
 
