@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T;
+  const int Lb = a.plen[b];  // loaded on entry, with the parent row
   if (tid == 0) s_err = 0;
   __syncthreads();
   if (tid < T) {
@@ -93,7 +94,6 @@ __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
     }
     __syncthreads();
   }
-  const int Lb = a.plen[b];
   int err = s_err;
   if (Lb < 0 || Lb > a.max_blocks * kBlockSize - T) err |= SPEC_DEV_LENGTH;
   if (err) {  // nothing is written for this sequence
@@ -117,14 +117,16 @@ __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
     long si[kUnroll], di[kUnroll];
     const void* src[kUnroll];
     void* dst[kUnroll];
-    bool live[kUnroll], rot[kUnroll];
-    int node[kUnroll];
+    bool live[kUnroll], rot[kUnroll], kvrow[kUnroll];
+    int node[kUnroll], blk[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int row = row0 + u;
       live[u] = false;
       rot[u] = false;
+      kvrow[u] = false;
       node[u] = 0;
+      blk[u] = 0;
       si[u] = di[u] = 0;
       src[u] = nullptr;
       dst[u] = nullptr;
@@ -141,30 +143,38 @@ __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
         const bool is_k = r < a.Hq + a.Hkv;
         const int g = r - a.Hq - (is_k ? 0 : a.Hkv);
         const int t = Lb + i;
-        const int blk = bt_b[t / kBlockSize];
-        if (blk < 0 || blk >= a.num_blocks) {
-          if (lane == 0) report(a.status, b, SPEC_DEV_BLOCK);
-          continue;
-        }
+        blk[u] = bt_b[t / kBlockSize];
         si[u] = ((static_cast<long>(b) * T + i) * a.Hkv + g) * a.D;
-        di[u] = ((static_cast<long>(blk) * a.Hkv + g) * kBlockSize + t % kBlockSize) * a.D;
+        di[u] = (static_cast<long>(g) * kBlockSize + t % kBlockSize) * a.D;  // + the block's offset once it is known
         src[u] = is_k ? a.k_new : a.v_new;
         dst[u] = is_k ? a.k_cache : a.v_cache;
         rot[u] = is_k && a.rotate != 0;
         live[u] = true;
+        kvrow[u] = true;
       }
     }
     if (lane < half) {
+      // unconditional loads, issued back to back (rows past the run read the
+      // first row again and store nothing; row0 < r_end, so that one is live)
       float x0[kUnroll], x1[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        x0[u] = live[u] ? ld_elt<kBf16>(src[u], si[u] + lane) : 0.f;
-        x1[u] = live[u] ? ld_elt<kBf16>(src[u], si[u] + lane + half) : 0.f;
+        const void* sp = live[u] ? src[u] : src[0];
+        const long sx = live[u] ? si[u] : si[0];
+        x0[u] = ld_elt<kBf16>(sp, sx + lane);
+        x1[u] = ld_elt<kBf16>(sp, sx + lane + half);
       }
       const double inv_freq = exp2(-(2.0 * lane / a.D) * a.log2_theta);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         if (!live[u]) continue;
+        if (kvrow[u]) {
+          if (blk[u] < 0 || blk[u] >= a.num_blocks) {
+            if (lane == 0) report(a.status, b, SPEC_DEV_BLOCK);
+            continue;
+          }
+          di[u] += static_cast<long>(blk[u]) * a.Hkv * kBlockSize * a.D;
+        }
         float y0 = x0[u], y1 = x1[u];
         if (rot[u]) {
           if (node[u] != trig_node) {
