@@ -56,7 +56,8 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 METRIC = "verified tree tokens/sec at 1 MI355X"
 
 
-KERNEL_KEYS = (("tree_attn", ("attn_",)), ("tree_reject_compact", ("reject",)), ("kv_compact", ("kv_compact",)))
+KERNEL_KEYS = (("tree_attn", ("attn_",)), ("tree_reject_compact", ("reject",)), ("kv_compact", ("kv_compact",)),
+               ("tree_kv_write", ("kv_write",)), ("tree_truncate", ("truncate_kernel",)))
 CALIB_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
 
 
