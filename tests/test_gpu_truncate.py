@@ -137,7 +137,8 @@ def test_nonfinite_row_reported_and_left_alone():
         assert np.array_equal(got[i, j], ref[n, 0])
 
 
-@pytest.mark.parametrize("cfg,k,p,wr", [(1, 40, 0.9, False), (4, 0, 0.8, False), (4, 50, 0.95, True)])
+@pytest.mark.parametrize("cfg,k,p,wr", [(1, 40, 0.9, False), (4, 0, 0.8, False), (4, 50, 0.95, True),
+                                        (2, 50, 0.9, False), (3, 0, 0.8, True), (3, 100, 0.95, True)])
 def test_verify_step_on_truncated_target(cfg, k, p, wr):
     w = make_config(cfg, with_kv=False)
     print(f"truncate+reject config {cfg} k={k} p={p} wr={wr}", flush=True)
