@@ -164,3 +164,17 @@ def test_verify_step_on_truncated_target(cfg, k, p, wr):
         ref["flag_path_len"][b] = 0
         ref["flag_kind"][b] = "accept"
     compare_reject(got, ref)
+
+
+def test_empty_batch_and_longest_row():
+    empty = torch.zeros((0, 3, 100), dtype=torch.float32, device="cuda")
+    assert stv.spec_tree_truncate(empty, 1.0, 5, 0.9).shape == (0, 3, 100)
+    V = 1 << 24  # the longest row the call takes, read from global memory in each pass
+    x = _rows("normal", 1, 1, V, seed=77)
+    print(f"truncate V={V}", flush=True)
+    xd = torch.from_numpy(x).cuda()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for k, p in ((1000, 0.9), (0, 0.5)):
+        got = stv.spec_tree_truncate(xd, 1.0, k, p, out=torch.empty_like(xd), status=status).cpu().numpy()
+        assert int(status.abs().sum()) == 0
+        assert check_rows(x, got, 1.0, k, p) <= 1
