@@ -113,6 +113,8 @@ __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
   const int r_end = min(nrows, r_begin + rpw);
   int trig_node = -1;  // node whose cosine and sine this lane holds
   double c = 1.0, sn = 0.0;
+  // (node, row within the node) of the next row, stepped along the run
+  int next_i = r_begin / per_node, next_r = r_begin - next_i * per_node;
   for (int row0 = r_begin; row0 < r_end; row0 += kUnroll) {
     long si[kUnroll], di[kUnroll];
     const void* src[kUnroll];
@@ -131,7 +133,11 @@ __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
       src[u] = nullptr;
       dst[u] = nullptr;
       if (row >= r_end) continue;
-      const int i = row / per_node, r = row % per_node;
+      const int i = next_i, r = next_r;
+      if (++next_r == per_node) {
+        next_r = 0;
+        ++next_i;
+      }
       node[u] = i;
       if (r < a.Hq) {  // a query head, rotated in place
         si[u] = di[u] = ((static_cast<long>(b) * T + i) * a.Hq + r) * a.D;
