@@ -122,3 +122,42 @@ def test_kv_write_bad_inputs_leave_the_sequence_unwritten():
             blk, off = int(w.block_table[b][t // 16]), t % 16
             assert np.array_equal(k_after[blk, :, off].view(np.uint8), k_before[blk, :, off].view(np.uint8))
             assert np.array_equal(v_after[blk, :, off].view(np.uint8), v_before[blk, :, off].view(np.uint8))
+
+
+def test_kv_write_bad_block_index_skips_only_that_page():
+    w = make_workload(name="bad_block", tag=722, V=8, B=2, Hq=4, Hkv=2, D=128, dtype="bf16", prefix=[10, 20],
+                      tree="random", T=12, max_depth=3)
+    print(f"[kv_write] bad block index B={w.B} T={w.T}", flush=True)
+    d = DevWorkload(w)
+    nb = d.k.shape[0]
+    table = w.block_table.copy()
+    assert table.shape[1] >= 2
+    table[0, 1] = nb  # slots 16.. of sequence 0 (tree nodes 6..11) point outside the cache
+    k_new = _rows(w, 11, (w.B, w.T, w.Hkv, w.D))
+    v_new = _rows(w, 12, (w.B, w.T, w.Hkv, w.D))
+    q = dev_kv(w, w.q)
+    k_before, v_before = host_kv(w, d.k).copy(), host_kv(w, d.v).copy()
+    stv.spec_tree_kv_write(dev_kv(w, k_new), dev_kv(w, v_new), q, d.k, d.v, torch.from_numpy(table).cuda(),
+                           d.prefix_lens, d.parent, 10000.0, status=d.status)
+    torch.cuda.synchronize()
+    bit = {name: b for b, name in stv.DEV_ERRORS.items()}
+    st = d.status.tolist()
+    assert st[0] == bit["block"] and st[1] == 0, st
+    q_ref, k_ref, v_ref = oracle.tree_kv_write(k_new, v_new, w.q, w.k_cache, w.v_cache, w.block_table,
+                                               w.prefix_lens, w.parent, 10000.0, dtype=w.dtype)
+    k_got, v_got = host_kv(w, d.k), host_kv(w, d.v)
+    written = np.zeros((nb, 16), dtype=bool)
+    for b in range(w.B):
+        for i in range(w.T):
+            t = int(w.prefix_lens[b]) + i
+            if b == 0 and t >= 16:
+                continue  # the skipped page
+            blk, off = int(w.block_table[b][t // 16]), t % 16
+            written[blk, off] = True
+            assert np.array_equal(v_got[blk, :, off], v_new[b, i]), f"V row of node {i}, sequence {b}"
+            _close(_widen(w, k_got[blk, :, off]), k_ref[blk, :, off], w.dtype, f"K row of node {i}, sequence {b}")
+    for name, got, before in (("K", k_got, k_before), ("V", v_got, v_before)):
+        g = got.transpose(0, 2, 1, 3)[~written]
+        o = before.transpose(0, 2, 1, 3)[~written]
+        assert np.array_equal(g.view(np.uint8), o.view(np.uint8)), f"{name}: a slot outside the written rows changed"
+    _close(_widen(w, host_kv(w, q)), q_ref, w.dtype, "queries")  # the queries are rotated all the same
