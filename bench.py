@@ -265,7 +265,9 @@ def sweep():
     and of the EAGLE-style one (B8, 32 q / 8 kv heads, V 128256, tau 0.7, random
     trees of depth <= 6), T from 1 to 256 (128 for the wider one), timed per call
     as in the main run (graphs of back-to-back calls over input copies that
-    together exceed the 256 MB MALL where memory allows)."""
+    together exceed the 256 MB MALL where memory allows).  Each point times the
+    attention and the sampler with compaction (the step), and the tree K/V write
+    that precedes them (reported on its own)."""
     import torch
 
     import tree_verify_attention_masked_amd as stv
@@ -308,8 +310,14 @@ def sweep():
                                                  bt, lens, w.without_replacement, w.seed, 0, status=status,
                                                  workspace=rej_ws)
 
+                kv_new = torch.zeros((w.B, w.T, w.Hkv, w.D), dtype=cps[0]["k"].dtype, device=dev)
+
+                def kvw(c):
+                    stv.spec_tree_kv_write(kv_new, kv_new, c["q"], c["k"], c["v"], bt, lens, parent, 10000.0,
+                                           status=status)
+
                 us = {}
-                for key, fn in (("attn_us", attn), ("reject_compact_us", rejc)):
+                for key, fn in (("attn_us", attn), ("reject_compact_us", rejc), ("kv_write_us", kvw)):
                     for c in cps:  # eager pass: validates every copy
                         fn(c)
                     torch.cuda.synchronize()
@@ -321,6 +329,7 @@ def sweep():
                 print(json.dumps({"shape": name, "T": w.T, "prefix": L, "B": w.B, "depth": int(w.info["depth"]),
                                   "attn_us": round(us["attn_us"], 2),
                                   "reject_compact_us": round(us["reject_compact_us"], 2),
+                                  "kv_write_us": round(us["kv_write_us"], 2),
                                   "step_us": round(step, 2), "verified_tokens_per_s": round(w.B * w.T / step * 1e6, 1),
                                   "attn_GBps": round(a_bytes / us["attn_us"] / 1e3, 1),
                                   "attn_TFLOPs": round(a_flops / us["attn_us"] / 1e6, 2), "input_copies": R}),
