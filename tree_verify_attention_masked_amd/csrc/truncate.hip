@@ -76,6 +76,7 @@ struct Shared {
   int sel, n, found;
   double a_sel;
   float t, tmin;
+  float tmax[kThreads];  // per-thread maxima of the row
 };
 
 // Sums in a fixed order, so every thread gets the same value on every run.
@@ -179,8 +180,8 @@ __device__ __forceinline__ void for_row(const R& row, int V, int tid, F&& f) {
 // list (and nothing lies above the range), gather all of them, so that the
 // list then holds every element >= the returned threshold (*listed = count,
 // else 0).
-template <bool kLds>
-__device__ float select_threshold(const Row<kLds>& row, int V, bool mass, double target, float lo, float hi,
+template <typename R>
+__device__ float select_threshold(const R row, int V, bool mass, double target, float lo, float hi,
                                   float m, double c, Shared& sh, int tid, int lane, int wave, bool keep_top,
                                   int* listed) {
   *listed = 0;
@@ -323,6 +324,7 @@ __global__ __launch_bounds__(kThreads) void truncate_kernel(const TrArgs a) {
     sh.red_i[0][wave] = nfin;
     sh.red_i[1][wave] = bad;
   }
+  const float my_max = mx;               // this thread's largest finite logit (-inf if none)
   block_minmax(mn, mx, sh, lane, wave);  // its barriers also publish red_i
   nfin = 0;
   bad = 0;
@@ -338,8 +340,55 @@ __global__ __launch_bounds__(kThreads) void truncate_kernel(const TrArgs a) {
   } else if (nfin > 0) {
     int listed = 0;  // > 0: the candidate list holds every element >= t
     if (a.top_k > 0 && a.top_k < nfin) {
-      t = select_threshold<kLds>(row, V, false, static_cast<double>(a.top_k), mn, mx, mx, a.c, sh, tid, lane,
-                                 wave, a.top_p < 1.0f && a.tau > 0.0f, &listed);
+      bool done = false;
+      if (a.top_k <= kThreads) {
+        // The k-th largest of the per-thread maxima bounds the k-th largest logit from below
+        // (those k maxima are k elements of the row).  When every logit at or above the
+        // bound fits the candidate list, the threshold is read off the list, which then
+        // holds the whole top; otherwise the search below runs over the row.
+        sh.tmax[tid] = my_max;
+        __syncthreads();
+        int unused;
+        const float bound = select_threshold(Row<true>{nullptr, sh.tmax}, kThreads, false,
+                                             static_cast<double>(a.top_k), mn, mx, mx, a.c, sh, tid, lane, wave,
+                                             false, &unused);
+        if (tid == 0) sh.n = 0;
+        __syncthreads();
+        for_row(row, V, tid, [&](int, float l) {
+          if (l >= bound) {
+            const int k = atomicAdd(&sh.n, 1);
+            if (k < kCand) sh.cv[k] = l;
+          }
+        });
+        __syncthreads();
+        const int n = sh.n;
+        if (n <= kCand) {
+          const int ncp = (n + kPad - 1) / kPad * kPad;
+          if (tid < ncp) sh.cm[tid] = tid < n ? 1.0 : 0.0;
+          if (tid >= n && tid < ncp) sh.cv[tid] = -INFINITY;
+          if (tid == 0) sh.found = 0;
+          __syncthreads();
+          if (tid < n) {
+            double above, eq;
+            bool lower;
+            rank_in_list(sh, ncp, sh.cv[tid], above, eq, lower);
+            const double k = static_cast<double>(a.top_k);
+            if (above < k && above + eq >= k) {
+              sh.t = sh.cv[tid];
+              sh.found = 1;
+            }
+          }
+          __syncthreads();
+          t = sh.found ? sh.t : bound;  // always found: the list holds every logit >= the k-th largest
+          listed = (a.top_p < 1.0f && a.tau > 0.0f) ? n : 0;
+          __syncthreads();
+          done = true;
+        }
+      }
+      if (!done) {
+        t = select_threshold(row, V, false, static_cast<double>(a.top_k), mn, mx, mx, a.c, sh, tid, lane, wave,
+                             a.top_p < 1.0f && a.tau > 0.0f, &listed);
+      }
     }
     if (a.top_p < 1.0f) {
       if (a.tau == 0.0f) {
@@ -374,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void truncate_kernel(const TrArgs a) {
         });
         z = block_sum(z, sh, lane, wave);
         int unused;
-        t = select_threshold<kLds>(row, V, true, static_cast<double>(a.top_p) * z, lo, mx, mx, a.c, sh, tid,
+        t = select_threshold(row, V, true, static_cast<double>(a.top_p) * z, lo, mx, mx, a.c, sh, tid,
                                    lane, wave, false, &unused);
       }
     }
