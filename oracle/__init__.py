@@ -36,6 +36,11 @@ from .attention import tree_attention, tree_attention_rows  # noqa: F401
 from .reject import (  # noqa: F401
     PhiloxDraws,
     accept_draw,
+    accept_margin,
+    final_margin,
+    accept_flag_probability,
+    final_flag_probability,
+    final_draw_candidates,
     inverse_cdf,
     residual_update,
     without_replacement_update,

@@ -77,10 +77,41 @@ def inverse_cdf(weights: np.ndarray, u: float) -> int:
     return x
 
 
-def _final_margin(weights, u, x):
+def accept_margin(r, p_x, q_x):
+    """Distance of the uniform r from the accept threshold p(x)/q(x) of the
+    test r * q(x) < p(x); infinite when q(x) = 0 (the decision then does not
+    depend on r)."""
+    if q_x <= 0:
+        return math.inf
+    return abs(float(r) - float(p_x) / float(q_x))
+
+
+def final_margin(weights, u, x):
+    """Distance of the uniform u from the nearer edge of the chosen token's
+    interval [C[x-1], C[x]) / C[V-1] of the normalised CDF (C[-1] = 0)."""
     c = np.cumsum(np.asarray(weights, dtype=np.float64))
     lo = c[x - 1] / c[-1] if x > 0 else 0.0
     return min(u - lo, c[x] / c[-1] - u)
+
+
+def accept_flag_probability(p_x, q_x, margin=None):
+    """Probability over a uniform r in [0, 1) that accept_margin(r, p_x, q_x) < margin:
+    the length of (ratio - margin, ratio + margin) inside [0, 1)."""
+    margin = FLAG_MARGIN if margin is None else margin
+    if q_x <= 0:
+        return 0.0
+    ratio = float(p_x) / float(q_x)
+    return max(0.0, min(1.0, ratio + margin) - max(0.0, ratio - margin))
+
+
+def final_flag_probability(weights, margin=None):
+    """Probability over a uniform u in [0, 1) that the final draw from `weights`
+    is flagged: u falls within `margin` of an edge of the interval of the token
+    it selects.  Token x's interval has length w(x)/W; the part of it within
+    `margin` of either edge has length min(w(x)/W, 2 margin)."""
+    margin = FLAG_MARGIN if margin is None else margin
+    w = np.asarray(weights, dtype=np.float64)
+    return float(np.minimum(w / w.sum(), 2.0 * margin).sum())
 
 
 def final_draw_candidates(weights, u, margin=None):
@@ -100,21 +131,21 @@ class PhiloxDraws:
     def __init__(self, seed: int, offset: int):
         self.seed = int(seed)
         self.offset = int(offset)
-        self.records = []  # (kind, b, node, margin, path_len)
+        self.records = []  # (kind, b, node, margin, path_len, flag probability of the draw)
         self.path_len = 0
         self.final_candidates = None  # set when the final draw is flagged
 
     def accept(self, b, node, p_x, q_x) -> bool:
         r = uniform_draw(self.seed, self.offset, b, node, PURPOSE_ACCEPT)
-        ratio = p_x / q_x if q_x > 0 else math.inf
-        self.records.append(("accept", b, node, abs(r - ratio), self.path_len))
+        self.records.append(("accept", b, node, accept_margin(r, p_x, q_x), self.path_len,
+                             accept_flag_probability(p_x, q_x)))
         return bool(accept_draw(r, p_x, q_x))
 
     def sample(self, b, node, weights) -> int:
         u = uniform_draw(self.seed, self.offset, b, node, PURPOSE_FINAL)
         x = inverse_cdf(weights, u)
-        m = _final_margin(weights, u, x)
-        self.records.append(("final", b, node, m, self.path_len))
+        m = final_margin(weights, u, x)
+        self.records.append(("final", b, node, m, self.path_len, final_flag_probability(weights)))
         if m < FLAG_MARGIN:
             self.final_candidates = final_draw_candidates(weights, u)
         return x
@@ -171,7 +202,11 @@ def tree_reject(target_logits, draft_probs, draft_tokens, parent, temperature,
     FLAG_MARGIN of its threshold, else the path length when the first such
     draw was taken (outputs beyond that point are not decided robustly);
     `flag_kind` [B]: "" / "accept" / "final" for that first flagged draw, and
-    `final_candidates`: {b: tokens a flagged final draw may return}."""
+    `final_candidates`: {b: tokens a flagged final draw may return};
+    `flag_prob` [B]: the probability, over the uniforms of the draws the walk
+    took, that at least one of them is flagged (1 - prod(1 - p_draw)); the
+    number of flagged sequences in a batch is a sum of independent Bernoulli
+    variables with these means."""
     B, T, V = target_logits.shape
     tau = float(np.float32(temperature))
     acc = np.full((B, T), -1, dtype=np.int32)
@@ -181,6 +216,7 @@ def tree_reject(target_logits, draft_probs, draft_tokens, parent, temperature,
     kind_of = [""] * B
     cands = {}
     margins = []
+    fprob = np.zeros(B, dtype=np.float64)
     for b in range(B):
         draws = PhiloxDraws(seed, offset)
         path, emitted = reject_sequence(target_logits[b], draft_probs[b], draft_tokens[b],
@@ -190,13 +226,16 @@ def tree_reject(target_logits, draft_probs, draft_tokens, parent, temperature,
         out[b, :L] = [int(draft_tokens[b][n]) for n in path[1:]]
         out[b, L] = emitted
         nacc[b] = L
-        for kind, _, node, m, plen in draws.records:
+        keep = 1.0
+        for kind, _, node, m, plen, pf in draws.records:
             margins.append(m)
+            keep *= 1.0 - pf
             if m < FLAG_MARGIN and flag[b] < 0:
                 flag[b] = plen
                 kind_of[b] = kind
+        fprob[b] = 1.0 - keep
         if kind_of[b] == "final":
             cands[b] = draws.final_candidates
     return {"accepted_nodes": acc, "out_tokens": out, "num_accepted": nacc,
             "flag_path_len": flag, "flag_kind": kind_of, "final_candidates": cands,
-            "margins": np.array(margins)}
+            "margins": np.array(margins), "flag_prob": fprob}

@@ -158,6 +158,21 @@ def compare_reject(got, ref, stats=None):
     return flagged
 
 
+def flag_cap(probs, alpha=1e-6) -> int:
+    """Upper bound on the number of flagged sequences: the smallest k with
+    P(X > k) <= alpha for X a sum of independent Bernoulli variables with the
+    given means (the oracle's per-sequence flag probabilities, `flag_prob`),
+    from the exact Poisson-binomial distribution (convolution of the terms)."""
+    dist = np.array([1.0])
+    for p in np.asarray(probs, dtype=np.float64).ravel():
+        nxt = np.zeros(dist.size + 1)
+        nxt[:-1] += dist * (1.0 - p)
+        nxt[1:] += dist * p
+        dist = nxt
+    tail = 1.0 - np.cumsum(dist)  # tail[k] = P(X > k)
+    return int(np.argmax(tail <= alpha))
+
+
 def oracle_reject(w, temperature=None, without_replacement=None, seed=None, offset=None):
     return oracle.tree_reject(w.target_logits, w.draft_probs, w.draft_tokens, w.parent,
                               w.temperature if temperature is None else temperature,

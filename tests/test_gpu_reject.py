@@ -9,21 +9,31 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import DevWorkload, compare_reject, oracle_reject
+from helpers import DevWorkload, compare_reject, flag_cap, oracle_reject
 from workloads import make_config, make_workload
 
 pytestmark = pytest.mark.gpu
 
 
 def _many_offsets(w, offsets, temperature=None, wr=None):
+    """GPU against oracle on every offset.  The number of sequences the oracle
+    flags (a draw within 1e-6 of its threshold: those are compared only up to
+    that draw) must stay below the 1e-6 upper quantile of its own distribution,
+    a sum of Bernoulli variables with the oracle's per-sequence flag
+    probabilities, so a flagging mistake that excuses more cannot pass."""
     d = DevWorkload(w)
     flagged = 0
+    probs = []
     for off in offsets:
         got = d.reject(temperature=temperature, without_replacement=wr, offset=off)
         torch.cuda.synchronize()
         ref = oracle_reject(w, temperature=temperature, without_replacement=wr, offset=off)
         flagged += compare_reject(got, ref)
+        probs.extend(ref["flag_prob"].tolist())
     assert int(d.status.abs().sum()) == 0
+    cap = flag_cap(probs)
+    print(f"[reject] flagged {flagged} of {len(probs)} (expected {sum(probs):.3f}, cap {cap})", flush=True)
+    assert flagged <= cap
     return flagged
 
 
@@ -39,7 +49,7 @@ def test_tiny_vocab_many_draws(V, wr):
                       parent=TINY_TREE, draft_mode="without_replacement" if wr else "iid",
                       temperature=0.8, without_replacement=wr, with_kv=True)
     print(f"[reject] tiny V={V} wr={wr}", flush=True)
-    assert _many_offsets(w, range(60)) <= 3
+    _many_offsets(w, range(60))
 
 
 def test_greedy_tiny():
@@ -48,28 +58,28 @@ def test_greedy_tiny():
     _many_offsets(w, [0])
 
 
-# Large vocabularies: a final draw is flagged whenever the chosen token's CDF
-# interval is narrower than ~2e-6 (common at V >= 32000); flagged sequences are
-# still checked (see compare_reject).  The bounds below only catch a flood.
+# Large vocabularies: a final draw is flagged with probability sum_x min(p(x), 2e-6)
+# (about 5 % at V = 32000 with logits ~ N(0, 2^2)); flagged sequences are still
+# checked up to the flagged draw (see compare_reject), and their count is capped
+# by the oracle's own flag probabilities (see _many_offsets).
 @pytest.mark.parametrize("cfg", [0, 1, 3])
 def test_config_parity(cfg):
     w = make_config(cfg)
     print(f"[reject] config {cfg} {w.name}", flush=True)
-    flagged = _many_offsets(w, range(12))
-    assert flagged <= 12 * w.B // 2
+    _many_offsets(w, range(12))
 
 
 def test_config2_greedy_and_sampled():
     w = make_config(2)
     print("[reject] config 2 greedy + 0.7", flush=True)
     assert _many_offsets(w, [0], temperature=0.0) == 0
-    assert _many_offsets(w, range(3)) <= 3 * w.B // 2
+    _many_offsets(w, range(3))
 
 
 def test_config4_parity():
     w = make_config(4, with_kv=False)
     print("[reject] config 4", flush=True)
-    assert _many_offsets(w, range(2)) <= 2 * w.B // 2
+    _many_offsets(w, range(2))
 
 
 def test_worked_example_on_gpu():
