@@ -3,19 +3,24 @@
 A step = spec_tree_attn -> spec_tree_reject_compact (tree rejection sampling,
 then compaction of the KV cache along the accepted path, in one launch; the
 same outputs as spec_tree_reject followed by spec_kv_compact) over one batch
-of the synthetic workload (default: the chain configuration, a Llama-2-13B-
-shaped layer: 40 MHA heads, head dim 128, bf16 paged KV, prefix 2048, chain
-of 4 drafts + root, vocabulary 32000, temperature 1).  Metric: verified tree
-tokens per second = B * T / step time.
+of the synthetic workload.  Default workload: batched serving, the largest
+configuration that fits one GPU (64 sequences, 32 query / 8 kv heads, head dim
+128, bf16 paged KV with a shuffled block table, prefixes uniform in
+[512, 16384], a random 16-node tree of depth <= 5 per sequence, vocabulary
+32000, temperature 1).  Metric: verified tree tokens per second = B * T / step
+time.  The chain workload (a Llama-2-13B-shaped layer, chain of 4 drafts) is
+measured as well and reported under `extra`.
 
 Inputs are resident in HBM before timing starts.  Several copies of every
-input are cycled so that consecutive steps never find their data in the
-256 MB MALL / L2 (each copy is re-read only after the others have streamed
-through).  Steps are replayed from HIP graphs (one graph holds several
-consecutive steps, each on the next copy), so the timed region holds only GPU
-work and one host launch per several steps; the K timed steps are bracketed by
-torch.cuda.synchronize().  Per-kernel average durations come from HIP events
-around graphs that repeat one call many times on the same stream.
+input are cycled where they fit, so that consecutive steps do not find their
+data in the 256 MB MALL / L2.  Steps are replayed from HIP graphs: one graph
+holds G consecutive step slots, slot j on input copy j % R with its own Philox
+offset (offset + j), so consecutive steps take different walks; the timed
+region holds only GPU work and one host launch per G steps; the K timed steps
+are bracketed by torch.cuda.synchronize().  Per-kernel average durations come
+from HIP events around graphs that repeat one call many times on the current
+stream (the stream the kernels run on).  `step_us` gives the spread (p10, p50,
+p90) of 100 single-step replays, each bracketed by events.
 
 The line's `kernels` also times spec_tree_kv_write (the step before attention:
 the tree's K/V rows into the cache, rotated for their tree positions) and
@@ -25,12 +30,14 @@ whose target is not truncated.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
-`roofline.traffic` comes from the committed rocprofv3 counter summary
-(profiles/pmc_<workload>.md, FETCH_SIZE and WRITE_SIZE per dispatch, scaled by
-what the same counters read for a plain 256 MiB copy); it is null when that
-summary was taken from other kernel sources than the ones built now.
-`--summarize trace|pmc DIR...` turns rocprofv3 CSV output into those summaries
-(host only, no GPU).
+`roofline` covers the dominant (longest) kernel of the step; `step_roofline`
+the whole step (algorithmic bytes of attention, walked logit rows and moved KV
+rows over the step time).  `roofline.traffic` comes from the committed
+rocprofv3 counter summary (profiles/pmc_<workload>.md, FETCH_SIZE and
+WRITE_SIZE per dispatch, scaled by what the same counters read for a plain
+1 GiB device copy); it is null when that summary was taken from other kernel
+sources than the ones built now.  `--summarize trace|pmc DIR...` turns
+rocprofv3 CSV output into those summaries (host only, no GPU).
 """
 from __future__ import annotations
 
@@ -59,6 +66,7 @@ METRIC = "verified tree tokens/sec at 1 MI355X"
 KERNEL_KEYS = (("tree_attn", ("attn_",)), ("tree_reject_compact", ("reject",)), ("kv_compact", ("kv_compact",)),
                ("tree_kv_write", ("kv_write",)), ("tree_truncate", ("truncate_kernel",)))
 CALIB_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
+CALIB_BYTES_BIG = 1 << 30  # a second calibration copy, four times the 256 MB MALL
 
 
 def log(*a):
@@ -107,22 +115,27 @@ def summarize(kind, dirs, workload):
         return "\n".join(out)
     # pmc: dirs = [fetch_dir, write_dir]
     per = {}
-    calib = {}
+    calib = {}  # counter -> [(dispatch id, KiB)] of the calibration copies, in dispatch order
     for d, counter in zip(dirs, ("FETCH_SIZE", "WRITE_SIZE")):
         disp = {}
         for r in read_csvs(d, "counter_collection.csv"):
             if r.get("Counter_Name") != counter:
                 continue
-            key = (r.get("Dispatch_Id"), r.get("Kernel_Name", ""))
+            key = (int(r.get("Dispatch_Id", 0)), r.get("Kernel_Name", ""))
             disp[key] = disp.get(key, 0.0) + float(r.get("Counter_Value", 0))
-        for (_, name), kib in disp.items():
+        for (did, name), kib in sorted(disp.items()):
             k = kernel_key(name)
             if k:
                 per.setdefault(k, {}).setdefault(counter, []).append(kib)
-            elif "copy" in name.lower() and kib > 0.5 * CALIB_BYTES / 1024:
+            elif "copy" in name.lower() and kib > 0.1 * CALIB_BYTES / 1024:
                 calib.setdefault(counter, []).append(kib)
-    factors = {c: (float(np.median(v)) * 1024 / CALIB_BYTES if v else None) for c, v in calib.items()}
-    res = {"workload": workload, "source_sha256": kernel_source_hash(), "calibration": factors, "kernels": {}}
+    # the first copy moves 256 MiB (the size of the MALL), the second 1 GiB; the
+    # larger one scales the counters (its data cannot sit in the MALL)
+    sizes = (CALIB_BYTES, CALIB_BYTES_BIG)
+    by_size = {c: {f"{n >> 20}MiB": round(kib * 1024 / n, 4) for kib, n in zip(v, sizes)} for c, v in calib.items()}
+    factors = {c: (v[-1] * 1024 / sizes[len(v) - 1] if v else None) for c, v in calib.items()}
+    res = {"workload": workload, "source_sha256": kernel_source_hash(), "calibration": factors,
+           "calibration_by_copy_size": by_size, "kernels": {}}
     out.append("| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/launch (scaled) |")
     out.append("|---|---|---|---|---|")
     for k, cs in sorted(per.items()):
@@ -133,8 +146,9 @@ def summarize(kind, dirs, workload):
         res["kernels"][k] = {"fetch_kib": round(f, 1), "write_kib": round(wv, 1), "traffic_bytes": int(traffic)}
         out.append(f"| {k} | {len(cs.get('FETCH_SIZE', []))} | {f:.1f} | {wv:.1f} | {traffic / 1e6:.3f} MB |")
     out.append("")
-    out.append(f"Calibration (256 MiB device copy): FETCH_SIZE reads {factors.get('FETCH_SIZE')} x, "
-               f"WRITE_SIZE {factors.get('WRITE_SIZE')} x the bytes copied.")
+    out.append(f"Calibration (plain device copies; counter KiB x 1024 / bytes copied): {json.dumps(by_size)}; "
+               f"scaled by the largest copy: FETCH_SIZE {factors.get('FETCH_SIZE')}, "
+               f"WRITE_SIZE {factors.get('WRITE_SIZE')}.")
     out.append("")
     out.append("```json")
     out.append(json.dumps(res))
@@ -187,34 +201,40 @@ def compact_bytes(w, acc, nacc):
     return moved * w.Hkv * w.D * elt * 2 * 2  # K and V, read + write
 
 
-def cpu_baseline(cfg, budget_s):
-    """The oracle (as it stands) on the same workload, timed on the host cores."""
+def cpu_baseline(w, budget_s, max_seqs=8):
+    """The oracle (as it stands) on the same workload, timed on the host cores.
+
+    A batch of more than `max_seqs` sequences is sampled: the first `max_seqs`
+    of them, with their own pages (the oracle's compaction copies the whole
+    cache it is given).  The value is verified tree tokens per second of the
+    oracle's attention + walk + compaction over the sample, repeated until
+    `budget_s` seconds have passed."""
     import oracle
-    from workloads import make_config
+    from workloads import sub_batch
 
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    w = make_config(cfg)
+    sample = w if w.B <= max_seqs else sub_batch(w, range(max_seqs))
     steps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.tree_attention(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_lens, w.parent, w.scale,
-                              dtype=w.dtype)
-        r = oracle.tree_reject(w.target_logits, w.draft_probs, w.draft_tokens, w.parent, w.temperature,
-                               w.without_replacement, w.seed, steps)
-        oracle.kv_compact(w.k_cache, w.v_cache, w.block_table, w.prefix_lens, r["accepted_nodes"],
-                          r["num_accepted"])
+        oracle.tree_attention(sample.q, sample.k_cache, sample.v_cache, sample.block_table, sample.prefix_lens,
+                              sample.parent, sample.scale, dtype=sample.dtype)
+        r = oracle.tree_reject(sample.target_logits, sample.draft_probs, sample.draft_tokens, sample.parent,
+                               sample.temperature, sample.without_replacement, sample.seed, steps)
+        oracle.kv_compact(sample.k_cache, sample.v_cache, sample.block_table, sample.prefix_lens,
+                          r["accepted_nodes"], r["num_accepted"])
         steps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or steps >= 200:
             break
-    return {"value": w.B * w.T * steps / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{steps} full steps of the same workload (fp64 NumPy attention + walk + compaction), "
-                      f"{el:.1f} s, {len(os.sched_getaffinity(0))} host cores visible"}
-
+    what = (f"sequences 0-{sample.B - 1} of the {w.B}-sequence batch" if sample is not w else "the whole batch")
+    return {"value": sample.B * sample.T * steps / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} steps over {what} (fp64 NumPy attention + walk + compaction), {el:.1f} s, "
+                      f"{len(os.sched_getaffinity(0))} host cores visible"}
 
 
 def capture_graph(fn_list):
@@ -337,20 +357,198 @@ def sweep():
                 del cps, attn_ws, rej_ws
                 torch.cuda.empty_cache()
 
+def measure(cfg, args, quick=False):
+    """One workload: the timed step line and its per-kernel figures (see the module docstring)."""
+    import torch
+
+    import tree_verify_attention_masked_amd as stv
+    from workloads import make_config
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] building workload {cfg}")
+    w = make_config(cfg)
+
+    def up(a, kv=False):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if kv and w.dtype == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to(dev)
+
+    per_copy = (w.k_cache.nbytes * 2 + w.q.nbytes + w.target_logits.nbytes + w.draft_probs.nbytes)
+    R = args.copies or max(1, min(16, math.ceil(768e6 / per_copy)))
+    log(f"[bench] {R} input copies of {per_copy / 1e6:.1f} MB")
+    shared = dict(bt=up(w.block_table), lens=up(w.prefix_lens), parent=up(w.parent), tok=up(w.draft_tokens))
+    copies = []
+    for _ in range(R):
+        c = dict(q=up(w.q, True), k=up(w.k_cache, True), v=up(w.v_cache, True), logits=up(w.target_logits),
+                 probs=up(w.draft_probs))
+        c["out"] = torch.empty_like(c["q"])
+        c["status"] = torch.zeros((w.B,), dtype=torch.int32, device=dev)
+        copies.append(c)
+    code = stv.SPEC_BF16 if w.dtype == "bf16" else stv.SPEC_F32
+    ws_attn = stv.spec_tree_attn_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, w.max_blocks, code)
+    attn_ws = torch.zeros(max(ws_attn, 1), dtype=torch.uint8, device=dev)  # zero once: split arrival counters
+    rej_ws = torch.zeros(int(stv.load_library().spec_tree_reject_workspace_size(w.B, w.T, w.V)),
+                         dtype=torch.uint8, device=dev)  # zero once: the sampler's epochs and tagged exchange slots
+
+    # Step slots: one graph holds G consecutive steps; slot j runs on input copy
+    # j % R with Philox offset (offset + j), so consecutive steps take different
+    # walks, and keeps its own outputs.
+    G = R * max(1, math.ceil(8 / R))
+    slots = []
+    for j in range(G):
+        slots.append(dict(c=copies[j % R], offset=args.offset + j,
+                          acc=torch.empty((w.B, w.T), dtype=torch.int32, device=dev),
+                          toks=torch.empty((w.B, w.T), dtype=torch.int32, device=dev),
+                          nacc=torch.empty((w.B,), dtype=torch.int32, device=dev),
+                          new_lens=torch.empty((w.B,), dtype=torch.int32, device=dev)))
+
+    def attn(c):
+        stv.spec_tree_attn(c["q"], c["k"], c["v"], shared["bt"], shared["lens"], shared["parent"], scale=w.scale,
+                           out=c["out"], status=c["status"], workspace=attn_ws if ws_attn else None)
+
+    def reject_compact(c, sl=None):
+        sl = sl or slots[0]
+        stv.spec_tree_reject_compact(c["logits"], c["probs"], shared["tok"], shared["parent"], w.temperature,
+                                     c["k"], c["v"], shared["bt"], shared["lens"], w.without_replacement, w.seed,
+                                     sl["offset"], accepted_nodes=sl["acc"], out_tokens=sl["toks"],
+                                     num_accepted=sl["nacc"], new_lens=sl["new_lens"], status=c["status"],
+                                     workspace=rej_ws)
+
+    def step(sl):
+        attn(sl["c"])
+        reject_compact(sl["c"], sl)
+
+    if args.calib_copy and not quick:  # plain copies of known size, for scaling the HBM counters
+        for nbytes in (CALIB_BYTES, CALIB_BYTES_BIG):
+            src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+
+    for sl in slots:  # eager pass: validates every copy and slot
+        step(sl)
+    torch.cuda.synchronize()
+    st = sum(int(c["status"].abs().sum()) for c in copies)
+    if st:
+        raise SystemExit(f"device reported input errors: {[c['status'].tolist() for c in copies]}")
+
+    step_graphs = [capture_graph([lambda sl=sl: step(sl)]) for sl in slots]
+    run_graph = capture_graph([lambda sl=sl: step(sl) for sl in slots])
+    log(f"[bench] captured {len(step_graphs)} step graphs and one graph of {G} steps; warmup {args.warmup}")
+    for i in range(args.warmup):
+        step_graphs[i % G].replay()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K // G):
+        run_graph.replay()
+    for i in range(K % G):
+        step_graphs[i % G].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"[bench] {K} steps ({K // G} replays of {G} steps + {K % G} single steps): wall {wall * 1e3:.3f} ms")
+    ms_per_step = wall * 1e3 / K
+    value = w.B * w.T * K / wall
+
+    # spread: 100 single-step replays, each bracketed by events on the current stream
+    n_spread = 30 if quick else 100
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread + 1)]
+    evs[0].record()
+    for i in range(n_spread):
+        step_graphs[i % G].replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n_spread)])
+    spread = {"p10": round(float(np.percentile(per, 10)), 2), "p50": round(float(np.percentile(per, 50)), 2),
+              "p90": round(float(np.percentile(per, 90)), 2), "n": n_spread,
+              "note": "single-step graph replays, launch gap included"}
+
+    # accepted tokens per step over every slot's walk (each slot has its own offset)
+    accs = [sl["acc"].cpu().numpy() for sl in slots]
+    naccs = [sl["nacc"].cpu().numpy() for sl in slots]
+    lp1 = np.concatenate([n + 1 for n in naccs]).astype(np.float64)
+
+    # per-kernel average durations: one graph = reps launches of one call over the copies
+    reps = args.kernel_reps or max(R, 8 * R if per_copy < 100e6 else R)
+    kdur = {}
+    for name, fn in (("tree_attn", attn), ("tree_reject_compact", reject_compact)):
+        kdur[name] = seconds_per_call(fn, copies, reps, 60 if quick else 200)
+        log(f"[bench] {name}: {kdur[name] * 1e6:.2f} us per call")
+
+    a_bytes, a_flops = attn_work(w)
+    rb, cb = [], []
+    for acc, nacc in zip(accs, naccs):
+        stop_rej = []  # did the stop node form a residual (some child of it rejected)?
+        for b in range(w.B):
+            u = int(acc[b][int(nacc[b])])
+            stop_rej.append(any(int(w.parent[b][i]) == u for i in range(1, w.T)))
+        rb.append(reject_bytes(w, nacc, stop_rej))
+        cb.append(compact_bytes(w, acc, nacc))
+    rc_bytes = float(np.mean(rb)) + float(np.mean(cb))
+    work = {"tree_attn": ("hbm", a_bytes, a_flops), "tree_reject_compact": ("hbm", rc_bytes, 0.0)}
+    kernels = {}
+    for name, (b_, by, fl) in work.items():
+        kernels[name] = {"us": round(kdur[name] * 1e6, 2), "bytes": int(by),
+                         "GB/s": round(by / kdur[name] / 1e9, 1)}
+        if fl:
+            kernels[name]["TFLOP/s"] = round(fl / kdur[name] / 1e12, 2)
+    kernels["tree_attn"]["hbm_frac"] = round(a_bytes / kdur["tree_attn"] / 1e9 / HBM_PEAK_GBS, 4)
+    kernels["tree_attn"]["mfma_frac"] = round(a_flops / kdur["tree_attn"] / 1e12 / BF16_PEAK_TFLOPS, 4)
+    step_bytes = a_bytes + rc_bytes
+    step_roof = {"bound": "hbm", "bytes": int(step_bytes), "achieved": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "note": "algorithmic bytes of the whole step (attention, the walked rows, moved KV rows) / step time"}
+    return dict(w=w, value=value, ms_per_step=ms_per_step, spread=spread, lp1=lp1, kdur=kdur, work=work,
+                kernels=kernels, step_roof=step_roof, copies=copies, slots=slots, shared=shared, R=R, reps=reps,
+                a_bytes=a_bytes, a_flops=a_flops)
+
+
+def roofline_of(m):
+    """The `roofline` object for the dominant (longest) kernel of a measurement."""
+    kdur, work = m["kdur"], m["work"]
+    dominant = max(kdur, key=kdur.get)
+    bound, bytes_, flops = work[dominant]
+    if dominant == "tree_attn" and flops / max(bytes_, 1) > BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+        bound = "mfma"
+    if bound == "hbm":
+        achieved = bytes_ / kdur[dominant] / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = flops / kdur[dominant] / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = dominant
+    t_bytes = committed_traffic(m["w"].name, dominant)
+    if t_bytes is not None:
+        roof["traffic"] = t_bytes
+    return roof
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1, help="workload id 0..4 (default 1: chain)")
+    ap.add_argument("--config", type=int, default=4,
+                    help="workload id 0..4 (default 4: batched serving, the largest single-GPU configuration)")
+    ap.add_argument("--also", default="1",
+                    help="comma-separated workload ids also measured (step and attention figures only) and "
+                         "reported under `extra`; empty for none")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: auto, >= 768 MB)")
     ap.add_argument("--kernel-reps", type=int, default=0, help="launches per per-kernel timing graph")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
-    ap.add_argument("--offset", type=int, default=0)
-    ap.add_argument("--calib-copy", action="store_true", help="run one 256 MiB device copy (counter calibration)")
+    ap.add_argument("--offset", type=int, default=0, help="Philox offset of the first step slot")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run plain 256 MiB and 1 GiB device copies (counter calibration)")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
                     help="trace DIR | pmc FETCH_DIR WRITE_DIR: print a markdown summary of rocprofv3 output")
-    ap.add_argument("--workload-name", default="chain", help="workload name recorded by --summarize pmc")
+    ap.add_argument("--workload-name", default="batched_serving", help="workload name recorded by --summarize pmc")
     ap.add_argument("--sweep", action="store_true", help="verify cost against tree size and prefix length (one GPU)")
     args = ap.parse_args()
 
@@ -370,105 +568,16 @@ def main():
     import torch
 
     import tree_verify_attention_masked_amd as stv
-    from workloads import make_config
 
     stv.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log(f"[bench] building workload {args.config}")
-    w = make_config(args.config)
-
-    def up(a, kv=False):
-        t = torch.from_numpy(np.ascontiguousarray(a))
-        if kv and w.dtype == "bf16":
-            t = t.view(torch.int16).view(torch.bfloat16)
-        return t.to(dev)
-
-    per_copy = (w.k_cache.nbytes * 2 + w.q.nbytes + w.target_logits.nbytes + w.draft_probs.nbytes)
-    R = args.copies or max(1, min(16, math.ceil(768e6 / per_copy)))
-    log(f"[bench] {R} input copies of {per_copy / 1e6:.1f} MB")
-    shared = dict(bt=up(w.block_table), lens=up(w.prefix_lens), parent=up(w.parent), tok=up(w.draft_tokens))
-    copies = []
-    for _ in range(R):
-        c = dict(q=up(w.q, True), k=up(w.k_cache, True), v=up(w.v_cache, True), logits=up(w.target_logits),
-                 probs=up(w.draft_probs))
-        c["out"] = torch.empty_like(c["q"])
-        c["acc"] = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
-        c["toks"] = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
-        c["nacc"] = torch.empty((w.B,), dtype=torch.int32, device=dev)
-        c["new_lens"] = torch.empty((w.B,), dtype=torch.int32, device=dev)
-        c["status"] = torch.zeros((w.B,), dtype=torch.int32, device=dev)
-        copies.append(c)
-    code = stv.SPEC_BF16 if w.dtype == "bf16" else stv.SPEC_F32
-    ws_attn = stv.spec_tree_attn_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, w.max_blocks, code)
-    attn_ws = torch.zeros(max(ws_attn, 1), dtype=torch.uint8, device=dev)  # zero once: split arrival counters
-    rej_ws = torch.zeros(int(stv.load_library().spec_tree_reject_workspace_size(w.B, w.T, w.V)),
-                         dtype=torch.uint8, device=dev)  # zero once: the sampler's epochs and tagged exchange slots
-
-    def attn(c):
-        stv.spec_tree_attn(c["q"], c["k"], c["v"], shared["bt"], shared["lens"], shared["parent"], scale=w.scale,
-                           out=c["out"], status=c["status"], workspace=attn_ws if ws_attn else None)
-
-    def reject_compact(c):
-        stv.spec_tree_reject_compact(c["logits"], c["probs"], shared["tok"], shared["parent"], w.temperature,
-                                     c["k"], c["v"], shared["bt"], shared["lens"], w.without_replacement, w.seed,
-                                     args.offset, accepted_nodes=c["acc"], out_tokens=c["toks"],
-                                     num_accepted=c["nacc"], new_lens=c["new_lens"], status=c["status"],
-                                     workspace=rej_ws)
-
-    def step(c):
-        attn(c)
-        reject_compact(c)
-
-    if args.calib_copy:  # a plain copy of known size, for scaling the HBM counters
-        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    for c in copies:  # eager pass: validates and warms every copy
-        step(c)
-    torch.cuda.synchronize()
-    st = sum(int(c["status"].abs().sum()) for c in copies)
-    if st:
-        raise SystemExit(f"device reported input errors: {[c['status'].tolist() for c in copies]}")
-
-    # One graph holds G consecutive steps (step i on copy i % R), so a replay
-    # launches G steps at once and the host's per-launch cost is paid once per
-    # G steps; single-step graphs cover the remainder of K.
-    G = R * max(1, math.ceil(8 / R))
-    step_graphs = [capture_graph([lambda c=c: step(c)]) for c in copies]
-    run_graph = capture_graph([lambda c=copies[i % R]: step(c) for i in range(G)])
-    log(f"[bench] captured {len(step_graphs)} step graphs and one graph of {G} steps; warmup {args.warmup}")
-    for i in range(args.warmup):
-        step_graphs[i % R].replay()
-    torch.cuda.synchronize()
-
-    K = args.steps
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(K // G):
-        run_graph.replay()
-    for i in range(K % G):
-        step_graphs[i % R].replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    log(f"[bench] {K} steps ({K // G} replays of {G} steps + {K % G} single steps): wall {wall * 1e3:.3f} ms, "
-        f"events {gpu_ms:.3f} ms")
-    ms_per_step = wall * 1e3 / K
-    value = w.B * w.T * K / wall
-
-    # per-kernel average durations: one graph = reps launches of one call over the copies
-    reps = args.kernel_reps or max(R, 8 * R if per_copy < 100e6 else R)
-    kdur = {}
-    for name, fn in (("tree_attn", attn), ("tree_reject_compact", reject_compact)):
-        kdur[name] = seconds_per_call(fn, copies, reps, 200)
-        log(f"[bench] {name}: {kdur[name] * 1e6:.2f} us per call")
+    m = measure(args.config, args)
+    w, copies, shared, reps = m["w"], m["copies"], m["shared"], m["reps"]
+    roof = roofline_of(m)
+    kernels = m["kernels"]
+    value_main, ms_main, spread_main, step_roof_main, R_main = (m["value"], m["ms_per_step"], m["spread"],
+                                                                 m["step_roof"], m["R"])
 
     # The step before attention (not part of the timed step, whose inputs already
     # hold the tree's rows): the tree's K/V rows into the cache, keys and queries
@@ -492,42 +601,6 @@ def main():
 
     t_trunc = seconds_per_call(truncate, copies, reps, 200)
     log(f"[bench] tree_truncate: {t_trunc * 1e6:.2f} us per call")
-
-    acc = copies[0]["acc"].cpu().numpy()
-    nacc = copies[0]["nacc"].cpu().numpy()
-    # did the stop node form a residual (some child of it rejected)?
-    stop_rej = []
-    for b in range(w.B):
-        u = int(acc[b][int(nacc[b])])
-        stop_rej.append(any(int(w.parent[b][i]) == u for i in range(1, w.T)))
-    a_bytes, a_flops = attn_work(w)
-    work = {
-        "tree_attn": ("hbm", a_bytes, a_flops),
-        "tree_reject_compact": ("hbm", reject_bytes(w, nacc, stop_rej) + compact_bytes(w, acc, nacc), 0.0),
-    }
-    dominant = max(kdur, key=kdur.get)
-    bound, bytes_, flops = work[dominant]
-    if dominant == "tree_attn" and flops / max(bytes_, 1) > BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
-        bound = "mfma"
-    if bound == "hbm":
-        achieved = bytes_ / kdur[dominant] / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
-    else:
-        achieved = flops / kdur[dominant] / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
-    roof["kernel"] = dominant
-    t_bytes = committed_traffic(w.name, dominant)
-    if t_bytes is not None:
-        roof["traffic"] = t_bytes
-
-    kernels = {}
-    for name, (b_, by, fl) in work.items():
-        kernels[name] = {"us": round(kdur[name] * 1e6, 2), "bytes": int(by),
-                         "GB/s": round(by / kdur[name] / 1e9, 1)}
-        if fl:
-            kernels[name]["TFLOP/s"] = round(fl / kdur[name] / 1e12, 2)
     elt = 2 if w.dtype == "bf16" else 4
     kvw_bytes = w.B * w.T * w.D * elt * (4 * w.Hkv + 2 * w.Hq)  # K, V in and out; Q in and out
     kernels["tree_kv_write"] = {"us": round(t_kvw * 1e6, 2), "bytes": int(kvw_bytes),
@@ -536,22 +609,38 @@ def main():
     kernels["tree_truncate"] = {"us": round(t_trunc * 1e6, 2), "bytes": int(trunc_bytes),
                                 "GB/s": round(trunc_bytes / t_trunc / 1e9, 1), "in_step": False,
                                 "top_k": 50, "top_p": 0.9}
-    kernels["tree_attn"]["hbm_frac"] = round(a_bytes / kdur["tree_attn"] / 1e9 / HBM_PEAK_GBS, 4)
-    kernels["tree_attn"]["mfma_frac"] = round(a_flops / kdur["tree_attn"] / 1e12 / BF16_PEAK_TFLOPS, 4)
+    lp1 = m["lp1"]
+    accepted = {"mean": round(float(lp1.mean()), 3), "p10": float(np.percentile(lp1, 10)),
+                "p90": float(np.percentile(lp1, 90)), "walks": int(lp1.size)}
+    del m, copies, kv_new, trunc_out
+    torch.cuda.empty_cache()
+
+    extra = {}
+    for e in [int(x) for x in args.also.split(",") if x.strip() != ""]:
+        if e == args.config:
+            continue
+        me = measure(e, args, quick=True)
+        re_ = roofline_of(me)
+        extra[me["w"].name] = {"value": round(me["value"], 1), "unit": "tokens/s",
+                               "ms_per_step": round(me["ms_per_step"], 5), "step_us": me["spread"],
+                               "roofline": re_, "step_roofline": me["step_roof"], "kernels": me["kernels"],
+                               "accepted_per_step": round(float(me["lp1"].mean()), 3), "config": me["w"].summary()}
+        del me
+        torch.cuda.empty_cache()
 
     cpu = None
     if args.cpu_budget > 0:
         log(f"[bench] oracle baseline (~{args.cpu_budget:.0f} s)")
-        cpu = cpu_baseline(args.config, args.cpu_budget)
+        cpu = cpu_baseline(w, args.cpu_budget)
 
     cfg = w.summary()
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "metric": METRIC, "value": round(value_main, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_main, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu,
-        "kernels": kernels, "accepted_per_step": round(float(np.mean(nacc + 1)), 3),
-        "input_copies": R,
+        "data": "synthetic", "config": cfg, "roofline": roof, "step_roofline": step_roof_main,
+        "cpu_baseline": cpu, "kernels": kernels, "step_us": spread_main, "accepted_per_step": accepted,
+        "input_copies": R_main, "extra": extra,
     }
     print(json.dumps(line), flush=True)
 

@@ -12,4 +12,5 @@ from .gen import (  # noqa: F401
     make_workload,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    sub_batch,
 )

@@ -457,3 +457,28 @@ def make_config(cfg_id: int, seed: int = 0, **over) -> Workload:
         raise ValueError("config id must be 0..4")
     kw.update(over)
     return make_workload(name=CONFIG_NAMES[cfg_id], tag=cfg_id, seed=seed, **kw)
+
+
+def sub_batch(w: Workload, seqs) -> Workload:
+    """The sequences `seqs` of a workload as a workload of their own, with a
+    cache that holds only their pages (block table renumbered in the same
+    order, so each page keeps its contents).  Used to run a bounded sample of
+    a large batch through a slow reference."""
+    seqs = [int(b) for b in seqs]
+    table = w.block_table[seqs]
+    lens_total = [int(w.prefix_lens[b]) + w.T for b in seqs]
+    pages = [-(-n // BLOCK_SIZE) for n in lens_total]
+    used = np.concatenate([table[i, :p] for i, p in enumerate(pages)])
+    new_table = np.zeros((len(seqs), max(pages)), dtype=np.int32)
+    pos = 0
+    for i, p in enumerate(pages):
+        new_table[i, :p] = np.arange(pos, pos + p, dtype=np.int32)
+        pos += p
+    kc = None if w.k_cache is None else np.ascontiguousarray(w.k_cache[used])
+    vc = None if w.v_cache is None else np.ascontiguousarray(w.v_cache[used])
+    return Workload(name=w.name, tag=w.tag, dtype=w.dtype, B=len(seqs), T=w.T, Hq=w.Hq, Hkv=w.Hkv, D=w.D, V=w.V,
+                    q=w.q[seqs], k_cache=kc, v_cache=vc, block_table=new_table,
+                    prefix_lens=w.prefix_lens[seqs].copy(), parent=w.parent[seqs], draft_tokens=w.draft_tokens[seqs],
+                    target_logits=w.target_logits[seqs], draft_probs=w.draft_probs[seqs],
+                    temperature=w.temperature, without_replacement=w.without_replacement, seed=w.seed,
+                    offset=w.offset, info=dict(w.info))
