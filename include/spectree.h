@@ -15,7 +15,8 @@
  *
  * Conventions shared by every call
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
- *     allocates nothing, keeps no global state and is reentrant.
+ *     allocates nothing and is reentrant; the only state it keeps between
+ *     calls is a per-device cache of one occupancy query (the sampler's).
  *   - Each call only enqueues work on `stream` (a hipStream_t passed as void*;
  *     NULL = the default stream).  No call synchronises or copies to the host,
  *     so a caller can chain draft and verify steps without a CPU round trip.
@@ -69,8 +70,9 @@ enum {
   SPEC_DEV_NONFINITE = 16, /* NaN/Inf in a target-logit row or a draft probability that was read */
   SPEC_DEV_EMPTY = 32,     /* a distribution with zero total mass had to be sampled */
   SPEC_DEV_PATH = 64,      /* accepted path not of the form 0 = n_0 < n_1 < ... < n_L < T */
-  SPEC_DEV_TIMEOUT = 128   /* the workgroups sampling one sequence did not all run at once
-                              (bounded wait expired); outputs of that sequence are undefined */
+  SPEC_DEV_TIMEOUT = 128   /* a bounded wait between the workgroups sampling one sequence
+                              expired (other work held the CUs); the sequence gets the
+                              error outputs of spec_tree_reject */
 };
 
 /* Human-readable name of a spec_status value. */
@@ -107,9 +109,12 @@ int spec_version(void);
  *                is split over several workgroups, the first bytes hold one
  *                arrival counter per (sequence, kv head, block of query rows),
  *                which must be zero before the first call; every call that
- *                completes leaves them zero (zero-fill a workspace once, then
- *                reuse it).  The rest holds the splits' partial results.  Calls
- *                that overlap in time must not share a workspace.
+ *                completes leaves them zero, so for one shape a workspace is
+ *                zero-filled once and then reused.  The rest holds the splits'
+ *                partial results.  Where the counters end depends on (B, T,
+ *                Hq, Hkv, max_blocks_per_seq): zero-fill the workspace again
+ *                before a call with another shape (or keep one per shape).
+ *                Calls that overlap in time must not share a workspace.
  * Supported: dtype SPEC_BF16 with D = 128, dtype SPEC_F32 with D in {64, 128};
  * block_size = 16; 1 <= T <= 256; Hq % Hkv == 0.  B == 0 is a no-op.
  * ---------------------------------------------------------------------- */
@@ -161,17 +166,39 @@ int spec_tree_attn(const void* q, const void* k_cache, const void* v_cache,
  *                 zero before the first call.  It holds, per sequence, an exit
  *                 counter and a call epoch (the first 64 * B bytes) and the
  *                 exchange slots, each tagged with the call it was written in;
- *                 every call that completes leaves it ready for the next, so a
- *                 workspace is zero-filled once and then reused.  Calls that
- *                 overlap in time must not share a workspace.
- * Execution: each sequence is sampled by up to 64 cooperating workgroups that
- * exchange partial sums through the workspace; the grid (B x team size, at
- * most 256 workgroups unless B > 256) must be able to run at once, which holds
- * on an otherwise idle MI355X.  If it cannot, the waits are bounded and the
- * sequence reports SPEC_DEV_TIMEOUT.
+ *                 every call that completes leaves it ready for the next call
+ *                 with the SAME (B, T, V), so for one shape a workspace is
+ *                 zero-filled once and then reused.  Its layout depends on
+ *                 (B, T, V): zero-fill it again before a call with another
+ *                 shape (or keep one workspace per shape).  Calls that overlap
+ *                 in time must not share a workspace.
+ * Execution: each sequence is sampled by a team of up to 64 cooperating
+ * workgroups that exchange partial sums through the workspace.  Before the
+ * launch the team is sized so that the whole grid (B x team size) fits on the
+ * device at once (spec_tree_reject_plan with spec_tree_reject_max_resident);
+ * when not even two members per sequence fit, each sequence gets one
+ * workgroup, which waits for nobody.  Waits are bounded; a wait can run out
+ * only if other work holds the device's CUs for the whole bound, and then the
+ * sequence reports SPEC_DEV_TIMEOUT with the error outputs below.  Member 0
+ * of a team alone writes the sequence's outputs (and, in
+ * spec_tree_reject_compact, moves its KV rows), so they are always one
+ * consistent result.
  * Supported: 1 <= T <= 256, 1 <= V <= 262144, temperature >= 0 and finite.
  * ---------------------------------------------------------------------- */
 size_t spec_tree_reject_workspace_size(int B, int T, int V);
+
+/* Team plan of spec_tree_reject on a device that holds
+ * `max_resident_workgroups` of its workgroups at once: the number of
+ * workgroups per sequence (*team_size) and the vocabulary entries each owns
+ * (*slice_len).  B * *team_size <= max_resident_workgroups whenever
+ * *team_size > 1.  Host only; no GPU needed.  Returns SPEC_OK, or
+ * SPEC_ERR_INVALID_ARG / SPEC_ERR_UNSUPPORTED as spec_tree_reject would. */
+int spec_tree_reject_plan(int B, int T, int V, int64_t max_resident_workgroups, int* team_size, int* slice_len);
+
+/* Workgroups of the sampler kernel the current HIP device holds at once (its
+ * occupancy per CU times the CU count), as used by spec_tree_reject; 0 if the
+ * device cannot be queried. */
+int64_t spec_tree_reject_max_resident(void);
 
 int spec_tree_reject(const float* target_logits, const float* draft_probs,
                      const int32_t* draft_tokens, const int32_t* parent,

@@ -170,3 +170,32 @@ def test_truncate_host_validation(lib):
     assert call(B=0) == 0
     assert call(B=0, i=None) == 0    # nothing to do before the pointers matter
 
+
+
+def test_reject_team_plan_fits_the_resident_grid(lib):
+    # The sampler's team members wait for each other, so a team of more than one
+    # member needs the whole grid resident: B * team <= what the device holds.
+    full = 256  # one workgroup per CU on a 256-CU device
+    assert stv.spec_tree_reject_plan(1, 5, 32000, full) == (63, 508)       # chain: 63 members
+    assert stv.spec_tree_reject_plan(64, 16, 32000, full) == (4, 8000)     # batched serving
+    assert stv.spec_tree_reject_plan(1, 256, 32000, full) == (32, 1000)    # deep trees: at most 32
+    assert stv.spec_tree_reject_plan(1, 5, 1000, full) == (2, 500)         # at least 512 entries a member
+    for B in (1, 3, 8, 64, 100, 255, 256, 300, 1000):
+        for T in (1, 5, 16, 64, 256):
+            for V in (3, 1000, 32000, 128256, 262144):
+                for cap in (1, 2, 7, 64, 100, 255, 256, 1024):
+                    team, sl = stv.spec_tree_reject_plan(B, T, V, cap)
+                    assert team >= 1 and team * sl >= V and (team - 1) * sl < V
+                    assert team == 1 or B * team <= cap, (B, T, V, cap, team)
+                    assert team <= (32 if T > 16 else 64)
+                    # the workspace size query covers the largest team any device gets
+                    big, _ = stv.spec_tree_reject_plan(B, T, V, 1 << 40)
+                    assert team <= big
+    # a device holding fewer workgroups gets smaller teams, down to one per sequence
+    assert stv.spec_tree_reject_plan(64, 16, 32000, 128) == (2, 16000)
+    assert stv.spec_tree_reject_plan(64, 16, 32000, 127) == (1, 32000)
+    assert stv.spec_tree_reject_plan(300, 5, 32000, 256) == (1, 32000)
+    with pytest.raises(stv.SpecError):
+        stv.spec_tree_reject_plan(1, 5, 32000, 0)
+    with pytest.raises(stv.SpecError):
+        stv.spec_tree_reject_plan(1, 257, 32000, 256)

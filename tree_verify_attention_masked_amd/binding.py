@@ -40,6 +40,8 @@ _SIGNATURES = {
     "spec_tree_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                             ctypes.c_float, _i, _vp, _vp, _sz, _vp]),
     "spec_tree_reject_workspace_size": (_sz, [_i, _i, _i]),
+    "spec_tree_reject_plan": (_i, [_i, _i, _i, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
+    "spec_tree_reject_max_resident": (ctypes.c_int64, []),
     "spec_tree_reject": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_uint64,
                               ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_kv_compact": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
@@ -297,6 +299,21 @@ def spec_tree_kv_write(k_new, v_new, q, k_cache, v_cache, block_table, prefix_le
                                 block_table.shape[1], nb, float(rope_theta), _dtype_code(k_new),
                                 _stream(k_new.device))
     _check(rc, "spec_tree_kv_write")
+
+
+def spec_tree_reject_plan(B, T, V, max_resident_workgroups):
+    """(team size, slice length) the sampler uses on a device holding `max_resident_workgroups` of its
+    workgroups at once (host only)."""
+    team, sl = ctypes.c_int(0), ctypes.c_int(0)
+    rc = load_library().spec_tree_reject_plan(B, T, V, int(max_resident_workgroups), ctypes.byref(team),
+                                              ctypes.byref(sl))
+    _check(rc, "spec_tree_reject_plan")
+    return team.value, sl.value
+
+
+def spec_tree_reject_max_resident() -> int:
+    """Workgroups of the sampler kernel the current GPU holds at once."""
+    return int(load_library().spec_tree_reject_max_resident())
 
 
 def spec_status_string(code: int) -> str:

@@ -96,6 +96,16 @@ size_t spec_tree_reject_workspace_size(int B, int T, int V) {
   return reject_workspace_bytes(B, T, V);
 }
 
+int spec_tree_reject_plan(int B, int T, int V, int64_t max_resident_workgroups, int* team_size, int* slice_len) {
+  if (B < 1 || T < 1 || V < 1 || max_resident_workgroups < 1 || !team_size || !slice_len)
+    return SPEC_ERR_INVALID_ARG;
+  if (T > kMaxT || V > kMaxV) return SPEC_ERR_UNSUPPORTED;
+  reject_plan(B, T, V, static_cast<long>(max_resident_workgroups), team_size, slice_len);
+  return SPEC_OK;
+}
+
+int64_t spec_tree_reject_max_resident(void) { return reject_resident_capacity(); }
+
 }  // extern "C"
 
 namespace {

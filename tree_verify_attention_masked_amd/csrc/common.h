@@ -104,6 +104,8 @@ struct RejectLaunch {
 };
 
 size_t reject_workspace_bytes(int B, int T, int V);
+long reject_resident_capacity();  // workgroups of the sampler the current device holds at once (0: unknown)
+void reject_plan(int B, int T, int V, long resident, int* team, int* slice);
 size_t reject_workspace_zero_bytes(int B);
 hipError_t launch_reject(const RejectLaunch& a, hipStream_t stream);
 

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void kv_compact_kernel(const CompactLaunch a) 
     }
   }
   __syncthreads();
-  compact_move(a, b, g, a.prefix_lens[b], s_L, s_first, s_path, stage);  // no-op on error, nothing accepted, or a chain
+  compact_move(a, b, g, g + 1, a.prefix_lens[b], s_L, s_first, s_path, stage);  // no-op on error, nothing accepted, or a chain
 }
 
 }  // namespace

@@ -56,41 +56,53 @@ __device__ inline int compact_plan(const CompactLaunch& c, int b, int Lb, const 
 }
 
 // The whole workgroup (256 threads, every thread calls it): moves rows
-// first..L of kv head g of sequence b (prefix length Lb), as planned, through `stage`
-// (kCompactStageBytes of LDS).  A no-op when first > L.
-__device__ inline void compact_move(const CompactLaunch& c, int b, int g, int Lb, int L, int first,
+// first..L of kv heads g0 .. g1-1 of sequence b (prefix length Lb), as planned,
+// through `stage` (kCompactStageBytes of LDS).  Rows go in chunks of increasing
+// d; a chunk holds those rows of as many heads as the stage takes (heads are
+// independent, so their order within a chunk does not matter).  A no-op when
+// first > L.
+__device__ inline void compact_move(const CompactLaunch& c, int b, int g0, int g1, int Lb, int L, int first,
                                     const int* path, uint8_t* stage) {
-  if (L < 1 || first > L) return;
+  if (L < 1 || first > L || g1 <= g0) return;
   const int32_t* bt_b = c.block_table + static_cast<long>(b) * c.max_blocks;
   const int tid = threadIdx.x;
   const int row_bytes = c.D * c.elem_bytes;  // 256 or 512
   const int chunks = row_bytes / 16;         // 16-byte pieces per row
-  const int rows_per_stage = kCompactStageBytes / (2 * row_bytes);
+  const int pair_cap = kCompactStageBytes / (2 * row_bytes);  // (head, row) pairs per stage, K and V
+  const int nh = g1 - g0;
+  const int rows_per_stage = max(1, pair_cap / nh);
+  const int heads_per_stage = min(nh, pair_cap / rows_per_stage);
   for (int d0 = first; d0 <= L; d0 += rows_per_stage) {
     const int nrows = min(rows_per_stage, L + 1 - d0);
-    const int pieces = nrows * chunks;
-    for (int i = tid; i < 2 * pieces; i += 256) {
-      const int kv = i / pieces, rem = i % pieces;
-      const int r = rem / chunks, ch = rem % chunks;
-      const int src = Lb + path[d0 + r];
-      const long off =
-          ((static_cast<long>(bt_b[src / kBlockSize]) * c.Hkv + g) * kBlockSize + src % kBlockSize) * row_bytes +
-          ch * 16;
-      const uint8_t* base = static_cast<const uint8_t*>(kv ? c.v : c.k);
-      *reinterpret_cast<u32x4*>(stage + i * 16) = *reinterpret_cast<const u32x4*>(base + off);
+    for (int h0 = g0; h0 < g1; h0 += heads_per_stage) {
+      const int nhh = min(heads_per_stage, g1 - h0);
+      const int per_head = nrows * chunks;
+      const int pieces = nhh * per_head;  // per K or V
+      for (int i = tid; i < 2 * pieces; i += 256) {
+        const int kv = i / pieces, rem = i % pieces;
+        const int g = h0 + rem / per_head, rem2 = rem % per_head;
+        const int r = rem2 / chunks, ch = rem2 % chunks;
+        const int src = Lb + path[d0 + r];
+        const long off =
+            ((static_cast<long>(bt_b[src / kBlockSize]) * c.Hkv + g) * kBlockSize + src % kBlockSize) * row_bytes +
+            ch * 16;
+        const uint8_t* base = static_cast<const uint8_t*>(kv ? c.v : c.k);
+        *reinterpret_cast<u32x4*>(stage + i * 16) = *reinterpret_cast<const u32x4*>(base + off);
+      }
+      __syncthreads();
+      for (int i = tid; i < 2 * pieces; i += 256) {
+        const int kv = i / pieces, rem = i % pieces;
+        const int g = h0 + rem / per_head, rem2 = rem % per_head;
+        const int r = rem2 / chunks, ch = rem2 % chunks;
+        const int dst = Lb + d0 + r;
+        const long off =
+            ((static_cast<long>(bt_b[dst / kBlockSize]) * c.Hkv + g) * kBlockSize + dst % kBlockSize) * row_bytes +
+            ch * 16;
+        uint8_t* base = static_cast<uint8_t*>(kv ? c.v : c.k);
+        *reinterpret_cast<u32x4*>(base + off) = *reinterpret_cast<const u32x4*>(stage + i * 16);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    for (int i = tid; i < 2 * pieces; i += 256) {
-      const int kv = i / pieces, rem = i % pieces;
-      const int r = rem / chunks, ch = rem % chunks;
-      const int dst = Lb + d0 + r;
-      const long off =
-          ((static_cast<long>(bt_b[dst / kBlockSize]) * c.Hkv + g) * kBlockSize + dst % kBlockSize) * row_bytes +
-          ch * 16;
-      uint8_t* base = static_cast<uint8_t*>(kv ? c.v : c.k);
-      *reinterpret_cast<u32x4*>(base + off) = *reinterpret_cast<const u32x4*>(stage + i * 16);
-    }
-    __syncthreads();
   }
 }
 

@@ -50,6 +50,7 @@ constexpr int kEagerCap = 8192;  // floats of eager-row logit slices kept in LDS
 constexpr int kSliceCap = 8192;  // floats of the current row's logits / draft probs kept in LDS
 constexpr int kSyncStride = 16;  // uint32 words per sequence (64 B): [1] exit counter, [2] call epoch
 constexpr unsigned kSpinLimit = 1u << 24;
+constexpr long kUnboundedResidency = 1L << 40;
 
 struct Rec {
   float m;   // slice max logit (-inf if none)
@@ -65,10 +66,20 @@ struct Team {
   int NW, S, ld, E;  // members, slice length, LDS row stride (S rounded up to 4), eager rows (0, 1, 2, 4 or 8)
 };
 
-Team team_shape(int B, int T, int V) {
+// Team size: up to 64 members (32 for trees of more than 16 nodes), about 256
+// workgroups in all, at least 512 vocabulary entries per member, and never more
+// workgroups than the device can hold at once (`resident`): members of a team
+// wait for each other, so a team larger than one member needs the whole grid
+// resident; when even two members per sequence do not fit, each sequence gets
+// a single member, which waits for nobody.
+Team team_shape(int B, int T, int V, long resident) {
   Team t;
   int nw = std::max(1, std::min(T > 16 ? kDeepTeam : kMaxTeam, 256 / std::max(B, 1)));
   nw = std::min(nw, std::max(1, (V + 511) / 512));
+  if (static_cast<long>(nw) * B > resident) {
+    nw = static_cast<int>(std::max(1L, std::min<long>(nw, resident / std::max(B, 1))));
+    if (nw < 2) nw = 1;
+  }
   t.NW = nw;
   t.S = (V + nw - 1) / nw;
   t.ld = (t.S + 3) & ~3;
@@ -1044,6 +1055,24 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         }
       }
       __syncthreads();
+      // the drawn token goes to member 0, the only member that writes outputs:
+      // the owner publishes it in this exchange's slot, member 0 waits for it
+      if (xrow >= a.part_rows) {
+        if (tid == 0) sh_fail = 1;
+        break;
+      }
+      Slot* xs = part + xrow * NW;
+      ++xrow;
+      if (sh_owner != 0 && sh_err == 0) {
+        if (wg == sh_owner && tid == 0) put_slot(&xs[wg], Rec{0.f, sh_emit_local, 0.0}, tag);
+        if (wg == 0 && wave == 0) {
+          const Slot* const one[1] = {xs + sh_owner};
+          Rec rr[1];
+          get_slots<1>(one, 1, 1, tag, Rec{0.f, -1, 0.0}, rr, &sh_fail);
+          if (lane == 0) sh_emit_local = rr[0].idx;
+        }
+        __syncthreads();
+      }
       break;
     }
   }
@@ -1051,42 +1080,39 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   if (sh_fail && tid == 0) atomicOr(&sh_err, SPEC_DEV_TIMEOUT);
   __syncthreads();
 
-  // outputs: member 0 writes the path; the member holding the drawn token writes it
+  // Outputs and compaction: member 0 alone writes every output of the
+  // sequence and moves its KV rows, from its own view of the walk, so the
+  // results are one member's decisions even when another member's wait ran
+  // out (the others write nothing).
   const int err = sh_err;
   const int L = err ? 0 : sh_len - 1;
-  if (tid == 0) {
-    int32_t* acc_b = a.accepted + static_cast<long>(b) * T;
-    int32_t* out_b = a.out_tokens + static_cast<long>(b) * T;
-    if (wg == 0) {
+  if (wg == 0) {
+    if (tid == 0) {
+      int32_t* acc_b = a.accepted + static_cast<long>(b) * T;
+      int32_t* out_b = a.out_tokens + static_cast<long>(b) * T;
       for (int i = 0; i < T; ++i) {
         acc_b[i] = (i == 0) ? 0 : ((!err && i <= L) ? s_path[i] : -1);
-        if (err || i != L || a.greedy) out_b[i] = (!err && i < L) ? s_tok[s_path[i + 1]] : -1;
+        out_b[i] = (!err && i < L) ? s_tok[s_path[i + 1]] : -1;
       }
-      if (!err && a.greedy) out_b[L] = emitted;
+      if (!err) out_b[L] = a.greedy ? emitted : sh_emit_local;
       a.num_accepted[b] = L;
       report(a.status, b, err);
     }
-    if (!err && !a.greedy && wg == sh_owner) out_b[L] = sh_emit_local;
-  }
-  if (a.fuse) {
-    // KV compaction along the path every member holds (s_path[0..L]; L = 0
-    // after a sampler error, which leaves the cache as it is): member 0 plans
-    // it and reports, every member moves the kv heads g = wg, wg + NW, ...
-    // through its (now free) current-row LDS buffer
-    if (tid == 0) {
-      int first = 1 << 30;
-      const int cerr = compact_plan(a.c, b, c_lb, s_path, L, &first);
-      sh_c = cerr ? -1 : L;  // the walk is over: its scratch words are free
-      sh_x = first;
-      if (wg == 0) {
+    if (a.fuse) {
+      // KV compaction along the path (s_path[0..L]; L = 0 after a sampler
+      // error, which leaves the cache as it is), every kv head, through the
+      // (now free) current-row LDS buffer
+      if (tid == 0) {
+        int first = 1 << 30;
+        const int cerr = compact_plan(a.c, b, c_lb, s_path, L, &first);
+        sh_c = cerr ? -1 : L;  // the walk is over: its scratch words are free
+        sh_x = first;
         if (a.c.new_lens != nullptr) a.c.new_lens[b] = cerr ? c_lb : c_lb + L + 1;
         report(a.status, b, cerr);
       }
+      __syncthreads();
+      compact_move(a.c, b, 0, a.c.Hkv, c_lb, sh_c, sh_x, s_path, reinterpret_cast<uint8_t*>(cur_lbuf));
     }
-    __syncthreads();
-    const int cL = sh_c, cfirst = sh_x;
-    for (int g = wg; g < a.c.Hkv; g += NW)
-      compact_move(a.c, b, g, c_lb, cL, cfirst, s_path, reinterpret_cast<uint8_t*>(cur_lbuf));
   }
   if (tid == 0) {
     // Leave.  The last member out resets the exit counter and advances the
@@ -1115,19 +1141,48 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
 }  // namespace
 
 // Exchanges after the eager one: at most one per visited row past the eager
-// rows (<= T), one per rejected child (<= T - 1) and one final republish.
-int part_rows(int T) { return 2 * T + 1; }
+// rows (<= T), one per rejected child (<= T - 1), one final republish and the
+// drawn token.
+int part_rows(int T) { return 2 * T + 2; }
 
 size_t reject_workspace_bytes(int B, int T, int V) {
-  const Team t = team_shape(B, T, V);
+  const Team t = team_shape(B, T, V, kUnboundedResidency);  // the largest team any device gets
   const size_t sync = static_cast<size_t>(B) * kSyncStride * sizeof(unsigned);
   return sync + static_cast<size_t>(B) * t.NW * (std::max(t.E, 1) + part_rows(T)) * sizeof(Slot);
 }
 
 size_t reject_workspace_zero_bytes(int B) { return static_cast<size_t>(B) * kSyncStride * sizeof(unsigned); }
 
+// Workgroups of the sampler kernel the current device holds at once: its
+// occupancy per CU (LDS bound: one) times the CU count, queried once per
+// device.
+long reject_resident_capacity() {
+  static long cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int cus = 0, per_cu_fit = 0, per_cu_nofit = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_fit, reject_team_kernel<true>, kThreads, 0) !=
+          hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_nofit, reject_team_kernel<false>, kThreads, 0) !=
+          hipSuccess)
+    return 0;
+  const long cap = static_cast<long>(cus) * std::min(per_cu_fit, per_cu_nofit);
+  if (dev < 64) cache[dev] = cap;
+  return cap;
+}
+
+void reject_plan(int B, int T, int V, long resident, int* team, int* slice) {
+  const Team t = team_shape(B, T, V, resident);
+  *team = t.NW;
+  *slice = t.S;
+}
+
 hipError_t launch_reject(const RejectLaunch& L, hipStream_t stream) {
-  const Team t = team_shape(L.B, L.T, L.V);
+  const long resident = reject_resident_capacity();
+  if (resident <= 0) return hipErrorInvalidDevice;
+  const Team t = team_shape(L.B, L.T, L.V, resident);
   const bool greedy = (L.temperature == 0.0f);
   TArgs a{};
   a.logits = L.logits;
