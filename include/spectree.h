@@ -163,15 +163,14 @@ int spec_tree_attn(const void* q, const void* k_cache, const void* v_cache,
  *   status        [B] int32 or NULL; on a device-detected error the sequence
  *                 gets L = 0, accepted_nodes = [0, -1, ...], out_tokens all -1
  *   workspace     >= spec_tree_reject_workspace_size(B, T, V) bytes, all of it
- *                 zero before the first call.  It holds, per sequence, an exit
- *                 counter and a call epoch (the first 64 * B bytes) and the
- *                 exchange slots, each tagged with the call it was written in;
- *                 every call that completes leaves it ready for the next call
- *                 with the SAME (B, T, V), so for one shape a workspace is
- *                 zero-filled once and then reused.  Its layout depends on
- *                 (B, T, V): zero-fill it again before a call with another
- *                 shape (or keep one workspace per shape).  Calls that overlap
- *                 in time must not share a workspace.
+ *                 zero before the first call.  Its first 256 bytes hold the
+ *                 grid's exit counter and a call epoch; the rest holds the
+ *                 exchange slots, each tagged with the epoch of the call that
+ *                 wrote it, so a slot is only ever read by that call.  Every
+ *                 call that completes leaves the workspace ready for the next
+ *                 call of any shape it is large enough for: zero-fill it once,
+ *                 then reuse it.  Calls that overlap in time must not share a
+ *                 workspace.
  * Execution: each sequence is sampled by a team of up to 64 cooperating
  * workgroups that exchange partial sums through the workspace.  Before the
  * launch the team is sized so that the whole grid (B x team size) fits on the

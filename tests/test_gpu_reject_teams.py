@@ -6,9 +6,7 @@
 * one member per sequence (a batch larger than the device holds teams for),
   with slices in LDS and in global memory;
 * the team plan the library launches fits the device's resident grid;
-* one workspace reused across batch sizes 4, 8, 4 (zero-filled again at each
-  change of shape, as the header requires) and across repeated calls of one
-  shape (not zero-filled again).
+* one workspace, zero-filled once, reused across batch sizes and tree sizes.
 Every call is compared with the oracle as in test_gpu_reject.py.
 """
 import numpy as np
@@ -77,17 +75,14 @@ def test_one_member_per_sequence(V):
 
 
 def test_workspace_reused_across_shapes():
-    ws = torch.zeros(int(stv.load_library().spec_tree_reject_workspace_size(8, 10, 5000)), dtype=torch.uint8,
-                     device="cuda")
-    shapes = [4, 8, 4]
-    prev = None
-    for i, B in enumerate(shapes):
-        w = make_workload(tag=620 + B, B=B, Hq=2, Hkv=2, D=64, dtype="f32", V=5000, prefix=[4] * B, tree="random",
-                          T=10, max_depth=4, temperature=1.0, with_kv=False)
-        need = int(stv.load_library().spec_tree_reject_workspace_size(B, 10, 5000))
-        if B != prev:
-            ws[:need].zero_()  # another shape: zero-fill again, as the header requires
-        prev = B
-        print(f"[teams] workspace reuse call {i}: B={B}", flush=True)
-        d = DevWorkload(w)
-        _check(w, range(3), workspace=ws[:need], d=d)  # same shape three times without zero-filling
+    # one workspace, zero-filled once, for batches of 4, 8, then 4 sequences and
+    # two tree sizes: the slots the larger batch wrote sit where the smaller
+    # batch's slots of other sequences lie, and must never pass for them
+    lib = stv.load_library()
+    ws = torch.zeros(int(lib.spec_tree_reject_workspace_size(8, 14, 5000)), dtype=torch.uint8, device="cuda")
+    for i, (B, T) in enumerate([(4, 10), (8, 10), (4, 10), (8, 14), (4, 10)]):
+        w = make_workload(tag=620 + B + T, B=B, Hq=2, Hkv=2, D=64, dtype="f32", V=5000, prefix=[4] * B,
+                          tree="random", T=T, max_depth=4, temperature=1.0, with_kv=False)
+        need = int(lib.spec_tree_reject_workspace_size(B, T, 5000))
+        print(f"[teams] workspace reuse call {i}: B={B} T={T}", flush=True)
+        _check(w, range(3), workspace=ws[:need])  # three calls of each shape, never zero-filled again

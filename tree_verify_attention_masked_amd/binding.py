@@ -186,7 +186,7 @@ def spec_tree_reject(target_logits, draft_probs, draft_tokens, parent, temperatu
     if status is not None:
         _need(status, "status", torch.int32, 1)
     ws = int(lib.spec_tree_reject_workspace_size(B, T, V))
-    if workspace is None and ws > 0:  # zero-filled: exit counters, call epochs and tagged exchange slots
+    if workspace is None and ws > 0:  # zero-filled: its header holds the exit counter and the call epoch
         workspace = torch.zeros(ws, dtype=torch.uint8, device=dev)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib.spec_tree_reject(_ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(parent),
@@ -256,7 +256,7 @@ def spec_tree_reject_compact(target_logits, draft_probs, draft_tokens, parent, t
     if status is not None:
         _need(status, "status", torch.int32, 1)
     ws = int(lib.spec_tree_reject_workspace_size(B, T, V))
-    if workspace is None and ws > 0:  # zero-filled: exit counters, call epochs and tagged exchange slots
+    if workspace is None and ws > 0:  # zero-filled: its header holds the exit counter and the call epoch
         workspace = torch.zeros(ws, dtype=torch.uint8, device=dev)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib.spec_tree_reject_compact(_ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(parent),

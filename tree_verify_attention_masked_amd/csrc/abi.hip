@@ -141,6 +141,7 @@ int make_reject(const float* target_logits, const float* draft_probs, const int3
   L->num_accepted = num_accepted;
   L->status = status;
   L->workspace = workspace;
+  L->workspace_bytes = workspace_bytes;
   return SPEC_OK;
 }
 

@@ -100,13 +100,14 @@ struct RejectLaunch {
   int32_t* num_accepted;
   int32_t* status;
   void* workspace;
+  size_t workspace_bytes;
   const CompactLaunch* compact;  // non-null: compact the KV cache along the accepted path in the same launch
 };
 
 size_t reject_workspace_bytes(int B, int T, int V);
 long reject_resident_capacity();  // workgroups of the sampler the current device holds at once (0: unknown)
 void reject_plan(int B, int T, int V, long resident, int* team, int* slice);
-size_t reject_workspace_zero_bytes(int B);
+size_t reject_workspace_zero_bytes();
 hipError_t launch_reject(const RejectLaunch& a, hipStream_t stream);
 
 hipError_t launch_compact(const CompactLaunch& a, hipStream_t stream);

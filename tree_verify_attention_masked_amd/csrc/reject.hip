@@ -48,7 +48,7 @@ constexpr int kMaxTeam = 64;     // workgroups per sequence (one wave merges the
 constexpr int kDeepTeam = 32;    // at most this many for trees with deeper rows (more than 16 nodes)
 constexpr int kEagerCap = 8192;  // floats of eager-row logit slices kept in LDS
 constexpr int kSliceCap = 8192;  // floats of the current row's logits / draft probs kept in LDS
-constexpr int kSyncStride = 16;  // uint32 words per sequence (64 B): [1] exit counter, [2] call epoch
+constexpr int kHeaderBytes = 256;  // workspace header: word 0 exit counter of the grid, word 1 call epoch
 constexpr unsigned kSpinLimit = 1u << 24;
 constexpr long kUnboundedResidency = 1L << 40;
 
@@ -181,7 +181,9 @@ struct TArgs {
   int32_t* out_tokens;
   int32_t* num_accepted;
   int32_t* status;
-  unsigned* sync;  // [B][kSyncStride]: word 1 exit counter, word 2 call epoch
+  unsigned* hdr;   // workspace header: [0] exit counter of the grid, [1] call epoch
+  unsigned long long* slot_words;  // every 64-bit word of the workspace after the header
+  long n_slot_words;               // (cleared when the epoch wraps)
   Slot* eager;     // [B][NW][max(E,1)]: statistics of the eager rows
   Slot* part;      // [B][part_rows][NW]: one row of slots per later exchange
   int part_rows;
@@ -605,12 +607,11 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   const int i0 = min(n, 4 * c0), i1 = min(n, 4 * c1);
   const float* lg_b = a.logits + static_cast<long>(b) * T * V;
   const float* q_b = a.q + static_cast<long>(b) * T * V;
-  unsigned* ctr = a.sync + static_cast<long>(b) * kSyncStride;
   Slot* eager = a.eager + static_cast<long>(b) * NW * max(E, 1);
   Slot* part = a.part + static_cast<long>(b) * a.part_rows * NW;
   int xrow = 0;  // the next row of part slots (one per exchange after the eager one)
-  // the call's tag: the sequence's epoch (advanced by the last member to leave) + 1
-  const uint32_t epoch = __hip_atomic_load(ctr + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the call's tag: the workspace's epoch (advanced by the last workgroup of the grid to leave) + 1
+  const uint32_t epoch = __hip_atomic_load(a.hdr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t tag = epoch + 1u;
 
   // tree and tokens (T <= kThreads: one node per thread) and the eager logit and
@@ -1114,26 +1115,30 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       compact_move(a.c, b, 0, a.c.Hkv, c_lb, sh_c, sh_x, s_path, reinterpret_cast<uint8_t*>(cur_lbuf));
     }
   }
+  // Leave.  The last workgroup of the grid out resets the exit counter and
+  // advances the workspace's epoch, so the next call's tag differs from every
+  // tag written before, whatever shape the earlier calls had: a slot is valid
+  // only for the call that wrote it.  When the next tag would be 0 (after
+  // 2^32 - 1 calls) the epoch starts again at 0, and this workgroup first clears
+  // every word of the workspace after the header, so no slot written in an
+  // earlier cycle can carry a later tag.
   if (tid == 0) {
-    // Leave.  The last member out resets the exit counter and advances the
-    // sequence's epoch, so the next call's tag differs from every tag written
-    // before.  When the next tag would be 0 (after 2^32 - 1 calls) the epoch
-    // starts again at 0, and this member first clears every slot of the
-    // sequence, so no slot written in an earlier cycle can carry a later tag.
-    const unsigned prev = atomicAdd(ctr + 1, 1u);
-    if (prev == static_cast<unsigned>(NW - 1)) {
-      atomicExch(ctr + 1, 0u);
-      unsigned next = epoch + 1u;
-      if (next == 0xFFFFFFFFu) {
-        next = 0u;
-        const long ne = static_cast<long>(NW) * max(E, 1), np = static_cast<long>(a.part_rows) * NW;
-        for (long i = 0; i < ne + np; ++i) {
-          Slot* sl = i < ne ? eager + i : part + (i - ne);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) __hip_atomic_store(&sl->w[k], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-      atomicExch(ctr + 2, next);
+    const unsigned prev = atomicAdd(a.hdr, 1u);
+    sh_state = (prev == gridDim.x - 1u) ? 1 : 0;
+  }
+  __syncthreads();
+  if (sh_state == 1) {
+    unsigned next = epoch + 1u;
+    if (next == 0xFFFFFFFFu) {
+      next = 0u;
+      for (long i = tid; i < a.n_slot_words; i += kThreads)
+        __hip_atomic_store(a.slot_words + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    if (tid == 0) {
+      atomicExch(a.hdr, 0u);
+      atomicExch(a.hdr + 1, next);
     }
   }
 }
@@ -1147,11 +1152,10 @@ int part_rows(int T) { return 2 * T + 2; }
 
 size_t reject_workspace_bytes(int B, int T, int V) {
   const Team t = team_shape(B, T, V, kUnboundedResidency);  // the largest team any device gets
-  const size_t sync = static_cast<size_t>(B) * kSyncStride * sizeof(unsigned);
-  return sync + static_cast<size_t>(B) * t.NW * (std::max(t.E, 1) + part_rows(T)) * sizeof(Slot);
+  return kHeaderBytes + static_cast<size_t>(B) * t.NW * (std::max(t.E, 1) + part_rows(T)) * sizeof(Slot);
 }
 
-size_t reject_workspace_zero_bytes(int B) { return static_cast<size_t>(B) * kSyncStride * sizeof(unsigned); }
+size_t reject_workspace_zero_bytes() { return kHeaderBytes; }
 
 // Workgroups of the sampler kernel the current device holds at once: its
 // occupancy per CU (LDS bound: one) times the CU count, queried once per
@@ -1193,8 +1197,10 @@ hipError_t launch_reject(const RejectLaunch& L, hipStream_t stream) {
   a.out_tokens = L.out_tokens;
   a.num_accepted = L.num_accepted;
   a.status = L.status;
-  a.sync = static_cast<unsigned*>(L.workspace);
-  a.eager = reinterpret_cast<Slot*>(static_cast<char*>(L.workspace) + reject_workspace_zero_bytes(L.B));
+  a.hdr = static_cast<unsigned*>(L.workspace);
+  a.slot_words = reinterpret_cast<unsigned long long*>(static_cast<char*>(L.workspace) + kHeaderBytes);
+  a.n_slot_words = static_cast<long>((L.workspace_bytes - kHeaderBytes) / sizeof(unsigned long long));
+  a.eager = reinterpret_cast<Slot*>(static_cast<char*>(L.workspace) + kHeaderBytes);
   a.part = a.eager + static_cast<size_t>(L.B) * t.NW * std::max(t.E, 1);
   a.part_rows = part_rows(L.T);
   a.T = L.T;
