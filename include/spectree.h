@@ -263,6 +263,34 @@ int spec_tree_reject_compact(const float* target_logits, const float* draft_prob
                              int num_blocks, int dtype, void* stream);
 
 /* ----------------------------------------------------------------------
+ * spec_tree_reject_compact_noalloc — spec_tree_reject_compact without a
+ * caller-supplied workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The call itself allocates nothing: the sampler's workspace is
+ * a static device array of the library, 8 MiB per GPU (one copy on every GPU
+ * the library runs on, held until the process ends), zero-filled at load.
+ *
+ *   arguments  as for spec_tree_reject_compact, without workspace and
+ *              workspace_bytes; the caller still passes every input and output
+ *   returns    SPEC_ERR_WORKSPACE when spec_tree_reject_workspace_size(B, T, V)
+ *              exceeds 8 MiB (e.g. B * team size * (2T + 10) * 32 bytes past
+ *              that); otherwise as spec_tree_reject_compact
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents; each completed call leaves it ready for the next call of any
+ * shape.  Calls that overlap in time on one GPU (several streams or threads)
+ * race on it and must not be issued.
+ * ---------------------------------------------------------------------- */
+int spec_tree_reject_compact_noalloc(const float* target_logits, const float* draft_probs,
+                                     const int32_t* draft_tokens, const int32_t* parent,
+                                     int B, int T, int V, float temperature, int without_replacement,
+                                     uint64_t seed, uint64_t offset,
+                                     int32_t* accepted_nodes, int32_t* out_tokens, int32_t* num_accepted,
+                                     int32_t* status, void* k_cache, void* v_cache,
+                                     const int32_t* block_table, const int32_t* prefix_lens,
+                                     int32_t* new_lens, int Hkv, int D, int block_size,
+                                     int max_blocks_per_seq, int num_blocks, int dtype, void* stream);
+
+/* ----------------------------------------------------------------------
  * spec_tree_kv_write — the step before verify attention: write every tree
  * node's K and V rows into the paged cache, the key (and, if given, the
  * queries, in place) rotated for the node's position.

@@ -30,6 +30,7 @@ from .binding import (  # noqa: F401
     spec_tree_attn_workspace_size,
     spec_tree_reject,
     spec_tree_reject_compact,
+    spec_tree_reject_compact_noalloc,
     spec_tree_reject_max_resident,
     spec_tree_reject_plan,
     spec_tree_kv_write,

@@ -51,6 +51,9 @@ _SIGNATURES = {
     "spec_tree_reject_compact": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_uint64,
                                       ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp, _sz,
                                       _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "spec_tree_reject_compact_noalloc": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_uint64,
+                                              ctypes.c_uint64, _vp, _vp, _vp, _vp,
+                                              _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
 }
 
 _lib = None
@@ -267,6 +270,45 @@ def spec_tree_reject_compact(target_logits, draft_probs, draft_tokens, parent, t
                                       _ptr(prefix_lens), _ptr(new_lens), Hkv, D, bs, block_table.shape[1], nb,
                                       _dtype_code(k_cache), _stream(dev))
     _check(rc, "spec_tree_reject_compact")
+    return accepted_nodes, out_tokens, num_accepted, new_lens
+
+
+def spec_tree_reject_compact_noalloc(target_logits, draft_probs, draft_tokens, parent, temperature, k_cache,
+                                     v_cache, block_table, prefix_lens, accepted_nodes, out_tokens, num_accepted,
+                                     new_lens, without_replacement=False, seed=0, offset=0, status=None):
+    """spec_tree_reject_compact on the library's static workspace: the caller passes every output (nothing is
+    allocated here or in the call).  Returns (accepted_nodes, out_tokens, num_accepted, new_lens)."""
+    lib = load_library()
+    _need(target_logits, "target_logits", torch.float32, 3)
+    _need(draft_tokens, "draft_tokens", torch.int32, 2)
+    _need(parent, "parent", torch.int32, 2)
+    _need(k_cache, "k_cache", ndim=4)
+    _need(v_cache, "v_cache", k_cache.dtype, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(prefix_lens, "prefix_lens", torch.int32, 1)
+    B, T, V = target_logits.shape
+    if draft_probs is not None:
+        _need(draft_probs, "draft_probs", torch.float32, 3)
+        if tuple(draft_probs.shape) != (B, T, V):
+            raise ValueError("draft_probs shape disagrees with target_logits")
+    if tuple(draft_tokens.shape) != (B, T) or tuple(parent.shape) != (B, T):
+        raise ValueError("draft_tokens / parent shapes disagree with target_logits")
+    for t, name, shape in ((accepted_nodes, "accepted_nodes", (B, T)), (out_tokens, "out_tokens", (B, T)),
+                           (num_accepted, "num_accepted", (B,)), (new_lens, "new_lens", (B,))):
+        _need(t, name, torch.int32, len(shape))
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}")
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    nb, Hkv, bs, D = k_cache.shape
+    rc = lib.spec_tree_reject_compact_noalloc(_ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens),
+                                              _ptr(parent), B, T, V, float(temperature), int(bool(without_replacement)),
+                                              int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1),
+                                              _ptr(accepted_nodes), _ptr(out_tokens), _ptr(num_accepted), _ptr(status),
+                                              _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(prefix_lens),
+                                              _ptr(new_lens), Hkv, D, bs, block_table.shape[1], nb,
+                                              _dtype_code(k_cache), _stream(target_logits.device))
+    _check(rc, "spec_tree_reject_compact_noalloc")
     return accepted_nodes, out_tokens, num_accepted, new_lens
 
 

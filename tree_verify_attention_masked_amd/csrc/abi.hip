@@ -110,6 +110,11 @@ int64_t spec_tree_reject_max_resident(void) { return reject_resident_capacity();
 
 namespace {
 
+// Stand-in for the workspace pointer of the allocation-free entry point during
+// validation (never dereferenced: launch_reject_static puts the device address
+// of its static array in its place).
+void* const kStaticWorkspace = reinterpret_cast<void*>(static_cast<uintptr_t>(1));
+
 // Host validation of the sampler's arguments and its launch description.
 int make_reject(const float* target_logits, const float* draft_probs, const int32_t* draft_tokens,
                 const int32_t* parent, int B, int T, int V, float temperature, int without_replacement, uint64_t seed,
@@ -123,7 +128,7 @@ int make_reject(const float* target_logits, const float* draft_probs, const int3
     return SPEC_ERR_INVALID_ARG;
   if (temperature > 0.0f && !draft_probs) return SPEC_ERR_INVALID_ARG;
   const size_t need = reject_workspace_bytes(B, T, V);
-  if (workspace == nullptr || workspace_bytes < need) return SPEC_ERR_WORKSPACE;
+  if (workspace == nullptr || workspace_bytes < need) return SPEC_ERR_WORKSPACE;  // (see kStaticWorkspace)
   *L = RejectLaunch{};
   L->logits = target_logits;
   L->q = draft_probs;
@@ -222,6 +227,27 @@ int spec_tree_reject_compact(const float* target_logits, const float* draft_prob
   if (rc != SPEC_OK || B == 0) return rc;
   R.compact = &C;  // copied into the kernel arguments at launch
   const hipError_t e = launch_reject(R, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+int spec_tree_reject_compact_noalloc(const float* target_logits, const float* draft_probs,
+                                     const int32_t* draft_tokens, const int32_t* parent, int B, int T, int V,
+                                     float temperature, int without_replacement, uint64_t seed, uint64_t offset,
+                                     int32_t* accepted_nodes, int32_t* out_tokens, int32_t* num_accepted,
+                                     int32_t* status, void* k_cache, void* v_cache, const int32_t* block_table,
+                                     const int32_t* prefix_lens, int32_t* new_lens, int Hkv, int D, int block_size,
+                                     int max_blocks_per_seq, int num_blocks, int dtype, void* stream) {
+  RejectLaunch R;
+  int rc = make_reject(target_logits, draft_probs, draft_tokens, parent, B, T, V, temperature, without_replacement,
+                       seed, offset, accepted_nodes, out_tokens, num_accepted, status, kStaticWorkspace,
+                       reject_static_scratch_bytes(), &R);
+  if (rc != SPEC_OK) return rc;
+  CompactLaunch C;
+  rc = make_compact(k_cache, v_cache, block_table, prefix_lens, new_lens, B, T, Hkv, D, block_size,
+                    max_blocks_per_seq, num_blocks, dtype, status, &C);
+  if (rc != SPEC_OK || B == 0) return rc;
+  R.compact = &C;
+  const hipError_t e = launch_reject_static(R, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

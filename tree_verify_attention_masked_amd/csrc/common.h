@@ -109,6 +109,8 @@ long reject_resident_capacity();  // workgroups of the sampler the current devic
 void reject_plan(int B, int T, int V, long resident, int* team, int* slice);
 size_t reject_workspace_zero_bytes();
 hipError_t launch_reject(const RejectLaunch& a, hipStream_t stream);
+size_t reject_static_scratch_bytes();  // size of the allocation-free entry point's device array
+hipError_t launch_reject_static(const RejectLaunch& a, hipStream_t stream);  // on that array
 
 hipError_t launch_compact(const CompactLaunch& a, hipStream_t stream);
 

@@ -1183,6 +1183,55 @@ void reject_plan(int B, int T, int V, long resident, int* team, int* slice) {
   *slice = t.S;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: the sampler's workspace as a
+// file-scope device array, one copy per GPU, held until the process ends.  It
+// starts zero-filled (static storage); every completed call leaves it ready for
+// the next call of any shape (the epoch protocol above), so it is never
+// cleared again.  In host code `scratch` names a host-side stand-in: its device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is ever handed to a kernel.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of this device's copy of `scratch`, looked up at the first
+// call on the device; nullptr (with *err set) if the lookup fails.
+static void* scratch_address(hipError_t* err) {
+  static void* addr[kMaxDevices];
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess || p == nullptr) {
+      if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+size_t reject_static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t launch_reject_static(const RejectLaunch& L_in, hipStream_t stream) {
+  hipError_t err = hipSuccess;
+  void* p = scratch_address(&err);
+  if (p == nullptr) return err;
+  RejectLaunch L = L_in;
+  L.workspace = p;
+  L.workspace_bytes = kStaticScratchBytes;
+  return launch_reject(L, stream);
+}
+
 hipError_t launch_reject(const RejectLaunch& L, hipStream_t stream) {
   const long resident = reject_resident_capacity();
   if (resident <= 0) return hipErrorInvalidDevice;
