@@ -18,7 +18,10 @@ written from the pages that describe tree-based speculative decoding:
 * the step before attention: rotary positions that follow the tree and the
   write of the tree's K/V rows into the paged cache (``rope.py``);
 * top-k / top-p truncation of the target logits before the acceptance tests
-  (``truncate.py``).
+  (``truncate.py``);
+* the Sequoia tree-construction dynamic program over a positional acceptance
+  vector (``sequoia.py``; the objective and recurrence come from the published
+  Sequoia paper, the pages only name the method).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  It shares no code with the HIP library
@@ -52,3 +55,4 @@ from .reject import (  # noqa: F401
 from .compact import kv_compact  # noqa: F401
 from .rope import rope, tree_kv_write, tree_positions  # noqa: F401
 from .truncate import truncate_logits, truncate_row  # noqa: F401
+from .sequoia import expected_tokens, sequoia_tree  # noqa: F401
