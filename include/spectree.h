@@ -351,6 +351,32 @@ int spec_tree_kv_write(const void* k_new, const void* v_new, void* q, void* k_ca
 int spec_tree_truncate(const float* logits_in, float* logits_out, int B, int T, int V,
                        float temperature, int top_k, float top_p, int32_t* status, void* stream);
 
+/* ----------------------------------------------------------------------
+ * spec_sequoia_tree — Sequoia's tree construction: the draft-tree shape of n
+ * nodes and depth <= max_depth that maximises the expected number of tokens
+ * one verification step generates ("Sequoia: Scalable and Robust Speculative
+ * Decoding" summary, "Scalable Speculative Decoding", "Dynamic Programming";
+ * the objective and the dynamic program are those of the published Sequoia
+ * paper).  Positional acceptance: the k-th child of an accepted node, in the
+ * order the verifier tries siblings, is the one accepted with probability
+ * accept[k-1] (0 past the vector), whatever the node; a node is accepted with
+ * the product of those probabilities along its path, and the tree generates
+ * their sum (root: 1) tokens in expectation.  Host code: runs on the CPU, no
+ * GPU needed; every pointer is a HOST pointer.
+ *
+ *   accept    [K] double in [0, 1] (measured per-rank acceptance; K may be 0)
+ *   n         tree size, 1 <= n <= 4096
+ *   max_depth deepest node's depth in edges from the root (>= 1 when n > 1)
+ *   parent    [n] int32 out: parent array numbered breadth first, siblings in
+ *             rank order (parent[0] = -1, parent[i] < i), ready for the other
+ *             calls' `parent` argument
+ *   expected  out (nullable): the optimum's expected tokens per step
+ * Returns SPEC_OK; SPEC_ERR_INVALID_ARG for a bad argument or no feasible
+ * tree; SPEC_ERR_UNSUPPORTED when n > 4096 or the tables (about
+ * min(max_depth, n-1) * (min(K, n-1) + 2) * n entries) pass 16 Mi entries.
+ * ---------------------------------------------------------------------- */
+int spec_sequoia_tree(const double* accept, int K, int n, int max_depth, int32_t* parent, double* expected);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,7 +11,8 @@ include/spectree.h):
 and spec_tree_reject_compact, the last two in one launch; spec_tree_kv_write
 writes the tree's K/V rows into the paged cache (rotated for their tree
 positions) before the attention; spec_tree_truncate applies top-k / top-p to
-the target logits before the sampler.
+the target logits before the sampler; spec_sequoia_tree builds the Sequoia-optimal
+tree shape for a per-rank acceptance vector (host code).
 
 This package is the thin PyTorch binding: tensors in, device pointers and the
 current HIP stream out to the library.
@@ -25,6 +26,7 @@ from .binding import (  # noqa: F401
     header_functions,
     load_library,
     spec_kv_compact,
+    spec_sequoia_tree,
     spec_status_string,
     spec_tree_attn,
     spec_tree_attn_workspace_size,

@@ -40,6 +40,7 @@ _SIGNATURES = {
     "spec_tree_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                             ctypes.c_float, _i, _vp, _vp, _sz, _vp]),
     "spec_tree_reject_workspace_size": (_sz, [_i, _i, _i]),
+    "spec_sequoia_tree": (_i, [ctypes.c_void_p, _i, _i, _i, ctypes.c_void_p, ctypes.c_void_p]),
     "spec_tree_reject_plan": (_i, [_i, _i, _i, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
     "spec_tree_reject_max_resident": (ctypes.c_int64, []),
     "spec_tree_reject": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_uint64,
@@ -341,6 +342,21 @@ def spec_tree_kv_write(k_new, v_new, q, k_cache, v_cache, block_table, prefix_le
                                 block_table.shape[1], nb, float(rope_theta), _dtype_code(k_new),
                                 _stream(k_new.device))
     _check(rc, "spec_tree_kv_write")
+
+
+def spec_sequoia_tree(accept, n, max_depth):
+    """(parent array [n] int32 as a numpy array, expected tokens per step) of the Sequoia-optimal tree of n nodes
+    and depth <= max_depth for a per-rank acceptance vector (host only, no GPU)."""
+    import numpy as np
+
+    acc = np.ascontiguousarray(np.asarray(accept, dtype=np.float64).ravel())
+    parent = np.zeros(int(n), dtype=np.int32)
+    val = ctypes.c_double(0.0)
+    rc = load_library().spec_sequoia_tree(acc.ctypes.data_as(ctypes.c_void_p) if acc.size else None, int(acc.size),
+                                          int(n), int(max_depth), parent.ctypes.data_as(ctypes.c_void_p),
+                                          ctypes.byref(val))
+    _check(rc, "spec_sequoia_tree")
+    return parent, val.value
 
 
 def spec_tree_reject_plan(B, T, V, max_resident_workgroups):

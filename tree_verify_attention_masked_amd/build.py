@@ -3,7 +3,8 @@
     python -m tree_verify_attention_masked_amd.build
 
 Every kernel source under csrc/ is compiled for gfx950 only and linked into
-one shared library next to this file.  Packed-fp32 instruction selection is
+one shared library next to this file, with the host-only C++ (the Sequoia
+tree builder).  Packed-fp32 instruction selection is
 disabled for the device code.
 """
 from __future__ import annotations
@@ -29,7 +30,8 @@ def hipcc() -> str:
 
 
 def sources() -> list:
-    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+    """The kernels and the C ABI (*.hip) and host-only code (*.cpp)."""
+    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")) + glob.glob(os.path.join(PKG, "csrc", "*.cpp")))
 
 
 def build(verbose: bool = False) -> str:
