@@ -66,6 +66,12 @@ SMALL = [
     ("rows64_longest_first", dict(B=64, Hq=32, Hkv=8, D=128, dtype="bf16",
                                   prefix=[9000] + [16 + (37 * i) % 600 for i in range(63)], tree="random", T=16,
                                   max_depth=5, shuffle_blocks=True)),
+    # the persistent kernel (ragged batch, more 64-row items than resident
+    # workgroups) with last splits of 1 to 16 pages, i.e. items of 1 to 4 tiles,
+    # so the issue of tiles waits on the next item's prefetch and runs dry
+    ("rows64_persistent_tiny_items", dict(B=64, Hq=32, Hkv=8, D=128, dtype="bf16",
+                                          prefix=[16000] + [16 * (252 * (i % 3) + 1 + i % 16) - 16 for i in range(63)],
+                                          tree="random", T=16, max_depth=5, shuffle_blocks=True)),
     # fp32 kernel: ancestors past the first 64 lanes' words, GQA over a long and an almost empty prefix
     ("f32_d64_deep_chain", dict(B=1, Hq=2, Hkv=1, D=64, dtype="f32", prefix=[70], tree="chain", gamma=200)),
     ("f32_d128_gqa_tree", dict(B=2, Hq=6, Hkv=2, D=128, dtype="f32", prefix=[1300, 1], tree="random", T=40,
@@ -112,6 +118,27 @@ def test_bad_inputs_are_reported_not_faulted():
     d.attn()
     st = d.status.cpu().numpy()
     assert st[0] & 4 and st[1] & 1 and st[2] & 2
+
+
+def test_bad_inputs_are_reported_on_the_persistent_path():
+    # a batch that takes the persistent kernel: a bad parent row, a block index
+    # outside the pool and a bad prefix length are reported for their sequences,
+    # and every row of every other sequence still matches the oracle
+    w = make_workload(tag=484, B=64, Hq=32, Hkv=8, D=128, dtype="bf16", V=8,
+                      prefix=[9000] + [16 + (37 * i) % 600 for i in range(63)], tree="random", T=16, max_depth=5,
+                      shuffle_blocks=True)
+    d = DevWorkload(w)
+    bad = {3: "parent", 0: "block", 5: "length"}
+    d.parent[3, 7] = 12  # not topological
+    d.block_table[0, 300] = w.num_blocks + 7  # a page inside sequence 0's third split
+    d.prefix_lens[5] = -4
+    out = attn_to_f64(w, d.attn())
+    st = d.status.cpu().numpy()
+    assert st[3] & 1 and st[0] & 2 and st[5] & 4
+    assert all(st[b] == 0 for b in range(w.B) if b not in bad)
+    ref, ref_abs = oracle_attn(w)
+    keep = [b for b in range(w.B) if b not in bad]
+    assert_attn_close(out[keep], ref[keep], w.dtype, "persistent, good sequences", ref_abs[keep])
 
 
 def test_bad_inputs_are_reported_not_faulted_f32():

@@ -156,9 +156,10 @@ struct TArgs2 {
   int32_t* status;
   float* part_o;       // [items][RT][D]
   float* part_ml;      // [items][RT][2]
-  unsigned* counters;  // [B * Hkv * n_rt]
+  unsigned* counters;  // [B * Hkv * n_rt], then the item queue's [next id, workgroups done]
   int B, T, Hq, Hkv, G, R, n_rt, splits, pps, max_blocks, num_blocks;
   int reorder;  // longest items first (one row tile, B <= 64)
+  int persist;  // reorder, with each workgroup taking items from a queue until none is left
   long items;
   float sl2;
 };
@@ -195,73 +196,30 @@ __device__ int build_ancestors_lds(const int* par, int T, uint64_t* anc) {
 }
 
 template <int NRB>
-__global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const TArgs2 a) {
-  constexpr int RT = 64 * NRB;  // rows per workgroup
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[2 * kTileBytes];  // 2 x (4 K pages, 4 V pages)
-  __shared__ uint64_t anc[kMaxT * 4];
-  __shared__ int s_par[kMaxT];
-  __shared__ int s_blk[kMaxSplitPages];
-  __shared__ int s_last;
+struct TileLds {
+  __attribute__((aligned(16))) uint8_t tiles[2 * kTileBytes];  // 2 x (4 K pages, 4 V pages)
+  uint64_t anc[kMaxT * 4];
+  int s_par[kMaxT];
+  int s_blk[kMaxSplitPages];
+  int s_last, s_next;
+};
 
+// The work of one item (b, g, KV split, row tile), sequence b's prefix length
+// already clamped to its valid range (err: SPEC_DEV_LENGTH if it was not).
+// Every thread of the workgroup calls it; it returns at points the whole
+// workgroup reaches together, or after its merge.
+template <int NRB>
+__device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, int Lb, int err, TileLds<NRB>& L) {
+  constexpr int RT = 64 * NRB;  // rows per workgroup
+  uint8_t* tiles = L.tiles;
+  uint64_t* anc = L.anc;
+  int* s_par = L.s_par;
+  int* s_blk = L.s_blk;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int quad = lane >> 4;
-
-  long item;
-  bool reorder = false;
-  if constexpr (NRB == 1) reorder = a.reorder != 0;  // (the 128-row kernel is at its register limit)
-  if (reorder) {
-    // Ragged batch, one row tile, more items than resident workgroups: the
-    // longest items go first, so the short ones fill the tail.  Workgroup ids
-    // are taken in dispatch order: first every full split (pps pages) of every
-    // (b, g), then each (b, g)'s last split by decreasing length (ties: lower
-    // b), then ids that exit at once.  Lane b of each wave holds sequence b.
-    const int lane = tid & 63;
-    int lb = lane < a.B ? a.plen[lane] : 0;
-    const int cap = a.max_blocks * kBlockSize - a.T;
-    lb = lb < 0 ? 0 : (lb > cap ? cap : lb);
-    const int np = (lb + a.T + kBlockSize - 1) / kBlockSize;
-    const int nu = lane < a.B ? (np + a.pps - 1) / a.pps : 0;
-    const int full = lane < a.B ? (nu - 1) * a.Hkv : 0;
-    const int last = lane < a.B ? np - (nu - 1) * a.pps : -1;
-    int incl = full;  // inclusive prefix sum over sequences
-#pragma unroll
-    for (int w = 1; w < 64; w <<= 1) {
-      const int o = __shfl_up(incl, w);
-      if (lane >= w) incl += o;
-    }
-    const int F = __shfl(incl, 63);
-    const int id = static_cast<int>(blockIdx.x);
-    int b, g, s;
-    if (id < F) {
-      b = __ffsll(static_cast<long long>(__ballot(incl > id))) - 1;
-      const int k = id - (__shfl(incl, b) - __shfl(full, b));
-      const int ns = __shfl(nu, b) - 1;
-      g = k / ns;
-      s = k % ns;
-    } else if (id - F < a.B * a.Hkv) {
-      const int j = id - F, rank = j / a.Hkv;
-      g = j % a.Hkv;
-      int my_rank = 0;  // lanes before this one in the order of last splits
-      for (int o = 0; o < a.B; ++o) {
-        const int lo = __shfl(last, o);
-        my_rank += (lo > last || (lo == last && o < lane)) ? 1 : 0;
-      }
-      b = __ffsll(static_cast<long long>(__ballot(lane < a.B && my_rank == rank))) - 1;
-      s = __shfl(nu, b) - 1;
-    } else {
-      return;
-    }
-    item = (static_cast<long>(b) * a.Hkv + g) * a.splits + s;  // one row tile
-  } else {
-    // Consecutive workgroup ids are dealt round-robin to the 8 XCDs; give each
-    // XCD a contiguous run of items so the row tiles of one KV chunk share an L2.
-    const long per = (a.items + 7) / 8;
-    item = static_cast<long>(blockIdx.x % 8) * per + blockIdx.x / 8;
-  }
-  if (item >= a.items) return;
   const int rt = static_cast<int>(item % a.n_rt);
   long rest = item / a.n_rt;
   const int s = static_cast<int>(rest % a.splits);
@@ -270,13 +228,6 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
   const int b = static_cast<int>(rest / a.Hkv);
   const long bgr = (static_cast<long>(b) * a.Hkv + g) * a.n_rt + rt;
 
-  int err = 0;
-  int Lb = a.plen[b];
-  const int cap = a.max_blocks * kBlockSize - a.T;
-  if (Lb < 0 || Lb > cap) {
-    err |= SPEC_DEV_LENGTH;
-    Lb = Lb < 0 ? 0 : cap;
-  }
   const int n_keys = Lb + a.T;
   const int npages = (n_keys + kBlockSize - 1) / kBlockSize;
   const int n_used = (npages + a.pps - 1) / a.pps;  // splits of this (b, g) that hold keys
@@ -287,7 +238,10 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
   const int n_it = p1 > p0 ? (p1 - p0 + 3) / 4 : 0;
   const bool tail = n_it > 0 && kend > Lb;
 
-  // the split's block indices and the parent row, staged once in LDS
+  // The split's block indices and the parent row are staged once in LDS, the
+  // query fragments loaded beside them (one memory latency for all three); the
+  // first tile is issued as soon as the indices are in, and the ancestor sets
+  // are built while it lands.
   const int32_t* bt_b = a.bt + static_cast<long>(b) * a.max_blocks;
   for (int i = tid; i < p1 - p0; i += 256) {
     const int blk = bt_b[p0 + i];
@@ -297,8 +251,6 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
   }
   if (tail)
     for (int i = tid; i < a.T; i += 256) s_par[i] = a.parent[static_cast<long>(b) * a.T + i];
-  __syncthreads();
-  if (tail) err |= build_ancestors_lds(s_par, a.T, anc);
 
   // query fragments (B operand of S^T): Q[row][c*32 + quad*8 .. +7]
   const int row_base = rt * RT + wave * NRB * 16;
@@ -364,8 +316,9 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
       vt_off[dt] = vkey * 256 + (((2 * dt + ((l16 & 3) >> 1)) ^ (2 * (vkey & 7))) * 16) + (l16 & 1) * 8;
   }
 
-  __syncthreads();  // s_blk and anc are ready
+  __syncthreads();  // s_blk and s_par are ready
   if (n_it > 0) issue_tile(0);
+  if (tail) err |= build_ancestors_lds(s_par, a.T, anc);  // read after the loop's first barrier
 
   for (int it = 0; it < n_it; ++it) {
     wait_vm0();  // this wave's page of tile `it` has landed
@@ -522,10 +475,10 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
   __syncthreads();
   if (tid == 0) {
     const unsigned prev = __hip_atomic_fetch_add(&a.counters[bgr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == static_cast<unsigned>(n_used - 1));
+    L.s_last = (prev == static_cast<unsigned>(n_used - 1));
   }
   __syncthreads();
-  if (!s_last) return;
+  if (!L.s_last) return;
 
   // The last workgroup of (b, g, rt) merges every split: wave w takes the 16-row
   // blocks w, w+4, ..., each lane the elements it would hold in the accumulator
@@ -584,6 +537,149 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
   if (tid == 0) __hip_atomic_store(&a.counters[bgr], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Per-sequence quantities of the longest-first item order, lane b of every
+// wave holding sequence b (B <= 64): clamped prefix length, pages, splits that
+// hold keys, full splits over its kv heads, their running sum, the rank of its
+// last split (longer first, ties lower b), the prefix-length error bit.
+struct SeqTable {
+  int lb, np, nu, full, incl, rank, errlen;
+  int F, limit;  // full splits of the batch; ids that name an item
+};
+
+__device__ __forceinline__ SeqTable seq_table(const TArgs2& a) {
+  const int lane = threadIdx.x & 63;
+  SeqTable t;
+  const bool in = lane < a.B;
+  const int raw = in ? a.plen[lane] : 0;
+  const int cap = a.max_blocks * kBlockSize - a.T;
+  t.errlen = (in && (raw < 0 || raw > cap)) ? SPEC_DEV_LENGTH : 0;
+  t.lb = raw < 0 ? 0 : (raw > cap ? cap : raw);
+  t.np = in ? (t.lb + a.T + kBlockSize - 1) / kBlockSize : 0;
+  t.nu = in ? (t.np + a.pps - 1) / a.pps : 0;
+  t.full = in ? (t.nu - 1) * a.Hkv : 0;
+  const int last = in ? t.np - (t.nu - 1) * a.pps : -1;
+  int incl = t.full;
+#pragma unroll
+  for (int w = 1; w < 64; w <<= 1) {
+    const int o = __shfl_up(incl, w);
+    if (lane >= w) incl += o;
+  }
+  t.incl = incl;
+  t.F = __shfl(incl, 63);
+  int rank = 0;
+  for (int o = 0; o < a.B; ++o) {  // lane o's value through a scalar register: no LDS round trip per step
+    const int lo = __builtin_amdgcn_readlane(last, o);
+    rank += (lo > last || (lo == last && o < lane)) ? 1 : 0;
+  }
+  t.rank = rank;
+  t.limit = t.F + a.B * a.Hkv;
+  return t;
+}
+
+// Item of id v < t.limit in the longest-first order: every full split (pps
+// pages) of every (b, g) in sequence order, then each (b, g)'s last split by
+// decreasing length.  Returns the item and sets b's clamped prefix length and
+// error bit.
+__device__ __forceinline__ long seq_item(const TArgs2& a, const SeqTable& t, int v, int* Lb, int* err) {
+  const int lane = threadIdx.x & 63;
+  int b, g, s;
+  if (v < t.F) {
+    b = __ffsll(static_cast<long long>(__ballot(t.incl > v))) - 1;
+    const int k = v - (__shfl(t.incl, b) - __shfl(t.full, b));
+    const int ns = __shfl(t.nu, b) - 1;
+    g = k / ns;
+    s = k % ns;
+  } else {
+    const int j = v - t.F, rank = j / a.Hkv;
+    g = j % a.Hkv;
+    b = __ffsll(static_cast<long long>(__ballot(lane < a.B && t.rank == rank))) - 1;
+    s = __shfl(t.nu, b) - 1;
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  *Lb = __builtin_amdgcn_readfirstlane(__shfl(t.lb, b));
+  *err = __builtin_amdgcn_readfirstlane(__shfl(t.errlen, b));
+  return (static_cast<long>(b) * a.Hkv + __builtin_amdgcn_readfirstlane(g)) * a.splits +
+         __builtin_amdgcn_readfirstlane(s);
+}
+
+template <int NRB>
+__global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const TArgs2 a) {
+  __shared__ TileLds<NRB> L;
+  const int tid = threadIdx.x;
+  bool reorder = false;
+  if constexpr (NRB == 1) reorder = a.reorder != 0;  // (the 128-row kernel is at its register limit)
+  if (reorder && a.persist) {
+    // Items from a queue: workgroup w starts with item w of the longest-first
+    // order, then takes the next unclaimed one (an atomic counter in the
+    // workspace) until none is left, so that a CU -- or a whole XCD -- that
+    // runs faster takes more items (each XCD otherwise gets a fixed share of
+    // the workgroup ids, and the slowest sets the end).  The next id is
+    // claimed while the current item runs.  The last workgroup to leave
+    // resets the queue for the next call.
+    const SeqTable t = seq_table(a);
+    unsigned* queue = a.counters + static_cast<long>(a.B) * a.Hkv * a.n_rt;  // [next id, workgroups done]
+    const int G = static_cast<int>(gridDim.x);
+    int v = static_cast<int>(blockIdx.x);
+    while (v < t.limit) {
+      unsigned nxt = 0;
+      if (tid == 0) nxt = __hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int Lb, err;
+      const long item = seq_item(a, t, v, &Lb, &err);
+      tile_item_run<NRB>(a, item, Lb, err, L);
+      if (tid == 0) L.s_next = G + static_cast<int>(nxt);
+      __syncthreads();  // every wave is done with the item's LDS; the next id is published
+      v = L.s_next;
+      __syncthreads();  // s_next is rewritten only after every wave has read it
+    }
+    if (tid == 0) {
+      const unsigned prev = __hip_atomic_fetch_add(queue + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == static_cast<unsigned>(G - 1)) {  // every workgroup has claimed past the end: reset
+        __hip_atomic_store(queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    return;
+  }
+  long item;
+  int Lb, err = 0;
+  if (reorder) {
+    // Ragged batch, one row tile, more items than resident workgroups: the
+    // longest items go first (workgroup ids taken in dispatch order), so the
+    // short ones fill the tail.
+    const SeqTable t = seq_table(a);
+    if (static_cast<int>(blockIdx.x) >= t.limit) return;
+    item = seq_item(a, t, static_cast<int>(blockIdx.x), &Lb, &err);
+  } else {
+    // Consecutive workgroup ids are dealt round-robin to the 8 XCDs; give each
+    // XCD a contiguous run of items so the row tiles of one KV chunk share an L2.
+    const long per = (a.items + 7) / 8;
+    item = static_cast<long>(blockIdx.x % 8) * per + blockIdx.x / 8;
+    if (item >= a.items) return;
+    Lb = a.plen[item / a.n_rt / a.splits / a.Hkv];
+    const int cap = a.max_blocks * kBlockSize - a.T;
+    if (Lb < 0 || Lb > cap) {
+      err |= SPEC_DEV_LENGTH;
+      Lb = Lb < 0 ? 0 : cap;
+    }
+  }
+  tile_item_run<NRB>(a, item, Lb, err, L);
+}
+
+// Workgroups of attn_tile_kernel<1> the current device holds at once (its
+// occupancy per CU times the CU count), queried once per device.
+long tile_capacity() {
+  static long cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_tile_kernel<1>, 256, 0) != hipSuccess) return 0;
+  const long cap = static_cast<long>(cus) * per_cu;
+  if (dev < 64) cache[dev] = cap;
+  return cap;
+}
+
 template <int NRB>
 hipError_t run_tile(const TArgs2& args, hipStream_t stream) {
   const long grid = ((args.items + 7) / 8) * 8;
@@ -640,7 +736,7 @@ AttnPlan plan_attn(int B, int T, int Hq, int Hkv, int D, int max_blocks, int dty
   p.pps = static_cast<int>(pps);
   p.splits = static_cast<int>(splits);
   p.items = base * p.splits;
-  const size_t head = (static_cast<size_t>(base) * sizeof(unsigned) + 255) / 256 * 256;
+  const size_t head = (static_cast<size_t>(base + 2) * sizeof(unsigned) + 255) / 256 * 256;  // + the item queue
   p.ws_bytes = p.splits > 1 ? head + static_cast<size_t>(p.items) * p.rt * (kD + 2) * sizeof(float) : 0;
   return p;
 }
@@ -672,12 +768,23 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& L, hipStream
   a.sl2 = L.scale * kLog2e;
   if (plan.splits > 1) {
     const size_t base = static_cast<size_t>(L.B) * L.Hkv * plan.n_rt;
-    const size_t head = (base * sizeof(unsigned) + 255) / 256 * 256;
+    const size_t head = (static_cast<size_t>(base + 2) * sizeof(unsigned) + 255) / 256 * 256;
     a.counters = static_cast<unsigned*>(L.workspace);
     a.part_o = reinterpret_cast<float*>(static_cast<char*>(L.workspace) + head);
     a.part_ml = a.part_o + static_cast<size_t>(plan.items) * plan.rt * kD;
   }
-  if (plan.nrb == 1) return run_tile<1>(a, stream);
+  if (plan.nrb == 1) {
+    if (plan.reorder && plan.splits > 1) {  // the queue of items: one round of resident workgroups
+      const long cap = tile_capacity();
+      if (cap > 0) {
+        a.persist = 1;
+        const long grid = std::min<long>(cap, plan.items);
+        hipLaunchKernelGGL((attn_tile_kernel<1>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
+        return hipGetLastError();
+      }
+    }
+    return run_tile<1>(a, stream);
+  }
   return run_tile<2>(a, stream);
 }
 
