@@ -36,7 +36,7 @@ rows over the step time).  `roofline.traffic` comes from the committed
 rocprofv3 counter summary (profiles/pmc_<workload>.md, FETCH_SIZE and
 WRITE_SIZE per dispatch, scaled by what the same counters read for a plain
 1 GiB device copy); it is null when that summary was taken from other kernel
-sources than the ones built now.  `--summarize trace|pmc DIR...` turns
+sources than the ones built now.  `--summarize trace|pmc|sq DIR...` turns
 rocprofv3 CSV output into those summaries (host only, no GPU).
 """
 from __future__ import annotations
@@ -73,11 +73,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
-    """sha256 over the HIP sources and headers the library is built from."""
+KERNEL_SOURCES = {  # the sources each kernel key is built from (with common.h and the C-ABI header)
+    "tree_attn": ("attn_bf16.hip", "attn_stream.hip", "attn_f32.hip"),
+    "tree_reject_compact": ("reject.hip", "compact_dev.h"),
+    "kv_compact": ("compact.hip", "compact_dev.h"),
+    "tree_kv_write": ("kv_write.hip",),
+    "tree_truncate": ("truncate.hip",),
+}
+
+
+def kernel_source_hash(kernel=None):
+    """sha256 over the HIP sources and headers the library is built from (or those of one kernel key)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tree_verify_attention_masked_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*"))) + [os.path.join(ROOT, "include", "spectree.h")]:
+    if kernel is None:
+        files = sorted(glob.glob(os.path.join(csrc, "*")))
+    else:
+        files = [os.path.join(csrc, f) for f in sorted(KERNEL_SOURCES[kernel] + ("common.h",))]
+    for f in files + [os.path.join(ROOT, "include", "spectree.h")]:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
@@ -113,6 +126,8 @@ def summarize(kind, dirs, workload):
             out.append(f"| `{name[:90]}` | {r.get('Calls')} | {avg:.2f} | {float(r.get('TotalDurationNs', 0)) / 1e3:.1f} | "
                        f"{float(r.get('Percentage', 0)):.1f}% |")
         return "\n".join(out)
+    if kind == "sq":
+        return summarize_sq(dirs, workload)
     # pmc: dirs = [fetch_dir, write_dir]
     per = {}
     calib = {}  # counter -> [(dispatch id, KiB)] of the calibration copies, in dispatch order
@@ -143,7 +158,8 @@ def summarize(kind, dirs, workload):
         wv = float(np.mean(cs.get("WRITE_SIZE", [0.0])))
         ff, fw = factors.get("FETCH_SIZE") or 1.0, factors.get("WRITE_SIZE") or 1.0
         traffic = f * 1024 / ff + wv * 1024 / fw
-        res["kernels"][k] = {"fetch_kib": round(f, 1), "write_kib": round(wv, 1), "traffic_bytes": int(traffic)}
+        res["kernels"][k] = {"fetch_kib": round(f, 1), "write_kib": round(wv, 1), "traffic_bytes": int(traffic),
+                             "source_sha256": kernel_source_hash(k)}
         out.append(f"| {k} | {len(cs.get('FETCH_SIZE', []))} | {f:.1f} | {wv:.1f} | {traffic / 1e6:.3f} MB |")
     out.append("")
     out.append(f"Calibration (plain device copies; counter KiB x 1024 / bytes copied): {json.dumps(by_size)}; "
@@ -156,8 +172,55 @@ def summarize(kind, dirs, workload):
     return "\n".join(out)
 
 
+SIMDS = 1024  # MI355X: 256 compute units x 4 SIMDs
+DIES = 8  # accelerator dies (XCDs); GRBM_GUI_ACTIVE counts on each
+
+
+def summarize_sq(dirs, workload):
+    """Markdown summary of rocprofv3 --pmc runs of SQ / GRBM counters: per kernel, each counter
+    summed over its instances (shader engines, dies) per dispatch -- rocprofv3's CSV already holds
+    that sum -- and averaged over dispatches, with MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (kernel
+    cycles x SIMDs), the kernel's cycles being GRBM_GUI_ACTIVE per die (its sum over the dies / 8:
+    rocprofv3's own MFMA-utilisation expression takes the largest die), and wait = SQ_WAIT_ANY /
+    SQ_WAVE_CYCLES (wave cycles spent waiting on a counter or a dependency)."""
+    per = {}  # kernel key -> counter -> [per-dispatch value]
+    for d in dirs:
+        disp = {}
+        for r in read_csvs(d, "counter_collection.csv"):
+            k = kernel_key(r.get("Kernel_Name", ""))
+            if not k:
+                continue
+            c = r.get("Counter_Name")
+            key = (k, c, int(r.get("Dispatch_Id", 0)))
+            v = float(r.get("Counter_Value", 0))
+            disp[key] = disp.get(key, 0.0) + v
+        for (k, c, _), v in disp.items():
+            per.setdefault(k, {}).setdefault(c, []).append(v)
+    res = {"workload": workload, "kernels": {}}
+    out = ["| kernel | counter | dispatches | mean per dispatch |", "|---|---|---|---|"]
+    for k, cs in sorted(per.items()):
+        means = {c: float(np.mean(v)) for c, v in cs.items()}
+        for c in sorted(means):
+            out.append(f"| {k} | {c} | {len(cs[c])} | {means[c]:.4g} |")
+        derived = {}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in means and means.get("GRBM_GUI_ACTIVE"):
+            derived["kernel_cycles"] = means["GRBM_GUI_ACTIVE"] / DIES
+            derived["mfma_busy"] = means["SQ_VALU_MFMA_BUSY_CYCLES"] / (derived["kernel_cycles"] * SIMDS)
+        if "SQ_WAIT_ANY" in means and means.get("SQ_WAVE_CYCLES"):
+            derived["wait_any"] = means["SQ_WAIT_ANY"] / means["SQ_WAVE_CYCLES"]
+        if "SQ_WAIT_INST_ANY" in means and means.get("SQ_WAVE_CYCLES"):
+            derived["wait_inst_issue"] = means["SQ_WAIT_INST_ANY"] / means["SQ_WAVE_CYCLES"]
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in means:
+            derived["bf16_mfma_flops"] = means["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        res["kernels"][k] = {"means": {c: round(v, 1) for c, v in means.items()},
+                             "derived": {c: round(v, 4) for c, v in derived.items()},
+                             "source_sha256": kernel_source_hash(k)}
+    out += ["", "```json", json.dumps(res), "```"]
+    return "\n".join(out)
+
+
 def committed_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from profiles/pmc_<workload>.md, if taken from the current sources."""
+    """HBM bytes per launch of `kernel` from profiles/pmc_<workload>.md, if taken from that kernel's current sources."""
     f = os.path.join(ROOT, "profiles", f"pmc_{workload}.md")
     if not os.path.exists(f):
         return None
@@ -165,10 +228,10 @@ def committed_traffic(workload, kernel):
     if not m:
         return None
     d = json.loads(m.group(1))
-    if d.get("source_sha256") != kernel_source_hash():
-        return None
     k = d.get("kernels", {}).get(kernel)
-    return int(k["traffic_bytes"]) if k else None
+    if not k or k.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    return int(k["traffic_bytes"])
 
 
 def depths(parent_row):
@@ -547,7 +610,7 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="run plain 256 MiB and 1 GiB device copies (counter calibration)")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
-                    help="trace DIR | pmc FETCH_DIR WRITE_DIR: print a markdown summary of rocprofv3 output")
+                    help="trace DIR | pmc FETCH_DIR WRITE_DIR | sq DIR...: print a markdown summary of rocprofv3 output")
     ap.add_argument("--workload-name", default="batched_serving", help="workload name recorded by --summarize pmc")
     ap.add_argument("--sweep", action="store_true", help="verify cost against tree size and prefix length (one GPU)")
     args = ap.parse_args()
