@@ -54,7 +54,7 @@ extern "C" {
 typedef enum {
   SPEC_OK = 0,
   SPEC_ERR_INVALID_ARG = -1, /* null pointer, non-positive or inconsistent size */
-  SPEC_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype, D, block size, T > 256) */
+  SPEC_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype, D, block size, T > 512) */
   SPEC_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than the *_workspace_size */
   SPEC_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
 } spec_status;
@@ -116,7 +116,7 @@ int spec_version(void);
  *                before a call with another shape (or keep one per shape).
  *                Calls that overlap in time must not share a workspace.
  * Supported: dtype SPEC_BF16 with D = 128, dtype SPEC_F32 with D in {64, 128};
- * block_size = 16; 1 <= T <= 256; Hq % Hkv == 0.  B == 0 is a no-op.
+ * block_size = 16; 1 <= T <= 512; Hq % Hkv == 0.  B == 0 is a no-op.
  * ---------------------------------------------------------------------- */
 size_t spec_tree_attn_workspace_size(int B, int T, int Hq, int Hkv, int D,
                                      int max_blocks_per_seq, int dtype);
@@ -182,7 +182,7 @@ int spec_tree_attn(const void* q, const void* k_cache, const void* v_cache,
  * of a team alone writes the sequence's outputs (and, in
  * spec_tree_reject_compact, moves its KV rows), so they are always one
  * consistent result.
- * Supported: 1 <= T <= 256, 1 <= V <= 262144, temperature >= 0 and finite.
+ * Supported: 1 <= T <= 512, 1 <= V <= 262144, temperature >= 0 and finite.
  * ---------------------------------------------------------------------- */
 size_t spec_tree_reject_workspace_size(int B, int T, int V);
 

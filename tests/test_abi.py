@@ -61,7 +61,7 @@ def test_attn_host_validation(lib):
     assert _attn(lib, D=64) == -2  # bf16 needs D = 128
     assert _attn(lib, dtype=0, D=96) == -2
     assert _attn(lib, bs=8) == -2
-    assert _attn(lib, T=300, mb=40) == -2
+    assert _attn(lib, T=513, mb=40) == -2
     assert _attn(lib, mb=0) == -1
     assert _attn(lib, T=200, mb=8) == -1  # the table cannot even hold the tree
     assert _attn(lib, scale=float("nan")) == -1
@@ -84,7 +84,7 @@ def test_reject_host_validation(lib):
     assert _reject(lib, tau=-1.0) == -1
     assert _reject(lib, tau=float("inf")) == -1
     assert _reject(lib, T=0) == -1
-    assert _reject(lib, T=257) == -2
+    assert _reject(lib, T=513) == -2
     assert _reject(lib, V=300000) == -2
     assert _reject(lib, ws=None) == -3
     assert _reject(lib, wsz=10) == -3
@@ -113,7 +113,7 @@ def test_reject_compact_host_validation(lib):
                                             FAKE, FAKE, FAKE, None, a["ws"], a["wsz"], a["k"], FAKE, FAKE, FAKE,
                                             None, a["Hkv"], a["D"], a["bs"], a["mb"], a["nb"], a["dtype"], None)
     assert call(tau=-1.0) == -1     # the sampler's checks
-    assert call(T=257) == -2
+    assert call(T=513) == -2
     assert call(wsz=10) == -3
     assert call(k=None) == -1       # the compaction's checks
     assert call(D=32) == -2
@@ -138,7 +138,7 @@ def test_kv_write_host_validation(lib):
     assert call(theta=float("inf")) == -1
     assert call(D=64) == -2            # bf16 needs D = 128
     assert call(bs=8) == -2
-    assert call(T=300, mb=40) == -2
+    assert call(T=513, mb=40) == -2
     assert call(T=100, mb=4) == -1     # the table cannot hold the tree
     assert call(B=0) == 0
     assert call(B=0, q=None, Hq=0) == 0  # no queries to rotate
@@ -198,4 +198,4 @@ def test_reject_team_plan_fits_the_resident_grid(lib):
     with pytest.raises(stv.SpecError):
         stv.spec_tree_reject_plan(1, 5, 32000, 0)
     with pytest.raises(stv.SpecError):
-        stv.spec_tree_reject_plan(1, 257, 32000, 256)
+        stv.spec_tree_reject_plan(1, 513, 32000, 256)

@@ -76,6 +76,15 @@ SMALL = [
     ("f32_d64_deep_chain", dict(B=1, Hq=2, Hkv=1, D=64, dtype="f32", prefix=[70], tree="chain", gamma=200)),
     ("f32_d128_gqa_tree", dict(B=2, Hq=6, Hkv=2, D=128, dtype="f32", prefix=[1300, 1], tree="random", T=40,
                                max_depth=7, shuffle_blocks=True)),
+    # trees of more than 256 nodes: ancestor bitsets of up to 8 words, each item
+    # keeping only its own nodes' (32 nodes per 128-row item at 4 query heads per
+    # kv head; 128 for the chain, one head); tree keys in several 64-key tiles
+    ("rows_t300_sequoia", dict(B=1, Hq=8, Hkv=2, D=128, dtype="bf16", prefix=[700], tree="sequoia", T=300,
+                               max_depth=12, shuffle_blocks=True)),
+    ("rows_t512_tree_ragged", dict(B=2, Hq=4, Hkv=2, D=128, dtype="bf16", prefix=[0, 1500], tree="random", T=512,
+                                   max_depth=9)),
+    ("deep_chain_t512", dict(B=1, Hq=1, Hkv=1, D=128, dtype="bf16", prefix=[40], tree="chain", gamma=511)),
+    ("f32_t300_tree", dict(B=1, Hq=2, Hkv=1, D=64, dtype="f32", prefix=[33], tree="random", T=300, max_depth=20)),
 ]
 
 

@@ -130,3 +130,52 @@ def test_fused_reject_compact_equals_separate_calls(cfg):
     assert torch.equal(_bits(sep.k), _bits(fus.k)) and torch.equal(_bits(sep.v), _bits(fus.v))
     moved = int((acc1[:, 1:] != torch.arange(1, w.T, device=acc1.device)).logical_and(acc1[:, 1:] >= 0).sum())
     print(f"[fused] config {cfg}: accepted {n1.tolist()[:8]}, rows off their place {moved}", flush=True)
+
+
+def _caterpillar(n_spine):
+    """Spine nodes 0, 2, 4, ...: node 2k has the leaf 2k + 1, then the next spine node 2k + 2."""
+    parent = [-1]
+    for k in range(n_spine - 1):
+        parent += [2 * k, 2 * k]
+    return parent
+
+
+def test_random_paths_of_a_512_node_tree():
+    w = make_workload(tag=630, B=3, Hq=4, Hkv=2, D=128, dtype="bf16", V=8, prefix=[0, 40, 1000], tree="random",
+                      T=512, max_depth=12, shuffle_blocks=True)
+    _check(w, *_paths_for(w, np.random.default_rng(6)))
+
+
+def test_deep_path_of_a_511_node_tree():
+    """Greedy verification of a caterpillar whose spine tokens are the target's argmax:
+    the path is the 256-node spine, so 255 rows move; the fused call, the separate
+    calls and the oracle agree on the path and on the whole cache."""
+    parent = _caterpillar(256)
+    w = make_workload(tag=631, B=2, Hq=2, Hkv=2, D=128, dtype="bf16", V=16, prefix=[3, 77], tree="fixed",
+                      parent=parent, temperature=0.0)
+    T = len(parent)
+    for b in range(w.B):
+        for k in range(255):
+            top = int(np.argmax(w.target_logits[b, 2 * k]))
+            w.draft_tokens[b, 2 * k + 1] = (top + 1) % w.V  # the leaf, tried first, is rejected
+            w.draft_tokens[b, 2 * k + 2] = top
+    ref = oracle_reject(w)
+    assert ref["num_accepted"].tolist() == [255, 255]
+    k_ref, v_ref, lens_ref = oracle.kv_compact(w.k_cache, w.v_cache, w.block_table, w.prefix_lens,
+                                               ref["accepted_nodes"], ref["num_accepted"])
+    sep, fus = DevWorkload(w), DevWorkload(w)
+    acc1, toks1, n1 = sep.reject()
+    lens1 = sep.compact(acc1, n1)
+    acc2, toks2, n2, lens2 = stv.spec_tree_reject_compact(
+        fus.logits, fus.probs, fus.tokens, fus.parent, w.temperature, fus.k, fus.v, fus.block_table,
+        fus.prefix_lens, w.without_replacement, w.seed, w.offset, status=fus.status)
+    torch.cuda.synchronize()
+    assert compare_reject((acc1, toks1, n1), ref) == 0
+    for x, y, what in ((acc1, acc2, "accepted_nodes"), (toks1, toks2, "out_tokens"), (n1, n2, "num_accepted"),
+                       (lens1, lens2, "new_lens")):
+        assert torch.equal(x, y), what
+    for d in (sep, fus):
+        assert np.array_equal(host_kv(w, d.k).view(np.uint8), k_ref.view(np.uint8))
+        assert np.array_equal(host_kv(w, d.v).view(np.uint8), v_ref.view(np.uint8))
+        assert int(d.status.abs().sum()) == 0
+    assert np.array_equal(lens1.cpu().numpy(), lens_ref) and T == 511

@@ -83,6 +83,11 @@ CASES = [
      10000.0),
     ("bf16_unrotated", dict(B=2, Hq=4, Hkv=2, D=128, dtype="bf16", prefix=[16, 31], tree="random", T=9,
                             max_depth=3), 0.0),
+    # more than 256 nodes: two nodes per thread in the depth doubling
+    ("bf16_tree_t512", dict(B=2, Hq=4, Hkv=2, D=128, dtype="bf16", prefix=[5, 300], tree="random", T=512,
+                            max_depth=9, shuffle_blocks=True), 10000.0),
+    ("f32_deep_chain_t300", dict(B=1, Hq=2, Hkv=1, D=64, dtype="f32", prefix=[21], tree="chain", gamma=299),
+     10000.0),
 ]
 
 

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import tree_verify_attention_masked_amd as stv
 from helpers import DevWorkload, compare_reject, flag_cap, oracle_reject
 from workloads import make_config, make_workload
 
@@ -128,3 +129,32 @@ def test_statistics_single_child_acceptance_rate():
         _, _, nacc = d.reject(offset=off)
         acc += int(nacc.item())
     assert abs(acc / n - beta) < 4 * np.sqrt(beta * (1 - beta) / n)
+
+
+# Trees of more than 256 nodes (the sampler kernel with 512-node arrays, two
+# nodes per thread, half the eager space): a 512-node random tree at a small
+# vocabulary (frequent rejections, sibling residuals), a 300-node Sequoia-profile
+# tree drafted and verified without replacement, and a batch whose slices are
+# too long for the halved eager space but fit the current-row buffer (64
+# sequences, 4 members each, 4100-entry slices: no eager rows).
+def test_tree_of_512_nodes():
+    w = make_workload(tag=560, B=2, Hq=2, Hkv=2, D=64, dtype="f32", V=50, prefix=[4, 4], tree="random", T=512,
+                      max_depth=9, temperature=0.9, with_kv=False)
+    print(f"[reject] T=512 depth {w.info['depth']}", flush=True)
+    _many_offsets(w, range(20))
+
+
+def test_tree_of_300_nodes_without_replacement():
+    w = make_workload(tag=561, B=2, Hq=2, Hkv=2, D=64, dtype="f32", V=100, prefix=[4, 4], tree="sequoia", T=300,
+                      max_depth=12, draft_mode="without_replacement", temperature=0.6, without_replacement=True,
+                      with_kv=False)
+    print(f"[reject] T=300 sequoia widths {w.info['width_profile']}", flush=True)
+    _many_offsets(w, range(20))
+
+
+def test_large_tree_without_eager_rows():
+    w = make_workload(tag=562, B=64, Hq=2, Hkv=2, D=64, dtype="f32", V=16400, prefix=[4] * 64, tree="random",
+                      T=260, max_depth=6, temperature=1.0, with_kv=False)
+    assert stv.spec_tree_reject_plan(64, 260, 16400, 1 << 20) == (4, 4100)
+    print("[reject] B=64 T=260 V=16400", flush=True)
+    _many_offsets(w, range(2))

@@ -164,33 +164,57 @@ struct TArgs2 {
   float sl2;
 };
 
-// Ancestor-or-self bitsets (4 x 64 bits per node) from the LDS copy of a parent
-// row.  A node whose parent chain is not topological keeps only itself.
-__device__ int build_ancestors_lds(const int* par, int T, uint64_t* anc) {
+constexpr int kAncWords = kMaxT / 64;  // words of one node's ancestor-or-self bitset
+
+// Ancestor-or-self bitsets of every node of a parent row, by pointer doubling:
+// anc[i] holds the path from i up to, not including, jump[i] (at first {i} and
+// i's parent); each round joins the set of jump[i] and takes over its jump, so
+// ceil(log2(depth + 1)) rounds cover every path.  A node whose parent is not
+// an earlier node (or the root's is not -1) ends its path there.  `jump` is
+// the parent row (overwritten); `anc` holds T x kAncWords words.  Every thread
+// of the 256-thread workgroup calls it (T <= 512).
+__device__ int build_ancestors_lds(int* jump, int T, uint64_t* anc) {
+  const int tid = threadIdx.x;
+  const int nw = (T + 63) >> 6;
   int err = 0;
-  for (int i = threadIdx.x; i < T; i += blockDim.x) {
-    uint64_t w[4] = {0, 0, 0, 0};
-    int j = i;
-    bool ok = true;
-    for (int steps = 0; steps <= T; ++steps) {
-      w[j >> 6] |= 1ull << (j & 63);
-      const int p = par[j];
-      if (j == 0) {
-        ok = (p == -1);
-        break;
-      }
-      if (p < 0 || p >= j) {
-        ok = false;
-        break;
-      }
-      j = p;
-    }
-    if (!ok) {
+  for (int i = tid; i < T; i += 256) {
+    const int p = jump[i];
+    if (!(i == 0 ? p == -1 : (p >= 0 && p < i))) {
       err = SPEC_DEV_PARENT;
-      w[0] = w[1] = w[2] = w[3] = 0;
-      w[i >> 6] = 1ull << (i & 63);
+      jump[i] = -1;
     }
-    for (int k = 0; k < 4; ++k) anc[i * 4 + k] = w[k];
+#pragma unroll
+    for (int w = 0; w < kAncWords; ++w)
+      if (w < nw) anc[i * kAncWords + w] = (w == (i >> 6)) ? 1ull << (i & 63) : 0ull;
+  }
+  int pending = 1;
+  while (__syncthreads_or(pending)) {  // the barrier also publishes the last round's writes
+    uint64_t add[2][kAncWords];
+    int nj[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + 256 * k;
+      nj[k] = -2;  // nothing to join
+      const int j = i < T ? jump[i] : -1;
+      if (j >= 0) {
+        nj[k] = jump[j];
+#pragma unroll
+        for (int w = 0; w < kAncWords; ++w) add[k][w] = w < nw ? anc[j * kAncWords + w] : 0ull;
+      }
+    }
+    __syncthreads();  // every read of this round before any write
+    pending = 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + 256 * k;
+      if (nj[k] != -2) {
+#pragma unroll
+        for (int w = 0; w < kAncWords; ++w)
+          if (w < nw) anc[i * kAncWords + w] |= add[k][w];
+        jump[i] = nj[k];
+        pending |= nj[k] >= 0;
+      }
+    }
   }
   return err;
 }
@@ -198,11 +222,13 @@ __device__ int build_ancestors_lds(const int* par, int T, uint64_t* anc) {
 template <int NRB>
 struct TileLds {
   __attribute__((aligned(16))) uint8_t tiles[2 * kTileBytes];  // 2 x (4 K pages, 4 V pages)
-  uint64_t anc[kMaxT * 4];
+  uint64_t anc[64 * NRB * kAncWords];  // the bitsets of the item's nodes (at most one per row)
   int s_par[kMaxT];
   int s_blk[kMaxSplitPages];
   int s_last, s_next;
 };
+static_assert(kMaxT * kAncWords * sizeof(uint64_t) <= kTileBytes,
+              "the whole tree's bitsets are built in the second tile buffer");
 
 // The work of one item (b, g, KV split, row tile), sequence b's prefix length
 // already clamped to its valid range (err: SPEC_DEV_LENGTH if it was not).
@@ -254,12 +280,13 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
 
   // query fragments (B operand of S^T): Q[row][c*32 + quad*8 .. +7]
   const int row_base = rt * RT + wave * NRB * 16;
+  const int node0 = (rt * RT) / a.G;  // the item's first node: its rows hold nodes node0 .. node0 + RT - 1 at most
   bf16x8 qf[NRB][4];
   int node_of[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const int r = row_base + rb * 16 + l16;
-    node_of[rb] = r < a.R ? r / a.G : 0;
+    node_of[rb] = r < a.R ? r / a.G - node0 : 0;  // index among the item's nodes
     if (r < a.R) {
       const int node = r / a.G, hh = r % a.G;
       const uint16_t* qp = a.q + ((static_cast<long>(b) * a.T + node) * a.Hq + g * a.G + hh) * kD + quad * 8;
@@ -318,7 +345,17 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
 
   __syncthreads();  // s_blk and s_par are ready
   if (n_it > 0) issue_tile(0);
-  if (tail) err |= build_ancestors_lds(s_par, a.T, anc);  // read after the loop's first barrier
+  if (tail) {
+    // the whole tree's bitsets in tile buffer 1 (first written by tile 1, issued
+    // after the loop's first barrier), then the item's nodes' ones into `anc`
+    uint64_t* full = reinterpret_cast<uint64_t*>(tiles + kTileBytes);
+    err |= build_ancestors_lds(s_par, a.T, full);
+    const int nw = (a.T + 63) >> 6;
+    for (int e = tid; e < RT * kAncWords; e += 256) {
+      const int node = node0 + e / kAncWords, w = e % kAncWords;
+      anc[e] = (node < a.T && w < nw) ? full[node * kAncWords + w] : 0ull;
+    }
+  }
 
   for (int it = 0; it < n_it; ++it) {
     wait_vm0();  // this wave's page of tile `it` has landed
@@ -352,12 +389,12 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
         const uint32_t endm = nv >= 32 ? 0xFFFFFFFFu : (nv <= 0 ? 0u : ((1u << nv) - 1u));
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
-          const uint64_t* an = anc + node_of[rb] * 4;
+          const uint64_t* an = anc + node_of[rb] * kAncWords;
           uint32_t w;
           if (d >= 0) {
             const int wi = d >> 6, sh = d & 63;
-            const uint64_t lo = an[wi];
-            const uint64_t hi = wi + 1 < 4 ? an[wi + 1] : 0ull;
+            const uint64_t lo = wi < kAncWords ? an[wi] : 0ull;
+            const uint64_t hi = wi + 1 < kAncWords ? an[wi + 1] : 0ull;
             w = static_cast<uint32_t>(sh == 0 ? lo : ((lo >> sh) | (hi << (64 - sh))));
           } else if (d > -32) {
             w = (static_cast<uint32_t>(an[0]) << (-d)) | ((1u << (-d)) - 1u);

@@ -9,7 +9,7 @@
 namespace spectree {
 
 constexpr int kBlockSize = 16;
-constexpr int kMaxT = 256;          // ancestor bitsets hold 4 x 64 bits
+constexpr int kMaxT = 512;          // tree nodes: ancestor bitsets of 8 x 64 bits
 constexpr int kMaxV = 262144;       // rejected-token bitmap of the sampler lives in LDS
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -62,6 +62,7 @@ constexpr int kUnroll = 4;        // rows per wave in flight together
 template <bool kBf16>
 __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
   __shared__ int s_up[kMaxT], s_dep[kMaxT];
+  static_assert(kMaxT <= 512, "two nodes per thread");
   __shared__ int s_err;
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -69,28 +70,36 @@ __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
   const int Lb = a.plen[b];  // loaded on entry, with the parent row
   if (tid == 0) s_err = 0;
   __syncthreads();
-  if (tid < T) {
-    const int p = a.parent[static_cast<long>(b) * T + tid];
-    const bool ok = tid == 0 ? p == -1 : (p >= 0 && p < tid);
-    s_up[tid] = (tid == 0 || !ok) ? -1 : p;
-    s_dep[tid] = tid == 0 ? 0 : 1;
+  for (int i = tid; i < T; i += 256) {  // T <= 512: two nodes per thread at most
+    const int p = a.parent[static_cast<long>(b) * T + i];
+    const bool ok = i == 0 ? p == -1 : (p >= 0 && p < i);
+    s_up[i] = (i == 0 || !ok) ? -1 : p;
+    s_dep[i] = i == 0 ? 0 : 1;
     if (!ok) atomicOr(&s_err, SPEC_DEV_PARENT);
   }
   __syncthreads();
   for (int r = 0; (1 << r) < T; ++r) {  // after round r, up = the ancestor 2^(r+1) steps above (or -1)
-    int up = -1, dep = 0;
-    if (tid < T) {
-      up = s_up[tid];
-      dep = s_dep[tid];
-      if (up >= 0) {
-        dep += s_dep[up];
-        up = s_up[up];
+    int up[2] = {-1, -1}, dep[2] = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + 256 * k;
+      if (i < T) {
+        up[k] = s_up[i];
+        dep[k] = s_dep[i];
+        if (up[k] >= 0) {
+          dep[k] += s_dep[up[k]];
+          up[k] = s_up[up[k]];
+        }
       }
     }
     __syncthreads();
-    if (tid < T) {
-      s_up[tid] = up;
-      s_dep[tid] = dep;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + 256 * k;
+      if (i < T) {
+        s_up[i] = up[k];
+        s_dep[i] = dep[k];
+      }
     }
     __syncthreads();
   }

@@ -47,6 +47,8 @@ constexpr int kMaxEager = 8;     // rows whose statistics are taken before the w
 constexpr int kMaxTeam = 64;     // workgroups per sequence (one wave merges their partials)
 constexpr int kDeepTeam = 32;    // at most this many for trees with deeper rows (more than 16 nodes)
 constexpr int kEagerCap = 8192;  // floats of eager-row logit slices kept in LDS
+constexpr int kSmallTree = 256;  // trees up to this many nodes: the kernel with the larger eager space
+constexpr int kEagerCapBig = 4096;  // eager-slice floats beside the node arrays of a larger tree
 constexpr int kSliceCap = 8192;  // floats of the current row's logits / draft probs kept in LDS
 constexpr int kHeaderBytes = 256;  // workspace header: word 0 exit counter of the grid, word 1 call epoch
 constexpr unsigned kSpinLimit = 1u << 24;
@@ -84,7 +86,8 @@ Team team_shape(int B, int T, int V, long resident) {
   t.S = (V + nw - 1) / nw;
   t.ld = (t.S + 3) & ~3;
   int e = std::min(T, kMaxEager);
-  e = t.ld > kEagerCap ? 0 : std::min(e, kEagerCap / t.ld);  // >= 1 when the slice fits (T >= 1)
+  const int cap = T <= kSmallTree ? kEagerCap : kEagerCapBig;
+  e = t.ld > cap ? 0 : std::min(e, cap / t.ld);  // >= 1 when the slice fits a tree of up to kSmallTree nodes
   t.E = e >= 8 ? 8 : e >= 4 ? 4 : e >= 2 ? 2 : e;
   return t;
 }
@@ -569,18 +572,22 @@ __device__ __forceinline__ void merge_row(const Rec& r, bool member, bool greedy
 
 // kFits: the slice (S <= kSliceCap floats) lives in LDS, so every slice access is an
 // LDS access; otherwise the slices are read from global memory where they lie.
-template <bool kFits>
+// kTree: the largest tree (kSmallTree, or kMaxT with half the eager space, so
+// that the node arrays fit beside it).
+template <bool kFits, int kTree>
 __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
-  __shared__ __attribute__((aligned(16))) float eager_l[kEagerCap];  // logit slices of rows 0 .. E-1, stride ld
-  __shared__ __attribute__((aligned(16))) float eager_q[kEagerCap];  // their draft-probability slices
+  constexpr int kEager = kTree <= kSmallTree ? kEagerCap : kEagerCapBig;
+  static_assert(kTree <= 2 * kThreads, "two nodes per thread at most");
+  __shared__ __attribute__((aligned(16))) float eager_l[kEager];  // logit slices of rows 0 .. E-1, stride ld
+  __shared__ __attribute__((aligned(16))) float eager_q[kEager];  // their draft-probability slices
   __shared__ __attribute__((aligned(16))) float cur_lbuf[kSliceCap];
   __shared__ __attribute__((aligned(16))) float cur_qbuf[kSliceCap];
-  __shared__ int16_t first_child[kMaxT], next_sib[kMaxT];
-  __shared__ int s_par[kMaxT], s_tok[kMaxT], s_path[kMaxT];
-  __shared__ float s_lx[kMaxT], s_qx[kMaxT];  // logit / draft prob of node c's token in its parent's row
-  __shared__ int rej_tok[kMaxT];
-  __shared__ double s_ru[kMaxT], s_fu[kMaxT];  // accept draw of node c, final draw at node u
-  __shared__ double rej_c[kMaxT];
+  __shared__ int16_t first_child[kTree], next_sib[kTree];
+  __shared__ int s_par[kTree], s_tok[kTree], s_path[kTree];
+  __shared__ float s_lx[kTree], s_qx[kTree];  // logit / draft prob of node c's token in its parent's row
+  __shared__ int rej_tok[kTree];
+  __shared__ double s_ru[kTree], s_fu[kTree];  // accept draw of node c, final draw at node u
+  __shared__ double rej_c[kTree];
   __shared__ __attribute__((aligned(16))) double row_partials[2 * kThreads];  // one row's statistics partials
   __shared__ Rec s_rec[kMaxEager];
   // merged statistics of the eager rows (index r < E) and of the current deeper row (index kMaxEager)
@@ -614,12 +621,17 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   const uint32_t epoch = __hip_atomic_load(a.hdr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t tag = epoch + 1u;
 
-  // tree and tokens (T <= kThreads: one node per thread) and the eager logit and
+  // tree and tokens (nodes tid and tid + kThreads) and the eager logit and
   // draft slices, which depend on nothing else: all in flight together
   const int pv = a.parent[static_cast<long>(b) * T + min(tid, T - 1)];
   const int tv = a.tokens[static_cast<long>(b) * T + min(tid, T - 1)];
+  int pv2 = -1, tv2 = 0;
+  if (kTree > kThreads && tid + kThreads < T) {
+    pv2 = a.parent[static_cast<long>(b) * T + tid + kThreads];
+    tv2 = a.tokens[static_cast<long>(b) * T + tid + kThreads];
+  }
   const int c_lb = a.fuse ? a.c.prefix_lens[b] : 0;  // the compaction's prefix length, loaded early
-  if constexpr (kFits) {  // E >= 1 whenever the slice fits
+  if constexpr (kFits) {  // (E = 0 for a larger tree whose slice is too long for the eager space)
     stage_dma(eager_l, lg_b + v0, ld, V, E, n);
     if (!a.greedy) stage_dma(eager_q, q_b + v0, ld, V, E, n);
   }
@@ -634,6 +646,10 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   if (tid < T) {
     s_par[tid] = pv;
     s_tok[tid] = tv;
+  }
+  if (kTree > kThreads && tid + kThreads < T) {
+    s_par[tid + kThreads] = pv2;
+    s_tok[tid + kThreads] = tv2;
   }
   if (tid == 0) {
     sh_err = 0;
@@ -678,7 +694,8 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
     // whose parent is i) and next_sib[i] (the first c > i sharing i's parent) are
     // lowest-set-bit lookups, with no scan over the tree.  kids lives in cur_qbuf,
     // which is first written when a deeper row is staged.
-    constexpr int kKW = kMaxT / 32;  // bitset words per parent
+    constexpr int kKW = kTree / 32;  // bitset words per parent
+    static_assert(kTree * kKW <= kSliceCap, "the child bitsets fit the current-row draft buffer");
     const int nkw = (T + 31) >> 5;   // words in use
     uint32_t* kids = reinterpret_cast<uint32_t*>(cur_qbuf);
     for (int i = tid; i < T * kKW; i += kThreads)
@@ -722,11 +739,13 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
     // accept-test operands of every drafted node (logit and draft probability of
     // its token in its parent's row): loaded just before the first team barrier,
     // whose latency they share, and stored to LDS after it
-    const int cx = 1 + tid;
+    const int cx = 1 + tid, cx2 = 1 + tid + kThreads;  // nodes cx2 only in trees of more than kThreads + 1
     const int nd = min(cx, T - 1);  // lanes past the tree re-read a valid node (or element 0)
     const long off = nd >= 1 ? static_cast<long>(s_par[nd]) * V + s_tok[nd] : 0;
+    const bool two = kTree > kThreads && cx2 < T;
+    const long off2 = two ? static_cast<long>(s_par[cx2]) * V + s_tok[cx2] : 0;
     // statistics of the first E rows, from their LDS slices (landed before the tree build's barrier)
-    if (kFits) {
+    if (kFits && E > 0) {
       switch (E) {
         case 1:
           slice_stats_rows<1, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, cur_lbuf);
@@ -744,6 +763,8 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       if (tid < E) put_slot(&eager[wg * E + tid], s_rec[tid], tag);
       const float lx = lg_b[off];
       const float qx = (a.greedy ? lg_b : q_b)[off];
+      const float lx2 = two ? lg_b[off2] : 0.f;
+      const float qx2 = two ? (a.greedy ? lg_b : q_b)[off2] : 0.f;
       // gather every member's eager rows (wave w: rows w and w + 4) and merge them, member order
       const Rec none = Rec{-INFINITY, 0x7fffffff, 0.0};
       if (wave + kWaves < E) {
@@ -765,11 +786,19 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         s_lx[cx] = lx;
         s_qx[cx] = qx;
       }
+      if (two) {
+        s_lx[cx2] = lx2;
+        s_qx[cx2] = qx2;
+      }
       __syncthreads();
     } else {
       if (cx < T) {
         s_lx[cx] = lg_b[off];
         s_qx[cx] = (a.greedy ? lg_b : q_b)[off];
+      }
+      if (two) {
+        s_lx[cx2] = lg_b[off2];
+        s_qx[cx2] = (a.greedy ? lg_b : q_b)[off2];
       }
       __syncthreads();
     }
@@ -1165,14 +1194,18 @@ long reject_resident_capacity() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
   if (dev < 64 && cache[dev] > 0) return cache[dev];
-  int cus = 0, per_cu_fit = 0, per_cu_nofit = 0;
+  int cus = 0, per_cu[4] = {0, 0, 0, 0};
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_fit, reject_team_kernel<true>, kThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu[0], reject_team_kernel<true, kSmallTree>, kThreads, 0) !=
           hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_nofit, reject_team_kernel<false>, kThreads, 0) !=
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu[1], reject_team_kernel<false, kSmallTree>, kThreads, 0) !=
+          hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu[2], reject_team_kernel<true, kMaxT>, kThreads, 0) !=
+          hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu[3], reject_team_kernel<false, kMaxT>, kThreads, 0) !=
           hipSuccess)
     return 0;
-  const long cap = static_cast<long>(cus) * std::min(per_cu_fit, per_cu_nofit);
+  const long cap = static_cast<long>(cus) * std::min(std::min(per_cu[0], per_cu[1]), std::min(per_cu[2], per_cu[3]));
   if (dev < 64) cache[dev] = cap;
   return cap;
 }
@@ -1266,10 +1299,17 @@ hipError_t launch_reject(const RejectLaunch& L, hipStream_t stream) {
   a.fuse = L.compact != nullptr;
   if (a.fuse) a.c = *L.compact;
   const dim3 grid(static_cast<unsigned>(L.B * t.NW));
-  if (t.ld <= kSliceCap) {
-    hipLaunchKernelGGL(reject_team_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+  const bool fits = t.ld <= kSliceCap;
+  if (L.T <= kSmallTree) {
+    if (fits)
+      hipLaunchKernelGGL((reject_team_kernel<true, kSmallTree>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((reject_team_kernel<false, kSmallTree>), grid, dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(reject_team_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+    if (fits)
+      hipLaunchKernelGGL((reject_team_kernel<true, kMaxT>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((reject_team_kernel<false, kMaxT>), grid, dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
