@@ -336,8 +336,8 @@ def seconds_per_call(fn, copies, reps, calls):
 
 SWEEP_SHAPES = (
     # name, layer shape of the configuration it follows, tree builder, tree sizes, prefix lengths
-    ("sequoia_shape", 3, dict(), (1, 2, 4, 8, 16, 32, 64, 128, 256), (1024, 4096, 8192)),
-    ("eagle_shape", 2, dict(tree="random"), (1, 2, 4, 8, 16, 32, 64, 128), (1024, 4096)),
+    ("sequoia_shape", 3, dict(), (1, 2, 4, 8, 16, 32, 64, 128, 256, 384, 512), (1024, 4096, 8192)),
+    ("eagle_shape", 2, dict(tree="random"), (1, 2, 4, 8, 16, 32, 64, 128, 256, 512), (1024, 4096)),
 )
 
 
@@ -346,11 +346,15 @@ def sweep():
     the layer shapes of the Sequoia-scale configuration (B1, 64 q / 8 kv heads,
     V 32000, tau 0.6, without replacement, Sequoia-profile trees of depth <= 10)
     and of the EAGLE-style one (B8, 32 q / 8 kv heads, V 128256, tau 0.7, random
-    trees of depth <= 6), T from 1 to 256 (128 for the wider one), timed per call
-    as in the main run (graphs of back-to-back calls over input copies that
-    together exceed the 256 MB MALL where memory allows).  Each point times the
-    attention and the sampler with compaction (the step), and the tree K/V write
-    that precedes them (reported on its own)."""
+    trees of depth <= 6), T from 1 to 512, timed per call as in the main run
+    (graphs of back-to-back calls over input copies that together exceed the
+    256 MB MALL where memory allows).  Each point times the attention and the
+    sampler with compaction (the step), and the tree K/V write that precedes them
+    (reported on its own).  On the Sequoia shape each point also carries the
+    expected tokens one step generates with the Sequoia-optimal tree of that size
+    and depth bound for the generator's acceptance-by-rank vector
+    (spec_sequoia_tree), and so the expected generated tokens per second of
+    verification: the quantity the tree size is chosen by."""
     import torch
 
     import tree_verify_attention_masked_amd as stv
@@ -409,7 +413,12 @@ def sweep():
                     raise SystemExit(f"device reported input errors: {status.tolist()}")
                 a_bytes, a_flops = attn_work(w)
                 step = us["attn_us"] + us["reject_compact_us"]
-                print(json.dumps({"shape": name, "T": w.T, "prefix": L, "B": w.B, "depth": int(w.info["depth"]),
+                extra = {}
+                if "accept_profile" in w.info:
+                    _, e_tok = stv.spec_sequoia_tree(w.info["accept_profile"], w.T, depth_cap)
+                    extra = {"expected_tokens": round(e_tok, 4),
+                             "expected_tokens_per_s": round(w.B * e_tok / step * 1e6, 1)}
+                print(json.dumps({"shape": name, "T": w.T, "prefix": L, "B": w.B, "depth": int(w.info["depth"]), **extra,
                                   "attn_us": round(us["attn_us"], 2),
                                   "reject_compact_us": round(us["reject_compact_us"], 2),
                                   "kv_write_us": round(us["kv_write_us"], 2),

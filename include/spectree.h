@@ -10,7 +10,8 @@
  *   spec_kv_compact   keep only the accepted root-to-leaf path in the KV cache
  * and spec_tree_reject_compact, the last two in one launch; and, for the step
  * before them, spec_tree_kv_write (the tree's K/V rows into the paged cache,
- * keys and queries rotated for their tree positions); spec_tree_truncate
+ * keys and queries rotated for their tree positions), also fused with the
+ * attention in one launch as spec_tree_write_attn; spec_tree_truncate
  * applies top-k / top-p to the target logits before the sampler.
  *
  * Conventions shared by every call
@@ -318,6 +319,47 @@ int spec_tree_kv_write(const void* k_new, const void* v_new, void* q, void* k_ca
                        const int32_t* block_table, const int32_t* prefix_lens, const int32_t* parent,
                        int32_t* status, int B, int T, int Hq, int Hkv, int D, int block_size,
                        int max_blocks_per_seq, int num_blocks, float rope_theta, int dtype, void* stream);
+
+/* ----------------------------------------------------------------------
+ * spec_tree_write_attn — spec_tree_kv_write and spec_tree_attn in one launch:
+ * the step before verify attention (the tree's K/V rows into the paged cache,
+ * keys and queries rotated for the nodes' positions prefix_lens[b] +
+ * depth(i); "Report: Support nextn speculative decoding", implementation
+ * summary, step 3, and the position_ids of "Issue: Speculative Decoding on
+ * vLLM") fused with the tree attention over the prefix and the tree.
+ *
+ * Writes the same cache rows, bit for bit, as spec_tree_kv_write, and the same
+ * `out` as spec_tree_attn called after it on the rotated queries (bit for bit
+ * when T * Hq / Hkv > 16; below that spec_tree_attn sums in another order).
+ * The caller's `q` is not modified: the rotated queries live in the workspace.  Inside the launch the first B * Hkv work items write the rows of
+ * one (sequence, kv head) each; an attention item starts once the rows of its
+ * (sequence, kv head) are written (work items are claimed from a counter in
+ * the workspace, writers first, so this wait always ends).
+ *
+ *   k_new, v_new [B, T, Hkv, D] bf16: the nodes' keys (before rotation) and values
+ *   q            [B, T, Hq, D] bf16: the queries before rotation (read only)
+ *   k_cache, v_cache, block_table, prefix_lens, parent, out, scale, status
+ *                as for spec_tree_attn; the caches are written at the T slots
+ *                of each sequence only
+ *   rope_theta   >= 0 and finite; 0 writes and uses the rows unrotated
+ *   workspace    >= spec_tree_write_attn_workspace_size(...) bytes, never
+ *                NULL (it holds the work counter, B * Hkv flags and the
+ *                rotated queries), zero-filled before the first call; each
+ *                completed call leaves its counters and flags zero, so a
+ *                workspace serves later calls of the same shape as it is
+ *                (re-zero it when the shape changes, as for spec_tree_attn)
+ * Errors: a bad parent row or prefix length writes no cache row of that
+ * sequence, and its attention runs on the unrotated queries (status reports
+ * it); a bad block index skips that slot (SPEC_DEV_BLOCK).
+ * Supported: bf16, D = 128, block_size = 16, 1 <= T <= 512, Hq % Hkv == 0.
+ * ---------------------------------------------------------------------- */
+size_t spec_tree_write_attn_workspace_size(int B, int T, int Hq, int Hkv, int D, int max_blocks_per_seq,
+                                           int dtype);
+int spec_tree_write_attn(const void* k_new, const void* v_new, const void* q, void* k_cache, void* v_cache,
+                         const int32_t* block_table, const int32_t* prefix_lens, const int32_t* parent, void* out,
+                         int B, int T, int Hq, int Hkv, int D, int block_size, int max_blocks_per_seq,
+                         int num_blocks, float rope_theta, float scale, int dtype, int32_t* status,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------
  * spec_tree_truncate — top-k / top-p truncation of the target logits, for a

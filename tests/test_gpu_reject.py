@@ -132,11 +132,11 @@ def test_statistics_single_child_acceptance_rate():
 
 
 # Trees of more than 256 nodes (the sampler kernel with 512-node arrays, two
-# nodes per thread, half the eager space): a 512-node random tree at a small
+# nodes per thread, a smaller eager space): a 512-node random tree at a small
 # vocabulary (frequent rejections, sibling residuals), a 300-node Sequoia-profile
 # tree drafted and verified without replacement, and a batch whose slices are
-# too long for the halved eager space but fit the current-row buffer (64
-# sequences, 4 members each, 4100-entry slices: no eager rows).
+# too long for that eager space but fit the current-row buffer (64 sequences, 4
+# members each, 8000-entry slices: no eager rows, every visited row staged).
 def test_tree_of_512_nodes():
     w = make_workload(tag=560, B=2, Hq=2, Hkv=2, D=64, dtype="f32", V=50, prefix=[4, 4], tree="random", T=512,
                       max_depth=9, temperature=0.9, with_kv=False)
@@ -153,8 +153,8 @@ def test_tree_of_300_nodes_without_replacement():
 
 
 def test_large_tree_without_eager_rows():
-    w = make_workload(tag=562, B=64, Hq=2, Hkv=2, D=64, dtype="f32", V=16400, prefix=[4] * 64, tree="random",
-                      T=260, max_depth=6, temperature=1.0, with_kv=False)
-    assert stv.spec_tree_reject_plan(64, 260, 16400, 1 << 20) == (4, 4100)
-    print("[reject] B=64 T=260 V=16400", flush=True)
+    w = make_workload(tag=562, B=64, Hq=2, Hkv=2, D=64, dtype="f32", V=32000, prefix=[4] * 64, tree="random",
+                      T=257, max_depth=4, temperature=1.0, with_kv=False)
+    assert stv.spec_tree_reject_plan(64, 257, 32000, 1 << 20) == (4, 8000)
+    print("[reject] B=64 T=257 V=32000", flush=True)
     _many_offsets(w, range(2))

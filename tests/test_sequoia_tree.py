@@ -13,6 +13,7 @@ import pytest
 import tree_verify_attention_masked_amd as stv
 from oracle.sequoia import expected_tokens, sequoia_tree
 from test_oracle_sequoia import greedy_top_n
+from workloads import make_config
 
 
 def _vectors(seed):
@@ -56,3 +57,14 @@ def test_library_refuses_bad_arguments():
         with pytest.raises(stv.SpecError):
             stv.spec_sequoia_tree(accept, n, d)
     assert stv.spec_sequoia_tree([0.5], 1, 0)[0].tolist() == [-1]
+
+
+@pytest.mark.parametrize("T", [16, 256, 512])
+def test_sequoia_scale_trees_are_optimal_for_their_acceptance_vector(T):
+    """The Sequoia-scale workload keeps the T best nodes by path score under a
+    non-increasing acceptance-by-rank vector; the library's dynamic program must
+    find no better tree of that size and depth (the two agree to rounding)."""
+    w = make_config(3, T=T, prefix=64, max_depth=10, with_kv=False)
+    a = w.info["accept_profile"]
+    _, best = stv.spec_sequoia_tree(a, T, 10)
+    assert math.isclose(expected_tokens(list(w.parent[0]), a), best, rel_tol=1e-12)

@@ -37,5 +37,7 @@ from .binding import (  # noqa: F401
     spec_tree_reject_plan,
     spec_tree_kv_write,
     spec_tree_truncate,
+    spec_tree_write_attn,
+    spec_tree_write_attn_workspace_size,
     spec_version,
 )

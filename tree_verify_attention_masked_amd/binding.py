@@ -48,6 +48,9 @@ _SIGNATURES = {
     "spec_kv_compact": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "spec_tree_kv_write": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                                 ctypes.c_float, _i, _vp]),
+    "spec_tree_write_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "spec_tree_write_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                                  ctypes.c_float, ctypes.c_float, _i, _vp, _vp, _sz, _vp]),
     "spec_tree_truncate": (_i, [_vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_float, _vp, _vp]),
     "spec_tree_reject_compact": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_uint64,
                                       ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp, _sz,
@@ -342,6 +345,54 @@ def spec_tree_kv_write(k_new, v_new, q, k_cache, v_cache, block_table, prefix_le
                                 block_table.shape[1], nb, float(rope_theta), _dtype_code(k_new),
                                 _stream(k_new.device))
     _check(rc, "spec_tree_kv_write")
+
+
+def spec_tree_write_attn_workspace_size(B, T, Hq, Hkv, D, max_blocks_per_seq, dtype_code) -> int:
+    return int(load_library().spec_tree_write_attn_workspace_size(B, T, Hq, Hkv, D, max_blocks_per_seq, dtype_code))
+
+
+def spec_tree_write_attn(k_new, v_new, q, k_cache, v_cache, block_table, prefix_lens, parent, rope_theta,
+                         scale=None, out=None, status=None, workspace=None):
+    """spec_tree_kv_write and spec_tree_attn in one launch: the tree's K/V rows into the cache (keys rotated for
+    position prefix + depth), then attention with the queries rotated the same way (q itself is not modified).
+    k_new, v_new [B,T,Hkv,D], q [B,T,Hq,D], caches [num_blocks,Hkv,16,D] (bf16) -> out [B,T,Hq,D]."""
+    lib = load_library()
+    _need(q, "q", ndim=4)
+    _need(k_new, "k_new", q.dtype, 4)
+    _need(v_new, "v_new", q.dtype, 4)
+    _need(k_cache, "k_cache", q.dtype, 4)
+    _need(v_cache, "v_cache", q.dtype, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(prefix_lens, "prefix_lens", torch.int32, 1)
+    _need(parent, "parent", torch.int32, 2)
+    B, T, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or D2 != D:
+        raise ValueError("k_cache / v_cache / q shapes disagree")
+    if tuple(k_new.shape) != (B, T, Hkv, D) or tuple(v_new.shape) != (B, T, Hkv, D):
+        raise ValueError("k_new / v_new shapes disagree with q and the cache")
+    if tuple(parent.shape) != (B, T) or prefix_lens.shape[0] != B or block_table.shape[0] != B:
+        raise ValueError("parent / prefix_lens / block_table shapes disagree with q")
+    code = _dtype_code(q)
+    mb = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", q.dtype)
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    ws = int(lib.spec_tree_write_attn_workspace_size(B, T, Hq, Hkv, D, mb, code))
+    if workspace is None:  # zero-filled: its header holds the work counter and the write flags
+        workspace = torch.zeros(max(ws, 1), dtype=torch.uint8, device=q.device)
+    wsz = workspace.numel() * workspace.element_size()
+    rc = lib.spec_tree_write_attn(_ptr(k_new), _ptr(v_new), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(block_table), _ptr(prefix_lens), _ptr(parent), _ptr(out), B, T, Hq, Hkv, D,
+                                  bs, mb, nb, float(rope_theta), float(scale), code, _ptr(status), _ptr(workspace),
+                                  wsz, _stream(q.device))
+    _check(rc, "spec_tree_write_attn")
+    return out
 
 
 def spec_sequoia_tree(accept, n, max_depth):

@@ -286,6 +286,54 @@ int spec_tree_kv_write(const void* k_new, const void* v_new, void* q, void* k_ca
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
+size_t spec_tree_write_attn_workspace_size(int B, int T, int Hq, int Hkv, int D, int max_blocks_per_seq, int dtype) {
+  if (B <= 0 || T < 1 || T > kMaxT || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || max_blocks_per_seq < 1 ||
+      dtype != SPEC_BF16 || D != 128)
+    return 0;
+  return plan_attn_write(B, T, Hq, Hkv, max_blocks_per_seq).ws_bytes;
+}
+
+int spec_tree_write_attn(const void* k_new, const void* v_new, const void* q, void* k_cache, void* v_cache,
+                         const int32_t* block_table, const int32_t* prefix_lens, const int32_t* parent, void* out,
+                         int B, int T, int Hq, int Hkv, int D, int block_size, int max_blocks_per_seq, int num_blocks,
+                         float rope_theta, float scale, int dtype, int32_t* status, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const int rc = check_kv_shapes(B, T, Hkv, D, block_size, max_blocks_per_seq, num_blocks, dtype);
+  if (rc != SPEC_OK) return rc;
+  if (dtype != SPEC_BF16) return SPEC_ERR_UNSUPPORTED;
+  if (Hq < Hkv || Hq % Hkv != 0) return SPEC_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(rope_theta >= 0.0f) || std::isinf(rope_theta)) return SPEC_ERR_INVALID_ARG;
+  if (B == 0) return SPEC_OK;
+  if (!k_new || !v_new || !q || !k_cache || !v_cache || !block_table || !prefix_lens || !parent || !out)
+    return SPEC_ERR_INVALID_ARG;
+  const AttnPlan plan = plan_attn_write(B, T, Hq, Hkv, max_blocks_per_seq);
+  if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return SPEC_ERR_WORKSPACE;
+  AttnWriteLaunch W{};
+  AttnLaunch& L = W.attn;
+  L.q = q;
+  L.k = k_cache;
+  L.v = v_cache;
+  L.block_table = block_table;
+  L.prefix_lens = prefix_lens;
+  L.parent = parent;
+  L.out = out;
+  L.status = status;
+  L.workspace = workspace;
+  L.B = B;
+  L.T = T;
+  L.Hq = Hq;
+  L.Hkv = Hkv;
+  L.D = D;
+  L.max_blocks = max_blocks_per_seq;
+  L.num_blocks = num_blocks;
+  L.scale = scale;
+  W.k_new = k_new;
+  W.v_new = v_new;
+  W.theta = rope_theta;
+  const hipError_t e = launch_attn_write(plan, W, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
 int spec_tree_truncate(const float* logits_in, float* logits_out, int B, int T, int V, float temperature,
                        int top_k, float top_p, int32_t* status, void* stream) {
   if (B < 0 || T < 1 || V < 1) return SPEC_ERR_INVALID_ARG;

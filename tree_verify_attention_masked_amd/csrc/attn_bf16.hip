@@ -29,14 +29,17 @@
 // finish merges them (arrival counter in the workspace, reset by that
 // workgroup).
 #include <algorithm>
+#include <cmath>
 
 #include "common.h"
+#include "rope_dev.h"
 
 namespace spectree {
 namespace {
 
 constexpr int kD = 128;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr unsigned kFlagSpinLimit = 1u << 24;  // polls of a write item's flag (a few seconds)
 constexpr int kPageBytes = kBlockSize * kD * 2;  // one page of one head: 4 KB
 constexpr int kTileBytes = 8 * kPageBytes;       // 4 K pages, then 4 V pages: 64 keys
 constexpr int kMaxSplitPages = 1024;             // pages per split (planning keeps below)
@@ -159,9 +162,22 @@ struct TArgs2 {
   unsigned* counters;  // [B * Hkv * n_rt], then the item queue's [next id, workgroups done]
   int B, T, Hq, Hkv, G, R, n_rt, splits, pps, max_blocks, num_blocks;
   int reorder;  // longest items first (one row tile, B <= 64)
-  int persist;  // reorder, with each workgroup taking items from a queue until none is left
+  int persist;  // each workgroup takes items from a queue until none is left
   long items;
   float sl2;
+  // The tree's K/V write in the same launch: the queue's first n_write ids are
+  // write items, one per (b, g), then come the attention items; an attention
+  // item waits for its (b, g) flag before it reads queries or tree keys.
+  int n_write;             // B * Hkv
+  int rotate;              // rope_theta > 0
+  double log2_theta;
+  const uint16_t* q_src;   // [B,T,Hq,D] queries before rotation; `q` is then their rotated copy
+  const uint16_t* k_new;   // [B,T,Hkv,D] the nodes' keys before rotation
+  const uint16_t* v_new;   // [B,T,Hkv,D] their values
+  uint16_t* q_rot;         // = q, written by the write items
+  uint16_t* kc;            // = k, = v: the cache the write items fill
+  uint16_t* vc;
+  unsigned* flags;         // [B * Hkv]: nonzero once (b, g)'s rows are written
 };
 
 constexpr int kAncWords = kMaxT / 64;  // words of one node's ancestor-or-self bitset
@@ -234,7 +250,7 @@ static_assert(kMaxT * kAncWords * sizeof(uint64_t) <= kTileBytes,
 // already clamped to its valid range (err: SPEC_DEV_LENGTH if it was not).
 // Every thread of the workgroup calls it; it returns at points the whole
 // workgroup reaches together, or after its merge.
-template <int NRB>
+template <int NRB, bool kFused>
 __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, int Lb, int err, TileLds<NRB>& L) {
   constexpr int RT = 64 * NRB;  // rows per workgroup
   uint8_t* tiles = L.tiles;
@@ -267,7 +283,11 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
   // The split's block indices and the parent row are staged once in LDS, the
   // query fragments loaded beside them (one memory latency for all three); the
   // first tile is issued as soon as the indices are in, and the ancestor sets
-  // are built while it lands.
+  // are built while it lands.  With the K/V write in the same launch the item
+  // first waits for its (b, g) rows (queries and tree keys): its flag is read
+  // with the indices, and the queries are loaded after the barrier that follows.
+  unsigned flag = 1;
+  if (kFused && tid == 0) flag = __hip_atomic_load(&a.flags[b * a.Hkv + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int32_t* bt_b = a.bt + static_cast<long>(b) * a.max_blocks;
   for (int i = tid; i < p1 - p0; i += 256) {
     const int blk = bt_b[p0 + i];
@@ -287,17 +307,24 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
   for (int rb = 0; rb < NRB; ++rb) {
     const int r = row_base + rb * 16 + l16;
     node_of[rb] = r < a.R ? r / a.G - node0 : 0;  // index among the item's nodes
-    if (r < a.R) {
-      const int node = r / a.G, hh = r % a.G;
-      const uint16_t* qp = a.q + ((static_cast<long>(b) * a.T + node) * a.Hq + g * a.G + hh) * kD + quad * 8;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qf[rb][c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + c * 32));
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qf[rb][c] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-    }
   }
-
+  auto load_q = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r = row_base + rb * 16 + l16;
+      if (r < a.R) {
+        const int node = r / a.G, hh = r % a.G;
+        const uint16_t* qp = a.q + ((static_cast<long>(b) * a.T + node) * a.Hq + g * a.G + hh) * kD + quad * 8;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          qf[rb][c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + c * 32));
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qf[rb][c] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+      }
+    }
+  };
+  if constexpr (!kFused) load_q();
   float m_run[NRB], l_run[NRB];
   f32x4 o[NRB][8];
 #pragma unroll
@@ -343,7 +370,20 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
       vt_off[dt] = vkey * 256 + (((2 * dt + ((l16 & 3) >> 1)) ^ (2 * (vkey & 7))) * 16) + (l16 & 1) * 8;
   }
 
-  __syncthreads();  // s_blk and s_par are ready
+  if (kFused && tid == 0) {
+    // the write item of (b, g) took an earlier queue id, so it is running or
+    // done whatever else the device holds; the bound only guards the loop
+    for (unsigned spins = 0; flag == 0u; ++spins) {
+      if (spins > kFlagSpinLimit) {
+        err |= SPEC_DEV_TIMEOUT;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      flag = __hip_atomic_load(&a.flags[b * a.Hkv + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();  // s_blk and s_par are ready (and, fused, the item's rows are written)
+  if constexpr (kFused) load_q();
   if (n_it > 0) issue_tile(0);
   if (tail) {
     // the whole tree's bitsets in tile buffer 1 (first written by tile 1, issued
@@ -639,30 +679,235 @@ __device__ __forceinline__ long seq_item(const TArgs2& a, const SeqTable& t, int
          __builtin_amdgcn_readfirstlane(s);
 }
 
+constexpr int kTrigDepths = 32;  // depths whose cosines and sines a write item tabulates (32 KB of LDS)
+
+__device__ __forceinline__ void st_agent_u32(uint16_t* p, uint32_t v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Write item (b, g) of the fused launch: the tree's K rows of kv head g,
+// rotated for their positions Lb + depth(i), and its V rows into the cache at
+// slots Lb + i; the queries of the heads of group g, rotated the same way, into
+// their copy in the workspace (`q`).  Depths come from pointer doubling over the
+// parent row; cosines and sines are tabulated per (depth, pair) when the tree
+// is at most kTrigDepths deep.  Stores are agent-scope atomics (written through
+// to memory, like the split partials), so attention items on any die read the
+// rows once the flag is up.  A bad parent row or prefix length writes no cache
+// row and copies the queries unrotated; a bad block index skips that slot.
 template <int NRB>
+__device__ __forceinline__ void write_item(const TArgs2& a, int b, int g, TileLds<NRB>& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = a.T;
+  int* s_up = reinterpret_cast<int*>(L.tiles);
+  int* s_dep = s_up + kMaxT;
+  double2* trig = reinterpret_cast<double2*>(L.tiles + 2 * kMaxT * sizeof(int));  // [depth][64]
+  static_assert(2 * kMaxT * sizeof(int) + kTrigDepths * 64 * sizeof(double2) <= sizeof(L.tiles), "LDS");
+  const int Lb = a.plen[b];
+  int err = (Lb < 0 || Lb > a.max_blocks * kBlockSize - T) ? SPEC_DEV_LENGTH : 0;
+  if (tid == 0) L.s_last = 0;  // the tree's depth
+  for (int i = tid; i < T; i += 256) {
+    const int p = a.parent[static_cast<long>(b) * T + i];
+    const bool ok = i == 0 ? p == -1 : (p >= 0 && p < i);
+    s_up[i] = (i == 0 || !ok) ? -1 : p;
+    s_dep[i] = i == 0 ? 0 : 1;
+    if (!ok) err |= SPEC_DEV_PARENT;
+  }
+  __syncthreads();
+  for (int r = 0; (1 << r) < T; ++r) {  // after round r, up = the ancestor 2^(r+1) steps above (or -1)
+    int up[2] = {-1, -1}, dep[2] = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + 256 * k;
+      if (i < T) {
+        up[k] = s_up[i];
+        dep[k] = s_dep[i];
+        if (up[k] >= 0) {
+          dep[k] += s_dep[up[k]];
+          up[k] = s_up[up[k]];
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + 256 * k;
+      if (i < T) {
+        s_up[i] = up[k];
+        s_dep[i] = dep[k];
+      }
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < T; i += 256) atomicMax(&L.s_last, s_dep[i]);
+  report(a.status, b, err);
+  const bool bad = __syncthreads_or(err != 0);
+  const bool rotate = a.rotate && !bad;
+  const int n_dep = L.s_last + 1;
+  const bool table = rotate && n_dep <= kTrigDepths;
+  if (table)
+    for (int e = tid; e < n_dep * 64; e += 256) {
+      const double ang = rope_angle(Lb + (e >> 6), e & 63, kD, a.log2_theta);
+      trig[e] = double2{cos(ang), sin(ang)};
+    }
+  __syncthreads();
+
+  // rows of node i: the G query heads of group g, its key, its value; each
+  // half-wave takes one row, lane l the pairs (2l, 2l + 64) and (2l + 1, 2l + 65)
+  // as two 32-bit words; four rows per half-wave in flight together
+  constexpr int kU = 4;
+  const int per = a.G + 2;
+  const int n_rows = T * per;
+  const int hl = lane & 31;
+  const int32_t* bt_b = a.bt + static_cast<long>(b) * a.max_blocks;
+  for (int base = (wave * 2 + (lane >> 5)) * kU; base < n_rows; base += 8 * kU) {
+    uint32_t x0[kU], x1[kU];
+    int node[kU], kind[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int r = min(base + u, n_rows - 1);
+      node[u] = r / per;
+      kind[u] = r % per;  // < G: query head g*G + kind; G: key; G + 1: value
+      const uint16_t* src =
+          kind[u] < a.G ? a.q_src + ((static_cast<long>(b) * T + node[u]) * a.Hq + g * a.G + kind[u]) * kD
+                        : (kind[u] == a.G ? a.k_new : a.v_new) + ((static_cast<long>(b) * T + node[u]) * a.Hkv + g) * kD;
+      x0[u] = *reinterpret_cast<const uint32_t*>(src + 2 * hl);
+      x1[u] = *reinterpret_cast<const uint32_t*>(src + 64 + 2 * hl);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (base + u >= n_rows) break;
+      uint16_t* dst;
+      if (kind[u] < a.G) {
+        dst = a.q_rot + ((static_cast<long>(b) * T + node[u]) * a.Hq + g * a.G + kind[u]) * kD;
+      } else {
+        if (bad) continue;
+        const int t = Lb + node[u];
+        const int blk = bt_b[t / kBlockSize];
+        if (blk < 0 || blk >= a.num_blocks) {
+          if (hl == 0) report(a.status, b, SPEC_DEV_BLOCK);
+          continue;
+        }
+        dst = (kind[u] == a.G ? a.kc : a.vc) + ((static_cast<long>(blk) * a.Hkv + g) * kBlockSize + t % kBlockSize) * kD;
+      }
+      uint32_t y0 = x0[u], y1 = x1[u];
+      if (rotate && kind[u] <= a.G) {
+        const int d = s_dep[node[u]];
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int j = 2 * hl + e;
+          double c, sn;
+          if (table) {
+            const double2 cs = trig[d * 64 + j];
+            c = cs.x;
+            sn = cs.y;
+          } else {
+            const double ang = rope_angle(Lb + d, j, kD, a.log2_theta);
+            c = cos(ang);
+            sn = sin(ang);
+          }
+          float r0, r1;
+          rope_turn(bf16_to_f32(static_cast<uint16_t>(x0[u] >> (16 * e))),
+                    bf16_to_f32(static_cast<uint16_t>(x1[u] >> (16 * e))), c, sn, &r0, &r1);
+          lo |= static_cast<uint32_t>(f32_to_bf16(r0)) << (16 * e);
+          hi |= static_cast<uint32_t>(f32_to_bf16(r1)) << (16 * e);
+        }
+        y0 = lo;
+        y1 = hi;
+      }
+      st_agent_u32(dst + 2 * hl, y0);
+      st_agent_u32(dst + 64 + 2 * hl, y1);
+    }
+  }
+  wait_vm0();  // this wave's stores have completed
+  __syncthreads();
+  if (tid == 0) __hip_atomic_store(&a.flags[b * a.Hkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// kFused: the launch also writes the tree's K/V rows (write items first in the
+// queue); every item then comes from the queue.
+template <int NRB, bool kFused>
 __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const TArgs2 a) {
   __shared__ TileLds<NRB> L;
   const int tid = threadIdx.x;
   bool reorder = false;
   if constexpr (NRB == 1) reorder = a.reorder != 0;  // (the 128-row kernel is at its register limit)
-  if (reorder && a.persist) {
-    // Items from a queue: workgroup w starts with item w of the longest-first
-    // order, then takes the next unclaimed one (an atomic counter in the
-    // workspace) until none is left, so that a CU -- or a whole XCD -- that
-    // runs faster takes more items (each XCD otherwise gets a fixed share of
-    // the workgroup ids, and the slowest sets the end).  The next id is
-    // claimed while the current item runs.  The last workgroup to leave
-    // resets the queue for the next call.
-    const SeqTable t = seq_table(a);
+  if constexpr (kFused && NRB == 2) {
+    // One item per workgroup, its id claimed from the queue on entry (not the
+    // workgroup id: a workgroup that holds an id runs, so every write item an
+    // attention item waits for is running or done); no loop around the item,
+    // which would not fit the 128-row kernel's registers.  The last workgroup
+    // to leave resets the queue and the flags.
+    unsigned* queue = a.counters + static_cast<long>(a.B) * a.Hkv * a.n_rt;
+    if (tid == 0) L.s_next = static_cast<int>(__hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    __syncthreads();
+    const int v = L.s_next;
+    if (v < a.n_write) {
+      write_item<NRB>(a, v / a.Hkv, v % a.Hkv, L);
+    } else {
+      const long item = v - a.n_write;
+      int Lb = a.plen[item / a.n_rt / a.splits / a.Hkv], err = 0;
+      const int cap = a.max_blocks * kBlockSize - a.T;
+      if (Lb < 0 || Lb > cap) {
+        err |= SPEC_DEV_LENGTH;
+        Lb = Lb < 0 ? 0 : cap;
+      }
+      tile_item_run<NRB, true>(a, item, Lb, err, L);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned prev = __hip_atomic_fetch_add(queue + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      L.s_last = (prev == gridDim.x - 1u);
+    }
+    __syncthreads();
+    if (L.s_last) {
+      for (int i = tid; i < a.n_write; i += 256)
+        __hip_atomic_store(&a.flags[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) {
+        __hip_atomic_store(queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    return;
+  }
+  if (kFused || (NRB == 1 && a.persist)) {
+    // Items from a queue: workgroup w starts with id w, then takes the next
+    // unclaimed one (an atomic counter in the workspace) until none is left, so
+    // that a CU -- or a whole XCD -- that runs faster takes more items (each XCD
+    // otherwise gets a fixed share of the workgroup ids, and the slowest sets
+    // the end).  Ids below n_write are write items (fused launch); the rest
+    // name attention items, longest first when `reorder`.  The next id is
+    // claimed while the current item runs.  The last workgroup to leave resets
+    // the queue and the write flags for the next call.
+    SeqTable t{};
+    if (reorder) t = seq_table(a);
+    const int n_attn = reorder ? t.limit : static_cast<int>(a.items);
+    const int total = a.n_write + n_attn;
     unsigned* queue = a.counters + static_cast<long>(a.B) * a.Hkv * a.n_rt;  // [next id, workgroups done]
     const int G = static_cast<int>(gridDim.x);
     int v = static_cast<int>(blockIdx.x);
-    while (v < t.limit) {
+    while (v < total) {
       unsigned nxt = 0;
       if (tid == 0) nxt = __hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      int Lb, err;
-      const long item = seq_item(a, t, v, &Lb, &err);
-      tile_item_run<NRB>(a, item, Lb, err, L);
+      if (kFused && v < a.n_write) {
+        write_item<NRB>(a, v / a.Hkv, v % a.Hkv, L);
+      } else {
+        const int id = v - a.n_write;
+        int Lb, err = 0;
+        long item;
+        if (reorder) {
+          item = seq_item(a, t, id, &Lb, &err);
+        } else {
+          item = id;
+          Lb = a.plen[item / a.n_rt / a.splits / a.Hkv];
+          const int cap = a.max_blocks * kBlockSize - a.T;
+          if (Lb < 0 || Lb > cap) {
+            err |= SPEC_DEV_LENGTH;
+            Lb = Lb < 0 ? 0 : cap;
+          }
+        }
+        tile_item_run<NRB, kFused>(a, item, Lb, err, L);
+      }
       if (tid == 0) L.s_next = G + static_cast<int>(nxt);
       __syncthreads();  // every wave is done with the item's LDS; the next id is published
       v = L.s_next;
@@ -670,7 +915,14 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
     }
     if (tid == 0) {
       const unsigned prev = __hip_atomic_fetch_add(queue + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev == static_cast<unsigned>(G - 1)) {  // every workgroup has claimed past the end: reset
+      L.s_last = (prev == static_cast<unsigned>(G - 1));  // every workgroup has claimed past the end
+    }
+    __syncthreads();
+    if (L.s_last) {
+      if constexpr (kFused)
+        for (int i = tid; i < a.n_write; i += 256)
+        __hip_atomic_store(&a.flags[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) {
         __hip_atomic_store(queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -699,11 +951,12 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
       Lb = Lb < 0 ? 0 : cap;
     }
   }
-  tile_item_run<NRB>(a, item, Lb, err, L);
+  tile_item_run<NRB, kFused>(a, item, Lb, err, L);
 }
 
-// Workgroups of attn_tile_kernel<1> the current device holds at once (its
-// occupancy per CU times the CU count), queried once per device.
+// Workgroups of attn_tile_kernel<NRB, kFused> the current device holds at once
+// (occupancy per CU times the CU count), queried once per device.
+template <int NRB, bool kFused>
 long tile_capacity() {
   static long cache[64];
   int dev = 0;
@@ -711,7 +964,8 @@ long tile_capacity() {
   if (dev < 64 && cache[dev] > 0) return cache[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_tile_kernel<1>, 256, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_tile_kernel<NRB, kFused>, 256, 0) != hipSuccess)
+    return 0;
   const long cap = static_cast<long>(cus) * per_cu;
   if (dev < 64) cache[dev] = cap;
   return cap;
@@ -720,7 +974,7 @@ long tile_capacity() {
 template <int NRB>
 hipError_t run_tile(const TArgs2& args, hipStream_t stream) {
   const long grid = ((args.items + 7) / 8) * 8;
-  hipLaunchKernelGGL((attn_tile_kernel<NRB>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, args);
+  hipLaunchKernelGGL((attn_tile_kernel<NRB, false>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 
@@ -729,28 +983,9 @@ hipError_t run_tile(const TArgs2& args, hipStream_t stream) {
 #ifndef SPEC_TILE_RAGGED_PPS
 #define SPEC_TILE_RAGGED_PPS 256
 #endif
-AttnPlan plan_attn(int B, int T, int Hq, int Hkv, int D, int max_blocks, int dtype) {
-  AttnPlan p{};
-  const int G = Hq / Hkv;
-  p.rows = T * G;
-  if (dtype == SPEC_F32) {
-    p.mode = 0;
-    p.rt = 4;
-    p.nrb = 0;
-    p.n_rt = 0;
-    p.splits = 1;
-    p.pps = max_blocks;
-    p.items = (static_cast<long>(B) * T * Hq + 3) / 4;
-    p.ws_bytes = 0;
-    return p;
-  }
-  (void)D;
-  if (p.rows <= 16) {  // chains, decode, small trees: the streaming kernel
-    plan_stream(p, B, Hkv, max_blocks);
-    return p;
-  }
-  // more rows: 64-row tiles up to 64 rows per kv head, else 128-row tiles; two
-  // workgroups per CU
+// Tile-kernel shape of p.rows query rows per (sequence, kv head): 64-row tiles
+// up to 64 rows, else 128-row tiles; two workgroups per CU.
+static void plan_tile(AttnPlan& p, int B, int Hkv, int max_blocks) {
   p.mode = 2;
   p.nrb = p.rows <= 64 ? 1 : 2;
   p.rt = 64 * p.nrb;
@@ -773,13 +1008,48 @@ AttnPlan plan_attn(int B, int T, int Hq, int Hkv, int D, int max_blocks, int dty
   p.pps = static_cast<int>(pps);
   p.splits = static_cast<int>(splits);
   p.items = base * p.splits;
-  const size_t head = (static_cast<size_t>(base + 2) * sizeof(unsigned) + 255) / 256 * 256;  // + the item queue
+}
+
+AttnPlan plan_attn(int B, int T, int Hq, int Hkv, int D, int max_blocks, int dtype) {
+  AttnPlan p{};
+  const int G = Hq / Hkv;
+  p.rows = T * G;
+  if (dtype == SPEC_F32) {
+    p.mode = 0;
+    p.rt = 4;
+    p.nrb = 0;
+    p.n_rt = 0;
+    p.splits = 1;
+    p.pps = max_blocks;
+    p.items = (static_cast<long>(B) * T * Hq + 3) / 4;
+    p.ws_bytes = 0;
+    return p;
+  }
+  (void)D;
+  if (p.rows <= 16) {  // chains, decode, small trees: the streaming kernel
+    plan_stream(p, B, Hkv, max_blocks);
+    return p;
+  }
+  plan_tile(p, B, Hkv, max_blocks);
+  const size_t head = (static_cast<size_t>(p.items / p.splits + 2) * sizeof(unsigned) + 255) / 256 * 256;  // + the item queue
   p.ws_bytes = p.splits > 1 ? head + static_cast<size_t>(p.items) * p.rt * (kD + 2) * sizeof(float) : 0;
   return p;
 }
 
-hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& L, hipStream_t stream) {
-  if (plan.mode == 3) return launch_attn_stream(plan, L, stream);
+// The fused launch (the tree's K/V write, then attention): the tile kernel for
+// every bf16 shape, its items from the queue.  Workspace: arrival counters, the
+// queue, the write flags; the rotated queries; the split partials.
+AttnPlan plan_attn_write(int B, int T, int Hq, int Hkv, int max_blocks) {
+  AttnPlan p{};
+  p.rows = T * (Hq / Hkv);
+  plan_tile(p, B, Hkv, max_blocks);
+  const size_t base = static_cast<size_t>(p.items / p.splits);
+  const size_t head = ((base + 2 + static_cast<size_t>(B) * Hkv) * sizeof(unsigned) + 255) / 256 * 256;
+  const size_t qbytes = (static_cast<size_t>(B) * T * Hq * kD * sizeof(uint16_t) + 255) / 256 * 256;
+  p.ws_bytes = head + qbytes + (p.splits > 1 ? static_cast<size_t>(p.items) * p.rt * (kD + 2) * sizeof(float) : 0);
+  return p;
+}
+static TArgs2 tile_args(const AttnPlan& plan, const AttnLaunch& L) {
   TArgs2 a{};
   a.q = static_cast<const uint16_t*>(L.q);
   a.k = static_cast<const uint16_t*>(L.k);
@@ -803,6 +1073,12 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& L, hipStream
   a.items = plan.items;
   a.reorder = plan.reorder;
   a.sl2 = L.scale * kLog2e;
+  return a;
+}
+
+hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& L, hipStream_t stream) {
+  if (plan.mode == 3) return launch_attn_stream(plan, L, stream);
+  TArgs2 a = tile_args(plan, L);
   if (plan.splits > 1) {
     const size_t base = static_cast<size_t>(L.B) * L.Hkv * plan.n_rt;
     const size_t head = (static_cast<size_t>(base + 2) * sizeof(unsigned) + 255) / 256 * 256;
@@ -812,17 +1088,53 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& L, hipStream
   }
   if (plan.nrb == 1) {
     if (plan.reorder && plan.splits > 1) {  // the queue of items: one round of resident workgroups
-      const long cap = tile_capacity();
+      const long cap = tile_capacity<1, false>();
       if (cap > 0) {
         a.persist = 1;
         const long grid = std::min<long>(cap, plan.items);
-        hipLaunchKernelGGL((attn_tile_kernel<1>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((attn_tile_kernel<1, false>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
         return hipGetLastError();
       }
     }
     return run_tile<1>(a, stream);
   }
   return run_tile<2>(a, stream);
+}
+
+hipError_t launch_attn_write(const AttnPlan& plan, const AttnWriteLaunch& W, hipStream_t stream) {
+  const AttnLaunch& L = W.attn;
+  TArgs2 a = tile_args(plan, L);
+  char* ws = static_cast<char*>(L.workspace);
+  const size_t base = static_cast<size_t>(L.B) * L.Hkv * plan.n_rt;
+  const size_t head = ((base + 2 + static_cast<size_t>(L.B) * L.Hkv) * sizeof(unsigned) + 255) / 256 * 256;
+  const size_t qbytes = (static_cast<size_t>(L.B) * L.T * L.Hq * kD * sizeof(uint16_t) + 255) / 256 * 256;
+  a.counters = reinterpret_cast<unsigned*>(ws);
+  a.flags = a.counters + base + 2;
+  a.q_rot = reinterpret_cast<uint16_t*>(ws + head);
+  a.q = a.q_rot;
+  a.q_src = static_cast<const uint16_t*>(L.q);
+  if (plan.splits > 1) {
+    a.part_o = reinterpret_cast<float*>(ws + head + qbytes);
+    a.part_ml = a.part_o + static_cast<size_t>(plan.items) * plan.rt * kD;
+  }
+  a.k_new = static_cast<const uint16_t*>(W.k_new);
+  a.v_new = static_cast<const uint16_t*>(W.v_new);
+  a.kc = static_cast<uint16_t*>(const_cast<void*>(L.k));
+  a.vc = static_cast<uint16_t*>(const_cast<void*>(L.v));
+  a.rotate = W.theta > 0.0f ? 1 : 0;
+  a.log2_theta = W.theta > 0.0f ? std::log2(static_cast<double>(W.theta)) : 0.0;
+  a.persist = 1;
+  a.n_write = L.B * L.Hkv;
+  if (plan.nrb == 1) {  // resident workgroups loop over the queue
+    const long cap = tile_capacity<1, true>();
+    if (cap <= 0) return hipErrorInvalidDevice;
+    const long grid = std::min<long>(cap, a.n_write + plan.items);
+    hipLaunchKernelGGL((attn_tile_kernel<1, true>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
+  } else {  // one workgroup per queue id
+    const long grid = a.n_write + plan.items;
+    hipLaunchKernelGGL((attn_tile_kernel<2, true>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace spectree

@@ -70,6 +70,17 @@ struct AttnLaunch {
 };
 
 hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& a, hipStream_t stream);
+
+// The tree's K/V write and the attention in one launch (bf16, head dim 128):
+// attn.q holds the queries before rotation; the rotated ones go to the workspace.
+struct AttnWriteLaunch {
+  AttnLaunch attn;
+  const void* k_new;  // [B,T,Hkv,D] keys before rotation
+  const void* v_new;  // [B,T,Hkv,D]
+  float theta;        // rope base; 0: no rotation
+};
+AttnPlan plan_attn_write(int B, int T, int Hq, int Hkv, int max_blocks);
+hipError_t launch_attn_write(const AttnPlan& plan, const AttnWriteLaunch& w, hipStream_t stream);
 void plan_stream(AttnPlan& p, int B, int Hkv, int max_blocks);
 hipError_t launch_attn_stream(const AttnPlan& plan, const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnPlan& plan, const AttnLaunch& a, hipStream_t stream);

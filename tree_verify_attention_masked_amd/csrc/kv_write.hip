@@ -20,6 +20,7 @@
 #include <math.h>
 
 #include "common.h"
+#include "rope_dev.h"
 
 namespace spectree {
 namespace {
@@ -179,7 +180,6 @@ __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
         x0[u] = ld_elt<kBf16>(sp, sx + lane);
         x1[u] = ld_elt<kBf16>(sp, sx + lane + half);
       }
-      const double inv_freq = exp2(-(2.0 * lane / a.D) * a.log2_theta);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         if (!live[u]) continue;
@@ -193,13 +193,12 @@ __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
         float y0 = x0[u], y1 = x1[u];
         if (rot[u]) {
           if (node[u] != trig_node) {
-            const double ang = static_cast<double>(Lb + s_dep[node[u]]) * inv_freq;
+            const double ang = rope_angle(Lb + s_dep[node[u]], lane, a.D, a.log2_theta);
             c = cos(ang);
             sn = sin(ang);
             trig_node = node[u];
           }
-          y0 = static_cast<float>(static_cast<double>(x0[u]) * c - static_cast<double>(x1[u]) * sn);
-          y1 = static_cast<float>(static_cast<double>(x1[u]) * c + static_cast<double>(x0[u]) * sn);
+          rope_turn(x0[u], x1[u], c, sn, &y0, &y1);
         }
         st_elt<kBf16>(dst[u], di[u] + lane, y0);
         st_elt<kBf16>(dst[u], di[u] + lane + half, y1);

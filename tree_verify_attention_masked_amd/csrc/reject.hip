@@ -48,7 +48,7 @@ constexpr int kMaxTeam = 64;     // workgroups per sequence (one wave merges the
 constexpr int kDeepTeam = 32;    // at most this many for trees with deeper rows (more than 16 nodes)
 constexpr int kEagerCap = 8192;  // floats of eager-row logit slices kept in LDS
 constexpr int kSmallTree = 256;  // trees up to this many nodes: the kernel with the larger eager space
-constexpr int kEagerCapBig = 4096;  // eager-slice floats beside the node arrays of a larger tree
+constexpr int kEagerCapBig = 7680;  // eager-slice floats beside the node arrays of a larger tree
 constexpr int kSliceCap = 8192;  // floats of the current row's logits / draft probs kept in LDS
 constexpr int kHeaderBytes = 256;  // workspace header: word 0 exit counter of the grid, word 1 call epoch
 constexpr unsigned kSpinLimit = 1u << 24;
@@ -572,8 +572,8 @@ __device__ __forceinline__ void merge_row(const Rec& r, bool member, bool greedy
 
 // kFits: the slice (S <= kSliceCap floats) lives in LDS, so every slice access is an
 // LDS access; otherwise the slices are read from global memory where they lie.
-// kTree: the largest tree (kSmallTree, or kMaxT with half the eager space, so
-// that the node arrays fit beside it).
+// kTree: the largest tree (kSmallTree, or kMaxT with a smaller eager space, so
+// that the node arrays fit beside it in the 160 KB of LDS).
 template <bool kFits, int kTree>
 __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   constexpr int kEager = kTree <= kSmallTree ? kEagerCap : kEagerCapBig;

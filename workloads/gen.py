@@ -145,18 +145,23 @@ def tree_random_recursive(n: int, max_depth: int, rng: np.random.Generator) -> l
     return parent
 
 
+def sequoia_accept_profile(rng: np.random.Generator, rank_cap: int = 64) -> np.ndarray:
+    """Acceptance by child rank: a_r = 0.8/r*(1+0.05*xi_r), xi ~ U(-1, 1), made non-increasing."""
+    xi = rng.uniform(-1.0, 1.0, size=rank_cap)
+    a = np.array([0.8 / r * (1.0 + 0.05 * xi[r - 1]) for r in range(1, rank_cap + 1)])
+    return np.minimum.accumulate(a)
+
+
 def tree_sequoia_profile(n: int, depth_cap: int, rng: np.random.Generator, rank_cap: int = 64):
     """Best-first tree on an acceptance-by-rank profile (the DP-style shape).
 
-    The r-th child (r = 1, 2, ...) of any node has weight a_r = 0.8/r*(1+0.05*xi_r),
-    xi ~ U(-1, 1), made non-increasing; a node's score is the product of the
-    weights on its path.  The n highest-score nodes (depth <= depth_cap) are
-    kept and numbered breadth first; children keep their rank order.
-    Returns (parent, rank) with rank[i] = 1-based child rank of node i.
+    The r-th child (r = 1, 2, ...) of any node has weight a_r (sequoia_accept_profile);
+    a node's score is the product of the weights on its path.  The n highest-score
+    nodes (depth <= depth_cap) are kept and numbered breadth first; children keep
+    their rank order.  Returns (parent, rank, a) with rank[i] = 1-based child rank
+    of node i.
     """
-    xi = rng.uniform(-1.0, 1.0, size=rank_cap)
-    a = np.array([0.8 / r * (1.0 + 0.05 * xi[r - 1]) for r in range(1, rank_cap + 1)])
-    a = np.minimum.accumulate(a)
+    a = sequoia_accept_profile(rng, rank_cap)
     # heap of (-score, creation, parent_creation, rank, depth, parent_score)
     heap = [(-1.0, 0, -1, 0, 0, 1.0)]
     created = 1
@@ -186,7 +191,7 @@ def tree_sequoia_profile(n: int, depth_cap: int, rng: np.random.Generator, rank_
     parent = [-1 if c[1] < 0 else new_index[c[1]] for c in order]
     rank = [c[2] for c in order]
     assert all(c[1] in by_cid or c[1] < 0 for c in kept)
-    return parent, rank
+    return parent, rank, a
 
 
 # ----------------------------------------------------------------------------
@@ -397,7 +402,9 @@ def make_workload(*, name="custom", tag=100, B=1, Hq=2, Hkv=2, D=64, dtype="f32"
             elif tree == "random":
                 p = tree_random_recursive(T, max_depth, r_tree)
             elif tree == "sequoia":
-                p, rank = tree_sequoia_profile(T, max_depth, r_tree)
+                p, rank, a_rank = tree_sequoia_profile(T, max_depth, r_tree)
+                if b == 0:
+                    info["accept_profile"] = a_rank.tolist()
             else:
                 raise ValueError(tree)
             tl, q = _node_rows(r_rows, len(p), V, tau_d)
