@@ -63,7 +63,7 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 METRIC = "verified tree tokens/sec at 1 MI355X"
 
 
-KERNEL_KEYS = (("tree_attn", ("attn_",)), ("tree_reject_compact", ("reject",)), ("kv_compact", ("kv_compact",)),
+KERNEL_KEYS = (("tree_write_attn", ("attn_tile_kernel<1, true>", "attn_tile_kernel<2, true>")), ("tree_attn", ("attn_",)), ("tree_reject_compact", ("reject",)), ("kv_compact", ("kv_compact",)),
                ("tree_kv_write", ("kv_write",)), ("tree_truncate", ("truncate_kernel",)))
 CALIB_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
 CALIB_BYTES_BIG = 1 << 30  # a second calibration copy, four times the 256 MB MALL
@@ -74,6 +74,7 @@ def log(*a):
 
 
 KERNEL_SOURCES = {  # the sources each kernel key is built from (with common.h and the C-ABI header)
+    "tree_write_attn": ("attn_bf16.hip", "rope_dev.h"),
     "tree_attn": ("attn_bf16.hip", "attn_stream.hip", "attn_f32.hip"),
     "tree_reject_compact": ("reject.hip", "compact_dev.h"),
     "kv_compact": ("compact.hip", "compact_dev.h"),
@@ -249,6 +250,18 @@ def attn_work(w):
     return kv + qo, 4.0 * w.Hq * w.D * pairs
 
 
+def rope_theta(w):
+    """Rotary base of the layer a workload follows: Llama-3 (vocabulary 128256) 500000, else Llama-2's 10000."""
+    return 500000.0 if w.V == 128256 else 10000.0
+
+
+def write_bytes(w):
+    """Algorithmic bytes the tree's K/V write adds to a step: the nodes' new K and V rows read, and written
+    into the cache (the queries are read once either way, counted with the attention)."""
+    elt = 2 if w.dtype == "bf16" else 4
+    return 4 * w.B * w.T * w.Hkv * w.D * elt
+
+
 def reject_bytes(w, nacc, stop_rejections):
     """Bytes the walk needs: target-logit rows of the visited nodes, plus the
     draft row of a stop node whose residual had to be formed."""
@@ -264,14 +277,15 @@ def compact_bytes(w, acc, nacc):
     return moved * w.Hkv * w.D * elt * 2 * 2  # K and V, read + write
 
 
-def cpu_baseline(w, budget_s, max_seqs=8):
+def cpu_baseline(w, budget_s, theta=None, max_seqs=8):
     """The oracle (as it stands) on the same workload, timed on the host cores.
 
     A batch of more than `max_seqs` sequences is sampled: the first `max_seqs`
     of them, with their own pages (the oracle's compaction copies the whole
     cache it is given).  The value is verified tree tokens per second of the
-    oracle's attention + walk + compaction over the sample, repeated until
-    `budget_s` seconds have passed."""
+    oracle's step over the sample -- the tree's K/V write with rotation (when
+    `theta` is given, as in the timed step), attention, walk, compaction --
+    repeated until `budget_s` seconds have passed."""
     import oracle
     from workloads import sub_batch
 
@@ -281,22 +295,35 @@ def cpu_baseline(w, budget_s, max_seqs=8):
     except Exception:  # pragma: no cover
         threads = 1
     sample = w if w.B <= max_seqs else sub_batch(w, range(max_seqs))
+    from workloads.gen import f32_to_bf16_bits
+
+    rng = np.random.default_rng(7)
+    kv_new = [rng.standard_normal((sample.B, sample.T, sample.Hkv, sample.D), dtype=np.float32) for _ in range(2)]
+    if sample.dtype == "bf16":  # the oracle reads every input in the sample's storage type
+        kv_new = [f32_to_bf16_bits(x) for x in kv_new]
     steps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.tree_attention(sample.q, sample.k_cache, sample.v_cache, sample.block_table, sample.prefix_lens,
-                              sample.parent, sample.scale, dtype=sample.dtype)
+        if theta is None:
+            q, kc, vc, dt = sample.q, sample.k_cache, sample.v_cache, sample.dtype
+        else:  # fp64 rows in, fp64 caches out
+            q, kc, vc = oracle.tree_kv_write(kv_new[0], kv_new[1], sample.q, sample.k_cache, sample.v_cache,
+                                             sample.block_table, sample.prefix_lens, sample.parent, theta,
+                                             dtype=sample.dtype)
+            dt = "f64"
+        oracle.tree_attention(q, kc, vc, sample.block_table, sample.prefix_lens, sample.parent, sample.scale,
+                              dtype=dt)
         r = oracle.tree_reject(sample.target_logits, sample.draft_probs, sample.draft_tokens, sample.parent,
                                sample.temperature, sample.without_replacement, sample.seed, steps)
-        oracle.kv_compact(sample.k_cache, sample.v_cache, sample.block_table, sample.prefix_lens,
-                          r["accepted_nodes"], r["num_accepted"])
+        oracle.kv_compact(kc, vc, sample.block_table, sample.prefix_lens, r["accepted_nodes"], r["num_accepted"])
         steps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or steps >= 200:
             break
     what = (f"sequences 0-{sample.B - 1} of the {w.B}-sequence batch" if sample is not w else "the whole batch")
     return {"value": sample.B * sample.T * steps / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{steps} steps over {what} (fp64 NumPy attention + walk + compaction), {el:.1f} s, "
+            "sample": f"{steps} steps over {what} (fp64 NumPy {'K/V write with rotation + ' if theta else ''}"
+                      f"attention + walk + compaction), {el:.1f} s, "
                       f"{len(os.sched_getaffinity(0))} host cores visible"}
 
 
@@ -350,7 +377,9 @@ def sweep():
     (graphs of back-to-back calls over input copies that together exceed the
     256 MB MALL where memory allows).  Each point times the attention and the
     sampler with compaction (the step), and the tree K/V write that precedes them
-    (reported on its own).  On the Sequoia shape each point also carries the
+    (reported on its own), and spec_tree_write_attn, the write and the attention
+    in one launch (the step with the write: it and the sampler with compaction).
+    On the Sequoia shape each point also carries the
     expected tokens one step generates with the Sequoia-optimal tree of that size
     and depth bound for the generator's acceptance-by-rank vector
     (spec_sequoia_tree), and so the expected generated tokens per second of
@@ -399,12 +428,23 @@ def sweep():
 
                 kv_new = torch.zeros((w.B, w.T, w.Hkv, w.D), dtype=cps[0]["k"].dtype, device=dev)
 
+                theta = rope_theta(w)
+
                 def kvw(c):
-                    stv.spec_tree_kv_write(kv_new, kv_new, c["q"], c["k"], c["v"], bt, lens, parent, 10000.0,
+                    stv.spec_tree_kv_write(kv_new, kv_new, c["q"], c["k"], c["v"], bt, lens, parent, theta,
                                            status=status)
 
+                ws_wa = stv.spec_tree_write_attn_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, w.max_blocks,
+                                                                stv.SPEC_BF16)
+                wa_ws = torch.zeros(max(ws_wa, 1), dtype=torch.uint8, device=dev)
+
+                def wattn(c):
+                    stv.spec_tree_write_attn(kv_new, kv_new, c["q"], c["k"], c["v"], bt, lens, parent, theta,
+                                             scale=w.scale, out=c["out"], status=status, workspace=wa_ws)
+
                 us = {}
-                for key, fn in (("attn_us", attn), ("reject_compact_us", rejc), ("kv_write_us", kvw)):
+                for key, fn in (("attn_us", attn), ("reject_compact_us", rejc), ("kv_write_us", kvw),
+                                ("write_attn_us", wattn)):
                     for c in cps:  # eager pass: validates every copy
                         fn(c)
                     torch.cuda.synchronize()
@@ -422,6 +462,8 @@ def sweep():
                                   "attn_us": round(us["attn_us"], 2),
                                   "reject_compact_us": round(us["reject_compact_us"], 2),
                                   "kv_write_us": round(us["kv_write_us"], 2),
+                                  "write_attn_us": round(us["write_attn_us"], 2),
+                                  "step_with_write_us": round(us["write_attn_us"] + us["reject_compact_us"], 2),
                                   "step_us": round(step, 2), "verified_tokens_per_s": round(w.B * w.T / step * 1e6, 1),
                                   "attn_GBps": round(a_bytes / us["attn_us"] / 1e3, 1),
                                   "attn_TFLOPs": round(a_flops / us["attn_us"] / 1e6, 2), "input_copies": R}),
@@ -435,6 +477,7 @@ def measure(cfg, args, quick=False):
 
     import tree_verify_attention_masked_amd as stv
     from workloads import make_config
+    from workloads.gen import f32_to_bf16_bits
 
     dev = torch.device("cuda:0")
     log(f"[bench] building workload {cfg}")
@@ -451,15 +494,24 @@ def measure(cfg, args, quick=False):
     log(f"[bench] {R} input copies of {per_copy / 1e6:.1f} MB")
     shared = dict(bt=up(w.block_table), lens=up(w.prefix_lens), parent=up(w.parent), tok=up(w.draft_tokens))
     copies = []
+    fused = w.dtype == "bf16"  # the step writes the tree's K/V rows in the attention launch
+    theta = rope_theta(w)
+    rng = np.random.default_rng(1000 + cfg)
     for _ in range(R):
         c = dict(q=up(w.q, True), k=up(w.k_cache, True), v=up(w.v_cache, True), logits=up(w.target_logits),
                  probs=up(w.draft_probs))
+        if fused:  # the nodes' new K and V rows (before rotation), drawn here
+            for key in ("k_new", "v_new"):
+                x = rng.standard_normal((w.B, w.T, w.Hkv, w.D), dtype=np.float32)
+                c[key] = torch.from_numpy(f32_to_bf16_bits(x)).view(torch.bfloat16).to(dev)
         c["out"] = torch.empty_like(c["q"])
         c["status"] = torch.zeros((w.B,), dtype=torch.int32, device=dev)
         copies.append(c)
     code = stv.SPEC_BF16 if w.dtype == "bf16" else stv.SPEC_F32
     ws_attn = stv.spec_tree_attn_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, w.max_blocks, code)
     attn_ws = torch.zeros(max(ws_attn, 1), dtype=torch.uint8, device=dev)  # zero once: split arrival counters
+    ws_wa = stv.spec_tree_write_attn_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, w.max_blocks, code) if fused else 0
+    wa_ws = torch.zeros(max(ws_wa, 1), dtype=torch.uint8, device=dev)  # zero once: work counter and flags
     rej_ws = torch.zeros(int(stv.load_library().spec_tree_reject_workspace_size(w.B, w.T, w.V)),
                          dtype=torch.uint8, device=dev)  # zero once: the sampler's epochs and tagged exchange slots
 
@@ -479,6 +531,11 @@ def measure(cfg, args, quick=False):
         stv.spec_tree_attn(c["q"], c["k"], c["v"], shared["bt"], shared["lens"], shared["parent"], scale=w.scale,
                            out=c["out"], status=c["status"], workspace=attn_ws if ws_attn else None)
 
+    def write_attn(c):
+        stv.spec_tree_write_attn(c["k_new"], c["v_new"], c["q"], c["k"], c["v"], shared["bt"], shared["lens"],
+                                 shared["parent"], theta, scale=w.scale, out=c["out"], status=c["status"],
+                                 workspace=wa_ws)
+
     def reject_compact(c, sl=None):
         sl = sl or slots[0]
         stv.spec_tree_reject_compact(c["logits"], c["probs"], shared["tok"], shared["parent"], w.temperature,
@@ -487,7 +544,11 @@ def measure(cfg, args, quick=False):
                                      num_accepted=sl["nacc"], new_lens=sl["new_lens"], status=c["status"],
                                      workspace=rej_ws)
 
-    def step(sl):
+    def step(sl):  # the timed step: (K/V write and) attention, then rejection + compaction
+        (write_attn if fused else attn)(sl["c"])
+        reject_compact(sl["c"], sl)
+
+    def step_plain(sl):  # attention on rows already in the cache, then rejection + compaction
         attn(sl["c"])
         reject_compact(sl["c"], sl)
 
@@ -499,45 +560,54 @@ def measure(cfg, args, quick=False):
             torch.cuda.synchronize()
             del src, dst
 
-    for sl in slots:  # eager pass: validates every copy and slot
-        step(sl)
-    torch.cuda.synchronize()
-    st = sum(int(c["status"].abs().sum()) for c in copies)
-    if st:
-        raise SystemExit(f"device reported input errors: {[c['status'].tolist() for c in copies]}")
+    for fn in ((step, step_plain) if fused else (step,)):
+        for sl in slots:  # eager pass: validates every copy and slot
+            fn(sl)
+        torch.cuda.synchronize()
+        st = sum(int(c["status"].abs().sum()) for c in copies)
+        if st:
+            raise SystemExit(f"device reported input errors: {[c['status'].tolist() for c in copies]}")
 
-    step_graphs = [capture_graph([lambda sl=sl: step(sl)]) for sl in slots]
-    run_graph = capture_graph([lambda sl=sl: step(sl) for sl in slots])
-    log(f"[bench] captured {len(step_graphs)} step graphs and one graph of {G} steps; warmup {args.warmup}")
-    for i in range(args.warmup):
-        step_graphs[i % G].replay()
-    torch.cuda.synchronize()
+    def timed(fn, what):
+        """K steps of fn (graphs of G slots) between synchronisations, and the spread of single steps."""
+        step_graphs = [capture_graph([lambda sl=sl: fn(sl)]) for sl in slots]
+        run_graph = capture_graph([lambda sl=sl: fn(sl) for sl in slots])
+        log(f"[bench] {what}: captured {len(step_graphs)} step graphs and one graph of {G} steps; "
+            f"warmup {args.warmup}")
+        for i in range(args.warmup):
+            step_graphs[i % G].replay()
+        torch.cuda.synchronize()
+        K = args.steps
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K // G):
+            run_graph.replay()
+        for i in range(K % G):
+            step_graphs[i % G].replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        log(f"[bench] {what}: {K} steps ({K // G} replays of {G} steps + {K % G} single steps): "
+            f"wall {wall * 1e3:.3f} ms")
+        # spread: single-step replays, each bracketed by events on the current stream
+        n_spread = 30 if quick else 100
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread + 1)]
+        evs[0].record()
+        for i in range(n_spread):
+            step_graphs[i % G].replay()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        per = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n_spread)])
+        spread = {"p10": round(float(np.percentile(per, 10)), 2), "p50": round(float(np.percentile(per, 50)), 2),
+                  "p90": round(float(np.percentile(per, 90)), 2), "n": n_spread,
+                  "note": "single-step graph replays, launch gap included"}
+        return wall * 1e3 / K, w.B * w.T * K / wall, spread
 
-    K = args.steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(K // G):
-        run_graph.replay()
-    for i in range(K % G):
-        step_graphs[i % G].replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    log(f"[bench] {K} steps ({K // G} replays of {G} steps + {K % G} single steps): wall {wall * 1e3:.3f} ms")
-    ms_per_step = wall * 1e3 / K
-    value = w.B * w.T * K / wall
-
-    # spread: 100 single-step replays, each bracketed by events on the current stream
-    n_spread = 30 if quick else 100
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread + 1)]
-    evs[0].record()
-    for i in range(n_spread):
-        step_graphs[i % G].replay()
-        evs[i + 1].record()
-    torch.cuda.synchronize()
-    per = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n_spread)])
-    spread = {"p10": round(float(np.percentile(per, 10)), 2), "p50": round(float(np.percentile(per, 50)), 2),
-              "p90": round(float(np.percentile(per, 90)), 2), "n": n_spread,
-              "note": "single-step graph replays, launch gap included"}
+    ms_per_step, value, spread = timed(step, "step")
+    plain = None
+    if fused:
+        ms_plain, value_plain, spread_plain = timed(step_plain, "step without the K/V write")
+        plain = {"value": round(value_plain, 1), "ms_per_step": round(ms_plain, 5), "step_us": spread_plain,
+                 "note": "spec_tree_attn on rows already in the cache, then spec_tree_reject_compact"}
 
     # accepted tokens per step over every slot's walk (each slot has its own offset)
     accs = [sl["acc"].cpu().numpy() for sl in slots]
@@ -547,7 +617,8 @@ def measure(cfg, args, quick=False):
     # per-kernel average durations: one graph = reps launches of one call over the copies
     reps = args.kernel_reps or max(R, 8 * R if per_copy < 100e6 else R)
     kdur = {}
-    for name, fn in (("tree_attn", attn), ("tree_reject_compact", reject_compact)):
+    timed_calls = (("tree_write_attn", write_attn),) if fused else ()
+    for name, fn in timed_calls + (("tree_attn", attn), ("tree_reject_compact", reject_compact)):
         kdur[name] = seconds_per_call(fn, copies, reps, 60 if quick else 200)
         log(f"[bench] {name}: {kdur[name] * 1e6:.2f} us per call")
 
@@ -561,23 +632,33 @@ def measure(cfg, args, quick=False):
         rb.append(reject_bytes(w, nacc, stop_rej))
         cb.append(compact_bytes(w, acc, nacc))
     rc_bytes = float(np.mean(rb)) + float(np.mean(cb))
+    w_bytes = write_bytes(w) if fused else 0
     work = {"tree_attn": ("hbm", a_bytes, a_flops), "tree_reject_compact": ("hbm", rc_bytes, 0.0)}
+    if fused:
+        work["tree_write_attn"] = ("hbm", a_bytes + w_bytes, a_flops)
     kernels = {}
     for name, (b_, by, fl) in work.items():
         kernels[name] = {"us": round(kdur[name] * 1e6, 2), "bytes": int(by),
                          "GB/s": round(by / kdur[name] / 1e9, 1)}
         if fl:
             kernels[name]["TFLOP/s"] = round(fl / kdur[name] / 1e12, 2)
-    kernels["tree_attn"]["hbm_frac"] = round(a_bytes / kdur["tree_attn"] / 1e9 / HBM_PEAK_GBS, 4)
-    kernels["tree_attn"]["mfma_frac"] = round(a_flops / kdur["tree_attn"] / 1e12 / BF16_PEAK_TFLOPS, 4)
-    step_bytes = a_bytes + rc_bytes
+    for name in ("tree_write_attn", "tree_attn") if fused else ("tree_attn",):
+        kernels[name]["hbm_frac"] = round(work[name][1] / kdur[name] / 1e9 / HBM_PEAK_GBS, 4)
+        kernels[name]["mfma_frac"] = round(a_flops / kdur[name] / 1e12 / BF16_PEAK_TFLOPS, 4)
+    if fused:
+        kernels["tree_write_attn"]["rope_theta"] = theta
+        kernels["tree_attn"]["in_step"] = False
+    step_bytes = a_bytes + w_bytes + rc_bytes
     step_roof = {"bound": "hbm", "bytes": int(step_bytes), "achieved": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
                  "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                 "note": "algorithmic bytes of the whole step (attention, the walked rows, moved KV rows) / step time"}
-    return dict(w=w, value=value, ms_per_step=ms_per_step, spread=spread, lp1=lp1, kdur=kdur, work=work,
+                 "note": "algorithmic bytes of the whole step (the tree's K/V rows in and out, attention, the "
+                         "walked rows, moved KV rows) / step time" if fused else
+                         "algorithmic bytes of the whole step (attention, the walked rows, moved KV rows) / step time"}
+    step_kernels = {k: v for k, v in kdur.items() if not (fused and k == "tree_attn")}
+    return dict(w=w, value=value, ms_per_step=ms_per_step, spread=spread, lp1=lp1, kdur=step_kernels, work=work,
                 kernels=kernels, step_roof=step_roof, copies=copies, slots=slots, shared=shared, R=R, reps=reps,
-                a_bytes=a_bytes, a_flops=a_flops)
+                a_bytes=a_bytes, a_flops=a_flops, fused=fused, plain=plain, theta=theta)
 
 
 def roofline_of(m):
@@ -585,7 +666,7 @@ def roofline_of(m):
     kdur, work = m["kdur"], m["work"]
     dominant = max(kdur, key=kdur.get)
     bound, bytes_, flops = work[dominant]
-    if dominant == "tree_attn" and flops / max(bytes_, 1) > BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+    if dominant in ("tree_attn", "tree_write_attn") and flops / max(bytes_, 1) > BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
         bound = "mfma"
     if bound == "hbm":
         achieved = bytes_ / kdur[dominant] / 1e9
@@ -650,16 +731,17 @@ def main():
     kernels = m["kernels"]
     value_main, ms_main, spread_main, step_roof_main, R_main = (m["value"], m["ms_per_step"], m["spread"],
                                                                  m["step_roof"], m["R"])
+    fused_main, plain_main, theta_main = m["fused"], m["plain"], m["theta"]
 
-    # The step before attention (not part of the timed step, whose inputs already
-    # hold the tree's rows): the tree's K/V rows into the cache, keys and queries
-    # rotated for their tree positions.
+    # The step before attention as a launch of its own (the timed bf16 step does
+    # it inside the attention launch): the tree's K/V rows into the cache, keys
+    # and queries rotated for their tree positions.
     kv_new = dict(k=torch.zeros((w.B, w.T, w.Hkv, w.D), dtype=copies[0]["k"].dtype, device=dev))
     kv_new["v"] = torch.zeros_like(kv_new["k"])
 
     def kv_write(c):
         stv.spec_tree_kv_write(kv_new["k"], kv_new["v"], c["q"], c["k"], c["v"], shared["bt"], shared["lens"],
-                               shared["parent"], 10000.0, status=c["status"])
+                               shared["parent"], rope_theta(w), status=c["status"])
 
     t_kvw = seconds_per_call(kv_write, copies, reps, 200)
     log(f"[bench] tree_kv_write: {t_kvw * 1e6:.2f} us per call")
@@ -695,6 +777,7 @@ def main():
         re_ = roofline_of(me)
         extra[me["w"].name] = {"value": round(me["value"], 1), "unit": "tokens/s",
                                "ms_per_step": round(me["ms_per_step"], 5), "step_us": me["spread"],
+                               "kv_write_in_step": me["fused"], "without_kv_write": me["plain"],
                                "roofline": re_, "step_roofline": me["step_roof"], "kernels": me["kernels"],
                                "accepted_per_step": round(float(me["lp1"].mean()), 3), "config": me["w"].summary()}
         del me
@@ -703,7 +786,7 @@ def main():
     cpu = None
     if args.cpu_budget > 0:
         log(f"[bench] oracle baseline (~{args.cpu_budget:.0f} s)")
-        cpu = cpu_baseline(w, args.cpu_budget)
+        cpu = cpu_baseline(w, args.cpu_budget, theta_main if fused_main else None)
 
     cfg = w.summary()
     line = {
@@ -712,6 +795,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic", "config": cfg, "roofline": roof, "step_roofline": step_roof_main,
         "cpu_baseline": cpu, "kernels": kernels, "step_us": spread_main, "accepted_per_step": accepted,
+        "kv_write_in_step": fused_main, "without_kv_write": plain_main,
         "input_copies": R_main, "extra": extra,
     }
     print(json.dumps(line), flush=True)

@@ -329,12 +329,16 @@ int spec_tree_kv_write(const void* k_new, const void* v_new, void* q, void* k_ca
  * vLLM") fused with the tree attention over the prefix and the tree.
  *
  * Writes the same cache rows, bit for bit, as spec_tree_kv_write, and the same
- * `out` as spec_tree_attn called after it on the rotated queries (bit for bit
- * when T * Hq / Hkv > 16; below that spec_tree_attn sums in another order).
- * The caller's `q` is not modified: the rotated queries live in the workspace.  Inside the launch the first B * Hkv work items write the rows of
- * one (sequence, kv head) each; an attention item starts once the rows of its
- * (sequence, kv head) are written (work items are claimed from a counter in
- * the workspace, writers first, so this wait always ends).
+ * `out`, bit for bit, as spec_tree_attn called after it on the queries it
+ * rotated.  The caller's `q` is not modified.  Inside the launch the first
+ * work items write the tree's K/V rows of one sequence 64 rows at a time and
+ * count them; the attention items rotate their own queries, and an item that
+ * reads the tree's keys starts once its sequence's rows are all written (work
+ * items are claimed from a counter in the workspace, writers first and the
+ * splits holding tree keys last, so this wait always ends).  Shapes with at
+ * most 16 query rows per kv head (T * Hq / Hkv <= 16) take two launches
+ * instead: the write, with the rotated queries going to the workspace, then
+ * the attention.
  *
  *   k_new, v_new [B, T, Hkv, D] bf16: the nodes' keys (before rotation) and values
  *   q            [B, T, Hq, D] bf16: the queries before rotation (read only)
@@ -343,14 +347,15 @@ int spec_tree_kv_write(const void* k_new, const void* v_new, void* q, void* k_ca
  *                of each sequence only
  *   rope_theta   >= 0 and finite; 0 writes and uses the rows unrotated
  *   workspace    >= spec_tree_write_attn_workspace_size(...) bytes, never
- *                NULL (it holds the work counter, B * Hkv flags and the
- *                rotated queries), zero-filled before the first call; each
- *                completed call leaves its counters and flags zero, so a
- *                workspace serves later calls of the same shape as it is
- *                (re-zero it when the shape changes, as for spec_tree_attn)
+ *                NULL (it holds the work counter, B counts of written rows
+ *                and the split partials), zero-filled before the first call;
+ *                each completed call leaves its counters zero, so a workspace
+ *                serves later calls of the same shape as it is (re-zero it
+ *                when the shape changes, as for spec_tree_attn)
  * Errors: a bad parent row or prefix length writes no cache row of that
- * sequence, and its attention runs on the unrotated queries (status reports
- * it); a bad block index skips that slot (SPEC_DEV_BLOCK).
+ * sequence (status reports it; that sequence's outputs are then not
+ * meaningful, the other sequences' are exact); a bad block index skips that
+ * slot (SPEC_DEV_BLOCK).
  * Supported: bf16, D = 128, block_size = 16, 1 <= T <= 512, Hq % Hkv == 0.
  * ---------------------------------------------------------------------- */
 size_t spec_tree_write_attn_workspace_size(int B, int T, int Hq, int Hkv, int D, int max_blocks_per_seq,

@@ -166,18 +166,19 @@ struct TArgs2 {
   long items;
   float sl2;
   // The tree's K/V write in the same launch: the queue's first n_write ids are
-  // write items, one per (b, g), then come the attention items; an attention
-  // item waits for its (b, g) flag before it reads queries or tree keys.
-  int n_write;             // B * Hkv
-  int rotate;              // rope_theta > 0
+  // write items, n_chunks per sequence (chunk_rows of its 2 T Hkv K and V rows each),
+  // then come the attention items, which rotate their own queries; an item
+  // that holds tree keys waits until its sequence's chunks are all written.
+  int n_write;             // B * n_chunks
+  int n_chunks;            // per sequence: ceil(2 T Hkv / chunk_rows)
+  int chunk_rows;          // a multiple of 8, at most 64
+  int rotate;              // rope_theta > 0 (`q` holds the queries before rotation)
   double log2_theta;
-  const uint16_t* q_src;   // [B,T,Hq,D] queries before rotation; `q` is then their rotated copy
   const uint16_t* k_new;   // [B,T,Hkv,D] the nodes' keys before rotation
   const uint16_t* v_new;   // [B,T,Hkv,D] their values
-  uint16_t* q_rot;         // = q, written by the write items
   uint16_t* kc;            // = k, = v: the cache the write items fill
   uint16_t* vc;
-  unsigned* flags;         // [B * Hkv]: nonzero once (b, g)'s rows are written
+  unsigned* flags;         // [B]: chunks of the sequence written so far
 };
 
 constexpr int kAncWords = kMaxT / 64;  // words of one node's ancestor-or-self bitset
@@ -246,6 +247,166 @@ struct TileLds {
 static_assert(kMaxT * kAncWords * sizeof(uint64_t) <= kTileBytes,
               "the whole tree's bitsets are built in the second tile buffer");
 
+constexpr int kTrigDepths = 27;  // depths whose cosines and sines a fused item tabulates (27 KB of LDS)
+constexpr int kTrigOffset = 2 * kMaxT * sizeof(int) + 256;  // the table's place in its 32 KB buffer
+static_assert(kTrigOffset + kTrigDepths * 64 * sizeof(double2) <= kTileBytes, "the table fits a tile buffer");
+
+__device__ __forceinline__ void st_agent_u32(uint16_t* p, uint32_t v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every node's depth by pointer doubling over a parent row in LDS (a node whose
+// parent is not an earlier node stops its path there): s_dep[i], with s_up as
+// scratch.  Every thread of the 256-thread workgroup calls it (T <= 512); the
+// rounds' barriers also publish what the caller wrote to LDS before the call.
+__device__ void tree_depths(const int* par, int T, int* s_up, int* s_dep) {
+  const int tid = threadIdx.x;
+  int pending = 0;
+  for (int i = tid; i < T; i += 256) {
+    const int p = par[i];
+    const bool ok = i == 0 ? p == -1 : (p >= 0 && p < i);
+    s_up[i] = (i == 0 || !ok) ? -1 : p;
+    s_dep[i] = i == 0 ? 0 : 1;
+    pending |= s_up[i] >= 0;
+  }
+  // each round: up = the ancestor twice as far above (or -1); the rounds end
+  // once no node has an ancestor left to jump to (ceil(log2(depth)) of them)
+  while (__syncthreads_or(pending)) {
+    int up[2] = {-1, -1}, dep[2] = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + 256 * k;
+      if (i < T) {
+        up[k] = s_up[i];
+        dep[k] = s_dep[i];
+        if (up[k] >= 0) {
+          dep[k] += s_dep[up[k]];
+          up[k] = s_up[up[k]];
+        }
+      }
+    }
+    __syncthreads();
+    pending = 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + 256 * k;
+      if (i < T) {
+        s_up[i] = up[k];
+        s_dep[i] = dep[k];
+        pending |= up[k] >= 0;
+      }
+    }
+  }
+}
+
+constexpr int kWalkSteps = 32;  // parent chains walked one step at a time up to this length
+
+// Depths of nodes n0 .. n1 (at most 256 of them) into s_dep: each by walking its
+// parent chain when every such chain is at most kWalkSteps long (a bad parent
+// ends a chain), else for the whole tree by pointer doubling (tree_depths); and
+// their [min, max] into s_rng.  Every thread of the workgroup calls it.
+__device__ void node_depths(const int* par, int T, int n0, int n1, int* s_up, int* s_dep, int* s_rng) {
+  const int tid = threadIdx.x;
+  const int i = n0 + tid;
+  int d = 0, j = i;
+  if (i <= n1) {
+    for (int k = 0; k < kWalkSteps && j > 0; ++k) {
+      const int p = par[j];
+      if (!(p >= 0 && p < j)) {
+        j = 0;
+        break;
+      }
+      j = p;
+      ++d;
+    }
+  }
+  if (tid == 0) {
+    s_rng[0] = 0x7fffffff;
+    s_rng[1] = -1;
+  }
+  if (__syncthreads_or(i <= n1 && j > 0)) {
+    tree_depths(par, T, s_up, s_dep);
+  } else if (i <= n1) {
+    s_dep[i] = d;
+  }
+  __syncthreads();
+  if (i <= n1) {
+    atomicMin(&s_rng[0], s_dep[i]);
+    atomicMax(&s_rng[1], s_dep[i]);
+  }
+  __syncthreads();
+}
+
+// Cosine and sine at position p of pair j (out of line: it would take registers from the item).
+__device__ __noinline__ double2 trig_direct(int p, int j, double log2_theta) {
+  double c, sn;
+  rope_cos_sin(p, j, kD, log2_theta, &c, &sn);
+  return double2{c, sn};
+}
+
+// Cosines and sines of every (depth d in [dmin, dmin + n), pair j < 64) at
+// position Lb + d into trig[(d - dmin) * 64 + j], when n <= kTrigDepths.
+__device__ __forceinline__ void fill_trig(double2* trig, int Lb, int dmin, int n, double log2_theta) {
+  if (n > kTrigDepths) return;
+  for (int e = threadIdx.x; e < n * 64; e += 256) {
+    trig[e] = trig_direct(Lb + dmin + (e >> 6), e & 63, log2_theta);
+  }
+}
+
+__device__ __forceinline__ void trig_of(const double2* trig, int Lb, int dmin, int n, int d, int j, double log2_theta,
+                                        double* c, double* sn) {
+  const double2 cs = n <= kTrigDepths ? trig[(d - dmin) * 64 + j] : trig_direct(Lb + d, j, log2_theta);
+  *c = cs.x;
+  *sn = cs.y;
+}
+
+// Rotates the lane's query fragments (rows of nodes node0 .. node1) for their
+// positions Lb + depth: the fragment holds dims c*32 + quad*8 + e (c < 4,
+// e < 8), so the pairs (j, j + 64) of the rotation are (c, c + 2) for c < 2,
+// all within the lane.  Depths and the table live in `buf` (a free 32 KB tile
+// buffer); the last barrier lets the caller reuse it.
+template <int NRB>
+__device__ __forceinline__ void rotate_queries(const TArgs2& a, int Lb, int node0, int node1, int row_base, int l16,
+                                               int quad, const int* par, uint8_t* buf, bf16x8 (&qf)[NRB][4]) {
+  int* s_up = reinterpret_cast<int*>(buf);
+  int* s_dep = s_up + kMaxT;
+  int* s_rng = s_dep + kMaxT;  // [min, max] depth of the item's nodes
+  double2* trig = reinterpret_cast<double2*>(buf + kTrigOffset);
+  node_depths(par, a.T, node0, node1, s_up, s_dep, s_rng);
+  const int dmin = s_rng[0], n = s_rng[1] - s_rng[0] + 1;
+  fill_trig(trig, Lb, dmin, n, a.log2_theta);
+  __syncthreads();
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int r = row_base + rb * 16 + l16;
+    if (r >= a.R) continue;
+    const int d = s_dep[r / a.G];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      u32x4 lo = __builtin_bit_cast(u32x4, qf[rb][c]), hi = __builtin_bit_cast(u32x4, qf[rb][c + 2]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t nlo = 0, nhi = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          double cs, sn;
+          trig_of(trig, Lb, dmin, n, d, c * 32 + quad * 8 + 2 * k + h, a.log2_theta, &cs, &sn);
+          float y0, y1;
+          rope_turn(bf16_to_f32(static_cast<uint16_t>(lo[k] >> (16 * h))),
+                    bf16_to_f32(static_cast<uint16_t>(hi[k] >> (16 * h))), cs, sn, &y0, &y1);
+          nlo |= static_cast<uint32_t>(f32_to_bf16(y0)) << (16 * h);
+          nhi |= static_cast<uint32_t>(f32_to_bf16(y1)) << (16 * h);
+        }
+        lo[k] = nlo;
+        hi[k] = nhi;
+      }
+      qf[rb][c] = __builtin_bit_cast(bf16x8, lo);
+      qf[rb][c + 2] = __builtin_bit_cast(bf16x8, hi);
+    }
+  }
+  __syncthreads();
+}
+
 // The work of one item (b, g, KV split, row tile), sequence b's prefix length
 // already clamped to its valid range (err: SPEC_DEV_LENGTH if it was not).
 // Every thread of the workgroup calls it; it returns at points the whole
@@ -283,11 +444,13 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
   // The split's block indices and the parent row are staged once in LDS, the
   // query fragments loaded beside them (one memory latency for all three); the
   // first tile is issued as soon as the indices are in, and the ancestor sets
-  // are built while it lands.  With the K/V write in the same launch the item
-  // first waits for its (b, g) rows (queries and tree keys): its flag is read
-  // with the indices, and the queries are loaded after the barrier that follows.
-  unsigned flag = 1;
-  if (kFused && tid == 0) flag = __hip_atomic_load(&a.flags[b * a.Hkv + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // are built while it lands.  With the K/V write in the same launch an item
+  // that holds tree keys first waits for its sequence's rows (the count is read
+  // with the indices), and every item rotates its own queries while its first
+  // tile lands.
+  unsigned written = 0;
+  if (kFused && tail && tid == 0)
+    written = __hip_atomic_load(&a.flags[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int32_t* bt_b = a.bt + static_cast<long>(b) * a.max_blocks;
   for (int i = tid; i < p1 - p0; i += 256) {
     const int blk = bt_b[p0 + i];
@@ -295,7 +458,7 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
     if (!ok) err |= SPEC_DEV_BLOCK;
     s_blk[i] = ok ? blk : -1;
   }
-  if (tail)
+  if (tail || (kFused && a.rotate))
     for (int i = tid; i < a.T; i += 256) s_par[i] = a.parent[static_cast<long>(b) * a.T + i];
 
   // query fragments (B operand of S^T): Q[row][c*32 + quad*8 .. +7]
@@ -324,7 +487,7 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
       }
     }
   };
-  if constexpr (!kFused) load_q();
+  load_q();
   float m_run[NRB], l_run[NRB];
   f32x4 o[NRB][8];
 #pragma unroll
@@ -370,21 +533,26 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
       vt_off[dt] = vkey * 256 + (((2 * dt + ((l16 & 3) >> 1)) ^ (2 * (vkey & 7))) * 16) + (l16 & 1) * 8;
   }
 
-  if (kFused && tid == 0) {
-    // the write item of (b, g) took an earlier queue id, so it is running or
-    // done whatever else the device holds; the bound only guards the loop
-    for (unsigned spins = 0; flag == 0u; ++spins) {
+  if (kFused && tail && tid == 0) {
+    // the write items of sequence b took earlier queue ids, so they are running
+    // or done whatever else the device holds; the bound only guards the loop
+    for (unsigned spins = 0; written < static_cast<unsigned>(a.n_chunks); ++spins) {
       if (spins > kFlagSpinLimit) {
         err |= SPEC_DEV_TIMEOUT;
         break;
       }
       __builtin_amdgcn_s_sleep(1);
-      flag = __hip_atomic_load(&a.flags[b * a.Hkv + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      written = __hip_atomic_load(&a.flags[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __syncthreads();  // s_blk and s_par are ready (and, fused, the item's rows are written)
-  if constexpr (kFused) load_q();
+  __syncthreads();  // s_blk and s_par are ready (and, fused, the tree's rows are written)
   if (n_it > 0) issue_tile(0);
+  if constexpr (kFused) {
+    if (a.rotate) {
+      const int node1 = (min(a.R, (rt + 1) * RT) - 1) / a.G;  // the item's last node
+      rotate_queries<NRB>(a, Lb, node0, node1, row_base, l16, quad, s_par, tiles + kTileBytes, qf);
+    }
+  }
   if (tail) {
     // the whole tree's bitsets in tile buffer 1 (first written by tile 1, issued
     // after the loop's first barrier), then the item's nodes' ones into `anc`
@@ -679,138 +847,85 @@ __device__ __forceinline__ long seq_item(const TArgs2& a, const SeqTable& t, int
          __builtin_amdgcn_readfirstlane(s);
 }
 
-constexpr int kTrigDepths = 32;  // depths whose cosines and sines a write item tabulates (32 KB of LDS)
-
-__device__ __forceinline__ void st_agent_u32(uint16_t* p, uint32_t v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Write item (b, g) of the fused launch: the tree's K rows of kv head g,
-// rotated for their positions Lb + depth(i), and its V rows into the cache at
-// slots Lb + i; the queries of the heads of group g, rotated the same way, into
-// their copy in the workspace (`q`).  Depths come from pointer doubling over the
-// parent row; cosines and sines are tabulated per (depth, pair) when the tree
-// is at most kTrigDepths deep.  Stores are agent-scope atomics (written through
-// to memory, like the split partials), so attention items on any die read the
-// rows once the flag is up.  A bad parent row or prefix length writes no cache
-// row and copies the queries unrotated; a bad block index skips that slot.
+// Write item (b, chunk) of the fused launch: rows chunk*C .. chunk*C + C - 1 (C =
+// chunk_rows, a multiple of 8 up to 64) of sequence b's 2 T Hkv tree rows, row
+// 2 (i Hkv + g) + k being node i's key (k = 0), rotated for position Lb +
+// depth(i), or value (k = 1) of kv head g, into the cache at slot Lb + i.
+// Stores are agent-scope atomics (written through to memory, like the split
+// partials), so items on any die that read the tree's keys see them once the
+// sequence's count of written chunks is complete.  A bad parent row or prefix
+// length writes nothing; a bad block index skips that slot.  Either way the
+// chunk is counted.
 template <int NRB>
-__device__ __forceinline__ void write_item(const TArgs2& a, int b, int g, TileLds<NRB>& L) {
+__device__ __forceinline__ void write_item(const TArgs2& a, int b, int chunk, TileLds<NRB>& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T;
   int* s_up = reinterpret_cast<int*>(L.tiles);
   int* s_dep = s_up + kMaxT;
-  double2* trig = reinterpret_cast<double2*>(L.tiles + 2 * kMaxT * sizeof(int));  // [depth][64]
-  static_assert(2 * kMaxT * sizeof(int) + kTrigDepths * 64 * sizeof(double2) <= sizeof(L.tiles), "LDS");
+  int* s_rng = s_dep + kMaxT;
+  double2* trig = reinterpret_cast<double2*>(L.tiles + kTrigOffset);
+  const int n_rows = 2 * T * a.Hkv;
+  const int r0 = chunk * a.chunk_rows, r1 = min(n_rows, r0 + a.chunk_rows);
+  // the chunk's rows first (they depend on nothing): half-wave h takes rows
+  // r0 + h, r0 + h + 8, ..., lane l the pairs (2l, 2l + 64) and (2l + 1, 2l + 65)
+  // as two 32-bit words, all in flight while the depths are found
+  constexpr int kU = 8;
+  const int hl = lane & 31;
+  const int first = r0 + wave * 2 + (lane >> 5);
+  uint32_t x0[kU], x1[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int r = min(first + 8 * u, r1 - 1);
+    const int pr = r >> 1, i = pr / a.Hkv, g = pr % a.Hkv;
+    const uint16_t* src = ((r & 1) ? a.v_new : a.k_new) + ((static_cast<long>(b) * T + i) * a.Hkv + g) * kD;
+    x0[u] = *reinterpret_cast<const uint32_t*>(src + 2 * hl);
+    x1[u] = *reinterpret_cast<const uint32_t*>(src + 64 + 2 * hl);
+  }
   const int Lb = a.plen[b];
   int err = (Lb < 0 || Lb > a.max_blocks * kBlockSize - T) ? SPEC_DEV_LENGTH : 0;
-  if (tid == 0) L.s_last = 0;  // the tree's depth
   for (int i = tid; i < T; i += 256) {
     const int p = a.parent[static_cast<long>(b) * T + i];
-    const bool ok = i == 0 ? p == -1 : (p >= 0 && p < i);
-    s_up[i] = (i == 0 || !ok) ? -1 : p;
-    s_dep[i] = i == 0 ? 0 : 1;
-    if (!ok) err |= SPEC_DEV_PARENT;
+    if (!(i == 0 ? p == -1 : (p >= 0 && p < i))) err |= SPEC_DEV_PARENT;
+    L.s_par[i] = p;
   }
-  __syncthreads();
-  for (int r = 0; (1 << r) < T; ++r) {  // after round r, up = the ancestor 2^(r+1) steps above (or -1)
-    int up[2] = {-1, -1}, dep[2] = {0, 0};
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = tid + 256 * k;
-      if (i < T) {
-        up[k] = s_up[i];
-        dep[k] = s_dep[i];
-        if (up[k] >= 0) {
-          dep[k] += s_dep[up[k]];
-          up[k] = s_up[up[k]];
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = tid + 256 * k;
-      if (i < T) {
-        s_up[i] = up[k];
-        s_dep[i] = dep[k];
-      }
-    }
-    __syncthreads();
-  }
-  for (int i = tid; i < T; i += 256) atomicMax(&L.s_last, s_dep[i]);
+  const bool bad = __syncthreads_or(err != 0);  // also publishes s_par
   report(a.status, b, err);
-  const bool bad = __syncthreads_or(err != 0);
   const bool rotate = a.rotate && !bad;
-  const int n_dep = L.s_last + 1;
-  const bool table = rotate && n_dep <= kTrigDepths;
-  if (table)
-    for (int e = tid; e < n_dep * 64; e += 256) {
-      const double ang = rope_angle(Lb + (e >> 6), e & 63, kD, a.log2_theta);
-      trig[e] = double2{cos(ang), sin(ang)};
-    }
-  __syncthreads();
-
-  // rows of node i: the G query heads of group g, its key, its value; each
-  // half-wave takes one row, lane l the pairs (2l, 2l + 64) and (2l + 1, 2l + 65)
-  // as two 32-bit words; four rows per half-wave in flight together
-  constexpr int kU = 4;
-  const int per = a.G + 2;
-  const int n_rows = T * per;
-  const int hl = lane & 31;
-  const int32_t* bt_b = a.bt + static_cast<long>(b) * a.max_blocks;
-  for (int base = (wave * 2 + (lane >> 5)) * kU; base < n_rows; base += 8 * kU) {
-    uint32_t x0[kU], x1[kU];
-    int node[kU], kind[kU];
+  int dmin = 0, n = 0;
+  if (rotate) {
+    node_depths(L.s_par, T, (r0 >> 1) / a.Hkv, ((r1 - 1) >> 1) / a.Hkv, s_up, s_dep, s_rng);
+    dmin = s_rng[0];
+    n = s_rng[1] - s_rng[0] + 1;
+    fill_trig(trig, Lb, dmin, n, a.log2_theta);
+    __syncthreads();
+  }
+  if (!bad) {
+    const int32_t* bt_b = a.bt + static_cast<long>(b) * a.max_blocks;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int r = min(base + u, n_rows - 1);
-      node[u] = r / per;
-      kind[u] = r % per;  // < G: query head g*G + kind; G: key; G + 1: value
-      const uint16_t* src =
-          kind[u] < a.G ? a.q_src + ((static_cast<long>(b) * T + node[u]) * a.Hq + g * a.G + kind[u]) * kD
-                        : (kind[u] == a.G ? a.k_new : a.v_new) + ((static_cast<long>(b) * T + node[u]) * a.Hkv + g) * kD;
-      x0[u] = *reinterpret_cast<const uint32_t*>(src + 2 * hl);
-      x1[u] = *reinterpret_cast<const uint32_t*>(src + 64 + 2 * hl);
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (base + u >= n_rows) break;
-      uint16_t* dst;
-      if (kind[u] < a.G) {
-        dst = a.q_rot + ((static_cast<long>(b) * T + node[u]) * a.Hq + g * a.G + kind[u]) * kD;
-      } else {
-        if (bad) continue;
-        const int t = Lb + node[u];
-        const int blk = bt_b[t / kBlockSize];
-        if (blk < 0 || blk >= a.num_blocks) {
-          if (hl == 0) report(a.status, b, SPEC_DEV_BLOCK);
-          continue;
-        }
-        dst = (kind[u] == a.G ? a.kc : a.vc) + ((static_cast<long>(blk) * a.Hkv + g) * kBlockSize + t % kBlockSize) * kD;
+      const int r = first + 8 * u;
+      if (r >= r1) break;
+      const int pr = r >> 1, i = pr / a.Hkv, g = pr % a.Hkv;
+      const int t = Lb + i;
+      const int blk = bt_b[t / kBlockSize];
+      if (blk < 0 || blk >= a.num_blocks) {
+        if (hl == 0) report(a.status, b, SPEC_DEV_BLOCK);
+        continue;
       }
+      uint16_t* dst = ((r & 1) ? a.vc : a.kc) + ((static_cast<long>(blk) * a.Hkv + g) * kBlockSize + t % kBlockSize) * kD;
       uint32_t y0 = x0[u], y1 = x1[u];
-      if (rotate && kind[u] <= a.G) {
-        const int d = s_dep[node[u]];
+      if (rotate && !(r & 1)) {
+        const int d = s_dep[i];
         uint32_t lo = 0, hi = 0;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int j = 2 * hl + e;
-          double c, sn;
-          if (table) {
-            const double2 cs = trig[d * 64 + j];
-            c = cs.x;
-            sn = cs.y;
-          } else {
-            const double ang = rope_angle(Lb + d, j, kD, a.log2_theta);
-            c = cos(ang);
-            sn = sin(ang);
-          }
-          float r0, r1;
-          rope_turn(bf16_to_f32(static_cast<uint16_t>(x0[u] >> (16 * e))),
-                    bf16_to_f32(static_cast<uint16_t>(x1[u] >> (16 * e))), c, sn, &r0, &r1);
-          lo |= static_cast<uint32_t>(f32_to_bf16(r0)) << (16 * e);
-          hi |= static_cast<uint32_t>(f32_to_bf16(r1)) << (16 * e);
+        for (int h = 0; h < 2; ++h) {
+          double cs, sn;
+          trig_of(trig, Lb, dmin, n, d, 2 * hl + h, a.log2_theta, &cs, &sn);
+          float r_0, r_1;
+          rope_turn(bf16_to_f32(static_cast<uint16_t>(x0[u] >> (16 * h))),
+                    bf16_to_f32(static_cast<uint16_t>(x1[u] >> (16 * h))), cs, sn, &r_0, &r_1);
+          lo |= static_cast<uint32_t>(f32_to_bf16(r_0)) << (16 * h);
+          hi |= static_cast<uint32_t>(f32_to_bf16(r_1)) << (16 * h);
         }
         y0 = lo;
         y1 = hi;
@@ -821,7 +936,23 @@ __device__ __forceinline__ void write_item(const TArgs2& a, int b, int g, TileLd
   }
   wait_vm0();  // this wave's stores have completed
   __syncthreads();
-  if (tid == 0) __hip_atomic_store(&a.flags[b * a.Hkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_fetch_add(&a.flags[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Attention item of queue id `id` in a fused launch without the longest-first
+// order: split-major, so the splits that hold tree keys come last; sets b's
+// clamped prefix length and error bit.
+__device__ __forceinline__ long split_major_item(const TArgs2& a, int id, int* Lb, int* err) {
+  const long per_s = static_cast<long>(a.B) * a.Hkv * a.n_rt;
+  const int s = static_cast<int>(id / per_s);
+  const long rem = id - s * per_s;
+  const int b = static_cast<int>(rem / (static_cast<long>(a.Hkv) * a.n_rt));
+  const int g = static_cast<int>((rem / a.n_rt) % a.Hkv), rt = static_cast<int>(rem % a.n_rt);
+  int lb = a.plen[b];
+  const int cap = a.max_blocks * kBlockSize - a.T;
+  *err = (lb < 0 || lb > cap) ? SPEC_DEV_LENGTH : 0;
+  *Lb = lb < 0 ? 0 : (lb > cap ? cap : lb);
+  return ((static_cast<long>(b) * a.Hkv + g) * a.splits + s) * a.n_rt + rt;
 }
 
 // kFused: the launch also writes the tree's K/V rows (write items first in the
@@ -833,25 +964,27 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
   bool reorder = false;
   if constexpr (NRB == 1) reorder = a.reorder != 0;  // (the 128-row kernel is at its register limit)
   if constexpr (kFused && NRB == 2) {
-    // One item per workgroup, its id claimed from the queue on entry (not the
+    // One attention item per workgroup, ids claimed from the queue (not the
     // workgroup id: a workgroup that holds an id runs, so every write item an
-    // attention item waits for is running or done); no loop around the item,
-    // which would not fit the 128-row kernel's registers.  The last workgroup
-    // to leave resets the queue and the flags.
+    // attention item waits for is running or done).  A workgroup that claims
+    // write ids runs them and claims again; as many workgroups as attention
+    // items, so each ends with exactly one.  Only the write items sit in a loop:
+    // one around the attention item would not fit the 128-row kernel's
+    // registers.  The last workgroup to leave resets the queue and the counts.
     unsigned* queue = a.counters + static_cast<long>(a.B) * a.Hkv * a.n_rt;
-    if (tid == 0) L.s_next = static_cast<int>(__hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    __syncthreads();
+    for (;;) {
+      if (tid == 0) L.s_next = static_cast<int>(__hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      __syncthreads();
+      const int v = L.s_next;
+      __syncthreads();  // s_next is rewritten only after every wave has read it
+      if (v >= a.n_write) break;
+      write_item<NRB>(a, v / a.n_chunks, v % a.n_chunks, L);
+      __syncthreads();
+    }
     const int v = L.s_next;
-    if (v < a.n_write) {
-      write_item<NRB>(a, v / a.Hkv, v % a.Hkv, L);
-    } else {
-      const long item = v - a.n_write;
-      int Lb = a.plen[item / a.n_rt / a.splits / a.Hkv], err = 0;
-      const int cap = a.max_blocks * kBlockSize - a.T;
-      if (Lb < 0 || Lb > cap) {
-        err |= SPEC_DEV_LENGTH;
-        Lb = Lb < 0 ? 0 : cap;
-      }
+    if (v < a.n_write + static_cast<int>(a.items)) {
+      int Lb, err;
+      const long item = split_major_item(a, v - a.n_write, &Lb, &err);
       tile_item_run<NRB, true>(a, item, Lb, err, L);
     }
     __syncthreads();
@@ -861,7 +994,7 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
     }
     __syncthreads();
     if (L.s_last) {
-      for (int i = tid; i < a.n_write; i += 256)
+      for (int i = tid; i < a.B; i += 256)
         __hip_atomic_store(&a.flags[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (tid == 0) {
         __hip_atomic_store(queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -890,13 +1023,15 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
       unsigned nxt = 0;
       if (tid == 0) nxt = __hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (kFused && v < a.n_write) {
-        write_item<NRB>(a, v / a.Hkv, v % a.Hkv, L);
+        write_item<NRB>(a, v / a.n_chunks, v % a.n_chunks, L);
       } else {
         const int id = v - a.n_write;
         int Lb, err = 0;
         long item;
         if (reorder) {
           item = seq_item(a, t, id, &Lb, &err);
+        } else if (kFused) {
+          item = split_major_item(a, id, &Lb, &err);
         } else {
           item = id;
           Lb = a.plen[item / a.n_rt / a.splits / a.Hkv];
@@ -920,7 +1055,7 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
     __syncthreads();
     if (L.s_last) {
       if constexpr (kFused)
-        for (int i = tid; i < a.n_write; i += 256)
+        for (int i = tid; i < a.B; i += 256)
         __hip_atomic_store(&a.flags[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (tid == 0) {
         __hip_atomic_store(queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1036,19 +1171,26 @@ AttnPlan plan_attn(int B, int T, int Hq, int Hkv, int D, int max_blocks, int dty
   return p;
 }
 
-// The fused launch (the tree's K/V write, then attention): the tile kernel for
-// every bf16 shape, its items from the queue.  Workspace: arrival counters, the
-// queue, the write flags; the rotated queries; the split partials.
+// The fused launch (the tree's K/V write, then attention): the tile kernel,
+// its items from the queue.  Workspace: arrival counters, the queue, one count
+// of written chunks per sequence; the split partials.  Shapes of at most 16
+// query rows per kv head (the streaming kernel's) take two launches instead:
+// the write (the rotated queries into the workspace), then the attention.
 AttnPlan plan_attn_write(int B, int T, int Hq, int Hkv, int max_blocks) {
   AttnPlan p{};
   p.rows = T * (Hq / Hkv);
+  if (p.rows <= 16) {
+    p = plan_attn(B, T, Hq, Hkv, kD, max_blocks, SPEC_BF16);
+    p.ws_bytes += (static_cast<size_t>(B) * T * Hq * kD * sizeof(uint16_t) + 255) / 256 * 256;
+    return p;
+  }
   plan_tile(p, B, Hkv, max_blocks);
   const size_t base = static_cast<size_t>(p.items / p.splits);
-  const size_t head = ((base + 2 + static_cast<size_t>(B) * Hkv) * sizeof(unsigned) + 255) / 256 * 256;
-  const size_t qbytes = (static_cast<size_t>(B) * T * Hq * kD * sizeof(uint16_t) + 255) / 256 * 256;
-  p.ws_bytes = head + qbytes + (p.splits > 1 ? static_cast<size_t>(p.items) * p.rt * (kD + 2) * sizeof(float) : 0);
+  const size_t head = ((base + 2 + static_cast<size_t>(B)) * sizeof(unsigned) + 255) / 256 * 256;
+  p.ws_bytes = head + (p.splits > 1 ? static_cast<size_t>(p.items) * p.rt * (kD + 2) * sizeof(float) : 0);
   return p;
 }
+
 static TArgs2 tile_args(const AttnPlan& plan, const AttnLaunch& L) {
   TArgs2 a{};
   a.q = static_cast<const uint16_t*>(L.q);
@@ -1103,18 +1245,43 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& L, hipStream
 
 hipError_t launch_attn_write(const AttnPlan& plan, const AttnWriteLaunch& W, hipStream_t stream) {
   const AttnLaunch& L = W.attn;
-  TArgs2 a = tile_args(plan, L);
   char* ws = static_cast<char*>(L.workspace);
+  if (plan.mode == 3) {  // two launches: the write (queries rotated into the workspace), the streaming attention
+    const size_t qbytes = (static_cast<size_t>(L.B) * L.T * L.Hq * kD * sizeof(uint16_t) + 255) / 256 * 256;
+    KvWriteLaunch K{};
+    K.k_new = W.k_new;
+    K.v_new = W.v_new;
+    K.q = L.q;
+    K.q_out = ws;
+    K.k_cache = const_cast<void*>(L.k);
+    K.v_cache = const_cast<void*>(L.v);
+    K.block_table = L.block_table;
+    K.prefix_lens = L.prefix_lens;
+    K.parent = L.parent;
+    K.status = L.status;
+    K.B = L.B;
+    K.T = L.T;
+    K.Hq = L.Hq;
+    K.Hkv = L.Hkv;
+    K.D = L.D;
+    K.max_blocks = L.max_blocks;
+    K.num_blocks = L.num_blocks;
+    K.bf16 = 1;
+    K.theta = W.theta;
+    const hipError_t e = launch_kv_write(K, stream);
+    if (e != hipSuccess) return e;
+    AttnLaunch L2 = L;
+    L2.q = ws;
+    L2.workspace = ws + qbytes;
+    return launch_attn_stream(plan, L2, stream);
+  }
+  TArgs2 a = tile_args(plan, L);
   const size_t base = static_cast<size_t>(L.B) * L.Hkv * plan.n_rt;
-  const size_t head = ((base + 2 + static_cast<size_t>(L.B) * L.Hkv) * sizeof(unsigned) + 255) / 256 * 256;
-  const size_t qbytes = (static_cast<size_t>(L.B) * L.T * L.Hq * kD * sizeof(uint16_t) + 255) / 256 * 256;
+  const size_t head = ((base + 2 + static_cast<size_t>(L.B)) * sizeof(unsigned) + 255) / 256 * 256;
   a.counters = reinterpret_cast<unsigned*>(ws);
   a.flags = a.counters + base + 2;
-  a.q_rot = reinterpret_cast<uint16_t*>(ws + head);
-  a.q = a.q_rot;
-  a.q_src = static_cast<const uint16_t*>(L.q);
   if (plan.splits > 1) {
-    a.part_o = reinterpret_cast<float*>(ws + head + qbytes);
+    a.part_o = reinterpret_cast<float*>(ws + head);
     a.part_ml = a.part_o + static_cast<size_t>(plan.items) * plan.rt * kD;
   }
   a.k_new = static_cast<const uint16_t*>(W.k_new);
@@ -1124,14 +1291,18 @@ hipError_t launch_attn_write(const AttnPlan& plan, const AttnWriteLaunch& W, hip
   a.rotate = W.theta > 0.0f ? 1 : 0;
   a.log2_theta = W.theta > 0.0f ? std::log2(static_cast<double>(W.theta)) : 0.0;
   a.persist = 1;
-  a.n_write = L.B * L.Hkv;
+  const long cap = plan.nrb == 1 ? tile_capacity<1, true>() : plan.items;
+  if (cap <= 0) return hipErrorInvalidDevice;
+  // chunks of the write: 64 rows, so that few workgroups carry the write's
+  // latency (smaller chunks on every workgroup measured slower)
+  a.chunk_rows = 64;
+  a.n_chunks = (2 * L.T * L.Hkv + a.chunk_rows - 1) / a.chunk_rows;
+  a.n_write = L.B * a.n_chunks;
   if (plan.nrb == 1) {  // resident workgroups loop over the queue
-    const long cap = tile_capacity<1, true>();
-    if (cap <= 0) return hipErrorInvalidDevice;
     const long grid = std::min<long>(cap, a.n_write + plan.items);
     hipLaunchKernelGGL((attn_tile_kernel<1, true>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
-  } else {  // one workgroup per queue id
-    const long grid = a.n_write + plan.items;
+  } else {  // one workgroup per attention item (write items claimed on the way)
+    const long grid = plan.items;
     hipLaunchKernelGGL((attn_tile_kernel<2, true>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
   }
   return hipGetLastError();

@@ -128,7 +128,8 @@ hipError_t launch_compact(const CompactLaunch& a, hipStream_t stream);
 struct KvWriteLaunch {
   const void* k_new;
   const void* v_new;
-  void* q;  // nullable
+  const void* q;  // nullable
+  void* q_out;    // where the rotated queries go: q itself (in place) or another [B,T,Hq,D] buffer
   void* k_cache;
   void* v_cache;
   const int32_t* block_table;

@@ -28,7 +28,8 @@ namespace {
 struct KvArgs {
   const void* k_new;
   const void* v_new;
-  void* q;
+  const void* q;
+  void* q_out;
   void* k_cache;
   void* v_cache;
   const int32_t* bt;
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
       if (r < a.Hq) {  // a query head, rotated in place
         si[u] = di[u] = ((static_cast<long>(b) * T + i) * a.Hq + r) * a.D;
         src[u] = a.q;
-        dst[u] = a.q;
+        dst[u] = a.q_out;
         rot[u] = a.rotate != 0;
         live[u] = true;
       } else {
@@ -193,9 +194,7 @@ __global__ __launch_bounds__(256) void tree_kv_write_kernel(const KvArgs a) {
         float y0 = x0[u], y1 = x1[u];
         if (rot[u]) {
           if (node[u] != trig_node) {
-            const double ang = rope_angle(Lb + s_dep[node[u]], lane, a.D, a.log2_theta);
-            c = cos(ang);
-            sn = sin(ang);
+            rope_cos_sin(Lb + s_dep[node[u]], lane, a.D, a.log2_theta, &c, &sn);
             trig_node = node[u];
           }
           rope_turn(x0[u], x1[u], c, sn, &y0, &y1);
@@ -214,6 +213,7 @@ hipError_t launch_kv_write(const KvWriteLaunch& L, hipStream_t stream) {
   a.k_new = L.k_new;
   a.v_new = L.v_new;
   a.q = L.q;
+  a.q_out = L.q_out != nullptr ? L.q_out : const_cast<void*>(L.q);
   a.k_cache = L.k_cache;
   a.v_cache = L.v_cache;
   a.bt = L.block_table;

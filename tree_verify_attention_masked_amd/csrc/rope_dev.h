@@ -14,6 +14,11 @@ __device__ __forceinline__ double rope_angle(int pos, int j, int D, double log2_
   return static_cast<double>(pos) * exp2(-(2.0 * j / D) * log2_theta);
 }
 
+// Cosine and sine of the angle of pair j at position p (one shared argument reduction).
+__device__ __forceinline__ void rope_cos_sin(int pos, int j, int D, double log2_theta, double* c, double* s) {
+  sincos(rope_angle(pos, j, D, log2_theta), s, c);
+}
+
 __device__ __forceinline__ void rope_turn(float x0, float x1, double c, double s, float* y0, float* y1) {
   *y0 = static_cast<float>(fma(static_cast<double>(x0), c, -(static_cast<double>(x1) * s)));
   *y1 = static_cast<float>(fma(static_cast<double>(x1), c, static_cast<double>(x0) * s));
