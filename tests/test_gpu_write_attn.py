@@ -13,13 +13,12 @@ launch -- on the GPU, through the C ABI:
   reported and leaves that sequence's cache rows unwritten while the other
   sequences are exact.
 
-Shapes: every arrangement of the fused launch -- 64-row tiles looping over the
-queue (a ragged batch in longest-first order, and a small batch in split-major
-order), 128-row tiles one item per workgroup (a 70-node tree, a 300-node
-Sequoia-profile tree, and a 64-node chain whose items and write chunks span
-more depths than the cosine table holds, so the angles are computed one by
-one), a chain of 5 rows (two launches: the write, then the streaming kernel)
-and an unrotated write.
+Shapes: the one-launch path (ragged batches of 64 sequences in longest-first
+order: 16-node random trees, and 64-node chains whose items and chains go past
+the cosine table and the walked depths) and the two-launch path (64-row tiles
+in plain order, 128-row tiles on a 70-node tree, a 300-node Sequoia-profile tree
+and a 64-node chain, a chain of 5 rows on the streaming kernel, an unrotated
+write).
 """
 import numpy as np
 import pytest
@@ -37,6 +36,8 @@ CASES = [
     # (name, workload kwargs, rope theta, rows compared with the oracle: None = all)
     ("rows64_longest_first", dict(B=64, Hq=32, Hkv=8, prefix=[9000] + [16 + (37 * i) % 600 for i in range(63)],
                                   tree="random", T=16, max_depth=5, shuffle_blocks=True), 10000.0, 160),
+    ("rows64_chains_one_launch", dict(B=64, Hq=3, Hkv=3, prefix=[3000] + [16 + (53 * i) % 900 for i in range(63)],
+                                      tree="chain", gamma=63, shuffle_blocks=True), 10000.0, 200),
     ("rows64_plain_order", dict(B=3, Hq=8, Hkv=2, prefix=[1, 130, 700], tree="random", T=7, max_depth=4,
                                 shuffle_blocks=True), 10000.0, None),
     ("rows128_tree", dict(B=1, Hq=16, Hkv=1, prefix=[900], tree="random", T=70, max_depth=8,
@@ -158,16 +159,23 @@ def test_workspace_serves_calls_in_a_row():
         assert int(head.abs().sum()) == 0, f"call {call} left counters set"
 
 
-def test_bad_parent_is_reported_and_writes_nothing():
-    w = _workload("bad_parent", dict(B=3, Hq=8, Hkv=2, prefix=[40, 200, 7], tree="random", T=12, max_depth=4),
-                  960)
+BAD_PARENT = [
+    ("two_launches", dict(B=3, Hq=8, Hkv=2, prefix=[40, 200, 7], tree="random", T=12, max_depth=4)),
+    ("one_launch", dict(B=64, Hq=32, Hkv=8, prefix=[9000, 200] + [16 + (37 * i) % 600 for i in range(62)],
+                        tree="random", T=16, max_depth=5, shuffle_blocks=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw", BAD_PARENT, ids=[c[0] for c in BAD_PARENT])
+def test_bad_parent_is_reported_and_writes_nothing(name, kw):
+    w = _workload("bad_parent_" + name, kw, 960 + [c[0] for c in BAD_PARENT].index(name))
     k_new = _rows(41, (w.B, w.T, w.Hkv, w.D))
     v_new = _rows(42, (w.B, w.T, w.Hkv, w.D))
     d = DevWorkload(w)
     d.parent[1, 5] = 9  # not an earlier node
     out = _fused(w, d, k_new, v_new, 10000.0)
     st = d.status.cpu().tolist()
-    assert st[1] & 1 and st[0] == 0 and st[2] == 0, st
+    assert st[1] & 1 and st[0] == 0 and st[2] == 0 and sum(map(abs, st)) == st[1], st
     k_before = host_kv(w, dev_kv(w, w.k_cache))
     k_got = host_kv(w, d.k)
     for i in range(w.T):  # sequence 1's tree slots keep what the cache held

@@ -939,70 +939,15 @@ __device__ __forceinline__ void write_item(const TArgs2& a, int b, int chunk, Ti
   if (tid == 0) __hip_atomic_fetch_add(&a.flags[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Attention item of queue id `id` in a fused launch without the longest-first
-// order: split-major, so the splits that hold tree keys come last; sets b's
-// clamped prefix length and error bit.
-__device__ __forceinline__ long split_major_item(const TArgs2& a, int id, int* Lb, int* err) {
-  const long per_s = static_cast<long>(a.B) * a.Hkv * a.n_rt;
-  const int s = static_cast<int>(id / per_s);
-  const long rem = id - s * per_s;
-  const int b = static_cast<int>(rem / (static_cast<long>(a.Hkv) * a.n_rt));
-  const int g = static_cast<int>((rem / a.n_rt) % a.Hkv), rt = static_cast<int>(rem % a.n_rt);
-  int lb = a.plen[b];
-  const int cap = a.max_blocks * kBlockSize - a.T;
-  *err = (lb < 0 || lb > cap) ? SPEC_DEV_LENGTH : 0;
-  *Lb = lb < 0 ? 0 : (lb > cap ? cap : lb);
-  return ((static_cast<long>(b) * a.Hkv + g) * a.splits + s) * a.n_rt + rt;
-}
-
 // kFused: the launch also writes the tree's K/V rows (write items first in the
-// queue); every item then comes from the queue.
+// queue, then the longest-first attention items; 64-row tiles only).
 template <int NRB, bool kFused>
 __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const TArgs2 a) {
   __shared__ TileLds<NRB> L;
   const int tid = threadIdx.x;
   bool reorder = false;
   if constexpr (NRB == 1) reorder = a.reorder != 0;  // (the 128-row kernel is at its register limit)
-  if constexpr (kFused && NRB == 2) {
-    // One attention item per workgroup, ids claimed from the queue (not the
-    // workgroup id: a workgroup that holds an id runs, so every write item an
-    // attention item waits for is running or done).  A workgroup that claims
-    // write ids runs them and claims again; as many workgroups as attention
-    // items, so each ends with exactly one.  Only the write items sit in a loop:
-    // one around the attention item would not fit the 128-row kernel's
-    // registers.  The last workgroup to leave resets the queue and the counts.
-    unsigned* queue = a.counters + static_cast<long>(a.B) * a.Hkv * a.n_rt;
-    for (;;) {
-      if (tid == 0) L.s_next = static_cast<int>(__hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      __syncthreads();
-      const int v = L.s_next;
-      __syncthreads();  // s_next is rewritten only after every wave has read it
-      if (v >= a.n_write) break;
-      write_item<NRB>(a, v / a.n_chunks, v % a.n_chunks, L);
-      __syncthreads();
-    }
-    const int v = L.s_next;
-    if (v < a.n_write + static_cast<int>(a.items)) {
-      int Lb, err;
-      const long item = split_major_item(a, v - a.n_write, &Lb, &err);
-      tile_item_run<NRB, true>(a, item, Lb, err, L);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(queue + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      L.s_last = (prev == gridDim.x - 1u);
-    }
-    __syncthreads();
-    if (L.s_last) {
-      for (int i = tid; i < a.B; i += 256)
-        __hip_atomic_store(&a.flags[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (tid == 0) {
-        __hip_atomic_store(queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    return;
-  }
+  static_assert(!kFused || NRB == 1, "the fused launch runs 64-row tiles");
   if (kFused || (NRB == 1 && a.persist)) {
     // Items from a queue: workgroup w starts with id w, then takes the next
     // unclaimed one (an atomic counter in the workspace) until none is left, so
@@ -1030,8 +975,6 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
         long item;
         if (reorder) {
           item = seq_item(a, t, id, &Lb, &err);
-        } else if (kFused) {
-          item = split_major_item(a, id, &Lb, &err);
         } else {
           item = id;
           Lb = a.plen[item / a.n_rt / a.splits / a.Hkv];
@@ -1171,23 +1114,23 @@ AttnPlan plan_attn(int B, int T, int Hq, int Hkv, int D, int max_blocks, int dty
   return p;
 }
 
-// The fused launch (the tree's K/V write, then attention): the tile kernel,
-// its items from the queue.  Workspace: arrival counters, the queue, one count
-// of written chunks per sequence; the split partials.  Shapes of at most 16
-// query rows per kv head (the streaming kernel's) take two launches instead:
-// the write (the rotated queries into the workspace), then the attention.
+// The tree's K/V write and the attention: one launch of the tile kernel where
+// its items come from the longest-first queue (64-row tiles over a ragged batch
+// with more items than resident workgroups), whose many items per workgroup
+// hide the write; there the workspace holds arrival counters, the queue, one
+// count of written chunks per sequence, then the split partials.  Any other
+// shape takes two launches, which measured faster there: the write (rotated
+// queries into the workspace), then the attention of spec_tree_attn.
 AttnPlan plan_attn_write(int B, int T, int Hq, int Hkv, int max_blocks) {
-  AttnPlan p{};
-  p.rows = T * (Hq / Hkv);
-  if (p.rows <= 16) {
-    p = plan_attn(B, T, Hq, Hkv, kD, max_blocks, SPEC_BF16);
-    p.ws_bytes += (static_cast<size_t>(B) * T * Hq * kD * sizeof(uint16_t) + 255) / 256 * 256;
+  AttnPlan p = plan_attn(B, T, Hq, Hkv, kD, max_blocks, SPEC_BF16);
+  if (p.mode == 2 && p.nrb == 1 && p.reorder && p.splits > 1) {
+    p.fused = 1;
+    const size_t base = static_cast<size_t>(p.items / p.splits);
+    const size_t head = ((base + 2 + static_cast<size_t>(B)) * sizeof(unsigned) + 255) / 256 * 256;
+    p.ws_bytes = head + static_cast<size_t>(p.items) * p.rt * (kD + 2) * sizeof(float);
     return p;
   }
-  plan_tile(p, B, Hkv, max_blocks);
-  const size_t base = static_cast<size_t>(p.items / p.splits);
-  const size_t head = ((base + 2 + static_cast<size_t>(B)) * sizeof(unsigned) + 255) / 256 * 256;
-  p.ws_bytes = head + (p.splits > 1 ? static_cast<size_t>(p.items) * p.rt * (kD + 2) * sizeof(float) : 0);
+  p.ws_bytes += (static_cast<size_t>(B) * T * Hq * kD * sizeof(uint16_t) + 255) / 256 * 256;
   return p;
 }
 
@@ -1246,7 +1189,7 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& L, hipStream
 hipError_t launch_attn_write(const AttnPlan& plan, const AttnWriteLaunch& W, hipStream_t stream) {
   const AttnLaunch& L = W.attn;
   char* ws = static_cast<char*>(L.workspace);
-  if (plan.mode == 3) {  // two launches: the write (queries rotated into the workspace), the streaming attention
+  if (!plan.fused) {  // two launches: the write (queries rotated into the workspace), the attention
     const size_t qbytes = (static_cast<size_t>(L.B) * L.T * L.Hq * kD * sizeof(uint16_t) + 255) / 256 * 256;
     KvWriteLaunch K{};
     K.k_new = W.k_new;
@@ -1273,7 +1216,7 @@ hipError_t launch_attn_write(const AttnPlan& plan, const AttnWriteLaunch& W, hip
     AttnLaunch L2 = L;
     L2.q = ws;
     L2.workspace = ws + qbytes;
-    return launch_attn_stream(plan, L2, stream);
+    return launch_attn_bf16(plan, L2, stream);
   }
   TArgs2 a = tile_args(plan, L);
   const size_t base = static_cast<size_t>(L.B) * L.Hkv * plan.n_rt;
@@ -1291,20 +1234,16 @@ hipError_t launch_attn_write(const AttnPlan& plan, const AttnWriteLaunch& W, hip
   a.rotate = W.theta > 0.0f ? 1 : 0;
   a.log2_theta = W.theta > 0.0f ? std::log2(static_cast<double>(W.theta)) : 0.0;
   a.persist = 1;
-  const long cap = plan.nrb == 1 ? tile_capacity<1, true>() : plan.items;
+  const long cap = tile_capacity<1, true>();
   if (cap <= 0) return hipErrorInvalidDevice;
   // chunks of the write: 64 rows, so that few workgroups carry the write's
   // latency (smaller chunks on every workgroup measured slower)
   a.chunk_rows = 64;
   a.n_chunks = (2 * L.T * L.Hkv + a.chunk_rows - 1) / a.chunk_rows;
   a.n_write = L.B * a.n_chunks;
-  if (plan.nrb == 1) {  // resident workgroups loop over the queue
-    const long grid = std::min<long>(cap, a.n_write + plan.items);
-    hipLaunchKernelGGL((attn_tile_kernel<1, true>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
-  } else {  // one workgroup per attention item (write items claimed on the way)
-    const long grid = plan.items;
-    hipLaunchKernelGGL((attn_tile_kernel<2, true>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
-  }
+  // resident workgroups loop over the queue
+  const long grid = std::min<long>(cap, a.n_write + plan.items);
+  hipLaunchKernelGGL((attn_tile_kernel<1, true>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
