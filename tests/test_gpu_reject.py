@@ -158,3 +158,23 @@ def test_large_tree_without_eager_rows():
     assert stv.spec_tree_reject_plan(64, 257, 32000, 1 << 20) == (4, 8000)
     print("[reject] B=64 T=257 V=32000", flush=True)
     _many_offsets(w, range(2))
+
+
+# Eager row counts other than 1, 2, 4 and 8 (the rows whose statistics are taken
+# before the walk: min(T, 8, eager space / slice stride)): 3 (a chain of two
+# drafts), 6 (a six-node tree), 7 (a 300-node tree at 1000-entry slices, whose
+# eager space holds 7680 floats); the chain workload takes 5.
+EAGER = [
+    ("e3_chain", dict(B=2, V=3000, prefix=[4, 4], tree="chain", gamma=2, temperature=0.9), 12),
+    ("e6_tree", dict(B=3, V=5000, prefix=[4] * 3, tree="random", T=6, max_depth=3, temperature=1.0), 12),
+    ("e7_sequoia_t300", dict(B=1, V=32000, prefix=[4], tree="sequoia", T=300, max_depth=10, temperature=0.6,
+                             draft_mode="without_replacement", without_replacement=True), 6),
+]
+
+
+@pytest.mark.parametrize("name,kw,n_off", EAGER, ids=[e[0] for e in EAGER])
+def test_eager_row_counts(name, kw, n_off):
+    w = make_workload(tag=570 + [e[0] for e in EAGER].index(name), Hq=2, Hkv=2, D=64, dtype="f32", with_kv=False,
+                      **kw)
+    print(f"[reject] {name} B={w.B} T={w.T} V={w.V}", flush=True)
+    _many_offsets(w, range(n_off))

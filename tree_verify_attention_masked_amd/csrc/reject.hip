@@ -65,7 +65,7 @@ struct Slot {
 };
 
 struct Team {
-  int NW, S, ld, E;  // members, slice length, LDS row stride (S rounded up to 4), eager rows (0, 1, 2, 4 or 8)
+  int NW, S, ld, E;  // members, slice length, LDS row stride (S rounded up to 4), eager rows (0 to 8)
 };
 
 // Team size: up to 64 members (32 for trees of more than 16 nodes), about 256
@@ -88,7 +88,7 @@ Team team_shape(int B, int T, int V, long resident) {
   int e = std::min(T, kMaxEager);
   const int cap = T <= kSmallTree ? kEagerCap : kEagerCapBig;
   e = t.ld > cap ? 0 : std::min(e, cap / t.ld);  // >= 1 when the slice fits a tree of up to kSmallTree nodes
-  t.E = e >= 8 ? 8 : e >= 4 ? 4 : e >= 2 ? 2 : e;
+  t.E = e;
   return t;
 }
 
@@ -507,7 +507,7 @@ __device__ __forceinline__ void slice_stats_rows(const float* rows, int ld, int 
 // partials in LDS and no workgroup barrier before the reduction.
 template <int R>
 __device__ __forceinline__ void slice_stats_rows_by_wave(const float* rows, int ld, int n, int v0, bool greedy,
-                                                         double inv_tau, Rec* out) {
+                                                         double inv_tau, int E, Rec* out) {
   static_assert(R % kWaves == 0, "whole rows per wave");
   constexpr int RPW = R / kWaves;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -515,7 +515,12 @@ __device__ __forceinline__ void slice_stats_rows_by_wave(const float* rows, int 
   float mx[RPW];
   int ix[RPW];
   double z[RPW];
-  scan_chunks<RPW, true>(rows + wave * ld, kWaves * ld, n, v0, inv_tau, lane, nc, 64, mx, ix, z);
+  // rows wave, wave + 4, ... of the E staged ones; a wave past the last one
+  // scans row E - 1 again (its record is not published)
+  if (RPW == 1 || wave + kWaves < E)
+    scan_chunks<RPW, true>(rows + min(wave, E - 1) * ld, kWaves * ld, n, v0, inv_tau, lane, nc, 64, mx, ix, z);
+  else
+    scan_chunks<RPW, true>(rows + min(wave, E - 1) * ld, 0, n, v0, inv_tau, lane, nc, 64, mx, ix, z);
   float m[RPW];
   int arg[RPW];
   bool bad[RPW];
@@ -754,10 +759,11 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
           slice_stats_rows<2, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, cur_lbuf);
           break;
         case 4:
-          slice_stats_rows_by_wave<4>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec);
+        case 3:
+          slice_stats_rows_by_wave<4>(eager_l, ld, n, v0, a.greedy, a.inv_tau, E, s_rec);
           break;
-        default:
-          slice_stats_rows_by_wave<8>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec);
+        default:  // 5 to 8
+          slice_stats_rows_by_wave<8>(eager_l, ld, n, v0, a.greedy, a.inv_tau, E, s_rec);
           break;
       }
       if (tid < E) put_slot(&eager[wg * E + tid], s_rec[tid], tag);
