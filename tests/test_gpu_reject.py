@@ -161,12 +161,12 @@ def test_large_tree_without_eager_rows():
 
 
 # Eager row counts other than 1, 2, 4 and 8 (the rows whose statistics are taken
-# before the walk: min(T, 8, eager space / slice stride)): 3 (a chain of two
-# drafts), 6 (a six-node tree), 7 (a 300-node tree at 1000-entry slices, whose
-# eager space holds 7680 floats); the chain workload takes 5.
+# before the walk): a tree of more than 256 nodes keeps min(8, 7680 / slice
+# stride) of them, so 300-node trees over one sequence (32 members) at V = 70000,
+# 38400 and 32000 keep 3, 6 and 7.
 EAGER = [
-    ("e3_chain", dict(B=2, V=3000, prefix=[4, 4], tree="chain", gamma=2, temperature=0.9), 12),
-    ("e6_tree", dict(B=3, V=5000, prefix=[4] * 3, tree="random", T=6, max_depth=3, temperature=1.0), 12),
+    ("e3_t300", dict(B=1, V=70000, prefix=[4], tree="random", T=300, max_depth=8, temperature=0.9), 6),
+    ("e6_t300", dict(B=1, V=38400, prefix=[4], tree="random", T=300, max_depth=8, temperature=1.0), 6),
     ("e7_sequoia_t300", dict(B=1, V=32000, prefix=[4], tree="sequoia", T=300, max_depth=10, temperature=0.6,
                              draft_mode="without_replacement", without_replacement=True), 6),
 ]

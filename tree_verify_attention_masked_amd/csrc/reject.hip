@@ -88,7 +88,9 @@ Team team_shape(int B, int T, int V, long resident) {
   int e = std::min(T, kMaxEager);
   const int cap = T <= kSmallTree ? kEagerCap : kEagerCapBig;
   e = t.ld > cap ? 0 : std::min(e, cap / t.ld);  // >= 1 when the slice fits a tree of up to kSmallTree nodes
-  t.E = e;
+  // 5 to 7 rows cost each wave a second row scan; they pay only where the eager
+  // space is what limits the count (trees of more than kSmallTree nodes)
+  t.E = T > kSmallTree ? e : (e >= 8 ? 8 : e >= 4 ? 4 : e >= 2 ? 2 : e);
   return t;
 }
 
