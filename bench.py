@@ -1,9 +1,10 @@
 """Benchmark of one tree-verification step on one MI355X.
 
-A step = spec_tree_attn -> spec_tree_reject_compact (tree rejection sampling,
-then compaction of the KV cache along the accepted path, in one launch; the
-same outputs as spec_tree_reject followed by spec_kv_compact) over one batch
-of the synthetic workload.  Default workload: batched serving, the largest
+A step = spec_tree_write_attn (the tree's K/V rows into the paged cache,
+rotated for their tree positions, and the tree-masked attention; spec_tree_attn
+for the fp32 configuration) -> spec_tree_reject_compact (tree rejection
+sampling, then compaction of the KV cache along the accepted path, in one
+launch) over one batch of the synthetic workload.  Default workload: batched serving, the largest
 configuration that fits one GPU (64 sequences, 32 query / 8 kv heads, head dim
 128, bf16 paged KV with a shuffled block table, prefixes uniform in
 [512, 16384], a random 16-node tree of depth <= 5 per sequence, vocabulary
@@ -22,11 +23,13 @@ from HIP events around graphs that repeat one call many times on the current
 stream (the stream the kernels run on).  `step_us` gives the spread (p10, p50,
 p90) of 100 single-step replays, each bracketed by events.
 
-The line's `kernels` also times spec_tree_kv_write (the step before attention:
-the tree's K/V rows into the cache, rotated for their tree positions) and
-spec_tree_truncate (top-k 50 then top-p 0.9 on the target logits, out of place);
-neither is part of the timed step, whose inputs already hold the tree's rows and
-whose target is not truncated.
+The line also carries the same step without the write (`without_kv_write`) and
+the step against a truncated target (`truncated_target`: top-k 50 then top-p
+0.9, applied inside the sampler by spec_tree_reject_truncated to the rows its
+walk visits).  Its `kernels` also time spec_tree_kv_write (the write as a launch
+of its own), spec_tree_truncate (the same truncation as a separate pass over
+every target row, out of place) and the truncating sampler; none of these is
+part of the timed step, whose target is not truncated.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
@@ -61,6 +64,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 METRIC = "verified tree tokens/sec at 1 MI355X"
+TRUNC_K, TRUNC_P = 50, 0.9  # the truncated target measured beside the step: top-k 50, then top-p 0.9
 
 
 KERNEL_KEYS = (("tree_write_attn", ("attn_tile_kernel<1, true>", "attn_tile_kernel<2, true>")), ("tree_attn", ("attn_",)), ("tree_reject_compact", ("reject",)), ("kv_compact", ("kv_compact",)),
@@ -514,6 +518,8 @@ def measure(cfg, args, quick=False):
     wa_ws = torch.zeros(max(ws_wa, 1), dtype=torch.uint8, device=dev)  # zero once: work counter and flags
     rej_ws = torch.zeros(int(stv.load_library().spec_tree_reject_workspace_size(w.B, w.T, w.V)),
                          dtype=torch.uint8, device=dev)  # zero once: the sampler's epochs and tagged exchange slots
+    rej_ws_t = torch.zeros(int(stv.spec_tree_reject_truncated_workspace_size(w.B, w.T, w.V, TRUNC_K)),
+                           dtype=torch.uint8, device=dev)  # the truncating sampler's (slots and members' lists)
 
     # Step slots: one graph holds G consecutive steps; slot j runs on input copy
     # j % R with Philox offset (offset + j), so consecutive steps take different
@@ -544,6 +550,15 @@ def measure(cfg, args, quick=False):
                                      num_accepted=sl["nacc"], new_lens=sl["new_lens"], status=c["status"],
                                      workspace=rej_ws)
 
+    def reject_compact_trunc(c, sl=None):  # the same, against the target truncated inside the sampler
+        sl = sl or slots[0]
+        stv.spec_tree_reject_truncated(c["logits"], c["probs"], shared["tok"], shared["parent"], w.temperature,
+                                       TRUNC_K, TRUNC_P, w.without_replacement, w.seed, sl["offset"],
+                                       k_cache=c["k"], v_cache=c["v"], block_table=shared["bt"],
+                                       prefix_lens=shared["lens"], accepted_nodes=sl["acc"], out_tokens=sl["toks"],
+                                       num_accepted=sl["nacc"], new_lens=sl["new_lens"], status=c["status"],
+                                       workspace=rej_ws_t)
+
     def step(sl):  # the timed step: (K/V write and) attention, then rejection + compaction
         (write_attn if fused else attn)(sl["c"])
         reject_compact(sl["c"], sl)
@@ -551,6 +566,10 @@ def measure(cfg, args, quick=False):
     def step_plain(sl):  # attention on rows already in the cache, then rejection + compaction
         attn(sl["c"])
         reject_compact(sl["c"], sl)
+
+    def step_trunc(sl):  # the step against a top-k / top-p truncated target
+        (write_attn if fused else attn)(sl["c"])
+        reject_compact_trunc(sl["c"], sl)
 
     if args.calib_copy and not quick:  # plain copies of known size, for scaling the HBM counters
         for nbytes in (CALIB_BYTES, CALIB_BYTES_BIG):
@@ -560,7 +579,7 @@ def measure(cfg, args, quick=False):
             torch.cuda.synchronize()
             del src, dst
 
-    for fn in ((step, step_plain) if fused else (step,)):
+    for fn in ((step, step_plain, step_trunc) if fused else (step, step_trunc)):
         for sl in slots:  # eager pass: validates every copy and slot
             fn(sl)
         torch.cuda.synchronize()
@@ -609,7 +628,15 @@ def measure(cfg, args, quick=False):
         plain = {"value": round(value_plain, 1), "ms_per_step": round(ms_plain, 5), "step_us": spread_plain,
                  "note": "spec_tree_attn on rows already in the cache, then spec_tree_reject_compact"}
 
-    # accepted tokens per step over every slot's walk (each slot has its own offset)
+    ms_t, value_t, spread_t = timed(step_trunc, "step against the truncated target")
+    truncated = {"value": round(value_t, 1), "ms_per_step": round(ms_t, 5), "step_us": spread_t,
+                 "top_k": TRUNC_K, "top_p": TRUNC_P,
+                 "note": "the step with spec_tree_reject_truncated (top-k then top-p applied inside the sampler to "
+                         "the rows its walk visits) in place of spec_tree_reject_compact"}
+
+    # accepted tokens per step over every slot's walk (each slot has its own offset), untruncated target
+    for sl in slots:
+        step(sl)
     accs = [sl["acc"].cpu().numpy() for sl in slots]
     naccs = [sl["nacc"].cpu().numpy() for sl in slots]
     lp1 = np.concatenate([n + 1 for n in naccs]).astype(np.float64)
@@ -618,7 +645,8 @@ def measure(cfg, args, quick=False):
     reps = args.kernel_reps or max(R, 8 * R if per_copy < 100e6 else R)
     kdur = {}
     timed_calls = (("tree_write_attn", write_attn),) if fused else ()
-    for name, fn in timed_calls + (("tree_attn", attn), ("tree_reject_compact", reject_compact)):
+    for name, fn in timed_calls + (("tree_attn", attn), ("tree_reject_compact", reject_compact),
+                                   ("tree_reject_compact_truncated", reject_compact_trunc)):
         kdur[name] = seconds_per_call(fn, copies, reps, 60 if quick else 200)
         log(f"[bench] {name}: {kdur[name] * 1e6:.2f} us per call")
 
@@ -633,7 +661,8 @@ def measure(cfg, args, quick=False):
         cb.append(compact_bytes(w, acc, nacc))
     rc_bytes = float(np.mean(rb)) + float(np.mean(cb))
     w_bytes = write_bytes(w) if fused else 0
-    work = {"tree_attn": ("hbm", a_bytes, a_flops), "tree_reject_compact": ("hbm", rc_bytes, 0.0)}
+    work = {"tree_attn": ("hbm", a_bytes, a_flops), "tree_reject_compact": ("hbm", rc_bytes, 0.0),
+            "tree_reject_compact_truncated": ("hbm", rc_bytes, 0.0)}
     if fused:
         work["tree_write_attn"] = ("hbm", a_bytes + w_bytes, a_flops)
     kernels = {}
@@ -648,6 +677,8 @@ def measure(cfg, args, quick=False):
     if fused:
         kernels["tree_write_attn"]["rope_theta"] = theta
         kernels["tree_attn"]["in_step"] = False
+    kernels["tree_reject_compact_truncated"].update(in_step=False, top_k=TRUNC_K, top_p=TRUNC_P)
+    del work["tree_reject_compact_truncated"]
     step_bytes = a_bytes + w_bytes + rc_bytes
     step_roof = {"bound": "hbm", "bytes": int(step_bytes), "achieved": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -655,10 +686,11 @@ def measure(cfg, args, quick=False):
                  "note": "algorithmic bytes of the whole step (the tree's K/V rows in and out, attention, the "
                          "walked rows, moved KV rows) / step time" if fused else
                          "algorithmic bytes of the whole step (attention, the walked rows, moved KV rows) / step time"}
-    step_kernels = {k: v for k, v in kdur.items() if not (fused and k == "tree_attn")}
+    step_kernels = {k: v for k, v in kdur.items()
+                    if not (fused and k == "tree_attn") and k != "tree_reject_compact_truncated"}
     return dict(w=w, value=value, ms_per_step=ms_per_step, spread=spread, lp1=lp1, kdur=step_kernels, work=work,
                 kernels=kernels, step_roof=step_roof, copies=copies, slots=slots, shared=shared, R=R, reps=reps,
-                a_bytes=a_bytes, a_flops=a_flops, fused=fused, plain=plain, theta=theta)
+                a_bytes=a_bytes, a_flops=a_flops, fused=fused, plain=plain, theta=theta, truncated=truncated)
 
 
 def roofline_of(m):
@@ -731,7 +763,7 @@ def main():
     kernels = m["kernels"]
     value_main, ms_main, spread_main, step_roof_main, R_main = (m["value"], m["ms_per_step"], m["spread"],
                                                                  m["step_roof"], m["R"])
-    fused_main, plain_main, theta_main = m["fused"], m["plain"], m["theta"]
+    fused_main, plain_main, theta_main, trunc_main = m["fused"], m["plain"], m["theta"], m["truncated"]
 
     # The step before attention as a launch of its own (the timed bf16 step does
     # it inside the attention launch): the tree's K/V rows into the cache, keys
@@ -751,7 +783,7 @@ def main():
     trunc_out = torch.empty_like(copies[0]["logits"])
 
     def truncate(c):
-        stv.spec_tree_truncate(c["logits"], w.temperature, 50, 0.9, out=trunc_out, status=c["status"])
+        stv.spec_tree_truncate(c["logits"], w.temperature, TRUNC_K, TRUNC_P, out=trunc_out, status=c["status"])
 
     t_trunc = seconds_per_call(truncate, copies, reps, 200)
     log(f"[bench] tree_truncate: {t_trunc * 1e6:.2f} us per call")
@@ -762,7 +794,7 @@ def main():
     trunc_bytes = w.B * w.T * w.V * 4 * 2  # every logit read once and written once (out of place)
     kernels["tree_truncate"] = {"us": round(t_trunc * 1e6, 2), "bytes": int(trunc_bytes),
                                 "GB/s": round(trunc_bytes / t_trunc / 1e9, 1), "in_step": False,
-                                "top_k": 50, "top_p": 0.9}
+                                "top_k": TRUNC_K, "top_p": TRUNC_P}
     lp1 = m["lp1"]
     accepted = {"mean": round(float(lp1.mean()), 3), "p10": float(np.percentile(lp1, 10)),
                 "p90": float(np.percentile(lp1, 90)), "walks": int(lp1.size)}
@@ -778,6 +810,7 @@ def main():
         extra[me["w"].name] = {"value": round(me["value"], 1), "unit": "tokens/s",
                                "ms_per_step": round(me["ms_per_step"], 5), "step_us": me["spread"],
                                "kv_write_in_step": me["fused"], "without_kv_write": me["plain"],
+                               "truncated_target": me["truncated"],
                                "roofline": re_, "step_roofline": me["step_roof"], "kernels": me["kernels"],
                                "accepted_per_step": round(float(me["lp1"].mean()), 3), "config": me["w"].summary()}
         del me
@@ -795,7 +828,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic", "config": cfg, "roofline": roof, "step_roofline": step_roof_main,
         "cpu_baseline": cpu, "kernels": kernels, "step_us": spread_main, "accepted_per_step": accepted,
-        "kv_write_in_step": fused_main, "without_kv_write": plain_main,
+        "kv_write_in_step": fused_main, "without_kv_write": plain_main, "truncated_target": trunc_main,
         "input_copies": R_main, "extra": extra,
     }
     print(json.dumps(line), flush=True)

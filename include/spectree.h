@@ -401,6 +401,57 @@ int spec_tree_truncate(const float* logits_in, float* logits_out, int B, int T, 
                        float temperature, int top_k, float top_p, int32_t* status, void* stream);
 
 /* ----------------------------------------------------------------------
+ * spec_tree_reject_truncated — spec_tree_reject against the target truncated
+ * to top_k then top_p (the rules of spec_tree_truncate), with the truncation
+ * taken inside the sampler and only for the rows its walk visits, and
+ * optionally the compaction of spec_tree_reject_compact in the same launch.
+ * The Sequoia summary ("Sequoia: Scalable and Robust Speculative Decoding",
+ * the top-p robustness table) verifies against a nucleus-truncated target;
+ * nothing is written back to target_logits.
+ *
+ * Results equal those of spec_tree_truncate followed by spec_tree_reject
+ * (or spec_tree_reject_compact), except that the top-p masses here are fp64
+ * exponentials: a top_p within about 1e-15 relative of a cumulative mass may
+ * keep one group of equal logits more or fewer than exact arithmetic would.
+ * Each team member lists the largest values of its slice of a visited row;
+ * the members exchange the lists through the workspace (a second exchange,
+ * with K values each, when one slice held more of the row's top values than
+ * its first list) and every member finds the same threshold from them.
+ *
+ *   the first 7 arguments, temperature, without_replacement, seed, offset and
+ *     the outputs up to status  as for spec_tree_reject
+ *   top_k        1 .. 64 (>= the row's count of finite logits keeps them all)
+ *   top_p        > 0; >= 1: top-k only
+ *   workspace    >= spec_tree_reject_truncated_workspace_size(B, T, V, top_k)
+ *                bytes, zero before the first call, reusable as for
+ *                spec_tree_reject (the same epoch-tagged layout, with the
+ *                members' lists after the slots)
+ *   k_cache      NULL: no compaction (the arguments up to dtype are ignored);
+ *                otherwise k_cache .. dtype as for spec_tree_reject_compact
+ * temperature == 0 is greedy, which truncation does not change (the argmax is
+ * always kept).  Returns SPEC_ERR_UNSUPPORTED for top_k outside 1 .. 64 (use
+ * spec_tree_truncate, then spec_tree_reject), SPEC_ERR_INVALID_ARG for top_p
+ * <= 0 or NaN, otherwise as spec_tree_reject (and spec_kv_compact).
+ * ---------------------------------------------------------------------- */
+size_t spec_tree_reject_truncated_workspace_size(int B, int T, int V, int top_k);
+
+/* Team plan of spec_tree_reject_truncated (as spec_tree_reject_plan) and the
+ * length of the members' first lists (<= top_k).  Host only. */
+int spec_tree_reject_truncated_plan(int B, int T, int V, int top_k, int64_t max_resident_workgroups,
+                                    int* team_size, int* list_len);
+
+int spec_tree_reject_truncated(const float* target_logits, const float* draft_probs,
+                               const int32_t* draft_tokens, const int32_t* parent,
+                               int B, int T, int V, float temperature, int top_k, float top_p,
+                               int without_replacement, uint64_t seed, uint64_t offset,
+                               int32_t* accepted_nodes, int32_t* out_tokens, int32_t* num_accepted,
+                               int32_t* status, void* workspace, size_t workspace_bytes,
+                               void* k_cache, void* v_cache, const int32_t* block_table,
+                               const int32_t* prefix_lens, int32_t* new_lens,
+                               int Hkv, int D, int block_size, int max_blocks_per_seq,
+                               int num_blocks, int dtype, void* stream);
+
+/* ----------------------------------------------------------------------
  * spec_sequoia_tree — Sequoia's tree construction: the draft-tree shape of n
  * nodes and depth <= max_depth that maximises the expected number of tokens
  * one verification step generates ("Sequoia: Scalable and Robust Speculative

@@ -199,3 +199,51 @@ def test_reject_team_plan_fits_the_resident_grid(lib):
         stv.spec_tree_reject_plan(1, 5, 32000, 0)
     with pytest.raises(stv.SpecError):
         stv.spec_tree_reject_plan(1, 513, 32000, 256)
+
+
+def test_truncated_sampler_plan_and_validation(lib):
+    full = 256
+    # first lists of a later row: each member's slice cut into 4 parts from 2048 logits on (2 from 1024), a list
+    # of about twice a part's share of the top-k plus 6 (chain: 63 parts, 2 * 50 / 63 -> 2 + 6; batched serving:
+    # 4 members x 4 parts of 2000, 100 / 16 -> 7 + 6; EAGLE-style: 32 x 4 parts of 1002, 80 / 128 -> 1 + 6)
+    assert stv.spec_tree_reject_truncated_plan(1, 5, 32000, 50, full) == (63, 8)
+    assert stv.spec_tree_reject_truncated_plan(64, 16, 32000, 50, full) == (4, 13)
+    assert stv.spec_tree_reject_truncated_plan(8, 64, 128256, 40, full) == (32, 7)
+    assert stv.spec_tree_reject_truncated_plan(1, 256, 32000, 50, full) == (32, 10)
+    for B in (1, 3, 64, 300):
+        for T in (1, 5, 16, 300, 512):
+            for V in (3, 1000, 32000, 128256):
+                for k in (1, 7, 50, 64):
+                    team, kc = stv.spec_tree_reject_truncated_plan(B, T, V, k, full)
+                    assert team == stv.spec_tree_reject_plan(B, T, V, full)[0]
+                    assert 1 <= kc <= k
+                    # every list of one row fits the buffer that merges them (at most 4 parts a member)
+                    assert team * (k + 2) <= 7680 and 4 * team * (kc + 2) <= 7680
+    ws = lib.spec_tree_reject_truncated_workspace_size(2, 5, 32000, 50)
+    assert ws > lib.spec_tree_reject_workspace_size(2, 5, 32000)
+    assert lib.spec_tree_reject_truncated_workspace_size(2, 5, 32000, 64) > ws
+    assert lib.spec_tree_reject_truncated_workspace_size(2, 5, 32000, 0) == 0
+    assert lib.spec_tree_reject_truncated_workspace_size(2, 5, 32000, 65) == 0
+    for k in (0, 65):
+        with pytest.raises(stv.SpecError, match="UNSUPPORTED"):
+            stv.spec_tree_reject_truncated_plan(1, 5, 32000, k, full)
+
+    def call(**kw):  # every call below fails validation (or has nothing to do) before any launch
+        a = dict(B=1, T=5, V=100, tau=1.0, k=10, p=0.9, ws=FAKE, wsz=1 << 30, kc=None, Hkv=2, D=128, bs=16, mb=4,
+                 nb=4, dtype=1)
+        a.update(kw)
+        return lib.spec_tree_reject_truncated(FAKE, FAKE, FAKE, FAKE, a["B"], a["T"], a["V"], a["tau"], a["k"],
+                                              a["p"], 0, 0, 0, FAKE, FAKE, FAKE, None, a["ws"], a["wsz"], a["kc"],
+                                              FAKE, FAKE, FAKE, None, a["Hkv"], a["D"], a["bs"], a["mb"], a["nb"],
+                                              a["dtype"], None)
+    assert call(k=0) == -2
+    assert call(k=65) == -2
+    assert call(p=0.0) == -1
+    assert call(p=float("nan")) == -1
+    assert call(tau=-1.0) == -1
+    assert call(T=513) == -2
+    assert call(wsz=10) == -3
+    assert call(ws=FAKE, wsz=lib.spec_tree_reject_workspace_size(1, 5, 100)) == -3  # the plain sampler's is short
+    assert call(kc=FAKE, D=32) == -2    # the compaction's checks apply when a cache is given
+    assert call(kc=FAKE, Hkv=0) == -1
+    assert call(B=0) == 0

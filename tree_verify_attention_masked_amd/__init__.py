@@ -11,7 +11,8 @@ include/spectree.h):
 and spec_tree_reject_compact, the last two in one launch; spec_tree_kv_write
 writes the tree's K/V rows into the paged cache (rotated for their tree
 positions) before the attention; spec_tree_truncate applies top-k / top-p to
-the target logits before the sampler; spec_sequoia_tree builds the Sequoia-optimal
+the target logits before the sampler, and spec_tree_reject_truncated applies
+them inside the sampler to the rows its walk visits; spec_sequoia_tree builds the Sequoia-optimal
 tree shape for a per-rank acceptance vector (host code).
 
 This package is the thin PyTorch binding: tensors in, device pointers and the
@@ -35,6 +36,9 @@ from .binding import (  # noqa: F401
     spec_tree_reject_compact_noalloc,
     spec_tree_reject_max_resident,
     spec_tree_reject_plan,
+    spec_tree_reject_truncated,
+    spec_tree_reject_truncated_plan,
+    spec_tree_reject_truncated_workspace_size,
     spec_tree_kv_write,
     spec_tree_truncate,
     spec_tree_write_attn,

@@ -55,6 +55,11 @@ _SIGNATURES = {
     "spec_tree_reject_compact": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_uint64,
                                       ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp, _sz,
                                       _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "spec_tree_reject_truncated_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "spec_tree_reject_truncated_plan": (_i, [_i, _i, _i, _i, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
+    "spec_tree_reject_truncated": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_float, _i,
+                                        ctypes.c_uint64, ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp, _sz,
+                                        _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "spec_tree_reject_compact_noalloc": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, ctypes.c_float, _i, ctypes.c_uint64,
                                               ctypes.c_uint64, _vp, _vp, _vp, _vp,
                                               _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
@@ -275,6 +280,77 @@ def spec_tree_reject_compact(target_logits, draft_probs, draft_tokens, parent, t
                                       _dtype_code(k_cache), _stream(dev))
     _check(rc, "spec_tree_reject_compact")
     return accepted_nodes, out_tokens, num_accepted, new_lens
+
+
+def spec_tree_reject_truncated(target_logits, draft_probs, draft_tokens, parent, temperature, top_k, top_p=1.0,
+                               without_replacement=False, seed=0, offset=0, k_cache=None, v_cache=None,
+                               block_table=None, prefix_lens=None, accepted_nodes=None, out_tokens=None,
+                               num_accepted=None, new_lens=None, status=None, workspace=None):
+    """spec_tree_reject against the target truncated to top_k (1..64), then top_p, applied to the rows the walk
+    visits; with k_cache given, also the compaction of spec_tree_reject_compact.
+    Returns (accepted_nodes [B,T], out_tokens [B,T], num_accepted [B], new_lens [B] or None)."""
+    lib = load_library()
+    _need(target_logits, "target_logits", torch.float32, 3)
+    _need(draft_tokens, "draft_tokens", torch.int32, 2)
+    _need(parent, "parent", torch.int32, 2)
+    B, T, V = target_logits.shape
+    if draft_probs is not None:
+        _need(draft_probs, "draft_probs", torch.float32, 3)
+        if tuple(draft_probs.shape) != (B, T, V):
+            raise ValueError("draft_probs shape disagrees with target_logits")
+    if tuple(draft_tokens.shape) != (B, T) or tuple(parent.shape) != (B, T):
+        raise ValueError("draft_tokens / parent shapes disagree with target_logits")
+    dev = target_logits.device
+    compact = k_cache is not None
+    nb = Hkv = bs = D = mb = 0
+    code = SPEC_F32
+    if compact:
+        _need(k_cache, "k_cache", ndim=4)
+        _need(v_cache, "v_cache", k_cache.dtype, 4)
+        _need(block_table, "block_table", torch.int32, 2)
+        _need(prefix_lens, "prefix_lens", torch.int32, 1)
+        nb, Hkv, bs, D = k_cache.shape
+        mb = block_table.shape[1]
+        code = _dtype_code(k_cache)
+        if new_lens is None:
+            new_lens = torch.empty((B,), dtype=torch.int32, device=dev)
+    if accepted_nodes is None:
+        accepted_nodes = torch.empty((B, T), dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, T), dtype=torch.int32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    ws = int(lib.spec_tree_reject_truncated_workspace_size(B, T, V, int(top_k)))
+    if workspace is None and ws > 0:  # zero-filled: its header holds the exit counter and the call epoch
+        workspace = torch.zeros(ws, dtype=torch.uint8, device=dev)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.spec_tree_reject_truncated(_ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(parent),
+                                        B, T, V, float(temperature), int(top_k), float(top_p),
+                                        int(bool(without_replacement)), int(seed) & (2 ** 64 - 1),
+                                        int(offset) & (2 ** 64 - 1), _ptr(accepted_nodes), _ptr(out_tokens),
+                                        _ptr(num_accepted), _ptr(status), _ptr(workspace), wsz,
+                                        _ptr(k_cache) if compact else None, _ptr(v_cache) if compact else None,
+                                        _ptr(block_table) if compact else None,
+                                        _ptr(prefix_lens) if compact else None,
+                                        _ptr(new_lens) if compact else None, Hkv, D, bs, mb, nb, code, _stream(dev))
+    _check(rc, "spec_tree_reject_truncated")
+    return accepted_nodes, out_tokens, num_accepted, new_lens
+
+
+def spec_tree_reject_truncated_workspace_size(B, T, V, top_k) -> int:
+    return int(load_library().spec_tree_reject_truncated_workspace_size(B, T, V, top_k))
+
+
+def spec_tree_reject_truncated_plan(B, T, V, top_k, max_resident_workgroups):
+    """(team size, length of the members' first lists) of the truncating sampler on a device holding
+    `max_resident_workgroups` of its workgroups at once (host only)."""
+    team, kc = ctypes.c_int(0), ctypes.c_int(0)
+    rc = load_library().spec_tree_reject_truncated_plan(B, T, V, int(top_k), int(max_resident_workgroups),
+                                                        ctypes.byref(team), ctypes.byref(kc))
+    _check(rc, "spec_tree_reject_truncated_plan")
+    return team.value, kc.value
 
 
 def spec_tree_reject_compact_noalloc(target_logits, draft_probs, draft_tokens, parent, temperature, k_cache,

@@ -106,6 +106,20 @@ int spec_tree_reject_plan(int B, int T, int V, int64_t max_resident_workgroups, 
 
 int64_t spec_tree_reject_max_resident(void) { return reject_resident_capacity(); }
 
+size_t spec_tree_reject_truncated_workspace_size(int B, int T, int V, int top_k) {
+  if (B <= 0 || T < 1 || V < 1 || top_k < 1 || top_k > kTruncTopKMax) return 0;
+  return reject_trunc_workspace_bytes(B, T, V, top_k);
+}
+
+int spec_tree_reject_truncated_plan(int B, int T, int V, int top_k, int64_t max_resident_workgroups, int* team_size,
+                                    int* list_len) {
+  if (B < 1 || T < 1 || V < 1 || max_resident_workgroups < 1 || !team_size || !list_len)
+    return SPEC_ERR_INVALID_ARG;
+  if (T > kMaxT || V > kMaxV || top_k < 1 || top_k > kTruncTopKMax) return SPEC_ERR_UNSUPPORTED;
+  reject_trunc_plan(B, T, V, top_k, static_cast<long>(max_resident_workgroups), team_size, list_len);
+  return SPEC_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -226,6 +240,36 @@ int spec_tree_reject_compact(const float* target_logits, const float* draft_prob
                     max_blocks_per_seq, num_blocks, dtype, status, &C);
   if (rc != SPEC_OK || B == 0) return rc;
   R.compact = &C;  // copied into the kernel arguments at launch
+  const hipError_t e = launch_reject(R, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+int spec_tree_reject_truncated(const float* target_logits, const float* draft_probs, const int32_t* draft_tokens,
+                               const int32_t* parent, int B, int T, int V, float temperature, int top_k, float top_p,
+                               int without_replacement, uint64_t seed, uint64_t offset, int32_t* accepted_nodes,
+                               int32_t* out_tokens, int32_t* num_accepted, int32_t* status, void* workspace,
+                               size_t workspace_bytes, void* k_cache, void* v_cache, const int32_t* block_table,
+                               const int32_t* prefix_lens, int32_t* new_lens, int Hkv, int D, int block_size,
+                               int max_blocks_per_seq, int num_blocks, int dtype, void* stream) {
+  if (B < 0 || T < 1 || V < 1) return SPEC_ERR_INVALID_ARG;
+  if (top_k < 1 || top_k > kTruncTopKMax) return SPEC_ERR_UNSUPPORTED;
+  if (!(top_p > 0.0f)) return SPEC_ERR_INVALID_ARG;  // also NaN
+  RejectLaunch R;
+  int rc = make_reject(target_logits, draft_probs, draft_tokens, parent, B, T, V, temperature, without_replacement,
+                       seed, offset, accepted_nodes, out_tokens, num_accepted, status, workspace, workspace_bytes,
+                       &R);
+  if (rc != SPEC_OK) return rc;
+  if (B > 0 && workspace_bytes < reject_trunc_workspace_bytes(B, T, V, top_k)) return SPEC_ERR_WORKSPACE;
+  CompactLaunch C;
+  if (k_cache != nullptr) {
+    rc = make_compact(k_cache, v_cache, block_table, prefix_lens, new_lens, B, T, Hkv, D, block_size,
+                      max_blocks_per_seq, num_blocks, dtype, status, &C);
+    if (rc != SPEC_OK) return rc;
+  }
+  if (B == 0) return SPEC_OK;
+  R.top_k = top_k;
+  R.top_p = top_p;
+  if (k_cache != nullptr) R.compact = &C;
   const hipError_t e = launch_reject(R, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }

@@ -114,12 +114,17 @@ struct RejectLaunch {
   void* workspace;
   size_t workspace_bytes;
   const CompactLaunch* compact;  // non-null: compact the KV cache along the accepted path in the same launch
+  int top_k;    // 1 .. 64: truncate the visited target rows (top-k, then top-p); 0: no truncation
+  float top_p;  // > 0; >= 1: top-k only
 };
 
 size_t reject_workspace_bytes(int B, int T, int V);
 long reject_resident_capacity();  // workgroups of the sampler the current device holds at once (0: unknown)
 void reject_plan(int B, int T, int V, long resident, int* team, int* slice);
 size_t reject_workspace_zero_bytes();
+size_t reject_trunc_workspace_bytes(int B, int T, int V, int top_k);  // sampler with truncation
+void reject_trunc_plan(int B, int T, int V, int top_k, long resident, int* team, int* list_len);
+constexpr int kTruncTopKMax = 64;  // largest top_k the sampler truncates with
 hipError_t launch_reject(const RejectLaunch& a, hipStream_t stream);
 size_t reject_static_scratch_bytes();  // size of the allocation-free entry point's device array
 hipError_t launch_reject_static(const RejectLaunch& a, hipStream_t stream);  // on that array

@@ -34,6 +34,7 @@
 // (Salmon, Moraes, Dror, Shaw, SC'11), key (seed lo, seed hi), counter (node,
 // b, purpose + 2*(offset >> 32), offset lo); u = (word0 >> 8) * 2^-24.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "compact_dev.h"
@@ -197,6 +198,13 @@ struct TArgs {
   uint64_t seed, offset;
   int fuse;         // compact the KV cache along the accepted path after the walk
   CompactLaunch c;  // its arguments (accepted / num_accepted unused: the path is in LDS)
+  // truncation of the visited target rows (trunc != 0: top_k in 1 .. kTopKMax)
+  int trunc, top_k;     // K
+  int kc_e, q_e;        // eager rows: first-list length (<= K), parts a member's slice is cut into
+  int kc_d, q_d;        // later rows: the same
+  double top_p;         // >= 1: top-k only
+  unsigned long long* lists;  // [B][list_blocks][top_k + 2] tagged words: the lists of each row (see the kernel)
+  int list_blocks;
 };
 
 // Records cross workgroups (the team spans XCDs, whose L2s are not coherent
@@ -577,6 +585,720 @@ __device__ __forceinline__ void merge_row(const Rec& r, bool member, bool greedy
   }
 }
 
+// ---------------------------------------------------------------------------
+// Top-k / top-p truncation of the target rows the walk visits (the Sequoia
+// summary's top-p robustness table verifies against a nucleus-truncated
+// target; the rules come from Fan et al. 2018 and Holtzman et al. 2020).  Row u
+// keeps {x : l(x) >= t_u}: t_u is the K-th largest logit, then, for top_p < 1,
+// the largest kept value v whose set {l >= v} holds top_p of the kept mass of
+// softmax(l / temperature); equal logits are never split.  Dropped tokens get
+// p = 0 in the accept tests, the residuals and the final draws.
+//
+// Each member lists the kc largest values of its slice of the row (kc <= K):
+// t_w = its kc-th largest, e_w = how many of its elements equal t_w, and its
+// values above t_w.  Every element >= t_w of member w is then listed or
+// counted, so the union of the lists is complete above L = max_w t_w; when the
+// union holds at least K entries >= L, the global K-th largest lies there
+// (and is found by bisection over order-preserving keys, counting the union).
+// Otherwise (a slice held more than kc of the row's top values) the members
+// exchange their full K-lists, for which the union always suffices.
+// ---------------------------------------------------------------------------
+constexpr int kTopKMax = kTruncTopKMax;  // top_k taken inside the walk
+constexpr int kCandCap = 256;            // elements gathered for a slice's exact selection
+constexpr int kWaveSel = kSliceCap / kWaves;  // LDS floats of selection scratch per wave
+constexpr int kListPoll = 16;             // list words a thread polls at a time
+constexpr uint32_t kNoValue = 0x7FC00000u;  // NaN: a list word that is never counted
+
+// The selection helpers below are real calls (inlining them three times over
+// would spill the walk's registers); their pointers carry the address space,
+// so that their LDS and global accesses compile to LDS and global instructions
+// instead of generic (flat) ones.
+typedef __attribute__((address_space(3))) float lds_f;
+typedef __attribute__((address_space(3))) int lds_i;
+typedef __attribute__((address_space(3))) uint32_t lds_u;
+typedef __attribute__((address_space(3))) double lds_d;
+typedef __attribute__((address_space(3))) f32x4 lds_f4;
+typedef __attribute__((address_space(1))) unsigned long long gbl_u64;
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(3))) T* lds(T* p) {
+  return (__attribute__((address_space(3))) T*)(p);
+}
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gbl(T* p) {
+  return (__attribute__((address_space(1))) T*)(p);
+}
+template <bool kLds>
+__device__ __forceinline__ auto row_ptr(const float* p) {
+  if constexpr (kLds)
+    return (const lds_f*)(p);
+  else
+    return (const __attribute__((address_space(1))) float*)(p);
+}
+// a slice row: LDS or global memory
+template <bool kLds>
+using RowPtr = typename std::conditional<kLds, const lds_f*, const __attribute__((address_space(1))) float*>::type;
+template <bool kLds>
+__device__ __forceinline__ f32x4 row4(RowPtr<kLds> p, int valid) {
+  if constexpr (kLds) {
+    return *reinterpret_cast<const lds_f4*>(p);
+  } else {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < valid) v[e] = p[e];
+    return v;
+  }
+}
+
+static_assert(kCandCap + kTopKMax <= kWaveSel, "a wave's selection scratch holds its candidates and its list");
+
+// Order-preserving 32-bit keys of floats (-0 taken as +0), and back.
+__device__ __forceinline__ uint32_t okey(float f) {
+  const uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float okey_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+  v += dpp_i<kShr1, 0xF>(0, v);
+  v += dpp_i<kShr2, 0xF>(0, v);
+  v += dpp_i<kShr4, 0xF>(0, v);
+  v += dpp_i<kShr8, 0xF>(0, v);
+  v += dpp_i<kBcast15, 0xA>(0, v);
+  v += dpp_i<kBcast31, 0xC>(0, v);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) { return __builtin_amdgcn_readlane(wave_incl_scan_i(v), 63); }
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+// The value of lane ^ J: within a row of 16 lanes by DPP (quad permutes for
+// 1 and 2, row shifts for 4 and 8), across rows by ds_bpermute.
+template <int J>
+__device__ __forceinline__ int xor_lane_i(int x) {
+  if constexpr (J == 1) {
+    return __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);  // quad_perm [1, 0, 3, 2]
+  } else if constexpr (J == 2) {
+    return __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);  // quad_perm [2, 3, 0, 1]
+  } else if constexpr (J == 4 || J == 8) {
+    const int up = __builtin_amdgcn_update_dpp(x, x, 0x100 + J, 0xF, 0xF, false);  // row_shl: from lane + J
+    const int dn = __builtin_amdgcn_update_dpp(x, x, 0x110 + J, 0xF, 0xF, false);  // row_shr: from lane - J
+    return (threadIdx.x & J) ? dn : up;
+  } else {
+    return __shfl_xor(x, J);
+  }
+}
+template <int J>
+__device__ __forceinline__ float xor_lane_f(float x) {
+  return __builtin_bit_cast(float, xor_lane_i<J>(__builtin_bit_cast(int, x)));
+}
+template <int J>
+__device__ __forceinline__ double xor_lane_d(double x) {
+  const long long v = __builtin_bit_cast(long long, x);
+  const int lo = xor_lane_i<J>(static_cast<int>(v));
+  const int hi = xor_lane_i<J>(static_cast<int>(v >> 32));
+  return __builtin_bit_cast(double, (static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+// One compare-exchange step of a bitonic sort of the wave's 64 values, largest
+// first (K: the size of the blocks being merged, J: the partner distance); the
+// payload w moves with its value; equal values stay where they are.
+template <int K, int J, bool kPay>
+__device__ __forceinline__ void bitonic_step(float& v, double& w) {
+  const int lane = threadIdx.x & 63;
+  const float ov = xor_lane_f<J>(v);
+  const bool lower = (lane & J) == 0;
+  const bool desc = (lane & K) == 0;
+  const bool take = (lower == desc) ? ov > v : ov < v;
+  if constexpr (kPay) {
+    const double ow = xor_lane_d<J>(w);
+    w = take ? ow : w;
+  }
+  v = take ? ov : v;
+}
+template <bool kPay>
+__device__ __forceinline__ void wave_sort_desc(float& v, double& w) {
+  bitonic_step<2, 1, kPay>(v, w);
+  bitonic_step<4, 2, kPay>(v, w);
+  bitonic_step<4, 1, kPay>(v, w);
+  bitonic_step<8, 4, kPay>(v, w);
+  bitonic_step<8, 2, kPay>(v, w);
+  bitonic_step<8, 1, kPay>(v, w);
+  bitonic_step<16, 8, kPay>(v, w);
+  bitonic_step<16, 4, kPay>(v, w);
+  bitonic_step<16, 2, kPay>(v, w);
+  bitonic_step<16, 1, kPay>(v, w);
+  bitonic_step<32, 16, kPay>(v, w);
+  bitonic_step<32, 8, kPay>(v, w);
+  bitonic_step<32, 4, kPay>(v, w);
+  bitonic_step<32, 2, kPay>(v, w);
+  bitonic_step<32, 1, kPay>(v, w);
+  bitonic_step<64, 32, kPay>(v, w);
+  bitonic_step<64, 16, kPay>(v, w);
+  bitonic_step<64, 8, kPay>(v, w);
+  bitonic_step<64, 4, kPay>(v, w);
+  bitonic_step<64, 2, kPay>(v, w);
+  bitonic_step<64, 1, kPay>(v, w);
+}
+// Inclusive max-scan over the 64 lanes (lane order).
+__device__ __forceinline__ int wave_incl_max_i(int v) {
+  v = max(v, dpp_i<kShr1, 0xF>(INT_MIN, v));
+  v = max(v, dpp_i<kShr2, 0xF>(INT_MIN, v));
+  v = max(v, dpp_i<kShr4, 0xF>(INT_MIN, v));
+  v = max(v, dpp_i<kShr8, 0xF>(INT_MIN, v));
+  v = max(v, dpp_i<kBcast15, 0xA>(INT_MIN, v));
+  v = max(v, dpp_i<kBcast31, 0xC>(INT_MIN, v));
+  return v;
+}
+
+// lanes below this one whose bit is set in m
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+}
+
+// LDS scratch of one wave's selections (floats from its base):
+//   slice top-k:   [0, 576) each lane's candidates (kLaneSlots a lane, then a
+//                  slot that takes the rest), [576, 832) the candidates packed,
+//                  [832, 896) the list;
+//   row threshold: [0, 512) entry values, [512, 1024) their multiplicities,
+//                  [1024, 2048) their masses, then prefix sums (fp64), holding
+//                  before them the histogram [1024, 1280) and the kept entries
+//                  [1280, 1408).
+constexpr int kLaneSlots = 8, kSlotStride = kLaneSlots + 1;
+constexpr int kSelPacked = 576, kSelList = 832, kSelScratch = 1024;  // (a slice top-k's whole scratch)
+constexpr int kPairCap = 512;
+constexpr int kThrMult = 512, kThrMass = 1024, kThrHist = 1024, kThrKept = 1280, kThrKeptIdx = 1344;
+static_assert(64 * kSlotStride <= kSelPacked && kSelPacked + kCandCap <= kSelList && kSelList + 64 <= kSelScratch &&
+                  4 * kSelScratch <= kEagerCapBig &&
+                  kThrMult + kPairCap <= kThrMass && kThrMass + 2 * kPairCap <= kWaveSel &&
+                  kThrHist + 256 <= kThrKept && kThrKeptIdx + 64 <= kThrMass + 2 * kPairCap,
+              "selection scratch layout");
+
+// Four chunks of four elements a lane per step (chunks c, c + 64, c + 128,
+// c + 192), their loads issued together; elements past the slice read -inf.
+template <bool kLds>
+__device__ __forceinline__ void load_chunks4(RowPtr<kLds> row, int n, int nc, int c, f32x4 (&v)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int cu = c + 64 * u;
+    v[u] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (cu < nc) v[u] = row4<kLds>(row + 4 * cu, n - 4 * cu);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[u][e] = 4 * cu + e < n ? v[u][e] : -INFINITY;
+  }
+}
+
+// The kc largest values of one slice (n elements at `row`, LDS when kLds),
+// one wave: t = the kc-th largest value (-inf when the slice holds fewer than
+// kc values above -inf), e = how many elements equal it, and the a values
+// above it (fewer than kc; every value above -inf when t is -inf) at
+// sc + kSelList, in a fixed order (lane by lane, each lane's in index order).
+// NaN elements are passed over (the row's statistics report them).  Fast
+// path: t0, the kc-th largest of the lanes' maxima, has kc elements at or
+// above it, so the answer is >= t0; each lane keeps its elements >= t0 (about
+// kc in all for most rows), they are packed and ranked.  When a lane holds
+// more than kLaneSlots of them or all hold more than kCandCap (flat rows, many
+// ties), the answer is found by bisection over order-preserving keys between t0
+// and the slice's max, counting the slice.  The passes over the slice are
+// branch-free (a selected element is written to its lane's next slot, any
+// other to the lane's spare slot).
+struct SliceTop {
+  float t;
+  int e, a;
+};
+
+template <bool kLds>
+__device__ __forceinline__ SliceTop wave_slice_topk(RowPtr<kLds> row, int n, int kc, lds_f* sc) {
+  const int lane = threadIdx.x & 63;
+  const int nc = (n + 3) >> 2;
+  lds_f* slots = sc + lane * kSlotStride;
+  lds_f* packed = sc + kSelPacked;
+  lds_f* list = sc + kSelList;
+  float mx = -INFINITY;
+  for (int c = lane; c < nc; c += 256) {
+    f32x4 v[4];
+    load_chunks4<kLds>(row, n, nc, c, v);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, v[u][e]);  // NaN passed over
+  }
+  float srt = mx;  // the kc-th largest lane maximum (-inf when fewer than kc are finite)
+  double none = 0.0;
+  wave_sort_desc<false>(srt, none);
+  const float t0 = readlane_f(srt, kc - 1);
+  int cnt = 0;  // this lane's elements >= t0 (above -inf); the first kLaneSlots kept
+  for (int c = lane; c < nc; c += 256) {
+    f32x4 v[4];
+    load_chunks4<kLds>(row, n, nc, c, v);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = v[u][e];
+        const bool sel = x >= t0 && x > -INFINITY;
+        slots[sel ? min(cnt, kLaneSlots) : kLaneSlots] = x;
+        cnt += sel ? 1 : 0;
+      }
+  }
+  const int incl = wave_incl_scan_i(cnt);
+  const int C = __builtin_amdgcn_readlane(incl, 63);
+  if (!__any(cnt > kLaneSlots) && C <= kCandCap) {
+    for (int k = 0; k < cnt; ++k) packed[incl - cnt + k] = slots[k];
+    if (C < kc) {  // fewer than kc values above -inf: all of them
+      for (int i = lane; i < C; i += 64) list[i] = packed[i];
+      return SliceTop{-INFINITY, 0, C};
+    }
+    const int Cp = (C + 15) & ~15;
+    for (int i = C + lane; i < Cp; i += 64) packed[i] = __uint_as_float(kNoValue);
+    bool found = false;
+    float tv = 0.f;
+    for (int i = lane; i < C; i += 64) {
+      const float vi = packed[i];
+      int g = 0, q = 0;
+      for (int j = 0; j < Cp; j += 16) {
+        f32x4 w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const lds_f4*>(packed + j + 4 * u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            g += w[u][k] > vi ? 1 : 0;
+            q += w[u][k] == vi ? 1 : 0;
+          }
+      }
+      if (g < kc && kc <= g + q) {
+        found = true;
+        tv = vi;
+      }
+    }
+    // some candidate is the kc-th largest (the elements >= t0 are all packed)
+    const float t = readlane_f(tv, __ffsll(static_cast<long long>(__ballot(found))) - 1);
+    int a = 0, ne = 0;
+    for (int i0 = 0; i0 < C; i0 += 64) {
+      const int i = i0 + lane;
+      const float v = i < C ? packed[i] : __uint_as_float(kNoValue);
+      const bool up = v > t;
+      ne += v == t ? 1 : 0;
+      const unsigned long long bm = __ballot(up);
+      if (up) list[a + lanes_below(bm)] = v;
+      a += __builtin_popcountll(bm);
+    }
+    return SliceTop{t, wave_sum_i(ne), a};
+  }
+  // slow path: bisection for the largest key x with #{elements >= x} >= kc (count_ge(t0) >= kc)
+  auto count_ge = [&](float x) {
+    int c = 0;
+    for (int cc = lane; cc < nc; cc += 256) {
+      f32x4 v[4];
+      load_chunks4<kLds>(row, n, nc, cc, v);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c += (v[u][e] >= x && v[u][e] > -INFINITY) ? 1 : 0;
+    }
+    return wave_sum_i(c);
+  };
+  uint32_t lo = okey(t0), hi = okey(wave_max_f(mx));
+  while (lo < hi) {
+    const uint32_t mid = lo + ((hi - lo + 1u) >> 1);
+    if (count_ge(okey_value(mid)) >= kc)
+      lo = mid;
+    else
+      hi = mid - 1u;
+  }
+  const float t = okey_value(lo);
+  // the values above t (fewer than kc) lane by lane, each lane's in index order, and the count equal to t
+  int mine = 0, ne = 0;
+  for (int c = lane; c < nc; c += 256) {
+    f32x4 v[4];
+    load_chunks4<kLds>(row, n, nc, c, v);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mine += v[u][e] > t ? 1 : 0;
+        ne += v[u][e] == t ? 1 : 0;
+      }
+  }
+  const int inc2 = wave_incl_scan_i(mine);
+  int pos = inc2 - mine;
+  for (int c = lane; c < nc && pos < inc2; c += 256) {
+    f32x4 v[4];
+    load_chunks4<kLds>(row, n, nc, c, v);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (v[u][e] > t) {
+          if (pos < kTopKMax) list[pos] = v[u][e];
+          ++pos;
+        }
+  }
+  return SliceTop{t, wave_sum_i(ne), __builtin_amdgcn_readlane(inc2, 63)};
+}
+
+// A member's list (one wave): LW tagged 64-bit words, like the slots -- word 0
+// t_w, word 1 e_w, words 2 .. 2 + a the values above t_w, NaN after them.
+__device__ __forceinline__ void put_list(unsigned long long* dst, int LW, const SliceTop& st, const float* list,
+                                         uint32_t tag) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long tg = static_cast<unsigned long long>(tag) << 32;
+  for (int j = lane; j < LW; j += 64) {
+    uint32_t p = kNoValue;
+    if (j == 0)
+      p = __float_as_uint(st.t);
+    else if (j == 1)
+      p = static_cast<uint32_t>(st.e);
+    else if (j - 2 < st.a)
+      p = __float_as_uint(list[j - 2]);
+    __hip_atomic_store(dst + j, tg | p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The whole workgroup: the lists of nblk consecutive (row, member) blocks of
+// LW words (stride LWS words in the workspace) into U[blk * LW + j], each word
+// polled until it carries `tag` (bounded like get_slots), kListPoll words a
+// thread at a time.  Ends with a barrier.
+__device__ __forceinline__ void get_lists(const gbl_u64* src, int LWS, int LW, int nblk, uint32_t tag,
+                                                    lds_u* U, lds_i* fail) {
+  const int tid = threadIdx.x;
+  const int nwords = nblk * LW;
+  const float inv = 1.0f / static_cast<float>(LW);
+  for (int base = 0; base < nwords; base += kListPoll * kThreads) {
+    uint32_t pending = 0;
+#pragma unroll
+    for (int k = 0; k < kListPoll; ++k)
+      if (base + tid + k * kThreads < nwords) pending |= 1u << k;
+    unsigned spins = 0;
+    for (;;) {
+      unsigned long long w[kListPoll];
+#pragma unroll
+      for (int k = 0; k < kListPoll; ++k) {
+        w[k] = 0ull;
+        if ((pending >> k) & 1u) {
+          const int i = base + tid + k * kThreads;
+          const int blk = static_cast<int>((static_cast<float>(i) + 0.5f) * inv);
+          w[k] = __hip_atomic_load(const_cast<gbl_u64*>(src + static_cast<long>(blk) * LWS + (i - blk * LW)),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kListPoll; ++k)
+        if (((pending >> k) & 1u) && static_cast<uint32_t>(w[k] >> 32) == tag) {
+          U[base + tid + k * kThreads] = static_cast<uint32_t>(w[k]);
+          pending &= ~(1u << k);
+        }
+      if (!__syncthreads_or(pending != 0u)) break;
+      if (++spins > kSpinLimit) {
+        if (tid == 0) *fail = 1;
+        __syncthreads();
+        return;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+}
+
+// The row's lists: NB blocks of LW words in U (block b: t_b, e_b, then the
+// values above t_b, NaN after them), member w owning blocks w*Q .. w*Q+Q-1
+// (its slice cut into Q parts in index order).  An entry is a listed value
+// (multiplicity 1) or a block's t_b group (multiplicity e_b; none when t_b is
+// -inf).  Word i of U: block i / LW (taken in fp32, exact for these sizes).
+struct ListWord {
+  float v;  // NaN: no entry
+  int mult, blk;
+};
+__device__ __forceinline__ ListWord list_word(const lds_u* U, int nw, int LW, float inv, int i) {
+  ListWord e{__uint_as_float(kNoValue), 0, 0};
+  if (i < nw) {
+    const int b = static_cast<int>((static_cast<float>(i) + 0.5f) * inv);
+    const int j = i - b * LW;
+    e.blk = b;
+    if (j == 0) {
+      const float t = __uint_as_float(U[i]);
+      if (t > -INFINITY) {
+        e.v = t;
+        e.mult = static_cast<int>(U[i + 1]);
+      }
+    } else if (j >= 2) {
+      e.v = __uint_as_float(U[i]);
+      e.mult = 1;
+    }
+  }
+  return e;
+}
+
+// Member shares of the kept mass when the entries above L outnumber the
+// scratch: bisection for the K-th largest over the list words, the kept
+// entries by a pass over them, each member's mass summed over its blocks'
+// words in order.  (Rare: a union far larger than the lists usually are.)
+__device__ __forceinline__ void wave_row_threshold_slow(const lds_u* U, int NB, int Q, int NW, int LW, float L, int W,
+                                                        int K, double top_p, float m, double inv_tau, lds_f* sc,
+                                                        lds_f* thr, lds_d* iz_out, lds_d* mass) {
+  const int lane = threadIdx.x & 63;
+  const int nw = NB * LW;
+  const float inv = 1.0f / static_cast<float>(LW);
+  auto count_ge = [&](float x) {
+    int c = 0;
+    for (int i = lane; i < nw; i += 64) {
+      const ListWord e = list_word(U, nw, LW, inv, i);
+      c += e.v >= x ? e.mult : 0;
+    }
+    return wave_sum_i(c);
+  };
+  float tk = -INFINITY;
+  if (W >= K) {
+    uint32_t lo = okey(L), hi = okey(m);
+    while (lo < hi) {
+      const uint32_t mid = lo + ((hi - lo + 1u) >> 1);
+      if (count_ge(okey_value(mid)) >= K)
+        lo = mid;
+      else
+        hi = mid - 1u;
+    }
+    tk = okey_value(lo);
+  }
+  lds_f* kv = sc;
+  int ngt = 0, ntie = 0;
+  for (int i0 = 0; i0 < nw; i0 += 64) {
+    const ListWord e = list_word(U, nw, LW, inv, i0 + lane);
+    const bool up = e.v > tk;
+    ntie += e.v == tk ? e.mult : 0;
+    const unsigned long long bm = __ballot(up);
+    if (up) kv[ngt + lanes_below(bm)] = e.v;
+    ngt += __builtin_popcountll(bm);
+  }
+  ntie = wave_sum_i(ntie);
+  float ev = -INFINITY;
+  double em = 0.0;
+  const double tk_mass = tk > -INFINITY ? exp1((static_cast<double>(tk) - static_cast<double>(m)) * inv_tau) : 0.0;
+  if (lane < ngt) {
+    ev = kv[lane];
+    em = exp1((static_cast<double>(ev) - static_cast<double>(m)) * inv_tau);
+  } else if (lane == ngt && ntie > 0) {
+    ev = tk;
+    em = static_cast<double>(ntie) * tk_mass;
+  }
+  float t = tk;
+  if (top_p < 1.0) {
+    wave_sort_desc<true>(ev, em);
+    const double cum = wave_incl_scan(em);
+    const double zk = readlane_d(cum, 63);
+    const unsigned long long hb = __ballot(ev > -INFINITY && cum / zk >= top_p);
+    if (hb) t = readlane_f(ev, __ffsll(static_cast<long long>(hb)) - 1);
+  }
+  double share = 0.0;
+  if (lane < NW)
+    for (int i = lane * Q * LW; i < (lane + 1) * Q * LW; ++i) {
+      const ListWord e = list_word(U, nw, LW, inv, i);
+      if (e.v >= t) share += static_cast<double>(e.mult) * exp1((static_cast<double>(e.v) - static_cast<double>(m)) * inv_tau);
+    }
+  const double z = readlane_d(wave_incl_scan(share), 63);
+  const double iz = 1.0 / z;
+  if (lane < NW) mass[lane] = share * iz;
+  if (lane == 0) {
+    *thr = t;
+    *iz_out = iz;
+  }
+}
+
+// The row's threshold from its lists (one wave).  m: the row's max logit
+// (finite).  Writes *thr, *iz (1 / kept mass of exp((l - m) / t)) and mass[w]
+// (member w's share of the kept mass), all in fixed orders so that every
+// member gets the same values; or sets *fb when the lists were too short
+// (their lengths below K only).  sc: the wave's selection scratch.  The lanes
+// take the list words in turn: the entries >= L = max t_b are packed in word
+// order (block by block) by ballots; the K-th largest is found by rounds of a
+// 256-bin histogram of their keys, each round keeping the bin where the
+// running weight from the top reaches K (at most four rounds for 32-bit
+// keys); the kept entries (fewer than K above it, then its group) are sorted
+// by value across the lanes and their masses scanned for top-p; the members'
+// shares are differences of one prefix sum over the packed entries.
+constexpr int kMultBits = 24;  // a packed entry: multiplicity (< 2^24) | block << 24
+__device__ __forceinline__ void wave_row_threshold(lds_u* U, int NB, int Q, int NW, int LW, int K,
+                                                             double top_p, float m, double inv_tau, lds_f* sc,
+                                                             lds_f* thr, lds_d* iz_out, lds_d* mass, lds_i* fb) {
+  const int lane = threadIdx.x & 63;
+  float tmax = -INFINITY;
+  for (int b = lane; b < NB; b += 64) tmax = fmaxf(tmax, __uint_as_float(U[b * LW]));
+  const float L = wave_max_f(tmax);
+  const int nw = NB * LW;
+  const float inv = 1.0f / static_cast<float>(LW);
+  lds_f* pv = sc;
+  lds_u* pm = reinterpret_cast<lds_u*>(sc + kThrMult);
+  lds_d* pw = reinterpret_cast<lds_d*>(sc + kThrMass);
+  constexpr uint32_t kMultMask = (1u << kMultBits) - 1u;
+  // pack the entries >= L in word order
+  int P = 0, wsum = 0;
+  for (int i0 = 0; i0 < nw; i0 += 64) {
+    const ListWord e = list_word(U, nw, LW, inv, i0 + lane);
+    const bool keep = e.v >= L;  // (NaN never)
+    wsum += keep ? e.mult : 0;
+    const unsigned long long bm = __ballot(keep);
+    const int pos = P + lanes_below(bm);
+    if (keep && pos < kPairCap) {
+      pv[pos] = e.v;
+      pm[pos] = static_cast<uint32_t>(e.mult) | (static_cast<uint32_t>(e.blk) << kMultBits);
+    }
+    P += __builtin_popcountll(bm);
+  }
+  const int W = wave_sum_i(wsum);
+  if (L > -INFINITY && W < K) {  // the K-th largest may lie below some block's t_b
+    if (lane == 0) *fb = 1;
+    return;
+  }
+  if (lane == 0) *fb = 0;
+  if (P > kPairCap) {
+    wave_row_threshold_slow(U, NB, Q, NW, LW, L, W, K, top_p, m, inv_tau, sc, thr, iz_out, mass);
+    return;
+  }
+  // the K-th largest entry (weighted): keys in [lo, hi], `above` the weight over hi
+  float tk = -INFINITY;
+  if (W >= K) {
+    lds_u* hist = reinterpret_cast<lds_u*>(sc + kThrHist);
+    uint32_t lo = okey(L), hi = okey(m);
+    int above = 0;
+    while (lo < hi) {
+      const uint32_t range = hi - lo;
+      const int sh = range < 256u ? 0 : 24 - __builtin_clz(range);  // (range >> sh) < 256
+#pragma unroll
+      for (int k = 0; k < 4; ++k) hist[lane + 64 * k] = 0u;
+      for (int i = lane; i < P; i += 64) {
+        const uint32_t key = okey(pv[i]);
+        if (key >= lo && key <= hi)
+          __hip_atomic_fetch_add(&hist[(hi - key) >> sh], pm[i] & kMultMask, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
+      }
+      // lane l holds bins 4l .. 4l+3 (bin 0 = the highest keys)
+      int h[4], hs = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        h[k] = static_cast<int>(hist[4 * lane + k]);
+        hs += h[k];
+      }
+      const int hin = wave_incl_scan_i(hs);
+      int run = above + hin - hs, bin = -1, before = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bool here = bin < 0 && run + h[k] >= K;
+        bin = here ? 4 * lane + k : bin;
+        before = here ? run : before;
+        run += h[k];
+      }
+      const unsigned long long hb = __ballot(bin >= 0);  // some bin reaches K (W >= K)
+      const int src = __ffsll(static_cast<long long>(hb)) - 1;
+      const uint32_t b = static_cast<uint32_t>(__builtin_amdgcn_readlane(bin, src));
+      above = __builtin_amdgcn_readlane(before, src);
+      const uint32_t nhi = hi - (b << sh);
+      const uint32_t span = (1u << sh) - 1u;  // keys of the bin: [nhi - span, nhi] within [lo, hi]
+      lo = (nhi - lo >= span) ? nhi - span : lo;
+      hi = nhi;
+    }
+    tk = okey_value(lo);
+  }
+  // kept entries, one a lane: those above tk (fewer than K, in entry order), then tk's group
+  lds_f* kv = sc + kThrKept;
+  lds_i* kidx = reinterpret_cast<lds_i*>(sc + kThrKeptIdx);
+  int ngt = 0, ntie = 0;
+  for (int i0 = 0; i0 < P; i0 += 64) {
+    const int i = i0 + lane;
+    const float v = i < P ? pv[i] : __uint_as_float(kNoValue);
+    const bool up = v > tk;
+    ntie += (i < P && v == tk) ? static_cast<int>(pm[i] & kMultMask) : 0;
+    const unsigned long long bm = __ballot(up);
+    if (up) {
+      kv[ngt + lanes_below(bm)] = v;
+      kidx[ngt + lanes_below(bm)] = i;
+    }
+    ngt += __builtin_popcountll(bm);
+  }
+  ntie = wave_sum_i(ntie);
+  float ev = -INFINITY;
+  double em = 0.0;
+  int my_idx = -1;
+  if (lane < ngt) {
+    ev = kv[lane];
+    my_idx = kidx[lane];
+    em = exp1((static_cast<double>(ev) - static_cast<double>(m)) * inv_tau);
+  }
+  const double tk_mass = tk > -INFINITY ? exp1((static_cast<double>(tk) - static_cast<double>(m)) * inv_tau) : 0.0;
+  if (lane == ngt && ntie > 0) {
+    ev = tk;
+    em = static_cast<double>(ntie) * tk_mass;
+  }
+  float t = tk;
+  if (top_p < 1.0) {
+    float sv = ev;
+    double sm = em;
+    wave_sort_desc<true>(sv, sm);
+    const double cum = wave_incl_scan(sm);
+    const double zk = readlane_d(cum, 63);
+    const unsigned long long hb = __ballot(sv > -INFINITY && cum / zk >= top_p);
+    if (hb) t = readlane_f(sv, __ffsll(static_cast<long long>(hb)) - 1);
+    // (none: the kept mass summed short of top_p by rounding; the top-k set stays)
+  }
+  // kept mass of each packed entry (above tk: its own; tk's group: tk's mass times its multiplicity),
+  // then their prefix sums in entry order (block by block)
+  const double kept_tk = (t == tk) ? tk_mass : 0.0;
+  if (my_idx >= 0) pw[my_idx] = ev >= t ? em : 0.0;  // (kv and kidx were read: the masses may overlay them)
+  double carry = 0.0;
+  for (int i0 = 0; i0 < P; i0 += 64) {
+    const int i = i0 + lane;
+    double c = 0.0;
+    if (i < P) {
+      const float v = pv[i];
+      c = v > tk ? pw[i] : (v == tk ? static_cast<double>(pm[i] & kMultMask) * kept_tk : 0.0);
+    }
+    const double inc = wave_incl_scan(c) + carry;
+    if (i < P) pw[i] = inc;
+    carry = readlane_d(inc, 63);
+  }
+  // block b's entries end after the last of them (the values area is free now);
+  // blocks without entries end where the block before them does
+  lds_i* ends = reinterpret_cast<lds_i*>(pv);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) ends[lane + 64 * k] = 0;
+  for (int i0 = 0; i0 < P; i0 += 64) {
+    const int i = i0 + lane;
+    if (i < P) {
+      const uint32_t b = pm[i] >> kMultBits;
+      if (i + 1 == P || (pm[i + 1] >> kMultBits) != b) ends[b] = i + 1;
+    }
+  }
+  // max-scan over the NB (<= 256) blocks, four a lane
+  int e4[4], lm = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    lm = max(lm, ends[4 * lane + k]);
+    e4[k] = lm;
+  }
+  const int pre = wave_incl_max_i(lm);
+  const int carry_in = dpp_i<kWaveShr1, 0xF>(0, pre);  // the lanes before this one
+#pragma unroll
+  for (int k = 0; k < 4; ++k) ends[4 * lane + k] = max(e4[k], carry_in);
+  // member w: blocks w*Q .. w*Q+Q-1
+  double share = 0.0;
+  if (lane < NW) {
+    const int e = ends[(lane + 1) * Q - 1];
+    const int st = lane == 0 ? 0 : ends[lane * Q - 1];
+    share = (e > 0 ? pw[e - 1] : 0.0) - (st > 0 ? pw[st - 1] : 0.0);
+  }
+  const double iz = 1.0 / carry;
+  if (lane < NW) mass[lane] = share * iz;
+  if (lane == 0) {
+    *thr = t;
+    *iz_out = iz;
+  }
+}
+
 // kFits: the slice (S <= kSliceCap floats) lives in LDS, so every slice access is an
 // LDS access; otherwise the slices are read from global memory where they lie.
 // kTree: the largest tree (kSmallTree, or kMaxT with a smaller eager space, so
@@ -606,6 +1328,10 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   __shared__ double s_lastmass[kMaxTeam];  // the members' slice masses of the last residual pass
   __shared__ int sh_err, sh_fail, sh_len, sh_u, sh_c, sh_x, sh_state, sh_nrej, sh_emit_local, sh_owner, sh_arg;
   __shared__ double sh_m, sh_iz, sh_C, sh_Cold, sh_N, sh_s, sh_lo, sh_target, sh_total;
+  // truncation threshold of each eager row and of the current deeper row, and
+  // whether its lists were too short (a second round with K-lists follows)
+  __shared__ float s_thr[kMaxEager + 1];
+  __shared__ int s_tfb[kMaxEager + 1];
 
   const int NW = a.NW;
   const int b = blockIdx.x / NW;
@@ -627,6 +1353,53 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   // the call's tag: the workspace's epoch (advanced by the last workgroup of the grid to leave) + 1
   const uint32_t epoch = __hip_atomic_load(a.hdr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t tag = epoch + 1u;
+  // truncation: this sequence's lists, LWS words a block.  Eager rows: E rows
+  // of NW * q_e blocks (member w's slice cut into q_e parts, one a wave);
+  // later rows: a row of NW * q_d blocks each; second rounds (K-lists of whole
+  // slices): a row of NW blocks each.  Block of member w, part q: w * q + q.
+  const int LWS = a.top_k + 2;
+  const int NBe = NW * a.q_e, NBd = NW * a.q_d, LWe = a.kc_e + 2, LWd = a.kc_d + 2;
+  unsigned long long* const lists_b = a.trunc ? a.lists + static_cast<long>(b) * a.list_blocks * LWS : nullptr;
+  unsigned long long* const lists_d = lists_b + static_cast<long>(8) * NW * LWS;
+  unsigned long long* const lists_s = lists_d + static_cast<long>(T) * 4 * NW * LWS;
+  int drow = 0, srow = 0;  // rows of later first lists and of second rounds used so far
+  // part q of Q of a slice of n elements (a multiple of 4 long, so that parts stay 16-byte aligned)
+  auto part_of = [&](int q, int Q, int* len) __attribute__((always_inline)) {
+    const int nq = (n + 4 * Q - 1) / (4 * Q) * 4;
+    const int s0 = min(n, q * nq);
+    *len = min(n, s0 + nq) - s0;
+    return s0;
+  };
+  // row r's threshold from the lists in U (NB blocks, Q a member; one wave, sc
+  // its selection scratch), unless the row's statistics already failed (then
+  // nothing is kept back)
+  auto row_threshold = [&](int r, uint32_t* U, int NB, int Q, int LW, float* sc) __attribute__((always_inline)) {
+    if (e_err[r] == 0 && isfinite(e_m[r])) {
+      wave_row_threshold(lds(U), NB, Q, NW, LW, a.top_k, a.top_p, e_m[r], a.inv_tau, lds(sc), lds(&s_thr[r]),
+                         lds(&e_iz[r]), lds(&e_mass[r * kMaxTeam]), lds(&s_tfb[r]));
+    } else if (lane == 0) {
+      s_thr[r] = -INFINITY;
+      s_tfb[r] = 0;
+    }
+  };
+  // (whole workgroup) the members' K-lists of row r, whose first lists were too
+  // short, and its threshold from them; slice: this member's slice of the row
+  auto second_round = [&](int r, const float* slice, uint32_t* U, float* sc) __attribute__((always_inline)) {
+    if (srow >= T + kMaxEager) {  // more exchanges than planned: cannot happen for a valid tree
+      if (tid == 0) sh_fail = 1;
+      __syncthreads();
+      return;
+    }
+    unsigned long long* const row = lists_s + static_cast<long>(srow) * NW * LWS;
+    if (wave == 0) {
+      const SliceTop st = wave_slice_topk<kFits>(row_ptr<kFits>(slice), n, a.top_k, lds(sc));
+      put_list(row + static_cast<long>(wg) * LWS, LWS, st, sc + kSelList, tag);
+    }
+    get_lists(gbl(row), LWS, LWS, NW, tag, lds(U), lds(&sh_fail));
+    ++srow;
+    if (!sh_fail && wave == 0) row_threshold(r, U, NW, 1, LWS, sc);
+    __syncthreads();
+  };
 
   // tree and tokens (nodes tid and tid + kThreads) and the eager logit and
   // draft slices, which depend on nothing else: all in flight together
@@ -773,6 +1546,16 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       const float qx = (a.greedy ? lg_b : q_b)[off];
       const float lx2 = two ? lg_b[off2] : 0.f;
       const float qx2 = two ? (a.greedy ? lg_b : q_b)[off2] : 0.f;
+      if (a.trunc) {  // this member's first lists of the eager rows: (row, part) pairs dealt to the waves
+        float* sc = cur_qbuf + wave * kWaveSel;
+        for (int task = wave; task < E * a.q_e; task += kWaves) {
+          const int r = task / a.q_e, q = task - r * a.q_e;
+          int len;
+          const int s0 = part_of(q, a.q_e, &len);
+          const SliceTop st = wave_slice_topk<kFits>(row_ptr<kFits>(eager_l + r * ld + s0), len, a.kc_e, lds(sc));
+          put_list(lists_b + (static_cast<long>(r) * NBe + wg * a.q_e + q) * LWS, LWe, st, sc + kSelList, tag);
+        }
+      }
       // gather every member's eager rows (wave w: rows w and w + 4) and merge them, member order
       const Rec none = Rec{-INFINITY, 0x7fffffff, 0.0};
       if (wave + kWaves < E) {
@@ -799,6 +1582,17 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         s_qx[cx2] = qx2;
       }
       __syncthreads();
+      if (a.trunc) {  // every member's lists of the eager rows, then their thresholds
+        uint32_t* U = reinterpret_cast<uint32_t*>(cur_lbuf);
+        get_lists(gbl(lists_b), LWS, LWe, E * NBe, tag, lds(U), lds(&sh_fail));
+        if (!sh_fail) {
+          for (int r = wave; r < E; r += kWaves)
+            row_threshold(r, U + r * NBe * LWe, NBe, a.q_e, LWe, cur_qbuf + wave * kWaveSel);
+          __syncthreads();
+          for (int r = 0; r < E && !sh_fail; ++r)
+            if (s_tfb[r]) second_round(r, eager_l + r * ld, U, cur_qbuf);
+        }
+      }
     } else {
       if (cx < T) {
         s_lx[cx] = lg_b[off];
@@ -843,6 +1637,13 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         Slot* xs = part + xrow * NW;
         ++xrow;
         if (tid == 0) put_slot(&xs[wg], s_rec[0], tag);
+        if (a.trunc && wave < a.q_d && drow < T) {  // this member's first lists of the row, a part a wave
+          float* sc = eager_q + wave * kSelScratch;    // (the eager buffers are free now)
+          int len;
+          const int s0 = part_of(wave, a.q_d, &len);
+          const SliceTop st = wave_slice_topk<kFits>(row_ptr<kFits>(cl + s0), len, a.kc_d, lds(sc));
+          put_list(lists_d + (static_cast<long>(drow) * NBd + wg * a.q_d + wave) * LWS, LWd, st, sc + kSelList, tag);
+        }
         if (wave == 0) {
           const Slot* const rows1[1] = {xs};
           Rec r[1];
@@ -852,8 +1653,25 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         }
         __syncthreads();
         if (sh_fail) break;
+        if (a.trunc) {  // every member's list of the row, then its threshold
+          if (drow >= T) {  // more rows than the tree has: cannot happen for a valid tree
+            if (tid == 0) sh_fail = 1;
+            break;
+          }
+          uint32_t* U = reinterpret_cast<uint32_t*>(eager_l);
+          get_lists(gbl(lists_d + static_cast<long>(drow) * NBd * LWS), LWS, LWd, NBd, tag, lds(U), lds(&sh_fail));
+          ++drow;
+          if (sh_fail) break;
+          if (wave == 0) row_threshold(kMaxEager, U, NBd, a.q_d, LWd, eager_q);
+          __syncthreads();
+          if (s_tfb[kMaxEager]) {
+            second_round(kMaxEager, cl, U, eager_q);
+            if (sh_fail) break;
+          }
+        }
       }
       const int er = u < E ? u : kMaxEager;  // this row's merged statistics
+      const float thr = a.trunc ? s_thr[er] : -INFINITY;  // kept: logits >= thr
       if (tid == 0) {
         sh_err |= e_err[er];
         sh_m = e_m[er];
@@ -892,7 +1710,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         const int nrej = sh_nrej;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          w[e] *= iz;
+          w[e] = lv[e] >= thr ? w[e] * iz : 0.0;  // a truncated token has p = 0
           if (nrej > 0 || C != 0.0) {
             const int x = v0 + 4 * c + e;
             double cx = C;
@@ -938,7 +1756,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
             sh_state = 0;  // no untried child: final draw at u
           } else {
             const int x = s_tok[c];
-            const double px = exp1((static_cast<double>(s_lx[c]) - m) * a.inv_tau) * iz;
+            const double px = s_lx[c] >= thr ? exp1((static_cast<double>(s_lx[c]) - m) * a.inv_tau) * iz : 0.0;
             const float qf = s_qx[c];
             if (isnan(qf)) sh_err |= SPEC_DEV_NONFINITE;
             const double qx = static_cast<double>(qf);
@@ -1194,6 +2012,53 @@ size_t reject_workspace_bytes(int B, int T, int V) {
 
 size_t reject_workspace_zero_bytes() { return kHeaderBytes; }
 
+// Parts a member's slice of n logits is cut into when the selection takes
+// `rows` rows at once (a part a wave, four waves a workgroup): long slices are
+// split so that their passes run on several waves.
+static int slice_parts(int n, int rows) {
+  const int q = n >= 2048 ? 4 : (n >= 1024 ? 2 : 1);
+  return std::max(1, std::min(q, kWaves / std::max(rows, 1)));
+}
+
+// Length of the first lists of NB blocks for top-k K: about twice a block's
+// expected share of the top K plus a margin (so that a second round is rare),
+// bounded so that `rows` rows of lists fit `cap` words of the LDS buffer that
+// merges them.
+static int first_list_len(int NB, int K, int rows, int cap) {
+  int kc = std::min(K, (2 * K + NB - 1) / NB + 6);
+  while (kc > 1 && rows * NB * (kc + 2) > cap) --kc;
+  return kc;
+}
+
+struct TruncPlan {
+  int kc_e, q_e, kc_d, q_d;
+};
+static TruncPlan trunc_plan(const Team& t, int K) {
+  TruncPlan p;
+  p.q_e = slice_parts(t.S, t.E);
+  p.kc_e = first_list_len(t.NW * p.q_e, K, std::max(t.E, 1), kSliceCap);
+  p.q_d = slice_parts(t.S, 1);
+  p.kc_d = first_list_len(t.NW * p.q_d, K, 1, kEagerCapBig);
+  return p;
+}
+
+// List blocks per sequence: the eager rows' (at most 8 NW), a row of at most
+// 4 NW for each later row, a row of NW for each second round (at most T + 8).
+static long list_blocks(int NW, int T) { return static_cast<long>(NW) * (5L * T + 16); }
+
+size_t reject_trunc_workspace_bytes(int B, int T, int V, int top_k) {
+  const Team t = team_shape(B, T, V, kUnboundedResidency);  // the largest team any device gets
+  const size_t slots = static_cast<size_t>(B) * t.NW * (kMaxEager + part_rows(T)) * sizeof(Slot);
+  const size_t lists = static_cast<size_t>(B) * list_blocks(t.NW, T) * (top_k + 2) * sizeof(unsigned long long);
+  return kHeaderBytes + slots + lists;
+}
+
+void reject_trunc_plan(int B, int T, int V, int top_k, long resident, int* team, int* list_len) {
+  const Team t = team_shape(B, T, V, resident);
+  *team = t.NW;
+  *list_len = trunc_plan(t, top_k).kc_d;
+}
+
 // Workgroups of the sampler kernel the current device holds at once: its
 // occupancy per CU (LDS bound: one) times the CU count, queried once per
 // device.
@@ -1306,6 +2171,25 @@ hipError_t launch_reject(const RejectLaunch& L, hipStream_t stream) {
   a.offset = L.offset;
   a.fuse = L.compact != nullptr;
   if (a.fuse) a.c = *L.compact;
+  a.trunc = (!greedy && L.top_k > 0) ? 1 : 0;
+  a.top_k = 1;
+  a.kc_e = a.kc_d = a.q_e = a.q_d = 1;
+  a.top_p = 1.0;
+  if (a.trunc) {
+    if (L.top_k > kTopKMax) return hipErrorInvalidValue;
+    const TruncPlan tp = trunc_plan(t, L.top_k);
+    a.top_k = L.top_k;
+    a.kc_e = tp.kc_e;
+    a.q_e = tp.q_e;
+    a.kc_d = tp.kc_d;
+    a.q_d = tp.q_d;
+    a.top_p = static_cast<double>(L.top_p);
+    a.list_blocks = static_cast<int>(list_blocks(t.NW, L.T));
+    a.lists = reinterpret_cast<unsigned long long*>(a.part + static_cast<size_t>(L.B) * a.part_rows * t.NW);
+    const size_t used = static_cast<size_t>(reinterpret_cast<char*>(a.lists) - static_cast<char*>(L.workspace)) +
+                        static_cast<size_t>(L.B) * a.list_blocks * (a.top_k + 2) * sizeof(unsigned long long);
+    if (used > L.workspace_bytes) return hipErrorInvalidValue;
+  }
   const dim3 grid(static_cast<unsigned>(L.B * t.NW));
   const bool fits = t.ld <= kSliceCap;
   if (L.T <= kSmallTree) {
