@@ -404,7 +404,7 @@ __device__ __forceinline__ double wave_shift_up(double v, double first) { return
 // +inf pins the row's max at +inf with index -1.
 template <int NR, bool kLds>
 __device__ __forceinline__ void scan_chunks(const float* base, int stride, int n, int v0, double inv_tau, int c0, int nc,
-                                            int step, float (&mx)[NR], int (&ix)[NR], double (&z)[NR]) {
+                                            int step, bool noz, float (&mx)[NR], int (&ix)[NR], double (&z)[NR]) {
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     mx[r] = -INFINITY;
@@ -429,22 +429,25 @@ __device__ __forceinline__ void scan_chunks(const float* base, int stride, int n
         ix[r] = take ? (bad ? -1 : v0 + 4 * c + e) : ix[r];
       }
     }
-    double t[5 * NR];  // the chunk's terms, then the factor rescaling the running sum
+    if (!noz) {
+      double t[5 * NR];  // the chunk's terms, then the factor rescaling the running sum
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
+      for (int r = 0; r < NR; ++r) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) t[4 * r + e] = (static_cast<double>(v[r][e]) - static_cast<double>(cm[r])) * inv_tau;
-      t[4 * NR + r] = (static_cast<double>(mx[r]) - static_cast<double>(cm[r])) * inv_tau;
+        for (int e = 0; e < 4; ++e) t[4 * r + e] = (static_cast<double>(v[r][e]) - static_cast<double>(cm[r])) * inv_tau;
+        t[4 * NR + r] = (static_cast<double>(mx[r]) - static_cast<double>(cm[r])) * inv_tau;
+      }
+      exp_lockstep<5 * NR>(t);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        double zz = (mx[r] == -INFINITY) ? 0.0 : z[r] * t[4 * NR + r];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zz += (4 * c + e < n) ? t[4 * r + e] : 0.0;
+        z[r] = zz;
+      }
     }
-    exp_lockstep<5 * NR>(t);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      double zz = (mx[r] == -INFINITY) ? 0.0 : z[r] * t[4 * NR + r];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) zz += (4 * c + e < n) ? t[4 * r + e] : 0.0;
-      z[r] = zz;
-      mx[r] = cm[r];
-    }
+    for (int r = 0; r < NR; ++r) mx[r] = cm[r];
   }
 }
 
@@ -466,7 +469,7 @@ __device__ __forceinline__ void slice_stats_rows(const float* rows, int ld, int 
   float mx[R];
   int ix[R];
   double z[R];
-  scan_chunks<R, kLds>(rows, ld, n, v0, inv_tau, tid, nc, kThreads, mx, ix, z);
+  scan_chunks<R, kLds>(rows, ld, n, v0, inv_tau, tid, nc, kThreads, greedy, mx, ix, z);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     pm[r * kThreads + tid] = mx[r];
@@ -528,9 +531,9 @@ __device__ __forceinline__ void slice_stats_rows_by_wave(const float* rows, int 
   // rows wave, wave + 4, ... of the E staged ones; a wave past the last one
   // scans row E - 1 again (its record is not published)
   if (RPW == 1 || wave + kWaves < E)
-    scan_chunks<RPW, true>(rows + min(wave, E - 1) * ld, kWaves * ld, n, v0, inv_tau, lane, nc, 64, mx, ix, z);
+    scan_chunks<RPW, true>(rows + min(wave, E - 1) * ld, kWaves * ld, n, v0, inv_tau, lane, nc, 64, greedy, mx, ix, z);
   else
-    scan_chunks<RPW, true>(rows + min(wave, E - 1) * ld, 0, n, v0, inv_tau, lane, nc, 64, mx, ix, z);
+    scan_chunks<RPW, true>(rows + min(wave, E - 1) * ld, 0, n, v0, inv_tau, lane, nc, 64, greedy, mx, ix, z);
   float m[RPW];
   int arg[RPW];
   bool bad[RPW];
@@ -1007,6 +1010,46 @@ __device__ __forceinline__ void get_lists(const gbl_u64* src, int LWS, int LW, i
   }
 }
 
+// Threads t .. of nt (whole waves, t counted from the first of them): the
+// words of get_lists, each thread polling its own until they carry `tag`
+// (bounded like get_slots), with no barrier: the caller's barrier publishes U.
+__device__ __forceinline__ void poll_lists(const gbl_u64* src, int LWS, int LW, int nblk, uint32_t tag, lds_u* U,
+                                           lds_i* fail, int t, int nt) {
+  const int nwords = nblk * LW;
+  const float inv = 1.0f / static_cast<float>(LW);
+  for (int base = 0; base < nwords; base += kListPoll * nt) {
+    uint32_t pending = 0;
+#pragma unroll
+    for (int k = 0; k < kListPoll; ++k)
+      if (base + t + k * nt < nwords) pending |= 1u << k;
+    unsigned spins = 0;
+    while (__any(pending != 0u)) {
+      unsigned long long w[kListPoll];
+#pragma unroll
+      for (int k = 0; k < kListPoll; ++k) {
+        w[k] = 0ull;
+        if ((pending >> k) & 1u) {
+          const int i = base + t + k * nt;
+          const int blk = static_cast<int>((static_cast<float>(i) + 0.5f) * inv);
+          w[k] = __hip_atomic_load(const_cast<gbl_u64*>(src + static_cast<long>(blk) * LWS + (i - blk * LW)),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kListPoll; ++k)
+        if (((pending >> k) & 1u) && static_cast<uint32_t>(w[k] >> 32) == tag) {
+          U[base + t + k * nt] = static_cast<uint32_t>(w[k]);
+          pending &= ~(1u << k);
+        }
+      if (++spins > kSpinLimit) {
+        *fail = 1;
+        return;
+      }
+      if (__any(pending != 0u)) __builtin_amdgcn_s_sleep(1);
+    }
+  }
+}
+
 // The row's lists: NB blocks of LW words in U (block b: t_b, e_b, then the
 // values above t_b, NaN after them), member w owning blocks w*Q .. w*Q+Q-1
 // (its slice cut into Q parts in index order).  An entry is a listed value
@@ -1017,22 +1060,17 @@ struct ListWord {
   int mult, blk;
 };
 __device__ __forceinline__ ListWord list_word(const lds_u* U, int nw, int LW, float inv, int i) {
-  ListWord e{__uint_as_float(kNoValue), 0, 0};
-  if (i < nw) {
-    const int b = static_cast<int>((static_cast<float>(i) + 0.5f) * inv);
-    const int j = i - b * LW;
-    e.blk = b;
-    if (j == 0) {
-      const float t = __uint_as_float(U[i]);
-      if (t > -INFINITY) {
-        e.v = t;
-        e.mult = static_cast<int>(U[i + 1]);
-      }
-    } else if (j >= 2) {
-      e.v = __uint_as_float(U[i]);
-      e.mult = 1;
-    }
-  }
+  const int ic = min(i, nw - 1);
+  const float w0 = __uint_as_float(U[ic]);
+  const int w1 = static_cast<int>(U[min(ic + 1, nw - 1)]);  // (a t_b word is never the last)
+  const int b = static_cast<int>((static_cast<float>(i) + 0.5f) * inv);
+  const int j = i - b * LW;
+  const bool head = j == 0 && w0 > -INFINITY;
+  const bool val = j >= 2;
+  ListWord e;
+  e.v = (i < nw && (head || val)) ? w0 : __uint_as_float(kNoValue);
+  e.mult = head ? w1 : 1;
+  e.blk = b;
   return e;
 }
 
@@ -1136,19 +1174,24 @@ __device__ __forceinline__ void wave_row_threshold(lds_u* U, int NB, int Q, int 
   lds_u* pm = reinterpret_cast<lds_u*>(sc + kThrMult);
   lds_d* pw = reinterpret_cast<lds_d*>(sc + kThrMass);
   constexpr uint32_t kMultMask = (1u << kMultBits) - 1u;
-  // pack the entries >= L in word order
+  // pack the entries >= L in word order (four words a lane read at once)
   int P = 0, wsum = 0;
-  for (int i0 = 0; i0 < nw; i0 += 64) {
-    const ListWord e = list_word(U, nw, LW, inv, i0 + lane);
-    const bool keep = e.v >= L;  // (NaN never)
-    wsum += keep ? e.mult : 0;
-    const unsigned long long bm = __ballot(keep);
-    const int pos = P + lanes_below(bm);
-    if (keep && pos < kPairCap) {
-      pv[pos] = e.v;
-      pm[pos] = static_cast<uint32_t>(e.mult) | (static_cast<uint32_t>(e.blk) << kMultBits);
+  for (int i0 = 0; i0 < nw; i0 += 256) {
+    ListWord e[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) e[u] = list_word(U, nw, LW, inv, i0 + 64 * u + lane);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool keep = e[u].v >= L;  // (NaN never)
+      wsum += keep ? e[u].mult : 0;
+      const unsigned long long bm = __ballot(keep);
+      const int pos = P + lanes_below(bm);
+      if (keep && pos < kPairCap) {
+        pv[pos] = e[u].v;
+        pm[pos] = static_cast<uint32_t>(e[u].mult) | (static_cast<uint32_t>(e[u].blk) << kMultBits);
+      }
+      P += __builtin_popcountll(bm);
     }
-    P += __builtin_popcountll(bm);
   }
   const int W = wave_sum_i(wsum);
   if (L > -INFINITY && W < K) {  // the K-th largest may lie below some block's t_b
@@ -1235,68 +1278,80 @@ __device__ __forceinline__ void wave_row_threshold(lds_u* U, int NB, int Q, int 
     em = static_cast<double>(ntie) * tk_mass;
   }
   float t = tk;
+  const int nent = ngt + (ntie > 0 ? 1 : 0);
   if (top_p < 1.0) {
-    float sv = ev;
-    double sm = em;
-    wave_sort_desc<true>(sv, sm);
-    const double cum = wave_incl_scan(sm);
-    const double zk = readlane_d(cum, 63);
-    const unsigned long long hb = __ballot(sv > -INFINITY && cum / zk >= top_p);
-    if (hb) t = readlane_f(sv, __ffsll(static_cast<long long>(hb)) - 1);
+    // each kept entry: the mass of the entries above it and equal to it (LDS broadcast, entry order)
+    lds_f* kvv = sc + kThrKept;
+    lds_d* kvm = reinterpret_cast<lds_d*>(sc + kThrHist);
+    kvv[lane] = lane < nent ? ev : __uint_as_float(kNoValue);
+    kvm[lane] = lane < nent ? em : 0.0;
+    const double zk = readlane_d(wave_incl_scan(lane < nent ? em : 0.0), 63);
+    double above = 0.0, same = 0.0;
+    for (int j = 0; j < nent; j += 4) {
+      const f32x4 v4 = *reinterpret_cast<const lds_f4*>(kvv + j);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double mq = kvm[j + q];
+        above += v4[q] > ev ? mq : 0.0;
+        same += v4[q] == ev ? mq : 0.0;
+      }
+    }
+    const bool hit = lane < nent && above / zk < top_p && (above + same) / zk >= top_p;
+    const unsigned long long hb = __ballot(hit);
+    if (hb) t = readlane_f(ev, __ffsll(static_cast<long long>(hb)) - 1);
     // (none: the kept mass summed short of top_p by rounding; the top-k set stays)
   }
-  // kept mass of each packed entry (above tk: its own; tk's group: tk's mass times its multiplicity),
-  // then their prefix sums in entry order (block by block)
-  const double kept_tk = (t == tk) ? tk_mass : 0.0;
-  if (my_idx >= 0) pw[my_idx] = ev >= t ? em : 0.0;  // (kv and kidx were read: the masses may overlay them)
-  double carry = 0.0;
-  for (int i0 = 0; i0 < P; i0 += 64) {
-    const int i = i0 + lane;
-    double c = 0.0;
-    if (i < P) {
-      const float v = pv[i];
-      c = v > tk ? pw[i] : (v == tk ? static_cast<double>(pm[i] & kMultMask) * kept_tk : 0.0);
-    }
-    const double inc = wave_incl_scan(c) + carry;
-    if (i < P) pw[i] = inc;
-    carry = readlane_d(inc, 63);
-  }
-  // block b's entries end after the last of them (the values area is free now);
-  // blocks without entries end where the block before them does
-  lds_i* ends = reinterpret_cast<lds_i*>(pv);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) ends[lane + 64 * k] = 0;
-  for (int i0 = 0; i0 < P; i0 += 64) {
-    const int i = i0 + lane;
-    if (i < P) {
-      const uint32_t b = pm[i] >> kMultBits;
-      if (i + 1 == P || (pm[i + 1] >> kMultBits) != b) ends[b] = i + 1;
-    }
-  }
-  // max-scan over the NB (<= 256) blocks, four a lane
-  int e4[4], lm = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    lm = max(lm, ends[4 * lane + k]);
-    e4[k] = lm;
-  }
-  const int pre = wave_incl_max_i(lm);
-  const int carry_in = dpp_i<kWaveShr1, 0xF>(0, pre);  // the lanes before this one
-#pragma unroll
-  for (int k = 0; k < 4; ++k) ends[4 * lane + k] = max(e4[k], carry_in);
-  // member w: blocks w*Q .. w*Q+Q-1
-  double share = 0.0;
-  if (lane < NW) {
-    const int e = ends[(lane + 1) * Q - 1];
-    const int st = lane == 0 ? 0 : ends[lane * Q - 1];
-    share = (e > 0 ? pw[e - 1] : 0.0) - (st > 0 ? pw[st - 1] : 0.0);
-  }
-  const double iz = 1.0 / carry;
-  if (lane < NW) mass[lane] = share * iz;
+  // the kept mass (the members' shares are taken when a draw needs them: wave_row_shares)
+  const double z = readlane_d(wave_incl_scan((lane < nent && ev >= t) ? em : 0.0), 63);
+  (void)mass;
+  (void)Q;
+  (void)NW;
+  (void)my_idx;
+  (void)pw;
   if (lane == 0) {
     *thr = t;
-    *iz_out = iz;
+    *iz_out = 1.0 / z;
   }
+}
+
+// The members' shares of a row's kept mass (one wave), for a draw from the
+// row's truncated target: the entries >= t of its lists (NB blocks of LW words,
+// Q a member), 64 at a time in word order, their masses computed a lane each
+// and summed member by member in word order.  sc: 192 floats of scratch.
+__device__ __forceinline__ void wave_row_shares(const lds_u* U, int NB, int Q, int NW, int LW, float t, float m,
+                                                double inv_tau, double iz, lds_f* sc, lds_d* mass) {
+  const int lane = threadIdx.x & 63;
+  const int nw = NB * LW;
+  const float inv = 1.0f / static_cast<float>(LW);
+  lds_i* gb = reinterpret_cast<lds_i*>(sc);
+  lds_d* gw = reinterpret_cast<lds_d*>(sc + 64);
+  double share = 0.0;
+  int n_in = 0;
+  auto flush = [&]() {
+    for (int j = 0; j < n_in; j += 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool mine = j + q < n_in && gb[j + q] == lane;
+        share += mine ? gw[j + q] : 0.0;
+      }
+    }
+    n_in = 0;
+  };
+  for (int i0 = 0; i0 < nw; i0 += 64) {
+    const ListWord e = list_word(U, nw, LW, inv, i0 + lane);
+    const bool keep = e.v >= t;
+    const unsigned long long bm = __ballot(keep);
+    const int cnt = __builtin_popcountll(bm);
+    if (n_in + cnt > 64) flush();
+    if (keep) {
+      const int pos = n_in + lanes_below(bm);
+      gb[pos] = e.blk / Q;
+      gw[pos] = static_cast<double>(e.mult) * exp1((static_cast<double>(e.v) - static_cast<double>(m)) * inv_tau);
+    }
+    n_in += cnt;
+  }
+  flush();
+  if (lane < NW) mass[lane] = share * iz;
 }
 
 // kFits: the slice (S <= kSliceCap floats) lives in LDS, so every slice access is an
@@ -1332,6 +1387,8 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   // whether its lists were too short (a second round with K-lists follows)
   __shared__ float s_thr[kMaxEager + 1];
   __shared__ int s_tfb[kMaxEager + 1];
+  __shared__ int s_tsh[kMaxEager + 1];  // the row's member shares of its kept mass are in e_mass already
+  __shared__ int s_dnb, s_dq, s_dlw;    // the current later row's lists in eager_l: blocks, parts, words
 
   const int NW = a.NW;
   const int b = blockIdx.x / NW;
@@ -1363,6 +1420,9 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
   unsigned long long* const lists_d = lists_b + static_cast<long>(8) * NW * LWS;
   unsigned long long* const lists_s = lists_d + static_cast<long>(T) * 4 * NW * LWS;
   int drow = 0, srow = 0;  // rows of later first lists and of second rounds used so far
+  // the rows' sums of exp((l - max) / t) are not needed when greedy, nor when truncating (the threshold
+  // gives the kept mass): the statistics then take the max and its index only
+  const bool no_z = a.greedy || a.trunc;
   // part q of Q of a slice of n elements (a multiple of 4 long, so that parts stay 16-byte aligned)
   auto part_of = [&](int q, int Q, int* len) __attribute__((always_inline)) {
     const int nq = (n + 4 * Q - 1) / (4 * Q) * 4;
@@ -1380,7 +1440,15 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
     } else if (lane == 0) {
       s_thr[r] = -INFINITY;
       s_tfb[r] = 0;
+      if (e_err[r] == 0) e_err[r] = SPEC_DEV_EMPTY;  // (the max is -inf: nothing to keep)
     }
+  };
+  // row r's member shares of its kept mass (one wave; sc: 192 floats)
+  auto row_shares = [&](int r, uint32_t* U, int NB, int Q, int LW, float* sc) __attribute__((always_inline)) {
+    if (e_err[r] == 0 && isfinite(e_m[r]))
+      wave_row_shares(lds(U), NB, Q, NW, LW, s_thr[r], e_m[r], a.inv_tau, e_iz[r], lds(sc),
+                      lds(&e_mass[r * kMaxTeam]));
+    if (lane == 0) s_tsh[r] = 1;
   };
   // (whole workgroup) the members' K-lists of row r, whose first lists were too
   // short, and its threshold from them; slice: this member's slice of the row
@@ -1397,7 +1465,10 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
     }
     get_lists(gbl(row), LWS, LWS, NW, tag, lds(U), lds(&sh_fail));
     ++srow;
-    if (!sh_fail && wave == 0) row_threshold(r, U, NW, 1, LWS, sc);
+    if (!sh_fail && wave == 0) {
+      row_threshold(r, U, NW, 1, LWS, sc);
+      row_shares(r, U, NW, 1, LWS, sc);
+    }
     __syncthreads();
   };
 
@@ -1528,17 +1599,17 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
     if (kFits && E > 0) {
       switch (E) {
         case 1:
-          slice_stats_rows<1, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, cur_lbuf);
+          slice_stats_rows<1, true>(eager_l, ld, n, v0, no_z, a.inv_tau, s_rec, cur_lbuf);
           break;
         case 2:
-          slice_stats_rows<2, true>(eager_l, ld, n, v0, a.greedy, a.inv_tau, s_rec, cur_lbuf);
+          slice_stats_rows<2, true>(eager_l, ld, n, v0, no_z, a.inv_tau, s_rec, cur_lbuf);
           break;
         case 4:
         case 3:
-          slice_stats_rows_by_wave<4>(eager_l, ld, n, v0, a.greedy, a.inv_tau, E, s_rec);
+          slice_stats_rows_by_wave<4>(eager_l, ld, n, v0, no_z, a.inv_tau, E, s_rec);
           break;
         default:  // 5 to 8
-          slice_stats_rows_by_wave<8>(eager_l, ld, n, v0, a.greedy, a.inv_tau, E, s_rec);
+          slice_stats_rows_by_wave<8>(eager_l, ld, n, v0, no_z, a.inv_tau, E, s_rec);
           break;
       }
       if (tid < E) put_slot(&eager[wg * E + tid], s_rec[tid], tag);
@@ -1564,13 +1635,13 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         get_slots<2>(rows2, E, NW, tag, none, rr, &sh_fail);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          merge_row(rr[h], lane < NW, a.greedy, a.inv_tau, &e_m[wave + h * kWaves], &e_iz[wave + h * kWaves],
+          merge_row(rr[h], lane < NW, no_z, a.inv_tau, &e_m[wave + h * kWaves], &e_iz[wave + h * kWaves],
                     &e_arg[wave + h * kWaves], &e_err[wave + h * kWaves], &e_mass[(wave + h * kWaves) * kMaxTeam]);
       } else if (wave < E) {
         const Slot* const rows1[1] = {eager + wave};
         Rec rr[1];
         get_slots<1>(rows1, E, NW, tag, none, rr, &sh_fail);
-        merge_row(rr[0], lane < NW, a.greedy, a.inv_tau, &e_m[wave], &e_iz[wave], &e_arg[wave], &e_err[wave],
+        merge_row(rr[0], lane < NW, no_z, a.inv_tau, &e_m[wave], &e_iz[wave], &e_arg[wave], &e_err[wave],
                   &e_mass[wave * kMaxTeam]);
       }
       if (cx < T) {
@@ -1586,9 +1657,18 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
         uint32_t* U = reinterpret_cast<uint32_t*>(cur_lbuf);
         get_lists(gbl(lists_b), LWS, LWe, E * NBe, tag, lds(U), lds(&sh_fail));
         if (!sh_fail) {
-          for (int r = wave; r < E; r += kWaves)
+          for (int r = wave; r < E; r += kWaves) {
             row_threshold(r, U + r * NBe * LWe, NBe, a.q_e, LWe, cur_qbuf + wave * kWaveSel);
+            if (lane == 0) s_tsh[r] = 0;
+          }
           __syncthreads();
+          bool any_fb = false;
+          for (int r = 0; r < E; ++r) any_fb = any_fb || s_tfb[r] != 0;
+          if (any_fb) {  // a second round overwrites these lists: take every other row's shares first
+            for (int r = wave; r < E; r += kWaves)
+              if (!s_tfb[r]) row_shares(r, U + r * NBe * LWe, NBe, a.q_e, LWe, cur_qbuf + wave * kWaveSel);
+            __syncthreads();
+          }
           for (int r = 0; r < E && !sh_fail; ++r)
             if (s_tfb[r]) second_round(r, eager_l + r * ld, U, cur_qbuf);
         }
@@ -1629,7 +1709,7 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       }
       __syncthreads();
       if (u >= E) {  // a deeper row: its statistics now
-        slice_stats_rows<1, kFits>(cl, ld, n, v0, a.greedy, a.inv_tau, s_rec, row_partials);
+        slice_stats_rows<1, kFits>(cl, ld, n, v0, no_z, a.inv_tau, s_rec, row_partials);
         if (xrow >= a.part_rows) {  // more exchanges than planned: cannot happen for a valid tree
           if (tid == 0) sh_fail = 1;
           break;
@@ -1648,21 +1728,30 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
           const Slot* const rows1[1] = {xs};
           Rec r[1];
           get_slots<1>(rows1, 1, NW, tag, Rec{-INFINITY, 0x7fffffff, 0.0}, r, &sh_fail);
-          merge_row(r[0], lane < NW, a.greedy, a.inv_tau, &e_m[kMaxEager], &e_iz[kMaxEager], &e_arg[kMaxEager],
+          merge_row(r[0], lane < NW, no_z, a.inv_tau, &e_m[kMaxEager], &e_iz[kMaxEager], &e_arg[kMaxEager],
                     &e_err[kMaxEager], &e_mass[kMaxEager * kMaxTeam]);
+        } else if (a.trunc && drow < T) {  // meanwhile the other waves read every member's lists of the row
+          poll_lists(gbl(lists_d + static_cast<long>(drow) * NBd * LWS), LWS, LWd, NBd, tag,
+                     lds(reinterpret_cast<uint32_t*>(eager_l)), lds(&sh_fail), tid - 64, kThreads - 64);
         }
         __syncthreads();
         if (sh_fail) break;
-        if (a.trunc) {  // every member's list of the row, then its threshold
+        if (a.trunc) {  // the row's threshold from the lists
           if (drow >= T) {  // more rows than the tree has: cannot happen for a valid tree
             if (tid == 0) sh_fail = 1;
             break;
           }
           uint32_t* U = reinterpret_cast<uint32_t*>(eager_l);
-          get_lists(gbl(lists_d + static_cast<long>(drow) * NBd * LWS), LWS, LWd, NBd, tag, lds(U), lds(&sh_fail));
           ++drow;
-          if (sh_fail) break;
-          if (wave == 0) row_threshold(kMaxEager, U, NBd, a.q_d, LWd, eager_q);
+          if (wave == 0) {
+            row_threshold(kMaxEager, U, NBd, a.q_d, LWd, eager_q);
+            if (lane == 0) {
+              s_tsh[kMaxEager] = 0;
+              s_dnb = NBd;
+              s_dq = a.q_d;
+              s_dlw = LWd;
+            }
+          }
           __syncthreads();
           if (s_tfb[kMaxEager]) {
             second_round(kMaxEager, cl, U, eager_q);
@@ -1703,6 +1792,11 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
       const double m = sh_m, iz = sh_iz;
       // current residual weights of the 4 slice elements 4c .. 4c+3 (logits lv, draft probabilities qv)
       auto weight4 = [&](const f32x4& lv, const f32x4& qv, int c, double (&w)[4]) {
+        if (!(lv[0] >= thr || lv[1] >= thr || lv[2] >= thr || lv[3] >= thr)) {  // all truncated: p = 0, weight 0
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = 0.0;
+          return;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = (static_cast<double>(lv[e]) - m) * a.inv_tau;
         exp_lockstep<4>(w);
@@ -1859,6 +1953,13 @@ __global__ __launch_bounds__(kThreads) void reject_team_kernel(const TArgs a) {
           if (sh_fail) break;
         }
       }
+      if (a.trunc && !scanned && bonus && wave == 0 && !s_tsh[er]) {  // this row's shares, from its lists
+        if (er < E)
+          row_shares(er, reinterpret_cast<uint32_t*>(cur_lbuf) + er * NBe * LWe, NBe, a.q_e, LWe,
+                     reinterpret_cast<float*>(row_partials));
+        else
+          row_shares(er, reinterpret_cast<uint32_t*>(eager_l), s_dnb, s_dq, s_dlw, reinterpret_cast<float*>(row_partials));
+      }
       if (wave == 0) {
         double mass = 0.0;
         if (scanned || !bonus) {  // the masses gathered by the last exchange
@@ -2014,9 +2115,11 @@ size_t reject_workspace_zero_bytes() { return kHeaderBytes; }
 
 // Parts a member's slice of n logits is cut into when the selection takes
 // `rows` rows at once (a part a wave, four waves a workgroup): long slices are
-// split so that their passes run on several waves.
-static int slice_parts(int n, int rows) {
-  const int q = n >= 2048 ? 4 : (n >= 1024 ? 2 : 1);
+// split so that their passes run on several waves, while a row keeps at most
+// 64 blocks.
+static int slice_parts(int n, int rows, int NW) {
+  int q = n >= 2048 ? 4 : (n >= 1024 ? 2 : 1);
+  while (q > 1 && NW * q > 64) q >>= 1;  // (more blocks make the threshold's union longer than the passes save)
   return std::max(1, std::min(q, kWaves / std::max(rows, 1)));
 }
 
@@ -2035,9 +2138,9 @@ struct TruncPlan {
 };
 static TruncPlan trunc_plan(const Team& t, int K) {
   TruncPlan p;
-  p.q_e = slice_parts(t.S, t.E);
+  p.q_e = slice_parts(t.S, t.E, t.NW);
   p.kc_e = first_list_len(t.NW * p.q_e, K, std::max(t.E, 1), kSliceCap);
-  p.q_d = slice_parts(t.S, 1);
+  p.q_d = slice_parts(t.S, 1, t.NW);
   p.kc_d = first_list_len(t.NW * p.q_d, K, 1, kEagerCapBig);
   return p;
 }
