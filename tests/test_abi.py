@@ -203,12 +203,13 @@ def test_reject_team_plan_fits_the_resident_grid(lib):
 
 def test_truncated_sampler_plan_and_validation(lib):
     full = 256
-    # first lists of a later row: each member's slice cut into 4 parts from 2048 logits on (2 from 1024), a list
-    # of about twice a part's share of the top-k plus 6 (chain: 63 parts, 2 * 50 / 63 -> 2 + 6; batched serving:
-    # 4 members x 4 parts of 2000, 100 / 16 -> 7 + 6; EAGLE-style: 32 x 4 parts of 1002, 80 / 128 -> 1 + 6)
+    # first lists of a later row: each member's slice cut into 4 parts from 2048 logits on (2 from 1024) while a
+    # row keeps at most 64 lists, a list of about twice a part's share of the top-k plus 6 (chain: 63 parts,
+    # 2 * 50 / 63 -> 2 + 6; batched serving: 4 members x 4 parts of 2000, 100 / 16 -> 7 + 6; EAGLE-style:
+    # 32 members x 2 parts of 2004, 80 / 64 -> 2 + 6)
     assert stv.spec_tree_reject_truncated_plan(1, 5, 32000, 50, full) == (63, 8)
     assert stv.spec_tree_reject_truncated_plan(64, 16, 32000, 50, full) == (4, 13)
-    assert stv.spec_tree_reject_truncated_plan(8, 64, 128256, 40, full) == (32, 7)
+    assert stv.spec_tree_reject_truncated_plan(8, 64, 128256, 40, full) == (32, 8)
     assert stv.spec_tree_reject_truncated_plan(1, 256, 32000, 50, full) == (32, 10)
     for B in (1, 3, 64, 300):
         for T in (1, 5, 16, 300, 512):
