@@ -26,7 +26,8 @@ p90) of 100 single-step replays, each bracketed by events.
 The line also carries the same step without the write (`without_kv_write`) and
 the step against a truncated target (`truncated_target`: top-k 50 then top-p
 0.9, applied inside the sampler by spec_tree_reject_truncated to the rows its
-walk visits).  Its `kernels` also time spec_tree_kv_write (the write as a launch
+walk visits; `separate_pass` beside it: the same target truncated by
+spec_tree_truncate over every row before the plain sampler).  Its `kernels` also time spec_tree_kv_write (the write as a launch
 of its own), spec_tree_truncate (the same truncation as a separate pass over
 every target row, out of place) and the truncating sampler; none of these is
 part of the timed step, whose target is not truncated.
@@ -571,6 +572,15 @@ def measure(cfg, args, quick=False):
         (write_attn if fused else attn)(sl["c"])
         reject_compact_trunc(sl["c"], sl)
 
+    for c in copies:  # each copy's truncated target rows, written by the separate truncation pass
+        c["logits_t"] = torch.empty_like(c["logits"])
+
+    def step_trunc_pass(sl):  # the same target, truncated by a pass over every row before the plain sampler
+        c = sl["c"]
+        (write_attn if fused else attn)(c)
+        stv.spec_tree_truncate(c["logits"], w.temperature, TRUNC_K, TRUNC_P, out=c["logits_t"], status=c["status"])
+        reject_compact(dict(c, logits=c["logits_t"]), sl)
+
     if args.calib_copy and not quick:  # plain copies of known size, for scaling the HBM counters
         for nbytes in (CALIB_BYTES, CALIB_BYTES_BIG):
             src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
@@ -579,7 +589,7 @@ def measure(cfg, args, quick=False):
             torch.cuda.synchronize()
             del src, dst
 
-    for fn in ((step, step_plain, step_trunc) if fused else (step, step_trunc)):
+    for fn in ((step, step_plain, step_trunc, step_trunc_pass) if fused else (step, step_trunc, step_trunc_pass)):
         for sl in slots:  # eager pass: validates every copy and slot
             fn(sl)
         torch.cuda.synchronize()
@@ -633,6 +643,11 @@ def measure(cfg, args, quick=False):
                  "top_k": TRUNC_K, "top_p": TRUNC_P,
                  "note": "the step with spec_tree_reject_truncated (top-k then top-p applied inside the sampler to "
                          "the rows its walk visits) in place of spec_tree_reject_compact"}
+    ms_tp, value_tp, spread_tp = timed(step_trunc_pass, "step with a separate truncation pass")
+    truncated["separate_pass"] = {
+        "value": round(value_tp, 1), "ms_per_step": round(ms_tp, 5), "step_us": spread_tp,
+        "note": "the same target truncated by spec_tree_truncate over every row (out of place) before "
+                "spec_tree_reject_compact"}
 
     # accepted tokens per step over every slot's walk (each slot has its own offset), untruncated target
     for sl in slots:
