@@ -162,6 +162,7 @@ struct TArgs2 {
   unsigned* counters;  // [B * Hkv * n_rt], then the item queue's [next id, workgroups done]
   int B, T, Hq, Hkv, G, R, n_rt, splits, pps, max_blocks, num_blocks;
   int reorder;  // longest items first (one row tile, B <= 64)
+  int kv_stream;  // every K/V page is read by one item only: load it non-temporally
   int persist;  // each workgroup takes items from a queue until none is left
   long items;
   float sl2;
@@ -411,6 +412,21 @@ __device__ __forceinline__ void rotate_queries(const TArgs2& a, int Lb, int node
 // already clamped to its valid range (err: SPEC_DEV_LENGTH if it was not).
 // Every thread of the workgroup calls it; it returns at points the whole
 // workgroup reaches together, or after its merge.
+// One 16-key page of K and of V (a kv head's 4 KB each) straight into LDS,
+// 16 bytes a lane: bytes t*1024 + 16 i hold key 4t + i/16, chunk position
+// i%16, which is chunk position ^ key of K and position ^ 2*(key % 8) of V.
+// kAux: the loads' cache policy (kLoadNT for pages no other workgroup reads).
+template <int kAux>
+__device__ __forceinline__ void load_kv_page(const uint16_t* kp, const uint16_t* vp, uint8_t* kdst, uint8_t* vdst,
+                                             int dma_key, int dma_pos) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int key = 4 * t + dma_key;
+    __builtin_amdgcn_global_load_lds(kp + key * kD + ((dma_pos ^ key) * 8), kdst + t * 1024, 16, 0, kAux);
+    __builtin_amdgcn_global_load_lds(vp + key * kD + ((dma_pos ^ (2 * (key & 7))) * 8), vdst + t * 1024, 16, 0, kAux);
+  }
+}
+
 template <int NRB, bool kFused>
 __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, int Lb, int err, TileLds<NRB>& L) {
   constexpr int RT = 64 * NRB;  // rows per workgroup
@@ -514,13 +530,10 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
     const long base = (static_cast<long>(blk < 0 ? 0 : blk) * a.Hkv + g) * (kBlockSize * kD);
     uint8_t* kdst = tiles + (it & 1) * kTileBytes + wave * kPageBytes;
     uint8_t* vdst = kdst + 4 * kPageBytes;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int key = 4 * t + dma_key;
-      __builtin_amdgcn_global_load_lds(a.k + base + key * kD + ((dma_pos ^ key) * 8), kdst + t * 1024, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(a.v + base + key * kD + ((dma_pos ^ (2 * (key & 7))) * 8), vdst + t * 1024, 16, 0,
-                                       0);
-    }
+    if (a.kv_stream)
+      load_kv_page<kLoadNT>(a.k + base, a.v + base, kdst, vdst, dma_key, dma_pos);
+    else
+      load_kv_page<0>(a.k + base, a.v + base, kdst, vdst, dma_key, dma_pos);
   };
   // per-lane LDS offsets of the fragments within one page
   uint32_t k_off[4], vt_off[8];
@@ -1157,6 +1170,10 @@ static TArgs2 tile_args(const AttnPlan& plan, const AttnLaunch& L) {
   a.num_blocks = L.num_blocks;
   a.items = plan.items;
   a.reorder = plan.reorder;
+  // With one row tile per (b, g) each K/V page is read by one item; with several,
+  // the row tiles of a KV chunk find it in L2 (streaming loads made the 16-tile
+  // Sequoia-scale layer slower), so only the former load non-temporally.
+  a.kv_stream = plan.n_rt == 1;
   a.sl2 = L.scale * kLog2e;
   return a;
 }

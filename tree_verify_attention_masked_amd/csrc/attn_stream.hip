@@ -287,8 +287,9 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
       const int key = 4 * t + dma_key;
       const uint16_t* ks = a.k + base + key * kD + ((dma_pos ^ key) * 8);
       const uint16_t* vs = a.v + base + key * kD + ((dma_pos ^ (2 * (key & 7))) * 8);
-      __builtin_amdgcn_global_load_lds(ks, slot + t * 1024, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vs, slot + kPageBytes + t * 1024, 16, 0, 0);
+      // every page is read by this wave only: non-temporal loads
+      __builtin_amdgcn_global_load_lds(ks, slot + t * 1024, 16, 0, kLoadNT);
+      __builtin_amdgcn_global_load_lds(vs, slot + kPageBytes + t * 1024, 16, 0, kLoadNT);
     }
   };
 

@@ -11,6 +11,9 @@ namespace spectree {
 constexpr int kBlockSize = 16;
 constexpr int kMaxT = 512;          // tree nodes: ancestor bitsets of 8 x 64 bits
 constexpr int kMaxV = 262144;       // rejected-token bitmap of the sampler lives in LDS
+// Cache-policy operand of a vector memory instruction: the non-temporal (nt)
+// bit, for data read once, which should not displace what the caches hold.
+constexpr int kLoadNT = 2;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
