@@ -6,8 +6,12 @@ launch -- on the GPU, through the C ABI:
   attention tolerance of test_gpu_attention.py; the written cache rows within
   one bf16 unit of oracle/rope.py's, every other slot unchanged;
 * against the separate calls on the same inputs: spec_tree_kv_write, then
-  spec_tree_attn on the queries it rotated, leave the same cache and give the
-  same outputs, bit for bit;
+  spec_tree_attn on the queries it rotated, leave the same cache bit for bit;
+  their outputs agree within the stated bf16 attention tolerance everywhere,
+  and both are within the oracle's bound on the compared rows (the one-launch
+  path shortens the stream-K ranges of the workgroups that write, so a
+  (sequence, kv head) may be cut at other points: each piece rounds P to bf16
+  against its own running max and the partials merge in another order);
 * the caller's queries are left as they were; one workspace serves calls in a
   row (its counters are back at zero after each call); a bad parent row is
   reported and leaves that sequence's cache rows unwritten while the other
@@ -26,7 +30,7 @@ import torch
 
 import oracle
 import tree_verify_attention_masked_amd as stv
-from helpers import DevWorkload, abs_values, assert_attn_close, attn_to_f64, dev_kv, host_kv
+from helpers import BF16_ATOL, BF16_RTOL, DevWorkload, abs_values, assert_attn_close, attn_to_f64, dev_kv, host_kv
 from workloads import make_workload
 from workloads.gen import f32_to_bf16_bits
 
@@ -86,6 +90,14 @@ def _separate(w, k_new, v_new, theta):
     return d, out
 
 
+def _assert_same_outputs(out, out_sep, what):
+    """Outputs of the two paths everywhere: within the stated bf16 attention
+    tolerance of each other (the tight bound is checked against the oracle)."""
+    a, b = out.double(), out_sep.double()
+    bad = ~((a - b).abs() <= BF16_ATOL + BF16_RTOL * b.abs())
+    assert not bool(bad.any()), f"{what}: {int(bad.sum())} outputs differ from the separate calls"
+
+
 def _oracle(w, k_new, v_new, theta, rows):
     """Oracle rows of the fused call: rotate (fp64), round to bf16 as stored, attend."""
     q_rot, kc, vc = oracle.tree_kv_write(k_new, v_new, w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_lens,
@@ -111,17 +123,18 @@ def test_write_attn(name, kw, theta, n_rows):
     assert int(d.status.abs().sum()) == 0, d.status.tolist()
     d_sep, out_sep = _separate(w, k_new, v_new, theta)
     assert torch.equal(_bits(d.k), _bits(d_sep.k)) and torch.equal(_bits(d.v), _bits(d_sep.v)), "cache differs"
-    assert torch.equal(_bits(out), _bits(out_sep)), "outputs differ from the separate calls"
+    _assert_same_outputs(out, out_sep, name)
     rows = None
     if n_rows is not None:
         rng = np.random.default_rng(5)
         rows = [(int(rng.integers(w.B)), int(rng.integers(w.T)), int(rng.integers(w.Hq))) for _ in range(n_rows)]
         rows += [(w.B - 1, i, h) for i in range(w.T) for h in (0, w.Hq - 1)][:200]
     ref, ref_abs, kc, _ = _oracle(w, k_new, v_new, theta, rows)
-    got = attn_to_f64(w, out)
-    if rows is not None:
-        got = np.stack([got[b, i, h] for b, i, h in rows])
-    assert_attn_close(got, ref, "bf16", name, ref_abs)
+    for label, o in (("one launch", out), ("separate calls", out_sep)):
+        got = attn_to_f64(w, o)
+        if rows is not None:
+            got = np.stack([got[b, i, h] for b, i, h in rows])
+        assert_attn_close(got, ref, "bf16", f"{name}, {label}", ref_abs)
     # the cache against the oracle: written rows within one bf16 unit (values
     # exact), every other slot bit for bit as it was (unused slots hold NaN)
     k_got, v_got = host_kv(w, d.k), host_kv(w, d.v)
@@ -153,9 +166,11 @@ def test_workspace_serves_calls_in_a_row():
         d = DevWorkload(w)
         out = _fused(w, d, k_new, v_new, theta, workspace=ws)
         d_sep, out_sep = _separate(w, k_new, v_new, theta)
-        assert torch.equal(_bits(out), _bits(out_sep)), f"call {call}"
+        _assert_same_outputs(out, out_sep, f"call {call}")
         assert torch.equal(_bits(d.k), _bits(d_sep.k)), f"call {call}"
-        head = ws[: 4 * (w.B * w.Hkv * 1 + 2 + w.B)].view(torch.int32)  # arrival counters, queue, row counts
+        n_chunks = (2 * w.T * w.Hkv + 63) // 64
+        # arrival counters, [unused, workgroups done], written-chunk counts, chunk claims
+        head = ws[: 4 * (w.B * w.Hkv * 1 + 2 + w.B + w.B * n_chunks)].view(torch.int32)
         assert int(head.abs().sum()) == 0, f"call {call} left counters set"
 
 

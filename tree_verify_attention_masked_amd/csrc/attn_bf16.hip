@@ -28,6 +28,13 @@
 // unnormalised partials (O, m, l) and the last workgroup of a (b, g, rt) to
 // finish merges them (arrival counter in the workspace, reset by that
 // workgroup).
+//
+// A ragged batch with more items than resident workgroups (64-row tiles, one
+// row tile per (b, g)) is instead cut stream-K fashion: the (b, g) are laid end
+// to end as tiles plus a fixed cost each, and every resident workgroup takes an
+// equal range of that line, so all of them finish together whatever the mix of
+// lengths; a (b, g) cut between workgroups is merged like the splits (see
+// SkPlan).
 #include <algorithm>
 #include <cmath>
 
@@ -43,8 +50,21 @@ constexpr unsigned kFlagSpinLimit = 1u << 24;  // polls of a write item's flag (
 constexpr int kPageBytes = kBlockSize * kD * 2;  // one page of one head: 4 KB
 constexpr int kTileBytes = 8 * kPageBytes;       // 4 K pages, then 4 V pages: 64 keys
 constexpr int kMaxSplitPages = 1024;             // pages per split (planning keeps below)
+constexpr int kMaxPiecePages = 1536;             // pages per piece of the stream-K split (64-row tiles)
+// The stream-K split weighs each (b, g) as its tiles plus kSkItemUnits tiles'
+// worth of fixed cost (block indices and queries, the first tile's latency,
+// the ancestor sets, the epilogue) and a write chunk as kSkWriteUnits tiles.
+constexpr int kSkItemUnits = 5;
+constexpr int kSkWriteUnits = 6;
 
 __device__ __forceinline__ void wait_vm0() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// A workgroup barrier for data exchanged through LDS only: this wave's LDS
+// accesses complete, then the barrier.  Unlike __syncthreads() (a workgroup
+// fence, which waits for every outstanding memory access), it leaves the
+// direct global->LDS loads of a tile in flight, so work between a tile's issue
+// and its use overlaps the tile's latency.  The LDS it publishes must not be
+// what those loads write.
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -157,19 +177,19 @@ struct TArgs2 {
   const int32_t* parent;
   uint16_t* out;
   int32_t* status;
-  float* part_o;       // [items][RT][D]
-  float* part_ml;      // [items][RT][2]
-  unsigned* counters;  // [B * Hkv * n_rt], then the item queue's [next id, workgroups done]
+  float* part_o;       // [slots][RT][D]: one slot an item, or (stream-K) two a workgroup
+  float* part_ml;      // [slots][RT][2]
+  unsigned* counters;  // [B * Hkv * n_rt] arrivals, then [unused, workgroups done]
   int B, T, Hq, Hkv, G, R, n_rt, splits, pps, max_blocks, num_blocks;
-  int reorder;  // longest items first (one row tile, B <= 64)
+  int streamk;    // the stream-K split (64-row tiles, one row tile per (b, g), B <= 64)
   int kv_stream;  // every K/V page is read by one item only: load it non-temporally
-  int persist;  // each workgroup takes items from a queue until none is left
   long items;
   float sl2;
-  // The tree's K/V write in the same launch: the queue's first n_write ids are
-  // write items, n_chunks per sequence (chunk_rows of its 2 T Hkv K and V rows each),
-  // then come the attention items, which rotate their own queries; an item
-  // that holds tree keys waits until its sequence's chunks are all written.
+  // The tree's K/V write in the same launch (stream-K split only): n_write
+  // chunks, n_chunks per sequence (chunk_rows of its 2 T Hkv K and V rows
+  // each), each claimed before it is written; attention pieces rotate their
+  // own queries, and a piece that holds tree keys waits until its sequence's
+  // chunks are all written.
   int n_write;             // B * n_chunks
   int n_chunks;            // per sequence: ceil(2 T Hkv / chunk_rows)
   int chunk_rows;          // a multiple of 8, at most 64
@@ -179,22 +199,25 @@ struct TArgs2 {
   const uint16_t* v_new;   // [B,T,Hkv,D] their values
   uint16_t* kc;            // = k, = v: the cache the write items fill
   uint16_t* vc;
-  unsigned* flags;         // [B]: chunks of the sequence written so far
+  unsigned* flags;         // [B]: chunks of the sequence written so far, then [n_write] claim words
 };
 
 constexpr int kAncWords = kMaxT / 64;  // words of one node's ancestor-or-self bitset
 
 // Ancestor-or-self bitsets of every node of a parent row, by pointer doubling:
-// anc[i] holds the path from i up to, not including, jump[i] (at first {i} and
-// i's parent); each round joins the set of jump[i] and takes over its jump, so
-// ceil(log2(depth + 1)) rounds cover every path.  A node whose parent is not
-// an earlier node (or the root's is not -1) ends its path there.  `jump` is
-// the parent row (overwritten); `anc` holds T x kAncWords words.  Every thread
-// of the 256-thread workgroup calls it (T <= 512).
+// anc[i] holds the path from i up to, not including, jump[i] (at first {i},
+// jump[i] = i's parent); each round joins the set of jump[i] and takes over its
+// jump, so ceil(log2(T)) rounds cover every path (a path has at most T nodes).
+// A node whose parent is not an earlier node (or the root's is not -1) ends its
+// path there.  `jump` is the parent row (overwritten); `anc` holds T x
+// kAncWords words.  Every thread of the 256-thread workgroup calls it (T <=
+// 512); its barriers wait for LDS only (see lds_barrier), the first one for
+// every earlier reader of `jump` and `anc`, the last one publishing `anc`.
 __device__ int build_ancestors_lds(int* jump, int T, uint64_t* anc) {
   const int tid = threadIdx.x;
   const int nw = (T + 63) >> 6;
   int err = 0;
+  lds_barrier();
   for (int i = tid; i < T; i += 256) {
     const int p = jump[i];
     if (!(i == 0 ? p == -1 : (p >= 0 && p < i))) {
@@ -205,8 +228,9 @@ __device__ int build_ancestors_lds(int* jump, int T, uint64_t* anc) {
     for (int w = 0; w < kAncWords; ++w)
       if (w < nw) anc[i * kAncWords + w] = (w == (i >> 6)) ? 1ull << (i & 63) : 0ull;
   }
-  int pending = 1;
-  while (__syncthreads_or(pending)) {  // the barrier also publishes the last round's writes
+  const int rounds = T > 1 ? 32 - __clz(T - 1) : 0;
+  for (int round = 0; round < rounds; ++round) {
+    lds_barrier();  // the last round's writes (or the initial sets) are visible
     uint64_t add[2][kAncWords];
     int nj[2];
 #pragma unroll
@@ -220,8 +244,7 @@ __device__ int build_ancestors_lds(int* jump, int T, uint64_t* anc) {
         for (int w = 0; w < kAncWords; ++w) add[k][w] = w < nw ? anc[j * kAncWords + w] : 0ull;
       }
     }
-    __syncthreads();  // every read of this round before any write
-    pending = 0;
+    lds_barrier();  // every read of this round before any write
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int i = tid + 256 * k;
@@ -230,10 +253,10 @@ __device__ int build_ancestors_lds(int* jump, int T, uint64_t* anc) {
         for (int w = 0; w < kAncWords; ++w)
           if (w < nw) anc[i * kAncWords + w] |= add[k][w];
         jump[i] = nj[k];
-        pending |= nj[k] >= 0;
       }
     }
   }
+  lds_barrier();
   return err;
 }
 
@@ -242,7 +265,7 @@ struct TileLds {
   __attribute__((aligned(16))) uint8_t tiles[2 * kTileBytes];  // 2 x (4 K pages, 4 V pages)
   uint64_t anc[64 * NRB * kAncWords];  // the bitsets of the item's nodes (at most one per row)
   int s_par[kMaxT];
-  int s_blk[kMaxSplitPages];
+  int s_blk[NRB == 1 ? kMaxPiecePages : kMaxSplitPages];
   int s_last, s_next;
 };
 static_assert(kMaxT * kAncWords * sizeof(uint64_t) <= kTileBytes,
@@ -346,11 +369,14 @@ __device__ __noinline__ double2 trig_direct(int p, int j, double log2_theta) {
 }
 
 // Cosines and sines of every (depth d in [dmin, dmin + n), pair j < 64) at
-// position Lb + d into trig[(d - dmin) * 64 + j], when n <= kTrigDepths.
+// position Lb + d into trig[(d - dmin) * 64 + j], when n <= kTrigDepths (in
+// line: a call would make the caller wait for every load in flight).
 __device__ __forceinline__ void fill_trig(double2* trig, int Lb, int dmin, int n, double log2_theta) {
   if (n > kTrigDepths) return;
   for (int e = threadIdx.x; e < n * 64; e += 256) {
-    trig[e] = trig_direct(Lb + dmin + (e >> 6), e & 63, log2_theta);
+    double c, sn;
+    rope_cos_sin(Lb + dmin + (e >> 6), e & 63, kD, log2_theta, &c, &sn);
+    trig[e] = double2{c, sn};
   }
 }
 
@@ -361,30 +387,71 @@ __device__ __forceinline__ void trig_of(const double2* trig, int Lb, int dmin, i
   *sn = cs.y;
 }
 
-// Rotates the lane's query fragments (rows of nodes node0 .. node1) for their
-// positions Lb + depth: the fragment holds dims c*32 + quad*8 + e (c < 4,
-// e < 8), so the pairs (j, j + 64) of the rotation are (c, c + 2) for c < 2,
-// all within the lane.  Depths and the table live in `buf` (a free 32 KB tile
-// buffer); the last barrier lets the caller reuse it.
+// Depth of node i by walking its parent row (a parent that is not an earlier
+// node ends the walk there, as in node_depths).
+__device__ __forceinline__ int walk_depth(const int* par, int i) {
+  int d = 0;
+  while (i > 0) {
+    const int p = par[i];
+    if (!(p >= 0 && p < i)) break;
+    i = p;
+    ++d;
+  }
+  return d;
+}
+
+// Rotates the lane's query fragments for their rows' positions Lb + depth: the
+// fragment holds dims c*32 + quad*8 + e (c < 4, e < 8), so the pairs (j, j +
+// 64) of the rotation are (c, c + 2) for c < 2, all within the lane.  Each lane
+// walks its rows' parent chains; the cosines and sines of the item's range of
+// depths are tabulated in `buf` (a free 32 KB tile buffer) behind LDS-only
+// barriers, so a tile already issued stays in flight meanwhile.  The table is
+// read until the caller's next barrier.
 template <int NRB>
-__device__ __forceinline__ void rotate_queries(const TArgs2& a, int Lb, int node0, int node1, int row_base, int l16,
-                                               int quad, const int* par, uint8_t* buf, bf16x8 (&qf)[NRB][4]) {
-  int* s_up = reinterpret_cast<int*>(buf);
-  int* s_dep = s_up + kMaxT;
-  int* s_rng = s_dep + kMaxT;  // [min, max] depth of the item's nodes
+__device__ __forceinline__ void rotate_queries(const TArgs2& a, int Lb, int row_base, int l16, int quad,
+                                               const int* par, uint8_t* buf, bf16x8 (&qf)[NRB][4]) {
+  int* s_rng = reinterpret_cast<int*>(buf);  // each wave's [min, max] depth of its rows' nodes
   double2* trig = reinterpret_cast<double2*>(buf + kTrigOffset);
-  node_depths(par, a.T, node0, node1, s_up, s_dep, s_rng);
-  const int dmin = s_rng[0], n = s_rng[1] - s_rng[0] + 1;
+  int dep[NRB];
+  int lo = 0x7fffffff, hi = -1;
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int r = row_base + rb * 16 + l16;
+    dep[rb] = r < a.R ? walk_depth(par, r / a.G) : 0;
+    if (r < a.R) {
+      lo = min(lo, dep[rb]);
+      hi = max(hi, dep[rb]);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    lo = min(lo, __shfl_xor(lo, o));
+    hi = max(hi, __shfl_xor(hi, o));
+  }
+  // the item's range from the waves' ranges (plain LDS stores: LDS atomics
+  // would wait for the tile in flight)
+  if ((threadIdx.x & 63) == 0) {
+    s_rng[2 * (threadIdx.x >> 6)] = lo;
+    s_rng[2 * (threadIdx.x >> 6) + 1] = hi;
+  }
+  lds_barrier();
+  int dmin = s_rng[0], dmax = s_rng[1];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    dmin = min(dmin, s_rng[2 * w]);
+    dmax = max(dmax, s_rng[2 * w + 1]);
+  }
+  const int n = dmax >= dmin ? dmax - dmin + 1 : 0;
   fill_trig(trig, Lb, dmin, n, a.log2_theta);
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const int r = row_base + rb * 16 + l16;
     if (r >= a.R) continue;
-    const int d = s_dep[r / a.G];
+    const int d = dep[rb];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      u32x4 lo = __builtin_bit_cast(u32x4, qf[rb][c]), hi = __builtin_bit_cast(u32x4, qf[rb][c + 2]);
+      u32x4 lo4 = __builtin_bit_cast(u32x4, qf[rb][c]), hi4 = __builtin_bit_cast(u32x4, qf[rb][c + 2]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         uint32_t nlo = 0, nhi = 0;
@@ -393,25 +460,20 @@ __device__ __forceinline__ void rotate_queries(const TArgs2& a, int Lb, int node
           double cs, sn;
           trig_of(trig, Lb, dmin, n, d, c * 32 + quad * 8 + 2 * k + h, a.log2_theta, &cs, &sn);
           float y0, y1;
-          rope_turn(bf16_to_f32(static_cast<uint16_t>(lo[k] >> (16 * h))),
-                    bf16_to_f32(static_cast<uint16_t>(hi[k] >> (16 * h))), cs, sn, &y0, &y1);
+          rope_turn(bf16_to_f32(static_cast<uint16_t>(lo4[k] >> (16 * h))),
+                    bf16_to_f32(static_cast<uint16_t>(hi4[k] >> (16 * h))), cs, sn, &y0, &y1);
           nlo |= static_cast<uint32_t>(f32_to_bf16(y0)) << (16 * h);
           nhi |= static_cast<uint32_t>(f32_to_bf16(y1)) << (16 * h);
         }
-        lo[k] = nlo;
-        hi[k] = nhi;
+        lo4[k] = nlo;
+        hi4[k] = nhi;
       }
-      qf[rb][c] = __builtin_bit_cast(bf16x8, lo);
-      qf[rb][c + 2] = __builtin_bit_cast(bf16x8, hi);
+      qf[rb][c] = __builtin_bit_cast(bf16x8, lo4);
+      qf[rb][c + 2] = __builtin_bit_cast(bf16x8, hi4);
     }
   }
-  __syncthreads();
 }
 
-// The work of one item (b, g, KV split, row tile), sequence b's prefix length
-// already clamped to its valid range (err: SPEC_DEV_LENGTH if it was not).
-// Every thread of the workgroup calls it; it returns at points the whole
-// workgroup reaches together, or after its merge.
 // One 16-key page of K and of V (a kv head's 4 KB each) straight into LDS,
 // 16 bytes a lane: bytes t*1024 + 16 i hold key 4t + i/16, chunk position
 // i%16, which is chunk position ^ key of K and position ^ 2*(key % 8) of V.
@@ -427,8 +489,26 @@ __device__ __forceinline__ void load_kv_page(const uint16_t* kp, const uint16_t*
   }
 }
 
-template <int NRB, bool kFused>
-__device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, int Lb, int err, TileLds<NRB>& L) {
+// One piece of attention work: the rows of row tile rt of (b, g) against pages
+// [p0, p1) of its keys, sequence b's prefix length already clamped to its valid
+// range (err: SPEC_DEV_LENGTH if it was not).  Every thread of the workgroup
+// calls tile_item_run; it returns at points the whole workgroup reaches
+// together, or after its merge.  n_parts pieces of (b, g, rt) hold keys (one: the
+// output is written directly); otherwise this piece's partial goes to slot
+// pslot, arrivals are counted at counters[bgr], and the last piece to arrive
+// merges the partials of slots part_slot(0 .. n_parts - 1).  Every field is
+// wave-uniform.
+struct Piece {
+  int b, g, rt, p0, p1, n_parts;
+  long pslot, bgr;
+};
+
+template <int NRB>
+__device__ __forceinline__ void write_item(const TArgs2& a, int b, int chunk, TileLds<NRB>& L);
+
+template <int NRB, bool kFused, class PartSlot>
+__device__ __forceinline__ void tile_item_run(const TArgs2& a, const Piece& pc, int Lb, int err, TileLds<NRB>& L,
+                                              PartSlot part_slot) {
   constexpr int RT = 64 * NRB;  // rows per workgroup
   uint8_t* tiles = L.tiles;
   uint64_t* anc = L.anc;
@@ -439,20 +519,9 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int quad = lane >> 4;
-  const int rt = static_cast<int>(item % a.n_rt);
-  long rest = item / a.n_rt;
-  const int s = static_cast<int>(rest % a.splits);
-  rest /= a.splits;
-  const int g = static_cast<int>(rest % a.Hkv);
-  const int b = static_cast<int>(rest / a.Hkv);
-  const long bgr = (static_cast<long>(b) * a.Hkv + g) * a.n_rt + rt;
-
+  const int rt = pc.rt, g = pc.g, b = pc.b;
   const int n_keys = Lb + a.T;
-  const int npages = (n_keys + kBlockSize - 1) / kBlockSize;
-  const int n_used = (npages + a.pps - 1) / a.pps;  // splits of this (b, g) that hold keys
-  if (s >= n_used) return;
-  const int p0 = s * a.pps;
-  const int p1 = min(npages, p0 + a.pps);
+  const int p0 = pc.p0, p1 = pc.p1;
   const int kend = min(n_keys, p1 * kBlockSize);
   const int n_it = p1 > p0 ? (p1 - p0 + 3) / 4 : 0;
   const bool tail = n_it > 0 && kend > Lb;
@@ -546,9 +615,25 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
       vt_off[dt] = vkey * 256 + (((2 * dt + ((l16 & 3) >> 1)) ^ (2 * (vkey & 7))) * 16) + (l16 & 1) * 8;
   }
 
+  if (kFused && tail) {
+    // Sequence b's tree rows are written by the chunks' own workgroups first;
+    // a chunk nobody has claimed yet (its workgroup not started: the device
+    // holding other work) is written here instead, so the wait below always
+    // ends (the bound only guards the loop).  The tile buffers are still free.
+    if (tid == 0) L.s_next = written < static_cast<unsigned>(a.n_chunks) ? 1 : 0;
+    __syncthreads();
+    if (L.s_next) {
+      unsigned* claim = a.flags + a.B + static_cast<long>(b) * a.n_chunks;
+      for (int c = 0; c < a.n_chunks; ++c) {
+        __syncthreads();  // every wave has read s_last before it is rewritten
+        if (tid == 0)
+          L.s_last = __hip_atomic_exchange(claim + c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u ? 1 : 0;
+        __syncthreads();
+        if (L.s_last) write_item<NRB>(a, b, c, L);
+      }
+    }
+  }
   if (kFused && tail && tid == 0) {
-    // the write items of sequence b took earlier queue ids, so they are running
-    // or done whatever else the device holds; the bound only guards the loop
     for (unsigned spins = 0; written < static_cast<unsigned>(a.n_chunks); ++spins) {
       if (spins > kFlagSpinLimit) {
         err |= SPEC_DEV_TIMEOUT;
@@ -562,8 +647,7 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
   if (n_it > 0) issue_tile(0);
   if constexpr (kFused) {
     if (a.rotate) {
-      const int node1 = (min(a.R, (rt + 1) * RT) - 1) / a.G;  // the item's last node
-      rotate_queries<NRB>(a, Lb, node0, node1, row_base, l16, quad, s_par, tiles + kTileBytes, qf);
+      rotate_queries<NRB>(a, Lb, row_base, l16, quad, s_par, tiles + kTileBytes, qf);
     }
   }
   if (tail) {
@@ -688,7 +772,7 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
   for (int rb = 0; rb < NRB; ++rb) l_run[rb] = quad_sum(l_run[rb]);
   report(a.status, b, err);
 
-  const bool direct = (n_used == 1);
+  const bool direct = (pc.n_parts == 1);
   if (direct) {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -719,29 +803,28 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const int blk16 = wave * NRB + rb;
-    float* pb = a.part_o + (item * RT + blk16 * 16) * kD + lane;
+    float* pb = a.part_o + (pc.pslot * RT + blk16 * 16) * kD + lane;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) st_agent(pb + (dt * 4 + i) * 64, o[rb][dt][i]);
     if (quad == 0) {
-      st_agent(&a.part_ml[(item * RT + blk16 * 16 + l16) * 2 + 0], m_run[rb] * a.sl2);  // log2 units
-      st_agent(&a.part_ml[(item * RT + blk16 * 16 + l16) * 2 + 1], l_run[rb]);
+      st_agent(&a.part_ml[(pc.pslot * RT + blk16 * 16 + l16) * 2 + 0], m_run[rb] * a.sl2);  // log2 units
+      st_agent(&a.part_ml[(pc.pslot * RT + blk16 * 16 + l16) * 2 + 1], l_run[rb]);
     }
   }
   wait_vm0();  // this wave's partial stores have completed
   __syncthreads();
   if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(&a.counters[bgr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    L.s_last = (prev == static_cast<unsigned>(n_used - 1));
+    const unsigned prev = __hip_atomic_fetch_add(&a.counters[pc.bgr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    L.s_last = (prev == static_cast<unsigned>(pc.n_parts - 1));
   }
   __syncthreads();
   if (!L.s_last) return;
 
-  // The last workgroup of (b, g, rt) merges every split: wave w takes the 16-row
+  // The last workgroup of (b, g, rt) merges every piece: wave w takes the 16-row
   // blocks w, w+4, ..., each lane the elements it would hold in the accumulator
-  // layout, with the loads of four splits in flight at a time.
-  const long first = (bgr / a.n_rt) * a.splits * a.n_rt + rt;  // item of split 0
+  // layout, with the loads of KS pieces in flight at a time.
   constexpr int KS = NRB <= 2 ? 2 : 4;  // splits whose loads are in flight together
   for (int blk16 = wave; blk16 < RT / 16; blk16 += 4) {
     const int r = rt * RT + blk16 * 16 + l16;
@@ -749,7 +832,7 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
     float mstar = -INFINITY, lstar = 0.f, acc[32];
 #pragma unroll
     for (int e = 0; e < 32; ++e) acc[e] = 0.f;
-    for (int sp0 = 0; sp0 < n_used; sp0 += KS) {
+    for (int sp0 = 0; sp0 < pc.n_parts; sp0 += KS) {
       float ms[KS], ls[KS], x[KS][32];
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
@@ -757,8 +840,8 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
         ls[k] = 0.f;
 #pragma unroll
         for (int e = 0; e < 32; ++e) x[k][e] = 0.f;
-        if (sp0 + k < n_used) {
-          const long it2 = first + static_cast<long>(sp0 + k) * a.n_rt;
+        if (sp0 + k < pc.n_parts) {
+          const long it2 = part_slot(sp0 + k);
           ms[k] = ld_agent(&a.part_ml[(it2 * RT + blk16 * 16 + l16) * 2 + 0]);
           ls[k] = ld_agent(&a.part_ml[(it2 * RT + blk16 * 16 + l16) * 2 + 1]);
           const float* pb = a.part_o + (it2 * RT + blk16 * 16) * kD + lane;
@@ -792,72 +875,64 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const long item, 
       }
     }
   }
-  if (tid == 0) __hip_atomic_store(&a.counters[bgr], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&a.counters[pc.bgr], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Per-sequence quantities of the longest-first item order, lane b of every
-// wave holding sequence b (B <= 64): clamped prefix length, pages, splits that
-// hold keys, full splits over its kv heads, their running sum, the rank of its
-// last split (longer first, ties lower b), the prefix-length error bit.
-struct SeqTable {
-  int lb, np, nu, full, incl, rank, errlen;
-  int F, limit;  // full splits of the batch; ids that name an item
+// The stream-K split of a ragged batch (64-row tiles, one row tile per (b, g),
+// B <= 64).  Every (b, g) is laid end to end in (b, g) order as kSkItemUnits +
+// tiles units (tiles of 64 keys), so that the units measure time whatever the
+// mix of lengths; workgroup w takes units [u0(w), u0(w + 1)).  A (b, g) cut
+// between workgroups runs as pieces whose partials the last piece to arrive
+// merges.  With the fused K/V write, which spreads the n_write = q G + r write
+// chunks over the workgroups (about q + 1 on the first r), ranges are shorter
+// by kSkWriteUnits (W) per chunk: the first r workgroups take len1 = base -
+// W (q + 1) units, the others len2 = base - W q, base = ceil((U + n_write W) /
+// G).  Lane b of every wave holds sequence b.
+struct SkPlan {
+  int lb, np, tiles, errlen, incl;  // lane b: clamped prefix length, pages, tiles, error bit, running units
+  int U, r, len1, len2;             // all units; the ranges' two lengths
 };
 
-__device__ __forceinline__ SeqTable seq_table(const TArgs2& a) {
+__device__ __forceinline__ SkPlan sk_plan(const TArgs2& a, int n_write) {
   const int lane = threadIdx.x & 63;
-  SeqTable t;
+  SkPlan p;
   const bool in = lane < a.B;
   const int raw = in ? a.plen[lane] : 0;
   const int cap = a.max_blocks * kBlockSize - a.T;
-  t.errlen = (in && (raw < 0 || raw > cap)) ? SPEC_DEV_LENGTH : 0;
-  t.lb = raw < 0 ? 0 : (raw > cap ? cap : raw);
-  t.np = in ? (t.lb + a.T + kBlockSize - 1) / kBlockSize : 0;
-  t.nu = in ? (t.np + a.pps - 1) / a.pps : 0;
-  t.full = in ? (t.nu - 1) * a.Hkv : 0;
-  const int last = in ? t.np - (t.nu - 1) * a.pps : -1;
-  int incl = t.full;
+  p.errlen = (in && (raw < 0 || raw > cap)) ? SPEC_DEV_LENGTH : 0;
+  p.lb = raw < 0 ? 0 : (raw > cap ? cap : raw);
+  p.np = in ? (p.lb + a.T + kBlockSize - 1) / kBlockSize : 0;
+  p.tiles = (p.np + 3) / 4;
+  int incl = in ? a.Hkv * (kSkItemUnits + p.tiles) : 0;
 #pragma unroll
   for (int w = 1; w < 64; w <<= 1) {
     const int o = __shfl_up(incl, w);
     if (lane >= w) incl += o;
   }
-  t.incl = incl;
-  t.F = __shfl(incl, 63);
-  int rank = 0;
-  for (int o = 0; o < a.B; ++o) {  // lane o's value through a scalar register: no LDS round trip per step
-    const int lo = __builtin_amdgcn_readlane(last, o);
-    rank += (lo > last || (lo == last && o < lane)) ? 1 : 0;
+  p.incl = incl;
+  p.U = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+  const int G = static_cast<int>(gridDim.x);
+  const int q = n_write / G;
+  p.r = n_write % G;
+  int W = kSkWriteUnits;
+  int base = (p.U + n_write * W + G - 1) / G;
+  if (base - W * (q + 1) < 1) {  // (tiny batches: no allowance for the write)
+    W = 0;
+    base = (p.U + G - 1) / G;
   }
-  t.rank = rank;
-  t.limit = t.F + a.B * a.Hkv;
-  return t;
+  p.len1 = base - W * (q + 1);
+  p.len2 = base - W * q;
+  return p;
 }
 
-// Item of id v < t.limit in the longest-first order: every full split (pps
-// pages) of every (b, g) in sequence order, then each (b, g)'s last split by
-// decreasing length.  Returns the item and sets b's clamped prefix length and
-// error bit.
-__device__ __forceinline__ long seq_item(const TArgs2& a, const SeqTable& t, int v, int* Lb, int* err) {
-  const int lane = threadIdx.x & 63;
-  int b, g, s;
-  if (v < t.F) {
-    b = __ffsll(static_cast<long long>(__ballot(t.incl > v))) - 1;
-    const int k = v - (__shfl(t.incl, b) - __shfl(t.full, b));
-    const int ns = __shfl(t.nu, b) - 1;
-    g = k / ns;
-    s = k % ns;
-  } else {
-    const int j = v - t.F, rank = j / a.Hkv;
-    g = j % a.Hkv;
-    b = __ffsll(static_cast<long long>(__ballot(lane < a.B && t.rank == rank))) - 1;
-    s = __shfl(t.nu, b) - 1;
-  }
-  b = __builtin_amdgcn_readfirstlane(b);
-  *Lb = __builtin_amdgcn_readfirstlane(__shfl(t.lb, b));
-  *err = __builtin_amdgcn_readfirstlane(__shfl(t.errlen, b));
-  return (static_cast<long>(b) * a.Hkv + __builtin_amdgcn_readfirstlane(g)) * a.splits +
-         __builtin_amdgcn_readfirstlane(s);
+// First unit of workgroup w's range (clamped to U) and the workgroup whose range holds unit u < U.
+__device__ __forceinline__ int sk_u0(const SkPlan& p, int w) {
+  const int u = w <= p.r ? w * p.len1 : p.r * p.len1 + (w - p.r) * p.len2;
+  return min(u, p.U);
+}
+__device__ __forceinline__ int sk_w_of(const SkPlan& p, int u) {
+  const int k = p.r * p.len1;
+  return u < k ? u / p.len1 : p.r + (u - k) / p.len2;
 }
 
 // Write item (b, chunk) of the fused launch: rows chunk*C .. chunk*C + C - 1 (C =
@@ -952,97 +1027,121 @@ __device__ __forceinline__ void write_item(const TArgs2& a, int b, int chunk, Ti
   if (tid == 0) __hip_atomic_fetch_add(&a.flags[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// kFused: the launch also writes the tree's K/V rows (write items first in the
-// queue, then the longest-first attention items; 64-row tiles only).
+// kFused: the launch also writes the tree's K/V rows (stream-K split, 64-row
+// tiles only).
 template <int NRB, bool kFused>
 __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const TArgs2 a) {
   __shared__ TileLds<NRB> L;
   const int tid = threadIdx.x;
-  bool reorder = false;
-  if constexpr (NRB == 1) reorder = a.reorder != 0;  // (the 128-row kernel is at its register limit)
   static_assert(!kFused || NRB == 1, "the fused launch runs 64-row tiles");
-  if (kFused || (NRB == 1 && a.persist)) {
-    // Items from a queue: workgroup w starts with id w, then takes the next
-    // unclaimed one (an atomic counter in the workspace) until none is left, so
-    // that a CU -- or a whole XCD -- that runs faster takes more items (each XCD
-    // otherwise gets a fixed share of the workgroup ids, and the slowest sets
-    // the end).  Ids below n_write are write items (fused launch); the rest
-    // name attention items, longest first when `reorder`.  The next id is
-    // claimed while the current item runs.  The last workgroup to leave resets
-    // the queue and the write flags for the next call.
-    SeqTable t{};
-    if (reorder) t = seq_table(a);
-    const int n_attn = reorder ? t.limit : static_cast<int>(a.items);
-    const int total = a.n_write + n_attn;
-    unsigned* queue = a.counters + static_cast<long>(a.B) * a.Hkv * a.n_rt;  // [next id, workgroups done]
-    const int G = static_cast<int>(gridDim.x);
-    int v = static_cast<int>(blockIdx.x);
-    while (v < total) {
-      unsigned nxt = 0;
-      if (tid == 0) nxt = __hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (kFused && v < a.n_write) {
-        write_item<NRB>(a, v / a.n_chunks, v % a.n_chunks, L);
-      } else {
-        const int id = v - a.n_write;
-        int Lb, err = 0;
-        long item;
-        if (reorder) {
-          item = seq_item(a, t, id, &Lb, &err);
-        } else {
-          item = id;
-          Lb = a.plen[item / a.n_rt / a.splits / a.Hkv];
-          const int cap = a.max_blocks * kBlockSize - a.T;
-          if (Lb < 0 || Lb > cap) {
-            err |= SPEC_DEV_LENGTH;
-            Lb = Lb < 0 ? 0 : cap;
+  if constexpr (NRB == 1) {
+    if (kFused || a.streamk) {
+      // The stream-K split (see SkPlan): write chunks w, w + G, ... first, then
+      // the pieces of this workgroup's range of units, in (b, g) order.  Each
+      // chunk is claimed before it is written (a claim word a chunk), and a
+      // piece holding tree keys that finds its sequence's rows unwritten takes
+      // over the chunks nobody has claimed before it waits for the rest (see
+      // tile_item_run), so every wait ends whatever else the device holds.
+      const int n_write = kFused ? a.n_write : 0;
+      const SkPlan p = sk_plan(a, n_write);
+      const int G = static_cast<int>(gridDim.x), w = static_cast<int>(blockIdx.x);
+      if constexpr (kFused) {
+        unsigned* claim = a.flags + a.B;
+        for (int j = w; j < n_write; j += G) {
+          if (tid == 0)
+            L.s_next = __hip_atomic_exchange(claim + j, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u ? 1 : 0;
+          __syncthreads();
+          const bool mine = L.s_next != 0;
+          __syncthreads();  // every wave has read s_next before it is rewritten
+          if (mine) {
+            write_item<NRB>(a, j / a.n_chunks, j % a.n_chunks, L);
+            __syncthreads();  // the chunk's LDS is free again
           }
         }
-        tile_item_run<NRB, kFused>(a, item, Lb, err, L);
       }
-      if (tid == 0) L.s_next = G + static_cast<int>(nxt);
-      __syncthreads();  // every wave is done with the item's LDS; the next id is published
-      v = L.s_next;
-      __syncthreads();  // s_next is rewritten only after every wave has read it
-    }
-    if (tid == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(queue + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      L.s_last = (prev == static_cast<unsigned>(G - 1));  // every workgroup has claimed past the end
-    }
-    __syncthreads();
-    if (L.s_last) {
-      if constexpr (kFused)
-        for (int i = tid; i < a.B; i += 256)
-        __hip_atomic_store(&a.flags[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int lane = tid & 63;
+      int u = sk_u0(p, w);
+      const int u_end = sk_u0(p, w + 1);
+      while (u < u_end) {
+        // the (b, g) holding unit u: sequence b from the running sums, then its kv head
+        const int b = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<long long>(__ballot(lane < a.B && p.incl > u))) - 1);
+        const int incl_b = __builtin_amdgcn_readlane(p.incl, b);
+        const int tiles_b = __builtin_amdgcn_readlane(p.tiles, b);
+        const int per = kSkItemUnits + tiles_b;
+        const int start_b = incl_b - a.Hkv * per;
+        const int g = (u - start_b) / per;
+        const int s_bg = start_b + g * per;
+        const int f = s_bg + kSkItemUnits, e = f + tiles_b;  // the (b, g)'s tile units
+        const int t0 = max(u, f) - f, t1 = min(u_end, e) - f;
+        if (t1 > t0) {
+          Piece pc;
+          pc.b = b;
+          pc.g = g;
+          pc.rt = 0;
+          pc.p0 = 4 * t0;
+          pc.p1 = min(__builtin_amdgcn_readlane(p.np, b), 4 * t1);
+          const int w_first = sk_w_of(p, f);
+          pc.n_parts = sk_w_of(p, e - 1) - w_first + 1;
+          // two partial slots a workgroup: its first piece, its last one (the pieces between are whole (b, g))
+          pc.pslot = 2L * w + (sk_u0(p, w) >= s_bg ? 0 : 1);
+          pc.bgr = static_cast<long>(b) * a.Hkv + g;
+          tile_item_run<NRB, kFused>(a, pc, __builtin_amdgcn_readlane(p.lb, b), __builtin_amdgcn_readlane(p.errlen, b), L,
+                                     [&](int k) {
+                                       const int ww = w_first + k;
+                                       return 2L * ww + (sk_u0(p, ww) >= s_bg ? 0 : 1);
+                                     });
+          __syncthreads();  // every wave is done with the piece's LDS
+        }
+        u = e;
+      }
+      // the last workgroup to leave resets the write flags and claims for the next call
+      unsigned* done = a.counters + static_cast<long>(a.B) * a.Hkv * a.n_rt + 1;
       if (tid == 0) {
-        __hip_atomic_store(queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        L.s_last = (prev == static_cast<unsigned>(G - 1));
       }
-    }
-    return;
-  }
-  long item;
-  int Lb, err = 0;
-  if (reorder) {
-    // Ragged batch, one row tile, more items than resident workgroups: the
-    // longest items go first (workgroup ids taken in dispatch order), so the
-    // short ones fill the tail.
-    const SeqTable t = seq_table(a);
-    if (static_cast<int>(blockIdx.x) >= t.limit) return;
-    item = seq_item(a, t, static_cast<int>(blockIdx.x), &Lb, &err);
-  } else {
-    // Consecutive workgroup ids are dealt round-robin to the 8 XCDs; give each
-    // XCD a contiguous run of items so the row tiles of one KV chunk share an L2.
-    const long per = (a.items + 7) / 8;
-    item = static_cast<long>(blockIdx.x % 8) * per + blockIdx.x / 8;
-    if (item >= a.items) return;
-    Lb = a.plen[item / a.n_rt / a.splits / a.Hkv];
-    const int cap = a.max_blocks * kBlockSize - a.T;
-    if (Lb < 0 || Lb > cap) {
-      err |= SPEC_DEV_LENGTH;
-      Lb = Lb < 0 ? 0 : cap;
+      __syncthreads();
+      if (L.s_last) {
+        if constexpr (kFused)
+          for (int i = tid; i < a.B + n_write; i += 256)  // flags, then claim words
+            __hip_atomic_store(&a.flags[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return;
     }
   }
-  tile_item_run<NRB, kFused>(a, item, Lb, err, L);
+  // One item (b, g, KV split, row tile) a workgroup.  Consecutive workgroup ids
+  // are dealt round-robin to the 8 XCDs; give each XCD a contiguous run of items
+  // so the row tiles of one KV chunk share an L2.
+  const long per = (a.items + 7) / 8;
+  const long item = static_cast<long>(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (item >= a.items) return;
+  const int rt = static_cast<int>(item % a.n_rt);
+  long rest = item / a.n_rt;
+  const int s = static_cast<int>(rest % a.splits);
+  rest /= a.splits;
+  const int g = static_cast<int>(rest % a.Hkv);
+  const int b = static_cast<int>(rest / a.Hkv);
+  int Lb = a.plen[b], err = 0;
+  const int cap = a.max_blocks * kBlockSize - a.T;
+  if (Lb < 0 || Lb > cap) {
+    err |= SPEC_DEV_LENGTH;
+    Lb = Lb < 0 ? 0 : cap;
+  }
+  const int npages = (Lb + a.T + kBlockSize - 1) / kBlockSize;
+  const int n_used = (npages + a.pps - 1) / a.pps;  // splits of this (b, g) that hold keys
+  if (s >= n_used) return;
+  Piece pc;
+  pc.b = b;
+  pc.g = g;
+  pc.rt = rt;
+  pc.p0 = s * a.pps;
+  pc.p1 = min(npages, pc.p0 + a.pps);
+  pc.n_parts = n_used;
+  pc.pslot = item;
+  pc.bgr = (static_cast<long>(b) * a.Hkv + g) * a.n_rt + rt;
+  const long first = (static_cast<long>(b) * a.Hkv + g) * a.splits * a.n_rt + rt;  // item of split 0
+  tile_item_run<NRB, kFused>(a, pc, Lb, err, L, [&](int k) { return first + static_cast<long>(k) * a.n_rt; });
 }
 
 // Workgroups of attn_tile_kernel<NRB, kFused> the current device holds at once
@@ -1088,10 +1187,15 @@ static void plan_tile(AttnPlan& p, int B, int Hkv, int max_blocks) {
   // longest ones do not set the makespan alone
   splits = std::max<long>(splits, (max_blocks + 511) / 512);
   splits = std::min<long>(splits, std::max<long>(1, max_blocks / 16));
-  // a ragged batch with more items than resident workgroups is dispatched longest
-  // items first, and cut finer so that no item sets the makespan alone
-  p.reorder = (p.nrb == 1 && p.n_rt == 1 && B <= 64 && base * splits > 512) ? 1 : 0;  // 512: two per CU
-  if (p.reorder) splits = std::max<long>(splits, (max_blocks + SPEC_TILE_RAGGED_PPS - 1) / SPEC_TILE_RAGGED_PPS);
+  // a ragged batch with more items than resident workgroups (512: two per CU)
+  // takes the stream-K split, whose partials need two slots a resident
+  // workgroup: at least 1024 items' worth of workspace; its splits are then only
+  // the fallback's (no occupancy figure), cut so that no item sets the makespan alone
+  p.streamk = (p.nrb == 1 && p.n_rt == 1 && B <= 64 && base * splits > 512 && max_blocks <= kMaxPiecePages) ? 1 : 0;
+  if (p.streamk) {
+    splits = std::max<long>(splits, (max_blocks + SPEC_TILE_RAGGED_PPS - 1) / SPEC_TILE_RAGGED_PPS);
+    splits = std::max<long>(splits, (1024 + base - 1) / base);
+  }
   long pps = (max_blocks + splits - 1) / splits;
   pps = (pps + 3) / 4 * 4;
   pps = std::min<long>(pps, kMaxSplitPages);
@@ -1122,24 +1226,30 @@ AttnPlan plan_attn(int B, int T, int Hq, int Hkv, int D, int max_blocks, int dty
     return p;
   }
   plan_tile(p, B, Hkv, max_blocks);
-  const size_t head = (static_cast<size_t>(p.items / p.splits + 2) * sizeof(unsigned) + 255) / 256 * 256;  // + the item queue
+  const size_t head = (static_cast<size_t>(p.items / p.splits + 2) * sizeof(unsigned) + 255) / 256 * 256;  // + the exit counter
   p.ws_bytes = p.splits > 1 ? head + static_cast<size_t>(p.items) * p.rt * (kD + 2) * sizeof(float) : 0;
   return p;
 }
 
 // The tree's K/V write and the attention: one launch of the tile kernel where
-// its items come from the longest-first queue (64-row tiles over a ragged batch
-// with more items than resident workgroups), whose many items per workgroup
-// hide the write; there the workspace holds arrival counters, the queue, one
-// count of written chunks per sequence, then the split partials.  Any other
-// shape takes two launches, which measured faster there: the write (rotated
-// queries into the workspace), then the attention of spec_tree_attn.
+// its work is cut stream-K fashion (64-row tiles over a ragged batch with more
+// items than resident workgroups), the write chunks spread over the
+// workgroups; there the workspace holds arrival counters, [unused, workgroups
+// done], one count of written chunks per sequence, one claim word per chunk,
+// then the partials.  Any other shape takes two launches, which measured faster
+// there: the write (rotated queries into the workspace), then the attention of
+// spec_tree_attn.
+constexpr int kWriteChunkRows = 64;  // rows of a write chunk: few workgroups carry the write's latency
+static size_t fused_head_bytes(int B, int T, int Hkv, size_t arrivals) {
+  const size_t chunks = static_cast<size_t>(B) * ((2 * T * Hkv + kWriteChunkRows - 1) / kWriteChunkRows);
+  return ((arrivals + 2 + static_cast<size_t>(B) + chunks) * sizeof(unsigned) + 255) / 256 * 256;
+}
+
 AttnPlan plan_attn_write(int B, int T, int Hq, int Hkv, int max_blocks) {
   AttnPlan p = plan_attn(B, T, Hq, Hkv, kD, max_blocks, SPEC_BF16);
-  if (p.mode == 2 && p.nrb == 1 && p.reorder && p.splits > 1) {
+  if (p.mode == 2 && p.nrb == 1 && p.streamk && p.splits > 1) {
     p.fused = 1;
-    const size_t base = static_cast<size_t>(p.items / p.splits);
-    const size_t head = ((base + 2 + static_cast<size_t>(B)) * sizeof(unsigned) + 255) / 256 * 256;
+    const size_t head = fused_head_bytes(B, T, Hkv, static_cast<size_t>(p.items / p.splits));
     p.ws_bytes = head + static_cast<size_t>(p.items) * p.rt * (kD + 2) * sizeof(float);
     return p;
   }
@@ -1169,7 +1279,6 @@ static TArgs2 tile_args(const AttnPlan& plan, const AttnLaunch& L) {
   a.max_blocks = L.max_blocks;
   a.num_blocks = L.num_blocks;
   a.items = plan.items;
-  a.reorder = plan.reorder;
   // With one row tile per (b, g) each K/V page is read by one item; with several,
   // the row tiles of a KV chunk find it in L2 (streaming loads made the 16-tile
   // Sequoia-scale layer slower), so only the former load non-temporally.
@@ -1189,11 +1298,11 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& L, hipStream
     a.part_ml = a.part_o + static_cast<size_t>(plan.items) * plan.rt * kD;
   }
   if (plan.nrb == 1) {
-    if (plan.reorder && plan.splits > 1) {  // the queue of items: one round of resident workgroups
+    if (plan.streamk && plan.splits > 1) {  // the stream-K split over one round of resident workgroups
       const long cap = tile_capacity<1, false>();
       if (cap > 0) {
-        a.persist = 1;
-        const long grid = std::min<long>(cap, plan.items);
+        a.streamk = 1;
+        const long grid = std::min<long>(cap, plan.items / 2);  // two partial slots a workgroup
         hipLaunchKernelGGL((attn_tile_kernel<1, false>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
         return hipGetLastError();
       }
@@ -1237,7 +1346,7 @@ hipError_t launch_attn_write(const AttnPlan& plan, const AttnWriteLaunch& W, hip
   }
   TArgs2 a = tile_args(plan, L);
   const size_t base = static_cast<size_t>(L.B) * L.Hkv * plan.n_rt;
-  const size_t head = ((base + 2 + static_cast<size_t>(L.B)) * sizeof(unsigned) + 255) / 256 * 256;
+  const size_t head = fused_head_bytes(L.B, L.T, L.Hkv, base);
   a.counters = reinterpret_cast<unsigned*>(ws);
   a.flags = a.counters + base + 2;
   if (plan.splits > 1) {
@@ -1250,16 +1359,16 @@ hipError_t launch_attn_write(const AttnPlan& plan, const AttnWriteLaunch& W, hip
   a.vc = static_cast<uint16_t*>(const_cast<void*>(L.v));
   a.rotate = W.theta > 0.0f ? 1 : 0;
   a.log2_theta = W.theta > 0.0f ? std::log2(static_cast<double>(W.theta)) : 0.0;
-  a.persist = 1;
+  a.streamk = 1;
   const long cap = tile_capacity<1, true>();
   if (cap <= 0) return hipErrorInvalidDevice;
   // chunks of the write: 64 rows, so that few workgroups carry the write's
   // latency (smaller chunks on every workgroup measured slower)
-  a.chunk_rows = 64;
+  a.chunk_rows = kWriteChunkRows;
   a.n_chunks = (2 * L.T * L.Hkv + a.chunk_rows - 1) / a.chunk_rows;
   a.n_write = L.B * a.n_chunks;
-  // resident workgroups loop over the queue
-  const long grid = std::min<long>(cap, a.n_write + plan.items);
+  // one round of resident workgroups, two partial slots each
+  const long grid = std::min<long>(cap, plan.items / 2);
   hipLaunchKernelGGL((attn_tile_kernel<1, true>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

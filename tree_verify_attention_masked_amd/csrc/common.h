@@ -52,7 +52,7 @@ struct AttnPlan {
   int pps;        // pages per split
   long items;     // workgroups of the main kernel (before XCD padding)
   int depth;      // streaming kernel: page slots per wave
-  int reorder;    // tile kernel: longest items first (ragged batches with more items than resident workgroups)
+  int streamk;    // tile kernel: the stream-K split (ragged batches with more items than resident workgroups)
   int fused;      // spec_tree_write_attn: the write in the attention launch (else two launches)
   size_t ws_bytes;
 };
