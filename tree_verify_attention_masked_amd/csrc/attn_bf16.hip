@@ -1059,20 +1059,24 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
           }
         }
       }
+      // The range is taken from its end: its last piece is the head of a (b, g)
+      // (no tree keys) and its first the end of one (tree keys), so pieces that
+      // need the tree's rows come late, when the chunks are long written.
       const int lane = tid & 63;
-      int u = sk_u0(p, w);
-      const int u_end = sk_u0(p, w + 1);
-      while (u < u_end) {
-        // the (b, g) holding unit u: sequence b from the running sums, then its kv head
-        const int b = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<long long>(__ballot(lane < a.B && p.incl > u))) - 1);
+      const int u_begin = sk_u0(p, w);
+      int u = sk_u0(p, w + 1);  // units [u_begin, u) are still to do
+      while (u > u_begin) {
+        // the (b, g) holding unit u - 1: sequence b from the running sums, then its kv head
+        const int b =
+            __builtin_amdgcn_readfirstlane(__ffsll(static_cast<long long>(__ballot(lane < a.B && p.incl > u - 1))) - 1);
         const int incl_b = __builtin_amdgcn_readlane(p.incl, b);
         const int tiles_b = __builtin_amdgcn_readlane(p.tiles, b);
         const int per = kSkItemUnits + tiles_b;
         const int start_b = incl_b - a.Hkv * per;
-        const int g = (u - start_b) / per;
+        const int g = (u - 1 - start_b) / per;
         const int s_bg = start_b + g * per;
         const int f = s_bg + kSkItemUnits, e = f + tiles_b;  // the (b, g)'s tile units
-        const int t0 = max(u, f) - f, t1 = min(u_end, e) - f;
+        const int t0 = max(u_begin, f) - f, t1 = min(u, e) - f;
         if (t1 > t0) {
           Piece pc;
           pc.b = b;
@@ -1092,7 +1096,7 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
                                      });
           __syncthreads();  // every wave is done with the piece's LDS
         }
-        u = e;
+        u = s_bg;
       }
       // the last workgroup to leave resets the write flags and claims for the next call
       unsigned* done = a.counters + static_cast<long>(a.B) * a.Hkv * a.n_rt + 1;
