@@ -749,17 +749,6 @@ __device__ __forceinline__ void wave_sort_desc(float& v, double& w) {
   bitonic_step<64, 2, kPay>(v, w);
   bitonic_step<64, 1, kPay>(v, w);
 }
-// Inclusive max-scan over the 64 lanes (lane order).
-__device__ __forceinline__ int wave_incl_max_i(int v) {
-  v = max(v, dpp_i<kShr1, 0xF>(INT_MIN, v));
-  v = max(v, dpp_i<kShr2, 0xF>(INT_MIN, v));
-  v = max(v, dpp_i<kShr4, 0xF>(INT_MIN, v));
-  v = max(v, dpp_i<kShr8, 0xF>(INT_MIN, v));
-  v = max(v, dpp_i<kBcast15, 0xA>(INT_MIN, v));
-  v = max(v, dpp_i<kBcast31, 0xC>(INT_MIN, v));
-  return v;
-}
-
 // lanes below this one whose bit is set in m
 __device__ __forceinline__ int lanes_below(unsigned long long m) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
