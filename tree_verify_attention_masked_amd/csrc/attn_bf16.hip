@@ -58,13 +58,6 @@ constexpr int kSkItemUnits = 5;
 constexpr int kSkWriteUnits = 6;
 
 __device__ __forceinline__ void wait_vm0() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// A workgroup barrier for data exchanged through LDS only: this wave's LDS
-// accesses complete, then the barrier.  Unlike __syncthreads() (a workgroup
-// fence, which waits for every outstanding memory access), it leaves the
-// direct global->LDS loads of a tile in flight, so work between a tile's issue
-// and its use overlaps the tile's latency.  The LDS it publishes must not be
-// what those loads write.
-__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

@@ -33,6 +33,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// A workgroup barrier for data exchanged through LDS only: this wave's LDS
+// accesses complete, then the barrier.  Unlike __syncthreads() (a workgroup
+// fence, which waits for every outstanding memory access), it leaves direct
+// global->LDS loads in flight, so work between their issue and their use
+// overlaps their latency.  The LDS it publishes must not be what those loads
+// write.
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ void report(int32_t* status, int b, int32_t bits) {
   if (status != nullptr && bits != 0) atomicOr(status + b, bits);
 }
