@@ -122,6 +122,14 @@ __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// max(a, b) for operands that are not NaN, as one v_med3(a, b, pinf) with pinf
+// = +inf known only at run time (fmaxf quiets signalling NaNs first, one more
+// instruction per operand, and so does the med3 of a constant +inf, which the
+// compiler turns back into a max)
+__device__ __forceinline__ float max_nn(float a, float b, float pinf) { return __builtin_amdgcn_fmed3f(a, b, pinf); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kBf16Ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+
 // Max / sum over the four lanes l%16 + 16q of a row (VALU lane swaps, no LDS):
 // v_permlane16_swap of a value with a copy of itself leaves rows (0,1) and (2,3)
 // of the two registers exchanged, so combining them joins lanes l and l^16;
@@ -178,6 +186,7 @@ struct TArgs2 {
   int kv_stream;  // every K/V page is read by one item only: load it non-temporally
   long items;
   float sl2;
+  float pinf;  // +inf
   // The tree's K/V write in the same launch (stream-K split only): n_write
   // chunks, n_chunks per sequence (chunk_rows of its 2 T Hkv K and V rows
   // each), each claimed before it is written; attention pieces rotate their
@@ -732,19 +741,23 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const Piece& pc, 
 #pragma unroll
           for (int j = 0; j < 8; ++j) sv[j] = ((vis[rb] >> ((j >> 2) * 16 + (j & 3))) & 1u) ? sv[j] : -INFINITY;
         }
-        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        const float pi = a.pinf;
+        float mx = max_nn(max_nn(max_nn(sv[0], sv[1], pi), max_nn(sv[2], sv[3], pi), pi),
+                          max_nn(max_nn(sv[4], sv[5], pi), max_nn(sv[6], sv[7], pi), pi), pi);
         mx = quad_max(mx);
-        const float m_new = fmaxf(m_run[rb], mx);
+        const float m_new = max_nn(m_run[rb], mx, pi);
         const bool none = (m_new == -INFINITY);
-        const float msl = -m_new * a.sl2;
+        // A row with no visible key so far (m = -inf, every score -inf) takes
+        // its exponents against 0, so that each p is exp2(-inf) = 0.
+        const float msl = none ? 0.f : -m_new * a.sl2;
         bf16x8 pf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pf[j] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[j], a.sl2, msl)));
+        // the row sum adds the bf16 weights the PV product uses, two per v_dot2
         float psum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pj = none ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sv[j], a.sl2, msl));
-          psum += pj;
-          pf[j] = static_cast<__bf16>(pj);
-        }
+        for (int j = 0; j < 8; j += 2)
+          psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[j], pf[j + 1]}, kBf16Ones, psum, false);
         if (!__all(m_new == m_run[rb])) {  // the running max moved somewhere in the wave: rescale
           const float alpha = none ? 1.f : __builtin_amdgcn_exp2f((m_run[rb] - m_new) * a.sl2);
           l_run[rb] *= alpha;
@@ -1281,6 +1294,7 @@ static TArgs2 tile_args(const AttnPlan& plan, const AttnLaunch& L) {
   // Sequoia-scale layer slower), so only the former load non-temporally.
   a.kv_stream = plan.n_rt == 1;
   a.sl2 = L.scale * kLog2e;
+  a.pinf = INFINITY;
   return a;
 }
 
