@@ -23,6 +23,9 @@
  *     so a caller can chain draft and verify steps without a CPU round trip.
  *   - Shapes and pointers are checked on the host before anything is launched;
  *     a failed check returns a negative spec_status and launches nothing.
+ *     Queries, keys, values (new rows and caches) and attention outputs must
+ *     start on a 16-byte boundary (they move with 16-byte accesses); a pointer
+ *     that does not is SPEC_ERR_INVALID_ARG.
  *   - Device contents that the host cannot see without a copy (the parent
  *     array, block-table entries, prefix lengths, draft tokens, NaN logits,
  *     accepted paths) are checked by the kernels.  A kernel that finds a bad

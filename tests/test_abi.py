@@ -50,6 +50,8 @@ def _attn(lib, **kw):
     ptrs = [FAKE] * 7
     if kw.get("null_q"):
         ptrs[0] = None
+    if kw.get("misaligned"):
+        ptrs[0] = ctypes.c_void_p(0x1008)
     return lib.spec_tree_attn(*ptrs, a["B"], a["T"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["mb"], a["nb"],
                               a["scale"], a["dtype"], None, a["ws"], a["wsz"], None)
 
@@ -67,6 +69,7 @@ def test_attn_host_validation(lib):
     assert _attn(lib, scale=float("nan")) == -1
     assert _attn(lib, dtype=5) == -1
     assert _attn(lib, B=0) == 0  # empty batch: nothing to do
+    assert _attn(lib, misaligned=True) == -1  # rows move with 16-byte accesses
     # a split-KV plan without workspace
     assert _attn(lib, T=5, Hq=40, Hkv=40, mb=129, nb=129) == -3
 
@@ -142,6 +145,8 @@ def test_kv_write_host_validation(lib):
     assert call(T=100, mb=4) == -1     # the table cannot hold the tree
     assert call(B=0) == 0
     assert call(B=0, q=None, Hq=0) == 0  # no queries to rotate
+    assert call(k=ctypes.c_void_p(0x1002)) == -1  # rows move with 16-byte accesses
+    assert call(q=ctypes.c_void_p(0x1008)) == -1
 
 def test_binding_refuses_cpu_tensors():
     import torch

@@ -17,6 +17,9 @@ bool dtype_ok(int dtype, int D) {
   return false;
 }
 
+// Rows of queries, keys, values and outputs move with 16-byte vector accesses.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 // Shape checks shared by attention and compaction.  Returns SPEC_OK or an error.
 int check_kv_shapes(int B, int T, int Hkv, int D, int block_size, int max_blocks, int num_blocks, int dtype) {
   if (B < 0 || T < 1 || Hkv < 1 || D < 1 || max_blocks < 1 || num_blocks < 1) return SPEC_ERR_INVALID_ARG;
@@ -66,6 +69,7 @@ int spec_tree_attn(const void* q, const void* k_cache, const void* v_cache, cons
   if (!std::isfinite(scale)) return SPEC_ERR_INVALID_ARG;
   if (B == 0) return SPEC_OK;
   if (!q || !k_cache || !v_cache || !block_table || !prefix_lens || !parent || !out) return SPEC_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return SPEC_ERR_INVALID_ARG;
   const AttnPlan plan = plan_attn(B, T, Hq, Hkv, D, max_blocks_per_seq, dtype);
   if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes)) return SPEC_ERR_WORKSPACE;
   AttnLaunch L{};
@@ -307,6 +311,8 @@ int spec_tree_kv_write(const void* k_new, const void* v_new, void* q, void* k_ca
   if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !prefix_lens || !parent) {
     return SPEC_ERR_INVALID_ARG;
   }
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return SPEC_ERR_INVALID_ARG;
   KvWriteLaunch L{};
   L.k_new = k_new;
   L.v_new = v_new;
@@ -349,6 +355,9 @@ int spec_tree_write_attn(const void* k_new, const void* v_new, const void* q, vo
   if (!std::isfinite(scale) || !(rope_theta >= 0.0f) || std::isinf(rope_theta)) return SPEC_ERR_INVALID_ARG;
   if (B == 0) return SPEC_OK;
   if (!k_new || !v_new || !q || !k_cache || !v_cache || !block_table || !prefix_lens || !parent || !out)
+    return SPEC_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(out))
     return SPEC_ERR_INVALID_ARG;
   const AttnPlan plan = plan_attn_write(B, T, Hq, Hkv, max_blocks_per_seq);
   if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return SPEC_ERR_WORKSPACE;
