@@ -104,7 +104,7 @@ int spec_version(void);
  *   prefix_lens  [B] int32, >= 0
  *   parent       [B, T] int32
  *   out          [B, T, Hq, D] dtype (written)
- *   scale        softmax scale (callers normally pass 1/sqrt(D))
+ *   scale        softmax scale, finite and > 0 (callers normally pass 1/sqrt(D))
  *   status       [B] int32 or NULL; on a device-detected error the rows of the
  *                affected sequence are still written, from the subset of keys
  *                that could be read safely

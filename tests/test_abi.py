@@ -67,6 +67,8 @@ def test_attn_host_validation(lib):
     assert _attn(lib, mb=0) == -1
     assert _attn(lib, T=200, mb=8) == -1  # the table cannot even hold the tree
     assert _attn(lib, scale=float("nan")) == -1
+    assert _attn(lib, scale=0.0) == -1
+    assert _attn(lib, scale=-0.1) == -1
     assert _attn(lib, dtype=5) == -1
     assert _attn(lib, B=0) == 0  # empty batch: nothing to do
     assert _attn(lib, misaligned=True) == -1  # rows move with 16-byte accesses

@@ -66,7 +66,7 @@ int spec_tree_attn(const void* q, const void* k_cache, const void* v_cache, cons
   int rc = check_kv_shapes(B, T, Hkv, D, block_size, max_blocks_per_seq, num_blocks, dtype);
   if (rc != SPEC_OK) return rc;
   if (Hq < Hkv || Hq % Hkv != 0) return SPEC_ERR_INVALID_ARG;
-  if (!std::isfinite(scale)) return SPEC_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return SPEC_ERR_INVALID_ARG;  // the kernels track the largest score
   if (B == 0) return SPEC_OK;
   if (!q || !k_cache || !v_cache || !block_table || !prefix_lens || !parent || !out) return SPEC_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return SPEC_ERR_INVALID_ARG;
@@ -352,7 +352,8 @@ int spec_tree_write_attn(const void* k_new, const void* v_new, const void* q, vo
   if (rc != SPEC_OK) return rc;
   if (dtype != SPEC_BF16) return SPEC_ERR_UNSUPPORTED;
   if (Hq < Hkv || Hq % Hkv != 0) return SPEC_ERR_INVALID_ARG;
-  if (!std::isfinite(scale) || !(rope_theta >= 0.0f) || std::isinf(rope_theta)) return SPEC_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f) || !(rope_theta >= 0.0f) || std::isinf(rope_theta))
+    return SPEC_ERR_INVALID_ARG;
   if (B == 0) return SPEC_OK;
   if (!k_new || !v_new || !q || !k_cache || !v_cache || !block_table || !prefix_lens || !parent || !out)
     return SPEC_ERR_INVALID_ARG;

@@ -128,6 +128,7 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 // compiler turns back into a max)
 __device__ __forceinline__ float max_nn(float a, float b, float pinf) { return __builtin_amdgcn_fmed3f(a, b, pinf); }
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr float kLazyLog2 = 8.f;  // how far (log2 units) a row's max may pass the reference max
 constexpr bf16x2 kBf16Ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
 // Max / sum over the four lanes l%16 + 16q of a row (VALU lane swaps, no LDS):
@@ -577,6 +578,7 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const Piece& pc, 
   load_q();
   float m_run[NRB], l_run[NRB];
   f32x4 o[NRB][8];
+  const float lazy = kLazyLog2 / a.sl2;  // scale > 0
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     m_run[rb] = -INFINITY;
@@ -745,11 +747,21 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const Piece& pc, 
         float mx = max_nn(max_nn(max_nn(sv[0], sv[1], pi), max_nn(sv[2], sv[3], pi), pi),
                           max_nn(max_nn(sv[4], sv[5], pi), max_nn(sv[6], sv[7], pi), pi), pi);
         mx = quad_max(mx);
-        const float m_new = max_nn(m_run[rb], mx, pi);
-        const bool none = (m_new == -INFINITY);
+        // The reference max m_run moves only when a row's max passes it by more
+        // than lazy (kLazyLog2 in the exponent), so each p stays below
+        // 2^kLazyLog2 and the accumulators are rescaled rarely: once the first
+        // keys have set it, typically never again.
+        if (!__all(mx <= m_run[rb] + lazy)) {
+          const float m_new = max_nn(m_run[rb], mx, pi);
+          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run[rb] - m_new) * a.sl2);
+          l_run[rb] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) o[rb][dt] *= alpha;
+          m_run[rb] = m_new;
+        }
         // A row with no visible key so far (m = -inf, every score -inf) takes
         // its exponents against 0, so that each p is exp2(-inf) = 0.
-        const float msl = none ? 0.f : -m_new * a.sl2;
+        const float msl = m_run[rb] == -INFINITY ? 0.f : -m_run[rb] * a.sl2;
         bf16x8 pf;
 #pragma unroll
         for (int j = 0; j < 8; ++j) pf[j] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[j], a.sl2, msl)));
@@ -758,14 +770,7 @@ __device__ __forceinline__ void tile_item_run(const TArgs2& a, const Piece& pc, 
 #pragma unroll
         for (int j = 0; j < 8; j += 2)
           psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[j], pf[j + 1]}, kBf16Ones, psum, false);
-        if (!__all(m_new == m_run[rb])) {  // the running max moved somewhere in the wave: rescale
-          const float alpha = none ? 1.f : __builtin_amdgcn_exp2f((m_run[rb] - m_new) * a.sl2);
-          l_run[rb] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) o[rb][dt] *= alpha;
-        }
         l_run[rb] += psum;
-        m_run[rb] = m_new;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
           const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{vA[dt][0], vA[dt][1], vB[dt][0], vB[dt][1]});
