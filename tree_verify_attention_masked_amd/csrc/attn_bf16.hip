@@ -128,6 +128,7 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 // compiler turns back into a max)
 __device__ __forceinline__ float max_nn(float a, float b, float pinf) { return __builtin_amdgcn_fmed3f(a, b, pinf); }
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr long kWFirst = 12;  // pages of a first-round split, in eighths of a second-round one's
 constexpr float kLazyLog2 = 8.f;  // how far (log2 units) a row's max may pass the reference max
 constexpr bf16x2 kBf16Ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
@@ -187,7 +188,8 @@ struct TArgs2 {
   int kv_stream;  // every K/V page is read by one item only: load it non-temporally
   long items;
   float sl2;
-  float pinf;  // +inf
+  float pinf;   // +inf
+  int n_first;  // workgroups of the first dispatch round when the grid is two rounds of one a CU, else 0
   // The tree's K/V write in the same launch (stream-K split only): n_write
   // chunks, n_chunks per sequence (chunk_rows of its 2 T Hkv K and V rows
   // each), each claimed before it is written; attention pieces rotate their
@@ -1144,18 +1146,45 @@ __global__ __launch_bounds__(256, NRB <= 2 ? 2 : 1) void attn_tile_kernel(const 
     Lb = Lb < 0 ? 0 : cap;
   }
   const int npages = (Lb + a.T + kBlockSize - 1) / kBlockSize;
-  const int n_used = (npages + a.pps - 1) / a.pps;  // splits of this (b, g) that hold keys
+  const long first = (static_cast<long>(b) * a.Hkv + g) * a.splits * a.n_rt + rt;  // item of split 0
+  int n_used = (npages + a.pps - 1) / a.pps;  // splits of this (b, g) that hold keys
+  int p0 = s * a.pps, p1 = min(npages, p0 + a.pps);
+  if (a.n_first > 0 && npages >= 16 * a.splits) {
+    // The grid is two rounds of one workgroup a CU.  A CU's first workgroup
+    // runs ahead of the one dispatched onto it second (its older waves win the
+    // SIMD arbiter), so the splits of first-round workgroups get kWFirst/8 the
+    // pages of the others.  Integer weights, so every workgroup of the
+    // (b, g, rt) finds the same boundaries, rounded down to whole 64-key tiles
+    // (a partial tile costs a whole one); each split spans at least
+    // npages / (2 splits) >= 8 pages before rounding, so none is empty.
+    // When all of them fall in one round the equal splits stay.
+    long before = 0, total = 0, mine = 0;
+    int n_early = 0;
+    for (int k = 0; k < a.splits; ++k) {
+      const long it = first + static_cast<long>(k) * a.n_rt;
+      const long wg = (it % per) * 8 + it / per;  // the workgroup that runs item it
+      const long w = wg < a.n_first ? kWFirst : 8;
+      n_early += wg < a.n_first ? 1 : 0;
+      if (k < s) before += w;
+      if (k == s) mine = w;
+      total += w;
+    }
+    if (n_early > 0 && n_early < a.splits) {
+      p0 = static_cast<int>(npages * before / total) & ~3;
+      p1 = s == a.splits - 1 ? npages : static_cast<int>(npages * (before + mine) / total) & ~3;
+      n_used = a.splits;
+    }
+  }
   if (s >= n_used) return;
   Piece pc;
   pc.b = b;
   pc.g = g;
   pc.rt = rt;
-  pc.p0 = s * a.pps;
-  pc.p1 = min(npages, pc.p0 + a.pps);
+  pc.p0 = p0;
+  pc.p1 = p1;
   pc.n_parts = n_used;
   pc.pslot = item;
   pc.bgr = (static_cast<long>(b) * a.Hkv + g) * a.n_rt + rt;
-  const long first = (static_cast<long>(b) * a.Hkv + g) * a.splits * a.n_rt + rt;  // item of split 0
   tile_item_run<NRB, kFused>(a, pc, Lb, err, L, [&](int k) { return first + static_cast<long>(k) * a.n_rt; });
 }
 
@@ -1177,8 +1206,33 @@ long tile_capacity() {
 }
 
 template <int NRB>
-hipError_t run_tile(const TArgs2& args, hipStream_t stream) {
+hipError_t run_tile(const TArgs2& args_in, hipStream_t stream) {
+  TArgs2 args = args_in;
   const long grid = ((args.items + 7) / 8) * 8;
+  // Weighted splits (see the kernel) when the grid is two rounds of one
+  // workgroup a CU and the longest weighted split still fits the block-index
+  // buffer (a weighted split holds at most kWFirst/8 of pps pages).
+  int dev = 0, cus = 0;
+  const long cap = tile_capacity<NRB, false>();
+  const long max_pages = sizeof(TileLds<NRB>::s_blk) / sizeof(int);
+  args.n_first = 0;
+  if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                              hipSuccess &&
+      cap == 2L * cus && grid > cus && grid <= cap && static_cast<long>(args.pps) * kWFirst <= 8 * max_pages) {
+    // only where some (b, g, rt) has splits in both rounds (the kernel's own test)
+    const long per = (args.items + 7) / 8, n_bgr = static_cast<long>(args.B) * args.Hkv * args.n_rt;
+    bool mixed = false;
+    for (long bgr = 0; bgr < n_bgr && !mixed; ++bgr) {
+      const long first = (bgr / args.n_rt) * args.splits * args.n_rt + bgr % args.n_rt;
+      int n_early = 0;
+      for (int k = 0; k < args.splits; ++k) {
+        const long it = first + static_cast<long>(k) * args.n_rt;
+        n_early += (it % per) * 8 + it / per < cus ? 1 : 0;
+      }
+      mixed = n_early > 0 && n_early < args.splits;
+    }
+    if (mixed) args.n_first = cus;
+  }
   hipLaunchKernelGGL((attn_tile_kernel<NRB, false>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, args);
   return hipGetLastError();
 }
