@@ -53,6 +53,14 @@ SMALL = [
                                         gamma=95)),
     ("rows256_tree_short_prefix", dict(B=1, Hq=16, Hkv=1, D=128, dtype="bf16", prefix=[5], tree="random", T=64,
                                        max_depth=6)),
+    # the Sequoia-scale layer's launch shape (512 items, two rounds of one
+    # workgroup a CU, splits of each row tile in both rounds, so first-round
+    # splits are weighted) with prefixes long enough for weighted boundaries
+    # (1500, 8 waves of tiles) and too short for them (300: equal splits)
+    ("rows2048_weighted_splits", dict(B=1, Hq=64, Hkv=8, D=128, dtype="bf16", prefix=[1500], tree="random", T=256,
+                                      max_depth=10)),
+    ("rows2048_short_prefix", dict(B=1, Hq=64, Hkv=8, D=128, dtype="bf16", prefix=[300], tree="random", T=256,
+                                   max_depth=10)),
     # routing boundaries: 17 rows (the first tile-kernel shape), 64 rows over a
     # ragged batch whose sequences need 1..3 splits (later splits exit at once),
     # 65 rows (a second 128-row tile that is almost empty)
