@@ -16,6 +16,7 @@ import torch
 import oracle
 from helpers import DevWorkload, assert_attn_close, attn_to_f64, oracle_attn
 from workloads import make_config, make_workload
+from workloads.gen import bf16_bits_to_f32, f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -100,6 +101,24 @@ SMALL = [
 def test_small_cases(name, kw):
     w = make_workload(name=name, tag=400 + SMALL.index((name, kw)), V=8, **kw)
     print(f"[attn] {name} B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} lens={w.prefix_lens.tolist()}", flush=True)
+    _run_full(w)
+
+
+@pytest.mark.parametrize("Hq,T", [(16, 40), (8, 8)], ids=["rows320", "rows64"])
+def test_rising_scores_move_the_reference_max(Hq, T):
+    # Keys scaled up by 1 .. 9 along each sequence, so every row's largest score
+    # keeps growing: the tile kernels' reference max (which moves only when a
+    # row's max passes it by more than 2^8 in the exponent) moves many times,
+    # each move rescaling what was accumulated against the old one.
+    w = make_workload(name="rising", tag=470 + Hq, B=2, Hq=Hq, Hkv=2, D=128, dtype="bf16", V=8,
+                      prefix=[3000, 900], tree="random", T=T, max_depth=5, shuffle_blocks=True)
+    k = bf16_bits_to_f32(w.k_cache)
+    for b in range(w.B):
+        n = int(w.prefix_lens[b]) + w.T
+        for t in range(n):
+            k[w.block_table[b][t // 16], :, t % 16, :] *= 1.0 + 8.0 * t / n
+    w.k_cache = f32_to_bf16_bits(k)
+    print(f"[attn] rising scores B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} lens={w.prefix_lens.tolist()}", flush=True)
     _run_full(w)
 
 
