@@ -332,17 +332,22 @@ int spec_tree_kv_write(const void* k_new, const void* v_new, void* q, void* k_ca
  * vLLM") fused with the tree attention over the prefix and the tree.
  *
  * Writes the same cache rows, bit for bit, as spec_tree_kv_write, and the same
- * `out`, bit for bit, as spec_tree_attn called after it on the queries it
- * rotated.  The caller's `q` is not modified.  On a ragged batch of up to 64
- * sequences with at most 64 query rows per kv head and more work items than
- * the device holds at once (batched serving), the write runs inside the
- * attention launch: its first work items write the tree's K/V rows of one
- * sequence 64 rows at a time and count them, the attention items rotate their
- * own queries, and an item that reads the tree's keys starts once its
- * sequence's rows are all written (work items are claimed from a counter in
- * the workspace, writers first, so this wait always ends).  Every other shape
- * takes two launches, which measured faster there: the write, with the
- * rotated queries going to the workspace, then the attention.
+ * `out` as spec_tree_attn called after it on the queries it rotated (bit for
+ * bit except on the batched launch below, whose KV splits fall elsewhere, so
+ * its outputs differ by the bf16 rounding of the probabilities).  The
+ * caller's `q` is not modified.  With at most 16 query rows per kv head (the
+ * streaming kernel) it is one launch: every work item rotates its own queries,
+ * and an item whose KV range holds tree keys first writes its kv head's T key
+ * and value rows.  On a ragged batch of up to 64 sequences with at most 64
+ * query rows per kv head and more work items than the device holds at once
+ * (batched serving), the write also runs inside the attention launch: its
+ * first work items write the tree's K/V rows of one sequence 64 rows at a
+ * time and count them, the attention items rotate their own queries, and an
+ * item that reads the tree's keys starts once its sequence's rows are all
+ * written (work items are claimed from a counter in the workspace, writers
+ * first, so this wait always ends).  Every other shape takes two launches,
+ * which measured faster there: the write, with the rotated queries going to
+ * the workspace, then the attention.
  *
  *   k_new, v_new [B, T, Hkv, D] bf16: the nodes' keys (before rotation) and values
  *   q            [B, T, Hq, D] bf16: the queries before rotation (read only)
@@ -352,7 +357,8 @@ int spec_tree_kv_write(const void* k_new, const void* v_new, void* q, void* k_ca
  *   rope_theta   >= 0 and finite; 0 writes and uses the rows unrotated
  *   workspace    >= spec_tree_write_attn_workspace_size(...) bytes, never
  *                NULL (the work counter, B counts of written rows and the
- *                split partials, or the rotated queries and spec_tree_attn's
+ *                split partials; spec_tree_attn's workspace on the streaming
+ *                launch; or the rotated queries and spec_tree_attn's
  *                workspace), zero-filled before the first call;
  *                each completed call leaves its counters zero, so a workspace
  *                serves later calls of the same shape as it is (re-zero it

@@ -51,6 +51,12 @@ CASES = [
     ("deep_chain_direct_angles", dict(B=1, Hq=2, Hkv=1, prefix=[100], tree="chain", gamma=63), 10000.0, None),
     ("chain_rows5", dict(B=1, Hq=40, Hkv=40, prefix=[300], tree="chain", gamma=4), 10000.0, None),
     ("unrotated", dict(B=2, Hq=4, Hkv=2, prefix=[16, 31], tree="random", T=9, max_depth=3), 0.0, None),
+    # the streaming kernel's launch (at most 16 rows per kv head), which rotates
+    # its own queries and whose items holding tree keys write them: a tree that
+    # straddles two pages over several KV splits, and an unrotated ragged batch
+    ("stream_tail_straddles", dict(B=2, Hq=8, Hkv=8, prefix=[1918, 5000], tree="chain", gamma=4,
+                                   shuffle_blocks=True), 10000.0, None),
+    ("stream_unrotated", dict(B=3, Hq=8, Hkv=4, prefix=[0, 15, 333], tree="random", T=8, max_depth=3), 0.0, None),
 ]
 
 
@@ -178,6 +184,7 @@ BAD_PARENT = [
     ("two_launches", dict(B=3, Hq=8, Hkv=2, prefix=[40, 200, 7], tree="random", T=12, max_depth=4)),
     ("one_launch", dict(B=64, Hq=32, Hkv=8, prefix=[9000, 200] + [16 + (37 * i) % 600 for i in range(62)],
                         tree="random", T=16, max_depth=5, shuffle_blocks=True)),
+    ("stream_launch", dict(B=3, Hq=4, Hkv=4, prefix=[40, 200, 7], tree="random", T=6, max_depth=3)),
 ]
 
 

@@ -1322,6 +1322,10 @@ AttnPlan plan_attn_write(int B, int T, int Hq, int Hkv, int max_blocks) {
     p.ws_bytes = head + static_cast<size_t>(p.items) * p.rt * (kD + 2) * sizeof(float);
     return p;
   }
+  if (p.mode == 3 && T <= 16) {  // the streaming kernel writes and rotates in its own launch
+    p.fused = 1;
+    return p;
+  }
   p.ws_bytes += (static_cast<size_t>(B) * T * Hq * kD * sizeof(uint16_t) + 255) / 256 * 256;
   return p;
 }
@@ -1385,6 +1389,7 @@ hipError_t launch_attn_bf16(const AttnPlan& plan, const AttnLaunch& L, hipStream
 hipError_t launch_attn_write(const AttnPlan& plan, const AttnWriteLaunch& W, hipStream_t stream) {
   const AttnLaunch& L = W.attn;
   char* ws = static_cast<char*>(L.workspace);
+  if (plan.fused && plan.mode == 3) return launch_attn_stream_write(plan, W, stream);
   if (!plan.fused) {  // two launches: the write (queries rotated into the workspace), the attention
     const size_t qbytes = (static_cast<size_t>(L.B) * L.T * L.Hq * kD * sizeof(uint16_t) + 255) / 256 * 256;
     KvWriteLaunch K{};

@@ -26,6 +26,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "rope_dev.h"
 
 namespace spectree {
 namespace {
@@ -55,6 +56,15 @@ struct StArgs {
   int reorder;  // order items full splits first (B <= 64, more items than resident workgroups)
   long items;
   float sl2;
+  // The tree's K/V write in the same launch (kFused): every item rotates its own
+  // queries (q holds them before rotation), and each item whose range holds
+  // tree keys first writes its kv head's T key and value rows into the cache.
+  const uint16_t* k_new;  // [B,T,Hkv,D] the nodes' keys before rotation
+  const uint16_t* v_new;  // [B,T,Hkv,D] their values
+  uint16_t* kc;           // = k, = v: the cache the write fills
+  uint16_t* vc;
+  int rotate;             // rope_theta > 0
+  double log2_theta;
 };
 
 // Waits until at most n of this wave's vector-memory operations are in flight.
@@ -127,7 +137,7 @@ __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int NRB, int DEPTH>
+template <int NRB, int DEPTH, bool kFused>
 __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[4 * DEPTH * kSlotBytes];
   __shared__ int s_last;
@@ -234,7 +244,8 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
   // whose root has a parent) leaves its nodes with only themselves.
   uint64_t anc_row[NRB];
   const bool tail = kend > Lb;
-  if (tail) {
+  int dep = 0;  // (fused) depth of node `lane`
+  if (tail || kFused) {
     const bool in = lane < a.T;
     const bool valid = in && (lane == 0 ? par == -1 : (par >= 0 && par < lane));
     int j = (lane == 0 || !valid) ? lane : par;
@@ -248,6 +259,7 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
     }
     if (__any(in && !okc)) err |= SPEC_DEV_PARENT;
     if (!okc) A = 1ull << lane;
+    dep = __popcll(A) - 1;  // ancestors-or-self, less the node itself
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) anc_row[rb] = __shfl(A, node_of[rb]);
   } else {
@@ -292,6 +304,65 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
       __builtin_amdgcn_global_load_lds(vs, slot + kPageBytes + t * 1024, 16, 0, kLoadNT);
     }
   };
+
+  if constexpr (kFused) {
+    // Before the ring is filled: the cosines and sines of every node's pairs
+    // into it ([T][64] double2, T <= 16 here), the item's queries rotated in
+    // registers, and -- on an item whose range holds tree keys -- kv head g's T
+    // key (rotated) and value rows written into the cache at slots Lb + i,
+    // nothing for a bad parent row or prefix length (as spec_tree_kv_write).
+    // The same helpers as spec_tree_kv_write, so the stored bits are the same.
+    double2* trig = reinterpret_cast<double2*>(ring);
+    if (a.rotate) {
+      for (int nd = wave; nd < a.T; nd += 4) {
+        const int d = __shfl(dep, nd);
+        double c, sn;
+        rope_cos_sin(Lb + d, lane, kD, a.log2_theta, &c, &sn);
+        trig[nd * 64 + lane] = double2{c, sn};
+      }
+      __syncthreads();
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const double2* tn = trig + node_of[rb] * 64 + quad * 8;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const double2 cs = tn[c * 32 + e];
+            float y0, y1;
+            rope_turn(static_cast<float>(qf[rb][c][e]), static_cast<float>(qf[rb][c + 2][e]), cs.x, cs.y, &y0, &y1);
+            qf[rb][c][e] = __builtin_bit_cast(__bf16, f32_to_bf16(y0));
+            qf[rb][c + 2][e] = __builtin_bit_cast(__bf16, f32_to_bf16(y1));
+          }
+      }
+    }
+    if (tail && !(err & (SPEC_DEV_PARENT | SPEC_DEV_LENGTH))) {
+      for (int row = wave; row < 2 * a.T; row += 4) {  // row 2i: node i's key, 2i + 1: its value
+        const int i = row >> 1;
+        const bool isv = (row & 1) != 0;
+        const uint16_t* src = (isv ? a.v_new : a.k_new) + ((static_cast<long>(b) * a.T + i) * a.Hkv + g) * kD;
+        const uint16_t x0 = src[lane], x1 = src[lane + 64];
+        const int t = Lb + i;
+        const int bk = a.bt[static_cast<long>(b) * a.max_blocks + t / kBlockSize];
+        if (bk < 0 || bk >= a.num_blocks) {
+          err |= SPEC_DEV_BLOCK;
+          continue;
+        }
+        uint16_t y0 = x0, y1 = x1;
+        if (!isv && a.rotate) {
+          const double2 cs = trig[i * 64 + lane];
+          float f0, f1;
+          rope_turn(bf16_to_f32(x0), bf16_to_f32(x1), cs.x, cs.y, &f0, &f1);
+          y0 = f32_to_bf16(f0);
+          y1 = f32_to_bf16(f1);
+        }
+        uint16_t* dst = (isv ? a.vc : a.kc) + ((static_cast<long>(bk) * a.Hkv + g) * kBlockSize + t % kBlockSize) * kD;
+        dst[lane] = y0;
+        dst[lane + 64] = y1;
+      }
+    }
+    __syncthreads();  // the rows are stored (the barrier's fence waits for them) and the table is free
+  }
 
 #pragma unroll
   for (int k = 0; k < DEPTH; ++k)
@@ -496,9 +567,14 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(const StArgs a) {
 }
 
 template <int NRB, int DEPTH>
-hipError_t run_stream(const StArgs& args, hipStream_t stream) {
+hipError_t run_stream(const StArgs& args, bool fused, hipStream_t stream) {
   const long grid = args.items;
-  hipLaunchKernelGGL((attn_stream_kernel<NRB, DEPTH>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, args);
+  if (fused)
+    hipLaunchKernelGGL((attn_stream_kernel<NRB, DEPTH, true>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
+                       args);
+  else
+    hipLaunchKernelGGL((attn_stream_kernel<NRB, DEPTH, false>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                       stream, args);
   return hipGetLastError();
 }
 
@@ -553,7 +629,7 @@ void plan_stream(AttnPlan& p, int B, int Hkv, int max_blocks) {
   p.ws_bytes = p.splits > 1 ? head + static_cast<size_t>(p.items) * p.rows * (kD + 2) * sizeof(float) : 0;
 }
 
-hipError_t launch_attn_stream(const AttnPlan& plan, const AttnLaunch& L, hipStream_t stream) {
+static StArgs stream_args(const AttnPlan& plan, const AttnLaunch& L) {
   StArgs a{};
   a.q = static_cast<const uint16_t*>(L.q);
   a.k = static_cast<const uint16_t*>(L.k);
@@ -583,8 +659,24 @@ hipError_t launch_attn_stream(const AttnPlan& plan, const AttnLaunch& L, hipStre
     a.part_o = reinterpret_cast<float*>(static_cast<char*>(L.workspace) + head);
     a.part_ml = a.part_o + static_cast<size_t>(plan.items) * plan.rows * kD;
   }
+  return a;
+}
+
+hipError_t launch_attn_stream(const AttnPlan& plan, const AttnLaunch& L, hipStream_t stream) {
   if (plan.nrb != 1 || plan.depth != SPEC_STREAM_DEPTH) return hipErrorInvalidValue;  // not a planned shape
-  return run_stream<1, SPEC_STREAM_DEPTH>(a, stream);
+  return run_stream<1, SPEC_STREAM_DEPTH>(stream_args(plan, L), false, stream);
+}
+
+hipError_t launch_attn_stream_write(const AttnPlan& plan, const AttnWriteLaunch& W, hipStream_t stream) {
+  if (plan.nrb != 1 || plan.depth != SPEC_STREAM_DEPTH || W.attn.T > 16) return hipErrorInvalidValue;
+  StArgs a = stream_args(plan, W.attn);
+  a.k_new = static_cast<const uint16_t*>(W.k_new);
+  a.v_new = static_cast<const uint16_t*>(W.v_new);
+  a.kc = static_cast<uint16_t*>(const_cast<void*>(W.attn.k));
+  a.vc = static_cast<uint16_t*>(const_cast<void*>(W.attn.v));
+  a.rotate = W.theta > 0.0f ? 1 : 0;
+  a.log2_theta = W.theta > 0.0f ? log2(static_cast<double>(W.theta)) : 0.0;
+  return run_stream<1, SPEC_STREAM_DEPTH>(a, true, stream);
 }
 
 }  // namespace spectree

@@ -95,6 +95,8 @@ AttnPlan plan_attn_write(int B, int T, int Hq, int Hkv, int max_blocks);
 hipError_t launch_attn_write(const AttnPlan& plan, const AttnWriteLaunch& w, hipStream_t stream);
 void plan_stream(AttnPlan& p, int B, int Hkv, int max_blocks);
 hipError_t launch_attn_stream(const AttnPlan& plan, const AttnLaunch& a, hipStream_t stream);
+// the same launch with the tree's K/V write (spec_tree_write_attn on a streaming plan)
+hipError_t launch_attn_stream_write(const AttnPlan& plan, const AttnWriteLaunch& w, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnPlan& plan, const AttnLaunch& a, hipStream_t stream);
 
 struct CompactLaunch {
