@@ -68,7 +68,7 @@ METRIC = "verified tree tokens/sec at 1 MI355X"
 TRUNC_K, TRUNC_P = 50, 0.9  # the truncated target measured beside the step: top-k 50, then top-p 0.9
 
 
-KERNEL_KEYS = (("tree_write_attn", ("attn_tile_kernel<1, true>", "attn_tile_kernel<2, true>")), ("tree_attn", ("attn_",)), ("tree_reject_compact", ("reject",)), ("kv_compact", ("kv_compact",)),
+KERNEL_KEYS = (("tree_write_attn", ("attn_tile_kernel<1, true>", "attn_tile_kernel<2, true>", "attn_stream_kernel<1, 3, true>")), ("tree_attn", ("attn_",)), ("tree_reject_compact", ("reject",)), ("kv_compact", ("kv_compact",)),
                ("tree_kv_write", ("kv_write",)), ("tree_truncate", ("truncate_kernel",)))
 CALIB_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
 CALIB_BYTES_BIG = 1 << 30  # a second calibration copy, four times the 256 MB MALL
@@ -79,7 +79,7 @@ def log(*a):
 
 
 KERNEL_SOURCES = {  # the sources each kernel key is built from (with common.h and the C-ABI header)
-    "tree_write_attn": ("attn_bf16.hip", "rope_dev.h"),
+    "tree_write_attn": ("attn_bf16.hip", "attn_stream.hip", "rope_dev.h"),
     "tree_attn": ("attn_bf16.hip", "attn_stream.hip", "attn_f32.hip"),
     "tree_reject_compact": ("reject.hip", "compact_dev.h"),
     "kv_compact": ("compact.hip", "compact_dev.h"),
